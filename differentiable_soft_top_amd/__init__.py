@@ -1,1 +1,115 @@
-"""MI355X-native LapSum soft top-k (placeholder until the binding lands)."""
+"""MI355X-native LapSum soft top-k.
+
+    p, b = soft_topk(scores, k, alpha)
+
+``scores``: 1-D fp32 tensor on a ROCm device.  ``p[i] = F((scores[i]-b)/alpha)``
+with F the standard Laplace CDF and b (fp64, one-element device tensor) the
+threshold at which ``p.sum() == k``.  ``p`` is differentiable with respect to
+``scores`` through the library's analytic vector-Jacobian product.
+
+This module only marshals arguments: tensors supply device memory and the
+current stream; every step of the computation runs in the HIP library
+(``libsofttopk.so``, C ABI in include/soft_topk.h).  There is no CPU path.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import Params, SoftTopKError, Stats  # noqa: F401
+
+__all__ = ["soft_topk", "forward", "backward", "Params", "Stats", "SoftTopKError", "default_params"]
+
+
+def default_params() -> Params:
+    return _lib.default_params()
+
+
+def _stream_handle(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_scores(s):
+    import torch
+    if not isinstance(s, torch.Tensor) or s.device.type != "cuda":
+        raise TypeError("scores must be a tensor on a ROCm device")
+    if s.dtype != torch.float32 or s.dim() != 1 or not s.is_contiguous():
+        raise TypeError("scores must be a contiguous 1-D float32 tensor")
+
+
+def forward(s, k: float, alpha: float, params: Params | None = None, out_p=None, want_stats: bool = False):
+    """Run soft_topk_forward_ex; returns (p, b[, stats dict])."""
+    import torch
+    _check_scores(s)
+    lib = _lib.load()
+    n = s.numel()
+    pp = ctypes.byref(params) if params is not None else None
+    ws_bytes = lib.soft_topk_workspace_bytes(n, pp)
+    if ws_bytes == 0:
+        raise SoftTopKError(_lib.EINVAL, "invalid size or params (n=%d)" % n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=s.device)
+    p = out_p if out_p is not None else torch.empty_like(s)
+    b = torch.empty(1, dtype=torch.float64, device=s.device)
+    stats = Stats()
+    rc = lib.soft_topk_forward_ex(ctypes.c_void_p(s.data_ptr()), n, float(k), float(alpha),
+                                  ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                                  ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream_handle(s),
+                                  pp, ctypes.byref(stats))
+    _lib.check(rc, "soft_topk_forward")
+    if want_stats:
+        return p, b, stats.as_dict()
+    return p, b
+
+
+def backward(grad_p, s, alpha: float, b, out=None):
+    """Run soft_topk_backward: (d_i/alpha)(g_i - G/D)."""
+    import torch
+    _check_scores(s)
+    if grad_p.dtype != torch.float32 or grad_p.shape != s.shape or not grad_p.is_contiguous():
+        raise TypeError("grad_p must be a contiguous float32 tensor shaped like scores")
+    if b.dtype != torch.float64 or b.numel() != 1 or b.device != s.device:
+        raise TypeError("b must be the one-element float64 device tensor from forward")
+    lib = _lib.load()
+    n = s.numel()
+    ws_bytes = lib.soft_topk_backward_workspace_bytes(n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=s.device)
+    g = out if out is not None else torch.empty_like(s)
+    rc = lib.soft_topk_backward(ctypes.c_void_p(grad_p.data_ptr()), ctypes.c_void_p(s.data_ptr()), n,
+                                float(alpha), ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(g.data_ptr()),
+                                ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream_handle(s))
+    _lib.check(rc, "soft_topk_backward")
+    return g
+
+
+def _function():
+    import torch
+
+    class _SoftTopK(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, s, k, alpha, params):
+            p, b = forward(s, k, alpha, params)
+            ctx.save_for_backward(s, b)
+            ctx.alpha = float(alpha)
+            ctx.mark_non_differentiable(b)
+            return p, b
+
+        @staticmethod
+        def backward(ctx, gp, gb):
+            s, b = ctx.saved_tensors
+            if gp is None:
+                return None, None, None, None
+            return backward(gp.contiguous(), s, ctx.alpha, b), None, None, None
+
+    return _SoftTopK
+
+
+_FN = None
+
+
+def soft_topk(s, k: float, alpha: float, params: Params | None = None):
+    """Differentiable LapSum soft top-k: returns (p, b)."""
+    global _FN
+    if _FN is None:
+        _FN = _function()
+    return _FN.apply(s, k, alpha, params)

@@ -1,0 +1,304 @@
+// band_sort.hip -- sort of the middle band only.
+//
+// aiqbench.com abstract of Fast LapSum: bracketing "restricts sorting to a
+// narrow band of scores around the threshold"; gist.science summary,
+// section 2.2 step 3: the exact solver runs on that band alone.
+//
+// gfx950 design: a value-bucket sort.  The band lies in [bmin, bmax] (known
+// from pass-1) and its density there is smooth, so kBuckets equal-width value
+// buckets hold similar counts.  Three kernels:
+//   1. histogram: per-work-group LDS bucket counts; the last work-group turns
+//      them into global scatter offsets (bucket-major, work-group-minor);
+//   2. scatter: each element goes to its bucket (order within a bucket is
+//      arbitrary);
+//   3. bucket sort: one work-group per bucket sorts it in LDS (bitonic on
+//      order-preserving keys), writes it back and records the bucket
+//      summary (count, first, last, TA = sum e^{(x-last)/alpha},
+//      TB = sum e^{-(x-first)/alpha}) that the segment solve scans.
+// The bucket index floor((v - bmin) * kBuckets / (bmax - bmin)) is
+// non-decreasing in v, so the buckets concatenate into a sorted band.
+#include "stk_common.hpp"
+#include "stk_layout.hpp"
+#include "stk_prof.hpp"
+
+namespace stk {
+
+namespace {
+
+__device__ __forceinline__ int bucket_of(float v, double lo, double scale)
+{
+    const double t = ((double)v - lo) * scale;
+    int b = (int)t;
+    b = b < 0 ? 0 : b;
+    return b > kBuckets - 1 ? kBuckets - 1 : b;
+}
+
+// Shared early-exit test: band overflow or a non-finite score makes every
+// band kernel a no-op (the segment solve records why).
+__device__ __forceinline__ bool band_unusable(const Status* st, int64_t cap)
+{
+    return st->nB > (uint64_t)cap;
+}
+
+__device__ __forceinline__ int band_groups(uint64_t nB)
+{
+    return nB == 0 ? 1 : (int)((nB + kBandChunk - 1) / kBandChunk);
+}
+
+// Bucket range: the bracket itself when both ends are finite (the band lies
+// in [a_L, a_R)), else the band's own min/max from the pass-1 partials (same
+// fixed-order fold in every work-group, so every work-group maps a value to
+// the same bucket).
+__device__ void bucket_range(const BandArgs& a, double* lo, double* scale)
+{
+    __shared__ float mm[2];
+    const float aL = a.st->aL, aR = a.st->aR;
+    float l = aL, h = aR;
+    if (aL == -INFINITY || aR == INFINITY) {
+        float bmin = INFINITY, bmax = -INFINITY;
+        for (int i = threadIdx.x; i < a.p1_blocks; i += blockDim.x) {
+            bmin = fminf(bmin, a.p1[i].bmin);
+            bmax = fmaxf(bmax, a.p1[i].bmax);
+        }
+        bmin = wave_min(bmin);
+        bmax = wave_max(bmax);
+        __shared__ float wmm[2][kSortThreads / kWave];
+        if ((threadIdx.x & (kWave - 1)) == 0) {
+            wmm[0][threadIdx.x / kWave] = bmin;
+            wmm[1][threadIdx.x / kWave] = bmax;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float x = INFINITY, y = -INFINITY;
+            for (int w = 0; w < kSortThreads / kWave; ++w) {
+                x = fminf(x, wmm[0][w]);
+                y = fmaxf(y, wmm[1][w]);
+            }
+            mm[0] = x;
+            mm[1] = y;
+        }
+        __syncthreads();
+        l = mm[0];
+        h = mm[1];
+    }
+    *lo = l;
+    *scale = (h > l) ? (double)kBuckets / ((double)h - (double)l) : 0.0;
+}
+
+}  // namespace
+
+// Per-work-group bucket counts of one chunk of the band (no cross-group step:
+// the scatter kernel derives the offsets from all rows).
+__global__ __launch_bounds__(kSortThreads) void band_hist_kernel(BandArgs a)
+{
+    __shared__ uint32_t hist[kBuckets];
+    const Status* st = a.st;
+    if (band_unusable(st, a.cap))
+        return;
+    const uint64_t nB = st->nB;
+    const int used = band_groups(nB);
+    if ((int)blockIdx.x >= used)
+        return;
+    const int tid = threadIdx.x;
+    double lo, scale;
+    bucket_range(a, &lo, &scale);
+    for (int i = tid; i < kBuckets; i += kSortThreads)
+        hist[i] = 0;
+    __syncthreads();
+    const uint64_t e0 = (uint64_t)blockIdx.x * kBandChunk;
+    const uint64_t e1 = e0 + kBandChunk < nB ? e0 + kBandChunk : nB;
+    for (uint64_t i = e0 + tid; i < e1; i += kSortThreads)
+        atomicAdd(&hist[bucket_of(a.band[i], lo, scale)], 1u);
+    __syncthreads();
+    uint32_t* row = a.hist + (size_t)blockIdx.x * kBuckets;
+    for (int i = tid; i < kBuckets; i += kSortThreads)
+        row[i] = hist[i];
+}
+
+// Each work-group reads every row of the bucket histogram, forms the bucket
+// starts (exclusive scan of the column sums) and its own offsets (plus the
+// counts of the groups before it), then scatters its chunk.  Work-group 0
+// also publishes the bucket starts.
+__global__ __launch_bounds__(kSortThreads) void band_scatter_kernel(BandArgs a)
+{
+    constexpr int kPer = kBuckets / kSortThreads;  // buckets per thread
+    static_assert(kPer == 8, "two uint4 per thread");
+    __shared__ uint32_t cursor[kBuckets];
+    __shared__ uint32_t scan_tmp[kSortThreads];
+    const Status* st = a.st;
+    if (band_unusable(st, a.cap))
+        return;
+    const uint64_t nB = st->nB;
+    const int used = band_groups(nB);
+    if ((int)blockIdx.x >= used)
+        return;
+    const int tid = threadIdx.x;
+    const int me = blockIdx.x;
+    double lo, scale;
+    bucket_range(a, &lo, &scale);
+
+    uint32_t tot[kPer], before[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        tot[j] = 0;
+        before[j] = 0;
+    }
+    for (int w = 0; w < used; ++w) {
+        const uint4* row = reinterpret_cast<const uint4*>(a.hist + (size_t)w * kBuckets + tid * kPer);
+        const uint4 x = row[0], y = row[1];
+        const uint32_t v[kPer] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            tot[j] += v[j];
+            before[j] += w < me ? v[j] : 0u;
+        }
+    }
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        local += tot[j];
+    scan_tmp[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < kSortThreads; off <<= 1) {
+        const uint32_t v = tid >= off ? scan_tmp[tid - off] : 0u;
+        __syncthreads();
+        scan_tmp[tid] += v;
+        __syncthreads();
+    }
+    uint32_t base = scan_tmp[tid] - local;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int b = tid * kPer + j;
+        cursor[b] = base + before[j];
+        if (me == 0)
+            a.bstart[b] = base;
+        base += tot[j];
+    }
+    if (me == 0 && tid == 0)
+        a.bstart[kBuckets] = (uint32_t)nB;
+    __syncthreads();
+    const uint64_t e0 = (uint64_t)me * kBandChunk;
+    const uint64_t e1 = e0 + kBandChunk < nB ? e0 + kBandChunk : nB;
+    for (uint64_t i = e0 + tid; i < e1; i += kSortThreads) {
+        const float v = a.band[i];
+        const uint32_t pos = atomicAdd(&cursor[bucket_of(v, lo, scale)], 1u);
+        a.band_sorted[pos] = v;
+    }
+}
+
+// One work-group per bucket.
+__global__ __launch_bounds__(kSortThreads) void bucket_sort_kernel(BandArgs a)
+{
+    __shared__ uint32_t keys[kBucketCap];
+    __shared__ double red[2][kSortThreads / kWave];
+    __shared__ float redf[2][kSortThreads / kWave];
+    const Status* st = a.st;
+    if (band_unusable(st, a.cap))
+        return;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const uint32_t start = a.bstart[b];
+    const uint32_t end = a.bstart[b + 1];
+    const uint32_t cnt = end - start;
+    GroupAgg g;
+    g.cnt = cnt;
+    g.start = start;
+    if (cnt == 0) {
+        if (tid == 0) {
+            g.TA = 0.0;
+            g.TB = 0.0;
+            g.lo = 0.f;
+            g.hi = 0.f;
+            a.agg[b] = g;
+        }
+        return;
+    }
+    const double c = a.log2e_over_alpha;
+    float lo, hi;
+    double TA = 0.0, TB = 0.0;
+    if (cnt <= (uint32_t)kBucketCap) {
+        int n2 = 64;
+        while ((uint32_t)n2 < cnt)
+            n2 <<= 1;
+        for (int i = tid; i < n2; i += kSortThreads)
+            keys[i] = (uint32_t)i < cnt ? float_to_key(a.band_sorted[start + i]) : 0xFFFFFFFFu;
+        __syncthreads();
+        lds_bitonic_sort(keys, n2);
+        lo = key_to_float(keys[0]);
+        hi = key_to_float(keys[cnt - 1]);
+        const double dlo = lo, dhi = hi;
+        for (uint32_t i = tid; i < cnt; i += kSortThreads) {
+            const float v = key_to_float(keys[i]);
+            a.band_sorted[start + i] = v;
+            TA += exp2_nonpos(((double)v - dhi) * c);
+            TB += exp2_nonpos((dlo - (double)v) * c);
+        }
+    } else {
+        // too large for LDS: acceptable only if every value is equal
+        float mn = INFINITY, mx = -INFINITY;
+        for (uint32_t i = tid; i < cnt; i += kSortThreads) {
+            const float v = a.band_sorted[start + i];
+            mn = fminf(mn, v);
+            mx = fmaxf(mx, v);
+        }
+        mn = wave_min(mn);
+        mx = wave_max(mx);
+        if (lane == 0) {
+            redf[0][wave] = mn;
+            redf[1][wave] = mx;
+        }
+        __syncthreads();
+        lo = INFINITY;
+        hi = -INFINITY;
+        for (int w = 0; w < kSortThreads / kWave; ++w) {
+            lo = fminf(lo, redf[0][w]);
+            hi = fmaxf(hi, redf[1][w]);
+        }
+        if (lo != hi) {
+            if (tid == 0)
+                a.st->solve_state = kSolveBucketOverflow;
+            return;
+        }
+        for (uint32_t i = tid; i < cnt; i += kSortThreads) {
+            TA += 1.0;
+            TB += 1.0;
+        }
+    }
+    TA = wave_sum(TA);
+    TB = wave_sum(TB);
+    if (lane == 0) {
+        red[0][wave] = TA;
+        red[1][wave] = TB;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double sa = 0.0, sb = 0.0;
+        for (int w = 0; w < kSortThreads / kWave; ++w) {
+            sa += red[0][w];
+            sb += red[1][w];
+        }
+        g.TA = sa;
+        g.TB = sb;
+        g.lo = lo;
+        g.hi = hi;
+        a.agg[b] = g;
+    }
+}
+
+hipError_t launch_band_sort(const BandArgs& a, hipStream_t stream)
+{
+    STK_LAUNCH(kKBandHist, stream, band_hist_kernel, dim3(a.blocks), dim3(kSortThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    STK_LAUNCH(kKBandScatter, stream, band_scatter_kernel, dim3(a.blocks), dim3(kSortThreads), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    STK_LAUNCH(kKBucketSort, stream, bucket_sort_kernel, dim3(kBuckets), dim3(kSortThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace stk

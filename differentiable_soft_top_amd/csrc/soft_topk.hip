@@ -1,0 +1,650 @@
+// soft_topk.hip -- host orchestration and the C ABI (include/soft_topk.h).
+//
+// Route of one forward call (aiqbench.com abstract of Fast LapSum;
+// gist.science summary, section 2.2, "Probabilistic Bracketing" steps 1-4):
+//   sample -> select bracket -> pass-1 (tails + band) -> band sort ->
+//   segment solve with the bracket certificate -> emit p with the fp64 mass
+//   check -> one status read-back.
+// A rejected certificate widens the bracket on the failing side (the other
+// end becomes the rejected end, which is then a proven bound) and reruns
+// pass-1; an overfull band, an unsortable bucket, a failed mass check or
+// exhausted widenings take the full device radix sort, whose solve needs no
+// bracket.  The host only chooses among these routes; every step of the
+// arithmetic runs in the kernels.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "soft_topk.h"
+#include "stk_common.hpp"
+#include "stk_layout.hpp"
+
+namespace stk {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+thread_local int g_last_hip = 0;
+thread_local Status* g_pinned = nullptr;
+
+int hip_fail(hipError_t e)
+{
+    g_last_hip = (int)e;
+    return SOFT_TOPK_EHIP;
+}
+
+#define STK_HIP(expr)                         \
+    do {                                      \
+        const hipError_t e_ = (expr);         \
+        if (e_ != hipSuccess)                 \
+            return hip_fail(e_);              \
+    } while (0)
+
+int32_t stream_blocks(int64_t n)
+{
+    const int64_t n4 = n >> 2;
+    int64_t g = (n4 + 511) / 512;
+    g = std::max<int64_t>(1, std::min<int64_t>(g, kStreamMaxBlocks));
+    return (int32_t)g;
+}
+
+// The (D, G) reduction reads 8 B per score and streams at full rate with few
+// work-groups; fewer partials make the per-work-group fold in the gradient
+// kernel cheaper.
+int32_t vjp_reduce_blocks(int64_t n) { return std::min<int32_t>(stream_blocks(n), 512); }
+
+int64_t default_cap(int64_t n)
+{
+    int64_t c = n / 4;
+    c = std::max<int64_t>(c, 1 << 16);
+    c = std::min<int64_t>(c, 1 << 22);
+    return std::min<int64_t>(c, n);
+}
+
+void fill_defaults(soft_topk_params* p)
+{
+    p->seed = 0x5eedull;
+    p->samples = 65536;
+    p->z = 5.0;
+    p->band_capacity = 0;
+    p->max_widen = 2;
+    p->force_path = 0;
+    p->mass_tolerance = 0.0;
+}
+
+bool params_ok(const soft_topk_params& p)
+{
+    if (p.samples < 1024 || p.samples > 262144)
+        return false;
+    if (!(p.z > 0.0) || !isfinite(p.z) || p.z > 30.0)
+        return false;
+    if (p.band_capacity < 0 || p.max_widen < 0 || p.max_widen > 16)
+        return false;
+    if (p.force_path != 0 && p.force_path != SOFT_TOPK_PATH_FULLSORT)
+        return false;
+    if (!isfinite(p.mass_tolerance))
+        return false;
+    return true;
+}
+
+// ---- binomial rank arithmetic --------------------------------------------
+double log_pmf(int64_t m, double q, int64_t i)
+{
+    return lgamma((double)m + 1.0) - lgamma((double)i + 1.0) - lgamma((double)(m - i) + 1.0) +
+           (double)i * log(q) + (double)(m - i) * log1p(-q);
+}
+
+// P(X <= r), X ~ Binomial(m, q); summed from r downward while terms matter.
+double cdf_le(int64_t m, double q, int64_t r)
+{
+    if (r < 0)
+        return 0.0;
+    if (r >= m)
+        return 1.0;
+    double s = 0.0;
+    for (int64_t i = r; i >= 0; --i) {
+        const double t = exp(log_pmf(m, q, i));
+        s += t;
+        if ((double)i < (double)m * q && t < 1e-20 * s)
+            break;
+        if (s > 1.0)
+            break;
+    }
+    return std::min(s, 1.0);
+}
+
+// P(X >= r)
+double sf_ge(int64_t m, double q, int64_t r)
+{
+    if (r <= 0)
+        return 1.0;
+    if (r > m)
+        return 0.0;
+    double s = 0.0;
+    for (int64_t i = r; i <= m; ++i) {
+        const double t = exp(log_pmf(m, q, i));
+        s += t;
+        if ((double)i > (double)m * q && t < 1e-20 * s)
+            break;
+        if (s > 1.0)
+            break;
+    }
+    return std::min(s, 1.0);
+}
+
+// Lower rank: largest r >= 1 with P(X <= r-1) <= delta, else 0 (= -inf).
+int64_t lower_rank(int64_t m, double q, double z)
+{
+    const double delta = 0.5 * erfc(z / sqrt(2.0));
+    const double sd = sqrt((double)m * q * (1.0 - q));
+    int64_t r = (int64_t)floor((double)m * q - z * sd);
+    r = std::max<int64_t>(0, std::min<int64_t>(r, m));
+    while (r >= 1 && cdf_le(m, q, r - 1) > delta)
+        --r;
+    while (r + 1 <= m && cdf_le(m, q, r) <= delta)
+        ++r;
+    if (r >= 1 && cdf_le(m, q, r - 1) > delta)
+        r = 0;
+    return r;
+}
+
+// Upper rank: smallest r <= m with P(X >= r) <= delta, else m + 1 (= +inf).
+int64_t upper_rank(int64_t m, double q, double z)
+{
+    const double delta = 0.5 * erfc(z / sqrt(2.0));
+    const double sd = sqrt((double)m * q * (1.0 - q));
+    int64_t r = (int64_t)ceil((double)m * q + z * sd) + 1;
+    r = std::max<int64_t>(1, std::min<int64_t>(r, m + 1));
+    while (r <= m && sf_ge(m, q, r) > delta)
+        ++r;
+    while (r - 1 >= 1 && sf_ge(m, q, r - 1) <= delta)
+        --r;
+    return r;
+}
+
+void pilot_ranks(int32_t m, double q, int64_t rl, int64_t rr, int32_t* plo, int32_t* phi)
+{
+    const int32_t P = std::min<int32_t>(m, kPilot);
+    const double sd = sqrt((double)P * q * (1.0 - q));
+    const double zp = 7.0;
+    int64_t lo = rl <= 0 ? 0 : (int64_t)floor((double)rl * P / m - zp * sd - 2.0);
+    int64_t hi = rr > m ? (int64_t)P + 1 : (int64_t)ceil((double)rr * P / m + zp * sd + 2.0);
+    lo = std::max<int64_t>(0, std::min<int64_t>(lo, P));
+    hi = std::max<int64_t>(1, std::min<int64_t>(hi, (int64_t)P + 1));
+    *plo = (int32_t)lo;
+    *phi = (int32_t)hi;
+}
+
+uint32_t host_key(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct Ctx {
+    const float* s;
+    int64_t n;
+    double k, alpha, c;
+    float* p;
+    double* b;
+    char* ws;
+    Plan plan;
+    hipStream_t stream;
+    Status* st;
+};
+
+int read_status(const Ctx& x, Status* host)
+{
+    if (!g_pinned) {
+        void* ptr = nullptr;
+        STK_HIP(hipHostMalloc(&ptr, sizeof(Status), hipHostMallocDefault));
+        g_pinned = static_cast<Status*>(ptr);
+    }
+    STK_HIP(hipMemcpyAsync(g_pinned, x.st, sizeof(Status), hipMemcpyDeviceToHost, x.stream));
+    STK_HIP(hipStreamSynchronize(x.stream));
+    memcpy(host, g_pinned, sizeof(Status));
+    return SOFT_TOPK_OK;
+}
+
+template <typename T>
+T* at(const Ctx& x, size_t off)
+{
+    return reinterpret_cast<T*>(x.ws + off);
+}
+
+int enqueue_pass1(const Ctx& x)
+{
+    Pass1Args a;
+    a.s = x.s;
+    a.n = x.n;
+    a.log2e_over_alpha = x.c;
+    a.band = at<float>(x, x.plan.off_band);
+    a.cap = x.plan.cap;
+    a.partials = at<Pass1Partial>(x, x.plan.off_p1part);
+    a.blocks = x.plan.g_stream;
+    a.st = x.st;
+    STK_HIP(launch_pass1(a, x.stream));
+    return SOFT_TOPK_OK;
+}
+
+int enqueue_emit(const Ctx& x)
+{
+    EmitArgs e;
+    e.s = x.s;
+    e.n = x.n;
+    e.alpha = x.alpha;
+    e.log2e_over_alpha = x.c;
+    e.b = x.b;
+    e.p = x.p;
+    e.partials = at<double>(x, x.plan.off_emitpart);
+    e.blocks = x.plan.g_stream;
+    e.st = x.st;
+    STK_HIP(launch_emit(e, x.stream));
+    return SOFT_TOPK_OK;
+}
+
+// One bracketed round: select with ranks (rl, rr), pass-1, band sort, solve, emit.
+int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q)
+{
+    SelectArgs sa;
+    sa.samples = at<float>(x, x.plan.off_samples);
+    sa.m = x.plan.m;
+    sa.r_left = rl;
+    sa.r_right = rr;
+    pilot_ranks(x.plan.m, q, rl, rr, &sa.pilot_lo, &sa.pilot_hi);
+    sa.st = x.st;
+    STK_HIP(launch_select(sa, x.stream));
+    int rc = enqueue_pass1(x);
+    if (rc)
+        return rc;
+    BandArgs ba;
+    ba.p1 = at<Pass1Partial>(x, x.plan.off_p1part);
+    ba.p1_blocks = x.plan.g_stream;
+    ba.band = at<float>(x, x.plan.off_band);
+    ba.band_sorted = at<float>(x, x.plan.off_band_sorted);
+    ba.cap = x.plan.cap;
+    ba.hist = at<uint32_t>(x, x.plan.off_hist);
+    ba.bstart = at<uint32_t>(x, x.plan.off_bstart);
+    ba.agg = at<GroupAgg>(x, x.plan.off_agg);
+    ba.blocks = x.plan.g_band;
+    ba.log2e_over_alpha = x.c;
+    ba.st = x.st;
+    STK_HIP(launch_band_sort(ba, x.stream));
+    SolveArgs so;
+    so.p1 = ba.p1;
+    so.p1_blocks = ba.p1_blocks;
+    so.sorted = ba.band_sorted;
+    so.agg = ba.agg;
+    so.scan = at<GroupScan>(x, x.plan.off_scan);
+    so.groups = kBuckets;
+    so.tails = 1;
+    so.cap = x.plan.cap;
+    so.k = x.k;
+    so.alpha = x.alpha;
+    so.log2e_over_alpha = x.c;
+    so.out_b = x.b;
+    so.st = x.st;
+    STK_HIP(launch_solve(so, x.stream));
+    return enqueue_emit(x);
+}
+
+int enqueue_fullsort(const Ctx& x, const Status& last, bool have_range)
+{
+    STK_HIP(launch_reset_status(x.st, x.stream, false));
+    uint32_t kmin = 0;
+    int passes = 4;
+    if (have_range) {
+        kmin = host_key(last.smin);
+        const uint32_t span = host_key(last.smax) - kmin;
+        int bits = 0;
+        while (bits < 32 && (span >> bits) != 0)
+            ++bits;
+        passes = std::max(1, (bits + 7) / 8);
+    }
+    RadixArgs ra;
+    ra.s = x.s;
+    ra.n = x.n;
+    ra.keys0 = at<uint32_t>(x, x.plan.off_keys0);
+    ra.keys1 = at<uint32_t>(x, x.plan.off_keys1);
+    ra.hist = at<uint32_t>(x, x.plan.off_rhist);
+    ra.g_radix = x.plan.g_radix;
+    ra.key_min = kmin;
+    ra.passes = passes;
+    ra.st = x.st;
+    uint32_t* sorted = nullptr;
+    ra.sorted_out = &sorted;
+    STK_HIP(launch_radix_sort(ra, x.stream));
+    TileArgs ta;
+    ta.keys = sorted;
+    ta.n = x.n;
+    ta.key_min = kmin;
+    ta.agg = at<GroupAgg>(x, x.plan.off_agg);
+    ta.n_tiles = x.plan.n_tiles;
+    ta.log2e_over_alpha = x.c;
+    STK_HIP(launch_tile_aggregates(ta, x.stream));
+    SolveArgs so;
+    so.p1 = nullptr;
+    so.p1_blocks = 0;
+    so.sorted = reinterpret_cast<const float*>(sorted);
+    so.agg = ta.agg;
+    so.scan = at<GroupScan>(x, x.plan.off_scan);
+    so.groups = x.plan.n_tiles;
+    so.tails = 0;
+    so.cap = x.plan.cap;
+    so.k = x.k;
+    so.alpha = x.alpha;
+    so.log2e_over_alpha = x.c;
+    so.out_b = x.b;
+    so.st = x.st;
+    STK_HIP(launch_solve(so, x.stream));
+    return enqueue_emit(x);
+}
+
+bool mass_ok(const Status& h, double k, double tol)
+{
+    return h.emit_done && fabs(h.mass - k) <= tol;
+}
+
+}  // namespace
+
+Plan make_plan(int64_t n, int32_t m, int64_t cap)
+{
+    Plan p;
+    memset(&p, 0, sizeof(p));
+    p.n = n;
+    p.m = m;
+    p.cap = cap;
+    p.g_stream = stream_blocks(n);
+    p.g_band = (int32_t)std::max<int64_t>(1, (cap + kBandChunk - 1) / kBandChunk);
+    p.n_tiles = (int32_t)((n + kTile - 1) / kTile);
+    p.g_radix = (int32_t)((n + kRadixTile - 1) / kRadixTile);
+    const int64_t groups = std::max<int64_t>(kBuckets, p.n_tiles);
+    size_t o = 0;
+    p.off_status = o;
+    o = align_up(o + sizeof(Status));
+    p.off_samples = o;
+    o = align_up(o + sizeof(float) * (size_t)m);
+    p.off_p1part = o;
+    o = align_up(o + sizeof(Pass1Partial) * (size_t)p.g_stream);
+    p.off_band = o;
+    o = align_up(o + sizeof(float) * (size_t)cap);
+    p.off_band_sorted = o;
+    o = align_up(o + sizeof(float) * (size_t)cap);
+    p.off_hist = o;
+    o = align_up(o + sizeof(uint32_t) * (size_t)p.g_band * kBuckets);
+    p.off_bstart = o;
+    o = align_up(o + sizeof(uint32_t) * (kBuckets + 1));
+    p.off_agg = o;
+    o = align_up(o + sizeof(GroupAgg) * (size_t)groups);
+    p.off_scan = o;
+    o = align_up(o + sizeof(GroupScan) * (size_t)groups);
+    p.off_emitpart = o;
+    o = align_up(o + sizeof(double) * (size_t)p.g_stream);
+    p.off_keys0 = o;
+    o = align_up(o + sizeof(uint32_t) * (size_t)n);
+    p.off_keys1 = o;
+    o = align_up(o + sizeof(uint32_t) * (size_t)n);
+    p.off_rhist = o;
+    o = align_up(o + sizeof(uint32_t) * kRadixBins * (size_t)((p.g_radix + 3) & ~3));
+    p.total = o;
+    return p;
+}
+
+}  // namespace stk
+
+using namespace stk;
+
+namespace {
+
+bool n_ok(int64_t n) { return n >= 1 && n <= 0x7fffffffLL; }
+
+soft_topk_params resolve(const soft_topk_params* params)
+{
+    soft_topk_params p;
+    fill_defaults(&p);
+    if (params)
+        p = *params;
+    return p;
+}
+
+Plan plan_for(int64_t n, const soft_topk_params& p)
+{
+    const int64_t cap = p.band_capacity > 0 ? std::min<int64_t>(p.band_capacity, n) : default_cap(n);
+    return make_plan(n, p.samples, cap);
+}
+
+}  // namespace
+
+extern "C" {
+
+void soft_topk_default_params(soft_topk_params* params)
+{
+    if (params)
+        fill_defaults(params);
+}
+
+size_t soft_topk_workspace_bytes(int64_t n, const soft_topk_params* params)
+{
+    if (!n_ok(n))
+        return 0;
+    const soft_topk_params p = resolve(params);
+    if (!params_ok(p))
+        return 0;
+    return plan_for(n, p).total;
+}
+
+size_t soft_topk_backward_workspace_bytes(int64_t n)
+{
+    if (!n_ok(n))
+        return 0;
+    return align_up(sizeof(double) * 2 * (size_t)vjp_reduce_blocks(n));
+}
+
+const char* soft_topk_strerror(int code)
+{
+    switch (code) {
+    case SOFT_TOPK_OK:
+        return "ok";
+    case SOFT_TOPK_EINVAL:
+        return "invalid argument";
+    case SOFT_TOPK_ENONFINITE:
+        return "a score is NaN or infinite";
+    case SOFT_TOPK_EWORKSPACE:
+        return "workspace missing, misaligned or too small";
+    case SOFT_TOPK_EHIP:
+        return "HIP runtime error";
+    case SOFT_TOPK_ESOLVE:
+        return "no route produced a certified threshold";
+    default:
+        return "unknown error";
+    }
+}
+
+int soft_topk_last_hip_error(void) { return g_last_hip; }
+
+int soft_topk_bracket_ranks(int64_t m, double q, double z, int64_t* r_left, int64_t* r_right)
+{
+    if (m < 1 || !(q > 0.0) || !(q < 1.0) || !(z > 0.0) || !isfinite(z) || !r_left || !r_right)
+        return SOFT_TOPK_EINVAL;
+    *r_left = lower_rank(m, q, z);
+    *r_right = upper_rank(m, q, z);
+    return SOFT_TOPK_OK;
+}
+
+int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha, float* out_p,
+                         double* out_b, void* workspace, size_t workspace_bytes, void* stream,
+                         const soft_topk_params* params, soft_topk_stats* stats)
+{
+    if (!scores || !out_p || !out_b || !n_ok(n))
+        return SOFT_TOPK_EINVAL;
+    if (!(alpha > 0.0) || !isfinite(alpha) || !(k > 0.0) || !(k < (double)n) || !isfinite(k))
+        return SOFT_TOPK_EINVAL;
+    const soft_topk_params prm = resolve(params);
+    if (!params_ok(prm))
+        return SOFT_TOPK_EINVAL;
+    const Plan plan = plan_for(n, prm);
+    if (!workspace || workspace_bytes < plan.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return SOFT_TOPK_EWORKSPACE;
+
+    Ctx x;
+    x.s = scores;
+    x.n = n;
+    x.k = k;
+    x.alpha = alpha;
+    x.c = kLog2e / alpha;
+    x.p = out_p;
+    x.b = out_b;
+    x.ws = static_cast<char*>(workspace);
+    x.plan = plan;
+    x.stream = static_cast<hipStream_t>(stream);
+    x.st = reinterpret_cast<Status*>(x.ws + plan.off_status);
+
+    const double tol = prm.mass_tolerance > 0.0 ? prm.mass_tolerance : 1e-3 + 1e-12 * (double)n;
+    soft_topk_stats sx;
+    memset(&sx, 0, sizeof(sx));
+    Status h;
+    memset(&h, 0, sizeof(h));
+    bool have_range = false;
+    bool done = false;
+
+    if (prm.force_path != SOFT_TOPK_PATH_FULLSORT) {
+        const double q = 1.0 - k / (double)n;
+        int64_t rl = lower_rank(plan.m, q, prm.z);
+        int64_t rr = upper_rank(plan.m, q, prm.z);
+        STK_HIP(launch_sample(x.s, n, (float)alpha, prm.seed, plan.m, at<float>(x, plan.off_samples), x.st,
+                              x.stream));
+        for (int round = 0; round <= prm.max_widen && !done; ++round) {
+            int rc = enqueue_round(x, rl, rr, q);
+            if (rc)
+                return rc;
+            rc = read_status(x, &h);
+            if (rc)
+                return rc;
+            sx.rounds = round + 1;
+            sx.a_left = h.aL;
+            sx.a_right = h.aR;
+            sx.n_left = (int64_t)h.nL;
+            sx.n_right = (int64_t)h.nR;
+            sx.n_band = (int64_t)h.nB;
+            sx.mass_at_left = h.massL;
+            sx.mass_at_right = h.massR;
+            have_range = true;
+            if (h.nonfinite)
+                return SOFT_TOPK_ENONFINITE;
+            if (h.solve_state == kSolveOk && mass_ok(h, k, tol)) {
+                sx.path = round == 0 ? SOFT_TOPK_PATH_BRACKET : SOFT_TOPK_PATH_WIDENED;
+                done = true;
+                break;
+            }
+            if (h.solve_state == kSolveRejectLow) {
+                sx.reject_mask |= SOFT_TOPK_REJECT_LOW;
+                // b < a_L: the old lower end is now a proven upper end
+                const double z2 = prm.z * (double)(2 << round);
+                rr = rl;
+                rl = lower_rank(plan.m, q, z2);
+                if (rl >= rr)
+                    rl = 0;
+                continue;
+            }
+            if (h.solve_state == kSolveRejectHigh) {
+                sx.reject_mask |= SOFT_TOPK_REJECT_HIGH;
+                const double z2 = prm.z * (double)(2 << round);
+                rl = rr;
+                rr = upper_rank(plan.m, q, z2);
+                if (rr <= rl)
+                    rr = plan.m + 1;
+                continue;
+            }
+            if (h.solve_state == kSolveOverflow)
+                sx.reject_mask |= SOFT_TOPK_REJECT_OVERFLOW;
+            else if (h.solve_state == kSolveBucketOverflow)
+                sx.reject_mask |= SOFT_TOPK_REJECT_BUCKET;
+            else
+                sx.reject_mask |= SOFT_TOPK_REJECT_MASS;
+            break;  // widening cannot help: go to the full sort
+        }
+    } else {
+        // no bracketed round ran: one pass-1 with an empty band
+        // (a_L = a_R = +inf) gives the score range and the finiteness check
+        STK_HIP(launch_reset_status(x.st, x.stream, true));
+        int rc = enqueue_pass1(x);
+        if (rc)
+            return rc;
+        STK_HIP(launch_pass1_finalize(at<Pass1Partial>(x, plan.off_p1part), plan.g_stream, x.st, x.stream));
+        rc = read_status(x, &h);
+        if (rc)
+            return rc;
+        if (h.nonfinite)
+            return SOFT_TOPK_ENONFINITE;
+        have_range = true;
+    }
+
+    if (!done) {
+        int rc = enqueue_fullsort(x, h, have_range);
+        if (rc)
+            return rc;
+        rc = read_status(x, &h);
+        if (rc)
+            return rc;
+        if (h.solve_state != kSolveOk || !mass_ok(h, k, tol))
+            return SOFT_TOPK_ESOLVE;
+        sx.path = SOFT_TOPK_PATH_FULLSORT;
+    }
+    sx.b = h.b;
+    sx.mass = h.mass;
+    if (stats)
+        *stats = sx;
+    return SOFT_TOPK_OK;
+}
+
+int soft_topk_forward(const float* scores, int64_t n, double k, double alpha, float* out_p, double* out_b,
+                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    return soft_topk_forward_ex(scores, n, k, alpha, out_p, out_b, workspace, workspace_bytes, stream,
+                                nullptr, nullptr);
+}
+
+int soft_topk_backward(const float* grad_p, const float* scores, int64_t n, double alpha, const double* b,
+                       float* grad_s, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!grad_p || !scores || !b || !grad_s || !n_ok(n))
+        return SOFT_TOPK_EINVAL;
+    if (!(alpha > 0.0) || !isfinite(alpha))
+        return SOFT_TOPK_EINVAL;
+    const size_t need = soft_topk_backward_workspace_bytes(n);
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % 16) != 0)
+        return SOFT_TOPK_EWORKSPACE;
+    VjpArgs a;
+    a.g = grad_p;
+    a.s = scores;
+    a.n = n;
+    a.alpha = alpha;
+    a.log2e_over_alpha = kLog2e / alpha;
+    a.b = b;
+    a.grad = grad_s;
+    a.partials = static_cast<double*>(workspace);
+    a.blocks = stream_blocks(n);
+    a.reduce_blocks = vjp_reduce_blocks(n);
+    STK_HIP(launch_vjp(a, static_cast<hipStream_t>(stream)));
+    return SOFT_TOPK_OK;
+}
+
+int soft_topk_debug_sample(const float* scores, int64_t n, double alpha, uint64_t seed, int32_t m,
+                           float* out_samples, void* stream)
+{
+    if (!scores || !out_samples || !n_ok(n) || m < 1 || m > (1 << 24) || !(alpha > 0.0) || !isfinite(alpha))
+        return SOFT_TOPK_EINVAL;
+    STK_HIP(launch_sample(scores, n, (float)alpha, seed, m, out_samples, nullptr,
+                          static_cast<hipStream_t>(stream)));
+    return SOFT_TOPK_OK;
+}
+
+}  // extern "C"

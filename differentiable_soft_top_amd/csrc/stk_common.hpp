@@ -1,0 +1,199 @@
+// stk_common.hpp -- device helpers shared by the soft top-k kernels (gfx950).
+//
+// Nothing here is specific to one kernel: the fp64 exponential used wherever
+// a sum of exponentials feeds the threshold, the order-preserving fp32 key,
+// the Philox4x32-10 counter-based generator, wave-64 reductions and an LDS
+// bitonic sort.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace stk {
+
+constexpr int kWave = 64;
+constexpr double kLog2e = 1.4426950408889634;
+constexpr double kLn2 = 0.6931471805599453;
+
+// ---------------------------------------------------------------------------
+// 2^y for y <= 0 in fp64, relative error ~2e-16.
+// Range reduction y = j + r with j = rint(y), |r| <= 1/2, then
+// e^(r ln 2) by its Taylor series to degree 12 (the truncation term
+// (ln2/2)^13/13! is below 2e-16), then an exact scaling by 2^j.
+// Arguments below -1100 (and NaN) give 0.  Every exponential whose error
+// reaches the threshold goes through this function: the hardware fp32
+// exponential is accurate to ~1e-7, which summed over ~1e5 near-threshold
+// terms could move the selected mass by more than 1e-3.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double exp2_nonpos(double y)
+{
+    y = fmax(y, -1100.0);          // fmax(NaN, c) = c
+    y = fmin(y, 0.0);
+    const double j = __builtin_rint(y);
+    const double t = (y - j) * kLn2;
+    double p = 2.08767569878681e-09;
+    p = fma(p, t, 2.505210838544172e-08);
+    p = fma(p, t, 2.755731922398589e-07);
+    p = fma(p, t, 2.7557319223985893e-06);
+    p = fma(p, t, 2.48015873015873e-05);
+    p = fma(p, t, 0.0001984126984126984);
+    p = fma(p, t, 0.001388888888888889);
+    p = fma(p, t, 0.008333333333333333);
+    p = fma(p, t, 0.041666666666666664);
+    p = fma(p, t, 0.16666666666666666);
+    p = fma(p, t, 0.5);
+    p = fma(p, t, 1.0);
+    p = fma(p, t, 1.0);
+    return ldexp(p, (int)j);
+}
+
+// e^(x/alpha) for x <= 0 given inv = log2(e)/alpha.
+__device__ __forceinline__ double exp_scaled_nonpos(double x, double log2e_over_alpha)
+{
+    return exp2_nonpos(x * log2e_over_alpha);
+}
+
+// ---------------------------------------------------------------------------
+// Order-preserving map fp32 -> u32 (after folding -0 into +0, so the band
+// test a_L <= v and the key order agree).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t float_to_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t k)
+{
+    const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ bool is_nonfinite(float v)
+{
+    return (__float_as_uint(v) & 0x7f800000u) == 0x7f800000u;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11): ten rounds of two 32x32->64 multiplies with the
+// published multipliers and Weyl key increments.
+// ---------------------------------------------------------------------------
+struct Philox4 {
+    uint32_t v[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t lo0 = 0xD2511F53u * c0;
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c0);
+        const uint32_t lo1 = 0xCD9E8D57u * c2;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2);
+        const uint32_t n0 = hi1 ^ c1 ^ k0;
+        const uint32_t n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    Philox4 out;
+    out.v[0] = c0;
+    out.v[1] = c1;
+    out.v[2] = c2;
+    out.v[3] = c3;
+    return out;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-64 reductions (every lane receives the result; butterfly order is
+// fixed, so results are bitwise reproducible).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_min(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v = fminf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of active lanes below this one in `mask`.
+__device__ __forceinline__ uint32_t rank_in_mask(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// ---------------------------------------------------------------------------
+// Ascending bitonic sort of npow2 u32 keys in LDS by the whole work-group.
+// npow2 must be a power of two; the caller pads with 0xFFFFFFFF.
+// ---------------------------------------------------------------------------
+__device__ inline void lds_bitonic_sort(uint32_t* a, int npow2)
+{
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    for (int k = 2; k <= npow2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < npow2; i += nt) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint32_t x = a[i];
+                    const uint32_t y = a[ixj];
+                    const bool up = (i & k) == 0;
+                    if ((x > y) == up) {
+                        a[i] = y;
+                        a[ixj] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Release/acquire around "last work-group finishes the reduction" tickets.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void fence_agent() { __threadfence(); }
+
+}  // namespace stk

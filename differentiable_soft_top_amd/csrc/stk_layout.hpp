@@ -1,0 +1,230 @@
+// stk_layout.hpp -- device status block, per-work-group partials, workspace
+// plan and the host launchers of every kernel of the soft top-k path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace stk {
+
+// ---- fixed launch shapes -------------------------------------------------
+constexpr int kStreamThreads = 256;      // streaming kernels (pass-1, emit, VJP)
+constexpr int kStreamMaxBlocks = 2048;   // 8 work-groups per CU on 256 CUs
+constexpr int kSelectThreads = 1024;     // bracket select, segment solve
+constexpr int kPilot = 2048;             // pilot sample size of the select step
+constexpr int kCandCap = 16384;          // candidate keys held in LDS by the select step
+constexpr int kStageCap = 4096;          // band elements staged in LDS per pass-1 work-group
+constexpr int kBuckets = 2048;           // value buckets of the band sort
+constexpr int kBucketCap = 8192;         // largest bucket sorted in LDS
+constexpr int kBandChunk = 32768;        // band elements per work-group in histogram/scatter
+constexpr int kSortThreads = 256;        // threads of bucket-sort / tile work-groups
+constexpr int kTile = 4096;              // sorted elements per group in the full-sort solve
+constexpr int kRadixThreads = 256;
+constexpr int kRadixKeysPerThread = 32;
+constexpr int kRadixTile = kRadixThreads * kRadixKeysPerThread;  // 8192 keys
+constexpr int kRadixBins = 256;
+
+// ---- solve status codes (Status::solve_state) ----------------------------
+enum SolveState : uint32_t {
+    kSolveNotRun = 0,
+    kSolveOk = 1,
+    kSolveRejectLow = 2,       // M(a_L) < k: b below the bracket
+    kSolveRejectHigh = 3,      // M(a_R) > k: b at/above the bracket
+    kSolveOverflow = 4,        // band did not fit its buffer
+    kSolveNonfinite = 5,
+    kSolveBucketOverflow = 6,  // a band bucket exceeded the LDS sort capacity
+};
+
+// Device status block at workspace offset 0.  Every field is written by a
+// kernel; the host reads the whole block back once per forward round.
+struct alignas(16) Status {
+    // bracket (select step)
+    float aL, aR;
+    uint32_t select_info;        // bit0 pilot candidate overflow, bit1 rank below pilot, bit2 above
+    uint32_t cand_count;
+    // pass-1 totals
+    double SL, SR;               // sum_{s<a_L} e^{(s-a_L)/alpha}, sum_{s>=a_R} e^{-(s-a_R)/alpha}
+    uint64_t nL, nR;             // tail counts
+    uint64_t nB;                 // band count (global append cursor during pass-1)
+    float bmin, bmax;            // range of the band values
+    float smin, smax;            // range of all scores
+    uint32_t nonfinite;
+    uint32_t pad1;
+    // segment solve
+    double b;
+    double massL, massR;         // M(a_L), M(a_R)
+    uint32_t solve_state;
+    uint32_t pad2;
+    // certification pass (emit)
+    double mass;                 // fp64 sum of p over all n
+    uint32_t emit_done;
+    uint32_t pad3;
+    // "last work-group" tickets; zeroed by the first kernel of each forward
+    // and returned to zero by the work-group that consumes them
+    uint32_t ticket_pass1;
+    uint32_t ticket_hist;
+    uint32_t ticket_emit;
+    uint32_t ticket_radix;
+    uint32_t ticket_tile;
+    uint32_t pad4[3];
+};
+static_assert(sizeof(Status) <= 256, "status block must fit 256 bytes");
+
+struct alignas(16) Pass1Partial {
+    double SL, SR;
+    uint64_t nL, nR;
+    float bmin, bmax, smin, smax;
+    uint32_t nonfinite;
+    uint32_t pad[3];
+};
+
+// Summary of one sorted group (a band bucket or a tile of the full sort):
+// count, first and last value, start offset in the sorted array,
+// TA = sum e^{(x - hi)/alpha}, TB = sum e^{-(x - lo)/alpha}.
+struct alignas(16) GroupAgg {
+    double TA, TB;
+    float lo, hi;
+    uint32_t cnt;
+    uint32_t start;
+};
+
+// Per-group scan results of the segment solve: prefix sum anchored at the
+// group's last value (Pv), suffix of everything after the group anchored at
+// its first point (Sx, Sv; Sx = +inf when empty) and the count of scores
+// after the group (Cafter).
+struct alignas(16) GroupScan {
+    double Pv;
+    double Sx;
+    double Sv;
+    uint64_t Cafter;
+};
+
+// ---- workspace plan --------------------------------------------------------
+struct Plan {
+    int64_t n;
+    int32_t m;                   // samples
+    int64_t cap;                 // band capacity
+    int32_t g_stream;            // work-groups of the streaming kernels
+    int32_t g_band;              // max work-groups of band histogram/scatter
+    int32_t n_tiles;             // groups of the full-sort solve
+    int32_t g_radix;             // radix tiles
+    size_t off_status, off_samples, off_p1part, off_band, off_band_sorted;
+    size_t off_hist, off_bstart, off_agg, off_scan, off_emitpart, off_keys0, off_keys1, off_rhist;
+    size_t total;
+};
+
+Plan make_plan(int64_t n, int32_t m, int64_t cap);
+
+// ---- host launchers (each enqueues on `stream`, returns the launch status) --
+hipError_t launch_sample(const float* s, int64_t n, float alpha, uint64_t seed, int32_t m,
+                         float* out_samples, Status* st, hipStream_t stream);
+
+struct SelectArgs {
+    const float* samples;
+    int32_t m;
+    int64_t r_left, r_right;      // 1-based target ranks (0 = -inf, m+1 = +inf)
+    int32_t pilot_lo, pilot_hi;   // 1-based pilot ranks bounding the targets (0 / P+1 = open)
+    Status* st;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+struct Pass1Args {
+    const float* s;
+    int64_t n;
+    double log2e_over_alpha;
+    float* band;
+    int64_t cap;
+    Pass1Partial* partials;
+    int32_t blocks;
+    Status* st;
+};
+hipError_t launch_pass1(const Pass1Args& a, hipStream_t stream);
+hipError_t launch_pass1_finalize(const Pass1Partial* partials, int blocks, Status* st, hipStream_t stream);
+
+struct BandArgs {
+    const Pass1Partial* p1;       // pass-1 partials (band range when the bracket is open-ended)
+    int32_t p1_blocks;
+    const float* band;
+    float* band_sorted;
+    int64_t cap;
+    uint32_t* hist;               // [g_band][kBuckets]
+    uint32_t* bstart;             // [kBuckets + 1]
+    GroupAgg* agg;                // [kBuckets]
+    int32_t blocks;               // g_band
+    double log2e_over_alpha;
+    Status* st;
+};
+hipError_t launch_band_sort(const BandArgs& a, hipStream_t stream);
+
+struct SolveArgs {
+    const Pass1Partial* p1;       // pass-1 partials (tails of the bracketed route)
+    int32_t p1_blocks;
+    const float* sorted;          // sorted values
+    const GroupAgg* agg;
+    GroupScan* scan;              // scratch [groups]
+    int32_t groups;
+    int32_t tails;                // 1: bracketed (tails from status), 0: full sort (no tails)
+    int64_t cap;                  // band capacity (bracketed route)
+    double k;
+    double alpha;
+    double log2e_over_alpha;
+    double* out_b;
+    Status* st;
+};
+hipError_t launch_solve(const SolveArgs& a, hipStream_t stream);
+
+struct RadixArgs {
+    const float* s;
+    int64_t n;
+    uint32_t* keys0;
+    uint32_t* keys1;
+    uint32_t* hist;               // [kRadixBins][g_radix]
+    int32_t g_radix;
+    uint32_t key_min;             // subtracted from every key
+    int32_t passes;               // 8-bit digits to sort
+    Status* st;
+    uint32_t** sorted_out;        // receives keys0 or keys1 (host side)
+};
+hipError_t launch_radix_sort(const RadixArgs& a, hipStream_t stream);
+
+struct TileArgs {
+    uint32_t* keys;               // sorted keys (offset by key_min); overwritten with fp32 values
+    int64_t n;
+    uint32_t key_min;
+    GroupAgg* agg;
+    int32_t n_tiles;
+    double log2e_over_alpha;
+};
+hipError_t launch_tile_aggregates(const TileArgs& a, hipStream_t stream);
+
+struct EmitArgs {
+    const float* s;
+    int64_t n;
+    double alpha;
+    double log2e_over_alpha;
+    const double* b;
+    float* p;
+    double* partials;
+    int32_t blocks;
+    Status* st;
+};
+hipError_t launch_emit(const EmitArgs& a, hipStream_t stream);
+
+struct VjpArgs {
+    const float* g;
+    const float* s;
+    int64_t n;
+    double alpha;
+    double log2e_over_alpha;
+    const double* b;
+    float* grad;
+    double* partials;             // [reduce_blocks][2]
+    int32_t blocks;               // work-groups of the gradient kernel
+    int32_t reduce_blocks;        // work-groups of the (D, G) reduction
+};
+hipError_t launch_vjp(const VjpArgs& a, hipStream_t stream);
+
+hipError_t launch_reset_status(Status* st, hipStream_t stream, bool open_bracket);
+
+}  // namespace stk

@@ -1,0 +1,200 @@
+/*
+ * soft_topk.h -- C ABI of the MI355X (gfx950) LapSum soft top-k library.
+ *
+ * The operator (gist.science technical summary of "Fast LapSum: Exact
+ * Differentiable Top-k at Million Scale", section 2.1 "The LapSum Operator"):
+ *
+ *     p_i = F((s_i - b) / alpha),   F = standard Laplace CDF,
+ *     b   = the unique threshold with  sum_i p_i = k   (0 < k < n, alpha > 0),
+ *
+ * and its implicit-function vector-Jacobian product (same section: the
+ * backward pass is analytic):
+ *
+ *     d_i = exp(-|s_i - b| / alpha) / 2,   D = sum_i d_i,   G = sum_i g_i d_i,
+ *     grad_i = (d_i / alpha) * (g_i - G / D).
+ *
+ * The forward localises b by probabilistic bracketing (aiqbench.com abstract
+ * of Fast LapSum; gist.science summary section 2.2 "Probabilistic
+ * Bracketing", steps 1-4): a Philox sample of kernel-noised scores gives a
+ * binomial order-statistic bracket [a_L, a_R); one streaming pass folds the
+ * scores outside it into tail counts and exponential sums and keeps the band
+ * inside it; the band alone is sorted and solved in closed form (section 2.2
+ * "Full-Sort Solver"); the bracket is certified exactly, widened when the
+ * certificate fails, and a full device radix sort covers the worst case.
+ * The returned b is the exact root (up to fp64 rounding) whichever route is
+ * taken.
+ *
+ * Conventions shared by every entry point:
+ *  - Array pointers (scores, grad_p, out_p, grad_s, b, workspace) are DEVICE
+ *    pointers owned by the caller.  The library never allocates device memory.
+ *  - scores / p / gradients are fp32, contiguous, length n.  b is fp64.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every kernel is enqueued on it.
+ *  - Return value: 0 on success, else one of the SOFT_TOPK_E* codes below.
+ *    Arguments are validated on the host before anything is enqueued; on
+ *    SOFT_TOPK_EINVAL nothing is launched and the outputs are untouched.
+ *  - Limits: 1 <= n <= 2^31 - 1.
+ *  - Calls on different streams need distinct workspaces; the library keeps
+ *    no other state apart from one small pinned host buffer per host thread.
+ */
+#ifndef SOFT_TOPK_H
+#define SOFT_TOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SOFT_TOPK_OK 0
+#define SOFT_TOPK_EINVAL 1     /* bad n, k, alpha, pointer, or params      */
+#define SOFT_TOPK_ENONFINITE 2 /* a score is NaN or +-Inf                  */
+#define SOFT_TOPK_EWORKSPACE 3 /* workspace NULL or smaller than required  */
+#define SOFT_TOPK_EHIP 4       /* a HIP runtime call failed                */
+#define SOFT_TOPK_ESOLVE 5     /* every route failed its certificate       */
+
+/* Route the forward took (soft_topk_stats.path). */
+#define SOFT_TOPK_PATH_BRACKET 1  /* bracket certified on the first pass    */
+#define SOFT_TOPK_PATH_WIDENED 2  /* certified after widening the bracket   */
+#define SOFT_TOPK_PATH_FULLSORT 3 /* full device radix sort of all scores   */
+
+/* Why a bracketed round was rejected (soft_topk_stats.reject_mask bits). */
+#define SOFT_TOPK_REJECT_LOW 1       /* certificate: b lies below a_L        */
+#define SOFT_TOPK_REJECT_HIGH 2      /* certificate: b lies at/above a_R     */
+#define SOFT_TOPK_REJECT_OVERFLOW 4  /* band larger than its capacity        */
+#define SOFT_TOPK_REJECT_BUCKET 8    /* a band bucket too large to sort      */
+#define SOFT_TOPK_REJECT_MASS 16     /* post-solve mass check out of bounds  */
+
+/*
+ * Tuning and test knobs of the forward.  Pass NULL for the defaults, or fill
+ * with soft_topk_default_params() and change fields.  These do not change
+ * the result, only the route and its cost (the route-independence of b is
+ * what the certificate guarantees).
+ */
+typedef struct soft_topk_params {
+    uint64_t seed;          /* Philox key for the sampler (default 0x5eed)           */
+    int32_t samples;        /* sample size m, 1024..262144 (default 65536)            */
+    double z;               /* bracket half-width in binomial standard deviations;
+                               ranks use exact binomial tails at Phi(-z) (default 5) */
+    int64_t band_capacity;  /* max band elements (0 = default: clamp(n/4, 2^16, 2^22)) */
+    int32_t max_widen;      /* bracket widenings before the full sort (default 2)     */
+    int32_t force_path;     /* 0 auto, 3 = go straight to the full sort               */
+    double mass_tolerance;  /* post-solve |sum p - k| bound; <=0 = default
+                               (1e-3 + 1e-12 * n)                                    */
+} soft_topk_params;
+
+/* Host-side record of one forward call (all fields written on success). */
+typedef struct soft_topk_stats {
+    int32_t path;           /* SOFT_TOPK_PATH_*                                       */
+    int32_t rounds;         /* bracketed rounds run (0 when forced to full sort)      */
+    int32_t reject_mask;    /* OR of SOFT_TOPK_REJECT_* over rejected rounds          */
+    int32_t reserved;
+    float a_left, a_right;  /* bracket of the last bracketed round                    */
+    int64_t n_left, n_band, n_right; /* scores below / inside / at-or-above it        */
+    double mass_at_left;    /* M(a_L) of the last bracketed round                     */
+    double mass_at_right;   /* M(a_R) of the last bracketed round                     */
+    double b;               /* the threshold (also written to out_b on the device)    */
+    double mass;            /* fp64 sum of the emitted p (the certification pass)     */
+} soft_topk_stats;
+
+/* Fill *params with the defaults listed above. */
+void soft_topk_default_params(soft_topk_params* params);
+
+/*
+ * Bytes of device workspace soft_topk_forward / soft_topk_forward_ex need for
+ * n scores (params may be NULL).  Includes the full-sort buffers (two u32
+ * arrays of n) so every route fits.  Returns 0 if n is out of range.
+ */
+size_t soft_topk_workspace_bytes(int64_t n, const soft_topk_params* params);
+
+/* Bytes of device workspace soft_topk_backward needs for n scores. */
+size_t soft_topk_backward_workspace_bytes(int64_t n);
+
+/*
+ * Forward.  scores: fp32[n] (device).  k: budget, 0 < k < n (real values
+ * allowed).  alpha: temperature > 0, finite.  out_p: fp32[n] (device),
+ * out_p[i] = F((scores[i] - b)/alpha).  out_b: one fp64 (device) receiving b.
+ * workspace: soft_topk_workspace_bytes(n, NULL) bytes of device memory, any
+ * contents, 256-byte aligned.
+ * Synchronisation: enqueues on `stream`, then waits for that stream once (a
+ * ~100-byte status read-back) to certify the result before returning; on
+ * SOFT_TOPK_OK, out_p and out_b are final once the call returns.
+ * Errors: EINVAL / EWORKSPACE before any launch; ENONFINITE if a score is not
+ * finite (out_p / out_b then hold no result); EHIP with the HIP status kept
+ * for soft_topk_last_hip_error(); ESOLVE should not happen (every route ends
+ * in the full sort, whose solve is exact).
+ */
+int soft_topk_forward(const float* scores, int64_t n, double k, double alpha,
+                      float* out_p, double* out_b,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward with explicit params (NULL = defaults) and a host stats record
+ * (NULL = not wanted).  Same contract as soft_topk_forward. */
+int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
+                         float* out_p, double* out_b,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         const soft_topk_params* params, soft_topk_stats* stats);
+
+/*
+ * Backward (vector-Jacobian product).  grad_p: fp32[n] upstream gradient
+ * (device).  scores: the forward's fp32[n].  alpha: the forward's alpha.
+ * b: device pointer to the forward's fp64 threshold.  grad_s: fp32[n]
+ * (device) receiving (d_i/alpha)(g_i - G/D).  workspace:
+ * soft_topk_backward_workspace_bytes(n) bytes of device memory, any contents.
+ * Fully asynchronous on `stream` (no host synchronisation).
+ * Errors: EINVAL / EWORKSPACE before any launch; EHIP on a launch failure.
+ */
+int soft_topk_backward(const float* grad_p, const float* scores, int64_t n,
+                       double alpha, const double* b, float* grad_s,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text for a return code. */
+const char* soft_topk_strerror(int code);
+
+/* The HIP status (hipError_t as int) behind the last EHIP on this thread. */
+int soft_topk_last_hip_error(void);
+
+/*
+ * Host rank arithmetic of the bracket (exposed for tests; no GPU needed).
+ * For m samples of a law whose target quantile is q = 1 - k/n, returns the
+ * 1-based ranks r_left < r_right such that the order statistics Y_(r_left) and
+ * Y_(r_right) bracket the q-quantile except with probability
+ * Phi(-z) on each side under the Binomial(m, q) law of the count of samples at
+ * or below it.  r_left = 0 means -inf, r_right = m + 1 means +inf.
+ */
+int soft_topk_bracket_ranks(int64_t m, double q, double z,
+                            int64_t* r_left, int64_t* r_right);
+
+/*
+ * Diagnostic: run only the sampler on `scores` and write the m kernel-noised
+ * samples Y_j = s[I_j] + alpha * E_j (fp32, device) to out_samples, where
+ * (I_j, E_j) come from Philox4x32-10 with counter (j, 0, 0, 0) and key
+ * (seed low word, seed high word): I_j = floor(((hi32 << 32 | lo32) * n) / 2^64)
+ * from output words 0 (lo32) and 1 (hi32), E_j the Laplace(0,1) inverse CDF
+ * of u = (word2 + 0.5) / 2^32.  Asynchronous on `stream`.
+ */
+int soft_topk_debug_sample(const float* scores, int64_t n, double alpha,
+                           uint64_t seed, int32_t m, float* out_samples,
+                           void* stream);
+
+/*
+ * Diagnostic kernel timing.  soft_topk_profile_begin(mask) makes the library
+ * record a HIP event pair on the launch stream around every later launch of
+ * each kernel whose bit is set in `mask` (bit i = kernel id i, names from
+ * soft_topk_profile_kernel_name); soft_topk_profile_end waits for those
+ * events and writes, per kernel id, the summed milliseconds and the launch
+ * count into caller arrays of soft_topk_profile_kernel_count() entries
+ * (either may be NULL), then stops recording.  Process-wide; not meant for
+ * concurrent use from several threads.
+ */
+int soft_topk_profile_kernel_count(void);
+const char* soft_topk_profile_kernel_name(int id);
+int soft_topk_profile_begin(uint32_t kernel_mask);
+int soft_topk_profile_end(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOFT_TOPK_H */

@@ -15,7 +15,7 @@
  *   b      = the unique root of M(b) = k,  0 < k < n, alpha > 0
  *   p_i    = F((s_i - b)/alpha)
  *   VJP    : d_i = exp(-|s_i - b|/alpha)/2, D = sum d, G = sum g_i d_i,
- *            grad_i = (d_i/alpha) (g_i - G/D)
+ *            grad_i = (d_i/alpha) (g_i - G/D)   (G/D taken in scale-free form)
  *            (implicit differentiation of M(b) = k; section 2.1 states the
  *            backward pass is analytic.)
  *
@@ -202,6 +202,10 @@ int oracle_forward(const double* s, int64_t n, double k, double alpha,
  * Differentiating sum_j F((s_j - b)/alpha) = k gives db/ds_l = d_l / D, so
  * dp_i/ds_l = (d_i/alpha)(delta_il - d_l/D) and
  * grad_l = sum_i g_i dp_i/ds_l = (d_l/alpha)(g_l - G/D).
+ * G/D is a weighted mean of g with weights d_i; the common factor
+ * exp(-delta/alpha), delta = min_i |s_i - b|, cancels from it, so it is taken
+ * with weights w_i = exp(-(|s_i - b| - delta)/alpha) <= 1 (at least one equals
+ * 1), which stays finite when every d_i underflows.
  */
 int oracle_backward(const double* g, const double* s, int64_t n, double alpha,
                     double b, double* grad_out)
@@ -210,13 +214,17 @@ int oracle_backward(const double* g, const double* s, int64_t n, double alpha,
         return ORACLE_EINVAL;
     if (!(alpha > 0.0) || !isfinite(alpha) || !isfinite(b))
         return ORACLE_EINVAL;
-    double D = 0.0, G = 0.0;
+    double delta = fabs(s[0] - b);
+    for (int64_t i = 1; i < n; ++i)
+        if (fabs(s[i] - b) < delta)
+            delta = fabs(s[i] - b);
+    double W = 0.0, GW = 0.0;
     for (int64_t i = 0; i < n; ++i) {
-        double d = 0.5 * exp(-fabs(s[i] - b) / alpha);
-        D += d;
-        G += g[i] * d;
+        double w = exp(-(fabs(s[i] - b) - delta) / alpha);
+        W += w;
+        GW += g[i] * w;
     }
-    double ratio = G / D;
+    double ratio = GW / W;
     for (int64_t i = 0; i < n; ++i) {
         double d = 0.5 * exp(-fabs(s[i] - b) / alpha);
         grad_out[i] = (d / alpha) * (g[i] - ratio);

@@ -281,6 +281,25 @@ def pin_vjp(orc):
             np.linalg.norm(u) * np.linalg.norm(gv) + 1e-300)
 
 
+def pin_vjp_underflow(orc):
+    """When alpha is so small that every d_i underflows, the VJP is 0 (not
+    0/0); with partial underflow it still equals the definition's G/D form."""
+    for s, k, alpha in [(np.array([0.0, 1.0]), 1.0, 1e-4), (np.array([0.0, 1.0, 3.0, 7.0]), 2.0, 1e-5)]:
+        _, b = orc.forward(s, k, alpha)
+        g = np.arange(1.0, s.size + 1.0)
+        gr = orc.backward(g, s, alpha, b)
+        assert np.all(np.isfinite(gr)) and np.all(gr == 0.0), gr
+    rng = np.random.default_rng(17)
+    s = rng.normal(size=40)
+    g = rng.normal(size=40)
+    alpha = 0.01
+    _, b = orc.forward(s, 10.0, alpha)
+    d = 0.5 * np.exp(-np.abs(s - b) / alpha)
+    naive = (d / alpha) * (g - np.sum(g * d) / np.sum(d))
+    gr = orc.backward(g, s, alpha, b)
+    assert np.max(np.abs(gr - naive)) <= 1e-9 * np.max(np.abs(naive))
+
+
 ALL_PINS = [
     pin_bisection,
     pin_two_point_midpoint,
@@ -292,4 +311,5 @@ ALL_PINS = [
     pin_mass_and_order,
     pin_invariances,
     pin_vjp,
+    pin_vjp_underflow,
 ]

@@ -1,0 +1,378 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars (for fp32 inputs): |b_gpu - b_ref| <= 1e-5 * alpha, max|p_gpu - p_ref| <=
+1e-5, |sum p - k| <= 1e-3, backward rel-L2 <= 1e-4.  "sum p" is measured two
+ways: M_p, the fp64 sum of the GPU's fp32 p, and M_b, the oracle's fp64 mass
+at the GPU's b.  M_b carries the 1e-3 bar everywhere; M_p carries it on top of
+the oracle's own fp32-rounding floor (the fp64 sum of the oracle's p rounded
+to fp32), which on the clustered workload alone exceeds 1e-3.
+
+Small cases are compared element by element; the full-size workloads (the
+sizes the benchmark times, same launch configuration) on sampled indices
+against the oracle's threshold stored in tests/golden/thresholds.json plus
+properties that hold at any size.
+"""
+import hashlib
+import json
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import differentiable_soft_top_amd as stk  # noqa: E402
+from differentiable_soft_top_amd import _lib  # noqa: E402
+from differentiable_soft_top_amd.workloads import draw_grad, draw_scores, make_workload  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+with open(os.path.join(HERE, "golden", "thresholds.json")) as _f:
+    GOLD = json.load(_f)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    return torch.device("cuda:0")
+
+
+def params(**kw):
+    p = stk.default_params()
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def run(dev, s_np, k, alpha, g_np=None, prm=None):
+    s = torch.from_numpy(s_np).to(dev)
+    p, b, st = stk.forward(s, k, alpha, prm, want_stats=True)
+    out = {"p": p.cpu().numpy().astype(np.float64), "b": float(b.item()), "stats": st}
+    if g_np is not None:
+        g = torch.from_numpy(g_np).to(dev)
+        out["grad"] = stk.backward(g, s, alpha, b).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_full(res, s_np, k, alpha, g_np=None, mass_floor=0.0):
+    p_ref, b_ref = O.forward(s_np, k, alpha)
+    b = res["b"]
+    assert abs(b - b_ref) <= 1e-5 * alpha, (b, b_ref, (b - b_ref) / alpha)
+    assert np.max(np.abs(res["p"] - p_ref)) <= 1e-5
+    m_b = O.mass(s_np, b, alpha)
+    assert abs(m_b - k) <= 1e-3, m_b - k
+    floor = abs(float(np.sum(p_ref.astype(np.float32).astype(np.float64))) - k)
+    assert abs(float(np.sum(res["p"])) - k) <= 1e-3 + max(floor, mass_floor)
+    if g_np is not None:
+        grad_ref = O.backward(g_np, s_np, alpha, b_ref)
+        err = np.linalg.norm(res["grad"] - grad_ref)
+        ref = np.linalg.norm(grad_ref)
+        # n = 1, or every d_i below the fp32 range: the gradient is 0
+        assert np.all(np.isfinite(res["grad"]))
+        assert err <= 1e-4 * ref or err <= 1e-30, (err, ref)
+    return b_ref
+
+
+# --------------------------------------------------------------------------
+# element-by-element parity at sizes the oracle finishes in seconds; every
+# size spans several pass-1 work-groups and band buckets and ends ragged
+# --------------------------------------------------------------------------
+SMALL = [
+    ("c1", None),            # the 4096-score workload itself
+    ("c2", 100_003),
+    ("c3", 200_001),
+    ("c4", 300_007),
+    ("c2", 1_000_000),
+    ("c3", 1_000_001),
+]
+
+
+@pytest.mark.parametrize("name,n", SMALL, ids=["%s-%s" % (a, b) for a, b in SMALL])
+def test_small_parity(dev, name, n):
+    s_np, k, alpha, w = make_workload(name, n=n)
+    g_np = draw_grad(s_np.size, w.seed)
+    res = run(dev, s_np, k, alpha, g_np)
+    check_full(res, s_np, k, alpha, g_np)
+    assert res["stats"]["path"] == _lib.PATH_BRACKET, res["stats"]
+
+
+def test_clustered_small(dev):
+    """60% of the scores tied exactly at the threshold.  At this size the tied
+    band still fits its buffer and lands in one all-equal bucket, so the
+    certified route handles it; with a small band capacity the same input
+    takes the full sort.  Both must match the oracle."""
+    s_np, k, alpha, w = make_workload("c5", n=100_000)
+    g_np = draw_grad(s_np.size, w.seed)
+    res = run(dev, s_np, k, alpha, g_np)
+    check_full(res, s_np, k, alpha, g_np)
+    assert res["stats"]["path"] == _lib.PATH_BRACKET, res["stats"]
+    res = run(dev, s_np, k, alpha, g_np, params(band_capacity=1000))
+    check_full(res, s_np, k, alpha, g_np)
+    assert res["stats"]["path"] == _lib.PATH_FULLSORT, res["stats"]
+    assert res["stats"]["reject_mask"] & _lib.REJECT_OVERFLOW
+
+
+@pytest.mark.parametrize("name,n", [("c1", None), ("c2", 100_003), ("c4", 300_007), ("c3", 65_537)])
+def test_forced_full_sort_matches(dev, name, n):
+    s_np, k, alpha, w = make_workload(name, n=n)
+    g_np = draw_grad(s_np.size, w.seed)
+    res = run(dev, s_np, k, alpha, g_np, params(force_path=_lib.PATH_FULLSORT))
+    assert res["stats"]["path"] == _lib.PATH_FULLSORT
+    check_full(res, s_np, k, alpha, g_np)
+
+
+def test_route_independence(dev):
+    """Different Philox seeds, a too-narrow bracket (forcing rejections and
+    widening), an overfull band and the forced full sort all give the same b."""
+    s_np, k, alpha, _ = make_workload("c2", n=200_000)
+    _, b_ref = O.forward(s_np, k, alpha)
+    bs = {}
+    for tag, prm in [("seed1", params(seed=1)), ("seed2", params(seed=0xABCDEF)),
+                     ("narrow", params(z=0.05, max_widen=4)),
+                     ("overflow", params(band_capacity=16)),
+                     ("full", params(force_path=_lib.PATH_FULLSORT))]:
+        res = run(dev, s_np, k, alpha, None, prm)
+        bs[tag] = (res["b"], res["stats"])
+        assert abs(res["b"] - b_ref) <= 1e-5 * alpha, (tag, res["b"], b_ref)
+    assert bs["overflow"][1]["path"] == _lib.PATH_FULLSORT
+    assert bs["overflow"][1]["reject_mask"] & _lib.REJECT_OVERFLOW
+    assert bs["full"][1]["path"] == _lib.PATH_FULLSORT
+
+
+def test_narrow_bracket_widens(dev):
+    """With z tiny, the first bracket usually misses b; the certificate
+    rejects it and the widened bracket (or the full sort) still gives b."""
+    hits = 0
+    for seed in range(6):
+        s_np, k, alpha, _ = make_workload("c2", n=100_000, seed=seed)
+        res = run(dev, s_np, k, alpha, None, params(z=0.02, max_widen=6, seed=seed + 11))
+        _, b_ref = O.forward(s_np, k, alpha)
+        assert abs(res["b"] - b_ref) <= 1e-5 * alpha
+        st = res["stats"]
+        if st["reject_mask"] & (_lib.REJECT_LOW | _lib.REJECT_HIGH):
+            hits += 1
+            assert st["path"] in (_lib.PATH_WIDENED, _lib.PATH_FULLSORT)
+            assert st["rounds"] >= 2 or st["path"] == _lib.PATH_FULLSORT
+    assert hits >= 1
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+EDGE = [
+    ("n1_klow", np.array([0.7], np.float32), 0.3, 1.0),
+    ("n1_khigh", np.array([-2.0], np.float32), 0.9, 0.5),
+    ("n2_mid", np.array([1.0, 3.0], np.float32), 1.0, 0.25),
+    ("n3", np.array([0.0, 1.0, 2.0], np.float32), 1.5, 1.0),
+    ("n5_ragged", np.array([5.0, -1.0, 2.5, 2.5, 0.0], np.float32), 2.2, 0.3),
+    ("n7_ties", np.array([1, 1, 1, 2, 2, 3, 3], np.float32), 3.0, 0.01),
+    ("zeros_signed", np.array([0.0, -0.0, 0.0, -0.0, 1.0, -1.0], np.float32), 3.0, 0.5),
+]
+
+
+@pytest.mark.parametrize("tag,s_np,k,alpha", EDGE, ids=[e[0] for e in EDGE])
+def test_tiny_inputs(dev, tag, s_np, k, alpha):
+    g_np = np.linspace(-1, 1, s_np.size).astype(np.float32)
+    res = run(dev, s_np, k, alpha, g_np)
+    check_full(res, s_np, k, alpha, g_np)
+
+
+@pytest.mark.parametrize("case", ["equal", "sorted", "reversed", "k_tiny", "k_near_n", "alpha_huge",
+                                  "alpha_tiny", "negative", "bimodal", "k_half"])
+def test_structured_inputs(dev, case):
+    rng = np.random.default_rng(99)
+    n = 50_021
+    alpha = 0.05
+    if case == "equal":
+        s = np.full(n, 0.25, np.float32)
+        k = 1234.5
+    elif case == "sorted":
+        s = draw_scores("sorted_normal", n, 3)
+        k = 500.0
+    elif case == "reversed":
+        s = np.ascontiguousarray(draw_scores("sorted_normal", n, 4)[::-1])
+        k = 500.0
+    elif case == "k_tiny":
+        s = rng.standard_normal(n).astype(np.float32)
+        k = 1e-3
+    elif case == "k_near_n":
+        s = rng.standard_normal(n).astype(np.float32)
+        k = n - 1e-3
+    elif case == "alpha_huge":
+        s = rng.standard_normal(n).astype(np.float32)
+        k, alpha = 100.0, 1e3
+    elif case == "alpha_tiny":
+        s = rng.standard_normal(n).astype(np.float32)
+        k, alpha = 100.0, 1e-6
+    elif case == "negative":
+        s = (rng.standard_normal(n) - 50.0).astype(np.float32)
+        k = 2000.0
+    elif case == "bimodal":
+        s = np.concatenate([rng.normal(-3, 0.1, n // 2), rng.normal(3, 0.1, n - n // 2)]).astype(np.float32)
+        s = s[rng.permutation(n)]
+        k = n / 2
+    else:
+        s = rng.standard_normal(n).astype(np.float32)
+        k = n / 2
+    g = rng.standard_normal(n).astype(np.float32)
+    res = run(dev, s, k, alpha, g)
+    check_full(res, s, k, alpha, g)
+
+
+def test_unaligned_pointers(dev):
+    """Scores / outputs not 16-byte aligned take the scalar-load kernels."""
+    s_np, k, alpha, w = make_workload("c2", n=100_003)
+    g_np = draw_grad(s_np.size, w.seed)
+    base = torch.from_numpy(np.concatenate([[0.0], s_np]).astype(np.float32)).to(dev)
+    s = base[1:]
+    assert s.data_ptr() % 16 != 0
+    gbase = torch.from_numpy(np.concatenate([[0.0], g_np]).astype(np.float32)).to(dev)
+    g = gbase[1:]
+    p, b = stk.forward(s, k, alpha)
+    grad = stk.backward(g, s, alpha, b)
+    res = {"p": p.cpu().numpy().astype(np.float64), "b": float(b.item()),
+           "grad": grad.cpu().numpy().astype(np.float64)}
+    check_full(res, s_np, k, alpha, g_np)
+
+
+def test_nonfinite_is_rejected(dev):
+    s_np = np.random.default_rng(1).standard_normal(10_000).astype(np.float32)
+    for bad in (np.nan, np.inf, -np.inf):
+        t = s_np.copy()
+        t[1234] = bad
+        with pytest.raises(stk.SoftTopKError) as e:
+            stk.forward(torch.from_numpy(t).to(dev), 100.0, 0.1)
+        assert e.value.code == _lib.ENONFINITE
+        with pytest.raises(stk.SoftTopKError) as e:
+            stk.forward(torch.from_numpy(t).to(dev), 100.0, 0.1, params(force_path=_lib.PATH_FULLSORT))
+        assert e.value.code == _lib.ENONFINITE
+
+
+def test_invalid_arguments_raise(dev):
+    s = torch.zeros(10, device=dev)
+    for k, alpha in [(0.0, 1.0), (10.0, 1.0), (1.0, 0.0)]:
+        with pytest.raises(stk.SoftTopKError) as e:
+            stk.forward(s, k, alpha)
+        assert e.value.code == _lib.EINVAL
+
+
+def test_deterministic(dev):
+    s_np, k, alpha, _ = make_workload("c2", n=500_000)
+    s = torch.from_numpy(s_np).to(dev)
+    p1, b1 = stk.forward(s, k, alpha)
+    p2, b2 = stk.forward(s, k, alpha)
+    assert float(b1.item()) == float(b2.item())
+    assert torch.equal(p1, p2)
+
+
+def test_autograd_and_side_stream(dev):
+    s_np, k, alpha, w = make_workload("c1")
+    g_np = draw_grad(s_np.size, w.seed)
+    side = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(side):
+        s = torch.from_numpy(s_np).to(dev).requires_grad_(True)
+        p, b = stk.soft_topk(s, k, alpha)
+        (p * torch.from_numpy(g_np).to(dev)).sum().backward()
+    side.synchronize()
+    _, b_ref = O.forward(s_np, k, alpha)
+    grad_ref = O.backward(g_np, s_np, alpha, b_ref)
+    grad = s.grad.cpu().numpy().astype(np.float64)
+    assert np.linalg.norm(grad - grad_ref) / np.linalg.norm(grad_ref) <= 1e-4
+    assert abs(float(grad.sum())) <= 1e-3 * np.abs(grad).sum()
+
+
+# --------------------------------------------------------------------------
+# the sampler: device Philox draws against the published definition
+# --------------------------------------------------------------------------
+def _philox_ref(counter, key):
+    M0, M1, W0, W1 = 0xD2511F53, 0xCD9E8D57, 0x9E3779B9, 0xBB67AE85
+    c = list(counter)
+    k0, k1 = key
+    for _ in range(10):
+        p0 = M0 * c[0]
+        p1 = M1 * c[2]
+        c = [(p1 >> 32) ^ c[1] ^ k0, p1 & 0xFFFFFFFF, (p0 >> 32) ^ c[3] ^ k1, p0 & 0xFFFFFFFF]
+        k0 = (k0 + W0) & 0xFFFFFFFF
+        k1 = (k1 + W1) & 0xFFFFFFFF
+    return c
+
+
+def test_philox_reference_known_answers():
+    # Random123 known-answer vectors for Philox4x32-10
+    assert _philox_ref([0, 0, 0, 0], [0, 0]) == [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]
+    assert _philox_ref([0xFFFFFFFF] * 4, [0xFFFFFFFF] * 2) == [0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD]
+
+
+def test_sampler_matches_philox_definition(dev):
+    n = 123_457
+    s_np = np.random.default_rng(5).standard_normal(n).astype(np.float32)
+    alpha = 0.25
+    seed = 0x0123456789ABCDEF
+    m = 2048
+    s = torch.from_numpy(s_np).to(dev)
+    out = torch.empty(m, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    import ctypes
+    rc = lib.soft_topk_debug_sample(ctypes.c_void_p(s.data_ptr()), n, alpha, seed, m,
+                                    ctypes.c_void_p(out.data_ptr()),
+                                    ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    _lib.check(rc, "debug_sample")
+    y = out.cpu().numpy()
+    k0, k1 = seed & 0xFFFFFFFF, seed >> 32
+    for j in range(m):
+        w = _philox_ref([j, 0, 0, 0], [k0, k1])
+        idx = ((w[1] << 32 | w[0]) * n) >> 64
+        u = (w[2] + 0.5) / 2.0 ** 32
+        e = np.log(2 * u) if u < 0.5 else -np.log(2 * (1 - u))
+        ref = np.float32(float(s_np[idx]) + float(np.float32(alpha)) * e)
+        assert abs(float(y[j]) - float(ref)) <= 2 * abs(float(np.spacing(ref))), (j, y[j], ref)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, as the benchmark runs them
+# --------------------------------------------------------------------------
+def _sha(a):
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_full_size_workload(dev, name):
+    gold = GOLD[name]
+    s_np, k, alpha, w = make_workload(name)
+    g_np = draw_grad(s_np.size, w.seed)
+    assert _sha(s_np) == gold["sha256_scores"], "input generator drifted"
+    assert k == gold["k"]
+    s = torch.from_numpy(s_np).to(dev)
+    g = torch.from_numpy(g_np).to(dev)
+    p, b, st = stk.forward(s, k, alpha, want_stats=True)
+    grad = stk.backward(g, s, alpha, b)
+    torch.cuda.synchronize()
+    b_gpu = float(b.item())
+    b_ref = gold["b"]
+    assert abs(b_gpu - b_ref) <= 1e-5 * alpha, (b_gpu, b_ref, (b_gpu - b_ref) / alpha)
+    expect = _lib.PATH_FULLSORT if name == "c5" else _lib.PATH_BRACKET
+    assert st["path"] == expect, st
+
+    # sampled p and grad, one by one from the oracle's threshold and sums
+    rng = np.random.default_rng(1)
+    idx = np.concatenate([rng.integers(0, s_np.size, 200_000), np.argpartition(np.abs(s_np - b_ref), 5000)[:5000]])
+    p_np = p.cpu().numpy()
+    grad_np = grad.cpu().numpy()
+    x = (s_np[idx].astype(np.float64) - b_ref) / alpha
+    p_ref = O.laplace_cdf(x)
+    assert np.max(np.abs(p_np[idx] - p_ref)) <= 1e-5
+    d = 0.5 * np.exp(-np.abs(x))
+    grad_ref = (d / alpha) * (g_np[idx].astype(np.float64) - gold["G"] / gold["D"])
+    rel = np.linalg.norm(grad_np[idx] - grad_ref) / np.linalg.norm(grad_ref)
+    assert rel <= 1e-4, rel
+
+    # properties at full size
+    m_b = O.mass(s_np, b_gpu, alpha)
+    assert abs(m_b - k) <= 1e-3, m_b - k
+    m_p = float(np.sum(p_np.astype(np.float64)))
+    assert abs(m_p - k) <= 1e-3 + gold["mass_p32_rounding_floor"], m_p - k
+    assert abs(float(np.sum(grad_np.astype(np.float64)))) <= 1e-4 * float(np.sum(np.abs(grad_np)))
