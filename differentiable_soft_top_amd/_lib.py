@@ -25,6 +25,7 @@ class Params(ctypes.Structure):
         ("max_widen", ctypes.c_int32),
         ("force_path", ctypes.c_int32),
         ("mass_tolerance", ctypes.c_double),
+        ("verify_mass", ctypes.c_int32),
     ]
 
 

@@ -40,9 +40,18 @@ __device__ __forceinline__ bool band_unusable(const Status* st, int64_t cap)
     return st->nB > (uint64_t)cap;
 }
 
+// Elements per histogram/scatter work-group: at least kBandChunkMin, and
+// enough that at most kBandGroups work-groups share the band (the scatter
+// reads every group's histogram row).
+__device__ __forceinline__ uint64_t band_chunk(uint64_t nB)
+{
+    const uint64_t c = (nB + kBandGroups - 1) / kBandGroups;
+    return c < (uint64_t)kBandChunkMin ? (uint64_t)kBandChunkMin : c;
+}
+
 __device__ __forceinline__ int band_groups(uint64_t nB)
 {
-    return nB == 0 ? 1 : (int)((nB + kBandChunk - 1) / kBandChunk);
+    return nB == 0 ? 1 : (int)((nB + band_chunk(nB) - 1) / band_chunk(nB));
 }
 
 // Bucket range: the bracket itself when both ends are finite (the band lies
@@ -105,10 +114,24 @@ __global__ __launch_bounds__(kSortThreads) void band_hist_kernel(BandArgs a)
     for (int i = tid; i < kBuckets; i += kSortThreads)
         hist[i] = 0;
     __syncthreads();
-    const uint64_t e0 = (uint64_t)blockIdx.x * kBandChunk;
-    const uint64_t e1 = e0 + kBandChunk < nB ? e0 + kBandChunk : nB;
-    for (uint64_t i = e0 + tid; i < e1; i += kSortThreads)
-        atomicAdd(&hist[bucket_of(a.band[i], lo, scale)], 1u);
+    const uint64_t chunk = band_chunk(nB);
+    const uint64_t e0 = (uint64_t)blockIdx.x * chunk;
+    const uint64_t e1 = e0 + chunk < nB ? e0 + chunk : nB;
+    // eight loads in flight before the LDS atomics
+    for (uint64_t ib = e0; ib < e1; ib += 8 * kSortThreads) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint64_t i = ib + (uint64_t)j * kSortThreads + tid;
+            v[j] = i < e1 ? a.band[i] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint64_t i = ib + (uint64_t)j * kSortThreads + tid;
+            if (i < e1)
+                atomicAdd(&hist[bucket_of(v[j], lo, scale)], 1u);
+        }
+    }
     __syncthreads();
     uint32_t* row = a.hist + (size_t)blockIdx.x * kBuckets;
     for (int i = tid; i < kBuckets; i += kSortThreads)
@@ -122,7 +145,7 @@ __global__ __launch_bounds__(kSortThreads) void band_hist_kernel(BandArgs a)
 __global__ __launch_bounds__(kSortThreads) void band_scatter_kernel(BandArgs a)
 {
     constexpr int kPer = kBuckets / kSortThreads;  // buckets per thread
-    static_assert(kPer == 8, "two uint4 per thread");
+    static_assert(kPer == 2, "one uint2 per thread and row");
     __shared__ uint32_t cursor[kBuckets];
     __shared__ uint32_t scan_tmp[kSortThreads];
     const Status* st = a.st;
@@ -143,14 +166,20 @@ __global__ __launch_bounds__(kSortThreads) void band_scatter_kernel(BandArgs a)
         tot[j] = 0;
         before[j] = 0;
     }
-    for (int w = 0; w < used; ++w) {
-        const uint4* row = reinterpret_cast<const uint4*>(a.hist + (size_t)w * kBuckets + tid * kPer);
-        const uint4 x = row[0], y = row[1];
-        const uint32_t v[kPer] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+    // all rows' loads issued together (kBandGroups <= 128 rows)
+    static_assert(kBandGroups % 16 == 0, "row batches of 16");
+    for (int wb = 0; wb < used; wb += 16) {
+        uint2 x[16];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            tot[j] += v[j];
-            before[j] += w < me ? v[j] : 0u;
+        for (int u = 0; u < 16; ++u)
+            x[u] = wb + u < used ? *reinterpret_cast<const uint2*>(a.hist + (size_t)(wb + u) * kBuckets + tid * kPer)
+                                 : make_uint2(0u, 0u);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            tot[0] += x[u].x;
+            tot[1] += x[u].y;
+            before[0] += wb + u < me ? x[u].x : 0u;
+            before[1] += wb + u < me ? x[u].y : 0u;
         }
     }
     uint32_t local = 0;
@@ -177,16 +206,66 @@ __global__ __launch_bounds__(kSortThreads) void band_scatter_kernel(BandArgs a)
     if (me == 0 && tid == 0)
         a.bstart[kBuckets] = (uint32_t)nB;
     __syncthreads();
-    const uint64_t e0 = (uint64_t)me * kBandChunk;
-    const uint64_t e1 = e0 + kBandChunk < nB ? e0 + kBandChunk : nB;
-    for (uint64_t i = e0 + tid; i < e1; i += kSortThreads) {
-        const float v = a.band[i];
-        const uint32_t pos = atomicAdd(&cursor[bucket_of(v, lo, scale)], 1u);
-        a.band_sorted[pos] = v;
+    const uint64_t chunk = band_chunk(nB);
+    const uint64_t e0 = (uint64_t)me * chunk;
+    const uint64_t e1 = e0 + chunk < nB ? e0 + chunk : nB;
+    for (uint64_t ib = e0; ib < e1; ib += 8 * kSortThreads) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint64_t i = ib + (uint64_t)j * kSortThreads + tid;
+            v[j] = i < e1 ? a.band[i] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint64_t i = ib + (uint64_t)j * kSortThreads + tid;
+            if (i < e1) {
+                const uint32_t pos = atomicAdd(&cursor[bucket_of(v[j], lo, scale)], 1u);
+                a.band_sorted[pos] = v[j];
+            }
+        }
     }
 }
 
-// One work-group per bucket.
+// Fixed-order fold of pass-1 partials [i0, i1) by the first wave; lane 0
+// returns the result.
+__device__ Pass1Partial fold_partials_wave(const Pass1Partial* p, int i0, int i1)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    double SL = 0.0, SR = 0.0;
+    unsigned long long nL = 0, nR = 0;
+    uint32_t nf = 0;
+    float bmin = INFINITY, bmax = -INFINITY, smin = INFINITY, smax = -INFINITY;
+    for (int i = i0 + lane; i < i1; i += kWave) {
+        const Pass1Partial q = p[i];
+        SL += q.SL;
+        SR += q.SR;
+        nL += q.nL;
+        nR += q.nR;
+        nf |= q.nonfinite;
+        bmin = fminf(bmin, q.bmin);
+        bmax = fmaxf(bmax, q.bmax);
+        smin = fminf(smin, q.smin);
+        smax = fmaxf(smax, q.smax);
+    }
+    Pass1Partial r;
+    r.SL = wave_sum(SL);
+    r.SR = wave_sum(SR);
+    r.nL = wave_sum_u64(nL);
+    r.nR = wave_sum_u64(nR);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        nf |= __shfl_xor(nf, off, kWave);
+    r.nonfinite = nf;
+    r.bmin = wave_min(bmin);
+    r.bmax = wave_max(bmax);
+    r.smin = wave_min(smin);
+    r.smax = wave_max(smax);
+    return r;
+}
+
+// One work-group per bucket.  Each also folds its share of the pass-1
+// partials, so the single-work-group solve reads kBuckets of them.
 __global__ __launch_bounds__(kSortThreads) void bucket_sort_kernel(BandArgs a)
 {
     __shared__ uint32_t keys[kBucketCap];
@@ -199,6 +278,14 @@ __global__ __launch_bounds__(kSortThreads) void bucket_sort_kernel(BandArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
+    if (wave == 0) {
+        const int per = (a.p1_blocks + kBuckets - 1) / kBuckets;
+        const int i0 = b * per < a.p1_blocks ? b * per : a.p1_blocks;
+        const int i1 = i0 + per < a.p1_blocks ? i0 + per : a.p1_blocks;
+        const Pass1Partial r = fold_partials_wave(a.p1, i0, i1);
+        if (lane == 0)
+            a.p1_super[b] = r;
+    }
     const uint32_t start = a.bstart[b];
     const uint32_t end = a.bstart[b + 1];
     const uint32_t cnt = end - start;
@@ -222,8 +309,13 @@ __global__ __launch_bounds__(kSortThreads) void bucket_sort_kernel(BandArgs a)
         int n2 = 64;
         while ((uint32_t)n2 < cnt)
             n2 <<= 1;
-        for (int i = tid; i < n2; i += kSortThreads)
-            keys[i] = (uint32_t)i < cnt ? float_to_key(a.band_sorted[start + i]) : 0xFFFFFFFFu;
+        constexpr int kPerT = kBucketCap / kSortThreads;  // 32
+#pragma unroll
+        for (int j = 0; j < kPerT; ++j) {
+            const int i = j * kSortThreads + tid;
+            if (i < n2)
+                keys[i] = (uint32_t)i < cnt ? float_to_key(a.band_sorted[start + i]) : 0xFFFFFFFFu;
+        }
         __syncthreads();
         lds_bitonic_sort(keys, n2);
         lo = key_to_float(keys[0]);

@@ -64,7 +64,7 @@ __device__ __forceinline__ float emit_one(float v, double b, double c, double& a
 
 }  // namespace
 
-template <bool kVec>
+template <bool kVec, bool kNT>
 __global__ __launch_bounds__(kStreamThreads) void emit_kernel(EmitArgs a)
 {
     __shared__ double red[kStreamThreads / kWave];
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kStreamThreads) void emit_kernel(EmitArgs a)
             o.z = emit_one(v[u].z, b, c, acc);
             o.w = emit_one(v[u].w, b, c, acc);
             if (kVec) {
-                p4[q + u * kStreamThreads] = o;
+                store4<kNT>(&p4[q + u * kStreamThreads], o);
             } else {
                 float* p = a.p + 4 * (q + u * kStreamThreads);
                 p[0] = o.x;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kStreamThreads) void emit_kernel(EmitArgs a)
         o.z = emit_one(v.z, b, c, acc);
         o.w = emit_one(v.w, b, c, acc);
         if (kVec) {
-            p4[q] = o;
+            store4<kNT>(&p4[q], o);
         } else {
             float* p = a.p + 4 * q;
             p[0] = o.x;
@@ -184,10 +184,13 @@ __global__ __launch_bounds__(kStreamThreads) void emit_finalize_kernel(EmitArgs 
 hipError_t launch_emit(const EmitArgs& a, hipStream_t stream)
 {
     const bool vec = ((reinterpret_cast<uintptr_t>(a.s) | reinterpret_cast<uintptr_t>(a.p)) & 15u) == 0;
-    if (vec)
-        STK_LAUNCH(kKEmit, stream, emit_kernel<true>, dim3(a.blocks), dim3(kStreamThreads), 0, stream, a);
+    const bool nt = a.n >= kNontemporalMin;
+    if (vec && nt)
+        STK_LAUNCH(kKEmit, stream, (emit_kernel<true, true>), dim3(a.blocks), dim3(kStreamThreads), 0, stream, a);
+    else if (vec)
+        STK_LAUNCH(kKEmit, stream, (emit_kernel<true, false>), dim3(a.blocks), dim3(kStreamThreads), 0, stream, a);
     else
-        STK_LAUNCH(kKEmit, stream, emit_kernel<false>, dim3(a.blocks), dim3(kStreamThreads), 0, stream, a);
+        STK_LAUNCH(kKEmit, stream, (emit_kernel<false, false>), dim3(a.blocks), dim3(kStreamThreads), 0, stream, a);
     STK_LAUNCH(kKEmitFinal, stream, emit_finalize_kernel, dim3(1), dim3(kStreamThreads), 0, stream, a);
     return hipGetLastError();
 }
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_reduce_kernel(VjpArgs a)
     }
 }
 
-template <bool kVec>
+template <bool kVec, bool kNT>
 __global__ __launch_bounds__(kStreamThreads) void vjp_apply_kernel(VjpArgs a, int32_t reduce_blocks)
 {
     __shared__ double red[2][kStreamThreads / kWave];
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_kernel(VjpArgs a, in
         o.z = dens(v.z, b, c) * inv_alpha * (w.z - ratio);
         o.w = dens(v.w, b, c) * inv_alpha * (w.w - ratio);
         if (kVec) {
-            o4[q] = o;
+            store4<kNT>(&o4[q], o);
         } else {
             float* p = a.grad + 4 * q;
             p[0] = o.x;
@@ -381,12 +384,16 @@ hipError_t launch_vjp(const VjpArgs& a, hipStream_t stream)
     r.blocks = a.reduce_blocks;
     if (vec) {
         STK_LAUNCH(kKVjpReduce, stream, vjp_reduce_kernel<true>, dim3(r.blocks), dim3(kStreamThreads), 0, stream, r);
-        STK_LAUNCH(kKVjpApply, stream, vjp_apply_kernel<true>, dim3(a.blocks), dim3(kStreamThreads), 0, stream, a,
-                   r.blocks);
+        if (a.n >= kNontemporalMin)
+            STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<true, true>), dim3(a.blocks), dim3(kStreamThreads), 0,
+                       stream, a, r.blocks);
+        else
+            STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<true, false>), dim3(a.blocks), dim3(kStreamThreads), 0,
+                       stream, a, r.blocks);
     } else {
         STK_LAUNCH(kKVjpReduce, stream, vjp_reduce_kernel<false>, dim3(r.blocks), dim3(kStreamThreads), 0, stream, r);
-        STK_LAUNCH(kKVjpApply, stream, vjp_apply_kernel<false>, dim3(a.blocks), dim3(kStreamThreads), 0, stream, a,
-                   r.blocks);
+        STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<false, false>), dim3(a.blocks), dim3(kStreamThreads), 0,
+                   stream, a, r.blocks);
     }
     return hipGetLastError();
 }

@@ -11,12 +11,19 @@
 // [a_L, a_R] the left tail contributes SL e^{(a_L - b)/alpha} / 2 to M(b) and
 // the right tail nR - SR e^{-(a_R - b)/alpha} / 2.
 //
-// Design for gfx950: one work-group per contiguous chunk, 16-byte loads,
-// per-lane fp64 accumulators, band elements appended with one ballot and one
-// LDS atomic per wave into a 16 KiB LDS stage that is flushed with a single
-// global atomic per work-group, then a deterministic two-level reduction
-// (wave butterflies, a fixed-order pass over the per-group partials by the
-// last work-group to finish).
+// Design for gfx950: one work-group per contiguous chunk, sixteen scores per
+// lane per step (four 16-byte loads in flight).  Classification is fp32
+// compares only.  A tail score contributes 2^y with y = -|s - a|/alpha*log2e;
+// below y = -50 the term is under 2^-50 and is dropped (all dropped terms
+// together stay below n * 2^-50 < 2e-6, far under the mass tolerance), so only
+// "near" tail scores need the fp64 exponential.  Each lane queues its near
+// scores in its own LDS list and the wave then runs the exponential over the
+// queues with every lane busy, instead of paying it for every score.  Band
+// scores are queued in the same per-lane list (from the other end) and
+// appended with one LDS reservation per wave and step into a work-group
+// stage, flushed with one global reservation per work-group.  Counts are
+// exact; sums are fp64; per-group partials are folded in fixed order by the
+// consumer.
 #include "stk_common.hpp"
 #include "stk_layout.hpp"
 #include "stk_prof.hpp"
@@ -26,74 +33,116 @@ namespace stk {
 
 namespace {
 
-struct Acc {
+constexpr int kVals = 16;           // scores per lane per step
+constexpr int kLaneSlots = 17;      // per-lane LDS list (stride 17: no bank conflicts)
+constexpr double kTailCut = 50.0;   // tail terms below 2^-50 are dropped
+constexpr int kP1Stage = 2048;      // band scores staged per work-group
+
+struct Lanes {
+    float* stage;                   // LDS [kP1Stage]
+    uint32_t* stage_count;          // LDS reservation counter
+    float* my;                      // this lane's LDS list [kLaneSlots]
+};
+
+struct Ctx1 {
+    float aL, aR, tL, tR;
+    double daL, daR, c;
+    bool open;                      // a bracket end is infinite: track the band range
+    float* band;
+    int64_t cap;
+    unsigned long long* nB;
+};
+
+struct Acc1 {
     double SL, SR;
     uint32_t nL, nR;
-    float bmin, bmax, smin, smax;
-    uint32_t nonfinite;
+    float bmin, bmax;
+    float nf;                       // stays 0 unless a score is NaN or +-inf
 };
 
-struct Stage {
-    float* buf;        // LDS, kStageCap
-    uint32_t* count;   // LDS reservation counter
-};
-
-// Classify one score, accumulate tails, and append band members.  Called by
-// every lane of the wave (valid=false lanes contribute nothing), so the
-// ballot sees the whole wave.
-__device__ __forceinline__ void visit(float v, bool valid, float aL, float aR, double daL, double daR,
-                                      double c, Acc& acc, const Stage& stg, float* __restrict__ band,
-                                      int64_t cap, uint64_t* nB_global)
+// Classify up to 16 scores of this lane (v[i] valid iff bit i of `valid`;
+// kAll: all valid), fold near tail scores into the fp64 sums and append band
+// scores.  Called by every lane of the wave (the ballots and the reservation
+// are per wave).
+//
+// The per-lane list holds near scores from slot 0 up and band scores from
+// slot 16 down; both are stored unconditionally at their next free slot and
+// committed by bumping the count, which keeps the classification loop free of
+// branches (a speculative store only ever lands on a free slot: after i
+// scores nn + nb <= i, so the next near slot nn and the next band slot 16-nb
+// never reach a committed entry of the other list).
+template <bool kAll>
+__device__ __forceinline__ void step16(const float (&v)[kVals], uint32_t valid, const Ctx1& x, Acc1& acc,
+                                       const Lanes& L)
 {
-    const bool left = valid && (v < aL);
-    const bool right = valid && (v >= aR);
-    const bool in_band = valid && !left && !right;
-    if (valid) {
-        acc.nonfinite |= is_nonfinite(v) ? 1u : 0u;
-        acc.smin = fminf(acc.smin, v);
-        acc.smax = fmaxf(acc.smax, v);
+    uint32_t nn = 0, nb = 0;
+#pragma unroll
+    for (int i = 0; i < kVals; ++i) {
+        const bool ok = kAll || ((valid >> i) & 1u);
+        const float s = v[i];
+        const bool left = ok && s < x.aL;
+        const bool right = ok && s >= x.aR;
+        const bool band = ok && !(s < x.aL) && !(s >= x.aR);
+        acc.nL += left ? 1u : 0u;
+        acc.nR += right ? 1u : 0u;
+        const bool near = (left && s >= x.tL) || (right && s < x.tR);
+        L.my[nn] = s;
+        nn += near ? 1u : 0u;
+        L.my[kLaneSlots - 1 - nb] = s;
+        nb += band ? 1u : 0u;
+        acc.nf = fmaf(s, 0.f, acc.nf);
     }
-    const double x = left ? ((double)v - daL) : ((double)daR - (double)v);
-    const double y = (left || right) ? x * c : -2000.0;
-    const double e = exp2_nonpos(y);
-    acc.SL += left ? e : 0.0;
-    acc.SR += right ? e : 0.0;
-    acc.nL += left ? 1u : 0u;
-    acc.nR += right ? 1u : 0u;
-    if (in_band) {
-        acc.bmin = fminf(acc.bmin, v);
-        acc.bmax = fmaxf(acc.bmax, v);
+    // fp64 exponentials of the queued near scores, every lane busy
+    for (uint32_t j = 0; __ballot(j < nn) != 0; ++j) {
+        if (j < nn) {
+            const float s = L.my[j];
+            const bool left = s < x.aL;
+            const double d = left ? (double)s - x.daL : x.daR - (double)s;
+            const double e = exp2_nonpos(d * x.c);
+            if (left)
+                acc.SL += e;
+            else
+                acc.SR += e;
+        }
     }
-
-    const uint64_t mask = __ballot(in_band);
-    if (mask == 0)
+    // band append: lane offsets from the bit planes of nb (<= 16)
+    uint32_t prefix = 0, total = 0;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+        const uint64_t m = __ballot((nb >> b) & 1u);
+        prefix += rank_in_mask(m) << b;
+        total += (uint32_t)__popcll(m) << b;
+    }
+    if (total == 0)
         return;
-    const uint32_t total = (uint32_t)__popcll(mask);
-    const uint64_t active = __ballot(1);
-    const int leader = __ffsll((long long)active) - 1;
     const int lane = lane_id();
     uint32_t base = 0;
-    if (lane == leader)
-        base = atomicAdd(stg.count, total);
-    base = __shfl(base, leader, kWave);
-    const uint32_t pos = base + rank_in_mask(mask);
+    if (lane == 0)
+        base = atomicAdd(L.stage_count, total);
+    base = __shfl(base, 0, kWave);
     // reservations past the LDS stage go straight to the global band
-    const uint32_t first_over = base > (uint32_t)kStageCap ? base : (uint32_t)kStageCap;
+    const uint32_t first_over = base > (uint32_t)kP1Stage ? base : (uint32_t)kP1Stage;
     const uint32_t end = base + total;
     const uint32_t n_over = end > first_over ? end - first_over : 0u;
     unsigned long long gbase = 0;
     if (n_over) {
-        if (lane == leader)
-            gbase = atomicAdd((unsigned long long*)nB_global, (unsigned long long)n_over);
-        gbase = __shfl(gbase, leader, kWave);
+        if (lane == 0)
+            gbase = atomicAdd(x.nB, (unsigned long long)n_over);
+        gbase = __shfl(gbase, 0, kWave);
     }
-    if (in_band) {
-        if (pos < (uint32_t)kStageCap) {
-            stg.buf[pos] = v;
+    for (uint32_t k = 0; k < nb; ++k) {
+        const uint32_t pos = base + prefix + k;
+        const float s = L.my[kLaneSlots - 1 - k];
+        if (x.open) {
+            acc.bmin = fminf(acc.bmin, s);
+            acc.bmax = fmaxf(acc.bmax, s);
+        }
+        if (pos < (uint32_t)kP1Stage) {
+            L.stage[pos] = s;
         } else {
             const uint64_t g = (uint64_t)gbase + (pos - first_over);
-            if (g < (uint64_t)cap)
-                band[g] = v;
+            if (g < (uint64_t)x.cap)
+                x.band[g] = s;
         }
     }
 }
@@ -103,12 +152,13 @@ __device__ __forceinline__ void visit(float v, bool valid, float aL, float aR, d
 template <bool kVec>
 __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
 {
-    __shared__ float stage_buf[kStageCap];
+    __shared__ float stage_buf[kP1Stage];
+    __shared__ float lists[kStreamThreads * kLaneSlots];
     __shared__ uint32_t stage_count;
     __shared__ unsigned long long stage_base;
     __shared__ double red_d[2][kStreamThreads / kWave];
     __shared__ uint32_t red_u[3][kStreamThreads / kWave];
-    __shared__ float red_f[4][kStreamThreads / kWave];
+    __shared__ float red_f[2][kStreamThreads / kWave];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -119,74 +169,97 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
         stage_count = 0;
     __syncthreads();
 
-    const float aL = st->aL;
-    const float aR = st->aR;
-    const double daL = aL, daR = aR;
-    const double c = a.log2e_over_alpha;
-    Stage stg{stage_buf, &stage_count};
-    uint64_t* nB = &st->nB;
+    Ctx1 x;
+    x.aL = st->aL;
+    x.aR = st->aR;
+    x.daL = x.aL;
+    x.daR = x.aR;
+    x.c = a.log2e_over_alpha;
+    // near thresholds in fp32, rounded outward so no term >= 2^-50 is dropped
+    const double cut = kTailCut / x.c;
+    x.tL = (float)(x.daL - cut);
+    if ((double)x.tL > x.daL - cut)
+        x.tL = nextafterf(x.tL, -INFINITY);
+    x.tR = (float)(x.daR + cut);
+    if ((double)x.tR < x.daR + cut)
+        x.tR = nextafterf(x.tR, INFINITY);
+    x.open = (x.aL == -INFINITY) || (x.aR == INFINITY);
+    x.band = a.band;
+    x.cap = a.cap;
+    x.nB = reinterpret_cast<unsigned long long*>(&st->nB);
+    Lanes L{stage_buf, &stage_count, lists + tid * kLaneSlots};
 
-    Acc acc{0.0, 0.0, 0u, 0u, INFINITY, -INFINITY, INFINITY, -INFINITY, 0u};
+    Acc1 acc{0.0, 0.0, 0u, 0u, INFINITY, -INFINITY, 0.f};
 
     const int64_t n4 = a.n >> 2;
     const int64_t q0 = (n4 * blockIdx.x) / a.blocks;
     const int64_t q1 = (n4 * (blockIdx.x + 1)) / a.blocks;
     const float4* s4 = reinterpret_cast<const float4*>(a.s);
 
-    // main loop: four 16-byte loads in flight per lane; the trip count is
-    // the same for every lane, so the ballots below see whole waves
+    // uniform trip count: every lane runs every step (ballots see whole waves)
     int64_t qb = q0;
     for (; qb + 4 * kStreamThreads <= q1; qb += 4 * kStreamThreads) {
-        const int64_t q = qb + tid;
-        float4 v[4];
+        float v[kVals];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+            const int64_t q = qb + u * kStreamThreads + tid;
+            float4 f;
             if (kVec) {
-                v[u] = s4[q + u * kStreamThreads];
+                f = s4[q];
             } else {
-                const float* p = a.s + 4 * (q + u * kStreamThreads);
-                v[u] = make_float4(p[0], p[1], p[2], p[3]);
+                const float* p = a.s + 4 * q;
+                f = make_float4(p[0], p[1], p[2], p[3]);
             }
+            v[4 * u + 0] = f.x;
+            v[4 * u + 1] = f.y;
+            v[4 * u + 2] = f.z;
+            v[4 * u + 3] = f.w;
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            visit(v[u].x, true, aL, aR, daL, daR, c, acc, stg, a.band, a.cap, nB);
-            visit(v[u].y, true, aL, aR, daL, daR, c, acc, stg, a.band, a.cap, nB);
-            visit(v[u].z, true, aL, aR, daL, daR, c, acc, stg, a.band, a.cap, nB);
-            visit(v[u].w, true, aL, aR, daL, daR, c, acc, stg, a.band, a.cap, nB);
-        }
+        step16<true>(v, 0xFFFFu, x, acc, L);
     }
-    // remainder of the chunk; out-of-range lanes visit with valid=false
-    for (; qb < q1; qb += kStreamThreads) {
-        const int64_t qq = qb + tid;
-        const bool valid = qq < q1;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (valid) {
-            if (kVec) {
-                v = s4[qq];
-            } else {
-                const float* p = a.s + 4 * qq;
-                v = make_float4(p[0], p[1], p[2], p[3]);
+    if (qb < q1) {
+        float v[kVals];
+        uint32_t valid = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t q = qb + u * kStreamThreads + tid;
+            float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (q < q1) {
+                if (kVec) {
+                    f = s4[q];
+                } else {
+                    const float* p = a.s + 4 * q;
+                    f = make_float4(p[0], p[1], p[2], p[3]);
+                }
+                valid |= 0xFu << (4 * u);
             }
+            v[4 * u + 0] = f.x;
+            v[4 * u + 1] = f.y;
+            v[4 * u + 2] = f.z;
+            v[4 * u + 3] = f.w;
         }
-        visit(v.x, valid, aL, aR, daL, daR, c, acc, stg, a.band, a.cap, nB);
-        visit(v.y, valid, aL, aR, daL, daR, c, acc, stg, a.band, a.cap, nB);
-        visit(v.z, valid, aL, aR, daL, daR, c, acc, stg, a.band, a.cap, nB);
-        visit(v.w, valid, aL, aR, daL, daR, c, acc, stg, a.band, a.cap, nB);
+        step16<false>(v, valid, x, acc, L);
     }
     // the last 0..3 scores when n is not a multiple of 4
-    if (blockIdx.x == a.blocks - 1 && wave == 0) {
-        const int64_t i = 4 * n4 + lane;
-        const bool valid = lane < 4 && i < a.n;
-        const float v = valid ? a.s[i] : 0.f;
-        visit(v, valid, aL, aR, daL, daR, c, acc, stg, a.band, a.cap, nB);
+    if (blockIdx.x == a.blocks - 1) {
+        const int64_t i = 4 * n4 + tid;
+        float v[kVals];
+#pragma unroll
+        for (int k = 0; k < kVals; ++k)
+            v[k] = 0.f;
+        uint32_t valid = 0;
+        if (tid < 4 && i < a.n) {
+            v[0] = a.s[i];
+            valid = 1u;
+        }
+        step16<false>(v, valid, x, acc, L);
     }
 
     // flush the LDS stage with one global reservation
     __syncthreads();
-    const uint32_t staged = stage_count < (uint32_t)kStageCap ? stage_count : (uint32_t)kStageCap;
+    const uint32_t staged = stage_count < (uint32_t)kP1Stage ? stage_count : (uint32_t)kP1Stage;
     if (tid == 0)
-        stage_base = staged ? atomicAdd((unsigned long long*)nB, (unsigned long long)staged) : 0ull;
+        stage_base = staged ? atomicAdd(x.nB, (unsigned long long)staged) : 0ull;
     __syncthreads();
     for (uint32_t i = tid; i < staged; i += kStreamThreads) {
         const uint64_t g = (uint64_t)stage_base + i;
@@ -195,19 +268,17 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
     }
 
     // work-group reduction into this group's partial; the consumer (segment
-    // solve or finalize kernel) folds the partials in fixed order.  No
-    // ticket: an agent-scope fence per work-group would write back the whole
-    // L2 each time.
-    double SL = wave_sum(acc.SL);
-    double SR = wave_sum(acc.SR);
-    uint32_t nL = wave_sum_u32(acc.nL);
-    uint32_t nR = wave_sum_u32(acc.nR);
-    uint32_t nf = acc.nonfinite;
+    // solve) folds the partials in fixed order.  No ticket: an agent-scope
+    // fence per work-group would write back the whole L2 each time.
+    const double SL = wave_sum(acc.SL);
+    const double SR = wave_sum(acc.SR);
+    const uint32_t nL = wave_sum_u32(acc.nL);
+    const uint32_t nR = wave_sum_u32(acc.nR);
+    uint32_t nf = acc.nf != 0.f || acc.nf != acc.nf ? 1u : 0u;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         nf |= __shfl_xor(nf, off, kWave);
     const float bmin = wave_min(acc.bmin), bmax = wave_max(acc.bmax);
-    const float smin = wave_min(acc.smin), smax = wave_max(acc.smax);
     if (lane == 0) {
         red_d[0][wave] = SL;
         red_d[1][wave] = SR;
@@ -216,8 +287,6 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
         red_u[2][wave] = nf;
         red_f[0][wave] = bmin;
         red_f[1][wave] = bmax;
-        red_f[2][wave] = smin;
-        red_f[3][wave] = smax;
     }
     __syncthreads();
     if (tid == 0) {
@@ -239,11 +308,67 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
             p.nonfinite |= red_u[2][w];
             p.bmin = fminf(p.bmin, red_f[0][w]);
             p.bmax = fmaxf(p.bmax, red_f[1][w]);
-            p.smin = fminf(p.smin, red_f[2][w]);
-            p.smax = fmaxf(p.smax, red_f[3][w]);
         }
         a.partials[blockIdx.x] = p;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Score range and finiteness for the full-sort route (the radix sort only
+// sorts the key bits that vary between the smallest and largest score).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kStreamThreads) void range_kernel(const float* __restrict__ s, int64_t n,
+                                                               Pass1Partial* partials, int blocks)
+{
+    __shared__ float red[3][kStreamThreads / kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int64_t i0 = (n * blockIdx.x) / blocks;
+    const int64_t i1 = (n * (blockIdx.x + 1)) / blocks;
+    float mn = INFINITY, mx = -INFINITY, nf = 0.f;
+    for (int64_t i = i0 + tid; i < i1; i += kStreamThreads) {
+        const float v = s[i];
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+        nf = fmaf(v, 0.f, nf);
+    }
+    uint32_t bad = (nf != 0.f || nf != nf) ? 1u : 0u;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        bad |= __shfl_xor(bad, off, kWave);
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+        red[0][wave] = mn;
+        red[1][wave] = mx;
+        red[2][wave] = bad ? 1.f : 0.f;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        Pass1Partial p;
+        p.SL = 0.0;
+        p.SR = 0.0;
+        p.nL = 0;
+        p.nR = 0;
+        p.bmin = INFINITY;
+        p.bmax = -INFINITY;
+        p.smin = INFINITY;
+        p.smax = -INFINITY;
+        p.nonfinite = 0;
+        for (int w = 0; w < kStreamThreads / kWave; ++w) {
+            p.smin = fminf(p.smin, red[0][w]);
+            p.smax = fmaxf(p.smax, red[1][w]);
+            p.nonfinite |= red[2][w] != 0.f ? 1u : 0u;
+        }
+        partials[blockIdx.x] = p;
+    }
+}
+
+hipError_t launch_range(const float* s, int64_t n, Pass1Partial* partials, int blocks, hipStream_t stream)
+{
+    STK_LAUNCH(kKPass1, stream, range_kernel, dim3(blocks), dim3(kStreamThreads), 0, stream, s, n, partials, blocks);
+    return hipGetLastError();
 }
 
 __global__ __launch_bounds__(kStreamThreads) void pass1_finalize_kernel(const Pass1Partial* partials, int blocks,

@@ -16,10 +16,23 @@
 
 namespace stk {
 
-// One thread per sample.  Counter (j, 0, 0, 0), key (seed lo, seed hi).
-// Word 0/1 give a 64-bit uniform u64; the index is the high half of
-// u64 * n (unbiased to 2^-64 n, where a 32-bit product would skew indices by
-// up to n/2^32).  Word 2 gives u in (0,1) and E = F^{-1}(u).
+// Sample j: counter (j, 0, 0, 0), key (seed lo, seed hi).  Words 0/1 give a
+// 64-bit uniform u64; the index is the high half of u64 * n (unbiased to
+// 2^-64 n, where a 32-bit product would skew indices by up to n/2^32).  Word 2
+// gives u in (0,1) and E = F^{-1}(u).  Samples are regenerated wherever they
+// are needed (same counter, same value), never stored.
+__device__ __forceinline__ float sample_value(const float* __restrict__ s, int64_t n, float alpha, uint32_t k0,
+                                              uint32_t k1, uint32_t j)
+{
+    const Philox4 r = philox4x32_10(j, 0u, 0u, 0u, k0, k1);
+    const uint64_t u64 = ((uint64_t)r.v[1] << 32) | (uint64_t)r.v[0];
+    const uint64_t idx = __umul64hi(u64, (uint64_t)n);  // < n
+    const double u = ((double)r.v[2] + 0.5) * (1.0 / 4294967296.0);
+    const double e = (u < 0.5) ? log(2.0 * u) : -log(2.0 * (1.0 - u));
+    return (float)((double)s[idx] + (double)alpha * e);
+}
+
+// Diagnostic: write the m samples (soft_topk_debug_sample).
 __global__ __launch_bounds__(256) void sample_kernel(const float* __restrict__ s, int64_t n, float alpha,
                                                      uint32_t k0, uint32_t k1, int32_t m,
                                                      float* __restrict__ out)
@@ -27,23 +40,18 @@ __global__ __launch_bounds__(256) void sample_kernel(const float* __restrict__ s
     const int32_t j = blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= m)
         return;
-    const Philox4 r = philox4x32_10((uint32_t)j, 0u, 0u, 0u, k0, k1);
-    const uint64_t u64 = ((uint64_t)r.v[1] << 32) | (uint64_t)r.v[0];
-    const uint64_t idx = __umul64hi(u64, (uint64_t)n);  // < n
-    const double u = ((double)r.v[2] + 0.5) * (1.0 / 4294967296.0);
-    const double e = (u < 0.5) ? log(2.0 * u) : -log(2.0 * (1.0 - u));
-    out[j] = (float)((double)s[idx] + (double)alpha * e);
+    out[j] = sample_value(s, n, alpha, k0, k1, (uint32_t)j);
 }
 
-hipError_t launch_sample(const float* s, int64_t n, float alpha, uint64_t seed, int32_t m,
-                         float* out_samples, Status* st, hipStream_t stream)
+hipError_t launch_debug_sample(const float* s, int64_t n, float alpha, uint64_t seed, int32_t m,
+                               float* out_samples, hipStream_t stream)
 {
-    (void)st;
     const int blocks = (m + 255) / 256;
     STK_LAUNCH(kKSample, stream, sample_kernel, dim3(blocks), dim3(256), 0, stream, s, n, alpha,
-                       (uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32), m, out_samples);
+               (uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32), m, out_samples);
     return hipGetLastError();
 }
+
 
 // ---------------------------------------------------------------------------
 // Exact selection of up to two order statistics (1-based ranks r[0], r[1]) of
@@ -129,101 +137,115 @@ __device__ void lds_select2(const uint32_t* keys, int cnt, int64_t r0, int64_t r
 }
 
 // ---------------------------------------------------------------------------
-// Select the r_left-th and r_right-th smallest of the m samples with one
-// work-group: two pilot order statistics (from the first kPilot samples) that
-// enclose the targets with a wide margin; a count of the samples below the
-// lower one; the samples between them gathered into LDS; the targets
-// selected among those.  If the gather overflows or a target falls outside
-// the candidates, a pilot value with a more conservative rank is used instead
-// (the bracket only widens, so the certificate still decides).
-//
-// Also clears the per-round counters of the status block: this kernel runs
-// first in every bracketed round.
+// The localisation in three kernels, so no single work-group has to read all
+// m samples (one CU ingests only ~10 GB/s of freshly written data):
+//   pilot  (1 work-group)  -- the first P = min(m, kPilot) samples, two of
+//          their order statistics that enclose the target ranks with a wide
+//          margin (ranks from the host);
+//   filter (m/256 groups)  -- every sample regenerated, counted if below the
+//          lower pilot bound, appended to a candidate list if between them;
+//   select (1 work-group)  -- the target order statistics among the
+//          candidates, offset by the count below.
+// If the candidates overflow or a target falls outside them, a pilot value
+// with a more conservative rank is used (the bracket only widens, so the
+// certificate still decides).  The pilot kernel also clears the per-round
+// counters of the status block: it runs first in every bracketed round.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
+__global__ __launch_bounds__(kSelectThreads) void pilot_kernel(SampleArgs a)
 {
     __shared__ uint32_t pilot[kPilot];
-    __shared__ uint32_t cand[kCandCap];
-    __shared__ uint32_t cand_n;
-    __shared__ uint32_t wave_below[kSelectThreads / kWave];
-    __shared__ uint32_t sel[4];
-
+    __shared__ uint32_t sel[2];
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
     Status* st = a.st;
-
     if (tid == 0) {
-        cand_n = 0;
-        sel[0] = 0u;            // pilot lower bound: open
-        sel[1] = 0xFFFFFFFFu;   // pilot upper bound: open
+        sel[0] = 0u;            // open lower bound
+        sel[1] = 0xFFFFFFFFu;   // open upper bound
         st->nB = 0;
         st->solve_state = kSolveNotRun;
         st->emit_done = 0;
         st->nonfinite = 0;
+        st->cand_n = 0;
+        st->below_n = 0;
     }
-
-    // 1. pilot bounds: two order statistics of the first P samples
     const int P = a.m < kPilot ? a.m : kPilot;
     for (int i = tid; i < P; i += blockDim.x)
-        pilot[i] = float_to_key(a.samples[i]);
+        pilot[i] = float_to_key(sample_value(a.s, a.n, a.alpha, a.k0, a.k1, (uint32_t)i));
     __syncthreads();
     lds_select2(pilot, P, a.pilot_lo, a.pilot_hi, &sel[0], &sel[1]);
-    const uint32_t lo_key = sel[0];
-    const uint32_t hi_key = sel[1];
-
-    // 2. count below / gather candidates (eight loads in flight per thread)
-    constexpr int kBatch = 8;
-    uint32_t below = 0;
-    for (int base = 0; base < a.m; base += kBatch * kSelectThreads) {
-        uint32_t key[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int i = base + j * kSelectThreads + tid;
-            key[j] = i < a.m ? float_to_key(a.samples[i]) : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int i = base + j * kSelectThreads + tid;
-            const bool valid = i < a.m;
-            const bool is_below = valid && key[j] < lo_key;
-            const bool is_cand = valid && key[j] >= lo_key && key[j] <= hi_key;
-            below += is_below ? 1u : 0u;
-            const uint64_t mask = __ballot(is_cand);
-            if (mask) {
-                const uint32_t cnt = (uint32_t)__popcll(mask);
-                uint32_t pos0 = 0;
-                if (lane == 0)
-                    pos0 = atomicAdd(&cand_n, cnt);
-                pos0 = __shfl(pos0, 0, kWave);
-                if (is_cand) {
-                    const uint32_t pos = pos0 + rank_in_mask(mask);
-                    if (pos < (uint32_t)kCandCap)
-                        cand[pos] = key[j];
-                }
-            }
-        }
+    if (tid == 0) {
+        st->pilot_lo = sel[0];
+        st->pilot_hi = sel[1];
     }
-    below = wave_sum_u32(below);
-    if (lane == 0)
-        wave_below[wave] = below;
-    __syncthreads();
-    uint64_t cb = 0;
-    for (int w = 0; w < (int)(blockDim.x / kWave); ++w)
-        cb += wave_below[w];
-    const uint64_t cc = cand_n;
+}
 
-    // 3. the targets among the candidates
+__global__ __launch_bounds__(256) void filter_kernel(SampleArgs a)
+{
+    __shared__ uint32_t wcnt[2][256 / kWave];
+    __shared__ uint32_t base_s;
+    Status* st = a.st;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int32_t j = blockIdx.x * 256 + tid;
+    const bool valid = j < a.m;
+    const uint32_t key = valid ? float_to_key(sample_value(a.s, a.n, a.alpha, a.k0, a.k1, (uint32_t)j)) : 0u;
+    const uint32_t lo = st->pilot_lo, hi = st->pilot_hi;
+    const bool below = valid && key < lo;
+    const bool cand = valid && key >= lo && key <= hi;
+    const uint64_t bm = __ballot(below);
+    const uint64_t cm = __ballot(cand);
+    if (lane == 0) {
+        wcnt[0][wave] = (uint32_t)__popcll(bm);
+        wcnt[1][wave] = (uint32_t)__popcll(cm);
+    }
+    __syncthreads();
+    uint32_t woff = 0, tot_c = 0, tot_b = 0;
+    for (int w = 0; w < 256 / kWave; ++w) {
+        woff += w < wave ? wcnt[1][w] : 0u;
+        tot_c += wcnt[1][w];
+        tot_b += wcnt[0][w];
+    }
+    if (tid == 0) {
+        base_s = tot_c ? atomicAdd(&st->cand_n, tot_c) : 0u;
+        if (tot_b)
+            atomicAdd(&st->below_n, tot_b);
+    }
+    __syncthreads();
+    if (cand) {
+        const uint32_t pos = base_s + woff + rank_in_mask(cm);
+        if (pos < (uint32_t)kCandCap)
+            a.cand[pos] = key;
+    }
+}
+
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
+{
+    __shared__ uint32_t cand[kCandCap];
+    __shared__ uint32_t sel[2];
+    const int tid = threadIdx.x;
+    Status* st = a.st;
+    const uint64_t cb = st->below_n;
+    const uint64_t cc = st->cand_n;
+    const uint32_t lo_key = st->pilot_lo, hi_key = st->pilot_hi;
     const int64_t rl = a.r_left, rr = a.r_right;
     const bool overflow = cc > (uint64_t)kCandCap;
     const bool left_inf = rl <= 0;
     const bool right_inf = rr > (int64_t)a.m;
     const bool left_in = !left_inf && (uint64_t)rl > cb && (uint64_t)rl <= cb + cc;
     const bool right_in = !right_inf && (uint64_t)rr > cb && (uint64_t)rr <= cb + cc;
-    if (!overflow && (left_in || right_in))
-        lds_select2(cand, (int)cc, left_in ? rl - (int64_t)cb : 0, right_in ? rr - (int64_t)cb : 0, &sel[2],
-                    &sel[3]);
-
+    if (!overflow && (left_in || right_in)) {
+        // every candidate load issued at once
+        constexpr int kPer = kCandCap / kSelectThreads;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = j * kSelectThreads + tid;
+            if ((uint64_t)i < cc)
+                cand[i] = a.cand[i];
+        }
+        __syncthreads();
+        lds_select2(cand, (int)cc, left_in ? rl - (int64_t)cb : 0, right_in ? rr - (int64_t)cb : 0, &sel[0],
+                    &sel[1]);
+    }
     if (tid == 0) {
         // open pilot bounds stand for -inf / +inf
         const float lo_val = lo_key == 0u ? -INFINITY : key_to_float(lo_key);
@@ -241,7 +263,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
         } else if (overflow) {
             aL = lo_val;  // rank cb+1 <= r_left: conservative
         } else {
-            aL = key_to_float(sel[2]);
+            aL = key_to_float(sel[0]);
         }
         if (right_inf) {
             aR = INFINITY;
@@ -254,7 +276,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
         } else if (overflow) {
             aR = hi_val;  // rank cb+cc >= r_right: conservative
         } else {
-            aR = key_to_float(sel[3]);
+            aR = key_to_float(sel[1]);
         }
         st->aL = aL;
         st->aR = aR;
@@ -263,9 +285,12 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
     }
 }
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
+hipError_t launch_localize(const SampleArgs& sa, const SelectArgs& se, hipStream_t stream)
 {
-    STK_LAUNCH(kKSelect, stream, select_kernel, dim3(1), dim3(kSelectThreads), 0, stream, a);
+    STK_LAUNCH(kKPilot, stream, pilot_kernel, dim3(1), dim3(kSelectThreads), 0, stream, sa);
+    const int blocks = (sa.m + 255) / 256;
+    STK_LAUNCH(kKSample, stream, filter_kernel, dim3(blocks), dim3(256), 0, stream, sa);
+    STK_LAUNCH(kKSelect, stream, select_kernel, dim3(1), dim3(kSelectThreads), 0, stream, se);
     return hipGetLastError();
 }
 

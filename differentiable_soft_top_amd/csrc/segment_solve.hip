@@ -80,70 +80,104 @@ struct ScanLds {
     unsigned long long u[kT];
 };
 
-// Inclusive work-group scan of anchored sums; kForward: prefix over threads
-// 0..tid; else suffix over tid..nt-1.  Hillis-Steele in LDS.
-template <bool kForward>
-__device__ Anch wg_scan(Anch mine, ScanLds& L, double c)
+struct ScanOut {
+    Anch incl;  // over threads 0..tid (forward) or tid..nt-1 (backward)
+    Anch excl;  // the same without this thread
+};
+
+__device__ __forceinline__ Anch shfl_anch(Anch a, int src_lane)
 {
-    const int tid = threadIdx.x;
-    __syncthreads();  // earlier readers of L are done
-    L.x[tid] = mine.x;
-    L.v[tid] = mine.v;
-    L.h[tid] = mine.has;
-    __syncthreads();
-    for (int off = 1; off < kT; off <<= 1) {
-        const int j = kForward ? tid - off : tid + off;
-        const bool ok = kForward ? (j >= 0) : (j < kT);
-        Anch o;
-        o.x = 0.0;
-        o.v = 0.0;
-        o.has = 0;
-        if (ok) {
-            o.x = L.x[j];
-            o.v = L.v[j];
-            o.has = L.h[j];
-        }
-        __syncthreads();
-        if (ok)
-            mine = kForward ? fwd(o, mine, c) : bwd(mine, o, c);
-        L.x[tid] = mine.x;
-        L.v[tid] = mine.v;
-        L.h[tid] = mine.has;
-        __syncthreads();
-    }
-    return mine;
+    Anch o;
+    o.x = __shfl(a.x, src_lane, kWave);
+    o.v = __shfl(a.v, src_lane, kWave);
+    o.has = __shfl(a.has, src_lane, kWave);
+    return o;
 }
 
-// Read thread j's inclusive result from the last scan (identity if out of range).
-__device__ __forceinline__ Anch scan_at(const ScanLds& L, int j)
+__device__ __forceinline__ Anch empty_anch()
 {
     Anch a;
     a.x = 0.0;
     a.v = 0.0;
     a.has = 0;
-    if (j >= 0 && j < kT) {
-        a.x = L.x[j];
-        a.v = L.v[j];
-        a.has = L.h[j];
-    }
     return a;
 }
 
-// Inclusive prefix sum of u64 over the work-group.
+// Work-group scan of anchored sums: kForward is a prefix over threads
+// 0..tid, else a suffix over tid..nt-1.  Kogge-Stone over shuffles inside
+// each wave, then the wave totals (LDS) folded in order by every thread.
+template <bool kForward>
+__device__ ScanOut wg_scan(Anch mine, ScanLds& L, double c)
+{
+    constexpr int kWaves = kT / kWave;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    Anch incl = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int src = kForward ? lane - off : lane + off;
+        const Anch o = shfl_anch(incl, src < 0 ? 0 : (src >= kWave ? kWave - 1 : src));
+        if (kForward ? lane >= off : lane + off < kWave)
+            incl = kForward ? fwd(o, incl, c) : bwd(incl, o, c);
+    }
+    // within-wave exclusive value: the neighbour's inclusive one
+    const int nb = kForward ? lane - 1 : lane + 1;
+    Anch wex = shfl_anch(incl, nb < 0 ? 0 : (nb >= kWave ? kWave - 1 : nb));
+    if (kForward ? lane == 0 : lane == kWave - 1)
+        wex = empty_anch();
+    __syncthreads();  // earlier readers of L are done
+    if (kForward ? lane == kWave - 1 : lane == 0) {
+        L.x[wave] = incl.x;
+        L.v[wave] = incl.v;
+        L.h[wave] = incl.has;
+    }
+    __syncthreads();
+    Anch agg = empty_anch();
+    if (kForward) {
+        for (int w = 0; w < wave; ++w) {
+            Anch t;
+            t.x = L.x[w];
+            t.v = L.v[w];
+            t.has = L.h[w];
+            agg = fwd(agg, t, c);
+        }
+    } else {
+        for (int w = kWaves - 1; w > wave; --w) {
+            Anch t;
+            t.x = L.x[w];
+            t.v = L.v[w];
+            t.has = L.h[w];
+            agg = bwd(t, agg, c);
+        }
+    }
+    ScanOut out;
+    out.incl = kForward ? fwd(agg, incl, c) : bwd(incl, agg, c);
+    out.excl = kForward ? fwd(agg, wex, c) : bwd(wex, agg, c);
+    return out;
+}
+
+// Inclusive prefix sum of u64 over the work-group (shuffles + wave totals).
 __device__ unsigned long long wg_scan_u64(unsigned long long mine, ScanLds& L)
 {
     const int tid = threadIdx.x;
-    __syncthreads();
-    L.u[tid] = mine;
-    __syncthreads();
-    for (int off = 1; off < kT; off <<= 1) {
-        const unsigned long long o = tid >= off ? L.u[tid - off] : 0ull;
-        __syncthreads();
-        mine += o;
-        L.u[tid] = mine;
-        __syncthreads();
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    unsigned long long incl = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const unsigned long long o = __shfl_up(incl, off, kWave);
+        if (lane >= off)
+            incl += o;
     }
-    return mine;
+    __syncthreads();
+    if (lane == kWave - 1)
+        L.u[wave] = incl;
+    __syncthreads();
+    unsigned long long before = 0;
+    for (int w = 0; w < wave; ++w)
+        before += L.u[w];
+    return before + incl;
 }
 
 __device__ int wg_max_int(int v, int* red)
@@ -218,8 +252,11 @@ __global__ __launch_bounds__(kT) void solve_kernel(SolveArgs a)
     right.v = 0.0;
     unsigned long long nR = 0;
     if (a.tails) {
-        // fold the pass-1 partials (tails, counts, finiteness) into the status
-        const Pass1Partial tot = reduce_pass1(a.p1, a.p1_blocks, st);
+        // fold the pass-1 partials (tails, counts, finiteness) into the status;
+        // the band sort has pre-folded them unless the band overflowed
+        const bool folded = st->nB <= (uint64_t)a.cap;
+        const Pass1Partial tot = folded ? reduce_pass1(a.p1_super, kBuckets, st)
+                                        : reduce_pass1(a.p1, a.p1_blocks, st);
         if (tot.nonfinite) {
             if (tid == 0)
                 st->solve_state = kSolveNonfinite;
@@ -285,18 +322,18 @@ __global__ __launch_bounds__(kT) void solve_kernel(SolveArgs a)
     const unsigned long long cnt_incl = wg_scan_u64(cnt, L);
     if (tid == kT - 1)
         bc_u[0] = cnt_incl;  // total over groups
-    const Anch pre_incl = wg_scan<true>(pre, L, c);
-    const Anch pre_before = fwd(left, scan_at(L, tid - 1), c);
+    const ScanOut pre_s = wg_scan<true>(pre, L, c);
+    const Anch pre_before = fwd(left, pre_s.excl, c);
     if (tid == kT - 1) {
-        const Anch all = fwd(left, pre_incl, c);
+        const Anch all = fwd(left, pre_s.incl, c);
         bc_d[0] = all.x;
         bc_d[1] = all.v;
         bc_i[0] = all.has;
     }
-    const Anch suf_incl = wg_scan<false>(suf, L, c);
-    const Anch suf_after = bwd(scan_at(L, tid + 1), right, c);
+    const ScanOut suf_s = wg_scan<false>(suf, L, c);
+    const Anch suf_after = bwd(suf_s.excl, right, c);
     if (tid == 0) {
-        const Anch all = bwd(suf_incl, right, c);
+        const Anch all = bwd(suf_s.incl, right, c);
         bc_d[2] = all.x;
         bc_d[3] = all.v;
         bc_i[1] = all.has;
@@ -484,10 +521,8 @@ __global__ __launch_bounds__(kT) void solve_kernel(SolveArgs a)
         }
         Bv[i] = ls.v;
     }
-    wg_scan<true>(lp, L, c);
-    const Anch ex_pre = fwd(lo_node, scan_at(L, tid - 1), c);
-    wg_scan<false>(ls, L, c);
-    const Anch ex_suf = bwd(scan_at(L, tid + 1), Su, c);
+    const Anch ex_pre = fwd(lo_node, wg_scan<true>(lp, L, c).excl, c);
+    const Anch ex_suf = bwd(wg_scan<false>(ls, L, c).excl, Su, c);
 
     int jc = -1;
 #pragma unroll

@@ -75,6 +75,7 @@ void fill_defaults(soft_topk_params* p)
     p->max_widen = 2;
     p->force_path = 0;
     p->mass_tolerance = 0.0;
+    p->verify_mass = 0;
 }
 
 bool params_ok(const soft_topk_params& p)
@@ -89,6 +90,8 @@ bool params_ok(const soft_topk_params& p)
         return false;
     if (!isfinite(p.mass_tolerance))
         return false;
+    if (p.verify_mass != 0 && p.verify_mass != 1)
+        return false;
     return true;
 }
 
@@ -99,46 +102,52 @@ double log_pmf(int64_t m, double q, int64_t i)
            (double)i * log(q) + (double)(m - i) * log1p(-q);
 }
 
-// P(X <= r), X ~ Binomial(m, q); summed from r downward while terms matter.
+// P(X <= r), X ~ Binomial(m, q), for r below the mean: summed from r
+// downward with the ratio pmf(i-1)/pmf(i) = i (1-q) / ((m-i+1) q).
 double cdf_le(int64_t m, double q, int64_t r)
 {
     if (r < 0)
         return 0.0;
     if (r >= m)
         return 1.0;
-    double s = 0.0;
-    for (int64_t i = r; i >= 0; --i) {
-        const double t = exp(log_pmf(m, q, i));
+    double t = exp(log_pmf(m, q, r));
+    double s = t;
+    const double ratio_q = (1.0 - q) / q;
+    for (int64_t i = r; i >= 1; --i) {
+        t *= (double)i / (double)(m - i + 1) * ratio_q;
         s += t;
         if ((double)i < (double)m * q && t < 1e-20 * s)
             break;
         if (s > 1.0)
-            break;
+            return 1.0;
     }
     return std::min(s, 1.0);
 }
 
-// P(X >= r)
+// P(X >= r) for r above the mean: summed upward with
+// pmf(i+1)/pmf(i) = (m-i) q / ((i+1) (1-q)).
 double sf_ge(int64_t m, double q, int64_t r)
 {
     if (r <= 0)
         return 1.0;
     if (r > m)
         return 0.0;
-    double s = 0.0;
-    for (int64_t i = r; i <= m; ++i) {
-        const double t = exp(log_pmf(m, q, i));
+    double t = exp(log_pmf(m, q, r));
+    double s = t;
+    const double ratio_q = q / (1.0 - q);
+    for (int64_t i = r; i < m; ++i) {
+        t *= (double)(m - i) / (double)(i + 1) * ratio_q;
         s += t;
         if ((double)i > (double)m * q && t < 1e-20 * s)
             break;
         if (s > 1.0)
-            break;
+            return 1.0;
     }
     return std::min(s, 1.0);
 }
 
 // Lower rank: largest r >= 1 with P(X <= r-1) <= delta, else 0 (= -inf).
-int64_t lower_rank(int64_t m, double q, double z)
+int64_t lower_rank_exact(int64_t m, double q, double z)
 {
     const double delta = 0.5 * erfc(z / sqrt(2.0));
     const double sd = sqrt((double)m * q * (1.0 - q));
@@ -154,7 +163,7 @@ int64_t lower_rank(int64_t m, double q, double z)
 }
 
 // Upper rank: smallest r <= m with P(X >= r) <= delta, else m + 1 (= +inf).
-int64_t upper_rank(int64_t m, double q, double z)
+int64_t upper_rank_exact(int64_t m, double q, double z)
 {
     const double delta = 0.5 * erfc(z / sqrt(2.0));
     const double sd = sqrt((double)m * q * (1.0 - q));
@@ -165,6 +174,52 @@ int64_t upper_rank(int64_t m, double q, double z)
     while (r - 1 >= 1 && sf_ge(m, q, r - 1) <= delta)
         --r;
     return r;
+}
+
+// The ranks depend only on (m, q, z); a small per-thread cache keeps the
+// tail sums off the per-call path.
+struct RankMemo {
+    int64_t m;
+    double q, z;
+    int64_t rl, rr;
+    bool used;
+};
+thread_local RankMemo g_rank_memo[8];
+thread_local int g_rank_next = 0;
+
+void bracket_ranks(int64_t m, double q, double z, int64_t* rl, int64_t* rr)
+{
+    for (const RankMemo& e : g_rank_memo) {
+        if (e.used && e.m == m && e.q == q && e.z == z) {
+            *rl = e.rl;
+            *rr = e.rr;
+            return;
+        }
+    }
+    RankMemo& e = g_rank_memo[g_rank_next];
+    g_rank_next = (g_rank_next + 1) % 8;
+    e.m = m;
+    e.q = q;
+    e.z = z;
+    e.rl = lower_rank_exact(m, q, z);
+    e.rr = upper_rank_exact(m, q, z);
+    e.used = true;
+    *rl = e.rl;
+    *rr = e.rr;
+}
+
+int64_t lower_rank(int64_t m, double q, double z)
+{
+    int64_t a, b;
+    bracket_ranks(m, q, z, &a, &b);
+    return a;
+}
+
+int64_t upper_rank(int64_t m, double q, double z)
+{
+    int64_t a, b;
+    bracket_ranks(m, q, z, &a, &b);
+    return b;
 }
 
 void pilot_ranks(int32_t m, double q, int64_t rl, int64_t rr, int32_t* plo, int32_t* phi)
@@ -199,19 +254,54 @@ struct Ctx {
     Plan plan;
     hipStream_t stream;
     Status* st;
+    uint64_t seed;
 };
+
+// Two pinned status slots per host thread: slot 0 is filled right after the
+// segment solve (the bracket certificate), slot 1 after the certification
+// pass (the fp64 mass).  Each copy is followed by an event the host can wait
+// on without draining the rest of the stream.
+struct HostSlots {
+    Status* pinned = nullptr;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+};
+thread_local HostSlots g_host;
+
+int ensure_host_slots()
+{
+    if (!g_host.pinned) {
+        void* ptr = nullptr;
+        STK_HIP(hipHostMalloc(&ptr, 2 * sizeof(Status), hipHostMallocDefault));
+        g_host.pinned = static_cast<Status*>(ptr);
+        for (int i = 0; i < 2; ++i)
+            STK_HIP(hipEventCreateWithFlags(&g_host.ev[i], hipEventDisableTiming));
+    }
+    return SOFT_TOPK_OK;
+}
+
+int enqueue_status_copy(const Ctx& x, int slot)
+{
+    int rc = ensure_host_slots();
+    if (rc)
+        return rc;
+    STK_HIP(hipMemcpyAsync(g_host.pinned + slot, x.st, sizeof(Status), hipMemcpyDeviceToHost, x.stream));
+    STK_HIP(hipEventRecord(g_host.ev[slot], x.stream));
+    return SOFT_TOPK_OK;
+}
+
+int wait_status(int slot, Status* host)
+{
+    STK_HIP(hipEventSynchronize(g_host.ev[slot]));
+    memcpy(host, g_host.pinned + slot, sizeof(Status));
+    return SOFT_TOPK_OK;
+}
 
 int read_status(const Ctx& x, Status* host)
 {
-    if (!g_pinned) {
-        void* ptr = nullptr;
-        STK_HIP(hipHostMalloc(&ptr, sizeof(Status), hipHostMallocDefault));
-        g_pinned = static_cast<Status*>(ptr);
-    }
-    STK_HIP(hipMemcpyAsync(g_pinned, x.st, sizeof(Status), hipMemcpyDeviceToHost, x.stream));
-    STK_HIP(hipStreamSynchronize(x.stream));
-    memcpy(host, g_pinned, sizeof(Status));
-    return SOFT_TOPK_OK;
+    int rc = enqueue_status_copy(x, 0);
+    if (rc)
+        return rc;
+    return wait_status(0, host);
 }
 
 template <typename T>
@@ -254,20 +344,30 @@ int enqueue_emit(const Ctx& x)
 // One bracketed round: select with ranks (rl, rr), pass-1, band sort, solve, emit.
 int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q)
 {
-    SelectArgs sa;
-    sa.samples = at<float>(x, x.plan.off_samples);
+    SampleArgs sa;
+    sa.s = x.s;
+    sa.n = x.n;
+    sa.alpha = (float)x.alpha;
+    sa.k0 = (uint32_t)(x.seed & 0xffffffffu);
+    sa.k1 = (uint32_t)(x.seed >> 32);
     sa.m = x.plan.m;
-    sa.r_left = rl;
-    sa.r_right = rr;
     pilot_ranks(x.plan.m, q, rl, rr, &sa.pilot_lo, &sa.pilot_hi);
+    sa.cand = at<uint32_t>(x, x.plan.off_samples);
     sa.st = x.st;
-    STK_HIP(launch_select(sa, x.stream));
+    SelectArgs se;
+    se.cand = sa.cand;
+    se.m = x.plan.m;
+    se.r_left = rl;
+    se.r_right = rr;
+    se.st = x.st;
+    STK_HIP(launch_localize(sa, se, x.stream));
     int rc = enqueue_pass1(x);
     if (rc)
         return rc;
     BandArgs ba;
     ba.p1 = at<Pass1Partial>(x, x.plan.off_p1part);
     ba.p1_blocks = x.plan.g_stream;
+    ba.p1_super = at<Pass1Partial>(x, x.plan.off_super);
     ba.band = at<float>(x, x.plan.off_band);
     ba.band_sorted = at<float>(x, x.plan.off_band_sorted);
     ba.cap = x.plan.cap;
@@ -281,6 +381,7 @@ int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q)
     SolveArgs so;
     so.p1 = ba.p1;
     so.p1_blocks = ba.p1_blocks;
+    so.p1_super = ba.p1_super;
     so.sorted = ba.band_sorted;
     so.agg = ba.agg;
     so.scan = at<GroupScan>(x, x.plan.off_scan);
@@ -293,22 +394,18 @@ int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q)
     so.out_b = x.b;
     so.st = x.st;
     STK_HIP(launch_solve(so, x.stream));
-    return enqueue_emit(x);
+    return SOFT_TOPK_OK;
 }
 
-int enqueue_fullsort(const Ctx& x, const Status& last, bool have_range)
+int enqueue_fullsort(const Ctx& x, const Status& range)
 {
-    STK_HIP(launch_reset_status(x.st, x.stream, false));
-    uint32_t kmin = 0;
-    int passes = 4;
-    if (have_range) {
-        kmin = host_key(last.smin);
-        const uint32_t span = host_key(last.smax) - kmin;
-        int bits = 0;
-        while (bits < 32 && (span >> bits) != 0)
-            ++bits;
-        passes = std::max(1, (bits + 7) / 8);
-    }
+    // sort only the key bits that vary between the smallest and largest score
+    const uint32_t kmin = host_key(range.smin);
+    const uint32_t span = host_key(range.smax) - kmin;
+    int bits = 0;
+    while (bits < 32 && (span >> bits) != 0)
+        ++bits;
+    const int passes = std::max(1, (bits + 7) / 8);
     RadixArgs ra;
     ra.s = x.s;
     ra.n = x.n;
@@ -333,6 +430,7 @@ int enqueue_fullsort(const Ctx& x, const Status& last, bool have_range)
     SolveArgs so;
     so.p1 = nullptr;
     so.p1_blocks = 0;
+    so.p1_super = nullptr;
     so.sorted = reinterpret_cast<const float*>(sorted);
     so.agg = ta.agg;
     so.scan = at<GroupScan>(x, x.plan.off_scan);
@@ -345,7 +443,21 @@ int enqueue_fullsort(const Ctx& x, const Status& last, bool have_range)
     so.out_b = x.b;
     so.st = x.st;
     STK_HIP(launch_solve(so, x.stream));
-    return enqueue_emit(x);
+    return SOFT_TOPK_OK;
+}
+
+// After a solve: snapshot the certificate (slot 0), enqueue the emission and
+// its fp64 mass sum, snapshot again (slot 1).  The host then waits on slot 0
+// only, unless the mass must gate the result.
+int enqueue_certify_emit(const Ctx& x)
+{
+    int rc = enqueue_status_copy(x, 0);
+    if (rc)
+        return rc;
+    rc = enqueue_emit(x);
+    if (rc)
+        return rc;
+    return enqueue_status_copy(x, 1);
 }
 
 bool mass_ok(const Status& h, double k, double tol)
@@ -363,15 +475,15 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     p.m = m;
     p.cap = cap;
     p.g_stream = stream_blocks(n);
-    p.g_band = (int32_t)std::max<int64_t>(1, (cap + kBandChunk - 1) / kBandChunk);
+    p.g_band = kBandGroups;
     p.n_tiles = (int32_t)((n + kTile - 1) / kTile);
     p.g_radix = (int32_t)((n + kRadixTile - 1) / kRadixTile);
     const int64_t groups = std::max<int64_t>(kBuckets, p.n_tiles);
     size_t o = 0;
     p.off_status = o;
     o = align_up(o + sizeof(Status));
-    p.off_samples = o;
-    o = align_up(o + sizeof(float) * (size_t)m);
+    p.off_samples = o;  // candidate keys of the localisation
+    o = align_up(o + sizeof(uint32_t) * (size_t)kCandCap);
     p.off_p1part = o;
     o = align_up(o + sizeof(Pass1Partial) * (size_t)p.g_stream);
     p.off_band = o;
@@ -394,6 +506,8 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     o = align_up(o + sizeof(uint32_t) * (size_t)n);
     p.off_rhist = o;
     o = align_up(o + sizeof(uint32_t) * kRadixBins * (size_t)((p.g_radix + 3) & ~3));
+    p.off_super = o;
+    o = align_up(o + sizeof(Pass1Partial) * (size_t)kBuckets);
     p.total = o;
     return p;
 }
@@ -506,26 +620,31 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
     x.plan = plan;
     x.stream = static_cast<hipStream_t>(stream);
     x.st = reinterpret_cast<Status*>(x.ws + plan.off_status);
+    x.seed = prm.seed;
 
     const double tol = prm.mass_tolerance > 0.0 ? prm.mass_tolerance : 1e-3 + 1e-12 * (double)n;
     soft_topk_stats sx;
     memset(&sx, 0, sizeof(sx));
     Status h;
     memset(&h, 0, sizeof(h));
-    bool have_range = false;
     bool done = false;
+    // the fp64 mass of the emitted p gates the return only on request (or
+    // when the caller wants the stats); the exact bracket certificate always
+    // does
+    const bool wait_mass = prm.verify_mass != 0 || stats != nullptr;
 
     if (prm.force_path != SOFT_TOPK_PATH_FULLSORT) {
         const double q = 1.0 - k / (double)n;
         int64_t rl = lower_rank(plan.m, q, prm.z);
         int64_t rr = upper_rank(plan.m, q, prm.z);
-        STK_HIP(launch_sample(x.s, n, (float)alpha, prm.seed, plan.m, at<float>(x, plan.off_samples), x.st,
-                              x.stream));
         for (int round = 0; round <= prm.max_widen && !done; ++round) {
             int rc = enqueue_round(x, rl, rr, q);
             if (rc)
                 return rc;
-            rc = read_status(x, &h);
+            rc = enqueue_certify_emit(x);
+            if (rc)
+                return rc;
+            rc = wait_status(0, &h);
             if (rc)
                 return rc;
             sx.rounds = round + 1;
@@ -536,13 +655,21 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
             sx.n_band = (int64_t)h.nB;
             sx.mass_at_left = h.massL;
             sx.mass_at_right = h.massR;
-            have_range = true;
             if (h.nonfinite)
                 return SOFT_TOPK_ENONFINITE;
-            if (h.solve_state == kSolveOk && mass_ok(h, k, tol)) {
-                sx.path = round == 0 ? SOFT_TOPK_PATH_BRACKET : SOFT_TOPK_PATH_WIDENED;
-                done = true;
-                break;
+            if (h.solve_state == kSolveOk) {
+                if (wait_mass) {
+                    rc = wait_status(1, &h);
+                    if (rc)
+                        return rc;
+                }
+                if (!wait_mass || mass_ok(h, k, tol)) {
+                    sx.path = round == 0 ? SOFT_TOPK_PATH_BRACKET : SOFT_TOPK_PATH_WIDENED;
+                    done = true;
+                    break;
+                }
+                sx.reject_mask |= SOFT_TOPK_REJECT_MASS;
+                break;  // the certified b failed the mass check: full sort
             }
             if (h.solve_state == kSolveRejectLow) {
                 sx.reject_mask |= SOFT_TOPK_REJECT_LOW;
@@ -567,39 +694,42 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
                 sx.reject_mask |= SOFT_TOPK_REJECT_OVERFLOW;
             else if (h.solve_state == kSolveBucketOverflow)
                 sx.reject_mask |= SOFT_TOPK_REJECT_BUCKET;
-            else
-                sx.reject_mask |= SOFT_TOPK_REJECT_MASS;
             break;  // widening cannot help: go to the full sort
         }
-    } else {
-        // no bracketed round ran: one pass-1 with an empty band
-        // (a_L = a_R = +inf) gives the score range and the finiteness check
-        STK_HIP(launch_reset_status(x.st, x.stream, true));
-        int rc = enqueue_pass1(x);
-        if (rc)
-            return rc;
+    }
+
+    if (!done) {
+        // full-sort route: score range (and finiteness), then the radix sort
+        STK_HIP(launch_reset_status(x.st, x.stream, false));
+        STK_HIP(launch_range(x.s, n, at<Pass1Partial>(x, plan.off_p1part), plan.g_stream, x.stream));
         STK_HIP(launch_pass1_finalize(at<Pass1Partial>(x, plan.off_p1part), plan.g_stream, x.st, x.stream));
-        rc = read_status(x, &h);
+        int rc = read_status(x, &h);
         if (rc)
             return rc;
         if (h.nonfinite)
             return SOFT_TOPK_ENONFINITE;
-        have_range = true;
-    }
-
-    if (!done) {
-        int rc = enqueue_fullsort(x, h, have_range);
+        rc = enqueue_fullsort(x, h);
         if (rc)
             return rc;
-        rc = read_status(x, &h);
+        rc = enqueue_certify_emit(x);
         if (rc)
             return rc;
-        if (h.solve_state != kSolveOk || !mass_ok(h, k, tol))
+        rc = wait_status(0, &h);
+        if (rc)
+            return rc;
+        if (h.solve_state != kSolveOk)
             return SOFT_TOPK_ESOLVE;
+        if (wait_mass) {
+            rc = wait_status(1, &h);
+            if (rc)
+                return rc;
+            if (!mass_ok(h, k, tol))
+                return SOFT_TOPK_ESOLVE;
+        }
         sx.path = SOFT_TOPK_PATH_FULLSORT;
     }
     sx.b = h.b;
-    sx.mass = h.mass;
+    sx.mass = wait_mass ? h.mass : NAN;
     if (stats)
         *stats = sx;
     return SOFT_TOPK_OK;
@@ -642,8 +772,7 @@ int soft_topk_debug_sample(const float* scores, int64_t n, double alpha, uint64_
 {
     if (!scores || !out_samples || !n_ok(n) || m < 1 || m > (1 << 24) || !(alpha > 0.0) || !isfinite(alpha))
         return SOFT_TOPK_EINVAL;
-    STK_HIP(launch_sample(scores, n, (float)alpha, seed, m, out_samples, nullptr,
-                          static_cast<hipStream_t>(stream)));
+    STK_HIP(launch_debug_sample(scores, n, (float)alpha, seed, m, out_samples, static_cast<hipStream_t>(stream)));
     return SOFT_TOPK_OK;
 }
 

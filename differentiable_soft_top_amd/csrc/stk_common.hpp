@@ -165,29 +165,79 @@ __device__ __forceinline__ uint32_t rank_in_mask(uint64_t mask)
 }
 
 // ---------------------------------------------------------------------------
-// Ascending bitonic sort of npow2 u32 keys in LDS by the whole work-group.
-// npow2 must be a power of two; the caller pads with 0xFFFFFFFF.
+// Ascending bitonic sort of npow2 u32 keys in LDS by the whole work-group
+// (npow2 a power of two, at most 2 * kBitonicPairs * blockDim.x; the caller
+// pads with 0xFFFFFFFF and synchronises before the call).  Every stage walks
+// compare-exchange pairs, not indices, so no thread idles, and issues all its
+// pairs' LDS loads before any store.
 // ---------------------------------------------------------------------------
-__device__ inline void lds_bitonic_sort(uint32_t* a, int npow2)
+constexpr int kBitonicPairs = 16;
+
+template <int kPPT>
+__device__ inline void lds_bitonic_sort_ppt(uint32_t* a, int npow2)
 {
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
+    const int pairs = npow2 >> 1;
     for (int k = 2; k <= npow2; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < npow2; i += nt) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint32_t x = a[i];
-                    const uint32_t y = a[ixj];
+            uint32_t x[kPPT], y[kPPT];
+#pragma unroll
+            for (int r = 0; r < kPPT; ++r) {
+                const int p = tid + r * nt;
+                if (p < pairs) {
+                    const int i = 2 * p - (p & (j - 1));  // bit log2(j) of i is 0
+                    x[r] = a[i];
+                    y[r] = a[i + j];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < kPPT; ++r) {
+                const int p = tid + r * nt;
+                if (p < pairs) {
+                    const int i = 2 * p - (p & (j - 1));
                     const bool up = (i & k) == 0;
-                    if ((x > y) == up) {
-                        a[i] = y;
-                        a[ixj] = x;
+                    if ((x[r] > y[r]) == up) {
+                        a[i] = y[r];
+                        a[i + j] = x[r];
                     }
                 }
             }
             __syncthreads();
         }
+    }
+}
+
+// Dispatch on the pairs per thread so no masked-off pair slots are issued.
+__device__ inline void lds_bitonic_sort(uint32_t* a, int npow2)
+{
+    const int ppt = (npow2 / 2 + blockDim.x - 1) / blockDim.x;
+    if (ppt <= 1)
+        lds_bitonic_sort_ppt<1>(a, npow2);
+    else if (ppt <= 2)
+        lds_bitonic_sort_ppt<2>(a, npow2);
+    else if (ppt <= 4)
+        lds_bitonic_sort_ppt<4>(a, npow2);
+    else if (ppt <= 8)
+        lds_bitonic_sort_ppt<8>(a, npow2);
+    else
+        lds_bitonic_sort_ppt<kBitonicPairs>(a, npow2);
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte store, optionally non-temporal (streaming outputs of large vectors:
+// keeps them from crowding the caches ahead of the next pass's reads).
+// ---------------------------------------------------------------------------
+typedef float stk_f4v __attribute__((ext_vector_type(4)));
+
+template <bool kNT>
+__device__ __forceinline__ void store4(float4* p, float4 v)
+{
+    if (kNT) {
+        stk_f4v w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<stk_f4v*>(p));
+    } else {
+        *p = v;
     }
 }
 

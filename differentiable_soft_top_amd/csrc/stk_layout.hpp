@@ -15,15 +15,17 @@ constexpr int kSelectThreads = 1024;     // bracket select, segment solve
 constexpr int kPilot = 2048;             // pilot sample size of the select step
 constexpr int kCandCap = 16384;          // candidate keys held in LDS by the select step
 constexpr int kStageCap = 4096;          // band elements staged in LDS per pass-1 work-group
-constexpr int kBuckets = 2048;           // value buckets of the band sort
+constexpr int kBuckets = 512;            // value buckets of the band sort
 constexpr int kBucketCap = 8192;         // largest bucket sorted in LDS
-constexpr int kBandChunk = 32768;        // band elements per work-group in histogram/scatter
+constexpr int kBandGroups = 128;         // work-groups of band histogram/scatter
+constexpr int kBandChunkMin = 2048;      // band elements per such work-group (at least)
 constexpr int kSortThreads = 256;        // threads of bucket-sort / tile work-groups
 constexpr int kTile = 4096;              // sorted elements per group in the full-sort solve
 constexpr int kRadixThreads = 256;
 constexpr int kRadixKeysPerThread = 32;
 constexpr int kRadixTile = kRadixThreads * kRadixKeysPerThread;  // 8192 keys
 constexpr int kRadixBins = 256;
+constexpr int64_t kNontemporalMin = 1 << 25;  // outputs of at least 128 MiB bypass the caches
 
 // ---- solve status codes (Status::solve_state) ----------------------------
 enum SolveState : uint32_t {
@@ -43,6 +45,8 @@ struct alignas(16) Status {
     float aL, aR;
     uint32_t select_info;        // bit0 pilot candidate overflow, bit1 rank below pilot, bit2 above
     uint32_t cand_count;
+    uint32_t pilot_lo, pilot_hi; // candidate key range from the pilot
+    uint32_t cand_n, below_n;    // candidate append cursor, samples below the range
     // pass-1 totals
     double SL, SR;               // sum_{s<a_L} e^{(s-a_L)/alpha}, sum_{s>=a_R} e^{-(s-a_R)/alpha}
     uint64_t nL, nR;             // tail counts
@@ -110,24 +114,34 @@ struct Plan {
     int32_t n_tiles;             // groups of the full-sort solve
     int32_t g_radix;             // radix tiles
     size_t off_status, off_samples, off_p1part, off_band, off_band_sorted;
-    size_t off_hist, off_bstart, off_agg, off_scan, off_emitpart, off_keys0, off_keys1, off_rhist;
+    size_t off_hist, off_bstart, off_agg, off_scan, off_emitpart, off_keys0, off_keys1, off_rhist, off_super;
     size_t total;
 };
 
 Plan make_plan(int64_t n, int32_t m, int64_t cap);
 
 // ---- host launchers (each enqueues on `stream`, returns the launch status) --
-hipError_t launch_sample(const float* s, int64_t n, float alpha, uint64_t seed, int32_t m,
-                         float* out_samples, Status* st, hipStream_t stream);
-
-struct SelectArgs {
-    const float* samples;
-    int32_t m;
-    int64_t r_left, r_right;      // 1-based target ranks (0 = -inf, m+1 = +inf)
+struct SampleArgs {
+    const float* s;
+    int64_t n;
+    float alpha;
+    uint32_t k0, k1;              // Philox key (seed low / high word)
+    int32_t m;                    // samples
     int32_t pilot_lo, pilot_hi;   // 1-based pilot ranks bounding the targets (0 / P+1 = open)
+    uint32_t* cand;               // [kCandCap] candidate keys
     Status* st;
 };
-hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+struct SelectArgs {
+    const uint32_t* cand;
+    int32_t m;
+    int64_t r_left, r_right;      // 1-based target ranks (0 = -inf, m+1 = +inf)
+    Status* st;
+};
+
+hipError_t launch_localize(const SampleArgs& sa, const SelectArgs& se, hipStream_t stream);
+hipError_t launch_debug_sample(const float* s, int64_t n, float alpha, uint64_t seed, int32_t m,
+                               float* out_samples, hipStream_t stream);
 
 struct Pass1Args {
     const float* s;
@@ -141,10 +155,12 @@ struct Pass1Args {
 };
 hipError_t launch_pass1(const Pass1Args& a, hipStream_t stream);
 hipError_t launch_pass1_finalize(const Pass1Partial* partials, int blocks, Status* st, hipStream_t stream);
+hipError_t launch_range(const float* s, int64_t n, Pass1Partial* partials, int blocks, hipStream_t stream);
 
 struct BandArgs {
     const Pass1Partial* p1;       // pass-1 partials (band range when the bracket is open-ended)
     int32_t p1_blocks;
+    Pass1Partial* p1_super;       // [kBuckets] partials folded by groups of p1_blocks/kBuckets
     const float* band;
     float* band_sorted;
     int64_t cap;
@@ -160,6 +176,7 @@ hipError_t launch_band_sort(const BandArgs& a, hipStream_t stream);
 struct SolveArgs {
     const Pass1Partial* p1;       // pass-1 partials (tails of the bracketed route)
     int32_t p1_blocks;
+    const Pass1Partial* p1_super; // the same folded to kBuckets entries by the band sort
     const float* sorted;          // sorted values
     const GroupAgg* agg;
     GroupScan* scan;              // scratch [groups]

@@ -12,6 +12,7 @@ namespace stk {
 
 enum KernelId : int {
     kKSample = 0,
+    kKPilot,
     kKSelect,
     kKPass1,
     kKBandHist,

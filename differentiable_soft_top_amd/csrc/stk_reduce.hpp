@@ -25,6 +25,7 @@ __device__ inline Pass1Partial reduce_pass1(const Pass1Partial* __restrict__ par
     unsigned long long nL = 0, nR = 0;
     uint32_t nf = 0;
     float bmin = INFINITY, bmax = -INFINITY, smin = INFINITY, smax = -INFINITY;
+#pragma unroll 4
     for (int i = tid; i < blocks; i += blockDim.x) {
         const Pass1Partial p = partials[i];
         SL += p.SL;
