@@ -51,7 +51,38 @@ hipError_t launch_reset_status(Status* st, hipStream_t stream, bool open_bracket
 }
 
 // ---------------------------------------------------------------------------
+// Streaming layout shared by the three kernels below: tiles of kB float4 per
+// lane (kB * kStreamThreads float4 per work-group) taken in grid-stride
+// order, so the resident work-groups sweep the vectors together.  Each tile's
+// loads are all issued before its arithmetic, which then consumes them in
+// arrival order; no load is left in flight across iterations (the compiler's
+// wait counting would otherwise stall on it).  The ragged end (a partial tile
+// and the last n mod 4 scores) goes, element by element, to the work-group
+// whose next tile it would be.  Unaligned vectors take a plain element-wise
+// grid-stride loop.  Large vectors use the larger batch.
 namespace {
+
+template <int kB>
+__device__ __forceinline__ int64_t whole_tiles(int64_t n)
+{
+    return (n >> 2) / (kB * kStreamThreads);
+}
+
+// First element of the ragged end if this work-group owns it, else n.
+template <int kB>
+__device__ __forceinline__ int64_t ragged_start(int64_t n, int64_t T)
+{
+    const int64_t G = gridDim.x;
+    return ((T - (int64_t)blockIdx.x) % G == 0) ? T * (kB * kStreamThreads) * 4 : n;
+}
+
+template <int kB>
+__device__ __forceinline__ void load_q(const float4* __restrict__ p, int64_t t, float4 (&f)[kB])
+{
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+        f[u] = p[t * (kB * kStreamThreads) + u * kStreamThreads + threadIdx.x];
+}
 
 __device__ __forceinline__ float emit_one(float v, double b, double c, double& acc)
 {
@@ -62,9 +93,32 @@ __device__ __forceinline__ float emit_one(float v, double b, double c, double& a
     return (float)p;
 }
 
+// d = e^{-|s-b|/alpha}/2 in fp32 (s - b taken in fp64 first)
+__device__ __forceinline__ float dens(float v, double b, double c)
+{
+    const float y = (float)(fabs((double)v - b) * c);
+    return 0.5f * __builtin_amdgcn_exp2f(-y);
+}
+
+__device__ __forceinline__ void block_sum_to(double v, double* red, double* out)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    v = wave_sum(v);
+    if (lane == 0)
+        red[wave] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        for (int w = 0; w < kStreamThreads / kWave; ++w)
+            t += red[w];
+        *out = t;
+    }
+}
+
 }  // namespace
 
-template <bool kVec, bool kNT>
+template <int kB, bool kVec, bool kNT>
 __global__ __launch_bounds__(kStreamThreads) void emit_kernel(EmitArgs a)
 {
     __shared__ double red[kStreamThreads / kWave];
@@ -72,86 +126,34 @@ __global__ __launch_bounds__(kStreamThreads) void emit_kernel(EmitArgs a)
     if (st->solve_state != kSolveOk)
         return;
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
     const double b = *a.b;
     const double c = a.log2e_over_alpha;
+    const int64_t G = gridDim.x;
     double acc = 0.0;
-
-    const int64_t n4 = a.n >> 2;
-    const int64_t q0 = (n4 * blockIdx.x) / a.blocks;
-    const int64_t q1 = (n4 * (blockIdx.x + 1)) / a.blocks;
-    const float4* s4 = reinterpret_cast<const float4*>(a.s);
-    float4* p4 = reinterpret_cast<float4*>(a.p);
-    int64_t q = q0 + tid;
-    for (; q + 3 * kStreamThreads < q1; q += 4 * kStreamThreads) {
-        float4 v[4];
+    if (kVec) {
+        const int64_t T = whole_tiles<kB>(a.n);
+        const float4* s4 = reinterpret_cast<const float4*>(a.s);
+        float4* p4 = reinterpret_cast<float4*>(a.p);
+        for (int64_t t = blockIdx.x; t < T; t += G) {
+            float4 v[kB];
+            load_q<kB>(s4, t, v);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (kVec) {
-                v[u] = s4[q + u * kStreamThreads];
-            } else {
-                const float* s = a.s + 4 * (q + u * kStreamThreads);
-                v[u] = make_float4(s[0], s[1], s[2], s[3]);
+            for (int u = 0; u < kB; ++u) {
+                float4 o;
+                o.x = emit_one(v[u].x, b, c, acc);
+                o.y = emit_one(v[u].y, b, c, acc);
+                o.z = emit_one(v[u].z, b, c, acc);
+                o.w = emit_one(v[u].w, b, c, acc);
+                store4<kNT>(&p4[t * (kB * kStreamThreads) + u * kStreamThreads + tid], o);
             }
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            float4 o;
-            o.x = emit_one(v[u].x, b, c, acc);
-            o.y = emit_one(v[u].y, b, c, acc);
-            o.z = emit_one(v[u].z, b, c, acc);
-            o.w = emit_one(v[u].w, b, c, acc);
-            if (kVec) {
-                store4<kNT>(&p4[q + u * kStreamThreads], o);
-            } else {
-                float* p = a.p + 4 * (q + u * kStreamThreads);
-                p[0] = o.x;
-                p[1] = o.y;
-                p[2] = o.z;
-                p[3] = o.w;
-            }
-        }
-    }
-    for (; q < q1; q += kStreamThreads) {
-        float4 v;
-        if (kVec) {
-            v = s4[q];
-        } else {
-            const float* s = a.s + 4 * q;
-            v = make_float4(s[0], s[1], s[2], s[3]);
-        }
-        float4 o;
-        o.x = emit_one(v.x, b, c, acc);
-        o.y = emit_one(v.y, b, c, acc);
-        o.z = emit_one(v.z, b, c, acc);
-        o.w = emit_one(v.w, b, c, acc);
-        if (kVec) {
-            store4<kNT>(&p4[q], o);
-        } else {
-            float* p = a.p + 4 * q;
-            p[0] = o.x;
-            p[1] = o.y;
-            p[2] = o.z;
-            p[3] = o.w;
-        }
-    }
-    if (blockIdx.x == a.blocks - 1 && tid < 4) {
-        const int64_t i = 4 * n4 + tid;
-        if (i < a.n)
+        for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads)
+            a.p[i] = emit_one(a.s[i], b, c, acc);
+    } else {
+        for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + tid; i < a.n; i += G * kStreamThreads)
             a.p[i] = emit_one(a.s[i], b, c, acc);
     }
-
-    acc = wave_sum(acc);
-    if (lane == 0)
-        red[wave] = acc;
-    __syncthreads();
-    if (tid == 0) {
-        double t = 0.0;
-        for (int w = 0; w < kStreamThreads / kWave; ++w)
-            t += red[w];
-        a.partials[blockIdx.x] = t;
-    }
+    block_sum_to(acc, red, &a.partials[blockIdx.x]);
 }
 
 // Certification sum: one work-group folds the emission partials in fixed
@@ -159,23 +161,15 @@ __global__ __launch_bounds__(kStreamThreads) void emit_kernel(EmitArgs a)
 __global__ __launch_bounds__(kStreamThreads) void emit_finalize_kernel(EmitArgs a)
 {
     __shared__ double red[kStreamThreads / kWave];
+    __shared__ double m;
     Status* st = a.st;
     if (st->solve_state != kSolveOk)
         return;
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
     double t = 0.0;
-    for (int i = tid; i < a.blocks; i += kStreamThreads)
+    for (int i = threadIdx.x; i < a.blocks; i += kStreamThreads)
         t += a.partials[i];
-    t = wave_sum(t);
-    if (lane == 0)
-        red[wave] = t;
-    __syncthreads();
-    if (tid == 0) {
-        double m = 0.0;
-        for (int w = 0; w < kStreamThreads / kWave; ++w)
-            m += red[w];
+    block_sum_to(t, red, &m);
+    if (threadIdx.x == 0) {
         st->mass = m;
         st->emit_done = 1;
     }
@@ -184,194 +178,112 @@ __global__ __launch_bounds__(kStreamThreads) void emit_finalize_kernel(EmitArgs 
 hipError_t launch_emit(const EmitArgs& a, hipStream_t stream)
 {
     const bool vec = ((reinterpret_cast<uintptr_t>(a.s) | reinterpret_cast<uintptr_t>(a.p)) & 15u) == 0;
-    const bool nt = a.n >= kNontemporalMin;
-    if (vec && nt)
-        STK_LAUNCH(kKEmit, stream, (emit_kernel<true, true>), dim3(a.blocks), dim3(kStreamThreads), 0, stream, a);
-    else if (vec)
-        STK_LAUNCH(kKEmit, stream, (emit_kernel<true, false>), dim3(a.blocks), dim3(kStreamThreads), 0, stream, a);
+    const dim3 grid(a.blocks), block(kStreamThreads);
+    if (!vec)
+        STK_LAUNCH(kKEmit, stream, (emit_kernel<1, false, false>), grid, block, 0, stream, a);
+    else if (a.n >= kNontemporalMin)
+        STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchLarge, true, true>), grid, block, 0, stream, a);
+    else if (a.n >= kStreamLargeMin)
+        STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchLarge, true, false>), grid, block, 0, stream, a);
     else
-        STK_LAUNCH(kKEmit, stream, (emit_kernel<false, false>), dim3(a.blocks), dim3(kStreamThreads), 0, stream, a);
+        STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchSmall, true, false>), grid, block, 0, stream, a);
     STK_LAUNCH(kKEmitFinal, stream, emit_finalize_kernel, dim3(1), dim3(kStreamThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-namespace {
-
-// d = e^{-|s-b|/alpha}/2 in fp32 (s - b taken in fp64 first)
-__device__ __forceinline__ float dens(float v, double b, double c)
-{
-    const float y = (float)(fabs((double)v - b) * c);
-    return 0.5f * __builtin_amdgcn_exp2f(-y);
-}
-
-}  // namespace
-
-template <bool kVec>
+template <int kB, bool kVec>
 __global__ __launch_bounds__(kStreamThreads) void vjp_reduce_kernel(VjpArgs a)
 {
     __shared__ double red[2][kStreamThreads / kWave];
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
     const double b = *a.b;
     const double c = a.log2e_over_alpha;
-    double D = 0.0, G = 0.0;
-    const int64_t n4 = a.n >> 2;
-    const int64_t q0 = (n4 * blockIdx.x) / a.blocks;
-    const int64_t q1 = (n4 * (blockIdx.x + 1)) / a.blocks;
-    const float4* s4 = reinterpret_cast<const float4*>(a.s);
-    const float4* g4 = reinterpret_cast<const float4*>(a.g);
-    int64_t q = q0 + tid;
-    for (; q + kStreamThreads < q1; q += 2 * kStreamThreads) {
-        float4 v0, v1, w0, w1;
-        if (kVec) {
-            v0 = s4[q];
-            v1 = s4[q + kStreamThreads];
-            w0 = g4[q];
-            w1 = g4[q + kStreamThreads];
-        } else {
-            const float* s = a.s + 4 * q;
-            const float* g = a.g + 4 * q;
-            v0 = make_float4(s[0], s[1], s[2], s[3]);
-            w0 = make_float4(g[0], g[1], g[2], g[3]);
-            s += 4 * kStreamThreads;
-            g += 4 * kStreamThreads;
-            v1 = make_float4(s[0], s[1], s[2], s[3]);
-            w1 = make_float4(g[0], g[1], g[2], g[3]);
+    const int64_t G = gridDim.x;
+    double D = 0.0, G_ = 0.0;
+    if (kVec) {
+        const int64_t T = whole_tiles<kB>(a.n);
+        const float4* s4 = reinterpret_cast<const float4*>(a.s);
+        const float4* g4 = reinterpret_cast<const float4*>(a.g);
+        for (int64_t t = blockIdx.x; t < T; t += G) {
+            float4 vs[kB], vg[kB];
+            load_q<kB>(s4, t, vs);
+            load_q<kB>(g4, t, vg);
+            // fp32 within a float4, fp64 across them
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                float d, dsum = 0.f, gsum = 0.f;
+                d = dens(vs[u].x, b, c); dsum += d; gsum += vg[u].x * d;
+                d = dens(vs[u].y, b, c); dsum += d; gsum += vg[u].y * d;
+                d = dens(vs[u].z, b, c); dsum += d; gsum += vg[u].z * d;
+                d = dens(vs[u].w, b, c); dsum += d; gsum += vg[u].w * d;
+                D += (double)dsum;
+                G_ += (double)gsum;
+            }
         }
-        float d;
-        float dsum = 0.f, gsum = 0.f;
-        d = dens(v0.x, b, c); dsum += d; gsum += w0.x * d;
-        d = dens(v0.y, b, c); dsum += d; gsum += w0.y * d;
-        d = dens(v0.z, b, c); dsum += d; gsum += w0.z * d;
-        d = dens(v0.w, b, c); dsum += d; gsum += w0.w * d;
-        d = dens(v1.x, b, c); dsum += d; gsum += w1.x * d;
-        d = dens(v1.y, b, c); dsum += d; gsum += w1.y * d;
-        d = dens(v1.z, b, c); dsum += d; gsum += w1.z * d;
-        d = dens(v1.w, b, c); dsum += d; gsum += w1.w * d;
-        D += (double)dsum;
-        G += (double)gsum;
-    }
-    for (; q < q1; q += kStreamThreads) {
-        float4 v, w;
-        if (kVec) {
-            v = s4[q];
-            w = g4[q];
-        } else {
-            const float* s = a.s + 4 * q;
-            const float* g = a.g + 4 * q;
-            v = make_float4(s[0], s[1], s[2], s[3]);
-            w = make_float4(g[0], g[1], g[2], g[3]);
-        }
-        float d;
-        float dsum = 0.f, gsum = 0.f;
-        d = dens(v.x, b, c); dsum += d; gsum += w.x * d;
-        d = dens(v.y, b, c); dsum += d; gsum += w.y * d;
-        d = dens(v.z, b, c); dsum += d; gsum += w.z * d;
-        d = dens(v.w, b, c); dsum += d; gsum += w.w * d;
-        D += (double)dsum;
-        G += (double)gsum;
-    }
-    if (blockIdx.x == a.blocks - 1 && tid < 4) {
-        const int64_t i = 4 * n4 + tid;
-        if (i < a.n) {
+        for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads) {
             const float d = dens(a.s[i], b, c);
             D += (double)d;
-            G += (double)(a.g[i] * d);
+            G_ += (double)(a.g[i] * d);
+        }
+    } else {
+        for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + tid; i < a.n; i += G * kStreamThreads) {
+            const float d = dens(a.s[i], b, c);
+            D += (double)d;
+            G_ += (double)(a.g[i] * d);
         }
     }
-    D = wave_sum(D);
-    G = wave_sum(G);
-    if (lane == 0) {
-        red[0][wave] = D;
-        red[1][wave] = G;
-    }
+    block_sum_to(D, red[0], &a.partials[2 * blockIdx.x]);
     __syncthreads();
-    if (tid == 0) {
-        double td = 0.0, tg = 0.0;
-        for (int w = 0; w < kStreamThreads / kWave; ++w) {
-            td += red[0][w];
-            tg += red[1][w];
-        }
-        a.partials[2 * blockIdx.x] = td;
-        a.partials[2 * blockIdx.x + 1] = tg;
-    }
+    block_sum_to(G_, red[1], &a.partials[2 * blockIdx.x + 1]);
 }
 
-template <bool kVec, bool kNT>
+template <int kB, bool kVec, bool kNT>
 __global__ __launch_bounds__(kStreamThreads) void vjp_apply_kernel(VjpArgs a, int32_t reduce_blocks)
 {
     __shared__ double red[2][kStreamThreads / kWave];
-    __shared__ float coef[2];
+    __shared__ double tot[2];
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
     // every work-group folds the partials in the same order
-    double D = 0.0, G = 0.0;
+    double D = 0.0, G_ = 0.0;
     for (int i = tid; i < reduce_blocks; i += kStreamThreads) {
         D += a.partials[2 * i];
-        G += a.partials[2 * i + 1];
+        G_ += a.partials[2 * i + 1];
     }
-    D = wave_sum(D);
-    G = wave_sum(G);
-    if (lane == 0) {
-        red[0][wave] = D;
-        red[1][wave] = G;
-    }
+    block_sum_to(D, red[0], &tot[0]);
     __syncthreads();
-    if (tid == 0) {
-        double td = 0.0, tg = 0.0;
-        for (int w = 0; w < kStreamThreads / kWave; ++w) {
-            td += red[0][w];
-            tg += red[1][w];
-        }
-        // every d_i underflowed (alpha tiny next to the gaps around b): the
-        // gradient is then 0 everywhere and the ratio is irrelevant
-        coef[0] = td > 0.0 ? (float)(tg / td) : 0.0f;
-        coef[1] = (float)(1.0 / a.alpha);
-    }
+    block_sum_to(G_, red[1], &tot[1]);
     __syncthreads();
-    const float ratio = coef[0];
-    const float inv_alpha = coef[1];
+    // every d_i underflowed (alpha tiny next to the gaps around b): the
+    // gradient is then 0 everywhere and the ratio is irrelevant
+    const float ratio = tot[0] > 0.0 ? (float)(tot[1] / tot[0]) : 0.0f;
+    const float inv_alpha = (float)(1.0 / a.alpha);
     const double b = *a.b;
     const double c = a.log2e_over_alpha;
-
-    const int64_t n4 = a.n >> 2;
-    const int64_t q0 = (n4 * blockIdx.x) / a.blocks;
-    const int64_t q1 = (n4 * (blockIdx.x + 1)) / a.blocks;
-    const float4* s4 = reinterpret_cast<const float4*>(a.s);
-    const float4* g4 = reinterpret_cast<const float4*>(a.g);
-    float4* o4 = reinterpret_cast<float4*>(a.grad);
-    for (int64_t q = q0 + tid; q < q1; q += kStreamThreads) {
-        float4 v, w;
-        if (kVec) {
-            v = s4[q];
-            w = g4[q];
-        } else {
-            const float* s = a.s + 4 * q;
-            const float* g = a.g + 4 * q;
-            v = make_float4(s[0], s[1], s[2], s[3]);
-            w = make_float4(g[0], g[1], g[2], g[3]);
+    const int64_t G = gridDim.x;
+    if (kVec) {
+        const int64_t T = whole_tiles<kB>(a.n);
+        const float4* s4 = reinterpret_cast<const float4*>(a.s);
+        const float4* g4 = reinterpret_cast<const float4*>(a.g);
+        float4* o4 = reinterpret_cast<float4*>(a.grad);
+        for (int64_t t = blockIdx.x; t < T; t += G) {
+            float4 vs[kB], vg[kB];
+            load_q<kB>(s4, t, vs);
+            load_q<kB>(g4, t, vg);
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                float4 o;
+                o.x = dens(vs[u].x, b, c) * inv_alpha * (vg[u].x - ratio);
+                o.y = dens(vs[u].y, b, c) * inv_alpha * (vg[u].y - ratio);
+                o.z = dens(vs[u].z, b, c) * inv_alpha * (vg[u].z - ratio);
+                o.w = dens(vs[u].w, b, c) * inv_alpha * (vg[u].w - ratio);
+                store4<kNT>(&o4[t * (kB * kStreamThreads) + u * kStreamThreads + tid], o);
+            }
         }
-        float4 o;
-        o.x = dens(v.x, b, c) * inv_alpha * (w.x - ratio);
-        o.y = dens(v.y, b, c) * inv_alpha * (w.y - ratio);
-        o.z = dens(v.z, b, c) * inv_alpha * (w.z - ratio);
-        o.w = dens(v.w, b, c) * inv_alpha * (w.w - ratio);
-        if (kVec) {
-            store4<kNT>(&o4[q], o);
-        } else {
-            float* p = a.grad + 4 * q;
-            p[0] = o.x;
-            p[1] = o.y;
-            p[2] = o.z;
-            p[3] = o.w;
-        }
-    }
-    if (blockIdx.x == a.blocks - 1 && tid < 4) {
-        const int64_t i = 4 * n4 + tid;
-        if (i < a.n)
+        for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads)
+            a.grad[i] = dens(a.s[i], b, c) * inv_alpha * (a.g[i] - ratio);
+    } else {
+        for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + tid; i < a.n; i += G * kStreamThreads)
             a.grad[i] = dens(a.s[i], b, c) * inv_alpha * (a.g[i] - ratio);
     }
 }
@@ -382,18 +294,22 @@ hipError_t launch_vjp(const VjpArgs& a, hipStream_t stream)
                        reinterpret_cast<uintptr_t>(a.grad)) & 15u) == 0;
     VjpArgs r = a;
     r.blocks = a.reduce_blocks;
-    if (vec) {
-        STK_LAUNCH(kKVjpReduce, stream, vjp_reduce_kernel<true>, dim3(r.blocks), dim3(kStreamThreads), 0, stream, r);
+    const dim3 block(kStreamThreads), gr(r.blocks), ga(a.blocks);
+    if (!vec) {
+        STK_LAUNCH(kKVjpReduce, stream, (vjp_reduce_kernel<1, false>), gr, block, 0, stream, r);
+        STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<1, false, false>), ga, block, 0, stream, a, r.blocks);
+    } else if (a.n >= kStreamLargeMin) {
+        STK_LAUNCH(kKVjpReduce, stream, (vjp_reduce_kernel<kVjpBatchLarge, true>), gr, block, 0, stream, r);
         if (a.n >= kNontemporalMin)
-            STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<true, true>), dim3(a.blocks), dim3(kStreamThreads), 0,
-                       stream, a, r.blocks);
+            STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<kVjpBatchLarge, true, true>), ga, block, 0, stream, a,
+                       r.blocks);
         else
-            STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<true, false>), dim3(a.blocks), dim3(kStreamThreads), 0,
-                       stream, a, r.blocks);
+            STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<kVjpBatchLarge, true, false>), ga, block, 0, stream, a,
+                       r.blocks);
     } else {
-        STK_LAUNCH(kKVjpReduce, stream, vjp_reduce_kernel<false>, dim3(r.blocks), dim3(kStreamThreads), 0, stream, r);
-        STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<false, false>), dim3(a.blocks), dim3(kStreamThreads), 0,
-                   stream, a, r.blocks);
+        STK_LAUNCH(kKVjpReduce, stream, (vjp_reduce_kernel<kVjpBatchSmall, true>), gr, block, 0, stream, r);
+        STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<kVjpBatchSmall, true, false>), ga, block, 0, stream, a,
+                   r.blocks);
     }
     return hipGetLastError();
 }

@@ -11,19 +11,23 @@
 // [a_L, a_R] the left tail contributes SL e^{(a_L - b)/alpha} / 2 to M(b) and
 // the right tail nR - SR e^{-(a_R - b)/alpha} / 2.
 //
-// Design for gfx950: one work-group per contiguous chunk, sixteen scores per
-// lane per step (four 16-byte loads in flight).  Classification is fp32
-// compares only.  A tail score contributes 2^y with y = -|s - a|/alpha*log2e;
-// below y = -50 the term is under 2^-50 and is dropped (all dropped terms
-// together stay below n * 2^-50 < 2e-6, far under the mass tolerance), so only
-// "near" tail scores need the fp64 exponential.  Each lane queues its near
-// scores in its own LDS list and the wave then runs the exponential over the
-// queues with every lane busy, instead of paying it for every score.  Band
-// scores are queued in the same per-lane list (from the other end) and
-// appended with one LDS reservation per wave and step into a work-group
-// stage, flushed with one global reservation per work-group.  Counts are
-// exact; sums are fp64; per-group partials are folded in fixed order by the
-// consumer.
+// Design for gfx950: the score vector is cut into tiles of 4096 scores
+// (sixteen per lane: four 16-byte loads) taken in grid-stride order, so the
+// resident work-groups sweep the vector together; two tiles' loads are issued
+// at once and the first is classified while the second is in flight.  A tail score contributes
+// 2^y with y = -|s - a|/alpha*log2e; below y = -50 the term is under 2^-50
+// and is dropped (all dropped terms together stay below n * 2^-50 < 2e-6, far
+// under the mass tolerance).  So a score is either "far" (s < t_L or
+// s >= t_R: only counted, two fp32 compares and two carry adds) or inside the
+// window [t_L, t_R), which holds the near tails and the band.  Window scores
+// are compacted per wave into an LDS list (mask ranks, one store), and the
+// wave then walks that list 64 at a time: near tail scores get the fp64
+// exponential with every lane busy, band scores are appended with one LDS
+// reservation per wave into a work-group stage, flushed with one global
+// reservation per work-group.  A NaN compares false both ways, so it lands in
+// the window list and is flagged there; +-inf is caught by max |s|.  Counts
+// are exact; sums are fp64; per-group partials are folded in fixed order by
+// the consumer.
 #include "stk_common.hpp"
 #include "stk_layout.hpp"
 #include "stk_prof.hpp"
@@ -33,70 +37,51 @@ namespace stk {
 
 namespace {
 
-constexpr int kVals = 16;           // scores per lane per step
-constexpr int kLaneSlots = 17;      // per-lane LDS list (stride 17: no bank conflicts)
-constexpr double kTailCut = 50.0;   // tail terms below 2^-50 are dropped
-constexpr int kP1Stage = 2048;      // band scores staged per work-group
-
-struct Lanes {
-    float* stage;                   // LDS [kP1Stage]
-    uint32_t* stage_count;          // LDS reservation counter
-    float* my;                      // this lane's LDS list [kLaneSlots]
-};
+constexpr int kVals = 16;                       // scores per lane per tile
+constexpr int kTileQ = kStreamThreads * kVals / 4;  // float4 per tile
+constexpr int kWin = kWave * kVals;             // window list per wave (worst case)
+constexpr int kWaves1 = kStreamThreads / kWave;
+constexpr double kTailCut = 50.0;               // tail terms below 2^-50 are dropped
+constexpr int kP1Stage = 2048;                  // band scores staged per work-group
 
 struct Ctx1 {
     float aL, aR, tL, tR;
     double daL, daR, c;
-    bool open;                      // a bracket end is infinite: track the band range
+    bool open;                                  // a bracket end is infinite: track the band range
     float* band;
     int64_t cap;
     unsigned long long* nB;
+    float* stage;                               // LDS [kP1Stage]
+    uint32_t* stage_count;                      // LDS reservation counter
+    float* win;                                 // this wave's LDS window list [kWin]
 };
 
 struct Acc1 {
     double SL, SR;
-    uint32_t nL, nR;
+    uint32_t nL, nR;                            // per-lane tail counts
     float bmin, bmax;
-    float nf;                       // stays 0 unless a score is NaN or +-inf
+    float amax;                                 // max |s| (+-inf shows here)
+    uint32_t nan;                               // a NaN reached the window list
 };
 
-// Classify up to 16 scores of this lane (v[i] valid iff bit i of `valid`;
-// kAll: all valid), fold near tail scores into the fp64 sums and append band
-// scores.  Called by every lane of the wave (the ballots and the reservation
-// are per wave).
-//
-// The per-lane list holds near scores from slot 0 up and band scores from
-// slot 16 down; both are stored unconditionally at their next free slot and
-// committed by bumping the count, which keeps the classification loop free of
-// branches (a speculative store only ever lands on a free slot: after i
-// scores nn + nb <= i, so the next near slot nn and the next band slot 16-nb
-// never reach a committed entry of the other list).
-template <bool kAll>
-__device__ __forceinline__ void step16(const float (&v)[kVals], uint32_t valid, const Ctx1& x, Acc1& acc,
-                                       const Lanes& L)
+// Walk this wave's window list: near tail scores into the fp64 sums, band
+// scores into the stage (or the global band past the stage).
+__device__ __forceinline__ void drain_window(uint32_t cnt, const Ctx1& x, Acc1& acc)
 {
-    uint32_t nn = 0, nb = 0;
-#pragma unroll
-    for (int i = 0; i < kVals; ++i) {
-        const bool ok = kAll || ((valid >> i) & 1u);
-        const float s = v[i];
+    const int lane = lane_id();
+    __builtin_amdgcn_wave_barrier();
+    for (uint32_t base = 0; base < cnt; base += kWave) {
+        const uint32_t j = base + (uint32_t)lane;
+        const bool ok = j < cnt;
+        const float s = ok ? x.win[j] : 0.f;
         const bool left = ok && s < x.aL;
         const bool right = ok && s >= x.aR;
-        const bool band = ok && !(s < x.aL) && !(s >= x.aR);
+        const bool nan = ok && s != s;
+        const bool band = ok && !left && !right && !nan;
         acc.nL += left ? 1u : 0u;
         acc.nR += right ? 1u : 0u;
-        const bool near = (left && s >= x.tL) || (right && s < x.tR);
-        L.my[nn] = s;
-        nn += near ? 1u : 0u;
-        L.my[kLaneSlots - 1 - nb] = s;
-        nb += band ? 1u : 0u;
-        acc.nf = fmaf(s, 0.f, acc.nf);
-    }
-    // fp64 exponentials of the queued near scores, every lane busy
-    for (uint32_t j = 0; __ballot(j < nn) != 0; ++j) {
-        if (j < nn) {
-            const float s = L.my[j];
-            const bool left = s < x.aL;
+        acc.nan |= nan ? 1u : 0u;
+        if (left || right) {
             const double d = left ? (double)s - x.daL : x.daR - (double)s;
             const double e = exp2_nonpos(d * x.c);
             if (left)
@@ -104,47 +89,90 @@ __device__ __forceinline__ void step16(const float (&v)[kVals], uint32_t valid, 
             else
                 acc.SR += e;
         }
-    }
-    // band append: lane offsets from the bit planes of nb (<= 16)
-    uint32_t prefix = 0, total = 0;
-#pragma unroll
-    for (int b = 0; b < 5; ++b) {
-        const uint64_t m = __ballot((nb >> b) & 1u);
-        prefix += rank_in_mask(m) << b;
-        total += (uint32_t)__popcll(m) << b;
-    }
-    if (total == 0)
-        return;
-    const int lane = lane_id();
-    uint32_t base = 0;
-    if (lane == 0)
-        base = atomicAdd(L.stage_count, total);
-    base = __shfl(base, 0, kWave);
-    // reservations past the LDS stage go straight to the global band
-    const uint32_t first_over = base > (uint32_t)kP1Stage ? base : (uint32_t)kP1Stage;
-    const uint32_t end = base + total;
-    const uint32_t n_over = end > first_over ? end - first_over : 0u;
-    unsigned long long gbase = 0;
-    if (n_over) {
+        const uint64_t mb = __builtin_amdgcn_ballot_w64(band);
+        if (mb == 0)
+            continue;
+        const uint32_t total = (uint32_t)__popcll(mb);
+        uint32_t sbase = 0;
         if (lane == 0)
-            gbase = atomicAdd(x.nB, (unsigned long long)n_over);
-        gbase = __shfl(gbase, 0, kWave);
-    }
-    for (uint32_t k = 0; k < nb; ++k) {
-        const uint32_t pos = base + prefix + k;
-        const float s = L.my[kLaneSlots - 1 - k];
-        if (x.open) {
-            acc.bmin = fminf(acc.bmin, s);
-            acc.bmax = fmaxf(acc.bmax, s);
+            sbase = atomicAdd(x.stage_count, total);
+        sbase = __shfl(sbase, 0, kWave);
+        // reservations past the LDS stage go straight to the global band
+        const uint32_t first_over = sbase > (uint32_t)kP1Stage ? sbase : (uint32_t)kP1Stage;
+        const uint32_t end = sbase + total;
+        const uint32_t n_over = end > first_over ? end - first_over : 0u;
+        unsigned long long gbase = 0;
+        if (n_over) {
+            if (lane == 0)
+                gbase = atomicAdd(x.nB, (unsigned long long)n_over);
+            gbase = __shfl(gbase, 0, kWave);
         }
-        if (pos < (uint32_t)kP1Stage) {
-            L.stage[pos] = s;
-        } else {
-            const uint64_t g = (uint64_t)gbase + (pos - first_over);
-            if (g < (uint64_t)x.cap)
-                x.band[g] = s;
+        if (band) {
+            const uint32_t pos = sbase + rank_in_mask(mb);
+            if (x.open) {
+                acc.bmin = fminf(acc.bmin, s);
+                acc.bmax = fmaxf(acc.bmax, s);
+            }
+            if (pos < (uint32_t)kP1Stage) {
+                x.stage[pos] = s;
+            } else {
+                const uint64_t g = (uint64_t)gbase + (pos - first_over);
+                if (g < (uint64_t)x.cap)
+                    x.band[g] = s;
+            }
         }
     }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Classify kVals scores of this lane (kAll: all valid, else bit i of
+// `valid`).  Far scores are counted; window scores are compacted into the
+// wave's list, which is then drained.  Called by every lane of the wave.
+template <bool kAll>
+__device__ __forceinline__ void classify(const float (&v)[kVals], uint32_t valid, const Ctx1& x, Acc1& acc)
+{
+    uint32_t cnt = 0;  // wave-uniform fill of the window list
+    const uint64_t live = __builtin_amdgcn_ballot_w64(true);
+#pragma unroll
+    for (int i = 0; i < kVals; ++i) {
+        const bool ok = kAll || ((valid >> i) & 1u);
+        const float s = v[i];
+        const bool lo = s < x.tL;
+        const bool hi = s >= x.tR;
+        acc.nL += (ok && lo) ? 1u : 0u;
+        acc.nR += (ok && hi) ? 1u : 0u;
+        acc.amax = fmaxf(acc.amax, ok ? fabsf(s) : 0.f);
+        // window mask from the ballots of the two compares (stays scalar)
+        uint64_t m = ~(__builtin_amdgcn_ballot_w64(lo) | __builtin_amdgcn_ballot_w64(hi)) & live;
+        if (!kAll)
+            m &= __builtin_amdgcn_ballot_w64(ok);
+        if (ok && !lo && !hi)  // this lane's bit of m
+            x.win[cnt + rank_in_mask(m)] = s;
+        cnt += (uint32_t)__popcll(m);
+    }
+    drain_window(cnt, x, acc);
+}
+
+template <int kU>
+__device__ __forceinline__ void classify_q(const float4 (&f)[kU], const Ctx1& x, Acc1& acc)
+{
+    float v[kVals];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        v[4 * u + 0] = f[u].x;
+        v[4 * u + 1] = f[u].y;
+        v[4 * u + 2] = f[u].z;
+        v[4 * u + 3] = f[u].w;
+    }
+    classify<true>(v, 0xFFFFu, x, acc);
+}
+
+template <int kU>
+__device__ __forceinline__ void load_tile(const float4* __restrict__ s4, int64_t t, float4 (&f)[kU])
+{
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+        f[u] = s4[t * (kU * kStreamThreads) + u * kStreamThreads + threadIdx.x];
 }
 
 }  // namespace
@@ -153,12 +181,12 @@ template <bool kVec>
 __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
 {
     __shared__ float stage_buf[kP1Stage];
-    __shared__ float lists[kStreamThreads * kLaneSlots];
+    __shared__ float win_buf[kWaves1][kWin];
     __shared__ uint32_t stage_count;
     __shared__ unsigned long long stage_base;
-    __shared__ double red_d[2][kStreamThreads / kWave];
-    __shared__ uint32_t red_u[3][kStreamThreads / kWave];
-    __shared__ float red_f[2][kStreamThreads / kWave];
+    __shared__ double red_d[2][kWaves1];
+    __shared__ uint32_t red_u[3][kWaves1];
+    __shared__ float red_f[3][kWaves1];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -175,7 +203,7 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
     x.daL = x.aL;
     x.daR = x.aR;
     x.c = a.log2e_over_alpha;
-    // near thresholds in fp32, rounded outward so no term >= 2^-50 is dropped
+    // window ends in fp32, rounded outward so no term >= 2^-50 is dropped
     const double cut = kTailCut / x.c;
     x.tL = (float)(x.daL - cut);
     if ((double)x.tL > x.daL - cut)
@@ -187,72 +215,65 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
     x.band = a.band;
     x.cap = a.cap;
     x.nB = reinterpret_cast<unsigned long long*>(&st->nB);
-    Lanes L{stage_buf, &stage_count, lists + tid * kLaneSlots};
+    x.stage = stage_buf;
+    x.stage_count = &stage_count;
+    x.win = win_buf[wave];
 
-    Acc1 acc{0.0, 0.0, 0u, 0u, INFINITY, -INFINITY, 0.f};
+    Acc1 acc{0.0, 0.0, 0u, 0u, INFINITY, -INFINITY, 0.f, 0u};
+    const int64_t G = gridDim.x;
+    int64_t rest = 0;  // first score not covered by whole tiles
 
-    const int64_t n4 = a.n >> 2;
-    const int64_t q0 = (n4 * blockIdx.x) / a.blocks;
-    const int64_t q1 = (n4 * (blockIdx.x + 1)) / a.blocks;
-    const float4* s4 = reinterpret_cast<const float4*>(a.s);
-
-    // uniform trip count: every lane runs every step (ballots see whole waves)
-    int64_t qb = q0;
-    for (; qb + 4 * kStreamThreads <= q1; qb += 4 * kStreamThreads) {
-        float v[kVals];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t q = qb + u * kStreamThreads + tid;
-            float4 f;
-            if (kVec) {
-                f = s4[q];
-            } else {
-                const float* p = a.s + 4 * q;
-                f = make_float4(p[0], p[1], p[2], p[3]);
-            }
-            v[4 * u + 0] = f.x;
-            v[4 * u + 1] = f.y;
-            v[4 * u + 2] = f.z;
-            v[4 * u + 3] = f.w;
+    if (kVec) {
+        const int64_t n4 = a.n >> 2;
+        const int64_t T = n4 / kTileQ;
+        const float4* s4 = reinterpret_cast<const float4*>(a.s);
+        constexpr int kU = kVals / 4;
+        // each step issues the loads of two tiles (eight 16-byte loads per
+        // lane) and classifies the first while the second is in flight
+        int64_t t = blockIdx.x;
+        for (; t + G < T; t += 2 * G) {
+            float4 fa[kU], fb[kU];
+            load_tile<kU>(s4, t, fa);
+            load_tile<kU>(s4, t + G, fb);
+            classify_q<kU>(fa, x, acc);
+            classify_q<kU>(fb, x, acc);
         }
-        step16<true>(v, 0xFFFFu, x, acc, L);
+        if (t < T) {
+            float4 fa[kU];
+            load_tile<kU>(s4, t, fa);
+            classify_q<kU>(fa, x, acc);
+        }
+        rest = T * (int64_t)kTileQ * 4;
+        // the ragged end (a partial tile and the last n mod 4 scores) goes to
+        // the work-group whose next tile it would be
+        if ((T - (int64_t)blockIdx.x) % G != 0)
+            rest = a.n;
+    } else {
+        // unaligned scores: plain grid-stride over scalar loads
+        for (int64_t i0 = (int64_t)blockIdx.x * (kStreamThreads * kVals); i0 < a.n;
+             i0 += G * (kStreamThreads * kVals)) {
+            float v[kVals];
+            uint32_t valid = 0;
+#pragma unroll
+            for (int k = 0; k < kVals; ++k) {
+                const int64_t i = i0 + (int64_t)k * kStreamThreads + tid;
+                v[k] = i < a.n ? a.s[i] : 0.f;
+                valid |= (i < a.n ? 1u : 0u) << k;
+            }
+            classify<false>(v, valid, x, acc);
+        }
+        rest = a.n;
     }
-    if (qb < q1) {
+    for (int64_t i0 = rest; i0 < a.n; i0 += kStreamThreads * kVals) {
         float v[kVals];
         uint32_t valid = 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t q = qb + u * kStreamThreads + tid;
-            float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (q < q1) {
-                if (kVec) {
-                    f = s4[q];
-                } else {
-                    const float* p = a.s + 4 * q;
-                    f = make_float4(p[0], p[1], p[2], p[3]);
-                }
-                valid |= 0xFu << (4 * u);
-            }
-            v[4 * u + 0] = f.x;
-            v[4 * u + 1] = f.y;
-            v[4 * u + 2] = f.z;
-            v[4 * u + 3] = f.w;
+        for (int k = 0; k < kVals; ++k) {
+            const int64_t i = i0 + (int64_t)k * kStreamThreads + tid;
+            v[k] = i < a.n ? a.s[i] : 0.f;
+            valid |= (i < a.n ? 1u : 0u) << k;
         }
-        step16<false>(v, valid, x, acc, L);
-    }
-    // the last 0..3 scores when n is not a multiple of 4
-    if (blockIdx.x == a.blocks - 1) {
-        const int64_t i = 4 * n4 + tid;
-        float v[kVals];
-#pragma unroll
-        for (int k = 0; k < kVals; ++k)
-            v[k] = 0.f;
-        uint32_t valid = 0;
-        if (tid < 4 && i < a.n) {
-            v[0] = a.s[i];
-            valid = 1u;
-        }
-        step16<false>(v, valid, x, acc, L);
+        classify<false>(v, valid, x, acc);
     }
 
     // flush the LDS stage with one global reservation
@@ -274,7 +295,7 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
     const double SR = wave_sum(acc.SR);
     const uint32_t nL = wave_sum_u32(acc.nL);
     const uint32_t nR = wave_sum_u32(acc.nR);
-    uint32_t nf = acc.nf != 0.f || acc.nf != acc.nf ? 1u : 0u;
+    uint32_t nf = (acc.nan != 0u || !(acc.amax < INFINITY)) ? 1u : 0u;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         nf |= __shfl_xor(nf, off, kWave);
@@ -300,7 +321,7 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
         p.bmax = -INFINITY;
         p.smin = INFINITY;
         p.smax = -INFINITY;
-        for (int w = 0; w < kStreamThreads / kWave; ++w) {
+        for (int w = 0; w < kWaves1; ++w) {
             p.SL += red_d[0][w];
             p.SR += red_d[1][w];
             p.nL += red_u[0][w];

@@ -45,18 +45,20 @@ int hip_fail(hipError_t e)
             return hip_fail(e_);              \
     } while (0)
 
-int32_t stream_blocks(int64_t n)
+int32_t grid_for(int64_t n, int tile_scores, int cap)
 {
-    const int64_t n4 = n >> 2;
-    int64_t g = (n4 + 511) / 512;
-    g = std::max<int64_t>(1, std::min<int64_t>(g, kStreamMaxBlocks));
-    return (int32_t)g;
+    const int64_t g = (n + tile_scores - 1) / tile_scores;
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(g, cap));
 }
 
-// The (D, G) reduction reads 8 B per score and streams at full rate with few
-// work-groups; fewer partials make the per-work-group fold in the gradient
-// kernel cheaper.
-int32_t vjp_reduce_blocks(int64_t n) { return std::min<int32_t>(stream_blocks(n), 512); }
+int32_t pass1_blocks(int64_t n) { return grid_for(n, kPass1TileScores, kGridPass1); }
+int32_t emit_blocks(int64_t n)
+{
+    return grid_for(n, 4 * kStreamThreads * (n >= kStreamLargeMin ? kEmitBatchLarge : kEmitBatchSmall), kGridEmit);
+}
+int32_t vjp_tile(int64_t n) { return 4 * kStreamThreads * (n >= kStreamLargeMin ? kVjpBatchLarge : kVjpBatchSmall); }
+int32_t vjp_reduce_blocks(int64_t n) { return grid_for(n, vjp_tile(n), kGridVjpReduce); }
+int32_t vjp_apply_blocks(int64_t n) { return grid_for(n, vjp_tile(n), kGridVjpApply); }
 
 int64_t default_cap(int64_t n)
 {
@@ -319,7 +321,7 @@ int enqueue_pass1(const Ctx& x)
     a.band = at<float>(x, x.plan.off_band);
     a.cap = x.plan.cap;
     a.partials = at<Pass1Partial>(x, x.plan.off_p1part);
-    a.blocks = x.plan.g_stream;
+    a.blocks = x.plan.g_pass1;
     a.st = x.st;
     STK_HIP(launch_pass1(a, x.stream));
     return SOFT_TOPK_OK;
@@ -335,7 +337,7 @@ int enqueue_emit(const Ctx& x)
     e.b = x.b;
     e.p = x.p;
     e.partials = at<double>(x, x.plan.off_emitpart);
-    e.blocks = x.plan.g_stream;
+    e.blocks = x.plan.g_emit;
     e.st = x.st;
     STK_HIP(launch_emit(e, x.stream));
     return SOFT_TOPK_OK;
@@ -366,7 +368,7 @@ int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q)
         return rc;
     BandArgs ba;
     ba.p1 = at<Pass1Partial>(x, x.plan.off_p1part);
-    ba.p1_blocks = x.plan.g_stream;
+    ba.p1_blocks = x.plan.g_pass1;
     ba.p1_super = at<Pass1Partial>(x, x.plan.off_super);
     ba.band = at<float>(x, x.plan.off_band);
     ba.band_sorted = at<float>(x, x.plan.off_band_sorted);
@@ -474,7 +476,8 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     p.n = n;
     p.m = m;
     p.cap = cap;
-    p.g_stream = stream_blocks(n);
+    p.g_pass1 = pass1_blocks(n);
+    p.g_emit = emit_blocks(n);
     p.g_band = kBandGroups;
     p.n_tiles = (int32_t)((n + kTile - 1) / kTile);
     p.g_radix = (int32_t)((n + kRadixTile - 1) / kRadixTile);
@@ -485,7 +488,7 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     p.off_samples = o;  // candidate keys of the localisation
     o = align_up(o + sizeof(uint32_t) * (size_t)kCandCap);
     p.off_p1part = o;
-    o = align_up(o + sizeof(Pass1Partial) * (size_t)p.g_stream);
+    o = align_up(o + sizeof(Pass1Partial) * (size_t)p.g_pass1);
     p.off_band = o;
     o = align_up(o + sizeof(float) * (size_t)cap);
     p.off_band_sorted = o;
@@ -499,7 +502,7 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     p.off_scan = o;
     o = align_up(o + sizeof(GroupScan) * (size_t)groups);
     p.off_emitpart = o;
-    o = align_up(o + sizeof(double) * (size_t)p.g_stream);
+    o = align_up(o + sizeof(double) * (size_t)p.g_emit);
     p.off_keys0 = o;
     o = align_up(o + sizeof(uint32_t) * (size_t)n);
     p.off_keys1 = o;
@@ -701,8 +704,8 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
     if (!done) {
         // full-sort route: score range (and finiteness), then the radix sort
         STK_HIP(launch_reset_status(x.st, x.stream, false));
-        STK_HIP(launch_range(x.s, n, at<Pass1Partial>(x, plan.off_p1part), plan.g_stream, x.stream));
-        STK_HIP(launch_pass1_finalize(at<Pass1Partial>(x, plan.off_p1part), plan.g_stream, x.st, x.stream));
+        STK_HIP(launch_range(x.s, n, at<Pass1Partial>(x, plan.off_p1part), plan.g_pass1, x.stream));
+        STK_HIP(launch_pass1_finalize(at<Pass1Partial>(x, plan.off_p1part), plan.g_pass1, x.st, x.stream));
         int rc = read_status(x, &h);
         if (rc)
             return rc;
@@ -761,7 +764,7 @@ int soft_topk_backward(const float* grad_p, const float* scores, int64_t n, doub
     a.b = b;
     a.grad = grad_s;
     a.partials = static_cast<double*>(workspace);
-    a.blocks = stream_blocks(n);
+    a.blocks = vjp_apply_blocks(n);
     a.reduce_blocks = vjp_reduce_blocks(n);
     STK_HIP(launch_vjp(a, static_cast<hipStream_t>(stream)));
     return SOFT_TOPK_OK;

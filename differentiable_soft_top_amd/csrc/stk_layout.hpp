@@ -10,11 +10,24 @@ namespace stk {
 
 // ---- fixed launch shapes -------------------------------------------------
 constexpr int kStreamThreads = 256;      // streaming kernels (pass-1, emit, VJP)
-constexpr int kStreamMaxBlocks = 2048;   // 8 work-groups per CU on 256 CUs
+// Streaming kernels walk tiles in grid-stride order; their grids are capped
+// at these work-group counts (measured on MI355X: a few resident work-groups
+// per CU sweeping the vectors together stream fastest).  Emission and VJP
+// tiles hold kB float4 per lane: the larger batch from kStreamLargeMin
+// scores on, the smaller one below (more work-groups for short vectors).
+constexpr int kPass1TileScores = 4096;   // scores per pass-1 tile
+constexpr int kEmitBatchLarge = 8;
+constexpr int kEmitBatchSmall = 2;
+constexpr int kVjpBatchLarge = 4;
+constexpr int kVjpBatchSmall = 1;
+constexpr int64_t kStreamLargeMin = 1 << 24;
+constexpr int kGridPass1 = 2048;
+constexpr int kGridEmit = 2048;
+constexpr int kGridVjpReduce = 512;
+constexpr int kGridVjpApply = 512;
 constexpr int kSelectThreads = 1024;     // bracket select, segment solve
 constexpr int kPilot = 2048;             // pilot sample size of the select step
 constexpr int kCandCap = 16384;          // candidate keys held in LDS by the select step
-constexpr int kStageCap = 4096;          // band elements staged in LDS per pass-1 work-group
 constexpr int kBuckets = 512;            // value buckets of the band sort
 constexpr int kBucketCap = 8192;         // largest bucket sorted in LDS
 constexpr int kBandGroups = 128;         // work-groups of band histogram/scatter
@@ -109,7 +122,8 @@ struct Plan {
     int64_t n;
     int32_t m;                   // samples
     int64_t cap;                 // band capacity
-    int32_t g_stream;            // work-groups of the streaming kernels
+    int32_t g_pass1;             // work-groups of pass-1 (and of the range pass)
+    int32_t g_emit;              // work-groups of the emission
     int32_t g_band;              // max work-groups of band histogram/scatter
     int32_t n_tiles;             // groups of the full-sort solve
     int32_t g_radix;             // radix tiles
