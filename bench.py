@@ -17,7 +17,14 @@ pre-pass) is bracketed by HIP events on its launch stream during the timed
 steps; achieved = its algorithmic bytes per launch / its mean duration.
 "traffic" comes from profiles/traffic.json (rocprofv3 FETCH_SIZE + WRITE_SIZE
 scaled by a copy kernel of known size) when it was taken from the current
-kernel source, else null.
+kernel source, else null.  That file is written by
+
+    rocprofv3 --pmc FETCH_SIZE -d <dirF> -o f --output-format csv -- python3 bench.py --profile-run
+    rocprofv3 --pmc WRITE_SIZE -d <dirW> -o w --output-format csv -- python3 bench.py --profile-run
+    python bench.py --pmc-summary <dirF>/f_counter_collection.csv <dirW>/w_counter_collection.csv
+
+(--profile-run: a few steps of the workload, then a plain device copy of
+COPY_BYTES bytes whose counter readings calibrate the two counters).
 
 "cpu_baseline" times the fp64 CPU oracle (forward + backward) on a bounded
 sample (the first 2^25 scores, k scaled) and scales by n log2 n.
@@ -97,9 +104,12 @@ def time_steps(torch, runner, steps, flush=None):
 
 
 def src_hash(name):
-    path = os.path.join(ROOT, "differentiable_soft_top_amd", "csrc", KERNEL_SOURCE[name])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Hash of the kernel's source file and the headers that shape its launch."""
+    h = hashlib.sha256()
+    for fn in (KERNEL_SOURCE[name], "stk_common.hpp", "stk_layout.hpp"):
+        with open(os.path.join(ROOT, "differentiable_soft_top_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_for(kernel, workload):
@@ -112,6 +122,80 @@ def traffic_for(kernel, workload):
     if not ent or ent.get("source_sha256") != src_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
+
+
+COPY_FLOATS = 100_000_000  # calibration copy: 400 MB read + 400 MB written
+
+
+def profile_run(torch, steps, warmup, workload):
+    """Short run for counter collection: the workload's steps, then one plain
+    device-to-device copy of known size (the calibration kernel)."""
+    from differentiable_soft_top_amd import _lib
+    from differentiable_soft_top_amd.workloads import draw_grad, make_workload
+    lib = _lib.load()
+    dev = torch.device("cuda:0")
+    s_np, k, alpha, w = make_workload(workload)
+    s = torch.from_numpy(s_np).to(dev)
+    g = torch.from_numpy(draw_grad(s_np.size, w.seed)).to(dev)
+    run = Runner(torch, lib, s, g, k, alpha)
+    for _ in range(warmup + steps):
+        run.step()
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_FLOATS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_run": workload, "steps": steps, "warmup": warmup, "copy_bytes": 4 * COPY_FLOATS}))
+
+
+def _read_counter_csv(path, counter):
+    """{kernel name: [value per dispatch]} from a rocprofv3 counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def pmc_summary(fetch_csv, write_csv, workload="c4"):
+    """Turn the two counter runs of --profile-run into profiles/traffic.json:
+    bytes per launch of each streaming kernel, each counter scaled so that the
+    calibration copy reads exactly its known size."""
+    fetch = _read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = _read_counter_csv(write_csv, "WRITE_SIZE")
+    copy_bytes = 4 * COPY_FLOATS
+
+    def copy_value(table):
+        vals = [v for name, vs in table.items() if "copyBuffer" in name for v in vs]
+        return max(vals) * 1024.0  # KiB -> bytes; the largest copy is the calibration one
+
+    f_scale = copy_bytes / copy_value(fetch)
+    w_scale = copy_bytes / copy_value(write)
+    n = int({"c2": 1e6, "c3": 1e7, "c4": 1e8}.get(workload, 1e8))
+    result = {"_calibration": {"copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+                               "fetch_csv": os.path.basename(fetch_csv), "write_csv": os.path.basename(write_csv)}}
+    ent = {}
+    for kname in ALGO_BYTES:
+        fk = [name for name in fetch if "stk::%s_kernel" % kname in name]
+        wk = [name for name in write if "stk::%s_kernel" % kname in name]
+        if not fk or not wk:
+            continue
+        fv = [v for name in fk for v in fetch[name]]
+        wv = [v for name in wk for v in write[name]]
+        fb = sum(fv) / len(fv) * 1024.0 * f_scale
+        wb = sum(wv) / len(wv) * 1024.0 * w_scale
+        ent[kname] = {"fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                      "bytes_per_launch": fb + wb, "algorithmic_bytes_per_launch": ALGO_BYTES[kname] * n,
+                      "launches": len(fv), "source_sha256": src_hash(kname)}
+    result[workload] = ent
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(result, f, indent=1, sort_keys=True)
+    print(json.dumps(result, indent=1, sort_keys=True))
 
 
 def cpu_baseline(s_np, g_np, k, alpha, sample_n=1 << 25):
@@ -143,7 +227,14 @@ def main():
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--sizes", default="c2,c3", help="extra workloads timed (comma list, '' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="counter-collection run: a few steps of --workload, then the calibration copy")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 counter CSVs (no GPU needed)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the operator is single-device); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -151,8 +242,12 @@ def main():
 
     import torch
 
+    if args.profile_run:
+        profile_run(torch, min(args.steps, 5), min(args.warmup, 2), args.workload)
+        return
+
     from differentiable_soft_top_amd import _lib
-    from differentiable_soft_top_amd.workloads import WORKLOADS, draw_grad, make_workload
+    from differentiable_soft_top_amd.workloads import draw_grad, make_workload
 
     lib = _lib.load()
     dev = torch.device("cuda:0")
