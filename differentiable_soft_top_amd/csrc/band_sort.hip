@@ -1,22 +1,23 @@
-// band_sort.hip -- sort of the middle band only.
+// band_sort.hip -- bucketing of the middle band (the band sort's first level).
 //
 // aiqbench.com abstract of Fast LapSum: bracketing "restricts sorting to a
 // narrow band of scores around the threshold"; gist.science summary,
 // section 2.2 step 3: the exact solver runs on that band alone.
 //
-// gfx950 design: a value-bucket sort.  The band lies in [bmin, bmax] (known
+// gfx950 design: a value-bucket sort whose second level runs in the solve.  The band lies in [bmin, bmax] (known
 // from pass-1) and its density there is smooth, so kBuckets equal-width value
 // buckets hold similar counts.  Three kernels:
 //   1. histogram: per-work-group LDS bucket counts; the last work-group turns
 //      them into global scatter offsets (bucket-major, work-group-minor);
 //   2. scatter: each element goes to its bucket (order within a bucket is
 //      arbitrary);
-//   3. bucket sort: one work-group per bucket sorts it in LDS (bitonic on
-//      order-preserving keys), writes it back and records the bucket
-//      summary (count, first, last, TA = sum e^{(x-last)/alpha},
-//      TB = sum e^{-(x-first)/alpha}) that the segment solve scans.
+//   3. bucket summaries: one work-group per bucket records its count,
+//      smallest and largest value and the anchored exponential sums
+//      (TA = sum e^{(x-last)/alpha}, TB = sum e^{-(x-first)/alpha}) that the
+//      segment solve scans.  No bucket is sorted here: the solve locates the
+//      one bucket that holds the root and sorts only that one, in LDS.
 // The bucket index floor((v - bmin) * kBuckets / (bmax - bmin)) is
-// non-decreasing in v, so the buckets concatenate into a sorted band.
+// non-decreasing in v, so bucket order is value order.
 #include "stk_common.hpp"
 #include "stk_layout.hpp"
 #include "stk_prof.hpp"
@@ -264,11 +265,15 @@ __device__ Pass1Partial fold_partials_wave(const Pass1Partial* p, int i0, int i1
     return r;
 }
 
-// One work-group per bucket.  Each also folds its share of the pass-1
-// partials, so the single-work-group solve reads kBuckets of them.
-__global__ __launch_bounds__(kSortThreads) void bucket_sort_kernel(BandArgs a)
+// One work-group per bucket: the bucket's summary for the level-1 scan of the
+// segment solve -- count, smallest and largest value, TA = sum e^{(x-hi)/alpha},
+// TB = sum e^{-(x-lo)/alpha} -- from its unordered elements.  Only the one
+// bucket that holds the root is ever sorted (by the solve, in LDS).  Each
+// work-group also folds its share of the pass-1 partials, so the
+// single-work-group solve reads kBuckets of them.
+__global__ __launch_bounds__(kSortThreads) void bucket_agg_kernel(BandArgs a)
 {
-    __shared__ uint32_t keys[kBucketCap];
+    constexpr int kHeld = 4;  // elements per thread kept in registers between the two sweeps
     __shared__ double red[2][kSortThreads / kWave];
     __shared__ float redf[2][kSortThreads / kWave];
     const Status* st = a.st;
@@ -287,8 +292,7 @@ __global__ __launch_bounds__(kSortThreads) void bucket_sort_kernel(BandArgs a)
             a.p1_super[b] = r;
     }
     const uint32_t start = a.bstart[b];
-    const uint32_t end = a.bstart[b + 1];
-    const uint32_t cnt = end - start;
+    const uint32_t cnt = a.bstart[b + 1] - start;
     GroupAgg g;
     g.cnt = cnt;
     g.start = start;
@@ -302,61 +306,52 @@ __global__ __launch_bounds__(kSortThreads) void bucket_sort_kernel(BandArgs a)
         }
         return;
     }
-    const double c = a.log2e_over_alpha;
-    float lo, hi;
-    double TA = 0.0, TB = 0.0;
-    if (cnt <= (uint32_t)kBucketCap) {
-        int n2 = 64;
-        while ((uint32_t)n2 < cnt)
-            n2 <<= 1;
-        constexpr int kPerT = kBucketCap / kSortThreads;  // 32
+    const float* x = a.band_sorted + start;
+    // sweep 1: smallest and largest value (the anchors)
+    float v[kHeld];
+    float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < kPerT; ++j) {
-            const int i = j * kSortThreads + tid;
-            if (i < n2)
-                keys[i] = (uint32_t)i < cnt ? float_to_key(a.band_sorted[start + i]) : 0xFFFFFFFFu;
+    for (int j = 0; j < kHeld; ++j) {
+        const uint32_t i = (uint32_t)(j * kSortThreads + tid);
+        v[j] = i < cnt ? x[i] : 0.f;
+        if (i < cnt) {
+            mn = fminf(mn, v[j]);
+            mx = fmaxf(mx, v[j]);
         }
-        __syncthreads();
-        lds_bitonic_sort(keys, n2);
-        lo = key_to_float(keys[0]);
-        hi = key_to_float(keys[cnt - 1]);
-        const double dlo = lo, dhi = hi;
-        for (uint32_t i = tid; i < cnt; i += kSortThreads) {
-            const float v = key_to_float(keys[i]);
-            a.band_sorted[start + i] = v;
-            TA += exp2_nonpos(((double)v - dhi) * c);
-            TB += exp2_nonpos((dlo - (double)v) * c);
+    }
+    for (uint32_t i = kHeld * kSortThreads + tid; i < cnt; i += kSortThreads) {
+        const float t = x[i];
+        mn = fminf(mn, t);
+        mx = fmaxf(mx, t);
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+        redf[0][wave] = mn;
+        redf[1][wave] = mx;
+    }
+    __syncthreads();
+    float lo = INFINITY, hi = -INFINITY;
+    for (int w = 0; w < kSortThreads / kWave; ++w) {
+        lo = fminf(lo, redf[0][w]);
+        hi = fmaxf(hi, redf[1][w]);
+    }
+    // sweep 2: the anchored exponential sums
+    const double c = a.log2e_over_alpha;
+    const double dlo = lo, dhi = hi;
+    double TA = 0.0, TB = 0.0;
+#pragma unroll
+    for (int j = 0; j < kHeld; ++j) {
+        const uint32_t i = (uint32_t)(j * kSortThreads + tid);
+        if (i < cnt) {
+            TA += exp2_nonpos(((double)v[j] - dhi) * c);
+            TB += exp2_nonpos((dlo - (double)v[j]) * c);
         }
-    } else {
-        // too large for LDS: acceptable only if every value is equal
-        float mn = INFINITY, mx = -INFINITY;
-        for (uint32_t i = tid; i < cnt; i += kSortThreads) {
-            const float v = a.band_sorted[start + i];
-            mn = fminf(mn, v);
-            mx = fmaxf(mx, v);
-        }
-        mn = wave_min(mn);
-        mx = wave_max(mx);
-        if (lane == 0) {
-            redf[0][wave] = mn;
-            redf[1][wave] = mx;
-        }
-        __syncthreads();
-        lo = INFINITY;
-        hi = -INFINITY;
-        for (int w = 0; w < kSortThreads / kWave; ++w) {
-            lo = fminf(lo, redf[0][w]);
-            hi = fmaxf(hi, redf[1][w]);
-        }
-        if (lo != hi) {
-            if (tid == 0)
-                a.st->solve_state = kSolveBucketOverflow;
-            return;
-        }
-        for (uint32_t i = tid; i < cnt; i += kSortThreads) {
-            TA += 1.0;
-            TB += 1.0;
-        }
+    }
+    for (uint32_t i = kHeld * kSortThreads + tid; i < cnt; i += kSortThreads) {
+        const double t = x[i];
+        TA += exp2_nonpos((t - dhi) * c);
+        TB += exp2_nonpos((dlo - t) * c);
     }
     TA = wave_sum(TA);
     TB = wave_sum(TB);
@@ -389,7 +384,7 @@ hipError_t launch_band_sort(const BandArgs& a, hipStream_t stream)
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    STK_LAUNCH(kKBucketSort, stream, bucket_sort_kernel, dim3(kBuckets), dim3(kSortThreads), 0, stream, a);
+    STK_LAUNCH(kKBucketAgg, stream, bucket_agg_kernel, dim3(kBuckets), dim3(kSortThreads), 0, stream, a);
     return hipGetLastError();
 }
 

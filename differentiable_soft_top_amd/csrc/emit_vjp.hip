@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kStreamThreads) void emit_finalize_kernel(EmitArgs 
     }
 }
 
-hipError_t launch_emit(const EmitArgs& a, hipStream_t stream)
+hipError_t launch_emit(const EmitArgs& a, bool fold_mass, hipStream_t stream)
 {
     const bool vec = ((reinterpret_cast<uintptr_t>(a.s) | reinterpret_cast<uintptr_t>(a.p)) & 15u) == 0;
     const dim3 grid(a.blocks), block(kStreamThreads);
@@ -187,7 +187,8 @@ hipError_t launch_emit(const EmitArgs& a, hipStream_t stream)
         STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchLarge, true, false>), grid, block, 0, stream, a);
     else
         STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchSmall, true, false>), grid, block, 0, stream, a);
-    STK_LAUNCH(kKEmitFinal, stream, emit_finalize_kernel, dim3(1), dim3(kStreamThreads), 0, stream, a);
+    if (fold_mass)
+        STK_LAUNCH(kKEmitFinal, stream, emit_finalize_kernel, dim3(1), dim3(kStreamThreads), 0, stream, a);
     return hipGetLastError();
 }
 

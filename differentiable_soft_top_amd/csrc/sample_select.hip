@@ -289,7 +289,7 @@ hipError_t launch_localize(const SampleArgs& sa, const SelectArgs& se, hipStream
 {
     STK_LAUNCH(kKPilot, stream, pilot_kernel, dim3(1), dim3(kSelectThreads), 0, stream, sa);
     const int blocks = (sa.m + 255) / 256;
-    STK_LAUNCH(kKSample, stream, filter_kernel, dim3(blocks), dim3(256), 0, stream, sa);
+    STK_LAUNCH(kKFilter, stream, filter_kernel, dim3(blocks), dim3(256), 0, stream, sa);
     STK_LAUNCH(kKSelect, stream, select_kernel, dim3(1), dim3(kSelectThreads), 0, stream, se);
     return hipGetLastError();
 }

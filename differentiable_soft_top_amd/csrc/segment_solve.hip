@@ -15,13 +15,14 @@
 // A left tail (scores < a_L) is a node at a_L with A = SL; a right tail
 // (scores >= a_R) a node at a_R with B = SR and count nR.
 //
-// gfx950 design, one 1024-thread work-group:
+// gfx950 design, one 512-thread work-group:
 //   level 1 -- groups (band buckets or full-sort tiles) carry (count, first,
 //     last, TA, TB); prefix and suffix anchored sums combine associatively,
 //     so a work-group scan over the groups gives M at every group end and
 //     the bracket certificate M(a_L) >= k >= M(a_R);
-//   level 2 -- the one group whose end first drops below k is scanned
-//     element by element the same way;
+//   level 2 -- the one group whose end first drops below k is sorted in LDS
+//     (band buckets arrive unordered; full-sort tiles arrive sorted) and
+//     scanned element by element the same way;
 //   closed form -- in the located gap [x_lo, x_hi], with v = e^{(x_lo-b)/alpha},
 //     w = e^{(b-x_hi)/alpha}, v w = g = e^{-(x_hi-x_lo)/alpha}, the mass is
 //     A v/2 + C - B w/2 = k: a quadratic solved in the cancellation-free
@@ -36,574 +37,673 @@ namespace stk {
 
 namespace {
 
-constexpr int kT = kSelectThreads;
+constexpr int kST = kSolveThreads;       // threads of the solve work-group
+constexpr int kSW = kST / kWave;         // its waves
+static_assert(kTile <= kBucketCap, "full-sort tiles must fit the level-2 buffers");
+static_assert(kBuckets % kST == 0, "pass-1 super partials per thread");
 
-// An anchored exponential sum: value v anchored at point x (has = 0: empty).
+// An anchored exponential sum: value v anchored at point x.  Every anchor
+// is an fp32 score (or a bracket end, itself a sample value), so x is fp32.
+// An empty prefix is (x = -inf, v = 0) and an empty suffix (x = +inf, v = 0):
+// with the exponential clamped to [0, 1] (exp2_nonpos: NaN and -inf give 0,
+// +inf gives 1) the combinations below need no emptiness flag.
 struct Anch {
-    double x;
+    float x;
     double v;
-    int has;
 };
 
-// earlier e, later l (x_e <= x_l): re-anchor at l's point
-__device__ __forceinline__ Anch fwd(Anch e, Anch l, double c)
-{
-    if (!l.has)
-        return e;
-    if (!e.has)
-        return l;
-    Anch r;
-    r.x = l.x;
-    r.v = l.v + exp2_nonpos((e.x - l.x) * c) * e.v;
-    r.has = 1;
-    return r;
-}
-
-// left l, right r (x_l <= x_r): re-anchor at l's point
-__device__ __forceinline__ Anch bwd(Anch l, Anch r, double c)
-{
-    if (!l.has)
-        return r;
-    if (!r.has)
-        return l;
-    Anch o;
-    o.x = l.x;
-    o.v = l.v + exp2_nonpos((l.x - r.x) * c) * r.v;
-    o.has = 1;
-    return o;
-}
-
-struct ScanLds {
-    double x[kT];
-    double v[kT];
-    int h[kT];
-    unsigned long long u[kT];
-};
-
-struct ScanOut {
-    Anch incl;  // over threads 0..tid (forward) or tid..nt-1 (backward)
-    Anch excl;  // the same without this thread
-};
-
-__device__ __forceinline__ Anch shfl_anch(Anch a, int src_lane)
-{
-    Anch o;
-    o.x = __shfl(a.x, src_lane, kWave);
-    o.v = __shfl(a.v, src_lane, kWave);
-    o.has = __shfl(a.has, src_lane, kWave);
-    return o;
-}
-
-__device__ __forceinline__ Anch empty_anch()
+__device__ __forceinline__ Anch node(float x, double v)
 {
     Anch a;
-    a.x = 0.0;
-    a.v = 0.0;
-    a.has = 0;
+    a.x = x;
+    a.v = v;
     return a;
 }
 
-// Work-group scan of anchored sums: kForward is a prefix over threads
-// 0..tid, else a suffix over tid..nt-1.  Kogge-Stone over shuffles inside
-// each wave, then the wave totals (LDS) folded in order by every thread.
-template <bool kForward>
-__device__ ScanOut wg_scan(Anch mine, ScanLds& L, double c)
+__device__ __forceinline__ Anch empty_pre() { return node(-INFINITY, 0.0); }
+__device__ __forceinline__ Anch empty_suf() { return node(INFINITY, 0.0); }
+
+// prefix: earlier e, later l (x_e <= x_l), anchored at the later point
+__device__ __forceinline__ Anch fwd(Anch e, Anch l, double c)
 {
-    constexpr int kWaves = kT / kWave;
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    Anch incl = mine;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int src = kForward ? lane - off : lane + off;
-        const Anch o = shfl_anch(incl, src < 0 ? 0 : (src >= kWave ? kWave - 1 : src));
-        if (kForward ? lane >= off : lane + off < kWave)
-            incl = kForward ? fwd(o, incl, c) : bwd(incl, o, c);
-    }
-    // within-wave exclusive value: the neighbour's inclusive one
-    const int nb = kForward ? lane - 1 : lane + 1;
-    Anch wex = shfl_anch(incl, nb < 0 ? 0 : (nb >= kWave ? kWave - 1 : nb));
-    if (kForward ? lane == 0 : lane == kWave - 1)
-        wex = empty_anch();
-    __syncthreads();  // earlier readers of L are done
-    if (kForward ? lane == kWave - 1 : lane == 0) {
-        L.x[wave] = incl.x;
-        L.v[wave] = incl.v;
-        L.h[wave] = incl.has;
-    }
-    __syncthreads();
-    Anch agg = empty_anch();
-    if (kForward) {
-        for (int w = 0; w < wave; ++w) {
-            Anch t;
-            t.x = L.x[w];
-            t.v = L.v[w];
-            t.has = L.h[w];
-            agg = fwd(agg, t, c);
-        }
-    } else {
-        for (int w = kWaves - 1; w > wave; --w) {
-            Anch t;
-            t.x = L.x[w];
-            t.v = L.v[w];
-            t.has = L.h[w];
-            agg = bwd(t, agg, c);
-        }
-    }
-    ScanOut out;
-    out.incl = kForward ? fwd(agg, incl, c) : bwd(incl, agg, c);
-    out.excl = kForward ? fwd(agg, wex, c) : bwd(wex, agg, c);
-    return out;
+    return node(fmaxf(e.x, l.x), l.v + exp2_nonpos_lowdepth(((double)e.x - (double)l.x) * c) * e.v);
 }
 
-// Inclusive prefix sum of u64 over the work-group (shuffles + wave totals).
-__device__ unsigned long long wg_scan_u64(unsigned long long mine, ScanLds& L)
+// suffix: left l, right r (x_l <= x_r), anchored at the left point
+__device__ __forceinline__ Anch bwd(Anch l, Anch r, double c)
 {
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    unsigned long long incl = mine;
+    return node(fminf(l.x, r.x), l.v + exp2_nonpos_lowdepth(((double)l.x - (double)r.x) * c) * r.v);
+}
+
+__device__ __forceinline__ Anch shfl_anch(Anch a, int src_lane)
+{
+    return node(__shfl(a.x, src_lane, kWave), __shfl(a.v, src_lane, kWave));
+}
+
+// Work-group scan of two anchored sums per thread: `pre` (this thread's
+// items folded forward, anchored at its last point) and `suf` (folded
+// backward, anchored at its first point), plus a u32 count.  Each wave scans
+// with shuffles (the two directions interleaved so their latencies
+// overlap); the wave totals meet in LDS behind one barrier; every wave then
+// scans the kSW totals with three more shuffle steps.
+struct WaveTot {
+    double pv, sv;
+    float px, sx;
+    uint32_t cnt;
+};
+
+struct Scan2 {
+    Anch pre_before, suf_after, pre_all, suf_all;
+    uint32_t cnt_before, cnt_all;
+};
+
+struct Scan2Part {
+    Anch pw_ex, sw_ex;   // within-wave exclusive values
+    uint32_t cw_ex;
+};
+
+__device__ __forceinline__ Scan2Part scan2_publish(Anch pre, Anch suf, uint32_t cnt, double c, WaveTot* wt)
+{
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    Anch p = pre, q = suf;
+    uint32_t n = cnt;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
-        const unsigned long long o = __shfl_up(incl, off, kWave);
-        if (lane >= off)
-            incl += o;
+        const Anch op = shfl_anch(p, lane >= off ? lane - off : lane);
+        const Anch oq = shfl_anch(q, lane + off < kWave ? lane + off : lane);
+        const uint32_t on = __shfl_up(n, off, kWave);
+        if (lane >= off) {
+            p = fwd(op, p, c);
+            n += on;
+        }
+        if (lane + off < kWave)
+            q = bwd(q, oq, c);
     }
-    __syncthreads();
+    Scan2Part r;
+    r.pw_ex = shfl_anch(p, lane > 0 ? lane - 1 : 0);
+    r.sw_ex = shfl_anch(q, lane < kWave - 1 ? lane + 1 : kWave - 1);
+    r.cw_ex = n - cnt;
+    if (lane == 0)
+        r.pw_ex = empty_pre();
     if (lane == kWave - 1)
-        L.u[wave] = incl;
-    __syncthreads();
-    unsigned long long before = 0;
-    for (int w = 0; w < wave; ++w)
-        before += L.u[w];
-    return before + incl;
-}
-
-__device__ int wg_max_int(int v, int* red)
-{
-    for (int off = 32; off > 0; off >>= 1) {
-        const int o = __shfl_xor(v, off, kWave);
-        v = o > v ? o : v;
+        r.sw_ex = empty_suf();
+    if (lane == kWave - 1) {
+        wt[wave].px = p.x;
+        wt[wave].pv = p.v;
+        wt[wave].cnt = n;
     }
-    __syncthreads();
-    if ((threadIdx.x & (kWave - 1)) == 0)
-        red[threadIdx.x / kWave] = v;
-    __syncthreads();
-    int r = red[0];
-    for (int w = 1; w < kT / kWave; ++w)
-        r = red[w] > r ? red[w] : r;
-    __syncthreads();
+    if (lane == 0) {
+        wt[wave].sx = q.x;
+        wt[wave].sv = q.v;
+    }
     return r;
 }
 
-__device__ int wg_min_int(int v, int* red)
+// after the barrier that follows scan2_publish
+__device__ __forceinline__ Scan2 scan2_finish(const WaveTot* wt, const Scan2Part& part, double c)
 {
-    return -wg_max_int(-v, red);
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    Anch p = empty_pre(), q = empty_suf();
+    uint32_t n = 0;
+    if (lane < kSW) {
+        p = node(wt[lane].px, wt[lane].pv);
+        q = node(wt[lane].sx, wt[lane].sv);
+        n = wt[lane].cnt;
+    }
+#pragma unroll
+    for (int off = 1; off < kSW; off <<= 1) {
+        const Anch op = shfl_anch(p, lane >= off ? lane - off : lane);
+        const Anch oq = shfl_anch(q, lane + off < kSW ? lane + off : lane);
+        const uint32_t on = __shfl_up(n, off, kWave);
+        if (lane >= off && lane < kSW) {
+            p = fwd(op, p, c);
+            n += on;
+        }
+        if (lane + off < kSW)
+            q = bwd(q, oq, c);
+    }
+    Anch pb = shfl_anch(p, wave > 0 ? wave - 1 : 0);
+    uint32_t nb = __shfl(n, wave > 0 ? wave - 1 : 0, kWave);
+    if (wave == 0) {
+        pb = empty_pre();
+        nb = 0;
+    }
+    Anch qa = shfl_anch(q, wave + 1 < kSW ? wave + 1 : 0);
+    if (wave == kSW - 1)
+        qa = empty_suf();
+    Scan2 r;
+    r.pre_before = fwd(pb, part.pw_ex, c);
+    r.pre_all = shfl_anch(p, kSW - 1);
+    r.suf_after = bwd(part.sw_ex, qa, c);
+    r.suf_all = shfl_anch(q, 0);
+    r.cnt_before = nb + part.cw_ex;
+    r.cnt_all = __shfl(n, kSW - 1, kWave);
+    return r;
+}
+
+// Ascending sort of kST * R keys, R per thread in blocked order (thread t
+// holds positions t*R .. t*R+R-1).  Bitonic network: partners inside a
+// thread are exchanged in registers, partners inside a wave by lane
+// shuffles, partners in other waves through LDS (two buffers alternate, one
+// barrier per such stage).  Every stage index is a compile-time constant.
+template <int R>
+__device__ __forceinline__ void block_bitonic_regs(uint32_t (&v)[R], uint32_t* buf0, uint32_t* buf1)
+{
+    constexpr int n2 = kST * R;
+    const int tid = threadIdx.x;
+    int flip = 0;
+#pragma unroll
+    for (int k = 2; k <= n2; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            if (j < R) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int p = r ^ j;
+                    if (p > r) {
+                        const bool up = ((tid * R + r) & k) == 0;
+                        const uint32_t a = v[r], b = v[p];
+                        const bool sw = (a > b) == up;
+                        v[r] = sw ? b : a;
+                        v[p] = sw ? a : b;
+                    }
+                }
+            } else if (j < kWave * R) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int i = tid * R + r;
+                    const uint32_t o = (uint32_t)__shfl_xor((int)v[r], j / R, kWave);
+                    const bool take_min = ((i & j) == 0) == ((i & k) == 0);
+                    v[r] = take_min ? (v[r] < o ? v[r] : o) : (v[r] > o ? v[r] : o);
+                }
+            } else {
+                uint32_t* buf = flip ? buf1 : buf0;
+                flip ^= 1;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    buf[tid * R + r] = v[r];
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int i = tid * R + r;
+                    const uint32_t o = buf[i ^ j];
+                    const bool take_min = ((i & j) == 0) == ((i & k) == 0);
+                    v[r] = take_min ? (v[r] < o ? v[r] : o) : (v[r] > o ? v[r] : o);
+                }
+            }
+        }
+    }
+}
+
+// Load cnt values (padded with +inf keys to kST * R), sort, store to keys.
+template <int R>
+__device__ void sort_group_into(const float* x, int cnt, uint32_t* keys, uint32_t* spare)
+{
+    const int tid = threadIdx.x;
+    uint32_t v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = tid * R + r;
+        v[r] = i < cnt ? float_to_key(x[i]) : 0xFFFFFFFFu;
+    }
+    block_bitonic_regs<R>(v, keys, spare);
+    __syncthreads();  // the last LDS stage's reads are done
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        keys[tid * R + r] = v[r];
 }
 
 // Mass at a point x with prefix P (anchored at x), count after C, and the
-// suffix S of everything after (anchored at its first point).
-__device__ __forceinline__ double mass_at(double x, double Pv, double C, Anch S, double c)
+// suffix S of everything after (anchored at its first point; may be empty).
+__device__ __forceinline__ double mass_at(float x, double Pv, double C, Anch S, double c)
 {
-    double m = 0.5 * Pv + C;
-    if (S.has)
-        m -= 0.5 * S.v * exp2_nonpos((x - S.x) * c);
-    return m;
+    return 0.5 * Pv + C - 0.5 * S.v * exp2_nonpos(((double)x - (double)S.x) * c);
 }
 
-// Root of A v/2 + C - B w/2 = k on [xlo, xhi] (either end may be open).
+// Root of A v/2 + C - B w/2 = k on [xlo, xhi] (an empty end has v = 0).
 __device__ double gap_root(Anch lo, Anch hi, double C, double k, double alpha, double c)
 {
     const double cc = C - k;
-    if (cc == 0.0 && lo.has && hi.has)
-        return 0.5 * (lo.x + hi.x) + 0.5 * alpha * log(lo.v / hi.v);
-    const double g = (lo.has && hi.has) ? exp2_nonpos((lo.x - hi.x) * c) : 0.0;
-    const double A = lo.has ? lo.v : 0.0;
-    const double B = hi.has ? hi.v : 0.0;
-    const double r = sqrt(cc * cc + A * B * g);
+    const double xlo = lo.x, xhi = hi.x;
+    if (cc == 0.0 && lo.v > 0.0 && hi.v > 0.0)
+        return 0.5 * (xlo + xhi) + 0.5 * alpha * log(lo.v / hi.v);
+    const double g = (lo.v > 0.0 && hi.v > 0.0) ? exp2_nonpos((xlo - xhi) * c) : 0.0;
+    const double r = sqrt(cc * cc + lo.v * hi.v * g);
     if (cc > 0.0)
-        return hi.x + alpha * log((cc + r) / B);
-    return lo.x - alpha * log((-cc + r) / A);
+        return xhi + alpha * log((cc + r) / hi.v);
+    return xlo - alpha * log((-cc + r) / lo.v);
+}
+
+// What a thread publishes about the groups it owns: the last one whose end
+// carries mass >= k (lo side of the root) and the first non-empty one whose
+// end carries less (the group that holds the root).
+struct RowHi {
+    GroupAgg g;
+    double Sv;                     // suffix of everything after the group
+    float Sx;
+    uint32_t Cafter;               // scores after the group (right tail included)
+};
+
+struct SolveLds {
+    WaveTot wt[kSW];
+    double pd[2][kSW];
+    unsigned long long pu[2][kSW];
+    uint32_t pnf[kSW];
+    float pf[4][kSW];
+    int imax[kSW], imin[kSW];
+    Anch lo[kST];
+    RowHi hi[kST];
+    uint32_t keys[kBucketCap];
+    double bv[kBucketCap];
+};
+
+__device__ __forceinline__ void block_max_min(int vmax, int vmin, SolveLds& L, int* omax, int* omin)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const int a = __shfl_xor(vmax, off, kWave);
+        const int b = __shfl_xor(vmin, off, kWave);
+        vmax = a > vmax ? a : vmax;
+        vmin = b < vmin ? b : vmin;
+    }
+    if (lane_id() == 0) {
+        L.imax[threadIdx.x / kWave] = vmax;
+        L.imin[threadIdx.x / kWave] = vmin;
+    }
+    __syncthreads();
+    int M = L.imax[0], m = L.imin[0];
+    for (int w = 1; w < kSW; ++w) {
+        M = L.imax[w] > M ? L.imax[w] : M;
+        m = L.imin[w] < m ? L.imin[w] : m;
+    }
+    *omax = M;
+    *omin = m;
+}
+
+__device__ __forceinline__ void finish(const SolveArgs& a, double b)
+{
+    *a.out_b = b;
+    a.st->b = b;
+    a.st->solve_state = isfinite(b) ? kSolveOk : kSolveRejectHigh;
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(kT) void solve_kernel(SolveArgs a)
+// One work-group.  Phases (barriers in brackets):
+//   1. fold the pass-1 partials; per-thread level-1 values; wave scans  [1]
+//   2. per-group masses, bracket certificate, the two groups around the
+//      root published to LDS                                            [1]
+//   3. the located group into LDS, sorted unless it comes from the full
+//      sort                                                             [few]
+//   4. level-2 scans, breakpoint masses                                 [1]
+//   5. the last breakpoint with mass >= k; its owner applies the closed
+//      form                                                             [1]
+__global__ __launch_bounds__(kST) void solve_kernel(SolveArgs a)
 {
-    __shared__ ScanLds L;
-    __shared__ int red[kT / kWave];
-    __shared__ double bc_d[8];
-    __shared__ unsigned long long bc_u[4];
-    __shared__ int bc_i[4];
-
+    __shared__ SolveLds L;
     Status* st = a.st;
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     const double c = a.log2e_over_alpha;
     const double k = a.k;
 
-    // ---- route checks (tails=1: bracketed band) ---------------------------
-    Anch left, right;
-    left.has = 0;
-    left.x = -INFINITY;
-    left.v = 0.0;
-    right.has = 0;
-    right.x = INFINITY;
-    right.v = 0.0;
-    unsigned long long nR = 0;
+    // ---- loads issued up front ----------------------------------------------
+    const int T = a.groups;
+    const int gpt = (T + kST - 1) / kST;
+    const int g0 = tid * gpt < T ? tid * gpt : T;
+    const int g1 = g0 + gpt < T ? g0 + gpt : T;
+    GroupAgg mine;
+    mine.cnt = 0;
+    if (gpt == 1 && g0 < T)
+        mine = a.agg[g0];
+    const uint64_t nB = a.tails ? st->nB : 0;
+    const float aL = a.tails ? st->aL : -INFINITY;
+    const float aR = a.tails ? st->aR : INFINITY;
+
+    // pass-1 totals (tails, counts, finiteness): the band sort pre-folded
+    // them into kBuckets partials unless the band overflowed; those are read
+    // speculatively, together with the band count that says whether they hold
+    double SL = 0.0, SR = 0.0;
+    unsigned long long nL = 0, nR = 0;
+    uint32_t nf = 0;
+    float bmin = INFINITY, bmax = -INFINITY, smin = INFINITY, smax = -INFINITY;
+    auto add = [&](const Pass1Partial& p) {
+        SL += p.SL;
+        SR += p.SR;
+        nL += p.nL;
+        nR += p.nR;
+        nf |= p.nonfinite;
+        bmin = fminf(bmin, p.bmin);
+        bmax = fmaxf(bmax, p.bmax);
+        smin = fminf(smin, p.smin);
+        smax = fmaxf(smax, p.smax);
+    };
     if (a.tails) {
-        // fold the pass-1 partials (tails, counts, finiteness) into the status;
-        // the band sort has pre-folded them unless the band overflowed
-        const bool folded = st->nB <= (uint64_t)a.cap;
-        const Pass1Partial tot = folded ? reduce_pass1(a.p1_super, kBuckets, st)
-                                        : reduce_pass1(a.p1, a.p1_blocks, st);
-        if (tot.nonfinite) {
+        constexpr int kSp = kBuckets / kST;
+        Pass1Partial sp[kSp];
+#pragma unroll
+        for (int r = 0; r < kSp; ++r)
+            sp[r] = a.p1_super[r * kST + tid];
+        if (nB <= (uint64_t)a.cap) {
+#pragma unroll
+            for (int r = 0; r < kSp; ++r)
+                add(sp[r]);
+        } else {
+            for (int i = tid; i < a.p1_blocks; i += kST)
+                add(a.p1[i]);
+        }
+    }
+    SL = wave_sum(SL);
+    SR = wave_sum(SR);
+    nL = wave_sum_u64(nL);
+    nR = wave_sum_u64(nR);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        nf |= __shfl_xor(nf, off, kWave);
+    bmin = wave_min(bmin);
+    bmax = wave_max(bmax);
+    smin = wave_min(smin);
+    smax = wave_max(smax);
+    if (lane == 0) {
+        L.pd[0][wave] = SL;
+        L.pd[1][wave] = SR;
+        L.pu[0][wave] = nL;
+        L.pu[1][wave] = nR;
+        L.pnf[wave] = nf;
+        L.pf[0][wave] = bmin;
+        L.pf[1][wave] = bmax;
+        L.pf[2][wave] = smin;
+        L.pf[3][wave] = smax;
+    }
+
+    // ---- level 1: this thread's groups folded, then the work-group scans ------------
+    Anch pre = empty_pre(), suf = empty_suf();
+    uint32_t cnt = 0;
+    if (gpt == 1) {
+        if (g0 < T && mine.cnt) {
+            pre = node(mine.hi, mine.TA);
+            suf = node(mine.lo, mine.TB);
+            cnt = mine.cnt;
+        }
+    } else {
+        for (int g = g0; g < g1; ++g) {
+            const GroupAgg G = a.agg[g];
+            if (G.cnt) {
+                pre = fwd(pre, node(G.hi, G.TA), c);
+                cnt += G.cnt;
+            }
+        }
+        for (int g = g1 - 1; g >= g0; --g) {
+            const GroupAgg G = a.agg[g];
+            if (G.cnt)
+                suf = bwd(node(G.lo, G.TB), suf, c);
+        }
+    }
+    const Scan2Part part1 = scan2_publish(pre, suf, cnt, c, L.wt);
+    __syncthreads();  // [1]
+
+    // every thread folds the wave values in the same order
+    SL = SR = 0.0;
+    nL = nR = 0;
+    nf = 0;
+    for (int w = 0; w < kSW; ++w) {
+        SL += L.pd[0][w];
+        SR += L.pd[1][w];
+        nL += L.pu[0][w];
+        nR += L.pu[1][w];
+        nf |= L.pnf[w];
+    }
+    if (a.tails && tid == 0) {
+        float f0 = INFINITY, f1 = -INFINITY, f2 = INFINITY, f3 = -INFINITY;
+        for (int w = 0; w < kSW; ++w) {
+            f0 = fminf(f0, L.pf[0][w]);
+            f1 = fmaxf(f1, L.pf[1][w]);
+            f2 = fminf(f2, L.pf[2][w]);
+            f3 = fmaxf(f3, L.pf[3][w]);
+        }
+        st->SL = SL;
+        st->SR = SR;
+        st->nL = nL;
+        st->nR = nR;
+        st->nonfinite = nf;
+        st->bmin = f0;
+        st->bmax = f1;
+        st->smin = f2;
+        st->smax = f3;
+    }
+    // the tails as virtual end nodes (an infinite bracket end has none)
+    Anch left = empty_pre(), right = empty_suf();
+    bool hasL = false, hasR = false;
+    if (a.tails) {
+        if (nf) {
             if (tid == 0)
                 st->solve_state = kSolveNonfinite;
             return;
         }
-        if (st->solve_state == kSolveBucketOverflow)
-            return;
-        if (st->nB > (uint64_t)a.cap) {
+        if (nB > (uint64_t)a.cap) {
             if (tid == 0)
                 st->solve_state = kSolveOverflow;
             return;
         }
-        const float aL = st->aL, aR = st->aR;
-        if (aL != -INFINITY) {
-            left.has = 1;
-            left.x = aL;
-            left.v = tot.SL;
-        }
-        if (aR != INFINITY) {
-            right.has = 1;
-            right.x = aR;
-            right.v = tot.SR;
-        }
-        nR = tot.nR;
+        hasL = aL != -INFINITY;
+        hasR = aR != INFINITY;
+        if (hasL)
+            left = node(aL, SL);
+        if (hasR)
+            right = node(aR, SR);
+    } else {
+        nR = 0;
     }
+    const Scan2 sc = scan2_finish(L.wt, part1, c);
+    const uint32_t NG = sc.cnt_all;
+    const uint32_t cnt_before = sc.cnt_before;
+    const Anch pre_before = fwd(left, sc.pre_before, c);  // everything before this thread's groups
+    const Anch suf_after = bwd(sc.suf_after, right, c);   // everything after them
 
-    // ---- level 1: groups ----------------------------------------------------
-    const int T = a.groups;
-    const int gpt = (T + kT - 1) / kT;
-    const int g0 = tid * gpt < T ? tid * gpt : T;
-    const int g1 = g0 + gpt < T ? g0 + gpt : T;
-
-    Anch pre;  // this thread's groups folded forward (anchored at last hi)
-    pre.has = 0;
-    pre.x = 0.0;
-    pre.v = 0.0;
-    Anch suf;  // folded backward (anchored at first lo)
-    suf.has = 0;
-    suf.x = 0.0;
-    suf.v = 0.0;
-    unsigned long long cnt = 0;
-    for (int g = g0; g < g1; ++g) {
-        const GroupAgg G = a.agg[g];
-        if (G.cnt == 0)
-            continue;
-        Anch t;
-        t.has = 1;
-        t.x = G.hi;
-        t.v = G.TA;
-        pre = fwd(pre, t, c);
-        cnt += G.cnt;
-    }
-    for (int g = g1 - 1; g >= g0; --g) {
-        const GroupAgg G = a.agg[g];
-        if (G.cnt == 0)
-            continue;
-        Anch t;
-        t.has = 1;
-        t.x = G.lo;
-        t.v = G.TB;
-        suf = bwd(t, suf, c);
-    }
-    const unsigned long long cnt_incl = wg_scan_u64(cnt, L);
-    if (tid == kT - 1)
-        bc_u[0] = cnt_incl;  // total over groups
-    const ScanOut pre_s = wg_scan<true>(pre, L, c);
-    const Anch pre_before = fwd(left, pre_s.excl, c);
-    if (tid == kT - 1) {
-        const Anch all = fwd(left, pre_s.incl, c);
-        bc_d[0] = all.x;
-        bc_d[1] = all.v;
-        bc_i[0] = all.has;
-    }
-    const ScanOut suf_s = wg_scan<false>(suf, L, c);
-    const Anch suf_after = bwd(suf_s.excl, right, c);
-    if (tid == 0) {
-        const Anch all = bwd(suf_s.incl, right, c);
-        bc_d[2] = all.x;
-        bc_d[3] = all.v;
-        bc_i[1] = all.has;
-    }
-    __syncthreads();
-    const unsigned long long NG = bc_u[0];
-    const unsigned long long cnt_before = cnt_incl - cnt;
-
-    // per-group scan values: walk backward for the suffix, forward for the prefix
-    {
-        Anch cur = suf_after;
-        for (int g = g1 - 1; g >= g0; --g) {
-            const GroupAgg G = a.agg[g];
-            a.scan[g].Sx = cur.has ? cur.x : INFINITY;
-            a.scan[g].Sv = cur.has ? cur.v : 0.0;
-            if (G.cnt) {
-                Anch t;
-                t.has = 1;
-                t.x = G.lo;
-                t.v = G.TB;
-                cur = bwd(t, cur, c);
-            }
-        }
-    }
-    int cand = -1;
-    {
-        Anch cur = pre_before;
-        unsigned long long through = cnt_before;
-        for (int g = g0; g < g1; ++g) {
-            const GroupAgg G = a.agg[g];
-            through += G.cnt;
-            const unsigned long long after = NG - through + nR;
-            a.scan[g].Cafter = after;
-            if (G.cnt) {
-                Anch t;
-                t.has = 1;
-                t.x = G.hi;
-                t.v = G.TA;
-                cur = fwd(cur, t, c);
-                a.scan[g].Pv = cur.v;
-                Anch S;
-                S.x = a.scan[g].Sx;
-                S.v = a.scan[g].Sv;
-                S.has = S.x != INFINITY;
-                const double m = mass_at((double)G.hi, cur.v, (double)after, S, c);
-                if (m >= k)
-                    cand = g;
-            }
-        }
-    }
-
-    // ---- certificate of the bracket ---------------------------------------
-    if (tid == 0) {
-        double mL = (double)(NG + nR), mR = 0.0;
-        if (a.tails) {
-            Anch Sall;
-            Sall.x = bc_d[2];
-            Sall.v = bc_d[3];
-            Sall.has = bc_i[1];
-            // at a_L: left tail A = SL, everything else after it
-            mL = left.has ? mass_at(left.x, left.v, (double)(NG + nR), Sall, c)
-                          : (double)(NG + nR);
-            // at a_R: all groups before it, right tail after it
-            Anch Pall;
-            Pall.x = bc_d[0];
-            Pall.v = bc_d[1];
-            Pall.has = bc_i[0];
-            if (right.has) {
-                double m = (double)nR - 0.5 * right.v;
-                if (Pall.has)
-                    m += 0.5 * Pall.v * exp2_nonpos((Pall.x - right.x) * c);
-                mR = m;
-            }
+    // ---- bracket certificate (every thread, same values) ---------------------------
+    if (a.tails) {
+        const Anch Sall = bwd(sc.suf_all, right, c);
+        const double mL = hasL ? mass_at(left.x, left.v, (double)NG + (double)nR, Sall, c) : (double)NG + (double)nR;
+        const Anch Pall = fwd(left, sc.pre_all, c);
+        double mR = 0.0;
+        if (hasR)
+            mR = (double)nR - 0.5 * right.v + 0.5 * Pall.v * exp2_nonpos(((double)Pall.x - (double)right.x) * c);
+        if (tid == 0) {
             st->massL = mL;
             st->massR = mR;
         }
-        int state = kSolveOk;
-        if (a.tails && left.has && !(mL >= k))
-            state = kSolveRejectLow;
-        else if (a.tails && right.has && !(mR <= k))
-            state = kSolveRejectHigh;
-        bc_i[2] = state;
-    }
-    __syncthreads();
-    if (bc_i[2] != kSolveOk) {
-        if (tid == 0)
-            st->solve_state = (uint32_t)bc_i[2];
-        return;
-    }
-
-    // ---- locate the group -----------------------------------------------------
-    const int tstar = wg_max_int(cand, red);
-    int unext = T;
-    for (int g = g0; g < g1; ++g) {
-        if (g > tstar && a.agg[g].cnt != 0) {
-            unext = g;
-            break;
+        const bool rejL = hasL && !(mL >= k);
+        const bool rejR = !rejL && hasR && !(mR <= k);
+        if (rejL || rejR) {
+            if (tid == 0)
+                st->solve_state = rejL ? kSolveRejectLow : kSolveRejectHigh;
+            return;
         }
     }
-    const int u = wg_min_int(unext, red);
 
-    // lower end of the located interval: the node at group t*'s end (or a_L)
-    Anch lo_node = left;
-    if (tstar >= 0) {
-        lo_node.has = 1;
-        lo_node.x = a.agg[tstar].hi;
-        lo_node.v = a.scan[tstar].Pv;
+    // ---- masses at the group ends; the two groups around the root ----------------------
+    int tc = -1, uc = T;
+    if (gpt == 1) {
+        if (g0 < T && mine.cnt) {
+            const Anch P = fwd(pre_before, node(mine.hi, mine.TA), c);
+            const uint32_t after = NG - (cnt_before + mine.cnt) + (uint32_t)nR;
+            if (mass_at(mine.hi, P.v, (double)after, suf_after, c) >= k) {
+                tc = g0;
+                L.lo[tid] = P;
+            } else {
+                uc = g0;
+                L.hi[tid].g = mine;
+                L.hi[tid].Sx = suf_after.x;
+                L.hi[tid].Sv = suf_after.v;
+                L.hi[tid].Cafter = after;
+            }
+        }
+    } else {
+        // per-group suffixes through the scratch array, then the forward walk
+        Anch cur = suf_after;
+        for (int g = g1 - 1; g >= g0; --g) {
+            const GroupAgg G = a.agg[g];
+            a.scan[g].Sx = cur.x;
+            a.scan[g].Sv = cur.v;
+            if (G.cnt)
+                cur = bwd(node(G.lo, G.TB), cur, c);
+        }
+        Anch P = pre_before;
+        uint32_t through = cnt_before;
+        for (int g = g0; g < g1; ++g) {
+            const GroupAgg G = a.agg[g];
+            if (!G.cnt)
+                continue;
+            through += G.cnt;
+            const uint32_t after = NG - through + (uint32_t)nR;
+            P = fwd(P, node(G.hi, G.TA), c);
+            const Anch S = node((float)a.scan[g].Sx, a.scan[g].Sv);
+            if (mass_at(G.hi, P.v, (double)after, S, c) >= k) {
+                tc = g;
+                L.lo[tid] = P;
+            } else if (uc == T) {
+                uc = g;
+                L.hi[tid].g = G;
+                L.hi[tid].Sx = S.x;
+                L.hi[tid].Sv = S.v;
+                L.hi[tid].Cafter = after;
+            }
+        }
     }
-
+    int tstar, u;
+    block_max_min(tc, uc, L, &tstar, &u);  // [1]
+    if (u < tstar) {
+        // rounding broke the monotone order of the group-end masses: take
+        // the first non-empty group after t* instead
+        __syncthreads();
+        int mine_u = T;
+        if (gpt == 1) {
+            if (g0 < T && g0 > tstar && mine.cnt) {
+                mine_u = g0;
+                L.hi[tid].g = mine;
+                L.hi[tid].Sx = suf_after.x;
+                L.hi[tid].Sv = suf_after.v;
+                L.hi[tid].Cafter = NG - (cnt_before + mine.cnt) + (uint32_t)nR;
+            }
+        } else {
+            uint32_t through = cnt_before;
+            for (int g = g0; g < g1; ++g) {
+                const GroupAgg G = a.agg[g];
+                through += G.cnt;
+                if (g > tstar && G.cnt) {
+                    mine_u = g;
+                    L.hi[tid].g = G;
+                    L.hi[tid].Sx = (float)a.scan[g].Sx;
+                    L.hi[tid].Sv = a.scan[g].Sv;
+                    L.hi[tid].Cafter = NG - through + (uint32_t)nR;
+                    break;
+                }
+            }
+        }
+        int dummy;
+        block_max_min(-1, mine_u, L, &dummy, &u);
+    }
+    Anch lo_node = left;
+    if (tstar >= 0)
+        lo_node = L.lo[tstar / gpt];
     if (u >= T) {
         // root between the last group and the right node
-        if (tid == 0) {
-            const double b = gap_root(lo_node, right, (double)nR, k, a.alpha, c);
-            *a.out_b = b;
-            st->b = b;
-            st->solve_state = isfinite(b) ? kSolveOk : kSolveRejectHigh;
-        }
+        if (tid == 0)
+            finish(a, gap_root(lo_node, right, (double)nR, k, a.alpha, c));
         return;
     }
-    const GroupAgg U = a.agg[u];
-    Anch Su;
-    Su.x = a.scan[u].Sx;
-    Su.v = a.scan[u].Sv;
-    Su.has = Su.x != INFINITY;
-    const unsigned long long Cu = a.scan[u].Cafter;
+    const RowHi Ur = L.hi[u / gpt];
+    const GroupAgg U = Ur.g;
+    const Anch Su = node(Ur.Sx, Ur.Sv);
+    const uint32_t Cu = Ur.Cafter;
     if (U.lo == U.hi) {
         // every value of the group is equal: the root lies before it
-        if (tid == 0) {
-            Anch t;
-            t.has = 1;
-            t.x = U.lo;
-            t.v = U.TB;
-            const Anch hi_node = bwd(t, Su, c);
-            const double b = gap_root(lo_node, hi_node, (double)(U.cnt + Cu), k, a.alpha, c);
-            *a.out_b = b;
-            st->b = b;
-            st->solve_state = isfinite(b) ? kSolveOk : kSolveRejectHigh;
-        }
+        if (tid == 0)
+            finish(a, gap_root(lo_node, bwd(node(U.lo, U.TB), Su, c), (double)U.cnt + (double)Cu, k, a.alpha, c));
+        return;
+    }
+    const int cntu = (int)U.cnt;
+    if (cntu > kBucketCap) {
+        if (tid == 0)
+            st->solve_state = kSolveBucketOverflow;
         return;
     }
 
-    // ---- level 2: elements of group u -------------------------------------------
-    // group sizes are <= kBucketCap (band buckets that are not all-equal) or
-    // kTile (full-sort tiles), so each thread holds at most kEpt elements
-    constexpr int kEpt = 8;
-    static_assert(kBucketCap <= kEpt * kT && kTile <= kEpt * kT, "group too large for level 2");
-    const int cntu = (int)U.cnt;
-    const int ept = (cntu + kT - 1) / kT;
+    // ---- level 2: the located group, sorted in LDS ------------------------------
+    {
+        const float* xg = a.sorted + U.start;
+        if (a.tails) {
+            // band buckets arrive unordered: sort the bucket
+            uint32_t* spare = reinterpret_cast<uint32_t*>(L.bv);
+            if (cntu <= kST)
+                sort_group_into<1>(xg, cntu, L.keys, spare);
+            else if (cntu <= 2 * kST)
+                sort_group_into<2>(xg, cntu, L.keys, spare);
+            else if (cntu <= 4 * kST)
+                sort_group_into<4>(xg, cntu, L.keys, spare);
+            else if (cntu <= 8 * kST)
+                sort_group_into<8>(xg, cntu, L.keys, spare);
+            else
+                sort_group_into<16>(xg, cntu, L.keys, spare);
+        } else {
+            // full-sort tiles arrive sorted
+            for (int i = tid; i < cntu; i += kST)
+                L.keys[i] = float_to_key(xg[i]);
+        }
+        __syncthreads();
+    }
+    const int ept = (cntu + kST - 1) / kST;
     const int e0 = tid * ept < cntu ? tid * ept : cntu;
     const int e1 = e0 + ept < cntu ? e0 + ept : cntu;
-    float xs[kEpt];
-    double Av[kEpt];  // prefix within this thread's elements, anchored at xs[i]
-    double Bv[kEpt];  // suffix within this thread's elements, anchored at xs[i]
-    const float* xg = a.sorted + U.start;
-#pragma unroll
-    for (int i = 0; i < kEpt; ++i)
-        xs[i] = (e0 + i < e1) ? xg[e0 + i] : 0.f;
-    Anch lp;
-    lp.has = 0;
-    lp.x = 0.0;
-    lp.v = 0.0;
-#pragma unroll
-    for (int i = 0; i < kEpt; ++i) {
-        if (e0 + i < e1) {
-            Anch t;
-            t.has = 1;
-            t.x = xs[i];
-            t.v = 1.0;
-            lp = fwd(lp, t, c);
-        }
-        Av[i] = lp.v;
+    // this thread's elements: the backward chain (suffix within the thread,
+    // anchored at each element) kept in LDS, the forward fold in registers
+    Anch ls = empty_suf();
+    for (int j = e1 - 1; j >= e0; --j) {
+        ls = bwd(node(key_to_float(L.keys[j]), 1.0), ls, c);
+        L.bv[j] = ls.v;
     }
-    Anch ls;
-    ls.has = 0;
-    ls.x = 0.0;
-    ls.v = 0.0;
-#pragma unroll
-    for (int i = kEpt - 1; i >= 0; --i) {
-        if (e0 + i < e1) {
-            Anch t;
-            t.has = 1;
-            t.x = xs[i];
-            t.v = 1.0;
-            ls = bwd(t, ls, c);
-        }
-        Bv[i] = ls.v;
-    }
-    const Anch ex_pre = fwd(lo_node, wg_scan<true>(lp, L, c).excl, c);
-    const Anch ex_suf = bwd(wg_scan<false>(ls, L, c).excl, Su, c);
+    Anch lp = empty_pre();
+    for (int j = e0; j < e1; ++j)
+        lp = fwd(lp, node(key_to_float(L.keys[j]), 1.0), c);
+    const Scan2Part part2 = scan2_publish(lp, ls, 0u, c, L.wt);
+    __syncthreads();  // [1]
+    const Scan2 s2 = scan2_finish(L.wt, part2, c);
+    const Anch ex_pre = fwd(lo_node, s2.pre_before, c);
+    const Anch ex_suf = bwd(s2.suf_after, Su, c);
 
+    // breakpoint masses: A_j walks forward from everything before, B_{j+1}
+    // is the stored chain re-anchored onto everything after
     int jc = -1;
-#pragma unroll
-    for (int i = 0; i < kEpt; ++i) {
-        const int j = e0 + i;
-        if (j < e1) {
-            Anch Ai;
-            Ai.has = 1;
-            Ai.x = xs[i];
-            Ai.v = Av[i];
-            const Anch Aj = fwd(ex_pre, Ai, c);
-            Anch Bn = ex_suf;
-            if (i + 1 < kEpt && j + 1 < e1) {
-                Anch Bi;
-                Bi.has = 1;
-                Bi.x = xs[i + 1];
-                Bi.v = Bv[i + 1];
-                Bn = bwd(Bi, ex_suf, c);
-            }
-            const double C = (double)(cntu - 1 - j) + (double)Cu;
-            const double m = mass_at((double)xs[i], Aj.v, C, Bn, c);
-            if (m >= k)
-                jc = j;
+    Anch jlo = empty_pre(), jhi = empty_suf();
+    Anch A = ex_pre;
+    for (int j = e0; j < e1; ++j) {
+        const float xj = key_to_float(L.keys[j]);
+        A = fwd(A, node(xj, 1.0), c);
+        const Anch Bn = j + 1 < e1 ? bwd(node(key_to_float(L.keys[j + 1]), L.bv[j + 1]), ex_suf, c) : ex_suf;
+        if (mass_at(xj, A.v, (double)(cntu - 1 - j) + (double)Cu, Bn, c) >= k) {
+            jc = j;
+            jlo = A;
+            jhi = Bn;
         }
     }
-    const int jstar = wg_max_int(jc, red);
-    // owners publish the two ends of the gap
-    if (jstar < 0 && tid == 0) {
-        bc_d[0] = lo_node.x;
-        bc_d[1] = lo_node.v;
-        bc_i[0] = lo_node.has;
-    }
-#pragma unroll
-    for (int i = 0; i < kEpt; ++i) {
-        const int j = e0 + i;
-        if (j < e1 && j == jstar) {
-            Anch Ai;
-            Ai.has = 1;
-            Ai.x = xs[i];
-            Ai.v = Av[i];
-            const Anch Aj = fwd(ex_pre, Ai, c);
-            bc_d[0] = Aj.x;
-            bc_d[1] = Aj.v;
-            bc_i[0] = 1;
-        }
-        if (j < e1 && j == jstar + 1) {
-            Anch Bi;
-            Bi.has = 1;
-            Bi.x = xs[i];
-            Bi.v = Bv[i];
-            const Anch Bj = bwd(Bi, ex_suf, c);
-            bc_d[2] = Bj.x;
-            bc_d[3] = Bj.v;
-            bc_i[1] = 1;
-        }
-    }
-    if (jstar + 1 >= cntu && tid == 0) {
-        bc_d[2] = Su.x;
-        bc_d[3] = Su.v;
-        bc_i[1] = Su.has;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        Anch lo, hi;
-        lo.x = bc_d[0];
-        lo.v = bc_d[1];
-        lo.has = bc_i[0];
-        hi.x = bc_d[2];
-        hi.v = bc_d[3];
-        hi.has = bc_i[1];
-        const double C = (jstar + 1 < cntu) ? (double)(cntu - 1 - jstar) + (double)Cu : (double)Cu;
-        const double b = gap_root(lo, hi, C, k, a.alpha, c);
-        *a.out_b = b;
-        st->b = b;
-        st->solve_state = isfinite(b) ? kSolveOk : kSolveRejectHigh;
+    int jstar, unused;
+    block_max_min(jc, 0, L, &jstar, &unused);  // [1]
+    if (jstar >= 0) {
+        if (jc == jstar)
+            finish(a, gap_root(jlo, jhi, (double)(cntu - 1 - jstar) + (double)Cu, k, a.alpha, c));
+    } else if (tid == 0) {
+        // the root lies before the group's first point
+        const Anch B0 = bwd(node(key_to_float(L.keys[0]), L.bv[0]), ex_suf, c);
+        finish(a, gap_root(lo_node, B0, (double)cntu + (double)Cu, k, a.alpha, c));
     }
 }
 
 hipError_t launch_solve(const SolveArgs& a, hipStream_t stream)
 {
-    STK_LAUNCH(kKSolve, stream, solve_kernel, dim3(1), dim3(kT), 0, stream, a);
+    STK_LAUNCH(kKSolve, stream, solve_kernel, dim3(1), dim3(kST), 0, stream, a);
     return hipGetLastError();
 }
 

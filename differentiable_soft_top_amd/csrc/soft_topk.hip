@@ -51,14 +51,24 @@ int32_t grid_for(int64_t n, int tile_scores, int cap)
     return (int32_t)std::max<int64_t>(1, std::min<int64_t>(g, cap));
 }
 
-int32_t pass1_blocks(int64_t n) { return grid_for(n, kPass1TileScores, kGridPass1); }
+// Pass 1 keeps about kPass1TilesPerGroup tiles per work-group (its per-group
+// cost -- the status read, the band flush, the partial -- is latency), with
+// at least one work-group per CU when there are that many tiles.
+int32_t pass1_blocks(int64_t n)
+{
+    const int64_t tiles = (n + kPass1TileScores - 1) / kPass1TileScores;
+    const int64_t spread = std::min<int64_t>(tiles, kCUs);
+    const int64_t g = std::max<int64_t>(spread, tiles / kPass1TilesPerGroup);
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(g, kGridPass1));
+}
 int32_t emit_blocks(int64_t n)
 {
     return grid_for(n, 4 * kStreamThreads * (n >= kStreamLargeMin ? kEmitBatchLarge : kEmitBatchSmall), kGridEmit);
 }
 int32_t vjp_tile(int64_t n) { return 4 * kStreamThreads * (n >= kStreamLargeMin ? kVjpBatchLarge : kVjpBatchSmall); }
-int32_t vjp_reduce_blocks(int64_t n) { return grid_for(n, vjp_tile(n), kGridVjpReduce); }
-int32_t vjp_apply_blocks(int64_t n) { return grid_for(n, vjp_tile(n), kGridVjpApply); }
+int32_t vjp_grid_cap(int64_t n) { return n >= kStreamLargeMin ? kGridVjpLarge : kGridVjpSmall; }
+int32_t vjp_reduce_blocks(int64_t n) { return grid_for(n, vjp_tile(n), vjp_grid_cap(n)); }
+int32_t vjp_apply_blocks(int64_t n) { return grid_for(n, vjp_tile(n), vjp_grid_cap(n)); }
 
 int64_t default_cap(int64_t n)
 {
@@ -327,7 +337,7 @@ int enqueue_pass1(const Ctx& x)
     return SOFT_TOPK_OK;
 }
 
-int enqueue_emit(const Ctx& x)
+int enqueue_emit(const Ctx& x, bool fold_mass)
 {
     EmitArgs e;
     e.s = x.s;
@@ -339,7 +349,7 @@ int enqueue_emit(const Ctx& x)
     e.partials = at<double>(x, x.plan.off_emitpart);
     e.blocks = x.plan.g_emit;
     e.st = x.st;
-    STK_HIP(launch_emit(e, x.stream));
+    STK_HIP(launch_emit(e, fold_mass, x.stream));
     return SOFT_TOPK_OK;
 }
 
@@ -448,18 +458,18 @@ int enqueue_fullsort(const Ctx& x, const Status& range)
     return SOFT_TOPK_OK;
 }
 
-// After a solve: snapshot the certificate (slot 0), enqueue the emission and
-// its fp64 mass sum, snapshot again (slot 1).  The host then waits on slot 0
-// only, unless the mass must gate the result.
-int enqueue_certify_emit(const Ctx& x)
+// After a solve: snapshot the certificate (slot 0) and enqueue the emission
+// with its per-work-group fp64 sums of p.  When the mass is to be waited for,
+// also enqueue the fold of those sums and a second snapshot (slot 1).
+int enqueue_certify_emit(const Ctx& x, bool wait_mass)
 {
     int rc = enqueue_status_copy(x, 0);
     if (rc)
         return rc;
-    rc = enqueue_emit(x);
+    rc = enqueue_emit(x, wait_mass);
     if (rc)
         return rc;
-    return enqueue_status_copy(x, 1);
+    return wait_mass ? enqueue_status_copy(x, 1) : SOFT_TOPK_OK;
 }
 
 bool mass_ok(const Status& h, double k, double tol)
@@ -644,7 +654,7 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
             int rc = enqueue_round(x, rl, rr, q);
             if (rc)
                 return rc;
-            rc = enqueue_certify_emit(x);
+            rc = enqueue_certify_emit(x, wait_mass);
             if (rc)
                 return rc;
             rc = wait_status(0, &h);
@@ -714,7 +724,7 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
         rc = enqueue_fullsort(x, h);
         if (rc)
             return rc;
-        rc = enqueue_certify_emit(x);
+        rc = enqueue_certify_emit(x, wait_mass);
         if (rc)
             return rc;
         rc = wait_status(0, &h);

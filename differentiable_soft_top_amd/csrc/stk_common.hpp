@@ -47,6 +47,32 @@ __device__ __forceinline__ double exp2_nonpos(double y)
     return ldexp(p, (int)j);
 }
 
+// The same function with the polynomial in Estrin's scheme: a few more
+// operations but a dependency depth of 5 instead of 13, for chains of
+// dependent exponentials (scans) where latency, not throughput, decides.
+__device__ __forceinline__ double exp2_nonpos_lowdepth(double y)
+{
+    y = fmax(y, -1100.0);
+    y = fmin(y, 0.0);
+    const double j = __builtin_rint(y);
+    const double t = (y - j) * kLn2;
+    const double t2 = t * t;
+    const double t4 = t2 * t2;
+    const double t8 = t4 * t4;
+    const double q01 = fma(t, 1.0, 1.0);
+    const double q23 = fma(t, 0.16666666666666666, 0.5);
+    const double q45 = fma(t, 0.008333333333333333, 0.041666666666666664);
+    const double q67 = fma(t, 0.0001984126984126984, 0.001388888888888889);
+    const double q89 = fma(t, 2.7557319223985893e-06, 2.48015873015873e-05);
+    const double qab = fma(t, 2.505210838544172e-08, 2.755731922398589e-07);
+    const double r0 = fma(q23, t2, q01);
+    const double r1 = fma(q67, t2, q45);
+    const double r2 = fma(qab, t2, q89);
+    const double s0 = fma(r1, t4, r0);
+    const double s1 = fma(2.08767569878681e-09, t4, r2);
+    return ldexp(fma(s1, t8, s0), (int)j);
+}
+
 // e^(x/alpha) for x <= 0 given inv = log2(e)/alpha.
 __device__ __forceinline__ double exp_scaled_nonpos(double x, double log2e_over_alpha)
 {

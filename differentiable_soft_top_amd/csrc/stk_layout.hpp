@@ -22,14 +22,20 @@ constexpr int kVjpBatchLarge = 4;
 constexpr int kVjpBatchSmall = 1;
 constexpr int64_t kStreamLargeMin = 1 << 24;
 constexpr int kGridPass1 = 2048;
+constexpr int kPass1TilesPerGroup = 5;
+constexpr int kCUs = 256;                // compute units of an MI355X
 constexpr int kGridEmit = 2048;
-constexpr int kGridVjpReduce = 512;
-constexpr int kGridVjpApply = 512;
-constexpr int kSelectThreads = 1024;     // bracket select, segment solve
+// VJP grids: vectors past kStreamLargeMin stream from HBM, where fewer
+// concurrent streams keep more DRAM pages open; smaller ones largely sit in
+// the last-level cache and want more work-groups in flight.
+constexpr int kGridVjpLarge = 256;
+constexpr int kGridVjpSmall = 1024;
+constexpr int kSelectThreads = 1024;     // bracket select
+constexpr int kSolveThreads = 512;       // segment solve
 constexpr int kPilot = 2048;             // pilot sample size of the select step
 constexpr int kCandCap = 16384;          // candidate keys held in LDS by the select step
 constexpr int kBuckets = 512;            // value buckets of the band sort
-constexpr int kBucketCap = 8192;         // largest bucket sorted in LDS
+constexpr int kBucketCap = 8192;         // largest group the solve sorts in LDS
 constexpr int kBandGroups = 128;         // work-groups of band histogram/scatter
 constexpr int kBandChunkMin = 2048;      // band elements per such work-group (at least)
 constexpr int kSortThreads = 256;        // threads of bucket-sort / tile work-groups
@@ -240,7 +246,7 @@ struct EmitArgs {
     int32_t blocks;
     Status* st;
 };
-hipError_t launch_emit(const EmitArgs& a, hipStream_t stream);
+hipError_t launch_emit(const EmitArgs& a, bool fold_mass, hipStream_t stream);
 
 struct VjpArgs {
     const float* g;

@@ -11,13 +11,14 @@
 namespace stk {
 
 enum KernelId : int {
-    kKSample = 0,
+    kKSample = 0,   // the diagnostic sampler
     kKPilot,
+    kKFilter,
     kKSelect,
     kKPass1,
     kKBandHist,
     kKBandScatter,
-    kKBucketSort,
+    kKBucketAgg,
     kKSolve,
     kKRadixUp,
     kKRadixDown,

@@ -84,10 +84,11 @@ typedef struct soft_topk_params {
                                (1e-3 + 1e-12 * n)                                    */
     int32_t verify_mass;    /* 1: wait for the certification pass (fp64 sum of p)
                                and reject a b whose mass misses k by more than
-                               mass_tolerance; 0 (default): that pass still runs
-                               on the device, but the call returns once the exact
-                               bracket certificate is in (it is also waited for
-                               whenever stats are requested)                       */
+                               mass_tolerance; 0 (default): the call returns once
+                               the exact bracket certificate is in, and the
+                               emission's fp64 partial sums of p are not folded
+                               (the pass runs in full whenever stats are
+                               requested, and stats.mass is NaN otherwise)      */
 } soft_topk_params;
 
 /* Host-side record of one forward call (all fields written on success). */
@@ -123,13 +124,13 @@ size_t soft_topk_backward_workspace_bytes(int64_t n);
  * out_p[i] = F((scores[i] - b)/alpha).  out_b: one fp64 (device) receiving b.
  * workspace: soft_topk_workspace_bytes(n, NULL) bytes of device memory, any
  * contents, 256-byte aligned.
- * Synchronisation: enqueues on `stream` and waits (a ~100-byte status
+ * Synchronisation: enqueues on `stream` and waits (a 256-byte status
  * read-back) until the segment solve has certified the bracket, so that the
  * route is settled on return.  b is final in device memory at that point; the
- * emission of p (and its fp64 mass sum) is already enqueued behind it and
- * completes in stream order, so any later work on `stream` sees the final p.
- * With params->verify_mass = 1 or a stats record, the call also waits for the
- * mass sum and rejects a b whose mass misses k.
+ * emission of p is already enqueued behind it and completes in stream order,
+ * so any later work on `stream` sees the final p.  With
+ * params->verify_mass = 1 or a stats record, the fp64 mass sum of p is also
+ * completed and waited for, and a b whose mass misses k is rejected.
  * Errors: EINVAL / EWORKSPACE before any launch; ENONFINITE if a score is not
  * finite (out_p / out_b then hold no result); EHIP with the HIP status kept
  * for soft_topk_last_hip_error(); ESOLVE should not happen (every route ends
