@@ -54,89 +54,6 @@ hipError_t launch_debug_sample(const float* s, int64_t n, float alpha, uint64_t 
 
 
 // ---------------------------------------------------------------------------
-// Exact selection of up to two order statistics (1-based ranks r[0], r[1]) of
-// cnt u32 keys held in LDS, by the whole work-group: most-significant-digit
-// radix select, four 8-bit digits, both targets refined together.  A rank
-// outside [1, cnt] is skipped (its output is left untouched).
-// ---------------------------------------------------------------------------
-__device__ void lds_select2(const uint32_t* keys, int cnt, int64_t r0, int64_t r1, uint32_t* out0, uint32_t* out1)
-{
-    __shared__ uint32_t hist[2][256];
-    __shared__ uint32_t prefix[2];
-    __shared__ int64_t rank[2];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    if (tid == 0) {
-        prefix[0] = 0;
-        prefix[1] = 0;
-        rank[0] = r0;
-        rank[1] = r1;
-    }
-    const bool act0 = r0 >= 1 && r0 <= cnt;
-    const bool act1 = r1 >= 1 && r1 <= cnt;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-        for (int i = tid; i < 512; i += blockDim.x)
-            (&hist[0][0])[i] = 0;
-        __syncthreads();
-        const uint32_t p0 = prefix[0], p1 = prefix[1];
-        for (int i = tid; i < cnt; i += blockDim.x) {
-            const uint32_t k = keys[i];
-            const uint32_t d = (k >> shift) & 0xFFu;
-            if (act0 && ((k ^ p0) & hmask) == 0)
-                atomicAdd(&hist[0][d], 1u);
-            if (act1 && ((k ^ p1) & hmask) == 0)
-                atomicAdd(&hist[1][d], 1u);
-        }
-        __syncthreads();
-        // wave t (t = 0, 1) finds the digit holding rank[t]
-        if (wave < 2 && (wave == 0 ? act0 : act1)) {
-            const int t = wave;
-            const uint32_t c0 = hist[t][4 * lane], c1 = hist[t][4 * lane + 1];
-            const uint32_t c2 = hist[t][4 * lane + 2], c3 = hist[t][4 * lane + 3];
-            const uint32_t mine = c0 + c1 + c2 + c3;
-            uint32_t incl = mine;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const uint32_t o = __shfl_up(incl, off, kWave);
-                if (lane >= off)
-                    incl += o;
-            }
-            const uint32_t excl = incl - mine;
-            const int64_t r = rank[t];
-            if ((int64_t)excl < r && r <= (int64_t)incl) {
-                int64_t rr = r - excl;
-                int d = 4 * lane;
-                if (rr > c0) {
-                    rr -= c0;
-                    ++d;
-                    if (rr > c1) {
-                        rr -= c1;
-                        ++d;
-                        if (rr > c2) {
-                            rr -= c2;
-                            ++d;
-                        }
-                    }
-                }
-                rank[t] = rr;
-                prefix[t] |= (uint32_t)d << shift;
-            }
-        }
-        __syncthreads();
-    }
-    if (tid == 0) {
-        if (act0)
-            *out0 = prefix[0];
-        if (act1)
-            *out1 = prefix[1];
-    }
-    __syncthreads();
-}
-
-// ---------------------------------------------------------------------------
 // The localisation in three kernels, so no single work-group has to read all
 // m samples (one CU ingests only ~10 GB/s of freshly written data):
 //   pilot  (1 work-group)  -- the first P = min(m, kPilot) samples, two of
@@ -146,20 +63,48 @@ __device__ void lds_select2(const uint32_t* keys, int cnt, int64_t r0, int64_t r
 //          lower pilot bound, appended to a candidate list if between them;
 //   select (1 work-group)  -- the target order statistics among the
 //          candidates, offset by the count below.
-// If the candidates overflow or a target falls outside them, a pilot value
-// with a more conservative rank is used (the bracket only widens, so the
-// certificate still decides).  The pilot kernel also clears the per-round
-// counters of the status block: it runs first in every bracketed round.
+// Order statistics are read off a work-group sort of the keys held in
+// registers (block_bitonic_regs).  If the candidates overflow or a target
+// falls outside them, a pilot value with a more conservative rank is used
+// (the bracket only widens, so the certificate still decides).  The pilot
+// kernel also clears the per-round counters of the status block: it runs
+// first in every bracketed round.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kSelectThreads) void pilot_kernel(SampleArgs a)
+namespace {
+
+// Sorting shapes: a full 1024-thread work-group (four waves per SIMD hide
+// the latency of the dependent compare-exchange chains), as few keys per
+// thread as the count allows.
+constexpr int kPilotThreads = 1024;
+constexpr int kPilotPer = kPilot / kPilotThreads;  // pilot keys per thread
+static_assert(kPilot % kPilotThreads == 0, "pilot keys per thread");
+static_assert(kCandCap == 16 * kSelectThreads, "select shapes cover the candidate capacity");
+
+// The keys at 1-based ranks r0 and r1 of the sorted blocked registers v
+// (kThreads * R positions) go to out[0] / out[1] (a rank outside the
+// positions writes nothing).
+template <int R>
+__device__ __forceinline__ void pick_ranks(const uint32_t (&v)[R], int64_t r0, int64_t r1, uint32_t* out)
 {
-    __shared__ uint32_t pilot[kPilot];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t rank = (int64_t)threadIdx.x * R + r + 1;
+        if (rank == r0)
+            out[0] = v[r];
+        if (rank == r1)
+            out[1] = v[r];
+    }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kPilotThreads) void pilot_kernel(SampleArgs a)
+{
+    __shared__ uint32_t buf[2][kPilot];
     __shared__ uint32_t sel[2];
     const int tid = threadIdx.x;
     Status* st = a.st;
     if (tid == 0) {
-        sel[0] = 0u;            // open lower bound
-        sel[1] = 0xFFFFFFFFu;   // open upper bound
         st->nB = 0;
         st->solve_state = kSolveNotRun;
         st->emit_done = 0;
@@ -168,10 +113,20 @@ __global__ __launch_bounds__(kSelectThreads) void pilot_kernel(SampleArgs a)
         st->below_n = 0;
     }
     const int P = a.m < kPilot ? a.m : kPilot;
-    for (int i = tid; i < P; i += blockDim.x)
-        pilot[i] = float_to_key(sample_value(a.s, a.n, a.alpha, a.k0, a.k1, (uint32_t)i));
+    uint32_t v[kPilotPer];
+#pragma unroll
+    for (int r = 0; r < kPilotPer; ++r) {
+        const int i = tid * kPilotPer + r;
+        v[r] = i < P ? float_to_key(sample_value(a.s, a.n, a.alpha, a.k0, a.k1, (uint32_t)i)) : 0xFFFFFFFFu;
+    }
+    block_bitonic_regs<kPilotThreads, kPilotPer>(v, buf[0], buf[1]);
+    if (tid == 0) {
+        sel[0] = 0u;            // open lower bound
+        sel[1] = 0xFFFFFFFFu;   // open upper bound
+    }
     __syncthreads();
-    lds_select2(pilot, P, a.pilot_lo, a.pilot_hi, &sel[0], &sel[1]);
+    pick_ranks<kPilotPer>(v, a.pilot_lo >= 1 ? a.pilot_lo : -1, a.pilot_hi <= P ? a.pilot_hi : -1, sel);
+    __syncthreads();
     if (tid == 0) {
         st->pilot_lo = sel[0];
         st->pilot_hi = sel[1];
@@ -218,9 +173,25 @@ __global__ __launch_bounds__(256) void filter_kernel(SampleArgs a)
     }
 }
 
+// Sort the cnt candidate keys (R per thread, padded with all-ones keys) and
+// pick two ranks.
+template <int R>
+__device__ void select_from(const uint32_t* __restrict__ cand, int cnt, int64_t r0, int64_t r1, uint32_t* buf0,
+                            uint32_t* buf1, uint32_t* out)
+{
+    uint32_t v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = threadIdx.x * R + r;
+        v[r] = i < cnt ? cand[i] : 0xFFFFFFFFu;
+    }
+    block_bitonic_regs<kSelectThreads, R>(v, buf0, buf1);
+    pick_ranks<R>(v, r0, r1, out);
+}
+
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
 {
-    __shared__ uint32_t cand[kCandCap];
+    __shared__ uint32_t buf[2][kCandCap];
     __shared__ uint32_t sel[2];
     const int tid = threadIdx.x;
     Status* st = a.st;
@@ -234,18 +205,22 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
     const bool left_in = !left_inf && (uint64_t)rl > cb && (uint64_t)rl <= cb + cc;
     const bool right_in = !right_inf && (uint64_t)rr > cb && (uint64_t)rr <= cb + cc;
     if (!overflow && (left_in || right_in)) {
-        // every candidate load issued at once
-        constexpr int kPer = kCandCap / kSelectThreads;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int i = j * kSelectThreads + tid;
-            if ((uint64_t)i < cc)
-                cand[i] = a.cand[i];
-        }
-        __syncthreads();
-        lds_select2(cand, (int)cc, left_in ? rl - (int64_t)cb : 0, right_in ? rr - (int64_t)cb : 0, &sel[0],
-                    &sel[1]);
+        // the sort shape follows the candidate count (uniform branch)
+        const int cnt = (int)cc;
+        const int64_t r0 = left_in ? rl - (int64_t)cb : -1;
+        const int64_t r1 = right_in ? rr - (int64_t)cb : -1;
+        if (cnt <= kSelectThreads)
+            select_from<1>(a.cand, cnt, r0, r1, buf[0], buf[1], sel);
+        else if (cnt <= 2 * kSelectThreads)
+            select_from<2>(a.cand, cnt, r0, r1, buf[0], buf[1], sel);
+        else if (cnt <= 4 * kSelectThreads)
+            select_from<4>(a.cand, cnt, r0, r1, buf[0], buf[1], sel);
+        else if (cnt <= 8 * kSelectThreads)
+            select_from<8>(a.cand, cnt, r0, r1, buf[0], buf[1], sel);
+        else
+            select_from<16>(a.cand, cnt, r0, r1, buf[0], buf[1], sel);
     }
+    __syncthreads();
     if (tid == 0) {
         // open pilot bounds stand for -inf / +inf
         const float lo_val = lo_key == 0u ? -INFINITY : key_to_float(lo_key);
@@ -287,7 +262,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
 
 hipError_t launch_localize(const SampleArgs& sa, const SelectArgs& se, hipStream_t stream)
 {
-    STK_LAUNCH(kKPilot, stream, pilot_kernel, dim3(1), dim3(kSelectThreads), 0, stream, sa);
+    STK_LAUNCH(kKPilot, stream, pilot_kernel, dim3(1), dim3(kPilotThreads), 0, stream, sa);
     const int blocks = (sa.m + 255) / 256;
     STK_LAUNCH(kKFilter, stream, filter_kernel, dim3(blocks), dim3(256), 0, stream, sa);
     STK_LAUNCH(kKSelect, stream, select_kernel, dim3(1), dim3(kSelectThreads), 0, stream, se);

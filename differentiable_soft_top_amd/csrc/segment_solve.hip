@@ -183,60 +183,6 @@ __device__ __forceinline__ Scan2 scan2_finish(const WaveTot* wt, const Scan2Part
     return r;
 }
 
-// Ascending sort of kST * R keys, R per thread in blocked order (thread t
-// holds positions t*R .. t*R+R-1).  Bitonic network: partners inside a
-// thread are exchanged in registers, partners inside a wave by lane
-// shuffles, partners in other waves through LDS (two buffers alternate, one
-// barrier per such stage).  Every stage index is a compile-time constant.
-template <int R>
-__device__ __forceinline__ void block_bitonic_regs(uint32_t (&v)[R], uint32_t* buf0, uint32_t* buf1)
-{
-    constexpr int n2 = kST * R;
-    const int tid = threadIdx.x;
-    int flip = 0;
-#pragma unroll
-    for (int k = 2; k <= n2; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            if (j < R) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int p = r ^ j;
-                    if (p > r) {
-                        const bool up = ((tid * R + r) & k) == 0;
-                        const uint32_t a = v[r], b = v[p];
-                        const bool sw = (a > b) == up;
-                        v[r] = sw ? b : a;
-                        v[p] = sw ? a : b;
-                    }
-                }
-            } else if (j < kWave * R) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int i = tid * R + r;
-                    const uint32_t o = (uint32_t)__shfl_xor((int)v[r], j / R, kWave);
-                    const bool take_min = ((i & j) == 0) == ((i & k) == 0);
-                    v[r] = take_min ? (v[r] < o ? v[r] : o) : (v[r] > o ? v[r] : o);
-                }
-            } else {
-                uint32_t* buf = flip ? buf1 : buf0;
-                flip ^= 1;
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    buf[tid * R + r] = v[r];
-                __syncthreads();
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int i = tid * R + r;
-                    const uint32_t o = buf[i ^ j];
-                    const bool take_min = ((i & j) == 0) == ((i & k) == 0);
-                    v[r] = take_min ? (v[r] < o ? v[r] : o) : (v[r] > o ? v[r] : o);
-                }
-            }
-        }
-    }
-}
-
 // Load cnt values (padded with +inf keys to kST * R), sort, store to keys.
 template <int R>
 __device__ void sort_group_into(const float* x, int cnt, uint32_t* keys, uint32_t* spare)
@@ -248,7 +194,7 @@ __device__ void sort_group_into(const float* x, int cnt, uint32_t* keys, uint32_
         const int i = tid * R + r;
         v[r] = i < cnt ? float_to_key(x[i]) : 0xFFFFFFFFu;
     }
-    block_bitonic_regs<R>(v, keys, spare);
+    block_bitonic_regs<kST, R>(v, keys, spare);
     __syncthreads();  // the last LDS stage's reads are done
 #pragma unroll
     for (int r = 0; r < R; ++r)

@@ -371,7 +371,6 @@ int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q)
     se.m = x.plan.m;
     se.r_left = rl;
     se.r_right = rr;
-    se.st = x.st;
     STK_HIP(launch_localize(sa, se, x.stream));
     int rc = enqueue_pass1(x);
     if (rc)

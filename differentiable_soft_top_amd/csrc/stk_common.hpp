@@ -2,8 +2,8 @@
 //
 // Nothing here is specific to one kernel: the fp64 exponential used wherever
 // a sum of exponentials feeds the threshold, the order-preserving fp32 key,
-// the Philox4x32-10 counter-based generator, wave-64 reductions and an LDS
-// bitonic sort.
+// the Philox4x32-10 counter-based generator, wave-64 reductions and a
+// work-group bitonic sort of keys held in registers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -191,63 +191,61 @@ __device__ __forceinline__ uint32_t rank_in_mask(uint64_t mask)
 }
 
 // ---------------------------------------------------------------------------
-// Ascending bitonic sort of npow2 u32 keys in LDS by the whole work-group
-// (npow2 a power of two, at most 2 * kBitonicPairs * blockDim.x; the caller
-// pads with 0xFFFFFFFF and synchronises before the call).  Every stage walks
-// compare-exchange pairs, not indices, so no thread idles, and issues all its
-// pairs' LDS loads before any store.
+// Ascending sort of kThreads * R u32 keys held R per thread in blocked order
+// (thread t holds positions t*R .. t*R+R-1) by a work-group of kThreads.
+// Bitonic network: partners inside a thread are exchanged in registers,
+// partners inside a wave by lane shuffles, partners in other waves through
+// LDS (buf0 / buf1, each kThreads * R keys, alternate; one barrier per such
+// stage).  Every stage index is a compile-time constant.  The caller
+// synchronises before reusing buf0 / buf1.
 // ---------------------------------------------------------------------------
-constexpr int kBitonicPairs = 16;
-
-template <int kPPT>
-__device__ inline void lds_bitonic_sort_ppt(uint32_t* a, int npow2)
+template <int kThreads, int R>
+__device__ __forceinline__ void block_bitonic_regs(uint32_t (&v)[R], uint32_t* buf0, uint32_t* buf1)
 {
+    constexpr int n2 = kThreads * R;
     const int tid = threadIdx.x;
-    const int nt = blockDim.x;
-    const int pairs = npow2 >> 1;
-    for (int k = 2; k <= npow2; k <<= 1) {
+    int flip = 0;
+#pragma unroll
+    for (int k = 2; k <= n2; k <<= 1) {
+#pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-            uint32_t x[kPPT], y[kPPT];
+            if (j < R) {
 #pragma unroll
-            for (int r = 0; r < kPPT; ++r) {
-                const int p = tid + r * nt;
-                if (p < pairs) {
-                    const int i = 2 * p - (p & (j - 1));  // bit log2(j) of i is 0
-                    x[r] = a[i];
-                    y[r] = a[i + j];
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < kPPT; ++r) {
-                const int p = tid + r * nt;
-                if (p < pairs) {
-                    const int i = 2 * p - (p & (j - 1));
-                    const bool up = (i & k) == 0;
-                    if ((x[r] > y[r]) == up) {
-                        a[i] = y[r];
-                        a[i + j] = x[r];
+                for (int r = 0; r < R; ++r) {
+                    const int p = r ^ j;
+                    if (p > r) {
+                        const bool up = ((tid * R + r) & k) == 0;
+                        const uint32_t a = v[r], b = v[p];
+                        const bool sw = (a > b) == up;
+                        v[r] = sw ? b : a;
+                        v[p] = sw ? a : b;
                     }
                 }
+            } else if (j < kWave * R) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int i = tid * R + r;
+                    const uint32_t o = (uint32_t)__shfl_xor((int)v[r], j / R, kWave);
+                    const bool take_min = ((i & j) == 0) == ((i & k) == 0);
+                    v[r] = take_min ? (v[r] < o ? v[r] : o) : (v[r] > o ? v[r] : o);
+                }
+            } else {
+                uint32_t* buf = flip ? buf1 : buf0;
+                flip ^= 1;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    buf[tid * R + r] = v[r];
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int i = tid * R + r;
+                    const uint32_t o = buf[i ^ j];
+                    const bool take_min = ((i & j) == 0) == ((i & k) == 0);
+                    v[r] = take_min ? (v[r] < o ? v[r] : o) : (v[r] > o ? v[r] : o);
+                }
             }
-            __syncthreads();
         }
     }
-}
-
-// Dispatch on the pairs per thread so no masked-off pair slots are issued.
-__device__ inline void lds_bitonic_sort(uint32_t* a, int npow2)
-{
-    const int ppt = (npow2 / 2 + blockDim.x - 1) / blockDim.x;
-    if (ppt <= 1)
-        lds_bitonic_sort_ppt<1>(a, npow2);
-    else if (ppt <= 2)
-        lds_bitonic_sort_ppt<2>(a, npow2);
-    else if (ppt <= 4)
-        lds_bitonic_sort_ppt<4>(a, npow2);
-    else if (ppt <= 8)
-        lds_bitonic_sort_ppt<8>(a, npow2);
-    else
-        lds_bitonic_sort_ppt<kBitonicPairs>(a, npow2);
 }
 
 // ---------------------------------------------------------------------------
