@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kSortThreads) void band_scatter_kernel(BandArgs a)
     constexpr int kPer = kBuckets / kSortThreads;  // buckets per thread
     static_assert(kPer == 2, "one uint2 per thread and row");
     __shared__ uint32_t cursor[kBuckets];
-    __shared__ uint32_t scan_tmp[kSortThreads];
+    __shared__ uint32_t scan_tmp[kSortThreads / kWave];
     const Status* st = a.st;
     if (band_unusable(st, a.cap))
         return;
@@ -187,15 +187,23 @@ __global__ __launch_bounds__(kSortThreads) void band_scatter_kernel(BandArgs a)
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
         local += tot[j];
-    scan_tmp[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < kSortThreads; off <<= 1) {
-        const uint32_t v = tid >= off ? scan_tmp[tid - off] : 0u;
-        __syncthreads();
-        scan_tmp[tid] += v;
-        __syncthreads();
+    // exclusive scan of the per-thread sums: lane shuffles, then the wave
+    // totals through LDS (one barrier)
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    uint32_t incl = local;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off, kWave);
+        if (lane >= off)
+            incl += o;
     }
-    uint32_t base = scan_tmp[tid] - local;
+    if (lane == kWave - 1)
+        scan_tmp[wave] = incl;
+    __syncthreads();
+    uint32_t base = incl - local;
+    for (int w = 0; w < wave; ++w)
+        base += scan_tmp[w];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int b = tid * kPer + j;
@@ -265,6 +273,65 @@ __device__ Pass1Partial fold_partials_wave(const Pass1Partial* p, int i0, int i1
     return r;
 }
 
+// ---------------------------------------------------------------------------
+// Order-independent sums.  A bucket's elements arrive in an order that
+// depends on atomic reservations (pass-1 band appends, scatter cursors), so
+// fp64 accumulation would round differently from run to run.  Each term
+// (an anchored exponential, in [0, 1]) is instead cut to a multiple of 2^-64
+// (truncation, a function of the term alone) and summed exactly as a 128-bit
+// integer; the total is converted back to fp64 once.  The cut costs under
+// 2^-64 per term, far below fp64 rounding of the sum.
+// ---------------------------------------------------------------------------
+struct Fix128 {
+    uint64_t lo, hi;  // value = (hi * 2^64 + lo) * 2^-64
+};
+
+__device__ __forceinline__ Fix128 fix_of(double e)
+{
+    const uint64_t bits = (uint64_t)__double_as_longlong(e);
+    const int E = (int)((bits >> 52) & 0x7FF);
+    Fix128 r;
+    r.lo = 0;
+    r.hi = 0;
+    if (E == 0 || (bits >> 63))
+        return r;  // zero, subnormal (below 2^-1022) or negative: nothing
+    const uint64_t mi = (bits & 0xFFFFFFFFFFFFFull) | (1ull << 52);  // e = mi * 2^(E - 1075)
+    const int sh = E - 1011;                                         // e * 2^64 = mi * 2^sh
+    if (sh >= 64) {
+        r.hi = mi << (sh - 64);  // only for e >= 2^11, not reached for terms in [0, 1]
+    } else if (sh > 0) {
+        r.lo = mi << sh;
+        r.hi = mi >> (64 - sh);
+    } else if (sh > -64) {
+        r.lo = mi >> (-sh);
+    }
+    return r;
+}
+
+__device__ __forceinline__ void fix_add(Fix128& a, const Fix128& b)
+{
+    const uint64_t lo = a.lo + b.lo;
+    a.hi += b.hi + (lo < a.lo ? 1ull : 0ull);
+    a.lo = lo;
+}
+
+__device__ __forceinline__ Fix128 fix_wave_sum(Fix128 v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        Fix128 o;
+        o.lo = __shfl_xor(v.lo, off, kWave);
+        o.hi = __shfl_xor(v.hi, off, kWave);
+        fix_add(v, o);
+    }
+    return v;
+}
+
+__device__ __forceinline__ double fix_to_double(const Fix128& v)
+{
+    return (double)v.hi + ldexp((double)v.lo, -64);
+}
+
 // One work-group per bucket: the bucket's summary for the level-1 scan of the
 // segment solve -- count, smallest and largest value, TA = sum e^{(x-hi)/alpha},
 // TB = sum e^{-(x-lo)/alpha} -- from its unordered elements.  Only the one
@@ -274,7 +341,7 @@ __device__ Pass1Partial fold_partials_wave(const Pass1Partial* p, int i0, int i1
 __global__ __launch_bounds__(kSortThreads) void bucket_agg_kernel(BandArgs a)
 {
     constexpr int kHeld = 4;  // elements per thread kept in registers between the two sweeps
-    __shared__ double red[2][kSortThreads / kWave];
+    __shared__ Fix128 red[2][kSortThreads / kWave];
     __shared__ float redf[2][kSortThreads / kWave];
     const Status* st = a.st;
     if (band_unusable(st, a.cap))
@@ -336,38 +403,38 @@ __global__ __launch_bounds__(kSortThreads) void bucket_agg_kernel(BandArgs a)
         lo = fminf(lo, redf[0][w]);
         hi = fmaxf(hi, redf[1][w]);
     }
-    // sweep 2: the anchored exponential sums
+    // sweep 2: the anchored exponential sums, exact and order-independent
     const double c = a.log2e_over_alpha;
     const double dlo = lo, dhi = hi;
-    double TA = 0.0, TB = 0.0;
+    Fix128 TA{0ull, 0ull}, TB{0ull, 0ull};
 #pragma unroll
     for (int j = 0; j < kHeld; ++j) {
         const uint32_t i = (uint32_t)(j * kSortThreads + tid);
         if (i < cnt) {
-            TA += exp2_nonpos(((double)v[j] - dhi) * c);
-            TB += exp2_nonpos((dlo - (double)v[j]) * c);
+            fix_add(TA, fix_of(exp2_nonpos(((double)v[j] - dhi) * c)));
+            fix_add(TB, fix_of(exp2_nonpos((dlo - (double)v[j]) * c)));
         }
     }
     for (uint32_t i = kHeld * kSortThreads + tid; i < cnt; i += kSortThreads) {
         const double t = x[i];
-        TA += exp2_nonpos((t - dhi) * c);
-        TB += exp2_nonpos((dlo - t) * c);
+        fix_add(TA, fix_of(exp2_nonpos((t - dhi) * c)));
+        fix_add(TB, fix_of(exp2_nonpos((dlo - t) * c)));
     }
-    TA = wave_sum(TA);
-    TB = wave_sum(TB);
+    TA = fix_wave_sum(TA);
+    TB = fix_wave_sum(TB);
     if (lane == 0) {
         red[0][wave] = TA;
         red[1][wave] = TB;
     }
     __syncthreads();
     if (tid == 0) {
-        double sa = 0.0, sb = 0.0;
+        Fix128 sa{0ull, 0ull}, sb{0ull, 0ull};
         for (int w = 0; w < kSortThreads / kWave; ++w) {
-            sa += red[0][w];
-            sb += red[1][w];
+            fix_add(sa, red[0][w]);
+            fix_add(sb, red[1][w]);
         }
-        g.TA = sa;
-        g.TB = sb;
+        g.TA = fix_to_double(sa);
+        g.TB = fix_to_double(sb);
         g.lo = lo;
         g.hi = hi;
         a.agg[b] = g;

@@ -36,11 +36,8 @@ __global__ void reset_status_kernel(Status* st, int open_bracket)
         st->nB = 0;
         st->solve_state = kSolveNotRun;
         st->emit_done = 0;
-        st->ticket_pass1 = 0;
-        st->ticket_hist = 0;
-        st->ticket_emit = 0;
+        st->ticket_select = 0;
         st->ticket_radix = 0;
-        st->ticket_tile = 0;
     }
 }
 

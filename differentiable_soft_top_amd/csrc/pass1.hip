@@ -58,7 +58,8 @@ struct Ctx1 {
 
 struct Acc1 {
     double SL, SR;
-    uint32_t nL, nR;                            // per-lane tail counts
+    uint32_t nL, nR;                            // per-lane counts of near tail scores
+    uint32_t farL, farR;                        // wave-wide counts of far tail scores
     float bmin, bmax;
     float amax;                                 // max |s| (+-inf shows here)
     uint32_t nan;                               // a NaN reached the window list
@@ -128,10 +129,15 @@ __device__ __forceinline__ void drain_window(uint32_t cnt, const Ctx1& x, Acc1& 
 // Classify kVals scores of this lane (kAll: all valid, else bit i of
 // `valid`).  Far scores are counted; window scores are compacted into the
 // wave's list, which is then drained.  Called by every lane of the wave.
+// The far counts are wave-wide (scalar popcounts of the compare masks):
+// far-left directly, far-right as what is neither far-left nor in the
+// window.
 template <bool kAll>
 __device__ __forceinline__ void classify(const float (&v)[kVals], uint32_t valid, const Ctx1& x, Acc1& acc)
 {
-    uint32_t cnt = 0;  // wave-uniform fill of the window list
+    uint32_t cnt = 0;   // wave-uniform fill of the window list
+    uint32_t lo_n = 0;  // wave-uniform far-left count
+    uint32_t ok_n = 0;  // wave-uniform count of valid scores
     const uint64_t live = __builtin_amdgcn_ballot_w64(true);
 #pragma unroll
     for (int i = 0; i < kVals; ++i) {
@@ -139,17 +145,23 @@ __device__ __forceinline__ void classify(const float (&v)[kVals], uint32_t valid
         const float s = v[i];
         const bool lo = s < x.tL;
         const bool hi = s >= x.tR;
-        acc.nL += (ok && lo) ? 1u : 0u;
-        acc.nR += (ok && hi) ? 1u : 0u;
         acc.amax = fmaxf(acc.amax, ok ? fabsf(s) : 0.f);
         // window mask from the ballots of the two compares (stays scalar)
-        uint64_t m = ~(__builtin_amdgcn_ballot_w64(lo) | __builtin_amdgcn_ballot_w64(hi)) & live;
-        if (!kAll)
-            m &= __builtin_amdgcn_ballot_w64(ok);
+        const uint64_t mlo = __builtin_amdgcn_ballot_w64(lo);
+        uint64_t m = ~(mlo | __builtin_amdgcn_ballot_w64(hi)) & live;
+        uint64_t mok = live;
+        if (!kAll) {
+            mok = __builtin_amdgcn_ballot_w64(ok);
+            m &= mok;
+        }
+        lo_n += (uint32_t)__popcll(mlo & mok);
+        ok_n += (uint32_t)__popcll(mok);
         if (ok && !lo && !hi)  // this lane's bit of m
             x.win[cnt + rank_in_mask(m)] = s;
         cnt += (uint32_t)__popcll(m);
     }
+    acc.farL += lo_n;
+    acc.farR += ok_n - lo_n - cnt;
     drain_window(cnt, x, acc);
 }
 
@@ -219,7 +231,7 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
     x.stage_count = &stage_count;
     x.win = win_buf[wave];
 
-    Acc1 acc{0.0, 0.0, 0u, 0u, INFINITY, -INFINITY, 0.f, 0u};
+    Acc1 acc{0.0, 0.0, 0u, 0u, 0u, 0u, INFINITY, -INFINITY, 0.f, 0u};
     const int64_t G = gridDim.x;
     int64_t rest = 0;  // first score not covered by whole tiles
 
@@ -293,8 +305,9 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
     // fence per work-group would write back the whole L2 each time.
     const double SL = wave_sum(acc.SL);
     const double SR = wave_sum(acc.SR);
-    const uint32_t nL = wave_sum_u32(acc.nL);
-    const uint32_t nR = wave_sum_u32(acc.nR);
+    // far counts are the same in every lane of a wave: counted once
+    const uint32_t nL = wave_sum_u32(acc.nL) + acc.farL;
+    const uint32_t nR = wave_sum_u32(acc.nR) + acc.farR;
     uint32_t nf = (acc.nan != 0u || !(acc.amax < INFINITY)) ? 1u : 0u;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)

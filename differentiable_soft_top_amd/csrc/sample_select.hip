@@ -54,15 +54,15 @@ hipError_t launch_debug_sample(const float* s, int64_t n, float alpha, uint64_t 
 
 
 // ---------------------------------------------------------------------------
-// The localisation in three kernels, so no single work-group has to read all
+// The localisation in two kernels, so no single work-group has to read all
 // m samples (one CU ingests only ~10 GB/s of freshly written data):
 //   pilot  (1 work-group)  -- the first P = min(m, kPilot) samples, two of
 //          their order statistics that enclose the target ranks with a wide
 //          margin (ranks from the host);
-//   filter (m/256 groups)  -- every sample regenerated, counted if below the
+//   filter (m/1024 groups) -- every sample regenerated, counted if below the
 //          lower pilot bound, appended to a candidate list if between them;
-//   select (1 work-group)  -- the target order statistics among the
-//          candidates, offset by the count below.
+//   select (the last filter work-group to finish) -- the target order
+//          statistics among the candidates, offset by the count below.
 // Order statistics are read off a work-group sort of the keys held in
 // registers (block_bitonic_regs).  If the candidates overflow or a target
 // falls outside them, a pilot value with a more conservative rank is used
@@ -111,6 +111,7 @@ __global__ __launch_bounds__(kPilotThreads) void pilot_kernel(SampleArgs a)
         st->nonfinite = 0;
         st->cand_n = 0;
         st->below_n = 0;
+        st->ticket_select = 0;
     }
     const int P = a.m < kPilot ? a.m : kPilot;
     uint32_t v[kPilotPer];
@@ -133,46 +134,6 @@ __global__ __launch_bounds__(kPilotThreads) void pilot_kernel(SampleArgs a)
     }
 }
 
-__global__ __launch_bounds__(256) void filter_kernel(SampleArgs a)
-{
-    __shared__ uint32_t wcnt[2][256 / kWave];
-    __shared__ uint32_t base_s;
-    Status* st = a.st;
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int32_t j = blockIdx.x * 256 + tid;
-    const bool valid = j < a.m;
-    const uint32_t key = valid ? float_to_key(sample_value(a.s, a.n, a.alpha, a.k0, a.k1, (uint32_t)j)) : 0u;
-    const uint32_t lo = st->pilot_lo, hi = st->pilot_hi;
-    const bool below = valid && key < lo;
-    const bool cand = valid && key >= lo && key <= hi;
-    const uint64_t bm = __ballot(below);
-    const uint64_t cm = __ballot(cand);
-    if (lane == 0) {
-        wcnt[0][wave] = (uint32_t)__popcll(bm);
-        wcnt[1][wave] = (uint32_t)__popcll(cm);
-    }
-    __syncthreads();
-    uint32_t woff = 0, tot_c = 0, tot_b = 0;
-    for (int w = 0; w < 256 / kWave; ++w) {
-        woff += w < wave ? wcnt[1][w] : 0u;
-        tot_c += wcnt[1][w];
-        tot_b += wcnt[0][w];
-    }
-    if (tid == 0) {
-        base_s = tot_c ? atomicAdd(&st->cand_n, tot_c) : 0u;
-        if (tot_b)
-            atomicAdd(&st->below_n, tot_b);
-    }
-    __syncthreads();
-    if (cand) {
-        const uint32_t pos = base_s + woff + rank_in_mask(cm);
-        if (pos < (uint32_t)kCandCap)
-            a.cand[pos] = key;
-    }
-}
-
 // Sort the cnt candidate keys (R per thread, padded with all-ones keys) and
 // pick two ranks.
 template <int R>
@@ -189,19 +150,109 @@ __device__ void select_from(const uint32_t* __restrict__ cand, int cnt, int64_t 
     pick_ranks<R>(v, r0, r1, out);
 }
 
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
+// The same for the largest candidate counts (targets near the median): a
+// bitonic network over LDS, slower but light on registers, so that the
+// common shapes above keep their register budget.
+__device__ void select_from_lds(const uint32_t* __restrict__ cand, int cnt, int64_t r0, int64_t r1, uint32_t* keys,
+                                uint32_t* out)
 {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kCandCap; i += kSelectThreads)
+        keys[i] = i < cnt ? cand[i] : 0xFFFFFFFFu;
+    __syncthreads();
+    for (int k = 2; k <= kCandCap; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int p = tid; p < kCandCap / 2; p += kSelectThreads) {
+                const int i = 2 * p - (p & (j - 1));  // bit log2(j) of i is 0
+                const uint32_t x = keys[i], y = keys[i + j];
+                if ((x > y) == ((i & k) == 0)) {
+                    keys[i] = y;
+                    keys[i + j] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (tid == 0) {
+        if (r0 >= 1 && r0 <= kCandCap)
+            out[0] = keys[r0 - 1];
+        if (r1 >= 1 && r1 <= kCandCap)
+            out[1] = keys[r1 - 1];
+    }
+}
+
+// Filter and select in one kernel.  Every work-group regenerates its share
+// of the samples, counts those below the lower pilot bound and appends those
+// between the bounds to the candidate list.  Then it takes a ticket; the
+// last work-group to finish (its writes made visible by the release fence
+// before each ticket, read after an acquire fence) selects the two target
+// order statistics among the candidates.  No work-group waits for another.
+__global__ __launch_bounds__(kSelectThreads) void filter_select_kernel(SampleArgs a, SelectArgs se)
+{
+    constexpr int kWaves = kSelectThreads / kWave;
     __shared__ uint32_t buf[2][kCandCap];
     __shared__ uint32_t sel[2];
-    const int tid = threadIdx.x;
+    __shared__ uint32_t wcnt[2][kWaves];
+    __shared__ uint32_t base_s;
+    __shared__ uint32_t is_last;
     Status* st = a.st;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+
+    // ---- filter ------------------------------------------------------------
+    {
+        const int32_t j = blockIdx.x * kSelectThreads + tid;
+        const bool valid = j < a.m;
+        const uint32_t key = valid ? float_to_key(sample_value(a.s, a.n, a.alpha, a.k0, a.k1, (uint32_t)j)) : 0u;
+        const uint32_t lo = st->pilot_lo, hi = st->pilot_hi;
+        const bool below = valid && key < lo;
+        const bool cand = valid && key >= lo && key <= hi;
+        const uint64_t bm = __ballot(below);
+        const uint64_t cm = __ballot(cand);
+        if (lane == 0) {
+            wcnt[0][wave] = (uint32_t)__popcll(bm);
+            wcnt[1][wave] = (uint32_t)__popcll(cm);
+        }
+        __syncthreads();
+        uint32_t woff = 0, tot_c = 0, tot_b = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            woff += w < wave ? wcnt[1][w] : 0u;
+            tot_c += wcnt[1][w];
+            tot_b += wcnt[0][w];
+        }
+        if (tid == 0) {
+            base_s = tot_c ? atomicAdd(&st->cand_n, tot_c) : 0u;
+            if (tot_b)
+                atomicAdd(&st->below_n, tot_b);
+        }
+        __syncthreads();
+        if (cand) {
+            const uint32_t pos = base_s + woff + rank_in_mask(cm);
+            if (pos < (uint32_t)kCandCap)
+                a.cand[pos] = key;
+        }
+    }
+
+    // ---- ticket: the last work-group selects ---------------------------------
+    __syncthreads();
+    if (tid == 0) {
+        fence_agent();  // release this work-group's candidates and counts
+        const uint32_t t = atomicAdd(&st->ticket_select, 1u);
+        is_last = t == gridDim.x - 1 ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!is_last)
+        return;
+    fence_agent();  // acquire every work-group's candidates and counts
+
     const uint64_t cb = st->below_n;
     const uint64_t cc = st->cand_n;
     const uint32_t lo_key = st->pilot_lo, hi_key = st->pilot_hi;
-    const int64_t rl = a.r_left, rr = a.r_right;
+    const int64_t rl = se.r_left, rr = se.r_right;
     const bool overflow = cc > (uint64_t)kCandCap;
     const bool left_inf = rl <= 0;
-    const bool right_inf = rr > (int64_t)a.m;
+    const bool right_inf = rr > (int64_t)se.m;
     const bool left_in = !left_inf && (uint64_t)rl > cb && (uint64_t)rl <= cb + cc;
     const bool right_in = !right_inf && (uint64_t)rr > cb && (uint64_t)rr <= cb + cc;
     if (!overflow && (left_in || right_in)) {
@@ -210,15 +261,15 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
         const int64_t r0 = left_in ? rl - (int64_t)cb : -1;
         const int64_t r1 = right_in ? rr - (int64_t)cb : -1;
         if (cnt <= kSelectThreads)
-            select_from<1>(a.cand, cnt, r0, r1, buf[0], buf[1], sel);
+            select_from<1>(se.cand, cnt, r0, r1, buf[0], buf[1], sel);
         else if (cnt <= 2 * kSelectThreads)
-            select_from<2>(a.cand, cnt, r0, r1, buf[0], buf[1], sel);
+            select_from<2>(se.cand, cnt, r0, r1, buf[0], buf[1], sel);
         else if (cnt <= 4 * kSelectThreads)
-            select_from<4>(a.cand, cnt, r0, r1, buf[0], buf[1], sel);
+            select_from<4>(se.cand, cnt, r0, r1, buf[0], buf[1], sel);
         else if (cnt <= 8 * kSelectThreads)
-            select_from<8>(a.cand, cnt, r0, r1, buf[0], buf[1], sel);
+            select_from<8>(se.cand, cnt, r0, r1, buf[0], buf[1], sel);
         else
-            select_from<16>(a.cand, cnt, r0, r1, buf[0], buf[1], sel);
+            select_from_lds(se.cand, cnt, r0, r1, buf[0], sel);
     }
     __syncthreads();
     if (tid == 0) {
@@ -263,9 +314,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
 hipError_t launch_localize(const SampleArgs& sa, const SelectArgs& se, hipStream_t stream)
 {
     STK_LAUNCH(kKPilot, stream, pilot_kernel, dim3(1), dim3(kPilotThreads), 0, stream, sa);
-    const int blocks = (sa.m + 255) / 256;
-    STK_LAUNCH(kKFilter, stream, filter_kernel, dim3(blocks), dim3(256), 0, stream, sa);
-    STK_LAUNCH(kKSelect, stream, select_kernel, dim3(1), dim3(kSelectThreads), 0, stream, se);
+    const int blocks = (sa.m + kSelectThreads - 1) / kSelectThreads;
+    STK_LAUNCH(kKSelect, stream, filter_select_kernel, dim3(blocks), dim3(kSelectThreads), 0, stream, sa, se);
     return hipGetLastError();
 }
 

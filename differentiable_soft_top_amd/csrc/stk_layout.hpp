@@ -85,12 +85,9 @@ struct alignas(16) Status {
     uint32_t pad3;
     // "last work-group" tickets; zeroed by the first kernel of each forward
     // and returned to zero by the work-group that consumes them
-    uint32_t ticket_pass1;
-    uint32_t ticket_hist;
-    uint32_t ticket_emit;
-    uint32_t ticket_radix;
-    uint32_t ticket_tile;
-    uint32_t pad4[3];
+    uint32_t ticket_select;      // filter work-groups done (cleared by the pilot kernel)
+    uint32_t ticket_radix;       // radix upsweep work-groups done (returned to 0 by the last)
+    uint32_t pad4[6];
 };
 static_assert(sizeof(Status) <= 256, "status block must fit 256 bytes");
 
