@@ -160,8 +160,10 @@ __global__ __launch_bounds__(kStreamThreads) void emit_finalize_kernel(EmitArgs 
     __shared__ double red[kStreamThreads / kWave];
     __shared__ double m;
     Status* st = a.st;
-    if (st->solve_state != kSolveOk)
+    if (st->solve_state != kSolveOk) {
+        publish_status(st, a.mirror);
         return;
+    }
     double t = 0.0;
     for (int i = threadIdx.x; i < a.blocks; i += kStreamThreads)
         t += a.partials[i];
@@ -170,6 +172,8 @@ __global__ __launch_bounds__(kStreamThreads) void emit_finalize_kernel(EmitArgs 
         st->mass = m;
         st->emit_done = 1;
     }
+    __syncthreads();
+    publish_status(st, a.mirror);
 }
 
 hipError_t launch_emit(const EmitArgs& a, bool fold_mass, hipStream_t stream)

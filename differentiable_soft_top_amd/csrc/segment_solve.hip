@@ -286,9 +286,8 @@ __device__ __forceinline__ void finish(const SolveArgs& a, double b)
 //   4. level-2 scans, breakpoint masses                                 [1]
 //   5. the last breakpoint with mass >= k; its owner applies the closed
 //      form                                                             [1]
-__global__ __launch_bounds__(kST) void solve_kernel(SolveArgs a)
+__device__ void solve_body(const SolveArgs& a, SolveLds& L)
 {
-    __shared__ SolveLds L;
     Status* st = a.st;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -645,6 +644,15 @@ __global__ __launch_bounds__(kST) void solve_kernel(SolveArgs a)
         const Anch B0 = bwd(node(key_to_float(L.keys[0]), L.bv[0]), ex_suf, c);
         finish(a, gap_root(lo_node, B0, (double)cntu + (double)Cu, k, a.alpha, c));
     }
+}
+
+__global__ __launch_bounds__(kST) void solve_kernel(SolveArgs a)
+{
+    __shared__ SolveLds L;
+    solve_body(a, L);
+    // every exit of the body ends here: publish the status for the host
+    __syncthreads();
+    publish_status(a.st, a.mirror);
 }
 
 hipError_t launch_solve(const SolveArgs& a, hipStream_t stream)

@@ -267,12 +267,16 @@ struct Ctx {
     hipStream_t stream;
     Status* st;
     uint64_t seed;
+    Status* mirror0;   // device address of host mirror slot 0 (solve)
+    Status* mirror1;   // device address of host mirror slot 1 (mass fold)
 };
 
-// Two pinned status slots per host thread: slot 0 is filled right after the
-// segment solve (the bracket certificate), slot 1 after the certification
-// pass (the fp64 mass).  Each copy is followed by an event the host can wait
-// on without draining the rest of the stream.
+// Two status mirrors per host thread in pinned, fine-grained host memory:
+// slot 0 is written by the segment solve as it finishes (the bracket
+// certificate), slot 1 by the fold of the certification pass (the fp64 mass).
+// Each is followed by an event the host can wait on without draining the
+// rest of the stream.  A plain copy into slot 0 serves the rare reads that
+// follow no solve (the score range of the full-sort route).
 struct HostSlots {
     Status* pinned = nullptr;
     hipEvent_t ev[2] = {nullptr, nullptr};
@@ -283,11 +287,26 @@ int ensure_host_slots()
 {
     if (!g_host.pinned) {
         void* ptr = nullptr;
-        STK_HIP(hipHostMalloc(&ptr, 2 * sizeof(Status), hipHostMallocDefault));
+        STK_HIP(hipHostMalloc(&ptr, 2 * sizeof(Status), hipHostMallocCoherent | hipHostMallocMapped | hipHostMallocPortable));
         g_host.pinned = static_cast<Status*>(ptr);
         for (int i = 0; i < 2; ++i)
             STK_HIP(hipEventCreateWithFlags(&g_host.ev[i], hipEventDisableTiming));
     }
+    return SOFT_TOPK_OK;
+}
+
+// Device-usable address of a mirror slot.
+Status* mirror_slot(int slot)
+{
+    void* dev = nullptr;
+    if (hipHostGetDevicePointer(&dev, g_host.pinned, 0) != hipSuccess || dev == nullptr)
+        return nullptr;
+    return static_cast<Status*>(dev) + slot;
+}
+
+int mark_status(const Ctx& x, int slot)
+{
+    STK_HIP(hipEventRecord(g_host.ev[slot], x.stream));
     return SOFT_TOPK_OK;
 }
 
@@ -297,8 +316,7 @@ int enqueue_status_copy(const Ctx& x, int slot)
     if (rc)
         return rc;
     STK_HIP(hipMemcpyAsync(g_host.pinned + slot, x.st, sizeof(Status), hipMemcpyDeviceToHost, x.stream));
-    STK_HIP(hipEventRecord(g_host.ev[slot], x.stream));
-    return SOFT_TOPK_OK;
+    return mark_status(x, slot);
 }
 
 int wait_status(int slot, Status* host)
@@ -349,6 +367,7 @@ int enqueue_emit(const Ctx& x, bool fold_mass)
     e.partials = at<double>(x, x.plan.off_emitpart);
     e.blocks = x.plan.g_emit;
     e.st = x.st;
+    e.mirror = x.mirror1;
     STK_HIP(launch_emit(e, fold_mass, x.stream));
     return SOFT_TOPK_OK;
 }
@@ -404,6 +423,7 @@ int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q)
     so.log2e_over_alpha = x.c;
     so.out_b = x.b;
     so.st = x.st;
+    so.mirror = x.mirror0;
     STK_HIP(launch_solve(so, x.stream));
     return SOFT_TOPK_OK;
 }
@@ -453,22 +473,24 @@ int enqueue_fullsort(const Ctx& x, const Status& range)
     so.log2e_over_alpha = x.c;
     so.out_b = x.b;
     so.st = x.st;
+    so.mirror = x.mirror0;
     STK_HIP(launch_solve(so, x.stream));
     return SOFT_TOPK_OK;
 }
 
-// After a solve: snapshot the certificate (slot 0) and enqueue the emission
-// with its per-work-group fp64 sums of p.  When the mass is to be waited for,
-// also enqueue the fold of those sums and a second snapshot (slot 1).
+// After a solve (which has written mirror slot 0 as it finished): mark slot
+// 0 and enqueue the emission with its per-work-group fp64 sums of p.  When
+// the mass is to be waited for, also enqueue the fold of those sums (which
+// writes slot 1) and mark slot 1.
 int enqueue_certify_emit(const Ctx& x, bool wait_mass)
 {
-    int rc = enqueue_status_copy(x, 0);
+    int rc = mark_status(x, 0);
     if (rc)
         return rc;
     rc = enqueue_emit(x, wait_mass);
     if (rc)
         return rc;
-    return wait_mass ? enqueue_status_copy(x, 1) : SOFT_TOPK_OK;
+    return wait_mass ? mark_status(x, 1) : SOFT_TOPK_OK;
 }
 
 bool mass_ok(const Status& h, double k, double tol)
@@ -633,6 +655,13 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
     x.stream = static_cast<hipStream_t>(stream);
     x.st = reinterpret_cast<Status*>(x.ws + plan.off_status);
     x.seed = prm.seed;
+    int hrc = ensure_host_slots();
+    if (hrc)
+        return hrc;
+    x.mirror0 = mirror_slot(0);
+    x.mirror1 = mirror_slot(1);
+    if (!x.mirror0 || !x.mirror1)
+        return SOFT_TOPK_EHIP;
 
     const double tol = prm.mass_tolerance > 0.0 ? prm.mass_tolerance : 1e-3 + 1e-12 * (double)n;
     soft_topk_stats sx;

@@ -90,6 +90,20 @@ struct alignas(16) Status {
     uint32_t pad4[6];
 };
 static_assert(sizeof(Status) <= 256, "status block must fit 256 bytes");
+static_assert(sizeof(Status) % 4 == 0, "status block is copied as 32-bit words");
+
+// Copy the status block to its host-visible mirror: one wave, one 32-bit
+// word per lane.  The caller has synchronised the work-group, so every
+// field this work-group wrote is in place; the stores to the mirror (pinned,
+// fine-grained host memory) are complete when the kernel is.
+__device__ __forceinline__ void publish_status(const Status* st, Status* mirror)
+{
+    constexpr int kWords = (int)(sizeof(Status) / 4);
+    if (mirror == nullptr)
+        return;
+    for (int i = threadIdx.x; i < kWords; i += 64)
+        reinterpret_cast<volatile uint32_t*>(mirror)[i] = reinterpret_cast<const volatile uint32_t*>(st)[i];
+}
 
 struct alignas(16) Pass1Partial {
     double SL, SR;
@@ -205,6 +219,7 @@ struct SolveArgs {
     double log2e_over_alpha;
     double* out_b;
     Status* st;
+    Status* mirror;               // host-visible copy of the status written at the end (may be null)
 };
 hipError_t launch_solve(const SolveArgs& a, hipStream_t stream);
 
@@ -242,6 +257,7 @@ struct EmitArgs {
     double* partials;
     int32_t blocks;
     Status* st;
+    Status* mirror;               // host-visible copy of the status written by the mass fold (may be null)
 };
 hipError_t launch_emit(const EmitArgs& a, bool fold_mass, hipStream_t stream);
 
