@@ -57,6 +57,14 @@ hipError_t launch_reset_status(Status* st, hipStream_t stream, bool open_bracket
 // and the last n mod 4 scores) goes, element by element, to the work-group
 // whose next tile it would be.  Unaligned vectors take a plain element-wise
 // grid-stride loop.  Large vectors use the larger batch.
+//
+// Direction: the emission re-reads the scores pass 1 has just streamed in
+// ascending order, and the VJP's second pass re-reads the scores and the
+// cotangent its first pass has just streamed in ascending order.  Both
+// second passes walk their tiles in descending order, so they begin with the
+// tiles most recently fetched, while those are still held in the caches
+// (measured on MI355X at 10^8 scores: about 5 us off the emission and
+// 15 us off the VJP's second pass).
 namespace {
 
 template <int kB>
@@ -131,7 +139,8 @@ __global__ __launch_bounds__(kStreamThreads) void emit_kernel(EmitArgs a)
         const int64_t T = whole_tiles<kB>(a.n);
         const float4* s4 = reinterpret_cast<const float4*>(a.s);
         float4* p4 = reinterpret_cast<float4*>(a.p);
-        for (int64_t t = blockIdx.x; t < T; t += G) {
+        for (int64_t t0 = blockIdx.x; t0 < T; t0 += G) {
+            const int64_t t = T - 1 - t0;  // descending: see the note above
             float4 v[kB];
             load_q<kB>(s4, t, v);
 #pragma unroll
@@ -268,7 +277,8 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_kernel(VjpArgs a, in
         const float4* s4 = reinterpret_cast<const float4*>(a.s);
         const float4* g4 = reinterpret_cast<const float4*>(a.g);
         float4* o4 = reinterpret_cast<float4*>(a.grad);
-        for (int64_t t = blockIdx.x; t < T; t += G) {
+        for (int64_t t0 = blockIdx.x; t0 < T; t0 += G) {
+            const int64_t t = T - 1 - t0;  // descending: see the note above
             float4 vs[kB], vg[kB];
             load_q<kB>(s4, t, vs);
             load_q<kB>(g4, t, vg);
