@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_PKG, "libsofttopk.so")
 
 OK, EINVAL, ENONFINITE, EWORKSPACE, EHIP, ESOLVE = 0, 1, 2, 3, 4, 5
 PATH_BRACKET, PATH_WIDENED, PATH_FULLSORT = 1, 2, 3
+BAND_DIRECT, BAND_BUCKETS = 1, 2
 REJECT_LOW, REJECT_HIGH, REJECT_OVERFLOW, REJECT_BUCKET, REJECT_MASS = 1, 2, 4, 8, 16
 
 
@@ -26,6 +27,7 @@ class Params(ctypes.Structure):
         ("force_path", ctypes.c_int32),
         ("mass_tolerance", ctypes.c_double),
         ("verify_mass", ctypes.c_int32),
+        ("band_route", ctypes.c_int32),
     ]
 
 
@@ -34,7 +36,7 @@ class Stats(ctypes.Structure):
         ("path", ctypes.c_int32),
         ("rounds", ctypes.c_int32),
         ("reject_mask", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("band_route", ctypes.c_int32),
         ("a_left", ctypes.c_float),
         ("a_right", ctypes.c_float),
         ("n_left", ctypes.c_int64),
@@ -47,7 +49,7 @@ class Stats(ctypes.Structure):
     ]
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class SoftTopKError(RuntimeError):

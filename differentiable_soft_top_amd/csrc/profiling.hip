@@ -12,7 +12,7 @@ namespace stk {
 namespace {
 
 const char* const kNames[kKernelCount] = {
-    "sample", "pilot", "filter", "select", "pass1", "band_hist", "band_scatter", "bucket_agg", "solve",
+    "sample", "filter", "select", "pass1", "band_hist", "band_scatter", "bucket_agg", "solve",
     "radix_upsweep", "radix_downsweep", "tile_agg", "emit", "emit_finalize", "vjp_reduce", "vjp_apply", "reset",
 };
 

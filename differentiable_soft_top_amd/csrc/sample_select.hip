@@ -54,268 +54,273 @@ hipError_t launch_debug_sample(const float* s, int64_t n, float alpha, uint64_t 
 
 
 // ---------------------------------------------------------------------------
-// The localisation in two kernels, so no single work-group has to read all
-// m samples (one CU ingests only ~10 GB/s of freshly written data):
-//   pilot  (1 work-group)  -- the first P = min(m, kPilot) samples, two of
-//          their order statistics that enclose the target ranks with a wide
-//          margin (ranks from the host);
-//   filter (m/1024 groups) -- every sample regenerated, counted if below the
-//          lower pilot bound, appended to a candidate list if between them;
-//   select (the last filter work-group to finish) -- the target order
-//          statistics among the candidates, offset by the count below.
-// Order statistics are read off a work-group sort of the keys held in
-// registers (block_bitonic_regs).  If the candidates overflow or a target
-// falls outside them, a pilot value with a more conservative rank is used
-// (the bracket only widens, so the certificate still decides).  The pilot
-// kernel also clears the per-round counters of the status block: it runs
-// first in every bracketed round.
+// The localisation in two kernels, so no single work-group has to draw all
+// m samples (a CU ingests only ~10 GB/s of freshly written data, and the
+// Philox rounds of 65536 samples would keep one CU busy for tens of us):
+//   filter (m / kFilterPer groups) -- each group draws its kFilterPer
+//          samples, takes two of its own order statistics that enclose the
+//          targets with a wide margin (expected local rank -+ 7 local
+//          binomial standard deviations - 4), counts its samples below the
+//          lower one and stores those between them, in a region of its own;
+//   select (1 group) -- with L the largest group lower bound and H the
+//          smallest upper bound, the rank of any x in [L, H] among all m
+//          samples is (samples below their group's bound) + (candidates
+//          <= x), so the target order statistics are the candidates of
+//          ranks r - below; it also clears the per-round counters of the
+//          status block (it runs right before pass-1).
+// Order statistics are selected digit by digit (block_select2), not sorted.
+// A target that falls outside [L, H] or outside the candidates (a margin
+// broken, about 1e-9 per group and side) is replaced by a conservative
+// bound (the smallest group lower bound / largest upper bound, or an open
+// end): the bracket only widens and the certificate still decides.
 // ---------------------------------------------------------------------------
 namespace {
 
-// Sorting shapes: a full 1024-thread work-group (four waves per SIMD hide
-// the latency of the dependent compare-exchange chains), as few keys per
-// thread as the count allows.
-constexpr int kPilotThreads = 1024;
-constexpr int kPilotPer = kPilot / kPilotThreads;  // pilot keys per thread
-static_assert(kPilot % kPilotThreads == 0, "pilot keys per thread");
-static_assert(kCandCap == 16 * kSelectThreads, "select shapes cover the candidate capacity");
+constexpr int kFilterThreads = kFilterPer;  // one sample per thread
+static_assert(kCandCap == 32 * kSelectThreads, "select shapes cover the candidate capacity");
 
-// The keys at 1-based ranks r0 and r1 of the sorted blocked registers v
-// (kThreads * R positions) go to out[0] / out[1] (a rank outside the
-// positions writes nothing).
-template <int R>
-__device__ __forceinline__ void pick_ranks(const uint32_t (&v)[R], int64_t r0, int64_t r1, uint32_t* out)
+// Local rank bounds of a group of mw samples for global ranks (rl, rr) of
+// m; -1 = open end.
+__device__ __forceinline__ void local_ranks(int64_t rl, int64_t rr, int32_t m, int32_t mw, double q, int64_t* lo,
+                                            int64_t* hi)
 {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int64_t rank = (int64_t)threadIdx.x * R + r + 1;
-        if (rank == r0)
-            out[0] = v[r];
-        if (rank == r1)
-            out[1] = v[r];
+    const double sd = sqrt((double)mw * q * (1.0 - q));
+    *lo = -1;
+    *hi = -1;
+    if (rl >= 1) {
+        const double e = (double)mw * (double)rl / (double)m;
+        const int64_t r = (int64_t)floor(e - 7.0 * sd - 4.0);
+        *lo = r >= 1 ? r : -1;
+    }
+    if (rr <= (int64_t)m) {
+        const double e = (double)mw * (double)rr / (double)m;
+        const int64_t r = (int64_t)ceil(e + 7.0 * sd + 4.0);
+        *hi = r <= (int64_t)mw ? r : -1;
     }
 }
 
-}  // namespace
-
-__global__ __launch_bounds__(kPilotThreads) void pilot_kernel(SampleArgs a)
-{
-    __shared__ uint32_t buf[2][kPilot];
-    __shared__ uint32_t sel[2];
-    const int tid = threadIdx.x;
-    Status* st = a.st;
-    if (tid == 0) {
-        st->nB = 0;
-        st->solve_state = kSolveNotRun;
-        st->emit_done = 0;
-        st->nonfinite = 0;
-        st->cand_n = 0;
-        st->below_n = 0;
-        st->ticket_select = 0;
-    }
-    const int P = a.m < kPilot ? a.m : kPilot;
-    uint32_t v[kPilotPer];
-#pragma unroll
-    for (int r = 0; r < kPilotPer; ++r) {
-        const int i = tid * kPilotPer + r;
-        v[r] = i < P ? float_to_key(sample_value(a.s, a.n, a.alpha, a.k0, a.k1, (uint32_t)i)) : 0xFFFFFFFFu;
-    }
-    block_bitonic_regs<kPilotThreads, kPilotPer>(v, buf[0], buf[1]);
-    if (tid == 0) {
-        sel[0] = 0u;            // open lower bound
-        sel[1] = 0xFFFFFFFFu;   // open upper bound
-    }
-    __syncthreads();
-    pick_ranks<kPilotPer>(v, a.pilot_lo >= 1 ? a.pilot_lo : -1, a.pilot_hi <= P ? a.pilot_hi : -1, sel);
-    __syncthreads();
-    if (tid == 0) {
-        st->pilot_lo = sel[0];
-        st->pilot_hi = sel[1];
-    }
-}
-
-// Sort the cnt candidate keys (R per thread, padded with all-ones keys) and
-// pick two ranks.
+// The keys at ranks r0 / r1 of the cnt candidates spread over the group
+// regions (start offsets off[0..groups], R per thread).
 template <int R>
-__device__ void select_from(const uint32_t* __restrict__ cand, int cnt, int64_t r0, int64_t r1, uint32_t* buf0,
-                            uint32_t* buf1, uint32_t* out)
+__device__ void select_from(const uint32_t* __restrict__ cand, const uint32_t* off, int groups, int cnt, int64_t r0,
+                            int64_t r1, uint32_t* hist, uint32_t* state, uint32_t* out)
 {
     uint32_t v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int i = threadIdx.x * R + r;
-        v[r] = i < cnt ? cand[i] : 0xFFFFFFFFu;
-    }
-    block_bitonic_regs<kSelectThreads, R>(v, buf0, buf1);
-    pick_ranks<R>(v, r0, r1, out);
-}
-
-// The same for the largest candidate counts (targets near the median): a
-// bitonic network over LDS, slower but light on registers, so that the
-// common shapes above keep their register budget.
-__device__ void select_from_lds(const uint32_t* __restrict__ cand, int cnt, int64_t r0, int64_t r1, uint32_t* keys,
-                                uint32_t* out)
-{
-    const int tid = threadIdx.x;
-    for (int i = tid; i < kCandCap; i += kSelectThreads)
-        keys[i] = i < cnt ? cand[i] : 0xFFFFFFFFu;
-    __syncthreads();
-    for (int k = 2; k <= kCandCap; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int p = tid; p < kCandCap / 2; p += kSelectThreads) {
-                const int i = 2 * p - (p & (j - 1));  // bit log2(j) of i is 0
-                const uint32_t x = keys[i], y = keys[i + j];
-                if ((x > y) == ((i & k) == 0)) {
-                    keys[i] = y;
-                    keys[i + j] = x;
-                }
+        uint32_t key = 0xFFFFFFFFu;
+        if (i < cnt) {
+            // the region holding candidate i: the last w with off[w] <= i
+            int lo = 0, hi = groups;  // off[lo] <= i < off[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (off[mid] <= (uint32_t)i)
+                    lo = mid;
+                else
+                    hi = mid;
             }
-            __syncthreads();
+            key = cand[(size_t)lo * kFilterPer + (i - off[lo])];
         }
+        v[r] = key;
     }
-    if (tid == 0) {
-        if (r0 >= 1 && r0 <= kCandCap)
-            out[0] = keys[r0 - 1];
-        if (r1 >= 1 && r1 <= kCandCap)
-            out[1] = keys[r1 - 1];
-    }
+    block_select2<kSelectThreads, R>(v, cnt, r0, r1, hist, state, out);
 }
 
-// Filter and select in one kernel.  Every work-group regenerates its share
-// of the samples, counts those below the lower pilot bound and appends those
-// between the bounds to the candidate list.  Then it takes a ticket; the
-// last work-group to finish (its writes made visible by the release fence
-// before each ticket, read after an acquire fence) selects the two target
-// order statistics among the candidates.  No work-group waits for another.
-__global__ __launch_bounds__(kSelectThreads) void filter_select_kernel(SampleArgs a, SelectArgs se)
+}  // namespace
+
+__global__ __launch_bounds__(kFilterThreads) void filter_kernel(SampleArgs a)
 {
-    constexpr int kWaves = kSelectThreads / kWave;
-    __shared__ uint32_t buf[2][kCandCap];
-    __shared__ uint32_t sel[2];
+    constexpr int kWaves = kFilterThreads / kWave;
+    __shared__ __align__(16) uint32_t hist[1024];  // block_select2 reads it as uint4
+    __shared__ uint32_t sstate[4 + 2 * (1024 / kWave)];  // block_select2 state (1024 threads)
+    __shared__ uint32_t bounds[2];
     __shared__ uint32_t wcnt[2][kWaves];
-    __shared__ uint32_t base_s;
-    __shared__ uint32_t is_last;
-    Status* st = a.st;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-
-    // ---- filter ------------------------------------------------------------
-    {
-        const int32_t j = blockIdx.x * kSelectThreads + tid;
-        const bool valid = j < a.m;
-        const uint32_t key = valid ? float_to_key(sample_value(a.s, a.n, a.alpha, a.k0, a.k1, (uint32_t)j)) : 0u;
-        const uint32_t lo = st->pilot_lo, hi = st->pilot_hi;
-        const bool below = valid && key < lo;
-        const bool cand = valid && key >= lo && key <= hi;
-        const uint64_t bm = __ballot(below);
-        const uint64_t cm = __ballot(cand);
-        if (lane == 0) {
-            wcnt[0][wave] = (uint32_t)__popcll(bm);
-            wcnt[1][wave] = (uint32_t)__popcll(cm);
-        }
-        __syncthreads();
-        uint32_t woff = 0, tot_c = 0, tot_b = 0;
-        for (int w = 0; w < kWaves; ++w) {
-            woff += w < wave ? wcnt[1][w] : 0u;
-            tot_c += wcnt[1][w];
-            tot_b += wcnt[0][w];
-        }
-        if (tid == 0) {
-            base_s = tot_c ? atomicAdd(&st->cand_n, tot_c) : 0u;
-            if (tot_b)
-                atomicAdd(&st->below_n, tot_b);
-        }
-        __syncthreads();
-        if (cand) {
-            const uint32_t pos = base_s + woff + rank_in_mask(cm);
-            if (pos < (uint32_t)kCandCap)
-                a.cand[pos] = key;
-        }
-    }
-
-    // ---- ticket: the last work-group selects ---------------------------------
-    __syncthreads();
+    const int32_t j0 = (int32_t)blockIdx.x * kFilterPer;
+    const int32_t mw = a.m - j0 < kFilterPer ? a.m - j0 : kFilterPer;
+    const bool valid = tid < mw;
+    const uint32_t key = valid ? float_to_key(sample_value(a.s, a.n, a.alpha, a.k0, a.k1, (uint32_t)(j0 + tid)))
+                               : 0xFFFFFFFFu;
+    int64_t rlo, rhi;
+    local_ranks(a.r_left, a.r_right, a.m, mw, a.q, &rlo, &rhi);
     if (tid == 0) {
-        fence_agent();  // release this work-group's candidates and counts
-        const uint32_t t = atomicAdd(&st->ticket_select, 1u);
-        is_last = t == gridDim.x - 1 ? 1u : 0u;
+        bounds[0] = 0u;           // open lower bound
+        bounds[1] = 0xFFFFFFFFu;  // open upper bound
+    }
+    uint32_t v[1] = {key};
+    block_select2<kFilterThreads, 1>(v, mw, rlo, rhi, hist, sstate, bounds);
+    const uint32_t lo = bounds[0], hi = bounds[1];
+    const bool below = valid && key < lo;
+    const bool cand = valid && key >= lo && key <= hi;
+    const uint64_t bm = __builtin_amdgcn_ballot_w64(below);
+    const uint64_t cm = __builtin_amdgcn_ballot_w64(cand);
+    if (lane == 0) {
+        wcnt[0][wave] = (uint32_t)__popcll(bm);
+        wcnt[1][wave] = (uint32_t)__popcll(cm);
     }
     __syncthreads();
-    if (!is_last)
-        return;
-    fence_agent();  // acquire every work-group's candidates and counts
+    uint32_t woff = 0, tot_c = 0, tot_b = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        woff += w < wave ? wcnt[1][w] : 0u;
+        tot_c += wcnt[1][w];
+        tot_b += wcnt[0][w];
+    }
+    if (cand)
+        a.cand[(size_t)blockIdx.x * kFilterPer + woff + rank_in_mask(cm)] = key;
+    if (tid == 0) {
+        FilterRec r;
+        r.below = tot_b;
+        r.cand = tot_c;
+        r.lo = lo;
+        r.hi = hi;
+        a.rec[blockIdx.x] = r;
+    }
+}
 
-    const uint64_t cb = st->below_n;
-    const uint64_t cc = st->cand_n;
-    const uint32_t lo_key = st->pilot_lo, hi_key = st->pilot_hi;
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs se)
+{
+    constexpr int kWaves = kSelectThreads / kWave;
+    static_assert(kSelectThreads == 1024 && kFilterThreads == 1024, "select state sized for 1024 threads; one thread per filter group (m <= 262144)");
+    __shared__ __align__(16) uint32_t hist[1024];  // block_select2 reads it as uint4
+    __shared__ uint32_t sstate[4 + 2 * (1024 / kWave)];  // block_select2 state (1024 threads)
+    __shared__ uint32_t sel[2];
+    __shared__ uint32_t off[kSelectThreads + 1];
+    __shared__ uint32_t wred[5][kWaves];
+    Status* st = se.st;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int G = se.groups;
+
+    // ---- the groups' records: candidate offsets, totals, bound extremes ------
+    FilterRec r;
+    r.below = 0;
+    r.cand = 0;
+    r.lo = 0u;           // neutral for the max of lower bounds
+    r.hi = 0xFFFFFFFFu;  // neutral for the min of upper bounds
+    uint32_t lo_min = 0xFFFFFFFFu, hi_max = 0u;
+    if (tid < G) {
+        r = se.rec[tid];
+        lo_min = r.lo;
+        hi_max = r.hi;
+    }
+    uint32_t incl = r.cand;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o, kWave);
+        if (lane >= o)
+            incl += t;
+    }
+    uint32_t bsum = r.below, lmax = r.lo, hmin = r.hi, lmin = lo_min, hmax = hi_max;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        bsum += __shfl_xor(bsum, o, kWave);
+        lmax = max(lmax, (uint32_t)__shfl_xor(lmax, o, kWave));
+        hmin = min(hmin, (uint32_t)__shfl_xor(hmin, o, kWave));
+        lmin = min(lmin, (uint32_t)__shfl_xor(lmin, o, kWave));
+        hmax = max(hmax, (uint32_t)__shfl_xor(hmax, o, kWave));
+    }
+    if (lane == kWave - 1)
+        wred[0][wave] = incl;  // wave total of candidates
+    if (lane == 0) {
+        wred[1][wave] = bsum;
+        wred[2][wave] = lmax;
+        wred[3][wave] = hmin;
+        wred[4][wave] = lmin;
+    }
+    __syncthreads();
+    uint32_t base = 0, C = 0, B = 0, L = 0u, H = 0xFFFFFFFFu, Lmin = 0xFFFFFFFFu;
+    for (int w = 0; w < kWaves; ++w) {
+        base += w < wave ? wred[0][w] : 0u;
+        C += wred[0][w];
+        B += wred[1][w];
+        L = max(L, wred[2][w]);
+        H = min(H, wred[3][w]);
+        Lmin = min(Lmin, wred[4][w]);
+    }
+    __syncthreads();
+    if (lane == 0)
+        wred[4][wave] = hmax;
+    if (tid <= G)
+        off[tid] = base + incl - r.cand;  // exclusive prefix; off[G] = C
+    if (tid == 0)
+        off[G] = C;
+    __syncthreads();
+    uint32_t Hmax = 0u;
+    for (int w = 0; w < kWaves; ++w)
+        Hmax = max(Hmax, wred[4][w]);
+
+    // ---- the target order statistics among the candidates --------------------
     const int64_t rl = se.r_left, rr = se.r_right;
-    const bool overflow = cc > (uint64_t)kCandCap;
-    const bool left_inf = rl <= 0;
-    const bool right_inf = rr > (int64_t)se.m;
-    const bool left_in = !left_inf && (uint64_t)rl > cb && (uint64_t)rl <= cb + cc;
-    const bool right_in = !right_inf && (uint64_t)rr > cb && (uint64_t)rr <= cb + cc;
-    if (!overflow && (left_in || right_in)) {
-        // the sort shape follows the candidate count (uniform branch)
-        const int cnt = (int)cc;
-        const int64_t r0 = left_in ? rl - (int64_t)cb : -1;
-        const int64_t r1 = right_in ? rr - (int64_t)cb : -1;
-        if (cnt <= kSelectThreads)
-            select_from<1>(se.cand, cnt, r0, r1, buf[0], buf[1], sel);
-        else if (cnt <= 2 * kSelectThreads)
-            select_from<2>(se.cand, cnt, r0, r1, buf[0], buf[1], sel);
-        else if (cnt <= 4 * kSelectThreads)
-            select_from<4>(se.cand, cnt, r0, r1, buf[0], buf[1], sel);
-        else if (cnt <= 8 * kSelectThreads)
-            select_from<8>(se.cand, cnt, r0, r1, buf[0], buf[1], sel);
-        else
-            select_from_lds(se.cand, cnt, r0, r1, buf[0], sel);
-    }
-    __syncthreads();
+    const bool overflow = C > (uint32_t)kCandCap;
+    const bool left_open = rl <= 0;
+    const bool right_open = rr > (int64_t)se.m;
+    const int64_t r0 = rl - (int64_t)B, r1 = rr - (int64_t)B;
+    const bool left_in = !left_open && !overflow && r0 >= 1 && r0 <= (int64_t)C;
+    const bool right_in = !right_open && !overflow && r1 >= 1 && r1 <= (int64_t)C;
     if (tid == 0) {
-        // open pilot bounds stand for -inf / +inf
-        const float lo_val = lo_key == 0u ? -INFINITY : key_to_float(lo_key);
-        const float hi_val = hi_key == 0xFFFFFFFFu ? INFINITY : key_to_float(hi_key);
+        sel[0] = 0u;
+        sel[1] = 0xFFFFFFFFu;
+    }
+    if (left_in || right_in) {
+        // the shape follows the candidate count (uniform branch)
+        const int cnt = (int)C;
+        const int64_t s0 = left_in ? r0 : -1, s1 = right_in ? r1 : -1;
+        if (cnt <= kSelectThreads)
+            select_from<1>(se.cand, off, G, cnt, s0, s1, hist, sstate, sel);
+        else if (cnt <= 2 * kSelectThreads)
+            select_from<2>(se.cand, off, G, cnt, s0, s1, hist, sstate, sel);
+        else if (cnt <= 4 * kSelectThreads)
+            select_from<4>(se.cand, off, G, cnt, s0, s1, hist, sstate, sel);
+        else if (cnt <= 8 * kSelectThreads)
+            select_from<8>(se.cand, off, G, cnt, s0, s1, hist, sstate, sel);
+        else if (cnt <= 16 * kSelectThreads)
+            select_from<16>(se.cand, off, G, cnt, s0, s1, hist, sstate, sel);
+        else
+            select_from<32>(se.cand, off, G, cnt, s0, s1, hist, sstate, sel);
+    }
+    if (tid == 0) {
         uint32_t info = overflow ? 1u : 0u;
         float aL, aR;
-        if (left_inf) {
+        if (left_open) {
             aL = -INFINITY;
-        } else if ((uint64_t)rl <= cb) {
-            aL = -INFINITY;  // target below every candidate: open the bracket
-            info |= 2u;
-        } else if ((uint64_t)rl > cb + cc) {
-            aL = hi_val;  // rank cb+cc < r_left: conservative
-            info |= 4u;
-        } else if (overflow) {
-            aL = lo_val;  // rank cb+1 <= r_left: conservative
-        } else {
+        } else if (left_in && sel[0] >= L && sel[0] <= H) {
             aL = key_to_float(sel[0]);
-        }
-        if (right_inf) {
-            aR = INFINITY;
-        } else if ((uint64_t)rr > cb + cc) {
-            aR = INFINITY;  // target above every candidate: open the bracket
-            info |= 4u;
-        } else if ((uint64_t)rr <= cb) {
-            aR = lo_val;  // rank cb+1 >= r_right: conservative
-            info |= 2u;
-        } else if (overflow) {
-            aR = hi_val;  // rank cb+cc >= r_right: conservative
         } else {
+            // conservative: no group's lower bound exceeds the target w.h.p.
+            aL = Lmin == 0u ? -INFINITY : key_to_float(Lmin);
+            info |= 2u;
+        }
+        if (right_open) {
+            aR = INFINITY;
+        } else if (right_in && sel[1] >= L && sel[1] <= H) {
             aR = key_to_float(sel[1]);
+        } else {
+            aR = Hmax == 0xFFFFFFFFu ? INFINITY : key_to_float(Hmax);
+            info |= 4u;
         }
         st->aL = aL;
         st->aR = aR;
         st->select_info = info;
-        st->cand_count = (uint32_t)(cc > 0xFFFFFFFFull ? 0xFFFFFFFFull : cc);
+        st->cand_count = C;
+        st->lo_key = L;
+        st->hi_key = H;
+        st->below_n = B;
+        // per-round counters of the passes that follow
+        st->nB = 0;
+        st->solve_state = kSolveNotRun;
+        st->emit_done = 0;
+        st->nonfinite = 0;
     }
 }
 
 hipError_t launch_localize(const SampleArgs& sa, const SelectArgs& se, hipStream_t stream)
 {
-    STK_LAUNCH(kKPilot, stream, pilot_kernel, dim3(1), dim3(kPilotThreads), 0, stream, sa);
-    const int blocks = (sa.m + kSelectThreads - 1) / kSelectThreads;
-    STK_LAUNCH(kKSelect, stream, filter_select_kernel, dim3(blocks), dim3(kSelectThreads), 0, stream, sa, se);
+    STK_LAUNCH(kKFilter, stream, filter_kernel, dim3(se.groups), dim3(kFilterThreads), 0, stream, sa);
+    STK_LAUNCH(kKSelect, stream, select_kernel, dim3(1), dim3(kSelectThreads), 0, stream, se);
     return hipGetLastError();
 }
 

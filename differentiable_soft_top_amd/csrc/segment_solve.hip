@@ -23,6 +23,9 @@
 //   level 2 -- the one group whose end first drops below k is sorted in LDS
 //     (band buckets arrive unordered; full-sort tiles arrive sorted) and
 //     scanned element by element the same way;
+//   direct -- a band small enough for one LDS sort skips the buckets: it is
+//     sorted and scanned whole at level 2, and the certificate comes from
+//     that scan's totals;
 //   closed form -- in the located gap [x_lo, x_hi], with v = e^{(x_lo-b)/alpha},
 //     w = e^{(b-x_hi)/alpha}, v w = g = e^{-(x_hi-x_lo)/alpha}, the mass is
 //     A v/2 + C - B w/2 = k: a quadratic solved in the cancellation-free
@@ -275,18 +278,138 @@ __device__ __forceinline__ void finish(const SolveArgs& a, double b)
     a.st->solve_state = isfinite(b) ? kSolveOk : kSolveRejectHigh;
 }
 
+// Level 2: cnt values at x (cnt >= 1 unless `certify`), sorted into LDS
+// unless they arrive sorted, scanned element by element between lo_node
+// (everything before them) and Su / Cu (the suffix and the count of
+// everything after them); the last breakpoint with mass >= k is located and
+// the closed form applied in the gap after it.  With `certify` the values
+// are the whole band, lo_node / Su the tail nodes and Cu the right-tail
+// count: the bracket certificate is then taken from the scan's totals first.
+struct Level2Job {
+    const float* xg;
+    int cntu;
+    bool unsorted, certify, hasL, hasR;
+    Anch lo_node, Su;
+    uint32_t Cu;
+};
+
+__device__ void level2(const SolveArgs& a, SolveLds& L, const Level2Job& job)
+{
+    const float* xg = job.xg;
+    const int cntu = job.cntu;
+    const Anch lo_node = job.lo_node, Su = job.Su;
+    const uint32_t Cu = job.Cu;
+    const bool certify = job.certify, hasL = job.hasL, hasR = job.hasR;
+    Status* st = a.st;
+    const int tid = threadIdx.x;
+    const double c = a.log2e_over_alpha;
+    const double k = a.k;
+    if (job.unsorted) {
+        uint32_t* spare = reinterpret_cast<uint32_t*>(L.bv);
+        if (cntu <= kST)
+            sort_group_into<1>(xg, cntu, L.keys, spare);
+        else if (cntu <= 2 * kST)
+            sort_group_into<2>(xg, cntu, L.keys, spare);
+        else if (cntu <= 4 * kST)
+            sort_group_into<4>(xg, cntu, L.keys, spare);
+        else if (cntu <= 8 * kST)
+            sort_group_into<8>(xg, cntu, L.keys, spare);
+        else
+            sort_group_into<16>(xg, cntu, L.keys, spare);
+    } else {
+        for (int i = tid; i < cntu; i += kST)
+            L.keys[i] = float_to_key(xg[i]);
+    }
+    __syncthreads();
+    const int ept = (cntu + kST - 1) / kST;
+    const int e0 = tid * ept < cntu ? tid * ept : cntu;
+    const int e1 = e0 + ept < cntu ? e0 + ept : cntu;
+    // this thread's elements: the backward chain (suffix within the thread,
+    // anchored at each element) kept in LDS, the forward fold in registers
+    Anch ls = empty_suf();
+    for (int j = e1 - 1; j >= e0; --j) {
+        ls = bwd(node(key_to_float(L.keys[j]), 1.0), ls, c);
+        L.bv[j] = ls.v;
+    }
+    Anch lp = empty_pre();
+    for (int j = e0; j < e1; ++j)
+        lp = fwd(lp, node(key_to_float(L.keys[j]), 1.0), c);
+    const Scan2Part part2 = scan2_publish(lp, ls, 0u, c, L.wt);
+    __syncthreads();  // [1]
+    const Scan2 s2 = scan2_finish(L.wt, part2, c);
+    const Anch ex_pre = fwd(lo_node, s2.pre_before, c);
+    const Anch ex_suf = bwd(s2.suf_after, Su, c);
+
+    if (certify) {
+        // M(a_L) >= k >= M(a_R) from the band's totals and the tails
+        const double all = (double)cntu + (double)Cu;
+        const Anch Sall = bwd(s2.suf_all, Su, c);
+        const double mL = hasL ? mass_at(lo_node.x, lo_node.v, all, Sall, c) : all;
+        double mR = 0.0;
+        if (hasR) {
+            const Anch Pall = fwd(lo_node, s2.pre_all, c);
+            mR = (double)Cu - 0.5 * Su.v + 0.5 * Pall.v * exp2_nonpos(((double)Pall.x - (double)Su.x) * c);
+        }
+        if (tid == 0) {
+            st->massL = mL;
+            st->massR = mR;
+        }
+        const bool rejL = hasL && !(mL >= k);
+        const bool rejR = !rejL && hasR && !(mR <= k);
+        if (rejL || rejR) {
+            if (tid == 0)
+                st->solve_state = rejL ? kSolveRejectLow : kSolveRejectHigh;
+            return;
+        }
+        if (cntu == 0) {
+            // empty band: the root lies between the two tail nodes
+            if (tid == 0)
+                finish(a, gap_root(lo_node, Su, (double)Cu, k, a.alpha, c));
+            return;
+        }
+    }
+
+    // breakpoint masses: A_j walks forward from everything before, B_{j+1}
+    // is the stored chain re-anchored onto everything after
+    int jc = -1;
+    Anch jlo = empty_pre(), jhi = empty_suf();
+    Anch A = ex_pre;
+    for (int j = e0; j < e1; ++j) {
+        const float xj = key_to_float(L.keys[j]);
+        A = fwd(A, node(xj, 1.0), c);
+        const Anch Bn = j + 1 < e1 ? bwd(node(key_to_float(L.keys[j + 1]), L.bv[j + 1]), ex_suf, c) : ex_suf;
+        if (mass_at(xj, A.v, (double)(cntu - 1 - j) + (double)Cu, Bn, c) >= k) {
+            jc = j;
+            jlo = A;
+            jhi = Bn;
+        }
+    }
+    int jstar, unused;
+    block_max_min(jc, 0, L, &jstar, &unused);  // [1]
+    if (jstar >= 0) {
+        if (jc == jstar)
+            finish(a, gap_root(jlo, jhi, (double)(cntu - 1 - jstar) + (double)Cu, k, a.alpha, c));
+    } else if (tid == 0) {
+        // the root lies before the first point
+        const Anch B0 = bwd(node(key_to_float(L.keys[0]), L.bv[0]), ex_suf, c);
+        finish(a, gap_root(lo_node, B0, (double)cntu + (double)Cu, k, a.alpha, c));
+    }
+}
+
 }  // namespace
 
 // One work-group.  Phases (barriers in brackets):
 //   1. fold the pass-1 partials; per-thread level-1 values; wave scans  [1]
 //   2. per-group masses, bracket certificate, the two groups around the
 //      root published to LDS                                            [1]
-//   3. the located group into LDS, sorted unless it comes from the full
-//      sort                                                             [few]
+//   (a directly sorted band skips 1's scans and 2: it goes to level 2 whole)
+//   3. level 2 (`level2`): the located group into LDS, sorted unless it
+//      comes from the full sort                                         [few]
 //   4. level-2 scans, breakpoint masses                                 [1]
 //   5. the last breakpoint with mass >= k; its owner applies the closed
 //      form                                                             [1]
-__device__ void solve_body(const SolveArgs& a, SolveLds& L)
+// Returns whether level 2 is needed (false: b or a rejection is recorded).
+__device__ bool solve_levels(const SolveArgs& a, SolveLds& L, Level2Job& job)
 {
     Status* st = a.st;
     const int tid = threadIdx.x;
@@ -329,10 +452,12 @@ __device__ void solve_body(const SolveArgs& a, SolveLds& L)
     if (a.tails) {
         constexpr int kSp = kBuckets / kST;
         Pass1Partial sp[kSp];
+        if (!a.direct) {
 #pragma unroll
-        for (int r = 0; r < kSp; ++r)
-            sp[r] = a.p1_super[r * kST + tid];
-        if (nB <= (uint64_t)a.cap) {
+            for (int r = 0; r < kSp; ++r)
+                sp[r] = a.p1_super[r * kST + tid];
+        }
+        if (!a.direct && nB <= (uint64_t)a.cap) {
 #pragma unroll
             for (int r = 0; r < kSp; ++r)
                 add(sp[r]);
@@ -387,7 +512,9 @@ __device__ void solve_body(const SolveArgs& a, SolveLds& L)
                 suf = bwd(node(G.lo, G.TB), suf, c);
         }
     }
-    const Scan2Part part1 = scan2_publish(pre, suf, cnt, c, L.wt);
+    Scan2Part part1;
+    if (!a.direct)
+        part1 = scan2_publish(pre, suf, cnt, c, L.wt);
     __syncthreads();  // [1]
 
     // every thread folds the wave values in the same order
@@ -426,12 +553,12 @@ __device__ void solve_body(const SolveArgs& a, SolveLds& L)
         if (nf) {
             if (tid == 0)
                 st->solve_state = kSolveNonfinite;
-            return;
+            return false;
         }
         if (nB > (uint64_t)a.cap) {
             if (tid == 0)
                 st->solve_state = kSolveOverflow;
-            return;
+            return false;
         }
         hasL = aL != -INFINITY;
         hasR = aR != INFINITY;
@@ -439,6 +566,24 @@ __device__ void solve_body(const SolveArgs& a, SolveLds& L)
             left = node(aL, SL);
         if (hasR)
             right = node(aR, SR);
+        if (a.direct) {
+            // the whole band sorted and scanned at once
+            if (nB > (uint64_t)kBucketCap) {
+                if (tid == 0)
+                    st->solve_state = kSolveDirectOverflow;
+                return false;
+            }
+            job.xg = a.sorted;
+            job.cntu = (int)nB;
+            job.unsorted = true;
+            job.certify = true;
+            job.hasL = hasL;
+            job.hasR = hasR;
+            job.lo_node = left;
+            job.Su = right;
+            job.Cu = (uint32_t)nR;
+            return true;
+        }
     } else {
         nR = 0;
     }
@@ -465,7 +610,7 @@ __device__ void solve_body(const SolveArgs& a, SolveLds& L)
         if (rejL || rejR) {
             if (tid == 0)
                 st->solve_state = rejL ? kSolveRejectLow : kSolveRejectHigh;
-            return;
+            return false;
         }
     }
 
@@ -558,7 +703,7 @@ __device__ void solve_body(const SolveArgs& a, SolveLds& L)
         // root between the last group and the right node
         if (tid == 0)
             finish(a, gap_root(lo_node, right, (double)nR, k, a.alpha, c));
-        return;
+        return false;
     }
     const RowHi Ur = L.hi[u / gpt];
     const GroupAgg U = Ur.g;
@@ -568,89 +713,34 @@ __device__ void solve_body(const SolveArgs& a, SolveLds& L)
         // every value of the group is equal: the root lies before it
         if (tid == 0)
             finish(a, gap_root(lo_node, bwd(node(U.lo, U.TB), Su, c), (double)U.cnt + (double)Cu, k, a.alpha, c));
-        return;
+        return false;
     }
     const int cntu = (int)U.cnt;
     if (cntu > kBucketCap) {
         if (tid == 0)
             st->solve_state = kSolveBucketOverflow;
-        return;
+        return false;
     }
 
-    // ---- level 2: the located group, sorted in LDS ------------------------------
-    {
-        const float* xg = a.sorted + U.start;
-        if (a.tails) {
-            // band buckets arrive unordered: sort the bucket
-            uint32_t* spare = reinterpret_cast<uint32_t*>(L.bv);
-            if (cntu <= kST)
-                sort_group_into<1>(xg, cntu, L.keys, spare);
-            else if (cntu <= 2 * kST)
-                sort_group_into<2>(xg, cntu, L.keys, spare);
-            else if (cntu <= 4 * kST)
-                sort_group_into<4>(xg, cntu, L.keys, spare);
-            else if (cntu <= 8 * kST)
-                sort_group_into<8>(xg, cntu, L.keys, spare);
-            else
-                sort_group_into<16>(xg, cntu, L.keys, spare);
-        } else {
-            // full-sort tiles arrive sorted
-            for (int i = tid; i < cntu; i += kST)
-                L.keys[i] = float_to_key(xg[i]);
-        }
-        __syncthreads();
-    }
-    const int ept = (cntu + kST - 1) / kST;
-    const int e0 = tid * ept < cntu ? tid * ept : cntu;
-    const int e1 = e0 + ept < cntu ? e0 + ept : cntu;
-    // this thread's elements: the backward chain (suffix within the thread,
-    // anchored at each element) kept in LDS, the forward fold in registers
-    Anch ls = empty_suf();
-    for (int j = e1 - 1; j >= e0; --j) {
-        ls = bwd(node(key_to_float(L.keys[j]), 1.0), ls, c);
-        L.bv[j] = ls.v;
-    }
-    Anch lp = empty_pre();
-    for (int j = e0; j < e1; ++j)
-        lp = fwd(lp, node(key_to_float(L.keys[j]), 1.0), c);
-    const Scan2Part part2 = scan2_publish(lp, ls, 0u, c, L.wt);
-    __syncthreads();  // [1]
-    const Scan2 s2 = scan2_finish(L.wt, part2, c);
-    const Anch ex_pre = fwd(lo_node, s2.pre_before, c);
-    const Anch ex_suf = bwd(s2.suf_after, Su, c);
-
-    // breakpoint masses: A_j walks forward from everything before, B_{j+1}
-    // is the stored chain re-anchored onto everything after
-    int jc = -1;
-    Anch jlo = empty_pre(), jhi = empty_suf();
-    Anch A = ex_pre;
-    for (int j = e0; j < e1; ++j) {
-        const float xj = key_to_float(L.keys[j]);
-        A = fwd(A, node(xj, 1.0), c);
-        const Anch Bn = j + 1 < e1 ? bwd(node(key_to_float(L.keys[j + 1]), L.bv[j + 1]), ex_suf, c) : ex_suf;
-        if (mass_at(xj, A.v, (double)(cntu - 1 - j) + (double)Cu, Bn, c) >= k) {
-            jc = j;
-            jlo = A;
-            jhi = Bn;
-        }
-    }
-    int jstar, unused;
-    block_max_min(jc, 0, L, &jstar, &unused);  // [1]
-    if (jstar >= 0) {
-        if (jc == jstar)
-            finish(a, gap_root(jlo, jhi, (double)(cntu - 1 - jstar) + (double)Cu, k, a.alpha, c));
-    } else if (tid == 0) {
-        // the root lies before the group's first point
-        const Anch B0 = bwd(node(key_to_float(L.keys[0]), L.bv[0]), ex_suf, c);
-        finish(a, gap_root(lo_node, B0, (double)cntu + (double)Cu, k, a.alpha, c));
-    }
+    job.xg = a.sorted + U.start;
+    job.cntu = cntu;
+    job.unsorted = a.tails != 0;  // band buckets arrive unordered, full-sort tiles sorted
+    job.certify = false;
+    job.hasL = false;
+    job.hasR = false;
+    job.lo_node = lo_node;
+    job.Su = Su;
+    job.Cu = Cu;
+    return true;
 }
 
 __global__ __launch_bounds__(kST) void solve_kernel(SolveArgs a)
 {
     __shared__ SolveLds L;
-    solve_body(a, L);
-    // every exit of the body ends here: publish the status for the host
+    Level2Job job;
+    if (solve_levels(a, L, job))
+        level2(a, L, job);
+    // every exit ends here: publish the status for the host
     __syncthreads();
     publish_status(a.st, a.mirror);
 }

@@ -88,6 +88,7 @@ void fill_defaults(soft_topk_params* p)
     p->force_path = 0;
     p->mass_tolerance = 0.0;
     p->verify_mass = 0;
+    p->band_route = 0;
 }
 
 bool params_ok(const soft_topk_params& p)
@@ -103,6 +104,8 @@ bool params_ok(const soft_topk_params& p)
     if (!isfinite(p.mass_tolerance))
         return false;
     if (p.verify_mass != 0 && p.verify_mass != 1)
+        return false;
+    if (p.band_route != 0 && p.band_route != SOFT_TOPK_BAND_DIRECT && p.band_route != SOFT_TOPK_BAND_BUCKETS)
         return false;
     return true;
 }
@@ -234,18 +237,7 @@ int64_t upper_rank(int64_t m, double q, double z)
     return b;
 }
 
-void pilot_ranks(int32_t m, double q, int64_t rl, int64_t rr, int32_t* plo, int32_t* phi)
-{
-    const int32_t P = std::min<int32_t>(m, kPilot);
-    const double sd = sqrt((double)P * q * (1.0 - q));
-    const double zp = 7.0;
-    int64_t lo = rl <= 0 ? 0 : (int64_t)floor((double)rl * P / m - zp * sd - 2.0);
-    int64_t hi = rr > m ? (int64_t)P + 1 : (int64_t)ceil((double)rr * P / m + zp * sd + 2.0);
-    lo = std::max<int64_t>(0, std::min<int64_t>(lo, P));
-    hi = std::max<int64_t>(1, std::min<int64_t>(hi, (int64_t)P + 1));
-    *plo = (int32_t)lo;
-    *phi = (int32_t)hi;
-}
+int32_t filter_groups(int32_t m) { return (m + kFilterPer - 1) / kFilterPer; }
 
 uint32_t host_key(float f)
 {
@@ -372,28 +364,10 @@ int enqueue_emit(const Ctx& x, bool fold_mass)
     return SOFT_TOPK_OK;
 }
 
-// One bracketed round: select with ranks (rl, rr), pass-1, band sort, solve, emit.
-int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q)
+// Band sort (unless the band is sorted whole) and the segment solve of a
+// bracketed round whose pass-1 has been enqueued.
+int enqueue_band_solve(const Ctx& x, bool direct)
 {
-    SampleArgs sa;
-    sa.s = x.s;
-    sa.n = x.n;
-    sa.alpha = (float)x.alpha;
-    sa.k0 = (uint32_t)(x.seed & 0xffffffffu);
-    sa.k1 = (uint32_t)(x.seed >> 32);
-    sa.m = x.plan.m;
-    pilot_ranks(x.plan.m, q, rl, rr, &sa.pilot_lo, &sa.pilot_hi);
-    sa.cand = at<uint32_t>(x, x.plan.off_samples);
-    sa.st = x.st;
-    SelectArgs se;
-    se.cand = sa.cand;
-    se.m = x.plan.m;
-    se.r_left = rl;
-    se.r_right = rr;
-    STK_HIP(launch_localize(sa, se, x.stream));
-    int rc = enqueue_pass1(x);
-    if (rc)
-        return rc;
     BandArgs ba;
     ba.p1 = at<Pass1Partial>(x, x.plan.off_p1part);
     ba.p1_blocks = x.plan.g_pass1;
@@ -407,16 +381,18 @@ int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q)
     ba.blocks = x.plan.g_band;
     ba.log2e_over_alpha = x.c;
     ba.st = x.st;
-    STK_HIP(launch_band_sort(ba, x.stream));
+    if (!direct)
+        STK_HIP(launch_band_sort(ba, x.stream));
     SolveArgs so;
     so.p1 = ba.p1;
     so.p1_blocks = ba.p1_blocks;
     so.p1_super = ba.p1_super;
-    so.sorted = ba.band_sorted;
+    so.sorted = direct ? ba.band : ba.band_sorted;
     so.agg = ba.agg;
     so.scan = at<GroupScan>(x, x.plan.off_scan);
-    so.groups = kBuckets;
+    so.groups = direct ? 0 : kBuckets;
     so.tails = 1;
+    so.direct = direct ? 1 : 0;
     so.cap = x.plan.cap;
     so.k = x.k;
     so.alpha = x.alpha;
@@ -426,6 +402,49 @@ int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q)
     so.mirror = x.mirror0;
     STK_HIP(launch_solve(so, x.stream));
     return SOFT_TOPK_OK;
+}
+
+// Whether a round with sample ranks (rl, rr) sorts its band whole: both
+// bracket ends finite and the expected band n (rr - rl) / m small enough.
+bool band_direct(const soft_topk_params& prm, int64_t n, int64_t m, int64_t rl, int64_t rr)
+{
+    if (prm.band_route == SOFT_TOPK_BAND_BUCKETS)
+        return false;
+    if (prm.band_route == SOFT_TOPK_BAND_DIRECT)
+        return true;
+    if (rl < 1 || rr > m)
+        return false;
+    return (double)n * (double)(rr - rl) / (double)m <= kDirectPredictMax;
+}
+
+// One bracketed round: select with ranks (rl, rr), pass-1, band sort, solve.
+int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q, bool direct)
+{
+    SampleArgs sa;
+    sa.s = x.s;
+    sa.n = x.n;
+    sa.alpha = (float)x.alpha;
+    sa.k0 = (uint32_t)(x.seed & 0xffffffffu);
+    sa.k1 = (uint32_t)(x.seed >> 32);
+    sa.m = x.plan.m;
+    sa.r_left = rl;
+    sa.r_right = rr;
+    sa.q = q;
+    sa.cand = at<uint32_t>(x, x.plan.off_samples);
+    sa.rec = at<FilterRec>(x, x.plan.off_frec);
+    SelectArgs se;
+    se.cand = sa.cand;
+    se.rec = sa.rec;
+    se.groups = filter_groups(x.plan.m);
+    se.m = x.plan.m;
+    se.r_left = rl;
+    se.r_right = rr;
+    se.st = x.st;
+    STK_HIP(launch_localize(sa, se, x.stream));
+    int rc = enqueue_pass1(x);
+    if (rc)
+        return rc;
+    return enqueue_band_solve(x, direct);
 }
 
 int enqueue_fullsort(const Ctx& x, const Status& range)
@@ -467,6 +486,7 @@ int enqueue_fullsort(const Ctx& x, const Status& range)
     so.scan = at<GroupScan>(x, x.plan.off_scan);
     so.groups = x.plan.n_tiles;
     so.tails = 0;
+    so.direct = 0;
     so.cap = x.plan.cap;
     so.k = x.k;
     so.alpha = x.alpha;
@@ -516,8 +536,10 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     size_t o = 0;
     p.off_status = o;
     o = align_up(o + sizeof(Status));
-    p.off_samples = o;  // candidate keys of the localisation
-    o = align_up(o + sizeof(uint32_t) * (size_t)kCandCap);
+    p.off_samples = o;  // candidate keys of the localisation, one region per filter group
+    o = align_up(o + sizeof(uint32_t) * (size_t)filter_groups(m) * kFilterPer);
+    p.off_frec = o;
+    o = align_up(o + sizeof(FilterRec) * (size_t)filter_groups(m));
     p.off_p1part = o;
     o = align_up(o + sizeof(Pass1Partial) * (size_t)p.g_pass1);
     p.off_band = o;
@@ -679,7 +701,8 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
         int64_t rl = lower_rank(plan.m, q, prm.z);
         int64_t rr = upper_rank(plan.m, q, prm.z);
         for (int round = 0; round <= prm.max_widen && !done; ++round) {
-            int rc = enqueue_round(x, rl, rr, q);
+            bool direct = band_direct(prm, n, plan.m, rl, rr);
+            int rc = enqueue_round(x, rl, rr, q, direct);
             if (rc)
                 return rc;
             rc = enqueue_certify_emit(x, wait_mass);
@@ -688,7 +711,21 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
             rc = wait_status(0, &h);
             if (rc)
                 return rc;
+            if (h.solve_state == kSolveDirectOverflow) {
+                // the band outgrew the whole-band sort: bucket the same band
+                direct = false;
+                rc = enqueue_band_solve(x, false);
+                if (rc)
+                    return rc;
+                rc = enqueue_certify_emit(x, wait_mass);
+                if (rc)
+                    return rc;
+                rc = wait_status(0, &h);
+                if (rc)
+                    return rc;
+            }
             sx.rounds = round + 1;
+            sx.band_route = direct ? SOFT_TOPK_BAND_DIRECT : SOFT_TOPK_BAND_BUCKETS;
             sx.a_left = h.aL;
             sx.a_right = h.aR;
             sx.n_left = (int64_t)h.nL;

@@ -191,6 +191,137 @@ __device__ __forceinline__ uint32_t rank_in_mask(uint64_t mask)
 }
 
 // ---------------------------------------------------------------------------
+// Two order statistics of the first cnt of kThreads * R u32 keys held R per
+// thread in blocked order (position t*R + r; the values in any order; keys
+// at positions >= cnt are ignored), without sorting: most-significant-digit
+// radix selection on the offsets key - min, 8 bits a round, from the highest
+// bit in which the offsets differ (so bits that every key shares cost no
+// round, and the first digit already spreads keys drawn from a narrow
+// range).  Each round counts, among the keys that share the digits chosen
+// so far for a target, how many carry each value of the next digit (LDS
+// atomics); one wave per target scans the 256 counts and keeps the digit
+// whose count range holds the target's remaining rank.  Both targets run
+// together (their prefixes may differ); a round costs two barriers, the two
+// 512-word histogram buffers alternating so that clearing the next round's
+// buffer never races with the scan of the current one.
+//   r0, r1 -- 1-based ranks; one outside [1, cnt] leaves its output untouched.
+//   hist   -- LDS, 2 * 512 words, 16-byte aligned;  state -- LDS, 4 + 2 *
+//             (kThreads / 64) words;  out -- 2 words.
+// Every thread of the work-group must call it; out is valid after it returns.
+// ---------------------------------------------------------------------------
+template <int kThreads, int R>
+__device__ __forceinline__ void block_select2(const uint32_t (&v)[R], int cnt, int64_t r0, int64_t r1, uint32_t* hist,
+                                              uint32_t* state, uint32_t* out)
+{
+    static_assert(kThreads >= 128, "one wave per target");
+    constexpr int kW = kThreads / kWave;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const bool want0 = r0 >= 1 && r0 <= (int64_t)cnt;
+    const bool want1 = r1 >= 1 && r1 <= (int64_t)cnt;
+    // ---- smallest and largest key ------------------------------------------
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (tid * R + r < cnt) {
+            mn = min(mn, v[r]);
+            mx = max(mx, v[r]);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor(mn, off, kWave));
+        mx = max(mx, (uint32_t)__shfl_xor(mx, off, kWave));
+    }
+    uint32_t* wmn = state + 4;
+    uint32_t* wmx = state + 4 + kW;
+    if (lane == 0) {
+        wmn[wave] = mn;
+        wmx[wave] = mx;
+    }
+    if (tid == 0) {
+        state[0] = 0u;  // offset digits chosen so far, target 0 / 1
+        state[1] = 0u;
+        state[2] = want0 ? (uint32_t)r0 : 1u;  // rank among the keys with those digits
+        state[3] = want1 ? (uint32_t)r1 : 1u;
+    }
+    __syncthreads();
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+    for (int w = 0; w < kW; ++w) {
+        mn = min(mn, wmn[w]);
+        mx = max(mx, wmx[w]);
+    }
+    const uint32_t span = mx >= mn ? mx - mn : 0u;  // cnt == 0 leaves mn > mx
+    const int bits = span ? 32 - __builtin_clz(span) : 0;
+    const int rounds = (bits + 7) / 8;
+    uint32_t mask = 0u;
+    for (int round = 0; round < rounds; ++round) {
+        const int shift = bits - 8 * (round + 1) > 0 ? bits - 8 * (round + 1) : 0;
+        uint32_t* h = hist + (round & 1) * 512;
+        for (int i = tid; i < 512; i += kThreads)
+            h[i] = 0u;
+        __syncthreads();  // cleared; state of the previous round visible
+        const uint32_t p0 = state[0], p1 = state[1];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (tid * R + r < cnt) {
+                const uint32_t o = v[r] - mn;
+                const uint32_t d = (o >> shift) & 255u;
+                if ((o & mask) == p0)
+                    atomicAdd(&h[d], 1u);
+                if ((o & mask) == p1)
+                    atomicAdd(&h[256 + d], 1u);
+            }
+        }
+        __syncthreads();  // counts complete
+        if (wave < 2) {
+            const uint4 c = *reinterpret_cast<const uint4*>(h + 256 * wave + 4 * lane);
+            const uint32_t loc = c.x + c.y + c.z + c.w;
+            uint32_t incl = loc;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const uint32_t o = __shfl_up(incl, off, kWave);
+                if (lane >= off)
+                    incl += o;
+            }
+            const uint32_t before = incl - loc;
+            const uint32_t rem = state[2 + wave];
+            if (rem > before && rem <= incl) {
+                uint32_t d = 4u * (uint32_t)lane, cum = before;
+                if (rem > cum + c.x) {
+                    cum += c.x;
+                    ++d;
+                    if (rem > cum + c.y) {
+                        cum += c.y;
+                        ++d;
+                        if (rem > cum + c.z) {
+                            cum += c.z;
+                            ++d;
+                        }
+                    }
+                }
+                state[wave] |= d << shift;
+                state[2 + wave] = rem - cum;
+            }
+        }
+        // the digits below `shift` stay unchosen; a short last round (bits
+        // not a multiple of 8) overlaps the previous one, whose digits then
+        // match on the overlap by construction
+        mask |= 255u << shift;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        if (want0)
+            out[0] = mn + state[0];
+        if (want1)
+            out[1] = mn + state[1];
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // Ascending sort of kThreads * R u32 keys held R per thread in blocked order
 // (thread t holds positions t*R .. t*R+R-1) by a work-group of kThreads.
 // Bitonic network: partners inside a thread are exchanged in registers,

@@ -32,10 +32,17 @@ constexpr int kGridVjpLarge = 256;
 constexpr int kGridVjpSmall = 1024;
 constexpr int kSelectThreads = 1024;     // bracket select
 constexpr int kSolveThreads = 512;       // segment solve
-constexpr int kPilot = 2048;             // pilot sample size of the select step
-constexpr int kCandCap = 16384;          // candidate keys held in LDS by the select step
+constexpr int kCandCap = 32768;          // candidate keys the select step holds (32 per thread)
+constexpr int kFilterPer = 1024;         // samples per filter work-group (one per thread)
 constexpr int kBuckets = 512;            // value buckets of the band sort
 constexpr int kBucketCap = 8192;         // largest group the solve sorts in LDS
+// The band is sorted whole (no buckets) when its expected size, n times the
+// bracket's sample-rank width over m, is at most this.  With the bracket's
+// ends at +-z binomial standard deviations, the band count spreads by about
+// sqrt(2)/(2z) of that expectation (0.14 at z = 5), so the cut-off sits over
+// four spreads below kBucketCap; a band that outgrows the sort anyway is
+// bucketed afterwards, without a new pass.
+constexpr double kDirectPredictMax = 5120.0;
 constexpr int kBandGroups = 128;         // work-groups of band histogram/scatter
 constexpr int kBandChunkMin = 2048;      // band elements per such work-group (at least)
 constexpr int kSortThreads = 256;        // threads of bucket-sort / tile work-groups
@@ -55,6 +62,7 @@ enum SolveState : uint32_t {
     kSolveOverflow = 4,        // band did not fit its buffer
     kSolveNonfinite = 5,
     kSolveBucketOverflow = 6,  // a band bucket exceeded the LDS sort capacity
+    kSolveDirectOverflow = 7,  // the band exceeded the whole-band sort (bucket it instead)
 };
 
 // Device status block at workspace offset 0.  Every field is written by a
@@ -62,10 +70,11 @@ enum SolveState : uint32_t {
 struct alignas(16) Status {
     // bracket (select step)
     float aL, aR;
-    uint32_t select_info;        // bit0 pilot candidate overflow, bit1 rank below pilot, bit2 above
-    uint32_t cand_count;
-    uint32_t pilot_lo, pilot_hi; // candidate key range from the pilot
-    uint32_t cand_n, below_n;    // candidate append cursor, samples below the range
+    uint32_t select_info;        // bit0 candidate overflow, bit1 / bit2 left / right end conservative
+    uint32_t cand_count;         // candidates over all filter work-groups
+    uint32_t lo_key, hi_key;     // keys where every group's candidates overlap: ranks exact in between
+    uint32_t below_n;            // samples below their group's lower bound
+    uint32_t pad0;
     // pass-1 totals
     double SL, SR;               // sum_{s<a_L} e^{(s-a_L)/alpha}, sum_{s>=a_R} e^{-(s-a_R)/alpha}
     uint64_t nL, nR;             // tail counts
@@ -83,11 +92,10 @@ struct alignas(16) Status {
     double mass;                 // fp64 sum of p over all n
     uint32_t emit_done;
     uint32_t pad3;
-    // "last work-group" tickets; zeroed by the first kernel of each forward
-    // and returned to zero by the work-group that consumes them
-    uint32_t ticket_select;      // filter work-groups done (cleared by the pilot kernel)
+    // "last work-group" ticket; zeroed before the kernel that uses it and
+    // returned to zero by the work-group that consumes it
     uint32_t ticket_radix;       // radix upsweep work-groups done (returned to 0 by the last)
-    uint32_t pad4[6];
+    uint32_t pad4[7];
 };
 static_assert(sizeof(Status) <= 256, "status block must fit 256 bytes");
 static_assert(sizeof(Status) % 4 == 0, "status block is copied as 32-bit words");
@@ -144,7 +152,7 @@ struct Plan {
     int32_t g_band;              // max work-groups of band histogram/scatter
     int32_t n_tiles;             // groups of the full-sort solve
     int32_t g_radix;             // radix tiles
-    size_t off_status, off_samples, off_p1part, off_band, off_band_sorted;
+    size_t off_status, off_samples, off_frec, off_p1part, off_band, off_band_sorted;
     size_t off_hist, off_bstart, off_agg, off_scan, off_emitpart, off_keys0, off_keys1, off_rhist, off_super;
     size_t total;
 };
@@ -152,21 +160,31 @@ struct Plan {
 Plan make_plan(int64_t n, int32_t m, int64_t cap);
 
 // ---- host launchers (each enqueues on `stream`, returns the launch status) --
+// What one filter work-group reports: its samples below its lower bound,
+// its candidates (stored in its own region of kFilterPer keys) and the
+// bounds themselves (0 / all-ones when open).
+struct alignas(16) FilterRec {
+    uint32_t below, cand, lo, hi;
+};
+
 struct SampleArgs {
     const float* s;
     int64_t n;
     float alpha;
     uint32_t k0, k1;              // Philox key (seed low / high word)
     int32_t m;                    // samples
-    int32_t pilot_lo, pilot_hi;   // 1-based pilot ranks bounding the targets (0 / P+1 = open)
-    uint32_t* cand;               // [kCandCap] candidate keys
-    Status* st;
+    int64_t r_left, r_right;      // 1-based target ranks (0 = -inf, m+1 = +inf)
+    double q;                     // target quantile 1 - k/n
+    uint32_t* cand;               // [groups * kFilterPer] candidate keys, one region per group
+    FilterRec* rec;               // [groups]
 };
 
 struct SelectArgs {
     const uint32_t* cand;
+    const FilterRec* rec;
+    int32_t groups;               // filter work-groups, ceil(m / kFilterPer)
     int32_t m;
-    int64_t r_left, r_right;      // 1-based target ranks (0 = -inf, m+1 = +inf)
+    int64_t r_left, r_right;
     Status* st;
 };
 
@@ -213,6 +231,7 @@ struct SolveArgs {
     GroupScan* scan;              // scratch [groups]
     int32_t groups;
     int32_t tails;                // 1: bracketed (tails from status), 0: full sort (no tails)
+    int32_t direct;               // bracketed: 1 = sort the unbucketed band (at `sorted`) whole
     int64_t cap;                  // band capacity (bracketed route)
     double k;
     double alpha;

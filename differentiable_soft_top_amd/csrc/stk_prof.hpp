@@ -12,7 +12,6 @@ namespace stk {
 
 enum KernelId : int {
     kKSample = 0,   // the diagnostic sampler
-    kKPilot,
     kKFilter,
     kKSelect,
     kKPass1,

@@ -59,6 +59,11 @@ extern "C" {
 #define SOFT_TOPK_PATH_WIDENED 2  /* certified after widening the bracket   */
 #define SOFT_TOPK_PATH_FULLSORT 3 /* full device radix sort of all scores   */
 
+/* How a bracketed round solved its band (soft_topk_params.band_route,
+ * soft_topk_stats.band_route). */
+#define SOFT_TOPK_BAND_DIRECT 1   /* the whole band sorted in one LDS sort     */
+#define SOFT_TOPK_BAND_BUCKETS 2  /* value buckets; only the root's is sorted  */
+
 /* Why a bracketed round was rejected (soft_topk_stats.reject_mask bits). */
 #define SOFT_TOPK_REJECT_LOW 1       /* certificate: b lies below a_L        */
 #define SOFT_TOPK_REJECT_HIGH 2      /* certificate: b lies at/above a_R     */
@@ -89,6 +94,10 @@ typedef struct soft_topk_params {
                                emission's fp64 partial sums of p are not folded
                                (the pass runs in full whenever stats are
                                requested, and stats.mass is NaN otherwise)      */
+    int32_t band_route;     /* 0 auto: sort the band whole when its expected size
+                               n (r_R - r_L) / m is at most 5120, else bucket it;
+                               SOFT_TOPK_BAND_DIRECT / _BUCKETS force a route (a
+                               band over 8192 scores is always bucketed)          */
 } soft_topk_params;
 
 /* Host-side record of one forward call (all fields written on success). */
@@ -96,7 +105,7 @@ typedef struct soft_topk_stats {
     int32_t path;           /* SOFT_TOPK_PATH_*                                       */
     int32_t rounds;         /* bracketed rounds run (0 when forced to full sort)      */
     int32_t reject_mask;    /* OR of SOFT_TOPK_REJECT_* over rejected rounds          */
-    int32_t reserved;
+    int32_t band_route;     /* SOFT_TOPK_BAND_* of the last bracketed round (0: none) */
     float a_left, a_right;  /* bracket of the last bracketed round                    */
     int64_t n_left, n_band, n_right; /* scores below / inside / at-or-above it        */
     double mass_at_left;    /* M(a_L) of the last bracketed round                     */

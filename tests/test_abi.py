@@ -87,7 +87,8 @@ def test_params_validation(lib):
     assert p.samples == 65536 and p.z == 5.0 and p.max_widen == 2 and p.force_path == 0
     assert lib.soft_topk_workspace_bytes(1000, ctypes.byref(p)) > 0
     for field, bad in [("samples", 10), ("samples", 1 << 20), ("z", 0.0), ("z", float("nan")),
-                       ("max_widen", -1), ("force_path", 7), ("band_capacity", -3), ("verify_mass", 2)]:
+                       ("max_widen", -1), ("force_path", 7), ("band_capacity", -3), ("verify_mass", 2),
+                       ("band_route", 3)]:
         q = _lib.default_params()
         setattr(q, field, bad)
         assert lib.soft_topk_workspace_bytes(1000, ctypes.byref(q)) == 0, field

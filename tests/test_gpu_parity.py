@@ -91,13 +91,34 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("route", ["auto", "buckets"])
 @pytest.mark.parametrize("name,n", SMALL, ids=["%s-%s" % (a, b) for a, b in SMALL])
-def test_small_parity(dev, name, n):
+def test_small_parity(dev, name, n, route):
+    """Both band routes: at these sizes the band is small enough to be sorted
+    whole (the automatic choice); forcing the value buckets runs the route
+    the larger workloads take on the same inputs."""
     s_np, k, alpha, w = make_workload(name, n=n)
     g_np = draw_grad(s_np.size, w.seed)
-    res = run(dev, s_np, k, alpha, g_np)
+    prm = params(band_route=_lib.BAND_BUCKETS) if route == "buckets" else None
+    res = run(dev, s_np, k, alpha, g_np, prm)
     check_full(res, s_np, k, alpha, g_np)
     assert res["stats"]["path"] == _lib.PATH_BRACKET, res["stats"]
+    want = _lib.BAND_BUCKETS if route == "buckets" else _lib.BAND_DIRECT
+    assert res["stats"]["band_route"] == want, res["stats"]
+
+
+def test_direct_band_overflow_falls_back_to_buckets(dev):
+    """A band forced onto the whole-band sort but larger than it (about 11,700
+    scores here) is bucketed instead, in the same round, without a new pass."""
+    s_np, k, alpha, w = make_workload("c4", n=3_000_007)
+    res = run(dev, s_np, k, alpha, None, params(band_route=_lib.BAND_DIRECT))
+    st = res["stats"]
+    assert st["n_band"] > 8192 and st["rounds"] == 1, st
+    assert st["path"] == _lib.PATH_BRACKET and st["band_route"] == _lib.BAND_BUCKETS, st
+    check_full(res, s_np, k, alpha)
+    auto = run(dev, s_np, k, alpha)
+    assert auto["stats"]["band_route"] == _lib.BAND_BUCKETS, auto["stats"]
+    assert auto["b"] == res["b"]
 
 
 def test_clustered_small(dev):
@@ -342,6 +363,42 @@ def test_sampler_matches_philox_definition(dev):
         e = np.log(2 * u) if u < 0.5 else -np.log(2 * (1 - u))
         ref = np.float32(float(s_np[idx]) + float(np.float32(alpha)) * e)
         assert abs(float(y[j]) - float(ref)) <= 2 * abs(float(np.spacing(ref))), (j, y[j], ref)
+
+
+@pytest.mark.parametrize("name,n,kfrac,prm", [
+    ("c2", 100_003, None, {}),
+    ("c3", 200_001, None, {"seed": 77}),
+    ("c4", 300_007, None, {"samples": 4096, "z": 3.0}),
+    ("c2", 100_003, 0.5, {}),
+    ("c2", 50_001, 0.999, {"samples": 1024, "z": 6.0}),
+], ids=["c2", "c3-seed", "c4-m4096", "c2-median", "c2-tail-m1024"])
+def test_bracket_is_the_exact_order_statistics(dev, name, n, kfrac, prm):
+    """The first round's bracket ends are the order statistics of the m
+    kernel-noised samples at the binomial ranks, exactly: the device selects
+    them digit by digit, the test sorts the same samples on the host.  The
+    median case passes over 8192 candidates to the selection (16 keys per
+    thread)."""
+    import ctypes
+    s_np, k, alpha, _ = make_workload(name, n=n)
+    if kfrac is not None:
+        k = kfrac * s_np.size
+    p = params(**prm)
+    res = run(dev, s_np, k, alpha, None, p)
+    st = res["stats"]
+    assert st["rounds"] == 1 and st["path"] == _lib.PATH_BRACKET, st
+    m = p.samples
+    s = torch.from_numpy(s_np).to(dev)
+    out = torch.empty(m, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    rc = lib.soft_topk_debug_sample(ctypes.c_void_p(s.data_ptr()), s_np.size, alpha, p.seed, m,
+                                    ctypes.c_void_p(out.data_ptr()),
+                                    ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    _lib.check(rc, "debug_sample")
+    y = np.sort(out.cpu().numpy())
+    rl, rr = _lib.bracket_ranks(m, 1.0 - k / s_np.size, p.z)
+    want_l = -np.inf if rl < 1 else float(y[rl - 1])
+    want_r = np.inf if rr > m else float(y[rr - 1])
+    assert st["a_left"] == want_l and st["a_right"] == want_r, (st["a_left"], want_l, st["a_right"], want_r)
 
 
 # --------------------------------------------------------------------------
