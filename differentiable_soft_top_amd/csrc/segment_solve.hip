@@ -186,22 +186,36 @@ __device__ __forceinline__ Scan2 scan2_finish(const WaveTot* wt, const Scan2Part
     return r;
 }
 
-// Load cnt values (padded with +inf keys to kST * R), sort, store to keys.
+// Load cnt values (R per thread), sort into keys[0 .. cnt).  Bucket sort
+// first (band values are spread evenly over a narrow range); if a bucket
+// overflows its register network, the values are loaded again and sorted by
+// a bitonic network, padded with +inf to kST * R.  spare: LDS, kST * R words.
 template <int R>
-__device__ void sort_group_into(const float* x, int cnt, uint32_t* keys, uint32_t* spare)
+__device__ __forceinline__ void load_keys(const float* x, int cnt, uint32_t (&v)[R])
 {
-    const int tid = threadIdx.x;
-    uint32_t v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int i = tid * R + r;
+        const int i = threadIdx.x * R + r;
         v[r] = i < cnt ? float_to_key(x[i]) : 0xFFFFFFFFu;
     }
+}
+
+template <int R>
+__device__ __forceinline__ void sort_group_into(const float* x, int cnt, uint32_t* keys, uint32_t* spare)
+{
+    {
+        uint32_t v[R];
+        load_keys<R>(x, cnt, v);
+        if (block_bucket_sort<kST, R>(v, cnt, keys, spare))
+            return;
+    }
+    uint32_t v[R];
+    load_keys<R>(x, cnt, v);
     block_bitonic_regs<kST, R>(v, keys, spare);
     __syncthreads();  // the last LDS stage's reads are done
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        keys[tid * R + r] = v[r];
+        keys[threadIdx.x * R + r] = v[r];
 }
 
 // Mass at a point x with prefix P (anchored at x), count after C, and the

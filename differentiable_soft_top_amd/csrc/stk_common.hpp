@@ -322,6 +322,201 @@ __device__ __forceinline__ void block_select2(const uint32_t (&v)[R], int cnt, i
 }
 
 // ---------------------------------------------------------------------------
+// Ascending bitonic network over N keys held in registers.  Stages are
+// template parameters, so every register index is a compile-time constant
+// (nested runtime-bounded loops would leave the unroller a variable trip
+// count and the array in scratch memory).
+// ---------------------------------------------------------------------------
+template <int N, int K, int J>
+struct RegBitonicStage {
+    static __device__ __forceinline__ void run(uint32_t (&a)[N])
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int l = i ^ J;
+            if (l > i) {
+                const uint32_t x = a[i], y = a[l];
+                const bool up = (i & K) == 0;
+                a[i] = up ? min(x, y) : max(x, y);
+                a[l] = up ? max(x, y) : min(x, y);
+            }
+        }
+        RegBitonicStage<N, K, J / 2>::run(a);
+    }
+};
+
+template <int N, int K>
+struct RegBitonicStage<N, K, 0> {
+    static __device__ __forceinline__ void run(uint32_t (&)[N]) {}
+};
+
+template <int N, int K, bool kDone = (K > N)>
+struct RegBitonicLevel {
+    static __device__ __forceinline__ void run(uint32_t (&a)[N])
+    {
+        RegBitonicStage<N, K, K / 2>::run(a);
+        RegBitonicLevel<N, 2 * K>::run(a);
+    }
+};
+
+template <int N, int K>
+struct RegBitonicLevel<N, K, true> {
+    static __device__ __forceinline__ void run(uint32_t (&)[N]) {}
+};
+
+template <int N>
+__device__ __forceinline__ void reg_bitonic(uint32_t (&a)[N])
+{
+    static_assert((N & (N - 1)) == 0, "power-of-two network");
+    RegBitonicLevel<N, 2>::run(a);
+}
+
+template <int N>
+__device__ __forceinline__ void sort_run(uint32_t* p, int c)
+{
+    uint32_t a[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        a[i] = i < c ? p[i] : 0xFFFFFFFFu;
+    reg_bitonic<N>(a);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        if (i < c)
+            p[i] = a[i];
+}
+
+// ---------------------------------------------------------------------------
+// Ascending sort of the first cnt of kThreads * R keys (held R per thread in
+// blocked order; positions >= cnt ignored) into keys[0 .. cnt), by buckets:
+// kThreads * B equal-width buckets over the offsets key - min (B = R / 4,
+// at least 1: about four keys a bucket when the keys fill their slots),
+// counted and scattered with LDS atomics; then each thread sorts its own B
+// buckets in registers (a bitonic network of 8 or 16 keys, the smaller one
+// when it holds the fullest bucket).  Suited to keys spread evenly over
+// their range (a band of scores around the threshold).  Returns false when
+// some bucket holds more than 16 keys; keys[] then holds them in bucket
+// order only and the caller sorts another way.
+//   scratch -- LDS, 2 * kThreads * B + 2 * (kThreads / 64) words.
+// Every thread of the work-group must call it; keys[] is complete when it
+// returns true.
+// ---------------------------------------------------------------------------
+template <int R>
+constexpr int bucket_sort_per_thread() { return R / 4 > 1 ? R / 4 : 1; }
+
+template <int kThreads, int R>
+__device__ __forceinline__ bool block_bucket_sort(const uint32_t (&v)[R], int cnt, uint32_t* keys, uint32_t* scratch)
+{
+    static_assert((kThreads & (kThreads - 1)) == 0, "power-of-two thread count");
+    constexpr int B = bucket_sort_per_thread<R>();
+    static_assert((B & (B - 1)) == 0, "power-of-two buckets per thread");
+    constexpr int kNB = kThreads * B;
+    constexpr int kW = kThreads / kWave;
+    uint32_t* bcnt = scratch;
+    uint32_t* cur = scratch + kNB;
+    uint32_t* wred = scratch + 2 * kNB;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (tid * R + r < cnt) {
+            mn = min(mn, v[r]);
+            mx = max(mx, v[r]);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor(mn, off, kWave));
+        mx = max(mx, (uint32_t)__shfl_xor(mx, off, kWave));
+    }
+    if (lane == 0) {
+        wred[wave] = mn;
+        wred[kW + wave] = mx;
+    }
+    __syncthreads();
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+    for (int w = 0; w < kW; ++w) {
+        mn = min(mn, wred[w]);
+        mx = max(mx, wred[kW + w]);
+    }
+    // bucket = floor(offset * kNB / (span + 1)) through a 32.32 fixed-point
+    // reciprocal rounded down: non-decreasing in the offset, below kNB, and
+    // the whole range of buckets in use
+    const uint32_t span = mx >= mn ? mx - mn : 0u;
+    const uint64_t inv = ((uint64_t)kNB << 32) / ((uint64_t)span + 1u);
+    auto bucket = [&](uint32_t key) { return (uint32_t)(((uint64_t)(key - mn) * inv) >> 32); };
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+        bcnt[tid * B + j] = 0u;
+    __syncthreads();  // counters cleared; every read of wred done
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (tid * R + r < cnt)
+            atomicAdd(&bcnt[bucket(v[r])], 1u);
+    __syncthreads();
+    uint32_t c[B];
+    uint32_t loc = 0u, cmax = 0u;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+        c[j] = bcnt[tid * B + j];
+        loc += c[j];
+        cmax = max(cmax, c[j]);
+    }
+    uint32_t incl = loc;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off, kWave);
+        if (lane >= off)
+            incl += o;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        cmax = max(cmax, (uint32_t)__shfl_xor(cmax, off, kWave));
+    if (lane == kWave - 1)
+        wred[wave] = incl;
+    if (lane == 0)
+        wred[kW + wave] = cmax;
+    __syncthreads();
+    uint32_t start = incl - loc;
+    cmax = 0u;
+    for (int w = 0; w < kW; ++w) {
+        start += w < wave ? wred[w] : 0u;
+        cmax = max(cmax, wred[kW + w]);
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+        cur[tid * B + j] = start;
+        start += c[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (tid * R + r < cnt) {
+            const uint32_t pos = atomicAdd(&cur[bucket(v[r])], 1u);
+            keys[pos] = v[r];
+        }
+    }
+    __syncthreads();
+    if (cmax > 16u)
+        return false;
+    // this thread's buckets, one at a time (after the scatter each cursor
+    // stands at its bucket's end)
+#pragma unroll 1
+    for (int j = 0; j < B; ++j) {
+        const uint32_t cj = bcnt[tid * B + j];
+        uint32_t* run = keys + (cur[tid * B + j] - cj);
+        if (cmax <= 8u)
+            sort_run<8>(run, (int)cj);
+        else
+            sort_run<16>(run, (int)cj);
+    }
+    __syncthreads();
+    return true;
+}
+
+// ---------------------------------------------------------------------------
 // Ascending sort of kThreads * R u32 keys held R per thread in blocked order
 // (thread t holds positions t*R .. t*R+R-1) by a work-group of kThreads.
 // Bitonic network: partners inside a thread are exchanged in registers,
