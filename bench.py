@@ -94,9 +94,9 @@ class Runner:
                                     v(self.b.data_ptr()), v(self.ws.data_ptr()), self.ws_bytes, self.stream,
                                     None, ctypes.byref(self.stats) if stats else None)
         self._lib.check(rc, "soft_topk_forward")
-        rc = L.soft_topk_backward(v(self.g.data_ptr()), v(self.s.data_ptr()), self.n, self.alpha,
-                                  v(self.b.data_ptr()), v(self.grad.data_ptr()), v(self.bws.data_ptr()),
-                                  self.bws_bytes, self.stream)
+        rc = L.soft_topk_backward_ex(v(self.g.data_ptr()), v(self.s.data_ptr()), self.n, self.alpha,
+                                     v(self.b.data_ptr()), v(self.grad.data_ptr()), v(self.ws.data_ptr()),
+                                     self.ws_bytes, v(self.bws.data_ptr()), self.bws_bytes, self.stream)
         self._lib.check(rc, "soft_topk_backward")
 
 

@@ -38,8 +38,10 @@ def _check_scores(s):
         raise TypeError("scores must be a contiguous 1-D float32 tensor")
 
 
-def forward(s, k: float, alpha: float, params: Params | None = None, out_p=None, want_stats: bool = False):
-    """Run soft_topk_forward_ex; returns (p, b[, stats dict])."""
+def forward(s, k: float, alpha: float, params: Params | None = None, out_p=None, want_stats: bool = False,
+            want_workspace: bool = False):
+    """Run soft_topk_forward_ex; returns (p, b[, stats dict][, workspace]).  The workspace, passed on to
+    backward(), lets it reuse what the forward recorded about saturated scores."""
     import torch
     _check_scores(s)
     lib = _lib.load()
@@ -57,13 +59,17 @@ def forward(s, k: float, alpha: float, params: Params | None = None, out_p=None,
                                   ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream_handle(s),
                                   pp, ctypes.byref(stats))
     _lib.check(rc, "soft_topk_forward")
+    out = (p, b)
     if want_stats:
-        return p, b, stats.as_dict()
-    return p, b
+        out += (stats.as_dict(),)
+    if want_workspace:
+        out += (ws,)
+    return out
 
 
-def backward(grad_p, s, alpha: float, b, out=None):
-    """Run soft_topk_backward: (d_i/alpha)(g_i - G/D)."""
+def backward(grad_p, s, alpha: float, b, out=None, fwd_workspace=None):
+    """Run soft_topk_backward_ex: (d_i/alpha)(g_i - G/D).  fwd_workspace: the forward's workspace
+    (from forward(..., want_workspace=True)), or None to read the scores throughout."""
     import torch
     _check_scores(s)
     if grad_p.dtype != torch.float32 or grad_p.shape != s.shape or not grad_p.is_contiguous():
@@ -75,9 +81,11 @@ def backward(grad_p, s, alpha: float, b, out=None):
     ws_bytes = lib.soft_topk_backward_workspace_bytes(n)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=s.device)
     g = out if out is not None else torch.empty_like(s)
-    rc = lib.soft_topk_backward(ctypes.c_void_p(grad_p.data_ptr()), ctypes.c_void_p(s.data_ptr()), n,
-                                float(alpha), ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(g.data_ptr()),
-                                ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream_handle(s))
+    fw = None if fwd_workspace is None else ctypes.c_void_p(fwd_workspace.data_ptr())
+    fw_bytes = 0 if fwd_workspace is None else fwd_workspace.numel() * fwd_workspace.element_size()
+    rc = lib.soft_topk_backward_ex(ctypes.c_void_p(grad_p.data_ptr()), ctypes.c_void_p(s.data_ptr()), n,
+                                   float(alpha), ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(g.data_ptr()),
+                                   fw, fw_bytes, ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream_handle(s))
     _lib.check(rc, "soft_topk_backward")
     return g
 
@@ -88,18 +96,18 @@ def _function():
     class _SoftTopK(torch.autograd.Function):
         @staticmethod
         def forward(ctx, s, k, alpha, params):
-            p, b = forward(s, k, alpha, params)
-            ctx.save_for_backward(s, b)
+            p, b, ws = forward(s, k, alpha, params, want_workspace=True)
+            ctx.save_for_backward(s, b, ws)
             ctx.alpha = float(alpha)
             ctx.mark_non_differentiable(b)
             return p, b
 
         @staticmethod
         def backward(ctx, gp, gb):
-            s, b = ctx.saved_tensors
+            s, b, ws = ctx.saved_tensors
             if gp is None:
                 return None, None, None, None
-            return backward(gp.contiguous(), s, ctx.alpha, b), None, None, None
+            return backward(gp.contiguous(), s, ctx.alpha, b, fwd_workspace=ws), None, None, None
 
     return _SoftTopK
 

@@ -86,6 +86,8 @@ def load():
     lib.soft_topk_forward_ex.restype = ctypes.c_int
     lib.soft_topk_backward.argtypes = [fp, fp, i64, dbl, dp, fp, vp, sz, vp]
     lib.soft_topk_backward.restype = ctypes.c_int
+    lib.soft_topk_backward_ex.argtypes = [fp, fp, i64, dbl, dp, fp, vp, sz, vp, sz, vp]
+    lib.soft_topk_backward_ex.restype = ctypes.c_int
     lib.soft_topk_strerror.argtypes = [ctypes.c_int]
     lib.soft_topk_strerror.restype = ctypes.c_char_p
     lib.soft_topk_last_hip_error.argtypes = []

@@ -37,6 +37,7 @@ __global__ void reset_status_kernel(Status* st, int open_bracket)
         st->solve_state = kSolveNotRun;
         st->emit_done = 0;
         st->ticket_radix = 0;
+        st->seg_valid = 0;
     }
 }
 
@@ -184,23 +185,6 @@ __global__ __launch_bounds__(kStreamThreads) void emit_finalize_kernel(EmitArgs 
     publish_status(st, a.mirror);
 }
 
-hipError_t launch_emit(const EmitArgs& a, bool fold_mass, hipStream_t stream)
-{
-    const bool vec = ((reinterpret_cast<uintptr_t>(a.s) | reinterpret_cast<uintptr_t>(a.p)) & 15u) == 0;
-    const dim3 grid(a.blocks), block(kStreamThreads);
-    if (!vec)
-        STK_LAUNCH(kKEmit, stream, (emit_kernel<1, false, false>), grid, block, 0, stream, a);
-    else if (a.n >= kNontemporalMin)
-        STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchLarge, true, true>), grid, block, 0, stream, a);
-    else if (a.n >= kStreamLargeMin)
-        STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchLarge, true, false>), grid, block, 0, stream, a);
-    else
-        STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchSmall, true, false>), grid, block, 0, stream, a);
-    if (fold_mass)
-        STK_LAUNCH(kKEmitFinal, stream, emit_finalize_kernel, dim3(1), dim3(kStreamThreads), 0, stream, a);
-    return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 template <int kB, bool kVec>
 __global__ __launch_bounds__(kStreamThreads) void vjp_reduce_kernel(VjpArgs a)
@@ -299,6 +283,418 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_kernel(VjpArgs a, in
     }
 }
 
+// ---------------------------------------------------------------------------
+// Saturated-score segments (from kSegMinN scores on, aligned vectors).  The
+// emission, which knows b, records for each wave's 1024-score share of a
+// large VJP tile the scores whose fp32 density d_i = dens(s_i) is not 0 and,
+// when there are at most kSegCap, their d values.  The VJP then reads those
+// instead of the scores: its reduction takes d from the record (exactly 0
+// elsewhere, which is what the scores give) and stores the matching g values
+// compacted in its workspace; its gradient kernel reads only the compacted
+// (d, g) pairs and writes 0 for the other scores (where the score-reading
+// formula gives +-0, the sign following g - G/D).  If G is not finite (a
+// non-finite g) the gradient kernel reads the scores throughout.  The
+// record's metadata (16 masks and the count per segment) is fetched for
+// kMetaChunk tiles at once into LDS, so a tile's data loads are issued
+// together and waited for once.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kSegV = 4 * kVjpBatchLarge;             // values per lane in a segment
+constexpr int kSegPerTile = kStreamThreads / kWave;   // segments per large VJP tile
+constexpr int kMetaChunk = 8;                         // tiles whose metadata is fetched at once
+static_assert(kSegV == 16 && kSegMeta == kSegV + 1 && (kSegCap & (kSegCap - 1)) == 0 && kSegCap >= 64,
+              "segment metadata: 16 masks and the count; power-of-two value regions");
+
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
+
+// A segment's listed values move between global memory and a wave's LDS
+// block (kSegCap floats) as whole blocks -- coalesced, ceil(cnt / 64) loads
+// or stores per lane -- and lanes pick or place their own values in LDS.
+// (Per-lane gathers of a few scattered values from global memory cost far
+// more than the bytes they move.)
+constexpr int kSegSteps = kSegCap / kWave;
+
+// blk[0 .. cnt) <- src[0 .. cnt) (all steps' loads issued, then one wait)
+__device__ __forceinline__ void block_in(const float* __restrict__ src, uint32_t cnt, float* blk)
+{
+    const int lane = lane_id();
+    float tmp[kSegSteps];
+#pragma unroll
+    for (int q = 0; q < kSegSteps; ++q) {
+        const uint32_t j = (uint32_t)(q * kWave + lane);
+        tmp[q] = j < cnt ? src[j] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kSegSteps; ++q) {
+        const uint32_t j = (uint32_t)(q * kWave + lane);
+        if (j < cnt)
+            blk[j] = tmp[q];
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Two blocks at once (one wait for both).
+__device__ __forceinline__ void block_in2(const float* __restrict__ s0, const float* __restrict__ s1, uint32_t cnt,
+                                          float* b0, float* b1)
+{
+    const int lane = lane_id();
+    float t0[kSegSteps], t1[kSegSteps];
+#pragma unroll
+    for (int q = 0; q < kSegSteps; ++q) {
+        const uint32_t j = (uint32_t)(q * kWave + lane);
+        t0[q] = j < cnt ? s0[j] : 0.0f;
+        t1[q] = j < cnt ? s1[j] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kSegSteps; ++q) {
+        const uint32_t j = (uint32_t)(q * kWave + lane);
+        if (j < cnt) {
+            b0[j] = t0[q];
+            b1[j] = t1[q];
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// dst[0 .. cnt) <- blk[0 .. cnt)
+__device__ __forceinline__ void block_out(const float* blk, uint32_t cnt, float* __restrict__ dst)
+{
+    const int lane = lane_id();
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < kSegSteps; ++q) {
+        const uint32_t j = (uint32_t)(q * kWave + lane);
+        if (j < cnt)
+            dst[j] = blk[j];
+    }
+}
+
+// Record segment `seg` from this wave's d values (value index order);
+// blk: this wave's LDS block.
+__device__ __forceinline__ void seg_record(const SegBufs& sb, int64_t seg, const float (&d)[kSegV], uint64_t* mstage,
+                                           float* blk)
+{
+    const int lane = lane_id();
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kSegV; ++i)
+        cnt += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(d[i] != 0.0f));
+    uint64_t* meta = sb.meta + seg * kSegMeta;
+    if (cnt > (uint32_t)kSegCap) {
+        if (lane == 0)
+            meta[kSegV] = kSegDense;
+        return;
+    }
+    uint32_t pre = 0;
+#pragma unroll
+    for (int i = 0; i < kSegV; ++i) {
+        const bool nz = d[i] != 0.0f;
+        const uint64_t lm = __builtin_amdgcn_ballot_w64(nz);
+        if (lane == 0)
+            mstage[i] = lm;
+        if (nz)
+            blk[pre + rank_in_mask(lm)] = d[i];
+        pre += (uint32_t)__popcll(lm);
+    }
+    block_out(blk, cnt, sb.val + seg * kSegCap);
+    if (lane < kSegV)
+        meta[lane] = mstage[lane];
+    else if (lane == kSegV)
+        meta[kSegV] = cnt;
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Metadata of this wave's segments of tiles tile(c), c < kMetaChunk, into
+// mlds (tiles without a record, or past the vector, read as dense).
+template <typename TileOf>
+__device__ __forceinline__ void fetch_meta(const VjpArgs& a, TileOf tile_of, int64_t T, uint64_t (&mlds)[kMetaChunk][kSegMeta])
+{
+    const int lane = lane_id();
+    const int wave = wave_index();
+    const int64_t Ts = a.seg_tiles < T ? a.seg_tiles : T;
+    const int j = lane < kSegMeta ? lane : kSegMeta - 1;
+    uint64_t w[kMetaChunk];
+#pragma unroll
+    for (int c = 0; c < kMetaChunk; ++c) {
+        const int64_t t = tile_of(c);
+        const int64_t tc = (t >= 0 && t < Ts) ? t : 0;
+        w[c] = a.seg.meta[(tc * kSegPerTile + wave) * kSegMeta + j];
+    }
+#pragma unroll
+    for (int c = 0; c < kMetaChunk; ++c) {
+        const int64_t t = tile_of(c);
+        const bool has = t >= 0 && t < Ts;
+        if (lane < kSegMeta)
+            mlds[c][lane] = has ? w[c] : (lane == kSegV ? (uint64_t)kSegDense : 0ull);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+}  // namespace
+
+template <bool kNT>
+__global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
+{
+    constexpr int kB = kVjpBatchLarge;  // one large VJP tile per step (a segment per wave)
+    __shared__ double red[kStreamThreads / kWave];
+    __shared__ uint64_t mstage[kStreamThreads / kWave][kSegV];
+    __shared__ float blk[kStreamThreads / kWave][kSegCap];
+    Status* st = a.st;
+    if (st->solve_state != kSolveOk)
+        return;
+    const int tid = threadIdx.x;
+    const int wave = wave_index();
+    const double b = *a.b;
+    const double c = a.log2e_over_alpha;
+    const int64_t G = gridDim.x;
+    double acc = 0.0;
+    const int64_t T = whole_tiles<kB>(a.n);
+    const float4* s4 = reinterpret_cast<const float4*>(a.s);
+    float4* p4 = reinterpret_cast<float4*>(a.p);
+    for (int64_t t0 = blockIdx.x; t0 < T; t0 += G) {
+        const int64_t t = T - 1 - t0;  // descending: see the note above
+        float4 v[kB];
+        load_q<kB>(s4, t, v);
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            float4 o;
+            o.x = emit_one(v[u].x, b, c, acc);
+            o.y = emit_one(v[u].y, b, c, acc);
+            o.z = emit_one(v[u].z, b, c, acc);
+            o.w = emit_one(v[u].w, b, c, acc);
+            store4<kNT>(&p4[t * (kB * kStreamThreads) + u * kStreamThreads + tid], o);
+        }
+        float d[kSegV];
+#pragma unroll
+        for (int q = 0; q < kB; ++q) {
+            d[4 * q + 0] = dens(v[q].x, b, c);
+            d[4 * q + 1] = dens(v[q].y, b, c);
+            d[4 * q + 2] = dens(v[q].z, b, c);
+            d[4 * q + 3] = dens(v[q].w, b, c);
+        }
+        seg_record(a.seg, t * kSegPerTile + wave, d, mstage[wave], blk[wave]);
+    }
+    for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads)
+        a.p[i] = emit_one(a.s[i], b, c, acc);
+    block_sum_to(acc, red, &a.partials[blockIdx.x]);
+    if (blockIdx.x == 0 && tid == 0) {
+        st->seg_valid = 1u;
+        st->seg_n = (uint64_t)a.n;
+        st->seg_alpha = a.alpha;
+        st->seg_scores = (uint64_t)reinterpret_cast<uintptr_t>(a.s);
+    }
+}
+
+namespace {
+
+__device__ __forceinline__ bool vjp_seg_usable(const VjpArgs& a)
+{
+    if (a.fst == nullptr || a.seg.meta == nullptr)
+        return false;
+    const Status* f = a.fst;
+    return f->seg_valid != 0u && f->b == *a.b && f->seg_n == (uint64_t)a.n && f->seg_alpha == a.alpha &&
+           f->seg_scores == (uint64_t)reinterpret_cast<uintptr_t>(a.s);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kStreamThreads) void vjp_reduce_seg_kernel(VjpArgs a)
+{
+    constexpr int kB = kVjpBatchLarge;
+    __shared__ double red[2][kStreamThreads / kWave];
+    __shared__ uint64_t mlds[kStreamThreads / kWave][kMetaChunk][kSegMeta];
+    __shared__ float dblk[kStreamThreads / kWave][kSegCap];
+    __shared__ float gblk[kStreamThreads / kWave][kSegCap];
+    const int tid = threadIdx.x;
+    const int wave = wave_index();
+    const double b = *a.b;
+    const double c = a.log2e_over_alpha;
+    const int64_t G = gridDim.x;
+    const bool use_seg = vjp_seg_usable(a);
+    const int64_t T = whole_tiles<kB>(a.n);
+    const float4* s4 = reinterpret_cast<const float4*>(a.s);
+    const float4* g4 = reinterpret_cast<const float4*>(a.g);
+    double D = 0.0, G_ = 0.0;
+    for (int64_t tb = blockIdx.x; tb < T; tb += kMetaChunk * G) {
+        if (use_seg)
+            fetch_meta(a, [&](int k) { return tb + (int64_t)k * G; }, T, mlds[wave]);
+        for (int k = 0; k < kMetaChunk; ++k) {
+            const int64_t t = tb + (int64_t)k * G;
+            if (t >= T)
+                break;
+            const uint32_t rec = use_seg ? (uint32_t)mlds[wave][k][kSegV] : kSegDense;
+            float4 vg[kB];
+            float d[kSegV];
+            // each branch issues all of its loads (g first) before any use
+            if (rec == kSegDense) {
+                float4 vs[kB];
+                load_q<kB>(g4, t, vg);
+                load_q<kB>(s4, t, vs);
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    d[4 * u + 0] = dens(vs[u].x, b, c);
+                    d[4 * u + 1] = dens(vs[u].y, b, c);
+                    d[4 * u + 2] = dens(vs[u].z, b, c);
+                    d[4 * u + 3] = dens(vs[u].w, b, c);
+                }
+            } else {
+                load_q<kB>(g4, t, vg);
+                block_in(a.seg.val + (t * kSegPerTile + wave) * kSegCap, rec, dblk[wave]);
+                // d from the block; this lane's listed g values into the g block
+                const uint64_t* m = mlds[wave][k];
+                uint64_t mk[kSegV];
+#pragma unroll
+                for (int i = 0; i < kSegV; ++i)
+                    mk[i] = m[i];
+                const int lane = lane_id();
+                uint32_t pre = 0;
+#pragma unroll
+                for (int i = 0; i < kSegV; ++i) {
+                    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(mk[i] >> 32));
+                    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)mk[i]);
+                    const uint64_t lm = ((uint64_t)hi << 32) | lo;
+                    const bool li = (lm >> lane) & 1ull;
+                    const uint32_t p = pre + rank_in_mask(lm);
+                    const float4 g = vg[i / 4];
+                    const float gi = (i & 3) == 0 ? g.x : (i & 3) == 1 ? g.y : (i & 3) == 2 ? g.z : g.w;
+                    d[i] = li ? dblk[wave][p] : 0.0f;
+                    if (li)
+                        gblk[wave][p] = gi;
+                    pre += (uint32_t)__popcll(lm);
+                }
+                block_out(gblk[wave], rec, a.gl + (t * kSegPerTile + wave) * kSegCap);
+                __builtin_amdgcn_wave_barrier();
+            }
+            // fp32 within a float4, fp64 across them (as the score-reading kernel)
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                float dsum = 0.f, gsum = 0.f;
+                dsum += d[4 * u + 0]; gsum += vg[u].x * d[4 * u + 0];
+                dsum += d[4 * u + 1]; gsum += vg[u].y * d[4 * u + 1];
+                dsum += d[4 * u + 2]; gsum += vg[u].z * d[4 * u + 2];
+                dsum += d[4 * u + 3]; gsum += vg[u].w * d[4 * u + 3];
+                D += (double)dsum;
+                G_ += (double)gsum;
+            }
+        }
+    }
+    for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads) {
+        const float dd = dens(a.s[i], b, c);
+        D += (double)dd;
+        G_ += (double)(a.g[i] * dd);
+    }
+    block_sum_to(D, red[0], &a.partials[2 * blockIdx.x]);
+    __syncthreads();
+    block_sum_to(G_, red[1], &a.partials[2 * blockIdx.x + 1]);
+}
+
+template <bool kNT>
+__global__ __launch_bounds__(kStreamThreads) void vjp_apply_seg_kernel(VjpArgs a, int32_t reduce_blocks)
+{
+    constexpr int kB = kVjpBatchLarge;
+    __shared__ double red[2][kStreamThreads / kWave];
+    __shared__ double tot[2];
+    __shared__ uint64_t mlds[kStreamThreads / kWave][kMetaChunk][kSegMeta];
+    __shared__ float dblk[kStreamThreads / kWave][kSegCap];
+    __shared__ float gblk[kStreamThreads / kWave][kSegCap];
+    const int tid = threadIdx.x;
+    const int wave = wave_index();
+    double D = 0.0, G_ = 0.0;
+    for (int i = tid; i < reduce_blocks; i += kStreamThreads) {
+        D += a.partials[2 * i];
+        G_ += a.partials[2 * i + 1];
+    }
+    block_sum_to(D, red[0], &tot[0]);
+    __syncthreads();
+    block_sum_to(G_, red[1], &tot[1]);
+    __syncthreads();
+    const float ratio = tot[0] > 0.0 ? (float)(tot[1] / tot[0]) : 0.0f;
+    const float inv_alpha = (float)(1.0 / a.alpha);
+    const double b = *a.b;
+    const double c = a.log2e_over_alpha;
+    const int64_t G = gridDim.x;
+    // a non-finite g leaves G non-finite: then every g is read, as the
+    // score-reading kernel does
+    const bool use_seg = vjp_seg_usable(a) && isfinite(tot[1]);
+    const int64_t T = whole_tiles<kB>(a.n);
+    const float4* s4 = reinterpret_cast<const float4*>(a.s);
+    const float4* g4 = reinterpret_cast<const float4*>(a.g);
+    float4* o4 = reinterpret_cast<float4*>(a.grad);
+    for (int64_t tb = blockIdx.x; tb < T; tb += kMetaChunk * G) {
+        // descending tiles: see the note above
+        if (use_seg)
+            fetch_meta(a, [&](int k) { return T - 1 - (tb + (int64_t)k * G); }, T, mlds[wave]);
+        for (int k = 0; k < kMetaChunk; ++k) {
+            const int64_t t0 = tb + (int64_t)k * G;
+            if (t0 >= T)
+                break;
+            const int64_t t = T - 1 - t0;
+            const uint32_t rec = use_seg ? (uint32_t)mlds[wave][k][kSegV] : kSegDense;
+            float o[kSegV];
+            if (rec == kSegDense) {
+                float4 vs[kB], vg[kB];
+                load_q<kB>(s4, t, vs);
+                load_q<kB>(g4, t, vg);
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    o[4 * u + 0] = dens(vs[u].x, b, c) * inv_alpha * (vg[u].x - ratio);
+                    o[4 * u + 1] = dens(vs[u].y, b, c) * inv_alpha * (vg[u].y - ratio);
+                    o[4 * u + 2] = dens(vs[u].z, b, c) * inv_alpha * (vg[u].z - ratio);
+                    o[4 * u + 3] = dens(vs[u].w, b, c) * inv_alpha * (vg[u].w - ratio);
+                }
+            } else {
+                const int64_t seg = t * kSegPerTile + wave;
+                block_in2(a.seg.val + seg * kSegCap, a.gl + seg * kSegCap, rec, dblk[wave], gblk[wave]);
+                const uint64_t* m = mlds[wave][k];
+                uint64_t mk[kSegV];
+#pragma unroll
+                for (int i = 0; i < kSegV; ++i)
+                    mk[i] = m[i];
+                const int lane = lane_id();
+                uint32_t pre = 0;
+#pragma unroll
+                for (int i = 0; i < kSegV; ++i) {
+                    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(mk[i] >> 32));
+                    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)mk[i]);
+                    const uint64_t lm = ((uint64_t)hi << 32) | lo;
+                    const bool li = (lm >> lane) & 1ull;
+                    const uint32_t p = pre + rank_in_mask(lm);
+                    o[i] = li ? dblk[wave][p] * inv_alpha * (gblk[wave][p] - ratio) : 0.0f;
+                    pre += (uint32_t)__popcll(lm);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+                store4<kNT>(&o4[t * (kB * kStreamThreads) + u * kStreamThreads + tid],
+                            make_float4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]));
+        }
+    }
+    for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads)
+        a.grad[i] = dens(a.s[i], b, c) * inv_alpha * (a.g[i] - ratio);
+}
+
+hipError_t launch_emit(const EmitArgs& a, bool fold_mass, hipStream_t stream)
+{
+    const bool vec = ((reinterpret_cast<uintptr_t>(a.s) | reinterpret_cast<uintptr_t>(a.p)) & 15u) == 0;
+    const dim3 grid(a.blocks), block(kStreamThreads);
+    if (!vec)
+        STK_LAUNCH(kKEmit, stream, (emit_kernel<1, false, false>), grid, block, 0, stream, a);
+    else if (a.seg.meta != nullptr && a.n >= kSegMinN && a.n >= kNontemporalMin)
+        STK_LAUNCH(kKEmit, stream, emit_seg_kernel<true>, grid, block, 0, stream, a);
+    else if (a.seg.meta != nullptr && a.n >= kSegMinN)
+        STK_LAUNCH(kKEmit, stream, emit_seg_kernel<false>, grid, block, 0, stream, a);
+    else if (a.n >= kNontemporalMin)
+        STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchLarge, true, true>), grid, block, 0, stream, a);
+    else if (a.n >= kStreamLargeMin)
+        STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchLarge, true, false>), grid, block, 0, stream, a);
+    else
+        STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchSmall, true, false>), grid, block, 0, stream, a);
+    if (fold_mass)
+        STK_LAUNCH(kKEmitFinal, stream, emit_finalize_kernel, dim3(1), dim3(kStreamThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_vjp(const VjpArgs& a, hipStream_t stream)
 {
     const bool vec = ((reinterpret_cast<uintptr_t>(a.s) | reinterpret_cast<uintptr_t>(a.g) |
@@ -309,6 +705,12 @@ hipError_t launch_vjp(const VjpArgs& a, hipStream_t stream)
     if (!vec) {
         STK_LAUNCH(kKVjpReduce, stream, (vjp_reduce_kernel<1, false>), gr, block, 0, stream, r);
         STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<1, false, false>), ga, block, 0, stream, a, r.blocks);
+    } else if (a.seg.meta != nullptr && a.n >= kSegMinN) {
+        STK_LAUNCH(kKVjpReduce, stream, vjp_reduce_seg_kernel, gr, block, 0, stream, r);
+        if (a.n >= kNontemporalMin)
+            STK_LAUNCH(kKVjpApply, stream, vjp_apply_seg_kernel<true>, ga, block, 0, stream, a, r.blocks);
+        else
+            STK_LAUNCH(kKVjpApply, stream, vjp_apply_seg_kernel<false>, ga, block, 0, stream, a, r.blocks);
     } else if (a.n >= kStreamLargeMin) {
         STK_LAUNCH(kKVjpReduce, stream, (vjp_reduce_kernel<kVjpBatchLarge, true>), gr, block, 0, stream, r);
         if (a.n >= kNontemporalMin)

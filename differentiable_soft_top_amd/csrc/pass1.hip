@@ -38,9 +38,10 @@ namespace stk {
 namespace {
 
 constexpr int kVals = 16;                       // scores per lane per tile
-constexpr int kTileQ = kStreamThreads * kVals / 4;  // float4 per tile
+static_assert(kPass1Threads * kVals == kPass1TileScores, "tile size shared with the host");
+constexpr int kTileQ = kPass1Threads * kVals / 4;  // float4 per tile
 constexpr int kWin = kWave * kVals;             // window list per wave (worst case)
-constexpr int kWaves1 = kStreamThreads / kWave;
+constexpr int kWaves1 = kPass1Threads / kWave;
 constexpr double kTailCut = 50.0;               // tail terms below 2^-50 are dropped
 constexpr int kP1Stage = 2048;                  // band scores staged per work-group
 
@@ -184,13 +185,13 @@ __device__ __forceinline__ void load_tile(const float4* __restrict__ s4, int64_t
 {
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-        f[u] = s4[t * (kU * kStreamThreads) + u * kStreamThreads + threadIdx.x];
+        f[u] = s4[t * (kU * kPass1Threads) + u * kPass1Threads + threadIdx.x];
 }
 
 }  // namespace
 
 template <bool kVec>
-__global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
+__global__ __launch_bounds__(kPass1Threads) void pass1_kernel(Pass1Args a)
 {
     __shared__ float stage_buf[kP1Stage];
     __shared__ float win_buf[kWaves1][kWin];
@@ -262,13 +263,13 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
             rest = a.n;
     } else {
         // unaligned scores: plain grid-stride over scalar loads
-        for (int64_t i0 = (int64_t)blockIdx.x * (kStreamThreads * kVals); i0 < a.n;
-             i0 += G * (kStreamThreads * kVals)) {
+        for (int64_t i0 = (int64_t)blockIdx.x * (kPass1Threads * kVals); i0 < a.n;
+             i0 += G * (kPass1Threads * kVals)) {
             float v[kVals];
             uint32_t valid = 0;
 #pragma unroll
             for (int k = 0; k < kVals; ++k) {
-                const int64_t i = i0 + (int64_t)k * kStreamThreads + tid;
+                const int64_t i = i0 + (int64_t)k * kPass1Threads + tid;
                 v[k] = i < a.n ? a.s[i] : 0.f;
                 valid |= (i < a.n ? 1u : 0u) << k;
             }
@@ -276,12 +277,12 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
         }
         rest = a.n;
     }
-    for (int64_t i0 = rest; i0 < a.n; i0 += kStreamThreads * kVals) {
+    for (int64_t i0 = rest; i0 < a.n; i0 += kPass1Threads * kVals) {
         float v[kVals];
         uint32_t valid = 0;
 #pragma unroll
         for (int k = 0; k < kVals; ++k) {
-            const int64_t i = i0 + (int64_t)k * kStreamThreads + tid;
+            const int64_t i = i0 + (int64_t)k * kPass1Threads + tid;
             v[k] = i < a.n ? a.s[i] : 0.f;
             valid |= (i < a.n ? 1u : 0u) << k;
         }
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(Pass1Args a)
     if (tid == 0)
         stage_base = staged ? atomicAdd(x.nB, (unsigned long long)staged) : 0ull;
     __syncthreads();
-    for (uint32_t i = tid; i < staged; i += kStreamThreads) {
+    for (uint32_t i = tid; i < staged; i += kPass1Threads) {
         const uint64_t g = (uint64_t)stage_base + i;
         if (g < (uint64_t)a.cap)
             a.band[g] = stage_buf[i];
@@ -421,9 +422,9 @@ hipError_t launch_pass1(const Pass1Args& a, hipStream_t stream)
 {
     const bool vec = (reinterpret_cast<uintptr_t>(a.s) & 15u) == 0;
     if (vec)
-        STK_LAUNCH(kKPass1, stream, pass1_kernel<true>, dim3(a.blocks), dim3(kStreamThreads), 0, stream, a);
+        STK_LAUNCH(kKPass1, stream, pass1_kernel<true>, dim3(a.blocks), dim3(kPass1Threads), 0, stream, a);
     else
-        STK_LAUNCH(kKPass1, stream, pass1_kernel<false>, dim3(a.blocks), dim3(kStreamThreads), 0, stream, a);
+        STK_LAUNCH(kKPass1, stream, pass1_kernel<false>, dim3(a.blocks), dim3(kPass1Threads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -314,6 +314,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs se)
         st->solve_state = kSolveNotRun;
         st->emit_done = 0;
         st->nonfinite = 0;
+        st->seg_valid = 0;
     }
 }
 

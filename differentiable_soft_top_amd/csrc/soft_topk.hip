@@ -68,6 +68,13 @@ int32_t emit_blocks(int64_t n)
 int32_t vjp_tile(int64_t n) { return 4 * kStreamThreads * (n >= kStreamLargeMin ? kVjpBatchLarge : kVjpBatchSmall); }
 int32_t vjp_grid_cap(int64_t n) { return n >= kStreamLargeMin ? kGridVjpLarge : kGridVjpSmall; }
 int32_t vjp_reduce_blocks(int64_t n) { return grid_for(n, vjp_tile(n), vjp_grid_cap(n)); }
+// grid of a segment VJP kernel: at most one work-group per large VJP tile
+int32_t seg_grid(int64_t n, int32_t cap) { return grid_for(n, 4 * kStreamThreads * kVjpBatchLarge, cap); }
+// reduction partials to provide for: either VJP route
+int32_t vjp_partial_blocks(int64_t n)
+{
+    return n >= kSegMinN ? std::max(vjp_reduce_blocks(n), seg_grid(n, kGridVjpSegReduce)) : vjp_reduce_blocks(n);
+}
 int32_t vjp_apply_blocks(int64_t n) { return grid_for(n, vjp_tile(n), vjp_grid_cap(n)); }
 
 int64_t default_cap(int64_t n)
@@ -239,6 +246,39 @@ int64_t upper_rank(int64_t m, double q, double z)
 
 int32_t filter_groups(int32_t m) { return (m + kFilterPer - 1) / kFilterPer; }
 
+// Segment buffers from offset o (none below kSegMinN scores); returns the
+// end.  One segment per wave share of every whole pass-1 tile.
+int64_t seg_count(int64_t n)
+{
+    // four segments per whole large VJP tile (the emission's tiles too)
+    const int64_t tiles = (n / 4) / (kVjpBatchLarge * kStreamThreads);
+    return n >= kSegMinN ? tiles * (kStreamThreads / kWave) : 0;
+}
+
+size_t seg_layout(int64_t n, size_t o, int64_t* n_seg, size_t* off_meta, size_t* off_val)
+{
+    const int64_t segs = seg_count(n);
+    *n_seg = segs;
+    *off_meta = o;
+    o = align_up(o + sizeof(uint64_t) * kSegMeta * (size_t)segs);
+    *off_val = o;
+    o = align_up(o + sizeof(float) * kSegCap * (size_t)segs);
+    return o;
+}
+
+// The segment buffers of a forward workspace at ws (all null when unused).
+SegBufs seg_bufs(char* ws, int64_t n_seg, size_t off_meta, size_t off_val)
+{
+    SegBufs b;
+    b.meta = nullptr;
+    b.val = nullptr;
+    if (n_seg > 0) {
+        b.meta = reinterpret_cast<uint64_t*>(ws + off_meta);
+        b.val = reinterpret_cast<float*>(ws + off_val);
+    }
+    return b;
+}
+
 uint32_t host_key(float f)
 {
     uint32_t u;
@@ -360,6 +400,7 @@ int enqueue_emit(const Ctx& x, bool fold_mass)
     e.blocks = x.plan.g_emit;
     e.st = x.st;
     e.mirror = x.mirror1;
+    e.seg = seg_bufs(x.ws, x.plan.n_seg, x.plan.off_seg_meta, x.plan.off_seg_val);
     STK_HIP(launch_emit(e, fold_mass, x.stream));
     return SOFT_TOPK_OK;
 }
@@ -536,6 +577,9 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     size_t o = 0;
     p.off_status = o;
     o = align_up(o + sizeof(Status));
+    // saturated-score segments first: their place depends on n alone, so the
+    // backward can find them in a forward workspace
+    o = seg_layout(n, o, &p.n_seg, &p.off_seg_meta, &p.off_seg_val);
     p.off_samples = o;  // candidate keys of the localisation, one region per filter group
     o = align_up(o + sizeof(uint32_t) * (size_t)filter_groups(m) * kFilterPer);
     p.off_frec = o;
@@ -615,7 +659,9 @@ size_t soft_topk_backward_workspace_bytes(int64_t n)
 {
     if (!n_ok(n))
         return 0;
-    return align_up(sizeof(double) * 2 * (size_t)vjp_reduce_blocks(n));
+    // the reduction partials, then the listed g values of the segments
+    return align_up(sizeof(double) * 2 * (size_t)vjp_partial_blocks(n)) +
+           align_up(sizeof(float) * kSegCap * (size_t)seg_count(n));
 }
 
 const char* soft_topk_strerror(int code)
@@ -823,6 +869,15 @@ int soft_topk_forward(const float* scores, int64_t n, double k, double alpha, fl
 int soft_topk_backward(const float* grad_p, const float* scores, int64_t n, double alpha, const double* b,
                        float* grad_s, void* workspace, size_t workspace_bytes, void* stream)
 {
+    return soft_topk_backward_ex(grad_p, scores, n, alpha, b, grad_s, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+int soft_topk_backward_ex(const float* grad_p, const float* scores, int64_t n, double alpha, const double* b,
+                          float* grad_s, const void* fwd_workspace, size_t fwd_workspace_bytes, void* workspace,
+                          size_t workspace_bytes, void* stream)
+{
+    if (fwd_workspace && (reinterpret_cast<uintptr_t>(fwd_workspace) % kAlign) != 0)
+        return SOFT_TOPK_EWORKSPACE;
     if (!grad_p || !scores || !b || !grad_s || !n_ok(n))
         return SOFT_TOPK_EINVAL;
     if (!(alpha > 0.0) || !isfinite(alpha))
@@ -841,6 +896,23 @@ int soft_topk_backward(const float* grad_p, const float* scores, int64_t n, doub
     a.partials = static_cast<double*>(workspace);
     a.blocks = vjp_apply_blocks(n);
     a.reduce_blocks = vjp_reduce_blocks(n);
+    a.fst = nullptr;
+    a.seg = seg_bufs(nullptr, 0, 0, 0);
+    a.seg_tiles = seg_count(n) / (kStreamThreads / kWave);
+    a.gl = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    align_up(sizeof(double) * 2 * (size_t)vjp_partial_blocks(n)));
+    if (fwd_workspace) {
+        int64_t n_seg;
+        size_t off_meta, off_val;
+        const size_t end = seg_layout(n, align_up(sizeof(Status)), &n_seg, &off_meta, &off_val);
+        if (n_seg > 0 && fwd_workspace_bytes >= end) {
+            char* fw = static_cast<char*>(const_cast<void*>(fwd_workspace));
+            a.fst = reinterpret_cast<const Status*>(fw);
+            a.seg = seg_bufs(fw, n_seg, off_meta, off_val);
+            a.reduce_blocks = seg_grid(n, kGridVjpSegReduce);
+            a.blocks = seg_grid(n, kGridVjpSegApply);
+        }
+    }
     STK_HIP(launch_vjp(a, static_cast<hipStream_t>(stream)));
     return SOFT_TOPK_OK;
 }

@@ -15,7 +15,8 @@ constexpr int kStreamThreads = 256;      // streaming kernels (pass-1, emit, VJP
 // per CU sweeping the vectors together stream fastest).  Emission and VJP
 // tiles hold kB float4 per lane: the larger batch from kStreamLargeMin
 // scores on, the smaller one below (more work-groups for short vectors).
-constexpr int kPass1TileScores = 4096;   // scores per pass-1 tile
+constexpr int kPass1Threads = 256;       // pass-1 work-group
+constexpr int kPass1TileScores = 16 * kPass1Threads;  // scores per pass-1 tile (16 per lane)
 constexpr int kEmitBatchLarge = 8;
 constexpr int kEmitBatchSmall = 2;
 constexpr int kVjpBatchLarge = 4;
@@ -30,10 +31,30 @@ constexpr int kGridEmit = 2048;
 // the last-level cache and want more work-groups in flight.
 constexpr int kGridVjpLarge = 256;
 constexpr int kGridVjpSmall = 1024;
+// The VJP over saturated-score segments is bound by dependent round trips,
+// not by DRAM pages: it wants several work-groups per CU.
+constexpr int kGridVjpSegReduce = 1024;
+constexpr int kGridVjpSegApply = 2048;
 constexpr int kSelectThreads = 1024;     // bracket select
 constexpr int kSolveThreads = 512;       // segment solve
 constexpr int kCandCap = 32768;          // candidate keys the select step holds (32 per thread)
 constexpr int kFilterPer = 1024;         // samples per filter work-group (one per thread)
+// Saturated-score segments.  A segment is one wave's share of a large VJP
+// tile: 1024 scores, lane l holding value i (0..15) at float4 (tile * 1024 +
+// (i / 4) * 256 + wave * 64 + l), component i % 4 (the emission walks the
+// same tiles when it records them).  The emission, which knows b, marks
+// in each segment the scores whose fp32 density d_i is not 0; a segment with
+// at most kSegCap of them ("listed") keeps their d values.  The VJP then
+// takes d from there instead of recomputing it from the scores: zero for
+// every other score, which is what the scores give.  Used from kSegMinN
+// scores on.
+constexpr int kSegScores = 1024;
+constexpr int kSegCap = 256;
+constexpr int kSegMeta = 17;                 // u64 words per segment: 16 listed masks, count
+constexpr uint32_t kSegDense = 0xFFFFFFFFu;
+constexpr int64_t kSegMinN = 1 << 24;
+static_assert(kStreamThreads == 256 && kVjpBatchLarge == 4 && kSegMinN >= kStreamLargeMin,
+              "segment geometry: large VJP tiles of 256 x 4 float4");
 constexpr int kBuckets = 512;            // value buckets of the band sort
 constexpr int kBucketCap = 8192;         // largest group the solve sorts in LDS
 // The band is sorted whole (no buckets) when its expected size, n times the
@@ -95,7 +116,13 @@ struct alignas(16) Status {
     // "last work-group" ticket; zeroed before the kernel that uses it and
     // returned to zero by the work-group that consumes it
     uint32_t ticket_radix;       // radix upsweep work-groups done (returned to 0 by the last)
-    uint32_t pad4[7];
+    // saturated-score segments written by this round's pass-1 (cleared by the
+    // select kernel and the full-sort reset), and what they were taken from:
+    // the VJP uses them only for the same scores, n and alpha (and b)
+    uint32_t seg_valid;
+    uint64_t seg_n;
+    double seg_alpha;
+    uint64_t seg_scores;
 };
 static_assert(sizeof(Status) <= 256, "status block must fit 256 bytes");
 static_assert(sizeof(Status) % 4 == 0, "status block is copied as 32-bit words");
@@ -154,6 +181,8 @@ struct Plan {
     int32_t g_radix;             // radix tiles
     size_t off_status, off_samples, off_frec, off_p1part, off_band, off_band_sorted;
     size_t off_hist, off_bstart, off_agg, off_scan, off_emitpart, off_keys0, off_keys1, off_rhist, off_super;
+    int64_t n_seg;               // saturated-score segments (0: not used at this n)
+    size_t off_seg_meta, off_seg_val;
     size_t total;
 };
 
@@ -191,6 +220,13 @@ struct SelectArgs {
 hipError_t launch_localize(const SampleArgs& sa, const SelectArgs& se, hipStream_t stream);
 hipError_t launch_debug_sample(const float* s, int64_t n, float alpha, uint64_t seed, int32_t m,
                                float* out_samples, hipStream_t stream);
+
+// Saturated-score segment storage (all null when not used).
+struct SegBufs {
+    uint64_t* meta;               // [n_seg][kSegMeta]: listed masks (words 0..15, only when sparse),
+                                  // listed count or kSegDense (word 16, low half)
+    float* val;                   // [n_seg][kSegCap] listed d values in (value index, lane) order
+};
 
 struct Pass1Args {
     const float* s;
@@ -277,6 +313,7 @@ struct EmitArgs {
     int32_t blocks;
     Status* st;
     Status* mirror;               // host-visible copy of the status written by the mass fold (may be null)
+    SegBufs seg;                  // used when pass-1 wrote them (st->seg_valid)
 };
 hipError_t launch_emit(const EmitArgs& a, bool fold_mass, hipStream_t stream);
 
@@ -291,6 +328,12 @@ struct VjpArgs {
     double* partials;             // [reduce_blocks][2]
     int32_t blocks;               // work-groups of the gradient kernel
     int32_t reduce_blocks;        // work-groups of the (D, G) reduction
+    // the forward's saved segments (null: none); used only when its status
+    // says they were taken from these scores, n, alpha and b
+    const Status* fst;
+    SegBufs seg;
+    int64_t seg_tiles;            // large VJP tiles that have segments
+    float* gl;                    // [n_seg][kSegCap] listed g values (backward workspace)
 };
 hipError_t launch_vjp(const VjpArgs& a, hipStream_t stream);
 

@@ -169,6 +169,28 @@ int soft_topk_backward(const float* grad_p, const float* scores, int64_t n,
                        double alpha, const double* b, float* grad_s,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward that may reuse what the forward recorded in its workspace
+ * (fwd_workspace, fwd_workspace_bytes: the forward call's workspace, not
+ * written since, 256-byte aligned; NULL = none, as soft_topk_backward).
+ * Gist.science summary of Fast LapSum, section 2.2: outside a narrow band
+ * of scores the soft indicator is saturated.  From 2^24 scores on, pass-1
+ * marks, per 1024-score segment, the scores farther than 110 alpha outside
+ * the bracket, where the fp32 density d_i is exactly 0 for every threshold
+ * the bracket admits; where such scores dominate a segment it keeps the
+ * others' values, and the backward then reads those instead of the scores.
+ * The result is the same as soft_topk_backward's (the same fp32 arithmetic
+ * on the same d_i, including NaN from a non-finite grad_p times 0).  The
+ * record is used only if the forward status in fwd_workspace names these
+ * scores (pointer), n, alpha and this b; otherwise the scores are read.
+ * The scores must be unchanged since that forward.  Errors as
+ * soft_topk_backward, plus EWORKSPACE for a misaligned fwd_workspace.
+ */
+int soft_topk_backward_ex(const float* grad_p, const float* scores, int64_t n,
+                          double alpha, const double* b, float* grad_s,
+                          const void* fwd_workspace, size_t fwd_workspace_bytes,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Text for a return code. */
 const char* soft_topk_strerror(int code);
 

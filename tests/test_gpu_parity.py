@@ -402,6 +402,78 @@ def test_bracket_is_the_exact_order_statistics(dev, name, n, kfrac, prm):
 
 
 # --------------------------------------------------------------------------
+# saturated-score segments (from 2^24 scores on): emission and the VJP read
+# the segments instead of the scores where pass-1 recorded them
+# --------------------------------------------------------------------------
+SEG_N = (1 << 24) + 4099  # whole tiles plus a ragged end
+
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+@pytest.mark.parametrize("order,kfrac", [("random", None), ("sorted", None), ("random", 0.5), ("sorted", 0.5)])
+def test_segments_match_oracle_and_score_path(dev, order, kfrac):
+    """c4's law (U(0,1), alpha = 1e-3) at 2^24 + 4099 scores: most segments
+    hold few listed scores; with k = n/2 many scores also lie far beyond the
+    right end (p = 1 without reading them).  Sorted, the segments are all
+    far-left (sparse, none listed), all listed (dense) or all far-right
+    (sparse, p = 1).  Element-wise parity with the oracle, and the backward
+    through the forward's record equals the score-reading backward: bit for
+    bit wherever the gradient is not zero; a zero is +0 where a record
+    served it, and the same +-0 where the segment was read from the scores."""
+    s_np, k, alpha, w = make_workload("c4", n=SEG_N)
+    if kfrac is not None:
+        k = kfrac * s_np.size
+    if order == "sorted":
+        s_np = np.sort(s_np)
+    g_np = draw_grad(s_np.size, w.seed)
+    s = torch.from_numpy(s_np).to(dev)
+    g = torch.from_numpy(g_np).to(dev)
+    p, b, st, ws = stk.forward(s, k, alpha, want_stats=True, want_workspace=True)
+    assert st["path"] == _lib.PATH_BRACKET, st
+    g_seg = stk.backward(g, s, alpha, b, fwd_workspace=ws)
+    g_dense = stk.backward(g, s, alpha, b)
+    torch.cuda.synchronize()
+    res = {"p": p.cpu().numpy().astype(np.float64), "b": float(b.item()), "stats": st,
+           "grad": g_seg.cpu().numpy().astype(np.float64)}
+    check_full(res, s_np, k, alpha, g_np)
+    gs, gd = g_seg.cpu().numpy(), g_dense.cpu().numpy()
+    nz = gd != 0
+    assert np.array_equal(_bits(gs[nz]), _bits(gd[nz]))
+    bz = _bits(gs[~nz])
+    assert np.all((bz == 0) | (bz == _bits(gd[~nz])))  # +0 from a record, else the same +-0
+
+
+def test_segments_nonfinite_cotangent_and_foreign_threshold(dev):
+    """A non-finite cotangent at a saturated score still enters G = sum g d
+    as g * 0 = NaN, so the whole gradient is NaN, as in the score-reading
+    path; a threshold other than the forward's makes the backward read the
+    scores."""
+    s_np, k, alpha, w = make_workload("c4", n=SEG_N)
+    g_np = draw_grad(s_np.size, w.seed)
+    far = np.flatnonzero(s_np < 0.5)[:3]
+    g_np[far[0]] = np.inf
+    g_np[far[1]] = np.nan
+    s = torch.from_numpy(s_np).to(dev)
+    g = torch.from_numpy(g_np).to(dev)
+    p, b, ws = stk.forward(s, k, alpha, want_workspace=True)
+    g_seg = stk.backward(g, s, alpha, b, fwd_workspace=ws).cpu().numpy()
+    g_dense = stk.backward(g, s, alpha, b).cpu().numpy()
+    assert np.all(np.isnan(g_seg))
+    assert np.array_equal(_bits(g_seg), _bits(g_dense))
+    g = torch.from_numpy(draw_grad(s_np.size, w.seed)).to(dev)
+    g_seg = stk.backward(g, s, alpha, b, fwd_workspace=ws).cpu().numpy()
+    assert g_seg[far[2]] == 0.0 and np.all(np.isfinite(g_seg))
+    assert np.array_equal(g_seg, stk.backward(g, s, alpha, b).cpu().numpy())
+    b2 = b + 1e-4  # another threshold: the record does not apply
+    g_seg2 = stk.backward(g, s, alpha, b2, fwd_workspace=ws).cpu().numpy()
+    g_dense2 = stk.backward(g, s, alpha, b2).cpu().numpy()
+    assert np.array_equal(_bits(g_seg2), _bits(g_dense2))
+    assert not np.array_equal(_bits(g_seg2), _bits(g_seg))
+
+
+# --------------------------------------------------------------------------
 # full-size workloads, as the benchmark runs them
 # --------------------------------------------------------------------------
 def _sha(a):
@@ -417,8 +489,8 @@ def test_full_size_workload(dev, name):
     assert k == gold["k"]
     s = torch.from_numpy(s_np).to(dev)
     g = torch.from_numpy(g_np).to(dev)
-    p, b, st = stk.forward(s, k, alpha, want_stats=True)
-    grad = stk.backward(g, s, alpha, b)
+    p, b, st, ws = stk.forward(s, k, alpha, want_stats=True, want_workspace=True)
+    grad = stk.backward(g, s, alpha, b, fwd_workspace=ws)  # as the benchmark calls it
     torch.cuda.synchronize()
     b_gpu = float(b.item())
     b_ref = gold["b"]
