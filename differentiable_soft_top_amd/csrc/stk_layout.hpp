@@ -34,7 +34,7 @@ constexpr int kGridVjpSmall = 1024;
 // The VJP over saturated-score segments is bound by dependent round trips,
 // not by DRAM pages: it wants several work-groups per CU.
 constexpr int kGridVjpSegReduce = 1024;
-constexpr int kGridVjpSegApply = 2048;
+constexpr int kGridVjpSegApply = 1024;
 constexpr int kSelectThreads = 1024;     // bracket select
 constexpr int kSolveThreads = 512;       // segment solve
 constexpr int kCandCap = 32768;          // candidate keys the select step holds (32 per thread)
