@@ -55,6 +55,11 @@ ALGO_BYTES = {"pass1": 4, "emit": 8, "vjp_reduce": 8, "vjp_apply": 12}
 STEP_BYTES = sum(ALGO_BYTES.values())  # 32 B per score for fwd + bwd
 KERNEL_SOURCE = {"pass1": "pass1.hip", "emit": "emit_vjp.hip", "vjp_reduce": "emit_vjp.hip",
                  "vjp_apply": "emit_vjp.hip"}
+# device symbols of each streaming step: the score-reading kernel and, from 2^24
+# scores on, the variant that uses the emission's saturated-segment record
+KERNEL_SYMBOLS = {"pass1": ("stk::pass1_kernel",), "emit": ("stk::emit_kernel", "stk::emit_seg_kernel"),
+                  "vjp_reduce": ("stk::vjp_reduce_kernel", "stk::vjp_reduce_seg_kernel"),
+                  "vjp_apply": ("stk::vjp_apply_kernel", "stk::vjp_apply_seg_kernel")}
 
 
 class Runner:
@@ -192,15 +197,15 @@ def pmc_summary(fetch_csv, write_csv, workload="c4"):
                                "fetch_csv": os.path.basename(fetch_csv), "write_csv": os.path.basename(write_csv)}}
     ent = {}
     for kname in ALGO_BYTES:
-        fk = [name for name in fetch if "stk::%s_kernel" % kname in name]
-        wk = [name for name in write if "stk::%s_kernel" % kname in name]
+        fk = [name for name in fetch if any(sym in name for sym in KERNEL_SYMBOLS[kname])]
+        wk = [name for name in write if any(sym in name for sym in KERNEL_SYMBOLS[kname])]
         if not fk or not wk:
             continue
         fv = [v for name in fk for v in fetch[name]]
         wv = [v for name in wk for v in write[name]]
         fb = sum(fv) / len(fv) * 1024.0 * f_scale
         wb = sum(wv) / len(wv) * 1024.0 * w_scale
-        ent[kname] = {"fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+        ent[kname] = {"kernels": sorted(set(fk)), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                       "bytes_per_launch": fb + wb, "algorithmic_bytes_per_launch": ALGO_BYTES[kname] * n,
                       "launches": len(fv), "source_sha256": src_hash(kname)}
     result[workload] = ent

@@ -7,9 +7,10 @@
 // gfx950 design: a value-bucket sort whose second level runs in the solve.  The band lies in [bmin, bmax] (known
 // from pass-1) and its density there is smooth, so kBuckets equal-width value
 // buckets hold similar counts.  Three kernels:
-//   1. histogram: per-work-group LDS bucket counts; the last work-group turns
-//      them into global scatter offsets (bucket-major, work-group-minor);
-//   2. scatter: each element goes to its bucket (order within a bucket is
+//   1. histogram: per-work-group LDS bucket counts, one row per work-group;
+//   2. scatter: every work-group reads all rows, forms the bucket starts and
+//      its own offsets (bucket-major, work-group-minor) and moves each
+//      element of its chunk to its bucket (order within a bucket is
 //      arbitrary);
 //   3. bucket summaries: one work-group per bucket records its count,
 //      smallest and largest value and the anchored exponential sums

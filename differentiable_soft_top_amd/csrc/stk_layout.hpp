@@ -116,9 +116,9 @@ struct alignas(16) Status {
     // "last work-group" ticket; zeroed before the kernel that uses it and
     // returned to zero by the work-group that consumes it
     uint32_t ticket_radix;       // radix upsweep work-groups done (returned to 0 by the last)
-    // saturated-score segments written by this round's pass-1 (cleared by the
-    // select kernel and the full-sort reset), and what they were taken from:
-    // the VJP uses them only for the same scores, n and alpha (and b)
+    // saturated-score segments recorded by this forward's emission (cleared by
+    // the select kernel and the full-sort reset), and what they were taken
+    // from: the VJP uses them only for the same scores, n and alpha (and b)
     uint32_t seg_valid;
     uint64_t seg_n;
     double seg_alpha;
