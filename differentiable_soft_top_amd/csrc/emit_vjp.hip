@@ -370,41 +370,6 @@ __device__ __forceinline__ void block_out(const float* blk, uint32_t cnt, float*
     }
 }
 
-// Record segment `seg` from this wave's d values (value index order);
-// blk: this wave's LDS block.
-__device__ __forceinline__ void seg_record(const SegBufs& sb, int64_t seg, const float (&d)[kSegV], uint64_t* mstage,
-                                           float* blk)
-{
-    const int lane = lane_id();
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int i = 0; i < kSegV; ++i)
-        cnt += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(d[i] != 0.0f));
-    uint64_t* meta = sb.meta + seg * kSegMeta;
-    if (cnt > (uint32_t)kSegCap) {
-        if (lane == 0)
-            meta[kSegV] = kSegDense;
-        return;
-    }
-    uint32_t pre = 0;
-#pragma unroll
-    for (int i = 0; i < kSegV; ++i) {
-        const bool nz = d[i] != 0.0f;
-        const uint64_t lm = __builtin_amdgcn_ballot_w64(nz);
-        if (lane == 0)
-            mstage[i] = lm;
-        if (nz)
-            blk[pre + rank_in_mask(lm)] = d[i];
-        pre += (uint32_t)__popcll(lm);
-    }
-    block_out(blk, cnt, sb.val + seg * kSegCap);
-    if (lane < kSegV)
-        meta[lane] = mstage[lane];
-    else if (lane == kSegV)
-        meta[kSegV] = cnt;
-    __builtin_amdgcn_wave_barrier();
-}
-
 // Metadata of this wave's segments of tiles tile(c), c < kMetaChunk, into
 // mlds (tiles without a record, or past the vector, read as dense).
 template <typename TileOf>
@@ -433,17 +398,30 @@ __device__ __forceinline__ void fetch_meta(const VjpArgs& a, TileOf tile_of, int
 
 }  // namespace
 
+// Emission with the record, one wave per segment.  A first walk over the
+// wave's 16 values per lane evaluates the fp32 density d of each score and
+// lists the scores with d != 0 (value index order, lanes ascending) in LDS.
+// An unlisted score has d = 0 in fp32, so its fp64 p (as the score-only
+// emission computes it) is below 2^-150 or above 1 - 2^-150: its p is 0 or 1
+// and it adds 0 or 1 to the mass.  The listed scores -- about a tenth of c4's
+// -- are then evaluated 64 at a time: p with the fp64 exponential (as the
+// score-only emission), d again for the record's values, which go straight
+// to global memory when the segment keeps them.  A last walk picks each
+// lane's listed p out of LDS and writes p; it also gathers the 16 masks, one
+// per lane, for the record's metadata.  The fp64 arithmetic is thus spent
+// once per 64 listed scores, not once per score.
 template <bool kNT>
 __global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
 {
     constexpr int kB = kVjpBatchLarge;  // one large VJP tile per step (a segment per wave)
+    constexpr int kL = kSegScores + kWave;  // the list, then one slot per lane for unlisted scores
     __shared__ double red[kStreamThreads / kWave];
-    __shared__ uint64_t mstage[kStreamThreads / kWave][kSegV];
-    __shared__ float blk[kStreamThreads / kWave][kSegCap];
+    __shared__ float lst[kStreamThreads / kWave][kL];  // listed scores, then their p
     Status* st = a.st;
     if (st->solve_state != kSolveOk)
         return;
     const int tid = threadIdx.x;
+    const int lane = lane_id();
     const int wave = wave_index();
     const double b = *a.b;
     const double c = a.log2e_over_alpha;
@@ -452,28 +430,63 @@ __global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
     const int64_t T = whole_tiles<kB>(a.n);
     const float4* s4 = reinterpret_cast<const float4*>(a.s);
     float4* p4 = reinterpret_cast<float4*>(a.p);
+    float* ls = lst[wave];
     for (int64_t t0 = blockIdx.x; t0 < T; t0 += G) {
         const int64_t t = T - 1 - t0;  // descending: see the note above
+        const int64_t seg = t * kSegPerTile + wave;
         float4 v[kB];
         load_q<kB>(s4, t, v);
+        uint32_t nzb = 0, rtb = 0, cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kSegV; ++i) {
+            const float4 q = v[i / 4];
+            const float sv = (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
+            const double x = (double)sv - b;
+            const float d = dens(sv, b, c);
+            const bool nz = d != 0.0f;
+            nzb |= (uint32_t)nz << i;
+            rtb |= (uint32_t)(x > 0.0) << i;
+            const uint64_t lm = __builtin_amdgcn_ballot_w64(nz);
+            // unlisted lanes write a slot of their own past the list (no
+            // branch, so each value's work stays in one block, in order)
+            ls[nz ? cnt + rank_in_mask(lm) : (uint32_t)(kSegScores + lane)] = sv;
+            cnt += (uint32_t)__popcll(lm);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        acc += (double)__popc(rtb & ~nzb);  // unlisted scores right of b: p = 1
+        __builtin_amdgcn_wave_barrier();
+        const bool keep = cnt <= (uint32_t)kSegCap;
+        float* val = a.seg.val + seg * kSegCap;
+        for (uint32_t j = (uint32_t)lane; j < cnt; j += kWave) {
+            const float sv = ls[j];
+            ls[j] = emit_one(sv, b, c, acc);
+            if (keep)
+                val[j] = dens(sv, b, c);
+        }
+        __builtin_amdgcn_wave_barrier();
+        uint32_t pre = 0, mlo = 0, mhi = 0;
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-            float4 o;
-            o.x = emit_one(v[u].x, b, c, acc);
-            o.y = emit_one(v[u].y, b, c, acc);
-            o.z = emit_one(v[u].z, b, c, acc);
-            o.w = emit_one(v[u].w, b, c, acc);
-            store4<kNT>(&p4[t * (kB * kStreamThreads) + u * kStreamThreads + tid], o);
-        }
-        float d[kSegV];
+            float o[4];
 #pragma unroll
-        for (int q = 0; q < kB; ++q) {
-            d[4 * q + 0] = dens(v[q].x, b, c);
-            d[4 * q + 1] = dens(v[q].y, b, c);
-            d[4 * q + 2] = dens(v[q].z, b, c);
-            d[4 * q + 3] = dens(v[q].w, b, c);
+            for (int h = 0; h < 4; ++h) {
+                const int i = 4 * u + h;
+                const bool nz = (nzb >> i) & 1u;
+                const uint64_t lm = __builtin_amdgcn_ballot_w64(nz);
+                mlo = lane == i ? (uint32_t)lm : mlo;  // lane i keeps mask i
+                mhi = lane == i ? (uint32_t)(lm >> 32) : mhi;
+                const float lp = ls[nz ? pre + rank_in_mask(lm) : (uint32_t)(kSegScores + lane)];
+                o[h] = nz ? lp : (((rtb >> i) & 1u) ? 1.0f : 0.0f);
+                pre += (uint32_t)__popcll(lm);
+            }
+            store4<kNT>(&p4[t * (kB * kStreamThreads) + u * kStreamThreads + tid], make_float4(o[0], o[1], o[2], o[3]));
         }
-        seg_record(a.seg, t * kSegPerTile + wave, d, mstage[wave], blk[wave]);
+        uint64_t* meta = a.seg.meta + seg * kSegMeta;
+        if (lane < kSegV && keep)
+            meta[lane] = ((uint64_t)mhi << 32) | (uint64_t)mlo;
+        else if (lane == kSegV)
+            meta[kSegV] = keep ? (uint64_t)cnt : (uint64_t)kSegDense;
+        __builtin_amdgcn_wave_barrier();
     }
     for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads)
         a.p[i] = emit_one(a.s[i], b, c, acc);
