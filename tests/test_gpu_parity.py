@@ -419,9 +419,11 @@ def test_segments_match_oracle_and_score_path(dev, order, kfrac):
     right end (p = 1 without reading them).  Sorted, the segments are all
     far-left (sparse, none listed), all listed (dense) or all far-right
     (sparse, p = 1).  Element-wise parity with the oracle, and the backward
-    through the forward's record equals the score-reading backward: bit for
-    bit wherever the gradient is not zero; a zero is +0 where a record
-    served it, and the same +-0 where the segment was read from the scores."""
+    through the forward's record equals the score-reading backward: each
+    element is the same fp32 product of the same d and g with G/D, which the
+    two sum over different work-group splits (fp64, so G/D may move by an
+    fp32 ulp); a zero is +0 where a record served it, and the same +-0 where
+    the segment was read from the scores."""
     s_np, k, alpha, w = make_workload("c4", n=SEG_N)
     if kfrac is not None:
         k = kfrac * s_np.size
@@ -440,9 +442,25 @@ def test_segments_match_oracle_and_score_path(dev, order, kfrac):
     check_full(res, s_np, k, alpha, g_np)
     gs, gd = g_seg.cpu().numpy(), g_dense.cpu().numpy()
     nz = gd != 0
-    assert np.array_equal(_bits(gs[nz]), _bits(gd[nz]))
+    _assert_score_path_equal(gs, gd, g_np, alpha)
     bz = _bits(gs[~nz])
     assert np.all((bz == 0) | (bz == _bits(gd[~nz])))  # +0 from a record, else the same +-0
+
+
+def _assert_score_path_equal(gs, gd, g_np, alpha):
+    """The record-using and the score-reading gradients: zero at the same
+    places, elsewhere the same fp32 product of d, 1/alpha and g - G/D, where
+    G/D may differ by an fp32 ulp (the two sum D and G over different
+    work-group splits): |G/D| <= max|g|, d/alpha <= 1/(2 alpha), plus each
+    product's rounding."""
+    assert np.array_equal(gs == 0, gd == 0)
+    nz = gd != 0
+    if not np.any(nz):
+        return
+    ulp_ratio = float(np.spacing(np.float32(np.max(np.abs(g_np)))))
+    ulp_grad = float(np.spacing(np.float32(np.max(np.abs(gd)))))
+    diff = np.max(np.abs(gs[nz].astype(np.float64) - gd[nz]))
+    assert diff <= 2 * ulp_ratio / (2 * alpha) + 2 * ulp_grad, (diff, ulp_ratio, ulp_grad)
 
 
 def test_segments_nonfinite_cotangent_and_foreign_threshold(dev):
@@ -462,14 +480,17 @@ def test_segments_nonfinite_cotangent_and_foreign_threshold(dev):
     g_dense = stk.backward(g, s, alpha, b).cpu().numpy()
     assert np.all(np.isnan(g_seg))
     assert np.array_equal(_bits(g_seg), _bits(g_dense))
-    g = torch.from_numpy(draw_grad(s_np.size, w.seed)).to(dev)
+    g_np = draw_grad(s_np.size, w.seed)
+    g = torch.from_numpy(g_np).to(dev)
     g_seg = stk.backward(g, s, alpha, b, fwd_workspace=ws).cpu().numpy()
     assert g_seg[far[2]] == 0.0 and np.all(np.isfinite(g_seg))
-    assert np.array_equal(g_seg, stk.backward(g, s, alpha, b).cpu().numpy())
+    _assert_score_path_equal(g_seg, stk.backward(g, s, alpha, b).cpu().numpy(), g_np, alpha)
     b2 = b + 1e-4  # another threshold: the record does not apply
     g_seg2 = stk.backward(g, s, alpha, b2, fwd_workspace=ws).cpu().numpy()
     g_dense2 = stk.backward(g, s, alpha, b2).cpu().numpy()
-    assert np.array_equal(_bits(g_seg2), _bits(g_dense2))
+    _assert_score_path_equal(g_seg2, g_dense2, g_np, alpha)
+    zero = g_dense2 == 0  # both read the scores: the same signed zeros
+    assert np.array_equal(np.signbit(g_seg2[zero]), np.signbit(g_dense2[zero]))
     assert not np.array_equal(_bits(g_seg2), _bits(g_seg))
 
 
