@@ -286,13 +286,14 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_kernel(VjpArgs a, in
 // ---------------------------------------------------------------------------
 // Saturated-score segments (from kSegMinN scores on, aligned vectors).  The
 // emission, which knows b, records for each wave's 1024-score share of a
-// large VJP tile the scores whose fp32 density d_i = dens(s_i) is not 0 and,
-// when there are at most kSegCap, their d values.  The VJP then reads those
-// instead of the scores: its reduction takes d from the record (exactly 0
-// elsewhere, which is what the scores give) and stores the matching g values
+// large VJP tile the scores whose fp32 density d_i = dens(s_i) is at least
+// kDensCut = 2^-40 (|s_i - b| < 27.7 alpha) and, when there are at most
+// kSegCap, their d values.  The VJP then reads those instead of the scores:
+// its reduction takes d from the record and 0 elsewhere (dropping terms
+// below 2^-40, which moves D and G by at most n 2^-40 and no gradient element
+// by more than 2^-39 of the largest one) and stores the matching g values
 // compacted in its workspace; its gradient kernel reads only the compacted
-// (d, g) pairs and writes 0 for the other scores (where the score-reading
-// formula gives +-0, the sign following g - G/D).  If G is not finite (a
+// (d, g) pairs and writes +0 for the other scores.  If G is not finite (a
 // non-finite g) the gradient kernel reads the scores throughout.  The
 // record's metadata (16 masks and the count per segment) is fetched for
 // kMetaChunk tiles at once into LDS, so a tile's data loads are issued
@@ -300,6 +301,7 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_kernel(VjpArgs a, in
 // ---------------------------------------------------------------------------
 namespace {
 
+constexpr float kDensCut = 0x1p-40f;                  // densities the record keeps (at least)
 constexpr int kSegV = 4 * kVjpBatchLarge;             // values per lane in a segment
 constexpr int kSegPerTile = kStreamThreads / kWave;   // segments per large VJP tile
 constexpr int kMetaChunk = 8;                         // tiles whose metadata is fetched at once
@@ -403,16 +405,18 @@ __device__ __forceinline__ void fetch_meta(const VjpArgs& a, TileOf tile_of, int
 
 // Emission with the record, one wave per segment.  A first walk over the
 // wave's 16 values per lane evaluates the fp32 density d of each score and
-// lists the scores with d != 0 (value index order, lanes ascending) in LDS.
-// An unlisted score has d = 0 in fp32, so its fp64 p (as the score-only
-// emission computes it) is below 2^-150 or above 1 - 2^-150: its p is 0 or 1
-// and it adds 0 or 1 to the mass.  The listed scores -- about a tenth of c4's
-// -- are then evaluated 64 at a time: p with the fp64 exponential (as the
-// score-only emission), d again for the record's values, which go straight
-// to global memory when the segment keeps them.  A last walk picks each
-// lane's listed p out of LDS and writes p; it also gathers the 16 masks, one
-// per lane, for the record's metadata.  The fp64 arithmetic is thus spent
-// once per 64 listed scores, not once per score.
+// lists the scores with d >= kDensCut (value index order, lanes ascending)
+// in LDS.  An unlisted score lies more than 27.7 alpha from b, so its p is d
+// (left of b) or 1 - d (right of b, 1 in fp32) with d < 2^-40: taken from
+// the fp32 d, p is within 1e-18 of the fp64 value, and the lane's unlisted
+// scores enter the mass as a count (right of b) plus an fp32 sum of their
+// signed d (at most 16 terms below 2^-40 per tile).  The listed scores --
+// about 4% of c4's -- are then evaluated 64 at a time: p with the fp64
+// exponential (as the score-only emission), d again for the record's
+// values, which go straight to global memory when the segment keeps them.
+// A last walk picks each lane's listed p out of LDS and writes p; it also
+// gathers the 16 masks, one per lane, for the record's metadata.  The fp64
+// arithmetic is thus spent once per 64 listed scores, not once per score.
 template <bool kNT>
 __global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
 {
@@ -439,16 +443,20 @@ __global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
         const int64_t seg = t * kSegPerTile + wave;
         float4 v[kB];
         load_q<kB>(s4, t, v);
-        uint32_t nzb = 0, rtb = 0, cnt = 0;
+        uint32_t nzb = 0, cnt = 0, n_right = 0;
+        float fp[kSegV];      // p of the score if it is not listed
+        float far_d = 0.0f;   // unlisted scores' signed d
 #pragma unroll
         for (int i = 0; i < kSegV; ++i) {
             const float4 q = v[i / 4];
             const float sv = (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
-            const double x = (double)sv - b;
+            const bool rt = (double)sv - b > 0.0;
             const float d = dens(sv, b, c);
-            const bool nz = d != 0.0f;
+            const bool nz = d >= kDensCut;
+            fp[i] = rt ? 1.0f : d;
+            far_d += nz ? 0.0f : (rt ? -d : d);
+            n_right += (uint32_t)(!nz && rt);
             nzb |= (uint32_t)nz << i;
-            rtb |= (uint32_t)(x > 0.0) << i;
             const uint64_t lm = __builtin_amdgcn_ballot_w64(nz);
             // unlisted lanes write a slot of their own past the list (no
             // branch, so each value's work stays in one block, in order)
@@ -456,7 +464,7 @@ __global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
             cnt += (uint32_t)__popcll(lm);
             __builtin_amdgcn_sched_barrier(0);
         }
-        acc += (double)__popc(rtb & ~nzb);  // unlisted scores right of b: p = 1
+        acc += (double)n_right + (double)far_d;  // unlisted scores: p = 1 - d or d
         __builtin_amdgcn_wave_barrier();
         const bool keep = cnt <= (uint32_t)kSegCap;
         float* val = a.seg.val + seg * kSegCap;
@@ -479,7 +487,7 @@ __global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
                 mlo = lane == i ? (uint32_t)lm : mlo;  // lane i keeps mask i
                 mhi = lane == i ? (uint32_t)(lm >> 32) : mhi;
                 const float lp = ls[nz ? pre + rank_in_mask(lm) : (uint32_t)(kSegScores + lane)];
-                o[h] = nz ? lp : (((rtb >> i) & 1u) ? 1.0f : 0.0f);
+                o[h] = nz ? lp : fp[i];
                 pre += (uint32_t)__popcll(lm);
             }
             store4<kNT>(&p4[t * (kB * kStreamThreads) + u * kStreamThreads + tid], make_float4(o[0], o[1], o[2], o[3]));
