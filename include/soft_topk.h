@@ -175,21 +175,23 @@ int soft_topk_backward(const float* grad_p, const float* scores, int64_t n,
  * written since, 256-byte aligned; NULL = none, as soft_topk_backward).
  * Gist.science summary of Fast LapSum, section 2.2: outside a narrow band
  * of scores around b the soft indicator is saturated, and there the fp32
- * density d_i = e^{-|s_i - b|/alpha}/2 is exactly 0.  From 2^24 scores on
+ * density d_i = e^{-|s_i - b|/alpha}/2 is negligible.  From 2^24 scores on
  * (16-byte aligned vectors), the forward's emission, which knows b, records
- * for every 1024-score segment which scores have d_i != 0 and, when at most
- * 256 do, their d_i.  The backward then takes d from that record instead of
- * reading the scores, and writes grad = 0 for the other scores of such a
- * segment.  Each gradient element is the same fp32 arithmetic on the same
- * d_i as soft_topk_backward's.  D and G are fp64 sums split over another
- * number of work-groups, so G/D may differ in its last fp64 bits before it
- * is rounded to fp32.  A zero served from the record is always +0, where
- * the score-reading formula gives -0 when g_i < G/D.  A non-finite grad_p makes G non-finite,
- * and then every score is read, so the NaN gradient matches too.  The record
- * is used only if the forward status in fwd_workspace names these scores
- * (pointer), n, alpha and this b; otherwise the scores are read.  The
- * scores must be unchanged since that forward.  The backward workspace also
- * holds the listed g values between its two kernels.  Errors as
+ * for every 1024-score segment which scores have d_i >= 2^-40
+ * (|s_i - b| < 27.7 alpha) and, when at most 256 do, their d_i.  The
+ * backward then takes d from that record instead of reading the scores: the
+ * other scores enter D and G with d = 0 and get grad = +0.  Leaving them out
+ * moves D and G by at most n 2^-40 and no element of the gradient by more
+ * than 2^-39 of the largest one.  Every other element is the same fp32
+ * arithmetic on the same d_i as soft_topk_backward's.  D and G are fp64 sums
+ * split over another number of work-groups, so G/D may differ in its last
+ * bits before it is rounded to fp32.  Every g enters G (as g * 0 where d is
+ * left out), so a non-finite grad_p makes G non-finite; then every score is
+ * read, and the NaN gradient matches soft_topk_backward's.  The record is
+ * used only if the forward status in fwd_workspace names these scores
+ * (pointer), n, alpha and this b; otherwise the scores are read.  The scores
+ * must be unchanged since that forward.  The backward workspace also holds
+ * the listed g values between its two kernels.  Errors as
  * soft_topk_backward, plus EWORKSPACE for a misaligned fwd_workspace.
  */
 int soft_topk_backward_ex(const float* grad_p, const float* scores, int64_t n,
