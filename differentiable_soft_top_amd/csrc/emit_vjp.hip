@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kStreamThreads) void emit_finalize_kernel(EmitArgs 
     __shared__ double m;
     Status* st = a.st;
     if (st->solve_state != kSolveOk) {
-        publish_status(st, a.mirror);
+        publish_status(st, a.mirror, 0u);
         return;
     }
     double t = 0.0;
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kStreamThreads) void emit_finalize_kernel(EmitArgs 
         st->emit_done = 1;
     }
     __syncthreads();
-    publish_status(st, a.mirror);
+    publish_status(st, a.mirror, 0u);
 }
 
 // ---------------------------------------------------------------------------

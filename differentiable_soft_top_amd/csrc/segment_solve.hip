@@ -756,7 +756,7 @@ __global__ __launch_bounds__(kST) void solve_kernel(SolveArgs a)
         level2(a, L, job);
     // every exit ends here: publish the status for the host
     __syncthreads();
-    publish_status(a.st, a.mirror);
+    publish_status(a.st, a.mirror, a.seq);
 }
 
 hipError_t launch_solve(const SolveArgs& a, hipStream_t stream)

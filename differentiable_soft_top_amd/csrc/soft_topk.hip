@@ -299,19 +299,24 @@ struct Ctx {
     hipStream_t stream;
     Status* st;
     uint64_t seed;
-    Status* mirror0;   // device address of host mirror slot 0 (solve)
-    Status* mirror1;   // device address of host mirror slot 1 (mass fold)
+    Mirror* mirror0;   // device address of host mirror slot 0 (solve)
+    Mirror* mirror1;   // device address of host mirror slot 1 (mass fold)
 };
 
 // Two status mirrors per host thread in pinned, fine-grained host memory:
 // slot 0 is written by the segment solve as it finishes (the bracket
 // certificate), slot 1 by the fold of the certification pass (the fp64 mass).
-// Each is followed by an event the host can wait on without draining the
-// rest of the stream.  A plain copy into slot 0 serves the rare reads that
-// follow no solve (the score range of the full-sort route).
+// A solve publishes slot 0 with a sequence number of its own, written after
+// a system-scope release: the host spins on that number instead of waiting
+// for an event, so nothing is recorded on the stream between the solve and
+// the emission (an event there costs the GPU a few microseconds between the
+// two kernels).  Slot 1, and a plain copy into slot 0 for the rare reads
+// that follow no solve (the score range of the full-sort route), are each
+// followed by an event the host waits on without draining the stream.
 struct HostSlots {
-    Status* pinned = nullptr;
+    Mirror* pinned = nullptr;
     hipEvent_t ev[2] = {nullptr, nullptr};
+    uint32_t seq = 0;      // last publication number handed out
 };
 thread_local HostSlots g_host;
 
@@ -319,8 +324,9 @@ int ensure_host_slots()
 {
     if (!g_host.pinned) {
         void* ptr = nullptr;
-        STK_HIP(hipHostMalloc(&ptr, 2 * sizeof(Status), hipHostMallocCoherent | hipHostMallocMapped | hipHostMallocPortable));
-        g_host.pinned = static_cast<Status*>(ptr);
+        STK_HIP(hipHostMalloc(&ptr, 2 * sizeof(Mirror), hipHostMallocCoherent | hipHostMallocMapped | hipHostMallocPortable));
+        memset(ptr, 0, 2 * sizeof(Mirror));
+        g_host.pinned = static_cast<Mirror*>(ptr);
         for (int i = 0; i < 2; ++i)
             STK_HIP(hipEventCreateWithFlags(&g_host.ev[i], hipEventDisableTiming));
     }
@@ -328,12 +334,20 @@ int ensure_host_slots()
 }
 
 // Device-usable address of a mirror slot.
-Status* mirror_slot(int slot)
+Mirror* mirror_slot(int slot)
 {
     void* dev = nullptr;
     if (hipHostGetDevicePointer(&dev, g_host.pinned, 0) != hipSuccess || dev == nullptr)
         return nullptr;
-    return static_cast<Status*>(dev) + slot;
+    return static_cast<Mirror*>(dev) + slot;
+}
+
+// The number the next solve publishes slot 0 with (never 0).
+uint32_t next_publication()
+{
+    if (++g_host.seq == 0u)
+        g_host.seq = 1u;
+    return g_host.seq;
 }
 
 int mark_status(const Ctx& x, int slot)
@@ -347,14 +361,38 @@ int enqueue_status_copy(const Ctx& x, int slot)
     int rc = ensure_host_slots();
     if (rc)
         return rc;
-    STK_HIP(hipMemcpyAsync(g_host.pinned + slot, x.st, sizeof(Status), hipMemcpyDeviceToHost, x.stream));
+    STK_HIP(hipMemcpyAsync(&g_host.pinned[slot].st, x.st, sizeof(Status), hipMemcpyDeviceToHost, x.stream));
     return mark_status(x, slot);
 }
 
 int wait_status(int slot, Status* host)
 {
     STK_HIP(hipEventSynchronize(g_host.ev[slot]));
-    memcpy(host, g_host.pinned + slot, sizeof(Status));
+    memcpy(host, &g_host.pinned[slot].st, sizeof(Status));
+    return SOFT_TOPK_OK;
+}
+
+// Wait for the last solve's publication of slot 0.  The stream is queried
+// now and then: an error on it is returned, and a stream that has drained
+// without the publication (which cannot happen short of an error) is one.
+int wait_solve(const Ctx& x, Status* host)
+{
+    const uint32_t want = g_host.seq;
+    const uint32_t* seq = &g_host.pinned[0].seq;
+    for (uint32_t spins = 1; __atomic_load_n(seq, __ATOMIC_ACQUIRE) != want; ++spins) {
+        if ((spins & 1023u) == 0u) {
+            const hipError_t e = hipStreamQuery(x.stream);
+            if (e == hipSuccess) {
+                if (__atomic_load_n(seq, __ATOMIC_ACQUIRE) == want)
+                    break;
+                return hip_fail(hipErrorLaunchFailure);
+            }
+            if (e != hipErrorNotReady)
+                return hip_fail(e);
+        }
+        __builtin_ia32_pause();
+    }
+    memcpy(host, const_cast<const Status*>(&g_host.pinned[0].st), sizeof(Status));
     return SOFT_TOPK_OK;
 }
 
@@ -441,6 +479,7 @@ int enqueue_band_solve(const Ctx& x, bool direct)
     so.out_b = x.b;
     so.st = x.st;
     so.mirror = x.mirror0;
+    so.seq = next_publication();
     STK_HIP(launch_solve(so, x.stream));
     return SOFT_TOPK_OK;
 }
@@ -535,20 +574,18 @@ int enqueue_fullsort(const Ctx& x, const Status& range)
     so.out_b = x.b;
     so.st = x.st;
     so.mirror = x.mirror0;
+    so.seq = next_publication();
     STK_HIP(launch_solve(so, x.stream));
     return SOFT_TOPK_OK;
 }
 
-// After a solve (which has written mirror slot 0 as it finished): mark slot
-// 0 and enqueue the emission with its per-work-group fp64 sums of p.  When
-// the mass is to be waited for, also enqueue the fold of those sums (which
-// writes slot 1) and mark slot 1.
+// After a solve (which publishes mirror slot 0 as it finishes): enqueue the
+// emission with its per-work-group fp64 sums of p.  When the mass is to be
+// waited for, also enqueue the fold of those sums (which writes slot 1) and
+// mark slot 1.
 int enqueue_certify_emit(const Ctx& x, bool wait_mass)
 {
-    int rc = mark_status(x, 0);
-    if (rc)
-        return rc;
-    rc = enqueue_emit(x, wait_mass);
+    int rc = enqueue_emit(x, wait_mass);
     if (rc)
         return rc;
     return wait_mass ? mark_status(x, 1) : SOFT_TOPK_OK;
@@ -754,7 +791,7 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
             rc = enqueue_certify_emit(x, wait_mass);
             if (rc)
                 return rc;
-            rc = wait_status(0, &h);
+            rc = wait_solve(x, &h);
             if (rc)
                 return rc;
             if (h.solve_state == kSolveDirectOverflow) {
@@ -766,7 +803,7 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
                 rc = enqueue_certify_emit(x, wait_mass);
                 if (rc)
                     return rc;
-                rc = wait_status(0, &h);
+                rc = wait_solve(x, &h);
                 if (rc)
                     return rc;
             }
@@ -838,7 +875,7 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
         rc = enqueue_certify_emit(x, wait_mass);
         if (rc)
             return rc;
-        rc = wait_status(0, &h);
+        rc = wait_solve(x, &h);
         if (rc)
             return rc;
         if (h.solve_state != kSolveOk)

@@ -127,17 +127,34 @@ struct alignas(16) Status {
 static_assert(sizeof(Status) <= 256, "status block must fit 256 bytes");
 static_assert(sizeof(Status) % 4 == 0, "status block is copied as 32-bit words");
 
+// A host-visible mirror of the status block (pinned, fine-grained host
+// memory) and the sequence number of the publication that filled it.
+struct alignas(16) Mirror {
+    Status st;
+    uint32_t seq;
+    uint32_t pad[3];
+};
+
 // Copy the status block to its host-visible mirror: one wave, one 32-bit
 // word per lane.  The caller has synchronised the work-group, so every
-// field this work-group wrote is in place; the stores to the mirror (pinned,
-// fine-grained host memory) are complete when the kernel is.
-__device__ __forceinline__ void publish_status(const Status* st, Status* mirror)
+// field this work-group wrote is in place.  The copy is released at system
+// scope before seq is written, so a host that reads seq (with acquire) sees
+// the whole block; without seq (0) the stores are complete when the kernel
+// is.
+__device__ __forceinline__ void publish_status(const Status* st, Mirror* mirror, uint32_t seq)
 {
     constexpr int kWords = (int)(sizeof(Status) / 4);
-    if (mirror == nullptr)
+    static_assert(kWords <= 64, "one word per lane of one wave");
+    if (mirror == nullptr || threadIdx.x >= 64)
         return;
-    for (int i = threadIdx.x; i < kWords; i += 64)
-        reinterpret_cast<volatile uint32_t*>(mirror)[i] = reinterpret_cast<const volatile uint32_t*>(st)[i];
+    if ((int)threadIdx.x < kWords)
+        reinterpret_cast<volatile uint32_t*>(&mirror->st)[threadIdx.x] =
+            reinterpret_cast<const volatile uint32_t*>(st)[threadIdx.x];
+    if (seq != 0u) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");  // system scope, release only
+        if (threadIdx.x == 0)
+            *reinterpret_cast<volatile uint32_t*>(&mirror->seq) = seq;
+    }
 }
 
 struct alignas(16) Pass1Partial {
@@ -274,7 +291,8 @@ struct SolveArgs {
     double log2e_over_alpha;
     double* out_b;
     Status* st;
-    Status* mirror;               // host-visible copy of the status written at the end (may be null)
+    Mirror* mirror;               // host-visible copy of the status written at the end (may be null)
+    uint32_t seq;                 // its publication number (0: none)
 };
 hipError_t launch_solve(const SolveArgs& a, hipStream_t stream);
 
@@ -312,7 +330,7 @@ struct EmitArgs {
     double* partials;
     int32_t blocks;
     Status* st;
-    Status* mirror;               // host-visible copy of the status written by the mass fold (may be null)
+    Mirror* mirror;               // host-visible copy of the status written by the mass fold (may be null)
     SegBufs seg;                  // used when pass-1 wrote them (st->seg_valid)
 };
 hipError_t launch_emit(const EmitArgs& a, bool fold_mass, hipStream_t stream);
