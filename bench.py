@@ -55,7 +55,7 @@ ALGO_BYTES = {"pass1": 4, "emit": 8, "vjp_reduce": 8, "vjp_apply": 12}
 STEP_BYTES = sum(ALGO_BYTES.values())  # 32 B per score for fwd + bwd
 KERNEL_SOURCE = {"pass1": "pass1.hip", "emit": "emit_vjp.hip", "vjp_reduce": "emit_vjp.hip",
                  "vjp_apply": "emit_vjp.hip"}
-# device symbols of each streaming step: the score-reading kernel and, from 2^24
+# device symbols of each streaming step: the score-reading kernel and, from 2^22
 # scores on, the variant that uses the emission's saturated-segment record
 KERNEL_SYMBOLS = {"pass1": ("stk::pass1_kernel",), "emit": ("stk::emit_kernel", "stk::emit_seg_kernel"),
                   "vjp_reduce": ("stk::vjp_reduce_kernel", "stk::vjp_reduce_seg_kernel"),

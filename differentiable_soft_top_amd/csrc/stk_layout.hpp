@@ -52,8 +52,8 @@ constexpr int kSegScores = 1024;
 constexpr int kSegCap = 256;
 constexpr int kSegMeta = 17;                 // u64 words per segment: 16 listed masks, count
 constexpr uint32_t kSegDense = 0xFFFFFFFFu;
-constexpr int64_t kSegMinN = 1 << 24;
-static_assert(kStreamThreads == 256 && kVjpBatchLarge == 4 && kSegMinN >= kStreamLargeMin,
+constexpr int64_t kSegMinN = 1 << 22;  // measured: from 10^7 scores on the record pays
+static_assert(kStreamThreads == 256 && kVjpBatchLarge == 4,
               "segment geometry: large VJP tiles of 256 x 4 float4");
 constexpr int kBuckets = 512;            // value buckets of the band sort
 constexpr int kBucketCap = 8192;         // largest group the solve sorts in LDS

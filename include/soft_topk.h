@@ -175,7 +175,7 @@ int soft_topk_backward(const float* grad_p, const float* scores, int64_t n,
  * written since, 256-byte aligned; NULL = none, as soft_topk_backward).
  * Gist.science summary of Fast LapSum, section 2.2: outside a narrow band
  * of scores around b the soft indicator is saturated, and there the fp32
- * density d_i = e^{-|s_i - b|/alpha}/2 is negligible.  From 2^24 scores on
+ * density d_i = e^{-|s_i - b|/alpha}/2 is negligible.  From 2^22 scores on
  * (16-byte aligned vectors), the forward's emission, which knows b, records
  * for every 1024-score segment which scores have d_i >= 2^-40
  * (|s_i - b| < 27.7 alpha) and, when at most 256 do, their d_i.  The

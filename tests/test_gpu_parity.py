@@ -402,8 +402,8 @@ def test_bracket_is_the_exact_order_statistics(dev, name, n, kfrac, prm):
 
 
 # --------------------------------------------------------------------------
-# saturated-score segments (from 2^24 scores on): emission and the VJP read
-# the segments instead of the scores where pass-1 recorded them
+# saturated-score segments (from 2^22 scores on): the VJP reads the
+# emission's record of the scores near b instead of the scores
 # --------------------------------------------------------------------------
 SEG_N = (1 << 24) + 4099  # whole tiles plus a ragged end
 
