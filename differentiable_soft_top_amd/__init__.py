@@ -18,7 +18,8 @@ import ctypes
 from . import _lib
 from ._lib import Params, SoftTopKError, Stats  # noqa: F401
 
-__all__ = ["soft_topk", "forward", "backward", "Params", "Stats", "SoftTopKError", "default_params"]
+__all__ = ["soft_topk", "forward", "backward", "rows_forward", "rows_backward", "Params", "Stats", "SoftTopKError",
+           "default_params"]
 
 
 def default_params() -> Params:
@@ -87,6 +88,53 @@ def backward(grad_p, s, alpha: float, b, out=None, fwd_workspace=None):
                                    float(alpha), ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(g.data_ptr()),
                                    fw, fw_bytes, ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream_handle(s))
     _lib.check(rc, "soft_topk_backward")
+    return g
+
+
+def _check_rows(s):
+    import torch
+    if not isinstance(s, torch.Tensor) or s.dtype != torch.float32 or s.dim() != 2 or not s.is_contiguous():
+        raise TypeError("scores must be a contiguous 2-D float32 tensor (rows x n_row)")
+    if s.device.type != "cuda":
+        raise TypeError("scores must live on a ROCm device")
+
+
+def rows_forward(s, k: float, alpha: float, out_p=None):
+    """Batched rows (soft_topk_rows_forward): s is rows x n_row; returns (p, b) with b one fp64
+    threshold per row.  A row holding a non-finite score gets b = NaN and p = NaN."""
+    import torch
+    _check_rows(s)
+    lib = _lib.load()
+    rows, n_row = s.shape
+    ws_bytes = lib.soft_topk_rows_workspace_bytes(rows, n_row)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=s.device)
+    p = out_p if out_p is not None else torch.empty_like(s)
+    b = torch.empty(rows, dtype=torch.float64, device=s.device)
+    rc = lib.soft_topk_rows_forward(ctypes.c_void_p(s.data_ptr()), rows, n_row, float(k), float(alpha),
+                                    ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                                    ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream_handle(s))
+    _lib.check(rc, "soft_topk_rows_forward")
+    return p, b
+
+
+def rows_backward(grad_p, s, alpha: float, b, out=None):
+    """Backward of rows_forward (soft_topk_rows_backward), each row with its own D and G."""
+    import torch
+    _check_rows(s)
+    if grad_p.dtype != torch.float32 or grad_p.shape != s.shape or not grad_p.is_contiguous():
+        raise TypeError("grad_p must be a contiguous float32 tensor shaped like scores")
+    if b.dtype != torch.float64 or b.numel() != s.shape[0] or b.device != s.device:
+        raise TypeError("b must be the per-row float64 device tensor from rows_forward")
+    lib = _lib.load()
+    rows, n_row = s.shape
+    ws_bytes = lib.soft_topk_rows_workspace_bytes(rows, n_row)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=s.device)
+    g = out if out is not None else torch.empty_like(s)
+    rc = lib.soft_topk_rows_backward(ctypes.c_void_p(grad_p.data_ptr()), ctypes.c_void_p(s.data_ptr()), rows,
+                                     n_row, float(alpha), ctypes.c_void_p(b.data_ptr()),
+                                     ctypes.c_void_p(g.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws_bytes,
+                                     _stream_handle(s))
+    _lib.check(rc, "soft_topk_rows_backward")
     return g
 
 

@@ -88,6 +88,12 @@ def load():
     lib.soft_topk_backward.restype = ctypes.c_int
     lib.soft_topk_backward_ex.argtypes = [fp, fp, i64, dbl, dp, fp, vp, sz, vp, sz, vp]
     lib.soft_topk_backward_ex.restype = ctypes.c_int
+    lib.soft_topk_rows_forward.argtypes = [fp, i64, i64, dbl, dbl, fp, dp, vp, sz, vp]
+    lib.soft_topk_rows_forward.restype = ctypes.c_int
+    lib.soft_topk_rows_backward.argtypes = [fp, fp, i64, i64, dbl, dp, fp, vp, sz, vp]
+    lib.soft_topk_rows_backward.restype = ctypes.c_int
+    lib.soft_topk_rows_workspace_bytes.argtypes = [i64, i64]
+    lib.soft_topk_rows_workspace_bytes.restype = sz
     lib.soft_topk_strerror.argtypes = [ctypes.c_int]
     lib.soft_topk_strerror.restype = ctypes.c_char_p
     lib.soft_topk_last_hip_error.argtypes = []

@@ -657,6 +657,24 @@ namespace {
 
 bool n_ok(int64_t n) { return n >= 1 && n <= 0x7fffffffLL; }
 
+bool rows_ok(int64_t rows, int64_t n_row)
+{
+    return rows >= 1 && n_row >= 1 && rows <= 0x7fffffffLL && n_ok(n_row) && rows <= INT64_MAX / n_row;
+}
+
+RowsArgs rows_args(const float* s, int64_t rows, int64_t n_row, double alpha)
+{
+    RowsArgs a;
+    memset(&a, 0, sizeof(a));
+    a.s = s;
+    a.rows = rows;
+    a.n_row = (int32_t)n_row;
+    a.alpha = alpha;
+    a.log2e_over_alpha = kLog2e / alpha;
+    return a;
+}
+
+
 soft_topk_params resolve(const soft_topk_params* params)
 {
     soft_topk_params p;
@@ -951,6 +969,75 @@ int soft_topk_backward_ex(const float* grad_p, const float* scores, int64_t n, d
         }
     }
     STK_HIP(launch_vjp(a, static_cast<hipStream_t>(stream)));
+    return SOFT_TOPK_OK;
+}
+
+size_t soft_topk_rows_workspace_bytes(int64_t rows, int64_t n_row)
+{
+    if (!rows_ok(rows, n_row) || n_row <= kRowMax)
+        return 0;
+    const size_t f = soft_topk_workspace_bytes(n_row, nullptr);
+    const size_t bw = soft_topk_backward_workspace_bytes(n_row);
+    return f > bw ? f : bw;
+}
+
+int soft_topk_rows_forward(const float* scores, int64_t rows, int64_t n_row, double k, double alpha, float* out_p,
+                           double* out_b, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!scores || !out_p || !out_b || !rows_ok(rows, n_row))
+        return SOFT_TOPK_EINVAL;
+    if (!(alpha > 0.0) || !isfinite(alpha) || !(k > 0.0) || !(k < (double)n_row) || !isfinite(k))
+        return SOFT_TOPK_EINVAL;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n_row <= kRowMax) {
+        RowsArgs a = rows_args(scores, rows, n_row, alpha);
+        a.p = out_p;
+        a.b = out_b;
+        a.k = k;
+        STK_HIP(launch_rows(a, true, st));
+        return SOFT_TOPK_OK;
+    }
+    // longer rows: the single-vector path, one row after another
+    if (!workspace || workspace_bytes < soft_topk_workspace_bytes(n_row, nullptr))
+        return SOFT_TOPK_EWORKSPACE;
+    for (int64_t r = 0; r < rows; ++r) {
+        float* p = out_p + r * n_row;
+        const int rc = soft_topk_forward(scores + r * n_row, n_row, k, alpha, p, out_b + r, workspace, workspace_bytes,
+                                         stream);
+        if (rc == SOFT_TOPK_ENONFINITE) {
+            // all-ones bytes are a NaN in fp32 and in fp64
+            STK_HIP(hipMemsetAsync(p, 0xFF, sizeof(float) * (size_t)n_row, st));
+            STK_HIP(hipMemsetAsync(out_b + r, 0xFF, sizeof(double), st));
+        } else if (rc) {
+            return rc;
+        }
+    }
+    return SOFT_TOPK_OK;
+}
+
+int soft_topk_rows_backward(const float* grad_p, const float* scores, int64_t rows, int64_t n_row, double alpha,
+                            const double* b, float* grad_s, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!grad_p || !scores || !b || !grad_s || !rows_ok(rows, n_row))
+        return SOFT_TOPK_EINVAL;
+    if (!(alpha > 0.0) || !isfinite(alpha))
+        return SOFT_TOPK_EINVAL;
+    if (n_row <= kRowMax) {
+        RowsArgs a = rows_args(scores, rows, n_row, alpha);
+        a.g = grad_p;
+        a.grad = grad_s;
+        a.b_in = b;
+        STK_HIP(launch_rows(a, false, static_cast<hipStream_t>(stream)));
+        return SOFT_TOPK_OK;
+    }
+    if (!workspace || workspace_bytes < soft_topk_backward_workspace_bytes(n_row))
+        return SOFT_TOPK_EWORKSPACE;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int rc = soft_topk_backward(grad_p + r * n_row, scores + r * n_row, n_row, alpha, b + r,
+                                          grad_s + r * n_row, workspace, workspace_bytes, stream);
+        if (rc)
+            return rc;
+    }
     return SOFT_TOPK_OK;
 }
 

@@ -55,6 +55,7 @@ constexpr uint32_t kSegDense = 0xFFFFFFFFu;
 constexpr int64_t kSegMinN = 1 << 22;  // measured: from 10^7 scores on the record pays
 static_assert(kStreamThreads == 256 && kVjpBatchLarge == 4,
               "segment geometry: large VJP tiles of 256 x 4 float4");
+constexpr int kRowMax = 8192;            // longest row one work-group solves (batched rows)
 constexpr int kBuckets = 512;            // value buckets of the band sort
 constexpr int kBucketCap = 8192;         // largest group the solve sorts in LDS
 // The band is sorted whole (no buckets) when its expected size, n times the
@@ -356,5 +357,20 @@ struct VjpArgs {
 hipError_t launch_vjp(const VjpArgs& a, hipStream_t stream);
 
 hipError_t launch_reset_status(Status* st, hipStream_t stream, bool open_bracket);
+
+// Batched rows (rows x n_row, row-major, n_row <= kRowMax): one work-group
+// per row.
+struct RowsArgs {
+    const float* s;
+    const float* g;               // backward: cotangent
+    float* p;                     // forward: output
+    float* grad;                  // backward: output
+    double* b;                    // forward: per-row thresholds (output)
+    const double* b_in;           // backward: per-row thresholds
+    int64_t rows;
+    int32_t n_row;
+    double k, alpha, log2e_over_alpha;
+};
+hipError_t launch_rows(const RowsArgs& a, bool forward, hipStream_t stream);
 
 }  // namespace stk

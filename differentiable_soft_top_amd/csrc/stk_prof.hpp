@@ -27,6 +27,8 @@ enum KernelId : int {
     kKVjpReduce,
     kKVjpApply,
     kKReset,
+    kKRowsForward,
+    kKRowsBackward,
     kKernelCount
 };
 

@@ -199,6 +199,42 @@ int soft_topk_backward_ex(const float* grad_p, const float* scores, int64_t n,
                           const void* fwd_workspace, size_t fwd_workspace_bytes,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Batched rows.  The aiqbench.com abstract and the gist.science summary of
+ * Fast LapSum (sections 1 and 2) name expert activation, token routing and
+ * attention pruning as the operator's uses: many independent rows, each a
+ * soft top-k of its own.  scores: fp32[rows * n_row] (device), row r at
+ * scores + r * n_row.  Every row gets its own threshold b_r (out_b: fp64[rows],
+ * device) with sum_i F((s_ri - b_r)/alpha) = k, and out_p[r * n_row + i] =
+ * F((s_ri - b_r)/alpha); k and alpha are shared by all rows (0 < k < n_row,
+ * alpha > 0).  Rows of at most 8192 scores are solved one work-group per
+ * row, fully asynchronously on `stream`, and need no workspace.  Longer
+ * rows run the single-vector forward row after row (each waits for its
+ * status) in `workspace`.  A row holding a NaN or an infinite score gets
+ * b = NaN and p = NaN; the call still returns OK.  Errors: EINVAL,
+ * EWORKSPACE before any launch; EHIP on a launch failure.
+ */
+int soft_topk_rows_forward(const float* scores, int64_t rows, int64_t n_row,
+                           double k, double alpha, float* out_p, double* out_b,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of the batched rows: grad_s[r * n_row + i] =
+ * (d_ri/alpha)(g_ri - G_r/D_r) with each row's own D_r and G_r, as in
+ * soft_topk_backward (b: the forward's out_b).  Rows of at most 8192 scores
+ * need no workspace and are fully asynchronous; longer rows run the
+ * single-vector backward row after row in `workspace`.  Errors as
+ * soft_topk_rows_forward.
+ */
+int soft_topk_rows_backward(const float* grad_p, const float* scores, int64_t rows,
+                            int64_t n_row, double alpha, const double* b,
+                            float* grad_s, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Workspace bytes for the batched calls: 0 for rows of at most 8192 scores
+ * (none needed) and for invalid sizes (the calls then return EINVAL). */
+size_t soft_topk_rows_workspace_bytes(int64_t rows, int64_t n_row);
+
 /* Text for a return code. */
 const char* soft_topk_strerror(int code);
 

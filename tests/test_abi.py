@@ -82,6 +82,46 @@ def test_backward_rejects_bad_arguments_before_launch(lib):
     assert lib.soft_topk_backward(fake, fake, 10, 0.1, fake, fake, fake, 1, None) == _lib.EWORKSPACE
 
 
+def test_rows_reject_bad_arguments_before_launch(lib):
+    fake = ctypes.c_void_p(0x1000)
+
+    def fwd(s=fake, rows=4, n_row=100, k=5.0, alpha=0.1, p=fake, b=fake, w=None, wb=0):
+        return lib.soft_topk_rows_forward(s, rows, n_row, k, alpha, p, b, w, wb, None)
+
+    assert fwd(rows=0) == _lib.EINVAL
+    assert fwd(rows=-1) == _lib.EINVAL
+    assert fwd(n_row=0) == _lib.EINVAL
+    assert fwd(k=0.0) == _lib.EINVAL
+    assert fwd(k=100.0) == _lib.EINVAL  # k must stay below n_row
+    assert fwd(alpha=0.0) == _lib.EINVAL
+    assert fwd(alpha=float("nan")) == _lib.EINVAL
+    assert fwd(s=None) == _lib.EINVAL
+    assert fwd(p=None) == _lib.EINVAL
+    assert fwd(b=None) == _lib.EINVAL
+    assert fwd(rows=1 << 31) == _lib.EINVAL  # one work-group per row
+    # rows longer than one work-group solves need the single-vector workspace
+    assert fwd(n_row=10000) == _lib.EWORKSPACE
+
+    def bwd(g=fake, s=fake, rows=4, n_row=100, alpha=0.1, b=fake, out=fake, w=None, wb=0):
+        return lib.soft_topk_rows_backward(g, s, rows, n_row, alpha, b, out, w, wb, None)
+
+    assert bwd(rows=0) == _lib.EINVAL
+    assert bwd(alpha=-1.0) == _lib.EINVAL
+    assert bwd(g=None) == _lib.EINVAL
+    assert bwd(b=None) == _lib.EINVAL
+    assert bwd(out=None) == _lib.EINVAL
+    assert bwd(n_row=10000) == _lib.EWORKSPACE
+
+
+def test_rows_workspace_sizes(lib):
+    for n_row in (1, 64, 100, 4096, 8192):
+        assert lib.soft_topk_rows_workspace_bytes(1000, n_row) == 0  # one work-group per row
+    big = lib.soft_topk_rows_workspace_bytes(3, 8193)
+    assert big >= lib.soft_topk_workspace_bytes(8193, None)
+    assert big >= lib.soft_topk_backward_workspace_bytes(8193)
+    assert lib.soft_topk_rows_workspace_bytes(0, 100) == 0
+
+
 def test_params_validation(lib):
     p = _lib.default_params()
     assert p.samples == 65536 and p.z == 5.0 and p.max_widen == 2 and p.force_path == 0

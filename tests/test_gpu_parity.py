@@ -506,6 +506,28 @@ def test_segments_nonfinite_cotangent_and_foreign_threshold(dev):
 
 
 # --------------------------------------------------------------------------
+# path coverage: the bracket certifies on its first round for every seed
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_certified_first_try_over_100_seeds(dev, name):
+    """100 Philox seeds per workload: every forward takes the bracket route on
+    its first round (no widening, no fallback) and returns the oracle's b.  At
+    z = 5 a side fails with probability below 3e-7, so a failure here points
+    at the sampler or the rank arithmetic, not at chance."""
+    gold = GOLD[name]
+    s_np, k, alpha, w = make_workload(name)
+    s = torch.from_numpy(s_np).to(dev)
+    rng = np.random.default_rng(12345)
+    seeds = [int(x) for x in rng.integers(1, 2 ** 63, 100)]
+    worst = 0.0
+    for seed in seeds:
+        _, b, st = stk.forward(s, k, alpha, params(seed=seed), want_stats=True)
+        assert st["path"] == _lib.PATH_BRACKET and st["rounds"] == 1, (name, seed, st)
+        worst = max(worst, abs(float(b.item()) - gold["b"]) / alpha)
+    assert worst <= 1e-5, (name, worst)
+
+
+# --------------------------------------------------------------------------
 # full-size workloads, as the benchmark runs them
 # --------------------------------------------------------------------------
 def _sha(a):

@@ -1,0 +1,145 @@
+"""GPU parity of the batched rows (soft_topk_rows_forward / _backward) against
+the fp64 CPU oracle applied row by row.
+
+Each row is its own soft top-k problem, so every row is held to the bars of
+the single-vector path: |b - b_ref| <= 1e-5 * alpha, max|p - p_ref| <= 1e-5,
+|sum p - k| <= 1e-3 (oracle mass at the GPU's b), backward rel-L2 <= 1e-4.
+The row lengths cover every work-group shape of the one-work-group path
+(64 threads up to 128 scores, 256 threads up to 4096, 512 up to 8192) with
+ragged ends and the shape boundaries, and the longer rows that run the
+single-vector path row after row.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import differentiable_soft_top_amd as stk  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    return torch.device("cuda:0")
+
+
+def run_rows(dev, s_np, k, alpha, g_np):
+    s = torch.from_numpy(s_np).to(dev)
+    g = torch.from_numpy(g_np).to(dev)
+    p, b = stk.rows_forward(s, k, alpha)
+    grad = stk.rows_backward(g, s, alpha, b)
+    torch.cuda.synchronize()
+    return p.cpu().numpy().astype(np.float64), b.cpu().numpy(), grad.cpu().numpy().astype(np.float64)
+
+
+def check_rows(s_np, k, alpha, g_np, p, b, grad):
+    for r in range(s_np.shape[0]):
+        p_ref, b_ref = O.forward(s_np[r], k, alpha)
+        assert abs(b[r] - b_ref) <= 1e-5 * alpha, (r, b[r], b_ref, (b[r] - b_ref) / alpha)
+        assert np.max(np.abs(p[r] - p_ref)) <= 1e-5, r
+        assert abs(O.mass(s_np[r], float(b[r]), alpha) - k) <= 1e-3, r
+        g_ref = O.backward(g_np[r], s_np[r], alpha, b_ref)
+        ref = np.linalg.norm(g_ref)
+        err = np.linalg.norm(grad[r] - g_ref)
+        if ref > 0:
+            assert err <= 1e-4 * ref, (r, err / ref)
+        else:  # every d_i below the fp32 range: the gradient is 0
+            assert err == 0.0, r
+
+
+CASES = [
+    # rows, n_row, k, alpha
+    (1, 1, 0.5, 0.1),
+    (5, 2, 1.0, 0.2),
+    (4, 3, 1.5, 0.05),
+    (7, 64, 8.0, 0.05),
+    (3, 65, 10.5, 0.1),
+    (17, 128, 16.0, 0.1),
+    (9, 129, 100.0, 0.3),
+    (4, 256, 32.0, 1.0),
+    (5, 257, 3.0, 0.01),
+    (3, 1000, 100.0, 0.1),
+    (6, 1024, 0.25, 0.1),
+    (2, 2048, 64.0, 0.1),
+    (2, 2049, 2040.0, 0.5),
+    (2, 4096, 4095.0, 0.1),
+    (2, 4097, 1.0, 0.1),
+    (2, 8192, 500.0, 0.03),
+]
+
+
+@pytest.mark.parametrize("rows,n_row,k,alpha", CASES)
+def test_rows_match_oracle(dev, rows, n_row, k, alpha):
+    rng = np.random.default_rng(1000 + n_row)
+    s_np = rng.standard_normal((rows, n_row)).astype(np.float32)
+    if n_row >= 64:
+        s_np[0] = np.round(s_np[0] * 8.0) / 8.0  # a row of heavy ties
+    g_np = rng.standard_normal((rows, n_row)).astype(np.float32)
+    p, b, grad = run_rows(dev, s_np, k, alpha, g_np)
+    check_rows(s_np, k, alpha, g_np, p, b, grad)
+
+
+def test_rows_edge_cases(dev):
+    """Equal scores (b = s0 - alpha F^-1(k/n)), a root beyond every score at
+    tiny alpha (the closed form's log branch), k near 0 and near n, a
+    clustered row, and shifted copies of one row (b shifts with them)."""
+    n = 300
+    rng = np.random.default_rng(7)
+    base = rng.standard_normal(n).astype(np.float32)
+    rows = [
+        np.full(n, 0.75, np.float32),
+        base,
+        base + np.float32(10.0),
+        np.concatenate([np.full(n // 2, -1.0, np.float32), np.full(n - n // 2, 1.0, np.float32)]),
+        (base * np.float32(1e-3)).astype(np.float32),
+    ]
+    s_np = np.stack(rows)
+    g_np = rng.standard_normal(s_np.shape).astype(np.float32)
+    for k, alpha in [(150.0, 1e-4), (0.001, 0.1), (n - 0.001, 0.1), (37.25, 0.02)]:
+        p, b, grad = run_rows(dev, s_np, k, alpha, g_np)
+        check_rows(s_np, k, alpha, g_np, p, b, grad)
+        assert abs((b[2] - b[1]) - 10.0) <= 1e-5 * alpha + 2e-6
+
+
+def test_rows_nonfinite_row_gives_nan_and_leaves_others(dev):
+    rng = np.random.default_rng(11)
+    for n_row in (100, 5000):
+        s_np = rng.standard_normal((4, n_row)).astype(np.float32)
+        s_np[1, 7] = np.nan
+        s_np[3, n_row - 1] = np.inf
+        g_np = rng.standard_normal(s_np.shape).astype(np.float32)
+        p, b, grad = run_rows(dev, s_np, 10.0, 0.1, g_np)
+        for r in (1, 3):
+            assert np.isnan(b[r]) and np.all(np.isnan(p[r])), (n_row, r)
+        ok = [0, 2]
+        check_rows(s_np[ok], 10.0, 0.1, g_np[ok], p[ok], b[ok], grad[ok])
+
+
+@pytest.mark.parametrize("rows,n_row", [(3, 8193), (2, 20000)])
+def test_long_rows_take_the_single_vector_path(dev, rows, n_row):
+    rng = np.random.default_rng(n_row)
+    s_np = rng.standard_normal((rows, n_row)).astype(np.float32)
+    s_np[-1, 5] = np.nan
+    g_np = rng.standard_normal((rows, n_row)).astype(np.float32)
+    k, alpha = 200.0, 0.05
+    p, b, grad = run_rows(dev, s_np, k, alpha, g_np)
+    assert np.isnan(b[-1]) and np.all(np.isnan(p[-1]))
+    check_rows(s_np[:-1], k, alpha, g_np[:-1], p[:-1], b[:-1], grad[:-1])
+
+
+def test_rows_equal_single_vector_calls(dev):
+    """A batch of rows gives each row what the single-vector operator gives
+    it (to the parity bar: the two solve with different sorts and scans)."""
+    rng = np.random.default_rng(3)
+    s_np = rng.standard_normal((6, 3000)).astype(np.float32)
+    k, alpha = 30.0, 0.05
+    s = torch.from_numpy(s_np).to(dev)
+    p, b = stk.rows_forward(s, k, alpha)
+    for r in range(6):
+        p1, b1 = stk.forward(s[r].contiguous(), k, alpha)
+        assert abs(float(b1.item()) - float(b[r].item())) <= 1e-5 * alpha
+        assert float(torch.max(torch.abs(p1 - p[r])).item()) <= 1e-5
