@@ -203,28 +203,23 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_reduce_kernel(VjpArgs a)
             float4 vs[kB], vg[kB];
             load_q<kB>(s4, t, vs);
             load_q<kB>(g4, t, vg);
-            // fp32 within a float4, fp64 across them
+            // fp64 sums of fp32 d and exact g d products: where one d
+            // dominates, g_i - G/D is small and needs G and D to far better
+            // than fp32 rounding of the dominant term
 #pragma unroll
             for (int u = 0; u < kB; ++u) {
-                float d, dsum = 0.f, gsum = 0.f;
-                d = dens(vs[u].x, b, c); dsum += d; gsum += vg[u].x * d;
-                d = dens(vs[u].y, b, c); dsum += d; gsum += vg[u].y * d;
-                d = dens(vs[u].z, b, c); dsum += d; gsum += vg[u].z * d;
-                d = dens(vs[u].w, b, c); dsum += d; gsum += vg[u].w * d;
-                D += (double)dsum;
-                G_ += (double)gsum;
+                acc_dg(dens(vs[u].x, b, c), vg[u].x, D, G_);
+                acc_dg(dens(vs[u].y, b, c), vg[u].y, D, G_);
+                acc_dg(dens(vs[u].z, b, c), vg[u].z, D, G_);
+                acc_dg(dens(vs[u].w, b, c), vg[u].w, D, G_);
             }
         }
         for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads) {
-            const float d = dens(a.s[i], b, c);
-            D += (double)d;
-            G_ += (double)(a.g[i] * d);
+            acc_dg(dens(a.s[i], b, c), a.g[i], D, G_);
         }
     } else {
         for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + tid; i < a.n; i += G * kStreamThreads) {
-            const float d = dens(a.s[i], b, c);
-            D += (double)d;
-            G_ += (double)(a.g[i] * d);
+            acc_dg(dens(a.s[i], b, c), a.g[i], D, G_);
         }
     }
     block_sum_to(D, red[0], &a.partials[2 * blockIdx.x]);
@@ -250,7 +245,7 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_kernel(VjpArgs a, in
     __syncthreads();
     // every d_i underflowed (alpha tiny next to the gaps around b): the
     // gradient is then 0 everywhere and the ratio is irrelevant
-    const float ratio = tot[0] > 0.0 ? (float)(tot[1] / tot[0]) : 0.0f;
+    const Ratio2 ratio = split_ratio(tot[0] > 0.0 ? tot[1] / tot[0] : 0.0);
     const float inv_alpha = (float)(1.0 / a.alpha);
     const double b = *a.b;
     const double c = a.log2e_over_alpha;
@@ -268,18 +263,18 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_kernel(VjpArgs a, in
 #pragma unroll
             for (int u = 0; u < kB; ++u) {
                 float4 o;
-                o.x = dens(vs[u].x, b, c) * inv_alpha * (vg[u].x - ratio);
-                o.y = dens(vs[u].y, b, c) * inv_alpha * (vg[u].y - ratio);
-                o.z = dens(vs[u].z, b, c) * inv_alpha * (vg[u].z - ratio);
-                o.w = dens(vs[u].w, b, c) * inv_alpha * (vg[u].w - ratio);
+                o.x = dens(vs[u].x, b, c) * inv_alpha * minus_ratio(vg[u].x, ratio);
+                o.y = dens(vs[u].y, b, c) * inv_alpha * minus_ratio(vg[u].y, ratio);
+                o.z = dens(vs[u].z, b, c) * inv_alpha * minus_ratio(vg[u].z, ratio);
+                o.w = dens(vs[u].w, b, c) * inv_alpha * minus_ratio(vg[u].w, ratio);
                 store4<kNT>(&o4[t * (kB * kStreamThreads) + u * kStreamThreads + tid], o);
             }
         }
         for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads)
-            a.grad[i] = dens(a.s[i], b, c) * inv_alpha * (a.g[i] - ratio);
+            a.grad[i] = dens(a.s[i], b, c) * inv_alpha * minus_ratio(a.g[i], ratio);
     } else {
         for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + tid; i < a.n; i += G * kStreamThreads)
-            a.grad[i] = dens(a.s[i], b, c) * inv_alpha * (a.g[i] - ratio);
+            a.grad[i] = dens(a.s[i], b, c) * inv_alpha * minus_ratio(a.g[i], ratio);
     }
 }
 
@@ -590,23 +585,18 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_reduce_seg_kernel(VjpArgs 
                 block_out(gblk[wave], rec, a.gl + (t * kSegPerTile + wave) * kSegCap);
                 __builtin_amdgcn_wave_barrier();
             }
-            // fp32 within a float4, fp64 across them (as the score-reading kernel)
+            // the score-reading kernel's sums
 #pragma unroll
             for (int u = 0; u < kB; ++u) {
-                float dsum = 0.f, gsum = 0.f;
-                dsum += d[4 * u + 0]; gsum += vg[u].x * d[4 * u + 0];
-                dsum += d[4 * u + 1]; gsum += vg[u].y * d[4 * u + 1];
-                dsum += d[4 * u + 2]; gsum += vg[u].z * d[4 * u + 2];
-                dsum += d[4 * u + 3]; gsum += vg[u].w * d[4 * u + 3];
-                D += (double)dsum;
-                G_ += (double)gsum;
+                acc_dg(d[4 * u + 0], vg[u].x, D, G_);
+                acc_dg(d[4 * u + 1], vg[u].y, D, G_);
+                acc_dg(d[4 * u + 2], vg[u].z, D, G_);
+                acc_dg(d[4 * u + 3], vg[u].w, D, G_);
             }
         }
     }
     for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads) {
-        const float dd = dens(a.s[i], b, c);
-        D += (double)dd;
-        G_ += (double)(a.g[i] * dd);
+        acc_dg(dens(a.s[i], b, c), a.g[i], D, G_);
     }
     block_sum_to(D, red[0], &a.partials[2 * blockIdx.x]);
     __syncthreads();
@@ -633,7 +623,7 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_seg_kernel(VjpArgs a
     __syncthreads();
     block_sum_to(G_, red[1], &tot[1]);
     __syncthreads();
-    const float ratio = tot[0] > 0.0 ? (float)(tot[1] / tot[0]) : 0.0f;
+    const Ratio2 ratio = split_ratio(tot[0] > 0.0 ? tot[1] / tot[0] : 0.0);
     const float inv_alpha = (float)(1.0 / a.alpha);
     const double b = *a.b;
     const double c = a.log2e_over_alpha;
@@ -662,10 +652,10 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_seg_kernel(VjpArgs a
                 load_q<kB>(g4, t, vg);
 #pragma unroll
                 for (int u = 0; u < kB; ++u) {
-                    o[4 * u + 0] = dens(vs[u].x, b, c) * inv_alpha * (vg[u].x - ratio);
-                    o[4 * u + 1] = dens(vs[u].y, b, c) * inv_alpha * (vg[u].y - ratio);
-                    o[4 * u + 2] = dens(vs[u].z, b, c) * inv_alpha * (vg[u].z - ratio);
-                    o[4 * u + 3] = dens(vs[u].w, b, c) * inv_alpha * (vg[u].w - ratio);
+                    o[4 * u + 0] = dens(vs[u].x, b, c) * inv_alpha * minus_ratio(vg[u].x, ratio);
+                    o[4 * u + 1] = dens(vs[u].y, b, c) * inv_alpha * minus_ratio(vg[u].y, ratio);
+                    o[4 * u + 2] = dens(vs[u].z, b, c) * inv_alpha * minus_ratio(vg[u].z, ratio);
+                    o[4 * u + 3] = dens(vs[u].w, b, c) * inv_alpha * minus_ratio(vg[u].w, ratio);
                 }
             } else {
                 const int64_t seg = t * kSegPerTile + wave;
@@ -684,7 +674,7 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_seg_kernel(VjpArgs a
                     const uint64_t lm = ((uint64_t)hi << 32) | lo;
                     const bool li = (lm >> lane) & 1ull;
                     const uint32_t p = pre + rank_in_mask(lm);
-                    o[i] = li ? dblk[wave][p] * inv_alpha * (gblk[wave][p] - ratio) : 0.0f;
+                    o[i] = li ? dblk[wave][p] * inv_alpha * minus_ratio(gblk[wave][p], ratio) : 0.0f;
                     pre += (uint32_t)__popcll(lm);
                 }
             }
@@ -695,7 +685,7 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_seg_kernel(VjpArgs a
         }
     }
     for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads)
-        a.grad[i] = dens(a.s[i], b, c) * inv_alpha * (a.g[i] - ratio);
+        a.grad[i] = dens(a.s[i], b, c) * inv_alpha * minus_ratio(a.g[i], ratio);
 }
 
 hipError_t launch_emit(const EmitArgs& a, bool fold_mass, hipStream_t stream)

@@ -138,6 +138,37 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
 }
 
 // ---------------------------------------------------------------------------
+// The VJP's g - G/D with the fp64 ratio carried as an unevaluated float pair
+// hi + lo.  Where g nearly cancels the ratio (one density dominating D, a
+// saturated row) g - hi is exact (the operands are within a factor of two),
+// so the small difference keeps its relative accuracy; a plain fp32 ratio
+// would leave an error of half its ulp there.  A non-finite ratio (a
+// non-finite g somewhere) passes through hi.
+// ---------------------------------------------------------------------------
+struct Ratio2 {
+    float hi, lo;
+};
+
+__device__ __forceinline__ Ratio2 split_ratio(double r)
+{
+    Ratio2 q;
+    q.hi = (float)r;
+    q.lo = isfinite(q.hi) ? (float)(r - (double)q.hi) : 0.0f;
+    return q;
+}
+
+__device__ __forceinline__ float minus_ratio(float g, Ratio2 q) { return (g - q.hi) - q.lo; }
+
+// D += d, G += g d in fp64 (the product of two floats is exact there).  The
+// ratio G/D is then off by fp64 rounding only, and the fp32 error of each d
+// moves it by a relative fp32 ulp of (g_i - G/D) d_i / D, never of G/D.
+__device__ __forceinline__ void acc_dg(float d, float g, double& D, double& G)
+{
+    D += (double)d;
+    G = fma((double)g, (double)d, G);
+}
+
+// ---------------------------------------------------------------------------
 // Wave-64 reductions (every lane receives the result; butterfly order is
 // fixed, so results are bitwise reproducible).
 // ---------------------------------------------------------------------------

@@ -203,7 +203,7 @@ def test_tiny_inputs(dev, tag, s_np, k, alpha):
 
 
 @pytest.mark.parametrize("case", ["equal", "sorted", "reversed", "k_tiny", "k_near_n", "alpha_huge",
-                                  "alpha_tiny", "negative", "bimodal", "k_half"])
+                                  "alpha_tiny", "negative", "bimodal", "k_half", "saturated"])
 def test_structured_inputs(dev, case):
     rng = np.random.default_rng(99)
     n = 50_021
@@ -232,6 +232,12 @@ def test_structured_inputs(dev, case):
     elif case == "negative":
         s = (rng.standard_normal(n) - 50.0).astype(np.float32)
         k = 2000.0
+    elif case == "saturated":
+        # b below every score and one score well apart from the rest: its
+        # density dominates D, so its gradient g_i - G/D nearly cancels
+        s = rng.standard_normal(n).astype(np.float32)
+        s[np.argmin(s)] -= 1.0
+        k = n - 0.5
     elif case == "bimodal":
         s = np.concatenate([rng.normal(-3, 0.1, n // 2), rng.normal(3, 0.1, n - n // 2)]).astype(np.float32)
         s = s[rng.permutation(n)]
