@@ -29,6 +29,9 @@ kernel source, else null.  That file is written by
 (--profile-run: a few steps of the workload, then a plain device copy of
 COPY_BYTES bytes whose counter readings calibrate the two counters).
 
+"rows" times the batched-row operator (one soft top-k per row) forward +
+backward on two row workloads, warm and cold, the same way.
+
 "cpu_baseline" times the fp64 CPU oracle (forward + backward) on a bounded
 sample (the first 2^25 scores, k scaled) and scales by n log2 n.
 """
@@ -103,6 +106,41 @@ class Runner:
                                      v(self.b.data_ptr()), v(self.grad.data_ptr()), v(self.ws.data_ptr()),
                                      self.ws_bytes, v(self.bws.data_ptr()), self.bws_bytes, self.stream)
         self._lib.check(rc, "soft_topk_backward")
+
+
+class RowsRunner:
+    """Batched rows: preallocated buffers, soft_topk_rows_forward then _backward."""
+
+    # algorithmic bytes per score: read s, write p; read s and g, write grad
+    BYTES_PER_SCORE = 20
+
+    def __init__(self, torch, lib, s2d, g2d, k, alpha):
+        self.lib = lib
+        self.k, self.alpha = float(k), float(alpha)
+        self.batches = [(s2d, g2d), (torch.flip(s2d, [1]).contiguous(), torch.flip(g2d, [1]).contiguous())]
+        self.turn = 0
+        self.rows, self.n_row = s2d.shape
+        self.p = torch.empty_like(s2d)
+        self.grad = torch.empty_like(s2d)
+        self.b = torch.empty(self.rows, dtype=torch.float64, device=s2d.device)
+        self.ws_bytes = lib.soft_topk_rows_workspace_bytes(self.rows, self.n_row)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=s2d.device)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(s2d.device).cuda_stream)
+        from differentiable_soft_top_amd import _lib
+        self._lib = _lib
+
+    def step(self):
+        L, v = self.lib, ctypes.c_void_p
+        s, g = self.batches[self.turn]
+        self.turn ^= 1
+        rc = L.soft_topk_rows_forward(v(s.data_ptr()), self.rows, self.n_row, self.k, self.alpha,
+                                      v(self.p.data_ptr()), v(self.b.data_ptr()), v(self.ws.data_ptr()),
+                                      self.ws_bytes, self.stream)
+        self._lib.check(rc, "soft_topk_rows_forward")
+        rc = L.soft_topk_rows_backward(v(g.data_ptr()), v(s.data_ptr()), self.rows, self.n_row, self.alpha,
+                                       v(self.b.data_ptr()), v(self.grad.data_ptr()), v(self.ws.data_ptr()),
+                                       self.ws_bytes, self.stream)
+        self._lib.check(rc, "soft_topk_rows_backward")
 
 
 def time_steps(torch, runner, steps, flush=None):
@@ -243,6 +281,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--sizes", default="c2,c3", help="extra workloads timed (comma list, '' for none)")
+    ap.add_argument("--rows", default="r1,r2", help="batched-row workloads timed (comma list, '' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="counter-collection run: a few steps of --workload, then the calibration copy")
@@ -326,6 +365,28 @@ def main():
         del erun
         torch.cuda.empty_cache()
 
+    rows_out = {}
+    from differentiable_soft_top_amd.workloads import make_row_workload
+    for rname in [x for x in args.rows.split(",") if x]:
+        s2_np, rk, ralpha, rw = make_row_workload(rname)
+        g2_np = draw_grad(s2_np.size, rw.seed).reshape(s2_np.shape)
+        rrun = RowsRunner(torch, lib, torch.from_numpy(s2_np).to(dev), torch.from_numpy(g2_np).to(dev), rk, ralpha)
+        for _ in range(3):
+            rrun.step()
+        warm = time_steps(torch, rrun, 50)
+        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        cold = time_steps(torch, rrun, 20, flush=flush)
+        del flush
+        med = float(np.median(warm))
+        rows_out[rname] = {
+            "workload": rw.description, "rows": rw.rows, "n_row": rw.n_row,
+            "median_ms": med, "p10_ms": float(np.percentile(warm, 10)), "p90_ms": float(np.percentile(warm, 90)),
+            "median_ms_cold": float(np.median(cold)),
+            "algorithmic_GBps": RowsRunner.BYTES_PER_SCORE * s2_np.size / (med / 1e3) / 1e9,
+        }
+        del rrun
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(s_np, g_np, k, alpha)
@@ -365,6 +426,7 @@ def main():
             "launches": dom_launches,
         },
         "sizes": sizes,
+        "rows": rows_out,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

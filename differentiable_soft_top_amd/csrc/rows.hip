@@ -7,22 +7,26 @@
 // row) gets b_r with sum_i F((s_ri - b_r)/alpha) = k, p_ri = F((s_ri -
 // b_r)/alpha), and the VJP of each row as in the single-vector path.
 //
-// gfx950 design: one work-group per row, the row held in registers.
+// gfx950 design: one work-group per row (one wave up to 1024 scores), the
+// row held in registers.
 //   forward -- the row is loaded coalesced (R scores per thread), copied as
 //     order-preserving keys and sorted by a register bitonic network (the
 //     sorted keys end in blocked order: thread t holds positions t*R ..
-//     t*R+R-1).  Each thread folds its run forward and backward into
-//     anchored sums; one work-group scan of those (the full-sort solver of
-//     section 2.2: stable prefix/suffix sums of shifted exponentials) gives
-//     every breakpoint's mass; the last breakpoint with mass >= k is found
+//     t*R+R-1).  The full-sort solver of section 2.2 then needs, at every
+//     breakpoint x_j, the left sum A_j = sum_{i<=j} e^{(x_i-x_j)/alpha} and
+//     the right sum sum_{i>j} e^{(x_j-x_i)/alpha}.  When the row spans at
+//     most kRowSpan in log2 units ((x_max - x_min) log2(e)/alpha), every
+//     E_i = e^{(x_i-x_r)/alpha} about the row's midpoint x_r and its
+//     reciprocal are normal fp64 numbers, so both sums are plain prefix and
+//     suffix sums of E and 1/E scaled by 1/E_j and E_j: one exponential per
+//     score, fp64 additions in the scans.  Each E is an fp32 exp2 of the
+//     fractional exponent times an exact power of two (relative error a few
+//     fp32 ulps, which moves b by about 1e-7 alpha).  Wider rows take the
+//     anchored sums of the single-vector segment solve (an exponential per
+//     combination, any range).  The last breakpoint with mass >= k is found
 //     by a block max and its owner applies the closed-form root (fp64).
-//     p is then emitted from the registers still holding the row in load
-//     order, in fp64 as in the single-vector emission.
-//   backward -- d = e^{-|s-b|/alpha}/2 in fp32 (s - b in fp64), D and G
-//     reduced in fp64 over the row, grad = (d/alpha)(g - G/D).
-// No host synchronisation: a row holding a NaN or an infinite score gets
-// b = NaN and p = NaN (the single-vector path reports ENONFINITE instead,
-// which would need a read-back per call).
+//     p = F((s - b)/alpha) is then emitted from the registers still holding
+//     the row in load order: s - b in fp64, the exponential in fp32.
 #include "stk_common.hpp"
 #include "stk_layout.hpp"
 #include "stk_prof.hpp"
@@ -32,12 +36,70 @@ namespace stk {
 
 namespace {
 
-// p = F((s - b)/alpha) in fp64 (the single-vector emission's arithmetic)
+// Largest row span, in log2 units, that the reference-point sums cover:
+// about the midpoint every exponent lies in [-900, 900], so E and 1/E are
+// normal fp64 numbers and row sums of them stay far from overflow.
+constexpr double kRowSpan = 1800.0;
+
+// p = F((s - b)/alpha): s - b in fp64, the exponential in fp32
 __device__ __forceinline__ float row_p(float v, double b, double c)
 {
     const double x = (double)v - b;
-    const double e = exp2_nonpos(-fabs(x) * c);
-    return (float)(x <= 0.0 ? 0.5 * e : 1.0 - 0.5 * e);
+    const float e = __builtin_amdgcn_exp2f((float)(-fabs(x) * c));
+    return x <= 0.0 ? 0.5f * e : 1.0f - 0.5f * e;
+}
+
+// E = 2^((x - xr) c) and 1/E: fp32 exp2 of the fractional exponent (in
+// [-1/2, 1/2]) scaled by the exact power of two
+__device__ __forceinline__ void ref_exp(float x, double xr, double c, double& e, double& ei)
+{
+    const double y = ((double)x - xr) * c;
+    const double j = __builtin_rint(y);
+    const float f = (float)(y - j);
+    const int ij = (int)j;
+    e = ldexp((double)__builtin_amdgcn_exp2f(f), ij);
+    ei = ldexp((double)__builtin_amdgcn_exp2f(-f), -ij);
+}
+
+// Block scan of this thread's run sums: the sum of `ps` over earlier
+// threads and of `ss` over later ones (exclusive both ways, additions only).
+template <int kW>
+__device__ __forceinline__ void scan_pair(double ps, double ss, double* wp, double* ws, double& pre, double& suf)
+{
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    double p = ps, q = ss;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const double op = __shfl_up(p, off, kWave);
+        const double oq = __shfl_down(q, off, kWave);
+        if (lane >= off)
+            p += op;
+        if (lane + off < kWave)
+            q += oq;
+    }
+    double pe = __shfl_up(p, 1, kWave);
+    double se = __shfl_down(q, 1, kWave);
+    if (lane == 0)
+        pe = 0.0;
+    if (lane == kWave - 1)
+        se = 0.0;
+    if (kW > 1) {
+        if (lane == kWave - 1)
+            wp[wave] = p;
+        if (lane == 0)
+            ws[wave] = q;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kW; ++w) {
+            if (w < wave)
+                pe += wp[w];
+            if (w > wave)
+                se += ws[w];
+        }
+    }
+    pre = pe;
+    suf = se;
 }
 
 // d = e^{-|s-b|/alpha}/2 in fp32, s - b in fp64 (the single-vector VJP's)
@@ -49,57 +111,99 @@ __device__ __forceinline__ float row_d(float v, double b, double c)
 
 }  // namespace
 
+// The root of one sorted row (blocked order, run e0 .. e0 + m - 1 in x) by
+// reference-point sums; xs is the first point of the next run (if any).
 template <int kT, int R>
-__global__ __launch_bounds__(kT) void rows_forward_kernel(RowsArgs a)
+__device__ __forceinline__ void solve_ref(const float (&x)[R], int e0, int m, float xs, float xmin, float xmax,
+                                          const RowsArgs& a, double* wp, double* ws, int* imax, double* bsh)
 {
-    static_assert(kT * R <= kRowMax && (kT % kWave) == 0, "row shape");
     constexpr int kW = kT / kWave;
-    __shared__ uint32_t buf0[kT * R];
-    __shared__ uint32_t buf1[kT * R];
-    __shared__ WaveTot wt[kW];
-    __shared__ int imax[kW];
-    __shared__ double bsh;
-    const int tid = threadIdx.x;
+    const int n = a.n_row;
+    const double c = a.log2e_over_alpha;
+    const double xr = 0.5 * ((double)xmin + (double)xmax);
+    double E[R], Ei[R], sv[R];
+    double ps = 0.0, ss = 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        E[r] = 0.0;
+        Ei[r] = 0.0;
+        if (r < m)
+            ref_exp(x[r], xr, c, E[r], Ei[r]);
+        ps += E[r];
+    }
+    // sv[r]: this run's 1/E after position r
+#pragma unroll
+    for (int r = R - 1; r >= 0; --r) {
+        sv[r] = ss;
+        ss += Ei[r];
+    }
+    double pre, suf;
+    scan_pair<kW>(ps, ss, wp, ws, pre, suf);
+    double En = 0.0, Ein = 0.0;  // the next run's first point
+    if (e0 + R < n)
+        ref_exp(xs, xr, c, En, Ein);
+
+    // mass at x_j: A_j / 2 + (points after j) - (right sum) / 2, with
+    // A_j = P_{<=j} / E_j and right sum E_j S_{>j}
+    int jc = -1;
+    Anch lo = empty_pre(), hi = empty_suf();
+    double P = pre;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r < m) {
+            P += E[r];
+            const double S = suf + sv[r];
+            const double A = P * Ei[r];
+            if (0.5 * A + (double)(n - 1 - (e0 + r)) - 0.5 * (E[r] * S) >= a.k) {
+                jc = e0 + r;
+                lo = node(x[r], A);
+                // the next point's right sum (anchored at it): S E_{j+1}
+                if (r + 1 < m)
+                    hi = node(x[r + 1], S * E[r + 1]);
+                else if (e0 + R < n)
+                    hi = node(xs, S * En);
+                else
+                    hi = empty_suf();
+            }
+        }
+    }
     const int lane = lane_id();
-    const int wave = tid / kWave;
+    const int wave = threadIdx.x / kWave;
+    int jmax = jc;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const int o = __shfl_xor(jmax, off, kWave);
+        jmax = o > jmax ? o : jmax;
+    }
+    if (kW > 1) {
+        if (lane == 0)
+            imax[wave] = jmax;
+        __syncthreads();
+        jmax = imax[0];
+        for (int w = 1; w < kW; ++w)
+            jmax = imax[w] > jmax ? imax[w] : jmax;
+    }
+    if (jmax >= 0) {
+        if (jc == jmax)
+            *bsh = gap_root(lo, hi, (double)(n - 1 - jmax), a.k, a.alpha, c);
+    } else if (threadIdx.x == 0) {
+        // the root lies before the first point: every point on the right
+        *bsh = gap_root(empty_pre(), node(x[0], (suf + ss) * E[0]), (double)n, a.k, a.alpha, c);
+    }
+}
+
+// The same root by anchored sums (any span): each combination rescales by
+// an exponential of the anchor difference.
+template <int kT, int R>
+__device__ __forceinline__ void solve_anchored(const float (&x)[R], int e0, int m, const RowsArgs& a, WaveTot* wt,
+                                               int* imax, double* bsh)
+{
+    constexpr int kW = kT / kWave;
     const int n = a.n_row;
     const double c = a.log2e_over_alpha;
     const double k = a.k;
-    const int64_t row = blockIdx.x;
-    const float* s = a.s + row * (int64_t)n;
-
-    // the row in load order (coalesced), and as keys
-    float vo[R];
-    uint32_t key[R];
-    bool bad = false;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int i = r * kT + tid;
-        vo[r] = i < n ? s[i] : 0.0f;
-        bad = bad || (i < n && !isfinite(vo[r]));
-        key[r] = i < n ? float_to_key(vo[r]) : 0xFFFFFFFFu;
-    }
-    if (__syncthreads_or(bad)) {
-        float* p = a.p + row * (int64_t)n;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int i = r * kT + tid;
-            if (i < n)
-                p[i] = NAN;
-        }
-        if (tid == 0)
-            a.b[row] = NAN;
-        return;
-    }
-    block_bitonic_regs<kT, R>(key, buf0, buf1);
-
-    // this thread's sorted run: positions e0 .. e0 + m - 1
-    const int e0 = tid * R;
-    const int m = n - e0 < 0 ? 0 : (n - e0 < R ? n - e0 : R);
-    float x[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        x[r] = key_to_float(key[r]);
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
     // backward chain within the run (suffix anchored at each element), then
     // the forward fold
     double bv[R];
@@ -136,27 +240,96 @@ __global__ __launch_bounds__(kT) void rows_forward_kernel(RowsArgs a)
             }
         }
     }
-    // the block's last such breakpoint; its owner (whose own last one it
-    // is) applies the closed form in the gap after it
     int jmax = jc;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const int o = __shfl_xor(jmax, off, kWave);
         jmax = o > jmax ? o : jmax;
     }
-    if (lane == 0)
-        imax[wave] = jmax;
-    __syncthreads();
-    int jstar = imax[0];
-    for (int w = 1; w < kW; ++w)
-        jstar = imax[w] > jstar ? imax[w] : jstar;
-    if (jstar >= 0) {
-        if (jc == jstar)
-            bsh = gap_root(jlo, jhi, (double)(n - 1 - jstar), k, a.alpha, c);
-    } else if (tid == 0) {
+    if (kW > 1) {
+        if (lane == 0)
+            imax[wave] = jmax;
+        __syncthreads();
+        jmax = imax[0];
+        for (int w = 1; w < kW; ++w)
+            jmax = imax[w] > jmax ? imax[w] : jmax;
+    }
+    if (jmax >= 0) {
+        if (jc == jmax)
+            *bsh = gap_root(jlo, jhi, (double)(n - 1 - jmax), k, a.alpha, c);
+    } else if (threadIdx.x == 0) {
         // the root lies before the first point
         const Anch B0 = bwd(node(x[0], bv[0]), ex_suf, c);
-        bsh = gap_root(empty_pre(), B0, (double)n, k, a.alpha, c);
+        *bsh = gap_root(empty_pre(), B0, (double)n, k, a.alpha, c);
+    }
+}
+
+template <int kT, int R>
+__global__ __launch_bounds__(kT) void rows_forward_kernel(RowsArgs a)
+{
+    static_assert(kT * R <= kRowMax && (kT % kWave) == 0, "row shape");
+    constexpr int kW = kT / kWave;
+    __shared__ uint32_t buf0[kT * R];
+    __shared__ uint32_t buf1[kT * R];
+    __shared__ WaveTot wt[kW];
+    __shared__ double wp[kW], ws[kW];
+    __shared__ int imax[kW];
+    __shared__ float first[kT];
+    __shared__ float ends[2];
+    __shared__ double bsh;
+    const int tid = threadIdx.x;
+    const int n = a.n_row;
+    const double c = a.log2e_over_alpha;
+    const int64_t row = blockIdx.x;
+    const float* s = a.s + row * (int64_t)n;
+
+    // the row in load order (coalesced), and as keys
+    float vo[R];
+    uint32_t key[R];
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = r * kT + tid;
+        vo[r] = i < n ? s[i] : 0.0f;
+        bad = bad || (i < n && !isfinite(vo[r]));
+        key[r] = i < n ? float_to_key(vo[r]) : 0xFFFFFFFFu;
+    }
+    if (__syncthreads_or(bad)) {
+        float* p = a.p + row * (int64_t)n;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = r * kT + tid;
+            if (i < n)
+                p[i] = NAN;
+        }
+        if (tid == 0)
+            a.b[row] = NAN;
+        return;
+    }
+    block_bitonic_regs<kT, R>(key, buf0, buf1);
+
+    // this thread's sorted run: positions e0 .. e0 + m - 1
+    const int e0 = tid * R;
+    const int m = n - e0 < 0 ? 0 : (n - e0 < R ? n - e0 : R);
+    float x[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        x[r] = key_to_float(key[r]);
+    // the row's ends and each run's first point
+    first[tid] = x[0];
+    if (tid == 0)
+        ends[0] = x[0];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (e0 + r == n - 1)
+            ends[1] = x[r];
+    __syncthreads();
+    const float xmin = ends[0], xmax = ends[1];
+    if (((double)xmax - (double)xmin) * c <= kRowSpan) {
+        const float xs = e0 + R < n ? first[tid + 1] : INFINITY;
+        solve_ref<kT, R>(x, e0, m, xs, xmin, xmax, a, wp, ws, imax, &bsh);
+    } else {
+        solve_anchored<kT, R>(x, e0, m, a, wt, imax, &bsh);
     }
     __syncthreads();
     const double b = bsh;
@@ -195,10 +368,8 @@ __global__ __launch_bounds__(kT) void rows_backward_kernel(RowsArgs a)
         dv[r] = in ? row_d(s[i], b, c) : 0.0f;
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        D += (double)dv[r];
-        G += (double)(gv[r] * dv[r]);
-    }
+    for (int r = 0; r < R; ++r)
+        acc_dg(dv[r], gv[r], D, G);
     D = wave_sum(D);
     G = wave_sum(G);
     if (lane == 0) {
@@ -212,14 +383,377 @@ __global__ __launch_bounds__(kT) void rows_backward_kernel(RowsArgs a)
         D += red[0][w];
         G += red[1][w];
     }
-    const float ratio = D > 0.0 ? (float)(G / D) : 0.0f;
+    const Ratio2 ratio = split_ratio(D > 0.0 ? G / D : 0.0);
     const float inv_alpha = (float)(1.0 / a.alpha);
     float* out = a.grad + row * (int64_t)n;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int i = r * kT + tid;
         if (i < n)
-            out[i] = dv[r] * inv_alpha * (gv[r] - ratio);
+            out[i] = dv[r] * inv_alpha * minus_ratio(gv[r], ratio);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Rows of up to 1024 scores: G lanes per row (G a power of two up to 64),
+// R scores per lane, 64 / G rows per wave.  Everything stays inside the
+// lane group -- the sort's exchanges, the scans, the reductions -- so a
+// wave needs no LDS and no barrier, and the work done once per row (the
+// closed-form root, the scans' shuffle steps, the reductions) serves the
+// wave's 64 / G rows in the same instructions.
+// ---------------------------------------------------------------------------
+constexpr int kGroupThreads = 256;
+
+// lane mask of this lane's group
+template <int G>
+__device__ __forceinline__ uint64_t group_mask()
+{
+    if (G == kWave)
+        return ~0ull;
+    return ((1ull << G) - 1ull) << (lane_id() & ~(G - 1));
+}
+
+template <int G>
+__device__ __forceinline__ bool group_any(bool v)
+{
+    return (__ballot(v) & group_mask<G>()) != 0ull;
+}
+
+template <int G>
+__device__ __forceinline__ int group_max(int v)
+{
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) {
+        const int o = __shfl_xor(v, off, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ double group_sum(double v)
+{
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Ascending sort of the group's G * R keys (blocked order: group lane gl
+// ends with positions gl * R .. gl * R + R - 1).  Bitonic network in its
+// direction-free form: each merge of two sorted halves first compares every
+// element of the lower half with its mirror image in the upper half, then
+// runs ascending half-cleaners; every compare-exchange puts the minimum at
+// the lower position.
+template <int G, int R>
+__device__ __forceinline__ void group_sort(uint32_t (&v)[R], int gl)
+{
+    constexpr int N = G * R;
+#pragma unroll
+    for (int k = 2; k <= N; k <<= 1) {
+        if (k <= R) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int q = r ^ (k - 1);
+                if ((r & (k >> 1)) == 0) {
+                    const uint32_t lo = v[r] < v[q] ? v[r] : v[q];
+                    const uint32_t hi = v[r] < v[q] ? v[q] : v[r];
+                    v[r] = lo;
+                    v[q] = hi;
+                }
+            }
+        } else {
+            // mirror partner: lane gl ^ (k / R - 1), register R - 1 - r
+            const bool lower = (gl & ((k >> 1) / R)) == 0;
+            uint32_t o[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                o[r] = (uint32_t)__shfl_xor((int)v[R - 1 - r], k / R - 1, kWave);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                v[r] = lower ? (v[r] < o[r] ? v[r] : o[r]) : (v[r] > o[r] ? v[r] : o[r]);
+        }
+#pragma unroll
+        for (int j = k >> 2; j > 0; j >>= 1) {
+            if (j < R) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if ((r & j) == 0) {
+                        const uint32_t lo = v[r] < v[r | j] ? v[r] : v[r | j];
+                        const uint32_t hi = v[r] < v[r | j] ? v[r | j] : v[r];
+                        v[r] = lo;
+                        v[r | j] = hi;
+                    }
+                }
+            } else {
+                const bool lower = (gl & (j / R)) == 0;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t o = (uint32_t)__shfl_xor((int)v[r], j / R, kWave);
+                    v[r] = lower ? (v[r] < o ? v[r] : o) : (v[r] > o ? v[r] : o);
+                }
+            }
+        }
+    }
+}
+
+// The gap of the group's sorted row where the mass crosses k, by
+// reference-point sums (span <= kRowSpan): on the lane that owns the gap's
+// left end (group lane 0 when the root lies before the first point), lo and
+// hi are the sums anchored at the gap's ends and C the points after it.
+struct RowGap {
+    Anch lo, hi;
+    double C;
+    int jstar;  // the gap's left end; -1: before the first point
+};
+
+template <int G, int R>
+__device__ __forceinline__ RowGap group_gap_ref(const float (&x)[R], int gl, int e0, int m, float xs, float xmin,
+                                                float xmax, int n, double k, double c)
+{
+    const double xr = 0.5 * ((double)xmin + (double)xmax);
+    // backward over the run: sv[r] = sum of 1/E after position r (kept), and
+    // the run's sums of E and 1/E; E and 1/E are recomputed in the forward
+    // pass below rather than kept (registers decide occupancy here)
+    double sv[R];
+    double ps = 0.0, ss = 0.0;
+#pragma unroll
+    for (int r = R - 1; r >= 0; --r) {
+        sv[r] = ss;
+        if (r < m) {
+            double e, ei;
+            ref_exp(x[r], xr, c, e, ei);
+            ps += e;
+            ss += ei;
+        }
+    }
+    // exclusive scans inside the group: E before this run, 1/E after it
+    double p = ps, q = ss;
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) {
+        const double op = __shfl_up(p, off, kWave);
+        const double oq = __shfl_down(q, off, kWave);
+        if (gl >= off)
+            p += op;
+        if (gl + off < G)
+            q += oq;
+    }
+    double pre = __shfl_up(p, 1, kWave);
+    double suf = __shfl_down(q, 1, kWave);
+    if (gl == 0)
+        pre = 0.0;
+    if (gl == G - 1)
+        suf = 0.0;
+
+    // mass at x_j: A_j / 2 + (points after j) - (right sum) / 2, with
+    // A_j = P_{<=j} / E_j and right sum E_j S_{>j}; the gap's right end
+    // carries S_{>j} E_{j+1}
+    int jc = -1;
+    Anch lo = empty_pre(), hi = empty_suf();
+    double P = pre;
+    double E0 = 0.0;
+    double e, ei;
+    ref_exp(x[0], xr, c, e, ei);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        // E of the next point: this run's next, or the next run's first
+        double en = 0.0, ein;
+        if (r + 1 < R)
+            ref_exp(x[r + 1], xr, c, en, ein);
+        else if (e0 + R < n)
+            ref_exp(xs, xr, c, en, ein);
+        if (r == 0)
+            E0 = e;
+        if (r < m) {
+            P += e;
+            const double S = suf + sv[r];
+            const double A = P * ei;
+            if (0.5 * A + (double)(n - 1 - (e0 + r)) - 0.5 * (e * S) >= k) {
+                jc = e0 + r;
+                lo = node(x[r], A);
+                hi = e0 + r + 1 < n ? node(r + 1 < R ? x[r + 1] : xs, S * en) : empty_suf();
+            }
+        }
+        e = en;
+        ei = ein;
+    }
+    RowGap gp;
+    gp.jstar = group_max<G>(jc);
+    gp.lo = lo;
+    gp.hi = hi;
+    gp.C = (double)(n - 1 - gp.jstar);
+    if (gp.jstar < 0) {
+        gp.lo = empty_pre();
+        gp.hi = node(x[0], (suf + ss) * E0);
+        gp.C = (double)n;
+    }
+    return gp;
+}
+
+// The same gap by anchored sums (any span).
+template <int G, int R>
+__device__ __forceinline__ RowGap group_gap_anchored(const float (&x)[R], int gl, int e0, int m, int n, double k,
+                                                     double c)
+{
+    const int lane = lane_id();
+    double bv[R];
+    Anch ls = empty_suf();
+#pragma unroll
+    for (int r = R - 1; r >= 0; --r) {
+        if (r < m)
+            ls = bwd(node(x[r], 1.0), ls, c);
+        bv[r] = ls.v;
+    }
+    Anch lp = empty_pre();
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (r < m)
+            lp = fwd(lp, node(x[r], 1.0), c);
+    Anch p = lp, q = ls;
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) {
+        const Anch op = shfl_anch(p, gl >= off ? lane - off : lane);
+        const Anch oq = shfl_anch(q, gl + off < G ? lane + off : lane);
+        if (gl >= off)
+            p = fwd(op, p, c);
+        if (gl + off < G)
+            q = bwd(q, oq, c);
+    }
+    Anch pre = shfl_anch(p, gl > 0 ? lane - 1 : lane);
+    Anch suf = shfl_anch(q, gl < G - 1 ? lane + 1 : lane);
+    if (gl == 0)
+        pre = empty_pre();
+    if (gl == G - 1)
+        suf = empty_suf();
+
+    int jc = -1;
+    Anch jlo = empty_pre(), jhi = empty_suf();
+    Anch A = pre;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r < m) {
+            A = fwd(A, node(x[r], 1.0), c);
+            const Anch Bn = r + 1 < m ? bwd(node(x[r + 1], bv[r + 1]), suf, c) : suf;
+            if (mass_at(x[r], A.v, (double)(n - 1 - (e0 + r)), Bn, c) >= k) {
+                jc = e0 + r;
+                jlo = A;
+                jhi = Bn;
+            }
+        }
+    }
+    RowGap gp;
+    gp.jstar = group_max<G>(jc);
+    gp.lo = jlo;
+    gp.hi = jhi;
+    gp.C = (double)(n - 1 - gp.jstar);
+    if (gp.jstar < 0) {
+        gp.lo = empty_pre();
+        gp.hi = bwd(node(x[0], bv[0]), suf, c);
+        gp.C = (double)n;
+    }
+    return gp;
+}
+
+template <int G, int R>
+__global__ __launch_bounds__(kGroupThreads) void rows_group_forward_kernel(RowsArgs a)
+{
+    static_assert(G >= 1 && G <= kWave && (G & (G - 1)) == 0, "group size");
+    const int lane = lane_id();
+    const int gl = lane & (G - 1);
+    const int base = lane & ~(G - 1);
+    const int64_t row = (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G;
+    const bool live = row < a.rows;
+    const int n = a.n_row;
+    const double c = a.log2e_over_alpha;
+    const float* s = a.s + row * (int64_t)n;
+
+    // the row in load order, and as keys
+    float vo[R];
+    uint32_t key[R];
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = r * G + gl;
+        const bool in = live && i < n;
+        vo[r] = in ? s[i] : 0.0f;
+        bad = bad || (in && !isfinite(vo[r]));
+        key[r] = in ? float_to_key(vo[r]) : 0xFFFFFFFFu;
+    }
+    bad = group_any<G>(bad);
+    group_sort<G, R>(key, gl);
+
+    const int e0 = gl * R;
+    const int m = n - e0 < 0 ? 0 : (n - e0 < R ? n - e0 : R);
+    float x[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        x[r] = key_to_float(key[r]);
+    // the row's ends, and the first point of the next lane's run
+    float xl = x[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r)
+        if (r == (n - 1) % R)
+            xl = x[r];
+    const float xmin = __shfl(x[0], base, kWave);
+    const float xmax = __shfl(xl, base + (n - 1) / R, kWave);
+    const float xs = __shfl(x[0], gl + 1 < G ? lane + 1 : lane, kWave);
+    const RowGap gp = ((double)xmax - (double)xmin) * c <= kRowSpan
+                          ? group_gap_ref<G, R>(x, gl, e0, m, xs, xmin, xmax, n, a.k, c)
+                          : group_gap_anchored<G, R>(x, gl, e0, m, n, a.k, c);
+    // every lane evaluates the closed form on its own (lo, hi); the owner's
+    // is the root
+    const double bl = gap_root(gp.lo, gp.hi, gp.C, a.k, a.alpha, c);
+    double b = __shfl(bl, base + (gp.jstar >= 0 ? gp.jstar / R : 0), kWave);
+    if (bad)
+        b = NAN;
+    if (!live)
+        return;
+    if (gl == 0)
+        a.b[row] = b;
+    float* p = a.p + row * (int64_t)n;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = r * G + gl;
+        if (i < n)
+            p[i] = bad ? NAN : row_p(vo[r], b, c);
+    }
+}
+
+template <int G, int R>
+__global__ __launch_bounds__(kGroupThreads) void rows_group_backward_kernel(RowsArgs a)
+{
+    const int gl = lane_id() & (G - 1);
+    const int64_t row = (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G;
+    const bool live = row < a.rows;
+    const int n = a.n_row;
+    const double c = a.log2e_over_alpha;
+    const float* s = a.s + row * (int64_t)n;
+    const float* g = a.g + row * (int64_t)n;
+    const double b = live ? a.b_in[row] : 0.0;
+    float dv[R], gv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = r * G + gl;
+        const bool in = live && i < n;
+        gv[r] = in ? g[i] : 0.0f;
+        dv[r] = in ? row_d(s[i], b, c) : 0.0f;
+    }
+    double D = 0.0, Gs = 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc_dg(dv[r], gv[r], D, Gs);
+    D = group_sum<G>(D);
+    Gs = group_sum<G>(Gs);
+    if (!live)
+        return;
+    const Ratio2 ratio = split_ratio(D > 0.0 ? Gs / D : 0.0);
+    const float inv_alpha = (float)(1.0 / a.alpha);
+    float* out = a.grad + row * (int64_t)n;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = r * G + gl;
+        if (i < n)
+            out[i] = dv[r] * inv_alpha * minus_ratio(gv[r], ratio);
     }
 }
 
@@ -235,23 +769,78 @@ hipError_t launch_rows_t(const RowsArgs& a, bool forward, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <int G, int R>
+hipError_t launch_group_t(const RowsArgs& a, bool forward, hipStream_t stream)
+{
+    constexpr int kRows = kGroupThreads / G;
+    const dim3 grid((uint32_t)((a.rows + kRows - 1) / kRows));
+    if (forward)
+        STK_LAUNCH(kKRowsForward, stream, (rows_group_forward_kernel<G, R>), grid, dim3(kGroupThreads), 0, stream, a);
+    else
+        STK_LAUNCH(kKRowsBackward, stream, (rows_group_backward_kernel<G, R>), grid, dim3(kGroupThreads), 0, stream,
+                   a);
+    return hipGetLastError();
+}
+
+// Forward shapes up to 1024 scores: 16 scores per lane from 33 on (the
+// sort's in-register stages are its cheapest; fewer lanes per row share the
+// per-row work among more rows), 4 or 8 below.
+hipError_t launch_group_forward(const RowsArgs& a, hipStream_t stream)
+{
+    const int n = a.n_row;
+    if (n <= 4)
+        return launch_group_t<1, 4>(a, true, stream);
+    if (n <= 8)
+        return launch_group_t<2, 4>(a, true, stream);
+    if (n <= 16)
+        return launch_group_t<4, 4>(a, true, stream);
+    if (n <= 32)
+        return launch_group_t<4, 8>(a, true, stream);
+    if (n <= 64)
+        return launch_group_t<4, 16>(a, true, stream);
+    if (n <= 128)
+        return launch_group_t<8, 16>(a, true, stream);
+    if (n <= 256)
+        return launch_group_t<16, 16>(a, true, stream);
+    if (n <= 512)
+        return launch_group_t<32, 16>(a, true, stream);
+    return launch_group_t<64, 16>(a, true, stream);
+}
+
+// Backward shapes up to 1024 scores: 4 scores per lane up to 256 (the
+// widest lane groups read the row in the fewest, best-coalesced requests).
+hipError_t launch_group_backward(const RowsArgs& a, hipStream_t stream)
+{
+    const int n = a.n_row;
+    if (n <= 4)
+        return launch_group_t<1, 4>(a, false, stream);
+    if (n <= 8)
+        return launch_group_t<2, 4>(a, false, stream);
+    if (n <= 16)
+        return launch_group_t<4, 4>(a, false, stream);
+    if (n <= 32)
+        return launch_group_t<8, 4>(a, false, stream);
+    if (n <= 64)
+        return launch_group_t<16, 4>(a, false, stream);
+    if (n <= 128)
+        return launch_group_t<32, 4>(a, false, stream);
+    if (n <= 256)
+        return launch_group_t<64, 4>(a, false, stream);
+    if (n <= 512)
+        return launch_group_t<64, 8>(a, false, stream);
+    return launch_group_t<64, 16>(a, false, stream);
+}
+
 }  // namespace
 
-// Work-group shape for a row: 64 threads up to 64 scores, 256 threads with
-// up to 16 scores each up to 4096, 512 threads with 16 each up to 8192.
+// Rows up to 1024 scores: lane groups, several rows per wave; longer rows,
+// one work-group of 256 threads (8 or 16 scores each) or 512 threads (16
+// each) per row.
 hipError_t launch_rows(const RowsArgs& a, bool forward, hipStream_t stream)
 {
     const int n = a.n_row;
-    if (n <= 64)
-        return launch_rows_t<64, 1>(a, forward, stream);
-    if (n <= 128)
-        return launch_rows_t<64, 2>(a, forward, stream);
-    if (n <= 256)
-        return launch_rows_t<256, 1>(a, forward, stream);
-    if (n <= 512)
-        return launch_rows_t<256, 2>(a, forward, stream);
     if (n <= 1024)
-        return launch_rows_t<256, 4>(a, forward, stream);
+        return forward ? launch_group_forward(a, stream) : launch_group_backward(a, stream);
     if (n <= 2048)
         return launch_rows_t<256, 8>(a, forward, stream);
     if (n <= 4096)

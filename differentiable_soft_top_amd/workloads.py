@@ -17,6 +17,13 @@ Named workloads (score vector, budget k, temperature alpha):
 
 The upstream gradient for the backward pass is an independent stream,
 ``default_rng(seed + 1).standard_normal(n)`` rounded to fp32.
+
+Batched-row workloads (rows x n_row scores, one soft top-k per row, shared k
+and alpha), shaped after the uses the pages name (expert routing, attention
+pruning):
+
+  r1  65,536 rows x 256      N(0,1)   k=8    alpha=0.1
+  r2  8,192 rows x 2,048     N(0,1)   k=64   alpha=0.05
 """
 from __future__ import annotations
 
@@ -108,3 +115,32 @@ def make_workload(name: str, n: int | None = None, seed: int | None = None):
     else:
         k = w.k if nn == w.n else max(1.0, round(w.k * nn / w.n))
     return s, float(k), float(w.alpha), w
+
+
+@dataclass(frozen=True)
+class RowWorkload:
+    name: str
+    rows: int
+    n_row: int
+    dist: str
+    k: float
+    alpha: float
+    seed: int = 0
+    description: str = ""
+
+
+ROW_WORKLOADS = {
+    "r1": RowWorkload("r1", 65536, 256, "normal", 8.0, 0.1, 0,
+                      "65536 rows x 256 N(0,1), k=8, alpha=0.1"),
+    "r2": RowWorkload("r2", 8192, 2048, "normal", 64.0, 0.05, 0,
+                      "8192 rows x 2048 N(0,1), k=64, alpha=0.05"),
+}
+
+
+def make_row_workload(name: str, rows: int | None = None):
+    """Return (scores fp32 [rows, n_row], k, alpha, workload) for a named row workload;
+    ``rows`` overrides the row count (same rows, fewer of them)."""
+    w = ROW_WORKLOADS[name]
+    r = w.rows if rows is None else int(rows)
+    s = draw_scores(w.dist, r * w.n_row, w.seed).reshape(r, w.n_row)
+    return np.ascontiguousarray(s), float(w.k), float(w.alpha), w
