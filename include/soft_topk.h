@@ -207,10 +207,14 @@ int soft_topk_backward_ex(const float* grad_p, const float* scores, int64_t n,
  * scores + r * n_row.  Every row gets its own threshold b_r (out_b: fp64[rows],
  * device) with sum_i F((s_ri - b_r)/alpha) = k, and out_p[r * n_row + i] =
  * F((s_ri - b_r)/alpha); k and alpha are shared by all rows (0 < k < n_row,
- * alpha > 0).  Rows of at most 8192 scores are solved one work-group per
- * row, fully asynchronously on `stream`, and need no workspace.  Longer
- * rows run the single-vector forward row after row (each waits for its
- * status) in `workspace`.  A row holding a NaN or an infinite score gets
+ * alpha > 0).  Rows of at most 8192 scores are solved on the device alone
+ * (several rows per wave up to 1024 scores, one work-group per row above),
+ * fully asynchronously on `stream`, and need no workspace; longer rows run
+ * the single-vector forward row after row (each waits for its status) in
+ * `workspace`.  Accuracy on the device-only rows: the sums use fp32
+ * exponentials (relative error a few 1e-7) inside fp64 sums and an fp64
+ * closed form, so b is within about 1e-7 * alpha and p within about 1e-7
+ * of the exact values.  A row holding a NaN or an infinite score gets
  * b = NaN and p = NaN; the call still returns OK.  Errors: EINVAL,
  * EWORKSPACE before any launch; EHIP on a launch failure.
  */
