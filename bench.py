@@ -30,7 +30,9 @@ kernel source, else null.  That file is written by
 COPY_BYTES bytes whose counter readings calibrate the two counters).
 
 "rows" times the batched-row operator (one soft top-k per row) forward +
-backward on two row workloads, warm and cold, the same way.
+backward on two row workloads, warm and cold, the same way; each carries the
+traffic of its two kernels when profiles/traffic.json holds current counter
+runs for it (the same three commands with --workload r1 or r2 added to each).
 
 "cpu_baseline" times the fp64 CPU oracle (forward + backward) on a bounded
 sample (the first 2^25 scores, k scaled) and scales by n log2 n.
@@ -63,6 +65,13 @@ KERNEL_SOURCE = {"pass1": "pass1.hip", "emit": "emit_vjp.hip", "vjp_reduce": "em
 KERNEL_SYMBOLS = {"pass1": ("stk::pass1_kernel",), "emit": ("stk::emit_kernel", "stk::emit_seg_kernel"),
                   "vjp_reduce": ("stk::vjp_reduce_kernel", "stk::vjp_reduce_seg_kernel"),
                   "vjp_apply": ("stk::vjp_apply_kernel", "stk::vjp_apply_seg_kernel")}
+# batched rows: the lane-group kernels (rows up to 1024 scores) and the
+# work-group-per-row kernels (longer rows); algorithmic bytes per score
+ROWS_ALGO_BYTES = {"rows_forward": 8, "rows_backward": 12}
+ROWS_SYMBOLS = {"rows_forward": ("stk::rows_group_forward_kernel", "stk::rows_forward_kernel"),
+                "rows_backward": ("stk::rows_group_backward_kernel", "stk::rows_backward_kernel")}
+for _k in ROWS_ALGO_BYTES:
+    KERNEL_SOURCE[_k] = "rows.hip"
 
 
 class Runner:
@@ -161,7 +170,7 @@ def time_steps(torch, runner, steps, flush=None):
 def src_hash(name):
     """Hash of the kernel's source file and the headers that shape its launch."""
     h = hashlib.sha256()
-    for fn in (KERNEL_SOURCE[name], "stk_common.hpp", "stk_layout.hpp"):
+    for fn in (KERNEL_SOURCE[name], "stk_common.hpp", "stk_layout.hpp", "stk_scan.hpp"):
         with open(os.path.join(ROOT, "differentiable_soft_top_amd", "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -173,7 +182,7 @@ def traffic_for(kernel, workload):
         return None
     with open(path) as f:
         tr = json.load(f)
-    ent = tr.get(workload, {}).get(kernel)
+    ent = tr.get(workload, {}).get("kernels", {}).get(kernel)
     if not ent or ent.get("source_sha256") != src_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
@@ -183,16 +192,22 @@ COPY_FLOATS = 100_000_000  # calibration copy: 400 MB read + 400 MB written
 
 
 def profile_run(torch, steps, warmup, workload):
-    """Short run for counter collection: the workload's steps, then one plain
-    device-to-device copy of known size (the calibration kernel)."""
+    """Short run for counter collection: the workload's steps (a single vector
+    c1..c5 or a batch of rows r1, r2), then one plain device-to-device copy of
+    known size (the calibration kernel)."""
     from differentiable_soft_top_amd import _lib
-    from differentiable_soft_top_amd.workloads import draw_grad, make_workload
+    from differentiable_soft_top_amd.workloads import ROW_WORKLOADS, draw_grad, make_row_workload, make_workload
     lib = _lib.load()
     dev = torch.device("cuda:0")
-    s_np, k, alpha, w = make_workload(workload)
-    s = torch.from_numpy(s_np).to(dev)
-    g = torch.from_numpy(draw_grad(s_np.size, w.seed)).to(dev)
-    run = Runner(torch, lib, s, g, k, alpha)
+    if workload in ROW_WORKLOADS:
+        s_np, k, alpha, w = make_row_workload(workload)
+        g_np = draw_grad(s_np.size, w.seed).reshape(s_np.shape)
+        run = RowsRunner(torch, lib, torch.from_numpy(s_np).to(dev), torch.from_numpy(g_np).to(dev), k, alpha)
+    else:
+        s_np, k, alpha, w = make_workload(workload)
+        s = torch.from_numpy(s_np).to(dev)
+        g = torch.from_numpy(draw_grad(s_np.size, w.seed)).to(dev)
+        run = Runner(torch, lib, s, g, k, alpha)
     for _ in range(warmup + steps):
         run.step()
     torch.cuda.synchronize()
@@ -217,9 +232,10 @@ def _read_counter_csv(path, counter):
 
 
 def pmc_summary(fetch_csv, write_csv, workload="c4"):
-    """Turn the two counter runs of --profile-run into profiles/traffic.json:
-    bytes per launch of each streaming kernel, each counter scaled so that the
-    calibration copy reads exactly its known size."""
+    """Turn the two counter runs of --profile-run into the workload's entry of
+    profiles/traffic.json: bytes per launch of each streaming kernel, each
+    counter scaled so that the calibration copy reads exactly its known size.
+    Other workloads' entries are kept."""
     fetch = _read_counter_csv(fetch_csv, "FETCH_SIZE")
     write = _read_counter_csv(write_csv, "WRITE_SIZE")
     copy_bytes = 4 * COPY_FLOATS
@@ -230,13 +246,19 @@ def pmc_summary(fetch_csv, write_csv, workload="c4"):
 
     f_scale = copy_bytes / copy_value(fetch)
     w_scale = copy_bytes / copy_value(write)
-    n = int({"c2": 1e6, "c3": 1e7, "c4": 1e8}.get(workload, 1e8))
-    result = {"_calibration": {"copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
-                               "fetch_csv": os.path.basename(fetch_csv), "write_csv": os.path.basename(write_csv)}}
+    from differentiable_soft_top_amd.workloads import ROW_WORKLOADS, WORKLOADS
+    if workload in ROW_WORKLOADS:
+        n = ROW_WORKLOADS[workload].rows * ROW_WORKLOADS[workload].n_row
+        algo, symbols = ROWS_ALGO_BYTES, ROWS_SYMBOLS
+    else:
+        n = WORKLOADS[workload].n
+        algo, symbols = ALGO_BYTES, KERNEL_SYMBOLS
+    calib = {"copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+             "fetch_csv": os.path.basename(fetch_csv), "write_csv": os.path.basename(write_csv)}
     ent = {}
-    for kname in ALGO_BYTES:
-        fk = [name for name in fetch if any(sym in name for sym in KERNEL_SYMBOLS[kname])]
-        wk = [name for name in write if any(sym in name for sym in KERNEL_SYMBOLS[kname])]
+    for kname in algo:
+        fk = [name for name in fetch if any(sym in name for sym in symbols[kname])]
+        wk = [name for name in write if any(sym in name for sym in symbols[kname])]
         if not fk or not wk:
             continue
         fv = [v for name in fk for v in fetch[name]]
@@ -244,10 +266,15 @@ def pmc_summary(fetch_csv, write_csv, workload="c4"):
         fb = sum(fv) / len(fv) * 1024.0 * f_scale
         wb = sum(wv) / len(wv) * 1024.0 * w_scale
         ent[kname] = {"kernels": sorted(set(fk)), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
-                      "bytes_per_launch": fb + wb, "algorithmic_bytes_per_launch": ALGO_BYTES[kname] * n,
+                      "bytes_per_launch": fb + wb, "algorithmic_bytes_per_launch": algo[kname] * n,
                       "launches": len(fv), "source_sha256": src_hash(kname)}
-    result[workload] = ent
     path = os.path.join(ROOT, "profiles", "traffic.json")
+    result = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            result = json.load(f)
+    result.pop("_calibration", None)  # older single-workload layout
+    result[workload] = {"calibration": calib, "kernels": ent}
     with open(path, "w") as f:
         json.dump(result, f, indent=1, sort_keys=True)
     print(json.dumps(result, indent=1, sort_keys=True))
@@ -284,7 +311,8 @@ def main():
     ap.add_argument("--rows", default="r1,r2", help="batched-row workloads timed (comma list, '' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
-                    help="counter-collection run: a few steps of --workload, then the calibration copy")
+                    help="counter-collection run: a few steps of --workload (c1..c5 or a row workload "
+                         "r1, r2), then the calibration copy")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 counter CSVs (no GPU needed)")
     args = ap.parse_args()
@@ -383,6 +411,8 @@ def main():
             "median_ms": med, "p10_ms": float(np.percentile(warm, 10)), "p90_ms": float(np.percentile(warm, 90)),
             "median_ms_cold": float(np.median(cold)),
             "algorithmic_GBps": RowsRunner.BYTES_PER_SCORE * s2_np.size / (med / 1e3) / 1e9,
+            # HBM bytes per launch from the counter runs (null when stale)
+            "traffic": {kname: traffic_for(kname, rname) for kname in ROWS_ALGO_BYTES},
         }
         del rrun
         torch.cuda.empty_cache()
