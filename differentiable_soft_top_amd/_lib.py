@@ -12,7 +12,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsofttopk.so")
 
 OK, EINVAL, ENONFINITE, EWORKSPACE, EHIP, ESOLVE = 0, 1, 2, 3, 4, 5
-PATH_BRACKET, PATH_WIDENED, PATH_FULLSORT = 1, 2, 3
+PATH_BRACKET, PATH_WIDENED, PATH_FULLSORT, PATH_SINGLE = 1, 2, 3, 4
 BAND_DIRECT, BAND_BUCKETS = 1, 2
 REJECT_LOW, REJECT_HIGH, REJECT_OVERFLOW, REJECT_BUCKET, REJECT_MASS = 1, 2, 4, 8, 16
 

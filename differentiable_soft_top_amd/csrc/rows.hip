@@ -833,6 +833,67 @@ hipError_t launch_group_backward(const RowsArgs& a, hipStream_t stream)
 
 }  // namespace
 
+constexpr int kSingleThreads = 256;
+
+__global__ __launch_bounds__(kSingleThreads) void single_status_kernel(SingleArgs a)
+{
+    constexpr int kW = kSingleThreads / kWave;
+    constexpr int kWords = (int)(sizeof(Status) / 4);
+    __shared__ double red[kW];
+    const int tid = threadIdx.x;
+    double m = 0.0;
+    for (int64_t i = tid; i < a.n; i += kSingleThreads)
+        m += (double)a.p[i];
+    m = wave_sum(m);
+    if (lane_id() == 0)
+        red[tid / kWave] = m;
+    if (tid < kWords)
+        reinterpret_cast<uint32_t*>(a.st)[tid] = 0u;
+    __syncthreads();
+    if (tid == 0) {
+        double tot = 0.0;
+        for (int w = 0; w < kW; ++w)
+            tot += red[w];
+        // the row kernel reports a non-finite score as b = NaN
+        const double b = *a.b;
+        const bool bad = b != b;
+        a.st->b = b;
+        a.st->mass = tot;
+        a.st->emit_done = 1u;
+        a.st->nonfinite = bad ? 1u : 0u;
+        a.st->solve_state = bad ? kSolveNonfinite : kSolveOk;
+    }
+    __syncthreads();
+    publish_status(a.st, a.mirror, a.seq);
+}
+
+// One row on its own (the single-vector route): the shortest chain per
+// thread, up to 1024 threads with at most 4 scores each, then 512 threads
+// with 16 (1024 threads with 8 would spill).
+hipError_t launch_row_alone(const RowsArgs& a, bool forward, hipStream_t stream)
+{
+    const int n = a.n_row;
+    if (n <= 64)
+        return forward ? launch_group_forward(a, stream) : launch_group_backward(a, stream);
+    if (n <= 256)
+        return launch_rows_t<256, 1>(a, forward, stream);
+    if (n <= 512)
+        return launch_rows_t<512, 1>(a, forward, stream);
+    if (n <= 1024)
+        return launch_rows_t<1024, 1>(a, forward, stream);
+    if (n <= 2048)
+        return launch_rows_t<1024, 2>(a, forward, stream);
+    if (n <= 4096)
+        return launch_rows_t<1024, 4>(a, forward, stream);
+    return launch_rows_t<512, 16>(a, forward, stream);
+}
+
+hipError_t launch_single_status(const SingleArgs& a, hipStream_t stream)
+{
+    single_status_kernel<<<1, kSingleThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
 // Rows up to 1024 scores: lane groups, several rows per wave; longer rows,
 // one work-group of 256 threads (8 or 16 scores each) or 512 threads (16
 // each) per row.

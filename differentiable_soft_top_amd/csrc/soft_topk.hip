@@ -106,7 +106,7 @@ bool params_ok(const soft_topk_params& p)
         return false;
     if (p.band_capacity < 0 || p.max_widen < 0 || p.max_widen > 16)
         return false;
-    if (p.force_path != 0 && p.force_path != SOFT_TOPK_PATH_FULLSORT)
+    if (p.force_path != 0 && p.force_path != SOFT_TOPK_PATH_BRACKET && p.force_path != SOFT_TOPK_PATH_FULLSORT)
         return false;
     if (!isfinite(p.mass_tolerance))
         return false;
@@ -797,7 +797,42 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
     // does
     const bool wait_mass = prm.verify_mass != 0 || stats != nullptr;
 
-    if (prm.force_path != SOFT_TOPK_PATH_FULLSORT) {
+    if (n <= kRowMax && prm.force_path == 0 && prm.band_route == 0) {
+        // one kernel sorts the whole vector in registers and solves it
+        // exactly (the full-sort solver, with no bracket to certify); a
+        // second folds the fp64 mass and publishes the status
+        RowsArgs ra = rows_args(scores, 1, n, alpha);
+        ra.p = out_p;
+        ra.b = out_b;
+        ra.k = k;
+        STK_HIP(launch_row_alone(ra, true, x.stream));
+        SingleArgs sa;
+        sa.p = out_p;
+        sa.b = out_b;
+        sa.n = n;
+        sa.st = x.st;
+        sa.mirror = x.mirror0;
+        sa.seq = next_publication();
+        STK_HIP(launch_single_status(sa, x.stream));
+        int rc = wait_solve(x, &h);
+        if (rc)
+            return rc;
+        if (h.nonfinite)
+            return SOFT_TOPK_ENONFINITE;
+        sx.n_band = n;
+        sx.a_left = -INFINITY;
+        sx.a_right = INFINITY;
+        sx.mass_at_left = (double)n;
+        sx.mass_at_right = 0.0;
+        if (prm.verify_mass == 0 || mass_ok(h, k, tol)) {
+            sx.path = SOFT_TOPK_PATH_SINGLE;
+            done = true;
+        } else {
+            sx.reject_mask |= SOFT_TOPK_REJECT_MASS;  // the full sort decides
+        }
+    }
+
+    if (!done && prm.force_path != SOFT_TOPK_PATH_FULLSORT) {
         const double q = 1.0 - k / (double)n;
         int64_t rl = lower_rank(plan.m, q, prm.z);
         int64_t rr = upper_rank(plan.m, q, prm.z);
@@ -940,6 +975,16 @@ int soft_topk_backward_ex(const float* grad_p, const float* scores, int64_t n, d
     const size_t need = soft_topk_backward_workspace_bytes(n);
     if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % 16) != 0)
         return SOFT_TOPK_EWORKSPACE;
+    if (n <= kRowMax) {
+        // one work-group reduces D and G and writes the gradient (the row
+        // kernel with one row)
+        RowsArgs ra = rows_args(scores, 1, n, alpha);
+        ra.g = grad_p;
+        ra.b_in = b;
+        ra.grad = grad_s;
+        STK_HIP(launch_row_alone(ra, false, static_cast<hipStream_t>(stream)));
+        return SOFT_TOPK_OK;
+    }
     VjpArgs a;
     a.g = grad_p;
     a.s = scores;

@@ -372,5 +372,21 @@ struct RowsArgs {
     double k, alpha, log2e_over_alpha;
 };
 hipError_t launch_rows(const RowsArgs& a, bool forward, hipStream_t stream);
+// One row (rows == 1, n_row <= kRowMax) with the shortest chain per thread:
+// the single-vector route, where latency matters rather than throughput.
+hipError_t launch_row_alone(const RowsArgs& a, bool forward, hipStream_t stream);
+
+// A single vector of at most kRowMax scores solved by the row kernels: one
+// work-group folds the fp64 sum of the emitted p, writes a fresh status
+// block (b, mass, the non-finite flag; no segment record) and publishes it.
+struct SingleArgs {
+    const float* p;
+    const double* b;
+    int64_t n;
+    Status* st;
+    Mirror* mirror;
+    uint32_t seq;
+};
+hipError_t launch_single_status(const SingleArgs& a, hipStream_t stream);
 
 }  // namespace stk

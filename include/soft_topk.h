@@ -58,6 +58,8 @@ extern "C" {
 #define SOFT_TOPK_PATH_BRACKET 1  /* bracket certified on the first pass    */
 #define SOFT_TOPK_PATH_WIDENED 2  /* certified after widening the bracket   */
 #define SOFT_TOPK_PATH_FULLSORT 3 /* full device radix sort of all scores   */
+#define SOFT_TOPK_PATH_SINGLE 4   /* n <= 8192: one kernel sorts all scores
+                                     in registers and solves them exactly   */
 
 /* How a bracketed round solved its band (soft_topk_params.band_route,
  * soft_topk_stats.band_route). */
@@ -84,7 +86,10 @@ typedef struct soft_topk_params {
                                ranks use exact binomial tails at Phi(-z) (default 5) */
     int64_t band_capacity;  /* max band elements (0 = default: clamp(n/4, 2^16, 2^22)) */
     int32_t max_widen;      /* bracket widenings before the full sort (default 2)     */
-    int32_t force_path;     /* 0 auto, 3 = go straight to the full sort               */
+    int32_t force_path;     /* 0 auto (n <= 8192: SOFT_TOPK_PATH_SINGLE, else the
+                               bracketed route); SOFT_TOPK_PATH_BRACKET: the
+                               bracketed route at every n; SOFT_TOPK_PATH_FULLSORT:
+                               straight to the full sort                         */
     double mass_tolerance;  /* post-solve |sum p - k| bound; <=0 = default
                                (1e-3 + 1e-12 * n)                                    */
     int32_t verify_mass;    /* 1: wait for the certification pass (fp64 sum of p)
@@ -103,10 +108,12 @@ typedef struct soft_topk_params {
 /* Host-side record of one forward call (all fields written on success). */
 typedef struct soft_topk_stats {
     int32_t path;           /* SOFT_TOPK_PATH_*                                       */
-    int32_t rounds;         /* bracketed rounds run (0 when forced to full sort)      */
+    int32_t rounds;         /* bracketed rounds run (0 on the full sort when forced,
+                               and on SOFT_TOPK_PATH_SINGLE)                      */
     int32_t reject_mask;    /* OR of SOFT_TOPK_REJECT_* over rejected rounds          */
     int32_t band_route;     /* SOFT_TOPK_BAND_* of the last bracketed round (0: none) */
-    float a_left, a_right;  /* bracket of the last bracketed round                    */
+    float a_left, a_right;  /* bracket of the last bracketed round (-inf / +inf and
+                               n_band = n on SOFT_TOPK_PATH_SINGLE)                */
     int64_t n_left, n_band, n_right; /* scores below / inside / at-or-above it        */
     double mass_at_left;    /* M(a_L) of the last bracketed round                     */
     double mass_at_right;   /* M(a_R) of the last bracketed round                     */
@@ -133,9 +140,14 @@ size_t soft_topk_backward_workspace_bytes(int64_t n);
  * out_p[i] = F((scores[i] - b)/alpha).  out_b: one fp64 (device) receiving b.
  * workspace: soft_topk_workspace_bytes(n, NULL) bytes of device memory, any
  * contents, 256-byte aligned.
+ * Route: up to 8192 scores (by default) one kernel sorts the whole vector in
+ * registers and solves it with the full-sort solver of the gist.science
+ * summary of Fast LapSum (section 2.2), exactly, with no bracket to certify;
+ * larger n take the bracketed route (sample, streaming pass, band sort,
+ * certified segment solve) with the full sort as its fallback.
  * Synchronisation: enqueues on `stream` and waits (a 256-byte status
- * read-back) until the segment solve has certified the bracket, so that the
- * route is settled on return.  b is final in device memory at that point; the
+ * read-back) until the segment solve has certified the bracket (or the
+ * one-kernel solve has ended), so that the route is settled on return.  b is final in device memory at that point; the
  * emission of p is already enqueued behind it and completes in stream order,
  * so any later work on `stream` sees the final p.  With
  * params->verify_mass = 1 or a stats record, the fp64 mass sum of p is also
@@ -162,7 +174,9 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
  * b: device pointer to the forward's fp64 threshold.  grad_s: fp32[n]
  * (device) receiving (d_i/alpha)(g_i - G/D).  workspace:
  * soft_topk_backward_workspace_bytes(n) bytes of device memory, any contents.
- * Fully asynchronous on `stream` (no host synchronisation).
+ * Fully asynchronous on `stream` (no host synchronisation).  Up to 8192
+ * scores one work-group computes D, G and the gradient in one kernel; larger
+ * n take a reduction kernel and a gradient kernel.
  * Errors: EINVAL / EWORKSPACE before any launch; EHIP on a launch failure.
  */
 int soft_topk_backward(const float* grad_p, const float* scores, int64_t n,

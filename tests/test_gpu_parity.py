@@ -96,10 +96,14 @@ SMALL = [
 def test_small_parity(dev, name, n, route):
     """Both band routes: at these sizes the band is small enough to be sorted
     whole (the automatic choice); forcing the value buckets runs the route
-    the larger workloads take on the same inputs."""
+    the larger workloads take on the same inputs.  (c1 is short enough for
+    the one-kernel route by default, so the bracketed route is forced.)"""
     s_np, k, alpha, w = make_workload(name, n=n)
     g_np = draw_grad(s_np.size, w.seed)
-    prm = params(band_route=_lib.BAND_BUCKETS) if route == "buckets" else None
+    if route == "buckets":
+        prm = params(band_route=_lib.BAND_BUCKETS)
+    else:
+        prm = params(force_path=_lib.PATH_BRACKET) if s_np.size <= 8192 else None
     res = run(dev, s_np, k, alpha, g_np, prm)
     check_full(res, s_np, k, alpha, g_np)
     assert res["stats"]["path"] == _lib.PATH_BRACKET, res["stats"]
@@ -195,11 +199,52 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("route", ["auto", "bracket"])
 @pytest.mark.parametrize("tag,s_np,k,alpha", EDGE, ids=[e[0] for e in EDGE])
-def test_tiny_inputs(dev, tag, s_np, k, alpha):
+def test_tiny_inputs(dev, tag, s_np, k, alpha, route):
     g_np = np.linspace(-1, 1, s_np.size).astype(np.float32)
-    res = run(dev, s_np, k, alpha, g_np)
+    prm = params(force_path=_lib.PATH_BRACKET) if route == "bracket" else None
+    res = run(dev, s_np, k, alpha, g_np, prm)
     check_full(res, s_np, k, alpha, g_np)
+    want = _lib.PATH_BRACKET if route == "bracket" else _lib.PATH_SINGLE
+    assert res["stats"]["path"] == want, res["stats"]
+
+
+@pytest.mark.parametrize("n", [2, 63, 64, 65, 300, 1000, 1024, 1025, 2000, 4096, 8191, 8192, 8193])
+def test_single_kernel_route(dev, n):
+    """Vectors of at most 8192 scores take the one-kernel route by default
+    (the whole vector sorted in registers and solved exactly, then the fp64
+    mass published); longer ones the bracketed route.  Both match the oracle
+    and agree with the bracketed route forced at the same size."""
+    rng = np.random.default_rng(n)
+    s_np = rng.standard_normal(n).astype(np.float32)
+    s_np[: n // 3] = np.round(s_np[: n // 3] * 4.0) / 4.0  # some ties
+    s_np = s_np[rng.permutation(n)]
+    g_np = rng.standard_normal(n).astype(np.float32)
+    for k in (0.5, n / 10.0, n - 0.25):
+        res = run(dev, s_np, k, 0.05, g_np)
+        check_full(res, s_np, k, 0.05, g_np)
+        st = res["stats"]
+        assert st["path"] == (_lib.PATH_SINGLE if n <= 8192 else _lib.PATH_BRACKET), st
+        assert abs(st["mass"] - k) <= 1e-3, st
+        assert st["b"] == res["b"]
+        forced = run(dev, s_np, k, 0.05, g_np, params(force_path=_lib.PATH_BRACKET))
+        assert forced["stats"]["path"] in (_lib.PATH_BRACKET, _lib.PATH_WIDENED, _lib.PATH_FULLSORT)
+        assert abs(forced["b"] - res["b"]) <= 2e-5 * 0.05
+
+
+def test_single_kernel_route_rejects_nonfinite_and_checks_mass(dev):
+    s_np = np.random.default_rng(5).standard_normal(3000).astype(np.float32)
+    for bad in (np.nan, np.inf, -np.inf):
+        t = s_np.copy()
+        t[2999] = bad
+        with pytest.raises(stk.SoftTopKError) as e:
+            stk.forward(torch.from_numpy(t).to(dev), 100.0, 0.1)
+        assert e.value.code == _lib.ENONFINITE
+    # the mass check on request, and the stats without it
+    res = run(dev, s_np, 100.0, 0.1, None, params(verify_mass=1))
+    assert res["stats"]["path"] == _lib.PATH_SINGLE and abs(res["stats"]["mass"] - 100.0) <= 1e-3
+    check_full(res, s_np, 100.0, 0.1)
 
 
 @pytest.mark.parametrize("case", ["equal", "sorted", "reversed", "k_tiny", "k_near_n", "alpha_huge",
@@ -527,7 +572,7 @@ def test_certified_first_try_over_100_seeds(dev, name):
     seeds = [int(x) for x in rng.integers(1, 2 ** 63, 100)]
     worst = 0.0
     for seed in seeds:
-        _, b, st = stk.forward(s, k, alpha, params(seed=seed), want_stats=True)
+        _, b, st = stk.forward(s, k, alpha, params(seed=seed, force_path=_lib.PATH_BRACKET), want_stats=True)
         assert st["path"] == _lib.PATH_BRACKET and st["rounds"] == 1, (name, seed, st)
         worst = max(worst, abs(float(b.item()) - gold["b"]) / alpha)
     assert worst <= 1e-5, (name, worst)
