@@ -7,12 +7,13 @@
 // row) gets b_r with sum_i F((s_ri - b_r)/alpha) = k, p_ri = F((s_ri -
 // b_r)/alpha), and the VJP of each row as in the single-vector path.
 //
-// gfx950 design: one work-group per row (one wave up to 1024 scores), the
-// row held in registers.
+// gfx950 design: rows up to 1024 scores are held by lane groups, several
+// rows per wave (below); longer rows by one work-group each; the row is
+// held in registers either way.
 //   forward -- the row is loaded coalesced (R scores per thread), copied as
-//     order-preserving keys and sorted by a register bitonic network (the
-//     sorted keys end in blocked order: thread t holds positions t*R ..
-//     t*R+R-1).  The full-sort solver of section 2.2 then needs, at every
+//     order-preserving keys and sorted by a bitonic network in its
+//     direction-free form (the sorted keys end in blocked order: thread t
+//     holds positions t*R .. t*R+R-1).  The full-sort solver of section 2.2 then needs, at every
 //     breakpoint x_j, the left sum A_j = sum_{i<=j} e^{(x_i-x_j)/alpha} and
 //     the right sum sum_{i>j} e^{(x_j-x_i)/alpha}.  When the row spans at
 //     most kRowSpan in log2 units ((x_max - x_min) log2(e)/alpha), every
@@ -111,6 +112,95 @@ __device__ __forceinline__ float row_d(float v, double b, double c)
 
 }  // namespace
 
+// Ascending sort of a work-group's kT * R keys into blocked order (thread t
+// ends with positions t * R .. t * R + R - 1): the bitonic network in its
+// direction-free form (each merge compares the lower half with the mirror
+// image of the upper half, then runs ascending half-cleaners).  Exchanges
+// inside a thread are bare min/max, inside a wave lane shuffles, across
+// waves one LDS round trip behind one barrier (two buffers used in turn).
+// LDS holds element (t, r) at r * kT + t, so a wave touches distinct banks.
+template <int kT, int R>
+__device__ __forceinline__ void block_sort_flip(uint32_t (&v)[R], uint32_t* buf0, uint32_t* buf1)
+{
+    constexpr int N = kT * R;
+    const int tid = threadIdx.x;
+    int flip = 0;
+#pragma unroll
+    for (int k = 2; k <= N; k <<= 1) {
+        if (k <= R) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int q = r ^ (k - 1);
+                if ((r & (k >> 1)) == 0) {
+                    const uint32_t lo = v[r] < v[q] ? v[r] : v[q];
+                    const uint32_t hi = v[r] < v[q] ? v[q] : v[r];
+                    v[r] = lo;
+                    v[q] = hi;
+                }
+            }
+        } else {
+            // mirror partner: thread tid ^ (k / R - 1), register R - 1 - r
+            const int d = k / R - 1;
+            const bool lower = (tid & ((k >> 1) / R)) == 0;
+            uint32_t o[R];
+            if (d < kWave) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    o[r] = (uint32_t)__shfl_xor((int)v[R - 1 - r], d, kWave);
+            } else {
+                uint32_t* buf = flip ? buf1 : buf0;
+                flip ^= 1;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    buf[r * kT + tid] = v[r];
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    o[r] = buf[(R - 1 - r) * kT + (tid ^ d)];
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                v[r] = lower ? (v[r] < o[r] ? v[r] : o[r]) : (v[r] > o[r] ? v[r] : o[r]);
+        }
+#pragma unroll
+        for (int j = k >> 2; j > 0; j >>= 1) {
+            if (j < R) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if ((r & j) == 0) {
+                        const uint32_t lo = v[r] < v[r | j] ? v[r] : v[r | j];
+                        const uint32_t hi = v[r] < v[r | j] ? v[r | j] : v[r];
+                        v[r] = lo;
+                        v[r | j] = hi;
+                    }
+                }
+            } else {
+                const int d = j / R;
+                const bool lower = (tid & d) == 0;
+                uint32_t o[R];
+                if (d < kWave) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        o[r] = (uint32_t)__shfl_xor((int)v[r], d, kWave);
+                } else {
+                    uint32_t* buf = flip ? buf1 : buf0;
+                    flip ^= 1;
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        buf[r * kT + tid] = v[r];
+                    __syncthreads();
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        o[r] = buf[r * kT + (tid ^ d)];
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    v[r] = lower ? (v[r] < o[r] ? v[r] : o[r]) : (v[r] > o[r] ? v[r] : o[r]);
+            }
+        }
+    }
+}
+
 // The root of one sorted row (blocked order, run e0 .. e0 + m - 1 in x) by
 // reference-point sums; xs is the first point of the next run (if any).
 template <int kT, int R>
@@ -121,51 +211,54 @@ __device__ __forceinline__ void solve_ref(const float (&x)[R], int e0, int m, fl
     const int n = a.n_row;
     const double c = a.log2e_over_alpha;
     const double xr = 0.5 * ((double)xmin + (double)xmax);
-    double E[R], Ei[R], sv[R];
+    // backward over the run: sv[r] = sum of 1/E after position r (kept), and
+    // the run's sums of E and 1/E; E and 1/E are recomputed in the forward
+    // pass below rather than kept (registers decide occupancy)
+    double sv[R];
     double ps = 0.0, ss = 0.0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        E[r] = 0.0;
-        Ei[r] = 0.0;
-        if (r < m)
-            ref_exp(x[r], xr, c, E[r], Ei[r]);
-        ps += E[r];
-    }
-    // sv[r]: this run's 1/E after position r
 #pragma unroll
     for (int r = R - 1; r >= 0; --r) {
         sv[r] = ss;
-        ss += Ei[r];
+        if (r < m) {
+            double e, ei;
+            ref_exp(x[r], xr, c, e, ei);
+            ps += e;
+            ss += ei;
+        }
     }
     double pre, suf;
     scan_pair<kW>(ps, ss, wp, ws, pre, suf);
-    double En = 0.0, Ein = 0.0;  // the next run's first point
-    if (e0 + R < n)
-        ref_exp(xs, xr, c, En, Ein);
 
     // mass at x_j: A_j / 2 + (points after j) - (right sum) / 2, with
-    // A_j = P_{<=j} / E_j and right sum E_j S_{>j}
+    // A_j = P_{<=j} / E_j and right sum E_j S_{>j}; the gap's right end
+    // carries S_{>j} E_{j+1}
     int jc = -1;
     Anch lo = empty_pre(), hi = empty_suf();
     double P = pre;
+    double E0 = 0.0;
+    double e, ei;
+    ref_exp(x[0], xr, c, e, ei);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
+        double en = 0.0, ein;
+        if (r + 1 < R)
+            ref_exp(x[r + 1], xr, c, en, ein);
+        else if (e0 + R < n)
+            ref_exp(xs, xr, c, en, ein);
+        if (r == 0)
+            E0 = e;
         if (r < m) {
-            P += E[r];
+            P += e;
             const double S = suf + sv[r];
-            const double A = P * Ei[r];
-            if (0.5 * A + (double)(n - 1 - (e0 + r)) - 0.5 * (E[r] * S) >= a.k) {
+            const double A = P * ei;
+            if (0.5 * A + (double)(n - 1 - (e0 + r)) - 0.5 * (e * S) >= a.k) {
                 jc = e0 + r;
                 lo = node(x[r], A);
-                // the next point's right sum (anchored at it): S E_{j+1}
-                if (r + 1 < m)
-                    hi = node(x[r + 1], S * E[r + 1]);
-                else if (e0 + R < n)
-                    hi = node(xs, S * En);
-                else
-                    hi = empty_suf();
+                hi = e0 + r + 1 < n ? node(r + 1 < R ? x[r + 1] : xs, S * en) : empty_suf();
             }
         }
+        e = en;
+        ei = ein;
     }
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -188,7 +281,7 @@ __device__ __forceinline__ void solve_ref(const float (&x)[R], int e0, int m, fl
             *bsh = gap_root(lo, hi, (double)(n - 1 - jmax), a.k, a.alpha, c);
     } else if (threadIdx.x == 0) {
         // the root lies before the first point: every point on the right
-        *bsh = gap_root(empty_pre(), node(x[0], (suf + ss) * E[0]), (double)n, a.k, a.alpha, c);
+        *bsh = gap_root(empty_pre(), node(x[0], (suf + ss) * E0), (double)n, a.k, a.alpha, c);
     }
 }
 
@@ -306,7 +399,7 @@ __global__ __launch_bounds__(kT) void rows_forward_kernel(RowsArgs a)
             a.b[row] = NAN;
         return;
     }
-    block_bitonic_regs<kT, R>(key, buf0, buf1);
+    block_sort_flip<kT, R>(key, buf0, buf1);
 
     // this thread's sorted run: positions e0 .. e0 + m - 1
     const int e0 = tid * R;
