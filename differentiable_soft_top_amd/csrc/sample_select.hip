@@ -318,6 +318,109 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs se)
     }
 }
 
+// ---------------------------------------------------------------------------
+// A heavily repeated value in the band (a cluster of exact ties, such as
+// many scores at one quantised level) makes the band overflow however the
+// bracket is drawn: no bracket around b can leave the tied scores out when
+// b lies among them.  The host then splits the bracket at that value, which
+// puts the whole cluster into one tail.  This kernel finds the candidate:
+// eight values taken from the buffer, each counted over an evenly spread
+// sample of up to 65,536 buffer entries.  Only a heuristic for the next
+// bracket: the certificate of that round decides.
+// ---------------------------------------------------------------------------
+constexpr int kModeThreads = 256;
+constexpr int kModeCands = 8;
+constexpr int kModeSample = 65536;
+
+__global__ __launch_bounds__(kModeThreads) void band_mode_kernel(const float* band, int64_t cap, Status* st)
+{
+    __shared__ uint32_t cnt[kModeThreads / kWave][kModeCands];
+    const int tid = threadIdx.x;
+    const int64_t m = (int64_t)st->nB < cap ? (int64_t)st->nB : cap;
+    float cand[kModeCands];
+#pragma unroll
+    for (int c = 0; c < kModeCands; ++c)
+        cand[c] = m > 0 ? band[(2 * c + 1) * m / (2 * kModeCands)] : 0.0f;
+    const int64_t S = m < kModeSample ? m : kModeSample;
+    uint32_t my[kModeCands];
+#pragma unroll
+    for (int c = 0; c < kModeCands; ++c)
+        my[c] = 0u;
+    for (int64_t j = tid; j < S; j += kModeThreads) {
+        const float v = band[j * m / S];
+#pragma unroll
+        for (int c = 0; c < kModeCands; ++c)
+            my[c] += v == cand[c] ? 1u : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < kModeCands; ++c) {
+        const uint32_t w = wave_sum_u32(my[c]);
+        if (lane_id() == 0)
+            cnt[tid / kWave][c] = w;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t best = 0u;
+        float bv = 0.0f;
+        for (int c = 0; c < kModeCands; ++c) {
+            uint32_t t = 0u;
+            for (int w = 0; w < kModeThreads / kWave; ++w)
+                t += cnt[w][c];
+            if (t > best) {
+                best = t;
+                bv = cand[c];
+            }
+        }
+        st->tie_value = bv;
+        st->tie_count = S > 0 ? (uint32_t)((double)best * (double)m / (double)S) : 0u;
+    }
+}
+
+hipError_t launch_band_mode(const float* band, int64_t cap, Status* st, hipStream_t stream)
+{
+    band_mode_kernel<<<1, kModeThreads, 0, stream>>>(band, cap, st);
+    return hipGetLastError();
+}
+
+__global__ void set_bracket_kernel(Status* st, float aL, float aR)
+{
+    if (threadIdx.x == 0) {
+        st->aL = aL;
+        st->aR = aR;
+        st->select_info = 0u;
+        st->cand_count = 0u;
+        st->lo_key = 0u;
+        st->hi_key = 0u;
+        st->below_n = 0u;
+        st->nB = 0;
+        st->solve_state = kSolveNotRun;
+        st->emit_done = 0;
+        st->nonfinite = 0;
+        st->seg_valid = 0;
+    }
+}
+
+hipError_t launch_set_bracket(Status* st, float aL, float aR, hipStream_t stream)
+{
+    set_bracket_kernel<<<1, kWave, 0, stream>>>(st, aL, aR);
+    return hipGetLastError();
+}
+
+__global__ void set_root_kernel(Status* st, double* out_b, double b)
+{
+    if (threadIdx.x == 0) {
+        st->b = b;
+        *out_b = b;
+        st->solve_state = kSolveOk;
+    }
+}
+
+hipError_t launch_set_root(Status* st, double* out_b, double b, hipStream_t stream)
+{
+    set_root_kernel<<<1, kWave, 0, stream>>>(st, out_b, b);
+    return hipGetLastError();
+}
+
 hipError_t launch_localize(const SampleArgs& sa, const SelectArgs& se, hipStream_t stream)
 {
     STK_LAUNCH(kKFilter, stream, filter_kernel, dim3(se.groups), dim3(kFilterThreads), 0, stream, sa);

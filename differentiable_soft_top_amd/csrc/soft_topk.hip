@@ -596,6 +596,132 @@ bool mass_ok(const Status& h, double k, double tol)
     return h.emit_done && fabs(h.mass - k) <= tol;
 }
 
+// b strictly between the tied value T and the next float T+ (the round
+// above T rejected low, M(T+) < k, and the round below rejected high,
+// M(T) > k): the cluster's weight pins b within one fp32 step of T, inside
+// the gap right of T.  The closed form of the full-sort solver (gist.science
+// summary of Fast LapSum, section 2.2) there, with both sums anchored at T:
+// the left sum A over every score <= T (the cluster included) from the round
+// above T, whose left tail held them; the right sum B over the scores > T
+// from the round below T, whose right tail held the cluster too (its count
+// nR - C is taken off); C the count of scores > T.
+int tie_root(const Ctx& x, float T, float Tp, const Status& above, const Status& below, bool wait_mass, double tol,
+             soft_topk_stats* sx, Status* h, bool* done)
+{
+    const double A = above.SL * exp2(((double)Tp - (double)T) * x.c);
+    const double C = (double)x.n - (double)above.nL;
+    const double B = below.SR - ((double)below.nR - C);
+    if (!(A > 0.0) || !(B > 0.0))
+        return SOFT_TOPK_OK;
+    const double cc = C - x.k;
+    const double r = sqrt(cc * cc + A * B);
+    const double b = cc > 0.0 ? (double)T + x.alpha * log((cc + r) / B) : (double)T - x.alpha * log((-cc + r) / A);
+    if (!(b >= (double)T && b <= (double)Tp))
+        return SOFT_TOPK_OK;
+    STK_HIP(launch_set_root(x.st, x.b, b, x.stream));
+    int rc = enqueue_certify_emit(x, wait_mass);
+    if (rc)
+        return rc;
+    if (wait_mass) {
+        rc = wait_status(1, h);
+        if (rc)
+            return rc;
+        if (!mass_ok(*h, x.k, tol)) {
+            sx->reject_mask |= SOFT_TOPK_REJECT_MASS;
+            return SOFT_TOPK_OK;
+        }
+    }
+    h->b = b;
+    sx->path = SOFT_TOPK_PATH_WIDENED;
+    *done = true;
+    return SOFT_TOPK_OK;
+}
+
+// A band (or a band bucket) too large to sort because one value fills a
+// large part of it: a cluster of exact ties that every bracket around b
+// contains when b lies among them.  Split the bracket at that value T: on
+// [T+, a_R) the whole cluster lies in the left tail, on [a_L, T) in the right
+// tail, and either band holds only the other scores near b.  The side above
+// T is tried first; the certificate of each round decides.  When the first
+// rejects low and the second high, b lies between T and T+ (tie_root).  No
+// dominant value, or any other outcome, leaves the full sort to decide.
+// Uses at most `rounds_left` more rounds.
+int tie_split(const Ctx& x, Status h0, int rounds_left, bool wait_mass, double tol, soft_topk_stats* sx, Status* h,
+              bool* done)
+{
+    STK_HIP(launch_band_mode(at<float>(x, x.plan.off_band), x.plan.cap, x.st, x.stream));
+    int rc = read_status(x, h);
+    if (rc)
+        return rc;
+    const int64_t m = std::min<int64_t>((int64_t)h0.nB, x.plan.cap);
+    if ((int64_t)h->tie_count < std::max<int64_t>(m / 8, 1024))
+        return SOFT_TOPK_OK;
+    const float T = h->tie_value;
+    const float Tp = nextafterf(T, INFINITY);
+    const float br[2][2] = {{Tp, h0.aR > Tp ? h0.aR : INFINITY}, {h0.aL < T ? h0.aL : -INFINITY, T}};
+    Status above;
+    bool above_low = false;
+    for (int i = 0; i < 2 && i < rounds_left; ++i) {
+        STK_HIP(launch_set_bracket(x.st, br[i][0], br[i][1], x.stream));
+        rc = enqueue_pass1(x);
+        if (rc)
+            return rc;
+        rc = enqueue_band_solve(x, false);
+        if (rc)
+            return rc;
+        rc = enqueue_certify_emit(x, wait_mass);
+        if (rc)
+            return rc;
+        rc = wait_solve(x, h);
+        if (rc)
+            return rc;
+        sx->rounds += 1;
+        sx->band_route = SOFT_TOPK_BAND_BUCKETS;
+        sx->a_left = h->aL;
+        sx->a_right = h->aR;
+        sx->n_left = (int64_t)h->nL;
+        sx->n_right = (int64_t)h->nR;
+        sx->n_band = (int64_t)h->nB;
+        sx->mass_at_left = h->massL;
+        sx->mass_at_right = h->massR;
+        if (h->nonfinite)
+            return SOFT_TOPK_ENONFINITE;
+        if (h->solve_state == kSolveOk) {
+            if (wait_mass) {
+                rc = wait_status(1, h);
+                if (rc)
+                    return rc;
+            }
+            if (!wait_mass || mass_ok(*h, x.k, tol)) {
+                sx->path = SOFT_TOPK_PATH_WIDENED;
+                *done = true;
+            } else {
+                sx->reject_mask |= SOFT_TOPK_REJECT_MASS;
+            }
+            return SOFT_TOPK_OK;
+        }
+        if (h->solve_state == kSolveRejectLow) {
+            sx->reject_mask |= SOFT_TOPK_REJECT_LOW;  // b < T+: the side below
+            if (i == 0) {
+                above = *h;
+                above_low = true;
+            }
+            continue;
+        }
+        if (h->solve_state == kSolveRejectHigh) {
+            sx->reject_mask |= SOFT_TOPK_REJECT_HIGH;
+            if (i == 1 && above_low)
+                return tie_root(x, T, Tp, above, *h, wait_mass, tol, sx, h, done);
+        } else if (h->solve_state == kSolveOverflow) {
+            sx->reject_mask |= SOFT_TOPK_REJECT_OVERFLOW;
+        } else if (h->solve_state == kSolveBucketOverflow) {
+            sx->reject_mask |= SOFT_TOPK_REJECT_BUCKET;
+        }
+        return SOFT_TOPK_OK;
+    }
+    return SOFT_TOPK_OK;
+}
+
 }  // namespace
 
 Plan make_plan(int64_t n, int32_t m, int64_t cap)
@@ -908,7 +1034,14 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
                 sx.reject_mask |= SOFT_TOPK_REJECT_OVERFLOW;
             else if (h.solve_state == kSolveBucketOverflow)
                 sx.reject_mask |= SOFT_TOPK_REJECT_BUCKET;
-            break;  // widening cannot help: go to the full sort
+            if ((h.solve_state == kSolveOverflow || h.solve_state == kSolveBucketOverflow) && round < prm.max_widen) {
+                // widening cannot shrink the band; a tied cluster in it can be
+                // split off into a tail
+                rc = tie_split(x, h, prm.max_widen - round, wait_mass, tol, &sx, &h, &done);
+                if (rc)
+                    return rc;
+            }
+            break;  // otherwise the full sort decides
         }
     }
 

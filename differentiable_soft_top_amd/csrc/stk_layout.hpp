@@ -124,6 +124,10 @@ struct alignas(16) Status {
     uint64_t seg_n;
     double seg_alpha;
     uint64_t seg_scores;
+    // the most frequent of a few candidate values in the band buffer, and
+    // its estimated count there (band_mode_kernel, after a band overflow)
+    float tie_value;
+    uint32_t tie_count;
 };
 static_assert(sizeof(Status) <= 256, "status block must fit 256 bytes");
 static_assert(sizeof(Status) % 4 == 0, "status block is copied as 32-bit words");
@@ -236,6 +240,16 @@ struct SelectArgs {
 };
 
 hipError_t launch_localize(const SampleArgs& sa, const SelectArgs& se, hipStream_t stream);
+// After a band or bucket overflow: estimate, from a sample of the band
+// buffer (its first min(nB, cap) entries), the count of the most frequent
+// of eight candidate values taken from it (Status::tie_value, tie_count).
+hipError_t launch_band_mode(const float* band, int64_t cap, Status* st, hipStream_t stream);
+// Start a round on an explicit bracket [aL, aR) (instead of the sampler's):
+// the bracket and the per-round fields the select kernel would set.
+hipError_t launch_set_bracket(Status* st, float aL, float aR, hipStream_t stream);
+// Hand a root found on the host to the emission: b into out_b and the
+// status, and the solve state OK.
+hipError_t launch_set_root(Status* st, double* out_b, double b, hipStream_t stream);
 hipError_t launch_debug_sample(const float* s, int64_t n, float alpha, uint64_t seed, int32_t m,
                                float* out_samples, hipStream_t stream);
 

@@ -150,6 +150,45 @@ def test_forced_full_sort_matches(dev, name, n):
     check_full(res, s_np, k, alpha, g_np)
 
 
+@pytest.mark.parametrize("where", ["above", "below", "pinned"])
+def test_tied_cluster_splits_the_bracket(dev, where):
+    """600,000 of 10^6 scores tied at T = 0.5.  "above" / "below": b lies
+    0.02 alpha above / below T (hundreds of fp32 ulps); the sampled bracket
+    around b holds the cluster, so the band overflows; the bracket is then
+    split at T, the cluster lands in one tail, and that round certifies
+    without the full sort.  "pinned": k is set (by the oracle's M) between
+    M(T+) and M(T), T+ the next float above T, so b lies strictly inside
+    (T, T+): both sides reject and the closed form in the gap right of T
+    gives b.  With no widening rounds allowed, the full sort gives the same
+    b."""
+    n, n_tie, alpha = 1_000_000, 600_000, 1e-3
+    rng = np.random.default_rng(31)
+    s_np = rng.standard_normal(n).astype(np.float32)
+    s_np[:n_tie] = np.float32(0.5)
+    s_np = s_np[rng.permutation(n)]
+    n_above = float(np.count_nonzero(s_np > 0.5))
+    t_up = float(np.nextafter(np.float32(0.5), np.float32(1.0)))
+    if where == "pinned":
+        k = 0.5 * (O.mass(s_np, 0.5, alpha) + O.mass(s_np, t_up, alpha))
+    else:
+        k = n_above + (0.49 if where == "above" else 0.51) * n_tie
+    g_np = rng.standard_normal(n).astype(np.float32)
+    res = run(dev, s_np, k, alpha, g_np)
+    check_full(res, s_np, k, alpha, g_np)
+    st = res["stats"]
+    assert st["path"] == _lib.PATH_WIDENED and st["reject_mask"] & _lib.REJECT_OVERFLOW, st
+    if where == "above":
+        assert st["a_left"] > 0.5, st
+    elif where == "below":
+        assert st["a_right"] == np.float32(0.5), st
+    else:
+        both = _lib.REJECT_LOW | _lib.REJECT_HIGH
+        assert st["reject_mask"] & both == both and 0.5 < res["b"] < t_up, st
+    full = run(dev, s_np, k, alpha, None, params(max_widen=0))
+    assert full["stats"]["path"] == _lib.PATH_FULLSORT, full["stats"]
+    assert abs(full["b"] - res["b"]) <= 2e-5 * alpha
+
+
 def test_route_independence(dev):
     """Different Philox seeds, a too-narrow bracket (forcing rejections and
     widening), an overfull band and the forced full sort all give the same b."""
@@ -556,6 +595,20 @@ def test_segments_nonfinite_cotangent_and_foreign_threshold(dev):
     assert not np.array_equal(_bits(g_seg2), _bits(g_seg))
 
 
+def test_c5_full_sort_fallback(dev):
+    """The clustered workload with no widening rounds allowed skips the tie
+    split: the band overflow sends it to the full device radix sort, which
+    returns the stored oracle b."""
+    gold = GOLD["c5"]
+    s_np, k, alpha, w = make_workload("c5")
+    s = torch.from_numpy(s_np).to(dev)
+    p, b, st = stk.forward(s, k, alpha, params(max_widen=0), want_stats=True)
+    assert st["path"] == _lib.PATH_FULLSORT and st["reject_mask"] & _lib.REJECT_OVERFLOW, st
+    assert abs(float(b.item()) - gold["b"]) <= 1e-5 * alpha
+    m = float(torch.sum(p.double()).item())
+    assert abs(m - k) <= 1e-3 + gold["mass_p32_rounding_floor"], (m, k)
+
+
 # --------------------------------------------------------------------------
 # path coverage: the bracket certifies on its first round for every seed
 # --------------------------------------------------------------------------
@@ -600,7 +653,9 @@ def test_full_size_workload(dev, name):
     b_gpu = float(b.item())
     b_ref = gold["b"]
     assert abs(b_gpu - b_ref) <= 1e-5 * alpha, (b_gpu, b_ref, (b_gpu - b_ref) / alpha)
-    expect = _lib.PATH_FULLSORT if name == "c5" else _lib.PATH_BRACKET
+    # c5: the tied cluster overflows every band; the split at the tied value
+    # brackets it (its own test forces the full sort on the same input)
+    expect = _lib.PATH_WIDENED if name == "c5" else _lib.PATH_BRACKET
     assert st["path"] == expect, st
 
     # sampled p and grad, one by one from the oracle's threshold and sums
