@@ -56,7 +56,8 @@ extern "C" {
 
 /* Route the forward took (soft_topk_stats.path). */
 #define SOFT_TOPK_PATH_BRACKET 1  /* bracket certified on the first pass    */
-#define SOFT_TOPK_PATH_WIDENED 2  /* certified after widening the bracket   */
+#define SOFT_TOPK_PATH_WIDENED 2  /* certified after widening the bracket, or
+                                     after splitting it at a tied value     */
 #define SOFT_TOPK_PATH_FULLSORT 3 /* full device radix sort of all scores   */
 #define SOFT_TOPK_PATH_SINGLE 4   /* n <= 8192: one kernel sorts all scores
                                      in registers and solves them exactly   */
@@ -85,7 +86,10 @@ typedef struct soft_topk_params {
     double z;               /* bracket half-width in binomial standard deviations;
                                ranks use exact binomial tails at Phi(-z) (default 5) */
     int64_t band_capacity;  /* max band elements (0 = default: clamp(n/4, 2^16, 2^22)) */
-    int32_t max_widen;      /* bracket widenings before the full sort (default 2)     */
+    int32_t max_widen;      /* extra bracketed rounds before the full sort: widenings
+                               after a rejected side, and the split of the bracket
+                               at a dominant tied value after a band overflow
+                               (default 2; 0: straight to the full sort)         */
     int32_t force_path;     /* 0 auto (n <= 8192: SOFT_TOPK_PATH_SINGLE, else the
                                bracketed route); SOFT_TOPK_PATH_BRACKET: the
                                bracketed route at every n; SOFT_TOPK_PATH_FULLSORT:
