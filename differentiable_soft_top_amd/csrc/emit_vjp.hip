@@ -36,7 +36,6 @@ __global__ void reset_status_kernel(Status* st, int open_bracket)
         st->nB = 0;
         st->solve_state = kSolveNotRun;
         st->emit_done = 0;
-        st->ticket_radix = 0;
         st->seg_valid = 0;
     }
 }

@@ -5,14 +5,17 @@
 // sort of all n scores on their order-preserving u32 keys, offset by the
 // smallest key so only the digits that vary are sorted (8-bit digits).
 //
-// Per digit, reduce-then-scan with two kernels:
-//   upsweep   -- each work-group histograms the digit of its 8192-key tile;
-//                the last work-group to finish turns the [digit][tile]
-//                histogram into exclusive global offsets;
+// Per digit, reduce-then-scan:
+//   upsweep   -- each work-group histograms the digit of its 8192-key tile
+//                into the [digit][tile] histogram;
+//   rowsum, rowscan -- one work-group per digit value: the row's total,
+//                then the row turned into exclusive global offsets (digit
+//                base from the totals of the smaller digits);
 //   downsweep -- each work-group ranks its tile's keys stably (wave-level
 //                match by eight ballots, wave counts combined in LDS in
-//                (round, wave, lane) order, i.e. index order) and writes
-//                each key to offset[digit][tile] + rank.
+//                (round, wave, lane) order, i.e. index order) into LDS in
+//                destination order, then writes each digit's run to
+//                offset[digit][tile] onwards.
 // Stability of every pass makes the LSD sort correct for any ties (the
 // clustered workload is 60% one value).
 #include "stk_common.hpp"
@@ -63,8 +66,6 @@ template <bool kFromFloat>
 __global__ __launch_bounds__(kRadixThreads) void radix_upsweep(PassArgs a)
 {
     __shared__ uint32_t hist[kRadixBins];
-    __shared__ uint32_t tot[kRadixBins];
-    __shared__ uint32_t is_last;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     for (int i = tid; i < kRadixBins; i += kRadixThreads)
@@ -83,71 +84,133 @@ __global__ __launch_bounds__(kRadixThreads) void radix_upsweep(PassArgs a)
     __syncthreads();
     for (int dgt = tid; dgt < kRadixBins; dgt += kRadixThreads)
         a.hist[(size_t)dgt * a.gp + blockIdx.x] = hist[dgt];
-    __syncthreads();
-    if (tid == 0) {
-        fence_agent();
-        const uint32_t t = atomicAdd(&a.st->ticket_radix, 1u);
-        is_last = t == (uint32_t)(a.g - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!is_last)
-        return;
-    fence_agent();
-
-    // last work-group: thread d owns digit row d of the histogram
-    static_assert(kRadixThreads == kRadixBins, "one thread per digit");
-    const int dgt = tid;
-    uint32_t* row = a.hist + (size_t)dgt * a.gp;
-    uint32_t total = 0;
-    for (int t = 0; t < a.g; t += 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(row + t);
-        total += v.x + (t + 1 < a.g ? v.y : 0u) + (t + 2 < a.g ? v.z : 0u) + (t + 3 < a.g ? v.w : 0u);
-    }
-    tot[dgt] = total;
-    __syncthreads();
-    for (int off = 1; off < kRadixBins; off <<= 1) {
-        const uint32_t v = dgt >= off ? tot[dgt - off] : 0u;
-        __syncthreads();
-        tot[dgt] += v;
-        __syncthreads();
-    }
-    uint32_t run = tot[dgt] - total;  // exclusive digit base
-    for (int t = 0; t < a.g; t += 4) {
-        uint4 v = *reinterpret_cast<const uint4*>(row + t);
-        uint4 o;
-        o.x = run;
-        run += v.x;
-        o.y = run;
-        run += (t + 1 < a.g) ? v.y : 0u;
-        o.z = run;
-        run += (t + 2 < a.g) ? v.z : 0u;
-        o.w = run;
-        run += (t + 3 < a.g) ? v.w : 0u;
-        *reinterpret_cast<uint4*>(row + t) = o;
-    }
-    if (tid == 0)
-        a.st->ticket_radix = 0;
 }
 
+// One work-group per digit: its count over all tiles, into the totals row
+// that follows the [digit][tile] histogram.
+__global__ __launch_bounds__(kRadixThreads) void radix_rowsum(PassArgs a)
+{
+    __shared__ uint32_t red[kRadixThreads / kWave];
+    const int tid = threadIdx.x;
+    const uint32_t* row = a.hist + (size_t)blockIdx.x * a.gp;
+    uint32_t s = 0;
+    for (int t = tid; t < a.g; t += kRadixThreads)
+        s += row[t];
+    s = wave_sum_u32(s);
+    if ((tid & (kWave - 1)) == 0)
+        red[tid / kWave] = s;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t tot = 0;
+        for (int w = 0; w < kRadixThreads / kWave; ++w)
+            tot += red[w];
+        a.hist[(size_t)kRadixBins * a.gp + blockIdx.x] = tot;
+    }
+}
+
+// One work-group per digit: the row's counts become exclusive global offsets
+// (all smaller digits first, then this digit's tiles in order).  Thread t
+// owns a contiguous run of tiles; one work-group scan joins the runs.
+__global__ __launch_bounds__(kRadixThreads) void radix_rowscan(PassArgs a)
+{
+    constexpr int kW = kRadixThreads / kWave;
+    __shared__ uint32_t wsum[kW];
+    __shared__ uint32_t base_sh;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int d = blockIdx.x;
+    const uint32_t* tot = a.hist + (size_t)kRadixBins * a.gp;
+    if (wave == 0) {
+        uint32_t s = 0;
+        for (int j = lane; j < d; j += kWave)
+            s += tot[j];
+        s = wave_sum_u32(s);
+        if (lane == 0)
+            base_sh = s;
+    }
+    uint32_t* row = a.hist + (size_t)d * a.gp;
+    const int per = (a.g + kRadixThreads - 1) / kRadixThreads;
+    const int t0 = tid * per < a.g ? tid * per : a.g;
+    const int t1 = t0 + per < a.g ? t0 + per : a.g;
+    uint32_t mine = 0;
+    for (int t = t0; t < t1; ++t)
+        mine += row[t];
+    uint32_t incl = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off, kWave);
+        if (lane >= off)
+            incl += o;
+    }
+    if (lane == kWave - 1)
+        wsum[wave] = incl;
+    __syncthreads();
+    uint32_t run = base_sh + incl - mine;
+    for (int w = 0; w < wave; ++w)
+        run += wsum[w];
+    for (int t = t0; t < t1; ++t) {
+        const uint32_t v = row[t];
+        row[t] = run;
+        run += v;
+    }
+}
+
+// The tile's keys are ranked stably into LDS in destination order (each
+// digit's run in index order), then written out run by run, so the global
+// stores go to consecutive addresses instead of 256 scattered buckets.  A
+// digit's count in this tile is the step from its offset to the next
+// tile's (or, for the last tile, to the next digit's first offset).
 template <bool kFromFloat>
 __global__ __launch_bounds__(kRadixThreads) void radix_downsweep(PassArgs a)
 {
     constexpr int kWaves = kRadixThreads / kWave;
     __shared__ uint32_t goff[kRadixBins];
+    __shared__ uint32_t lstart[kRadixBins];
     __shared__ uint32_t running[kRadixBins];
     __shared__ uint32_t wcnt[kWaves][kRadixBins];
     __shared__ uint32_t wpre[kWaves][kRadixBins];
+    __shared__ uint32_t stage[kRadixTile];
+    __shared__ uint32_t wsum[kWaves];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    for (int d = tid; d < kRadixBins; d += kRadixThreads) {
-        goff[d] = a.hist[(size_t)d * a.gp + blockIdx.x];
+    const int t = blockIdx.x;
+    static_assert(kRadixThreads == kRadixBins, "one thread per digit");
+    {
+        // this thread's digit: global offset and count in this tile
+        const int d = tid;
+        const uint32_t off = a.hist[(size_t)d * a.gp + t];
+        uint32_t next;
+        if (t + 1 < a.g)
+            next = a.hist[(size_t)d * a.gp + t + 1];
+        else if (d + 1 < kRadixBins)
+            next = a.hist[(size_t)(d + 1) * a.gp];
+        else
+            next = (uint32_t)a.n;
+        const uint32_t cnt = next - off;
+        goff[d] = off;
         running[d] = 0;
         for (int w = 0; w < kWaves; ++w)
             wcnt[w][d] = 0;
+        // exclusive scan of the counts over digits: the runs' starts in LDS
+        uint32_t incl = cnt;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t v = __shfl_up(incl, o, kWave);
+            if (lane >= o)
+                incl += v;
+        }
+        if (lane == kWave - 1)
+            wsum[wave] = incl;
+        __syncthreads();
+        uint32_t ex = incl - cnt;
+        for (int w = 0; w < wave; ++w)
+            ex += wsum[w];
+        lstart[d] = ex;
     }
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kRadixTile;
+    const int64_t base = (int64_t)t * kRadixTile;
     for (int r = 0; r < kRadixKeysPerThread; ++r) {
         const int64_t i = base + (int64_t)r * kRadixThreads + tid;
         const bool valid = i < a.n;
@@ -170,7 +233,15 @@ __global__ __launch_bounds__(kRadixThreads) void radix_downsweep(PassArgs a)
         }
         __syncthreads();
         if (valid)
-            a.out[goff[d] + wpre[wave][d] + rank] = key;
+            stage[lstart[d] + wpre[wave][d] + rank] = key;
+    }
+    __syncthreads();
+    const int64_t left = a.n - base;
+    const int cnt = left < (int64_t)kRadixTile ? (int)left : kRadixTile;
+    for (int j = tid; j < cnt; j += kRadixThreads) {
+        const uint32_t key = stage[j];
+        const uint32_t d = (key >> a.shift) & 0xFFu;
+        a.out[goff[d] + (uint32_t)j - lstart[d]] = key;
     }
 }
 
@@ -191,9 +262,14 @@ hipError_t launch_radix_sort(const RadixArgs& ra, hipStream_t stream)
         a.out = bufs[p & 1];
         if (p == 0) {
             STK_LAUNCH(kKRadixUp, stream, radix_upsweep<true>, dim3(a.g), dim3(kRadixThreads), 0, stream, a);
-            STK_LAUNCH(kKRadixDown, stream, radix_downsweep<true>, dim3(a.g), dim3(kRadixThreads), 0, stream, a);
         } else {
             STK_LAUNCH(kKRadixUp, stream, radix_upsweep<false>, dim3(a.g), dim3(kRadixThreads), 0, stream, a);
+        }
+        STK_LAUNCH(kKRadixScan, stream, radix_rowsum, dim3(kRadixBins), dim3(kRadixThreads), 0, stream, a);
+        STK_LAUNCH(kKRadixScan, stream, radix_rowscan, dim3(kRadixBins), dim3(kRadixThreads), 0, stream, a);
+        if (p == 0) {
+            STK_LAUNCH(kKRadixDown, stream, radix_downsweep<true>, dim3(a.g), dim3(kRadixThreads), 0, stream, a);
+        } else {
             STK_LAUNCH(kKRadixDown, stream, radix_downsweep<false>, dim3(a.g), dim3(kRadixThreads), 0, stream, a);
         }
         const hipError_t e = hipGetLastError();
