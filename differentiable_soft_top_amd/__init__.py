@@ -18,8 +18,8 @@ import ctypes
 from . import _lib
 from ._lib import Params, SoftTopKError, Stats  # noqa: F401
 
-__all__ = ["soft_topk", "forward", "backward", "rows_forward", "rows_backward", "Params", "Stats", "SoftTopKError",
-           "default_params"]
+__all__ = ["soft_topk", "forward", "backward", "rows_forward", "rows_backward", "threshold_curve", "Params", "Stats",
+           "SoftTopKError", "default_params"]
 
 
 def default_params() -> Params:
@@ -97,6 +97,26 @@ def _check_rows(s):
         raise TypeError("scores must be a contiguous 2-D float32 tensor (rows x n_row)")
     if s.device.type != "cuda":
         raise TypeError("scores must live on a ROCm device")
+
+
+def threshold_curve(s, alpha: float):
+    """soft_topk_threshold_curve: returns (sorted scores fp32, mass fp64), mass[j] being the k that the
+    threshold b = sorted[j] selects (non-increasing)."""
+    import torch
+    _check_scores(s)
+    lib = _lib.load()
+    n = s.numel()
+    ws_bytes = lib.soft_topk_workspace_bytes(n, None)
+    if ws_bytes == 0:
+        raise SoftTopKError(_lib.EINVAL, "invalid size (n=%d)" % n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=s.device)
+    xs = torch.empty_like(s)
+    mass = torch.empty(n, dtype=torch.float64, device=s.device)
+    rc = lib.soft_topk_threshold_curve(ctypes.c_void_p(s.data_ptr()), n, float(alpha), ctypes.c_void_p(xs.data_ptr()),
+                                       ctypes.c_void_p(mass.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws_bytes,
+                                       _stream_handle(s))
+    _lib.check(rc, "soft_topk_threshold_curve")
+    return xs, mass
 
 
 def rows_forward(s, k: float, alpha: float, out_p=None):

@@ -92,6 +92,8 @@ def load():
     lib.soft_topk_rows_forward.restype = ctypes.c_int
     lib.soft_topk_rows_backward.argtypes = [fp, fp, i64, i64, dbl, dp, fp, vp, sz, vp]
     lib.soft_topk_rows_backward.restype = ctypes.c_int
+    lib.soft_topk_threshold_curve.argtypes = [fp, i64, dbl, fp, dp, vp, sz, vp]
+    lib.soft_topk_threshold_curve.restype = ctypes.c_int
     lib.soft_topk_rows_workspace_bytes.argtypes = [i64, i64]
     lib.soft_topk_rows_workspace_bytes.restype = sz
     lib.soft_topk_strerror.argtypes = [ctypes.c_int]

@@ -13,8 +13,8 @@ namespace {
 
 const char* const kNames[kKernelCount] = {
     "sample", "filter", "select", "pass1", "band_hist", "band_scatter", "bucket_agg", "solve",
-    "radix_upsweep", "radix_downsweep", "tile_agg", "emit", "emit_finalize", "vjp_reduce", "vjp_apply", "reset",
-    "rows_forward", "rows_backward",
+    "radix_upsweep", "radix_downsweep", "radix_scan", "tile_agg", "emit", "emit_finalize", "vjp_reduce", "vjp_apply", "reset",
+    "rows_forward", "rows_backward", "curve_scan", "curve",
 };
 
 struct Pair {

@@ -527,7 +527,9 @@ int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q, bool direct)
     return enqueue_band_solve(x, direct);
 }
 
-int enqueue_fullsort(const Ctx& x, const Status& range)
+// Radix sort of all scores and summaries of 4096-score tiles of the sorted
+// values (which replace the keys in place).  Returns the sorted values.
+int enqueue_sorted_tiles(const Ctx& x, const Status& range, const float** sorted_values)
 {
     // sort only the key bits that vary between the smallest and largest score
     const uint32_t kmin = host_key(range.smin);
@@ -557,12 +559,22 @@ int enqueue_fullsort(const Ctx& x, const Status& range)
     ta.n_tiles = x.plan.n_tiles;
     ta.log2e_over_alpha = x.c;
     STK_HIP(launch_tile_aggregates(ta, x.stream));
+    *sorted_values = reinterpret_cast<const float*>(sorted);
+    return SOFT_TOPK_OK;
+}
+
+int enqueue_fullsort(const Ctx& x, const Status& range)
+{
+    const float* sorted = nullptr;
+    int rc = enqueue_sorted_tiles(x, range, &sorted);
+    if (rc)
+        return rc;
     SolveArgs so;
     so.p1 = nullptr;
     so.p1_blocks = 0;
     so.p1_super = nullptr;
-    so.sorted = reinterpret_cast<const float*>(sorted);
-    so.agg = ta.agg;
+    so.sorted = sorted;
+    so.agg = at<GroupAgg>(x, x.plan.off_agg);
     so.scan = at<GroupScan>(x, x.plan.off_scan);
     so.groups = x.plan.n_tiles;
     so.tails = 0;
@@ -768,7 +780,8 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     p.off_keys1 = o;
     o = align_up(o + sizeof(uint32_t) * (size_t)n);
     p.off_rhist = o;
-    o = align_up(o + sizeof(uint32_t) * kRadixBins * (size_t)((p.g_radix + 3) & ~3));
+    // [digit][tile] histogram, then one total per digit
+    o = align_up(o + sizeof(uint32_t) * kRadixBins * ((size_t)((p.g_radix + 3) & ~3) + 1));
     p.off_super = o;
     o = align_up(o + sizeof(Pass1Partial) * (size_t)kBuckets);
     p.total = o;
@@ -1079,6 +1092,62 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
     sx.mass = wait_mass ? h.mass : NAN;
     if (stats)
         *stats = sx;
+    return SOFT_TOPK_OK;
+}
+
+int soft_topk_threshold_curve(const float* scores, int64_t n, double alpha, float* out_sorted, double* out_mass,
+                              void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!scores || !out_sorted || !out_mass || !n_ok(n))
+        return SOFT_TOPK_EINVAL;
+    if (!(alpha > 0.0) || !isfinite(alpha))
+        return SOFT_TOPK_EINVAL;
+    const soft_topk_params prm = resolve(nullptr);
+    const Plan plan = plan_for(n, prm);
+    if (!workspace || workspace_bytes < plan.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return SOFT_TOPK_EWORKSPACE;
+    Ctx x;
+    memset(&x, 0, sizeof(x));
+    x.s = scores;
+    x.n = n;
+    x.alpha = alpha;
+    x.c = kLog2e / alpha;
+    x.ws = static_cast<char*>(workspace);
+    x.plan = plan;
+    x.stream = static_cast<hipStream_t>(stream);
+    x.st = reinterpret_cast<Status*>(x.ws + plan.off_status);
+    int rc = ensure_host_slots();
+    if (rc)
+        return rc;
+    x.mirror0 = mirror_slot(0);
+    x.mirror1 = mirror_slot(1);
+    if (!x.mirror0 || !x.mirror1)
+        return SOFT_TOPK_EHIP;
+    // score range (and finiteness), the radix sort, tile summaries, then
+    // the masses
+    Status h;
+    STK_HIP(launch_reset_status(x.st, x.stream, false));
+    STK_HIP(launch_range(x.s, n, at<Pass1Partial>(x, plan.off_p1part), plan.g_pass1, x.stream));
+    STK_HIP(launch_pass1_finalize(at<Pass1Partial>(x, plan.off_p1part), plan.g_pass1, x.st, x.stream));
+    rc = read_status(x, &h);
+    if (rc)
+        return rc;
+    if (h.nonfinite)
+        return SOFT_TOPK_ENONFINITE;
+    const float* sorted = nullptr;
+    rc = enqueue_sorted_tiles(x, h, &sorted);
+    if (rc)
+        return rc;
+    CurveArgs ca;
+    ca.sorted = sorted;
+    ca.agg = at<GroupAgg>(x, plan.off_agg);
+    ca.ex = x.ws + plan.off_scan;
+    ca.n = n;
+    ca.n_tiles = plan.n_tiles;
+    ca.log2e_over_alpha = x.c;
+    ca.out_sorted = out_sorted;
+    ca.out_mass = out_mass;
+    STK_HIP(launch_curve(ca, x.stream));
     return SOFT_TOPK_OK;
 }
 

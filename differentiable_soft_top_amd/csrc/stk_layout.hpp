@@ -114,9 +114,6 @@ struct alignas(16) Status {
     double mass;                 // fp64 sum of p over all n
     uint32_t emit_done;
     uint32_t pad3;
-    // "last work-group" ticket; zeroed before the kernel that uses it and
-    // returned to zero by the work-group that consumes it
-    uint32_t ticket_radix;       // radix upsweep work-groups done (returned to 0 by the last)
     // saturated-score segments recorded by this forward's emission (cleared by
     // the select kernel and the full-sort reset), and what they were taken
     // from: the VJP uses them only for the same scores, n and alpha (and b)
@@ -389,6 +386,21 @@ hipError_t launch_rows(const RowsArgs& a, bool forward, hipStream_t stream);
 // One row (rows == 1, n_row <= kRowMax) with the shortest chain per thread:
 // the single-vector route, where latency matters rather than throughput.
 hipError_t launch_row_alone(const RowsArgs& a, bool forward, hipStream_t stream);
+
+// The threshold curve: every score in ascending order with the mass
+// M(x_j) = sum_i F((s_i - x_j)/alpha) it would select as threshold, from the
+// full-sort route's sorted values and tile summaries.
+struct CurveArgs {
+    const float* sorted;          // ascending values (the full sort's output)
+    const GroupAgg* agg;          // [n_tiles] tile summaries
+    void* ex;                     // [n_tiles] scratch: sums before / after each tile
+    int64_t n;
+    int32_t n_tiles;
+    double log2e_over_alpha;
+    float* out_sorted;
+    double* out_mass;
+};
+hipError_t launch_curve(const CurveArgs& a, hipStream_t stream);
 
 // A single vector of at most kRowMax scores solved by the row kernels: one
 // work-group folds the fp64 sum of the emitted p, writes a fresh status

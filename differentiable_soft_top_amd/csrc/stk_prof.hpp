@@ -21,6 +21,7 @@ enum KernelId : int {
     kKSolve,
     kKRadixUp,
     kKRadixDown,
+    kKRadixScan,
     kKTileAgg,
     kKEmit,
     kKEmitFinal,
@@ -29,6 +30,8 @@ enum KernelId : int {
     kKReset,
     kKRowsForward,
     kKRowsBackward,
+    kKCurveScan,
+    kKCurve,
     kKernelCount
 };
 

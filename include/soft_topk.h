@@ -257,6 +257,27 @@ int soft_topk_rows_backward(const float* grad_p, const float* scores, int64_t ro
  * (none needed) and for invalid sizes (the calls then return EINVAL). */
 size_t soft_topk_rows_workspace_bytes(int64_t rows, int64_t n_row);
 
+/*
+ * Threshold curve.  The gist.science summary of Fast LapSum (section 2.2,
+ * "Full-Sort Solver") reads the root off the masses at the sorted scores;
+ * this call returns them.  scores: fp32[n] (device); alpha > 0, finite.
+ * out_sorted: fp32[n] (device), the scores in ascending order (-0 returned
+ * as +0: the sort keys equal values alike).  out_mass:
+ * fp64[n] (device), out_mass[j] = sum_i F((scores[i] - out_sorted[j])/alpha),
+ * the k that the threshold b = out_sorted[j] selects (non-increasing in j;
+ * for any 0 < k < n the forward's b lies in the gap where it crosses k).
+ * workspace: soft_topk_workspace_bytes(n, NULL) bytes (the forward's size),
+ * 256-byte aligned.  Route: the full device radix sort, summaries of
+ * 4096-score tiles, then the anchored prefix/suffix sums of every value.
+ * Synchronisation: one 256-byte status read-back (the score range, which
+ * decides the radix passes); the rest is enqueued on `stream`.
+ * Errors: EINVAL / EWORKSPACE before any launch; ENONFINITE if a score is not
+ * finite (the outputs then hold no result); EHIP on a HIP failure.
+ */
+int soft_topk_threshold_curve(const float* scores, int64_t n, double alpha, float* out_sorted,
+                              double* out_mass, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Text for a return code. */
 const char* soft_topk_strerror(int code);
 

@@ -1,0 +1,84 @@
+"""GPU parity of the threshold curve (soft_topk_threshold_curve): the sorted
+scores and the mass M(x_j) = sum_i F((s_i - x_j)/alpha) at every one of them,
+against the fp64 oracle's mass function evaluated at the same points.
+
+The sorted scores must equal a host sort (by value, with the same bit
+patterns).  Masses are fp64 sums of fp64 exponentials on both sides; they
+must agree to 1e-7 absolute (far inside the 1e-3 mass bar of the forward)
+plus 1e-11 n for the order in which the two sides add n terms, be
+non-increasing, and bracket the forward's b: b lies in the gap where the
+curve crosses k.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import differentiable_soft_top_amd as stk  # noqa: E402
+from differentiable_soft_top_amd import _lib  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    return torch.device("cuda:0")
+
+
+def same_values(xs, s_np):
+    """xs is s sorted: ascending by value, with the same bit patterns as s
+    except that -0 comes back as +0 (the sort keys equal values alike)."""
+    assert np.array_equal(xs, np.sort(s_np))
+    canon = (s_np + np.float32(0.0)).view(np.uint32)
+    assert np.array_equal(np.sort(xs.view(np.uint32)), np.sort(canon))
+
+
+def curve(dev, s_np, alpha):
+    xs, m = stk.threshold_curve(torch.from_numpy(s_np).to(dev), alpha)
+    torch.cuda.synchronize()
+    return xs.cpu().numpy(), m.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,alpha", [(1, 0.1), (2, 0.5), (777, 0.05), (4096, 0.1), (4097, 1e-4), (12289, 0.02)])
+def test_curve_matches_oracle_everywhere(dev, n, alpha):
+    rng = np.random.default_rng(n)
+    s_np = rng.standard_normal(n).astype(np.float32)
+    s_np[: n // 4] = np.round(s_np[: n // 4] * 8.0) / 8.0  # ties
+    xs, m = curve(dev, s_np, alpha)
+    same_values(xs, s_np)
+    ref = np.array([O.mass(s_np, float(x), alpha) for x in xs])
+    assert np.max(np.abs(m - ref)) <= 1e-7 + 1e-11 * n, np.max(np.abs(m - ref))
+    assert np.all(np.diff(m) <= 1e-9)
+
+
+def test_curve_large_sampled_and_brackets_the_forward(dev):
+    n, alpha = 1_000_003, 0.05
+    rng = np.random.default_rng(5)
+    s_np = (0.5 * rng.standard_t(3, n)).astype(np.float32)
+    xs, m = curve(dev, s_np, alpha)
+    same_values(xs, s_np)
+    assert np.all(np.diff(m) <= 1e-9)
+    idx = np.concatenate([[0, n - 1], rng.integers(0, n, 150)])
+    for j in idx:
+        assert abs(m[j] - O.mass(s_np, float(xs[j]), alpha)) <= 1e-7 + 1e-11 * n, j
+    for k in (0.5, 1000.0, n / 3.0, n - 2.5):
+        _, b = stk.forward(torch.from_numpy(s_np).to(dev), k, alpha)
+        b = float(b.item())
+        j = int(np.searchsorted(-m, -k, side="right")) - 1  # last j with m[j] >= k
+        lo = xs[j] if j >= 0 else -np.inf
+        hi = xs[j + 1] if j + 1 < n else np.inf
+        assert lo - 1e-6 * alpha <= b <= hi + 1e-6 * alpha, (k, j, lo, b, hi)
+
+
+def test_curve_rejects_nonfinite_and_bad_arguments(dev):
+    s_np = np.random.default_rng(1).standard_normal(5000).astype(np.float32)
+    s_np[17] = np.nan
+    with pytest.raises(stk.SoftTopKError) as e:
+        stk.threshold_curve(torch.from_numpy(s_np).to(dev), 0.1)
+    assert e.value.code == _lib.ENONFINITE
+    with pytest.raises(stk.SoftTopKError) as e:
+        stk.threshold_curve(torch.zeros(10, device=dev), 0.0)
+    assert e.value.code == _lib.EINVAL
