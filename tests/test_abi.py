@@ -82,6 +82,38 @@ def test_backward_rejects_bad_arguments_before_launch(lib):
     assert lib.soft_topk_backward(fake, fake, 10, 0.1, fake, fake, fake, 1, None) == _lib.EWORKSPACE
 
 
+def test_threshold_curve_rejects_bad_arguments_before_launch(lib):
+    fake = ctypes.c_void_p(0x1000)
+
+    def curve(s=fake, n=100, alpha=0.1, xs=fake, m=fake, w=None, wb=0):
+        return lib.soft_topk_threshold_curve(s, n, alpha, xs, m, w, wb, None)
+
+    assert curve(n=0) == _lib.EINVAL
+    assert curve(n=-5) == _lib.EINVAL
+    assert curve(alpha=0.0) == _lib.EINVAL
+    assert curve(alpha=float("inf")) == _lib.EINVAL
+    assert curve(s=None) == _lib.EINVAL
+    assert curve(xs=None) == _lib.EINVAL
+    assert curve(m=None) == _lib.EINVAL
+    # the forward's workspace size, 256-byte aligned
+    assert curve() == _lib.EWORKSPACE
+    need = lib.soft_topk_workspace_bytes(100, None)
+    assert curve(w=ctypes.c_void_p(0x1001), wb=need) == _lib.EWORKSPACE
+    assert curve(w=fake, wb=need - 1) == _lib.EWORKSPACE
+
+
+def test_force_path_values(lib):
+    p = _lib.Params()
+    lib.soft_topk_default_params(ctypes.byref(p))
+    fake = ctypes.c_void_p(0x1000)
+    for v, ok in [(0, True), (_lib.PATH_BRACKET, True), (_lib.PATH_FULLSORT, True), (_lib.PATH_WIDENED, False),
+                  (_lib.PATH_SINGLE, False), (7, False)]:
+        p.force_path = v
+        # a valid params block gets as far as the workspace check (none given)
+        rc = lib.soft_topk_forward_ex(fake, 100, 5.0, 0.1, fake, fake, None, 0, None, ctypes.byref(p), None)
+        assert rc == (_lib.EWORKSPACE if ok else _lib.EINVAL), (v, rc)
+
+
 def test_rows_reject_bad_arguments_before_launch(lib):
     fake = ctypes.c_void_p(0x1000)
 
