@@ -320,7 +320,7 @@ def main():
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
         return
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (the operator is single-device); "
+        print("bench.py: the benchmark runs on one GPU only (the operator is single-device); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
