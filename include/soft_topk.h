@@ -20,9 +20,10 @@
  * scores outside it into tail counts and exponential sums and keeps the band
  * inside it; the band alone is sorted and solved in closed form (section 2.2
  * "Full-Sort Solver"); the bracket is certified exactly, widened when the
- * certificate fails, and a full device radix sort covers the worst case.
- * The returned b is the exact root (up to fp64 rounding) whichever route is
- * taken.
+ * certificate fails, split at a tied value that floods the band, and a full
+ * device radix sort covers the worst case.  Vectors of at most 8192 scores
+ * are instead sorted and solved whole by one kernel.  The returned b is the
+ * exact root (up to fp64 rounding) whichever route is taken.
  *
  * Conventions shared by every entry point:
  *  - Array pointers (scores, grad_p, out_p, grad_s, b, workspace) are DEVICE
