@@ -240,7 +240,7 @@ __device__ __forceinline__ void solve_ref(const float (&x)[R], int e0, int m, fl
     ref_exp(x[0], xr, c, e, ei);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        double en = 0.0, ein;
+        double en = 0.0, ein = 0.0;
         if (r + 1 < R)
             ref_exp(x[r + 1], xr, c, en, ein);
         else if (e0 + R < n)
@@ -650,7 +650,7 @@ __device__ __forceinline__ RowGap group_gap_ref(const float (&x)[R], int gl, int
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         // E of the next point: this run's next, or the next run's first
-        double en = 0.0, ein;
+        double en = 0.0, ein = 0.0;
         if (r + 1 < R)
             ref_exp(x[r + 1], xr, c, en, ein);
         else if (e0 + R < n)

@@ -30,7 +30,6 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 thread_local int g_last_hip = 0;
-thread_local Status* g_pinned = nullptr;
 
 int hip_fail(hipError_t e)
 {

@@ -163,7 +163,7 @@ __device__ __forceinline__ double mass_at(float x, double Pv, double C, Anch S, 
 }
 
 // Root of A v/2 + C - B w/2 = k on [xlo, xhi] (an empty end has v = 0).
-__device__ double gap_root(Anch lo, Anch hi, double C, double k, double alpha, double c)
+__device__ inline double gap_root(Anch lo, Anch hi, double C, double k, double alpha, double c)
 {
     const double cc = C - k;
     const double xlo = lo.x, xhi = hi.x;
