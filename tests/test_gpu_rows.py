@@ -183,3 +183,20 @@ def test_rows_mixed_sum_forms_in_one_wave(dev):
         for k in (0.5, n_row / 3.0, n_row - 0.5):
             p, b, grad = run_rows(dev, s_np, k, 0.1, g_np)
             check_rows(s_np, k, 0.1, g_np, p, b, grad)
+
+
+@pytest.mark.parametrize("name", ["r1", "r2"])
+def test_bench_row_workloads_sampled(dev, name):
+    """The two batched-row workloads the benchmark times, at full size and
+    through the same calls: 40 sampled rows against the oracle (every bar),
+    and every row's mass within 1e-3 of k (the host's fp64 sum of the
+    emitted p of each row)."""
+    from differentiable_soft_top_amd.workloads import draw_grad, make_row_workload
+
+    s_np, k, alpha, w = make_row_workload(name)
+    g_np = draw_grad(s_np.size, w.seed).reshape(s_np.shape)
+    p, b, grad = run_rows(dev, s_np, k, alpha, g_np)
+    rows = np.random.default_rng(7).choice(s_np.shape[0], 40, replace=False)
+    check_rows(s_np[rows], k, alpha, g_np[rows], p[rows], b[rows], grad[rows])
+    mass = p.sum(axis=1)
+    assert np.max(np.abs(mass - k)) <= 1e-3, np.max(np.abs(mass - k))
