@@ -82,3 +82,24 @@ def test_curve_rejects_nonfinite_and_bad_arguments(dev):
     with pytest.raises(stk.SoftTopKError) as e:
         stk.threshold_curve(torch.zeros(10, device=dev), 0.0)
     assert e.value.code == _lib.EINVAL
+
+
+def test_curve_clustered_scores(dev):
+    """60% of the scores tied at one value (a block of equal values spanning
+    many 4096-value tiles), the rest N(0,1) and a far cluster: every tied
+    point gets the same mass (to rounding), and sampled points, the tie
+    included, match the oracle."""
+    from differentiable_soft_top_amd.workloads import make_workload
+
+    s_np, _, alpha, _ = make_workload("c5", n=300_000)
+    n = s_np.size
+    xs, m = curve(dev, s_np, alpha)
+    same_values(xs, s_np)
+    assert np.all(np.diff(m) <= 1e-9)
+    tie = np.flatnonzero(xs == np.float32(0.5))
+    # equal points, equal mass (each position adds its sums in its own
+    # order: equal to rounding)
+    assert tie.size > 100_000 and np.ptp(m[tie]) <= 1e-7 + 1e-11 * n, np.ptp(m[tie])
+    rng = np.random.default_rng(3)
+    for j in np.concatenate([tie[[0, -1]], [tie[0] - 1, tie[-1] + 1], rng.integers(0, n, 60)]):
+        assert abs(m[j] - O.mass(s_np, float(xs[j]), alpha)) <= 1e-7 + 1e-11 * n, j
