@@ -817,9 +817,13 @@ __global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(4
     }
 }
 
-template <int G, int R>
+// kVec: rows of a multiple of 4 scores on 16-byte aligned vectors; each lane
+// then moves whole float4s (lane gl holds float4s u * G + gl), which halves
+// the memory instructions; the sums only change order.
+template <int G, int R, bool kVec>
 __global__ __launch_bounds__(kGroupThreads) void rows_group_backward_kernel(RowsArgs a)
 {
+    static_assert(!kVec || R % 4 == 0, "whole float4s per lane");
     const int gl = lane_id() & (G - 1);
     const int64_t row = (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G;
     const bool live = row < a.rows;
@@ -829,12 +833,32 @@ __global__ __launch_bounds__(kGroupThreads) void rows_group_backward_kernel(Rows
     const float* g = a.g + row * (int64_t)n;
     const double b = live ? a.b_in[row] : 0.0;
     float dv[R], gv[R];
+    if (kVec) {
+        const float4* s4 = reinterpret_cast<const float4*>(s);
+        const float4* g4 = reinterpret_cast<const float4*>(g);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int i = r * G + gl;
-        const bool in = live && i < n;
-        gv[r] = in ? g[i] : 0.0f;
-        dv[r] = in ? row_d(s[i], b, c) : 0.0f;
+        for (int u = 0; u < R / 4; ++u) {
+            const int q = u * G + gl;
+            const bool in = live && 4 * q < n;
+            const float4 sq = in ? s4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 gq = in ? g4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            gv[4 * u + 0] = gq.x;
+            gv[4 * u + 1] = gq.y;
+            gv[4 * u + 2] = gq.z;
+            gv[4 * u + 3] = gq.w;
+            dv[4 * u + 0] = in ? row_d(sq.x, b, c) : 0.0f;
+            dv[4 * u + 1] = in ? row_d(sq.y, b, c) : 0.0f;
+            dv[4 * u + 2] = in ? row_d(sq.z, b, c) : 0.0f;
+            dv[4 * u + 3] = in ? row_d(sq.w, b, c) : 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = r * G + gl;
+            const bool in = live && i < n;
+            gv[r] = in ? g[i] : 0.0f;
+            dv[r] = in ? row_d(s[i], b, c) : 0.0f;
+        }
     }
     double D = 0.0, Gs = 0.0;
 #pragma unroll
@@ -847,11 +871,24 @@ __global__ __launch_bounds__(kGroupThreads) void rows_group_backward_kernel(Rows
     const Ratio2 ratio = split_ratio(D > 0.0 ? Gs / D : 0.0);
     const float inv_alpha = (float)(1.0 / a.alpha);
     float* out = a.grad + row * (int64_t)n;
+    if (kVec) {
+        float4* o4 = reinterpret_cast<float4*>(out);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int i = r * G + gl;
-        if (i < n)
-            out[i] = dv[r] * inv_alpha * minus_ratio(gv[r], ratio);
+        for (int u = 0; u < R / 4; ++u) {
+            const int q = u * G + gl;
+            if (4 * q < n)
+                o4[q] = make_float4(dv[4 * u + 0] * inv_alpha * minus_ratio(gv[4 * u + 0], ratio),
+                                    dv[4 * u + 1] * inv_alpha * minus_ratio(gv[4 * u + 1], ratio),
+                                    dv[4 * u + 2] * inv_alpha * minus_ratio(gv[4 * u + 2], ratio),
+                                    dv[4 * u + 3] * inv_alpha * minus_ratio(gv[4 * u + 3], ratio));
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = r * G + gl;
+            if (i < n)
+                out[i] = dv[r] * inv_alpha * minus_ratio(gv[r], ratio);
+        }
     }
 }
 
@@ -872,11 +909,17 @@ hipError_t launch_group_t(const RowsArgs& a, bool forward, hipStream_t stream)
 {
     constexpr int kRows = kGroupThreads / G;
     const dim3 grid((uint32_t)((a.rows + kRows - 1) / kRows));
+    const bool vec = (a.n_row % 4) == 0 &&
+                     ((reinterpret_cast<uintptr_t>(a.s) | reinterpret_cast<uintptr_t>(a.g) |
+                       reinterpret_cast<uintptr_t>(a.grad)) & 15u) == 0;
     if (forward)
         STK_LAUNCH(kKRowsForward, stream, (rows_group_forward_kernel<G, R>), grid, dim3(kGroupThreads), 0, stream, a);
+    else if (vec)
+        STK_LAUNCH(kKRowsBackward, stream, (rows_group_backward_kernel<G, R, true>), grid, dim3(kGroupThreads), 0,
+                   stream, a);
     else
-        STK_LAUNCH(kKRowsBackward, stream, (rows_group_backward_kernel<G, R>), grid, dim3(kGroupThreads), 0, stream,
-                   a);
+        STK_LAUNCH(kKRowsBackward, stream, (rows_group_backward_kernel<G, R, false>), grid, dim3(kGroupThreads), 0,
+                   stream, a);
     return hipGetLastError();
 }
 
