@@ -437,9 +437,13 @@ __global__ __launch_bounds__(kT) void rows_forward_kernel(RowsArgs a)
     }
 }
 
-template <int kT, int R>
+// kVec: as in the lane-group backward, whole float4s per thread (thread t
+// holds float4s u * kT + t) for rows of a multiple of 4 scores on aligned
+// vectors.
+template <int kT, int R, bool kVec>
 __global__ __launch_bounds__(kT) void rows_backward_kernel(RowsArgs a)
 {
+    static_assert(!kVec || R % 4 == 0, "whole float4s per thread");
     constexpr int kW = kT / kWave;
     __shared__ double red[2][kW];
     const int tid = threadIdx.x;
@@ -453,12 +457,32 @@ __global__ __launch_bounds__(kT) void rows_backward_kernel(RowsArgs a)
     const double b = a.b_in[row];
     float dv[R], gv[R];
     double D = 0.0, G = 0.0;
+    if (kVec) {
+        const float4* s4 = reinterpret_cast<const float4*>(s);
+        const float4* g4 = reinterpret_cast<const float4*>(g);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int i = r * kT + tid;
-        const bool in = i < n;
-        gv[r] = in ? g[i] : 0.0f;
-        dv[r] = in ? row_d(s[i], b, c) : 0.0f;
+        for (int u = 0; u < R / 4; ++u) {
+            const int q = u * kT + tid;
+            const bool in = 4 * q < n;
+            const float4 sq = in ? s4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 gq = in ? g4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            gv[4 * u + 0] = gq.x;
+            gv[4 * u + 1] = gq.y;
+            gv[4 * u + 2] = gq.z;
+            gv[4 * u + 3] = gq.w;
+            dv[4 * u + 0] = in ? row_d(sq.x, b, c) : 0.0f;
+            dv[4 * u + 1] = in ? row_d(sq.y, b, c) : 0.0f;
+            dv[4 * u + 2] = in ? row_d(sq.z, b, c) : 0.0f;
+            dv[4 * u + 3] = in ? row_d(sq.w, b, c) : 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = r * kT + tid;
+            const bool in = i < n;
+            gv[r] = in ? g[i] : 0.0f;
+            dv[r] = in ? row_d(s[i], b, c) : 0.0f;
+        }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -479,11 +503,24 @@ __global__ __launch_bounds__(kT) void rows_backward_kernel(RowsArgs a)
     const Ratio2 ratio = split_ratio(D > 0.0 ? G / D : 0.0);
     const float inv_alpha = (float)(1.0 / a.alpha);
     float* out = a.grad + row * (int64_t)n;
+    if (kVec) {
+        float4* o4 = reinterpret_cast<float4*>(out);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int i = r * kT + tid;
-        if (i < n)
-            out[i] = dv[r] * inv_alpha * minus_ratio(gv[r], ratio);
+        for (int u = 0; u < R / 4; ++u) {
+            const int q = u * kT + tid;
+            if (4 * q < n)
+                o4[q] = make_float4(dv[4 * u + 0] * inv_alpha * minus_ratio(gv[4 * u + 0], ratio),
+                                    dv[4 * u + 1] * inv_alpha * minus_ratio(gv[4 * u + 1], ratio),
+                                    dv[4 * u + 2] * inv_alpha * minus_ratio(gv[4 * u + 2], ratio),
+                                    dv[4 * u + 3] * inv_alpha * minus_ratio(gv[4 * u + 3], ratio));
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = r * kT + tid;
+            if (i < n)
+                out[i] = dv[r] * inv_alpha * minus_ratio(gv[r], ratio);
+        }
     }
 }
 
@@ -897,10 +934,17 @@ namespace {
 template <int kT, int R>
 hipError_t launch_rows_t(const RowsArgs& a, bool forward, hipStream_t stream)
 {
+    constexpr bool kCanVec = R % 4 == 0;
+    const bool vec = kCanVec && (a.n_row % 4) == 0 &&
+                     ((reinterpret_cast<uintptr_t>(a.s) | reinterpret_cast<uintptr_t>(a.g) |
+                       reinterpret_cast<uintptr_t>(a.grad)) & 15u) == 0;
+    const dim3 grid((uint32_t)a.rows);
     if (forward)
-        STK_LAUNCH(kKRowsForward, stream, (rows_forward_kernel<kT, R>), dim3((uint32_t)a.rows), dim3(kT), 0, stream, a);
+        STK_LAUNCH(kKRowsForward, stream, (rows_forward_kernel<kT, R>), grid, dim3(kT), 0, stream, a);
+    else if (vec)
+        STK_LAUNCH(kKRowsBackward, stream, (rows_backward_kernel<kT, R, kCanVec>), grid, dim3(kT), 0, stream, a);
     else
-        STK_LAUNCH(kKRowsBackward, stream, (rows_backward_kernel<kT, R>), dim3((uint32_t)a.rows), dim3(kT), 0, stream, a);
+        STK_LAUNCH(kKRowsBackward, stream, (rows_backward_kernel<kT, R, false>), grid, dim3(kT), 0, stream, a);
     return hipGetLastError();
 }
 
