@@ -44,6 +44,12 @@ constexpr int kWin = kWave * kVals;             // window list per wave (worst c
 constexpr int kWaves1 = kPass1Threads / kWave;
 constexpr double kTailCut = 50.0;               // tail terms below 2^-50 are dropped
 constexpr int kP1Stage = 2048;                  // band scores staged per work-group
+// A wave whose band scores overflow the stage takes the global band in
+// chunks of kP1Chunk slots (one global reservation per chunk, not per
+// batch); at the end the full stage fills every wave's unused chunk tail, so
+// the band has no holes and its count stays exact.
+constexpr int kP1Chunk = 512;
+static_assert(kPass1Threads / kWave * kP1Chunk <= kP1Stage, "the stage covers every chunk tail");
 
 struct Ctx1 {
     float aL, aR, tL, tR;
@@ -64,6 +70,8 @@ struct Acc1 {
     float bmin, bmax;
     float amax;                                 // max |s| (+-inf shows here)
     uint32_t nan;                               // a NaN reached the window list
+    unsigned long long chunk_next;              // wave-uniform: next free slot of this wave's chunk
+    uint32_t chunk_left;                        // wave-uniform: slots left in it
 };
 
 // Walk this wave's window list: near tail scores into the fp64 sums, band
@@ -99,15 +107,27 @@ __device__ __forceinline__ void drain_window(uint32_t cnt, const Ctx1& x, Acc1& 
         if (lane == 0)
             sbase = atomicAdd(x.stage_count, total);
         sbase = __shfl(sbase, 0, kWave);
-        // reservations past the LDS stage go straight to the global band
+        // reservations past the LDS stage go to this wave's chunk of the
+        // global band (a new chunk when it runs out; n_over <= 64 < kP1Chunk)
         const uint32_t first_over = sbase > (uint32_t)kP1Stage ? sbase : (uint32_t)kP1Stage;
         const uint32_t end = sbase + total;
         const uint32_t n_over = end > first_over ? end - first_over : 0u;
-        unsigned long long gbase = 0;
+        uint32_t take = 0;
+        unsigned long long g0 = 0, g1 = 0;
         if (n_over) {
-            if (lane == 0)
-                gbase = atomicAdd(x.nB, (unsigned long long)n_over);
-            gbase = __shfl(gbase, 0, kWave);
+            take = n_over < acc.chunk_left ? n_over : acc.chunk_left;
+            g0 = acc.chunk_next;
+            acc.chunk_next += take;
+            acc.chunk_left -= take;
+            if (take < n_over) {
+                unsigned long long nb = 0;
+                if (lane == 0)
+                    nb = atomicAdd(x.nB, (unsigned long long)kP1Chunk);
+                nb = __shfl(nb, 0, kWave);
+                g1 = nb;
+                acc.chunk_next = nb + (n_over - take);
+                acc.chunk_left = (uint32_t)kP1Chunk - (n_over - take);
+            }
         }
         if (band) {
             const uint32_t pos = sbase + rank_in_mask(mb);
@@ -118,7 +138,8 @@ __device__ __forceinline__ void drain_window(uint32_t cnt, const Ctx1& x, Acc1& 
             if (pos < (uint32_t)kP1Stage) {
                 x.stage[pos] = s;
             } else {
-                const uint64_t g = (uint64_t)gbase + (pos - first_over);
+                const uint32_t o = pos - first_over;  // rank among this batch's overflow
+                const uint64_t g = o < take ? (uint64_t)g0 + o : (uint64_t)g1 + (o - take);
                 if (g < (uint64_t)x.cap)
                     x.band[g] = s;
             }
@@ -197,6 +218,8 @@ __global__ __launch_bounds__(kPass1Threads) void pass1_kernel(Pass1Args a)
     __shared__ float win_buf[kWaves1][kWin];
     __shared__ uint32_t stage_count;
     __shared__ unsigned long long stage_base;
+    __shared__ unsigned long long tail_at[kWaves1];
+    __shared__ uint32_t tail_n[kWaves1];
     __shared__ double red_d[2][kWaves1];
     __shared__ uint32_t red_u[3][kWaves1];
     __shared__ float red_f[3][kWaves1];
@@ -232,7 +255,7 @@ __global__ __launch_bounds__(kPass1Threads) void pass1_kernel(Pass1Args a)
     x.stage_count = &stage_count;
     x.win = win_buf[wave];
 
-    Acc1 acc{0.0, 0.0, 0u, 0u, 0u, 0u, INFINITY, -INFINITY, 0.f, 0u};
+    Acc1 acc{0.0, 0.0, 0u, 0u, 0u, 0u, INFINITY, -INFINITY, 0.f, 0u, 0ull, 0u};
     const int64_t G = gridDim.x;
     int64_t rest = 0;  // first score not covered by whole tiles
 
@@ -289,14 +312,34 @@ __global__ __launch_bounds__(kPass1Threads) void pass1_kernel(Pass1Args a)
         classify<false>(v, valid, x, acc);
     }
 
-    // flush the LDS stage with one global reservation
+    // flush the LDS stage: its first entries fill the waves' unused chunk
+    // tails (a chunk exists only once the stage is full, and the tails add up
+    // to at most the stage), the rest takes one global reservation
+    if (lane == 0) {
+        tail_at[wave] = acc.chunk_next;
+        tail_n[wave] = acc.chunk_left;
+    }
     __syncthreads();
+    uint32_t tails = 0;
+    for (int w = 0; w < kWaves1; ++w)
+        tails += tail_n[w];
     const uint32_t staged = stage_count < (uint32_t)kP1Stage ? stage_count : (uint32_t)kP1Stage;
     if (tid == 0)
-        stage_base = staged ? atomicAdd(x.nB, (unsigned long long)staged) : 0ull;
+        stage_base = staged > tails ? atomicAdd(x.nB, (unsigned long long)(staged - tails)) : 0ull;
     __syncthreads();
     for (uint32_t i = tid; i < staged; i += kPass1Threads) {
-        const uint64_t g = (uint64_t)stage_base + i;
+        uint64_t g;
+        if (i < tails) {
+            uint32_t r = i;
+            int w = 0;
+            while (r >= tail_n[w]) {
+                r -= tail_n[w];
+                ++w;
+            }
+            g = tail_at[w] + r;
+        } else {
+            g = (uint64_t)stage_base + (i - tails);
+        }
         if (g < (uint64_t)a.cap)
             a.band[g] = stage_buf[i];
     }
