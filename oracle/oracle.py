@@ -132,8 +132,3 @@ def backward(g, s, alpha: float, b: float) -> np.ndarray:
 def mass(s, b: float, alpha: float) -> float:
     return default().mass(s, b, alpha)
 
-
-def laplace_cdf(x):
-    """Standard Laplace CDF, elementwise, fp64 (for one-by-one sampled checks)."""
-    x = np.asarray(x, dtype=np.float64)
-    return np.where(x <= 0, 0.5 * np.exp(np.minimum(x, 0.0)), 1.0 - 0.5 * np.exp(-np.maximum(x, 0.0)))

@@ -300,6 +300,56 @@ def pin_vjp_underflow(orc):
     assert np.max(np.abs(gr - naive)) <= 1e-9 * np.max(np.abs(naive))
 
 
+def pin_mass(orc):
+    """The selected mass M(b) = sum_i F((s_i - b)/alpha) (section 2.1), checked
+    against what fixes it without re-typing it: F(0) = 1/2 (every score at b
+    selects half a unit), F(x) + F(-x) = 1 (reflection: M_s(b) + M_{-s}(-b) = n),
+    the one-sided closed forms beyond every score (scipy's logsumexp), the
+    brute-force bisection root (60-digit decimal arithmetic) where the mass is
+    k, shift invariance, and strict decrease in b."""
+    rng = np.random.default_rng(77)
+    for n, s0, alpha in [(1, 0.0, 1.0), (7, -2.5, 0.1), (1000, 0.25, 1e-3)]:
+        m = orc.mass(np.full(n, s0), s0, alpha)
+        assert abs(m - n / 2) <= 1e-12 * n, (n, m)
+    for _ in range(30):
+        half = rng.normal(size=int(rng.integers(1, 40)))
+        c = float(rng.normal())
+        s = np.concatenate([c + half, c - half])
+        alpha = float(10 ** rng.uniform(-3, 1))
+        assert abs(orc.mass(s, c, alpha) - s.size / 2) <= 1e-12 * s.size
+    for _ in range(30):
+        n = int(rng.integers(1, 300))
+        s = rng.normal(size=n) * float(10 ** rng.uniform(-1, 1))
+        alpha = float(10 ** rng.uniform(-2, 0.5))
+        b = float(rng.normal() * 2)
+        m1, m2 = orc.mass(s, b, alpha), orc.mass(-s, -b, alpha)
+        assert abs(m1 + m2 - n) <= 1e-12 * n, (m1, m2, n)
+        c = float(rng.normal() * 8)
+        assert abs(orc.mass(s + c, b + c, alpha) - m1) <= 1e-9 * max(1.0, m1)
+        # beyond every score the mass is one exponential sum
+        hi = float(s.max()) + float(rng.uniform(0, 3)) * alpha
+        lo = float(s.min()) - float(rng.uniform(0, 3)) * alpha
+        m_hi = 0.5 * math.exp(logsumexp((s - hi) / alpha))
+        m_lo = n - 0.5 * math.exp(logsumexp((lo - s) / alpha))
+        assert abs(orc.mass(s, hi, alpha) - m_hi) <= 1e-12 * max(1.0, m_hi) * n, (hi, m_hi)
+        assert abs(orc.mass(s, lo, alpha) - m_lo) <= 1e-12 * n, (lo, m_lo)
+        # strictly decreasing in b
+        bs = np.sort(rng.normal(size=8) * 2)
+        ms = [orc.mass(s, float(x), alpha) for x in bs]
+        assert all(ms[i] >= ms[i + 1] for i in range(7)), ms
+        assert ms[0] > ms[-1] or bs[0] == bs[-1]
+    for c in range(25):
+        n = int(rng.integers(1, 40))
+        s = rng.normal(size=n)
+        if c % 3 == 0:
+            s = np.round(s * 2) / 2
+        alpha = float(10 ** rng.uniform(-2, 0.5))
+        k = float(rng.uniform(0.05, n - 0.05)) if n > 1 else 0.5
+        b = bisect_threshold(s, k, alpha)
+        m = orc.mass(s, b, alpha)
+        assert abs(m - k) <= 1e-9 * max(1.0, k), (n, k, alpha, m)
+
+
 ALL_PINS = [
     pin_bisection,
     pin_two_point_midpoint,
@@ -312,4 +362,5 @@ ALL_PINS = [
     pin_invariances,
     pin_vjp,
     pin_vjp_underflow,
+    pin_mass,
 ]

@@ -632,23 +632,25 @@ def test_certified_first_try_over_100_seeds(dev, name):
 
 
 # --------------------------------------------------------------------------
-# full-size workloads, as the benchmark runs them
+# full-size workloads with the certification pass waited for (a stats record
+# turns it on); the benchmark's own call sequence, with every element compared
+# with the oracle, is in test_gpu_fullsize.py
 # --------------------------------------------------------------------------
 def _sha(a):
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
 
 
 @pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
-def test_full_size_workload(dev, name):
+def test_full_size_route_and_certified_mass(dev, name):
+    """The route each full-size workload takes, b against the oracle's stored
+    b, and the certification pass: the fp64 mass the library folds from its
+    own p (stats.mass) and the oracle's mass at the GPU's b."""
     gold = GOLD[name]
     s_np, k, alpha, w = make_workload(name)
-    g_np = draw_grad(s_np.size, w.seed)
     assert _sha(s_np) == gold["sha256_scores"], "input generator drifted"
     assert k == gold["k"]
     s = torch.from_numpy(s_np).to(dev)
-    g = torch.from_numpy(g_np).to(dev)
-    p, b, st, ws = stk.forward(s, k, alpha, want_stats=True, want_workspace=True)
-    grad = stk.backward(g, s, alpha, b, fwd_workspace=ws)  # as the benchmark calls it
+    p, b, st = stk.forward(s, k, alpha, params(verify_mass=1), want_stats=True)
     torch.cuda.synchronize()
     b_gpu = float(b.item())
     b_ref = gold["b"]
@@ -657,23 +659,8 @@ def test_full_size_workload(dev, name):
     # brackets it (its own test forces the full sort on the same input)
     expect = _lib.PATH_WIDENED if name == "c5" else _lib.PATH_BRACKET
     assert st["path"] == expect, st
-
-    # sampled p and grad, one by one from the oracle's threshold and sums
-    rng = np.random.default_rng(1)
-    idx = np.concatenate([rng.integers(0, s_np.size, 200_000), np.argpartition(np.abs(s_np - b_ref), 5000)[:5000]])
-    p_np = p.cpu().numpy()
-    grad_np = grad.cpu().numpy()
-    x = (s_np[idx].astype(np.float64) - b_ref) / alpha
-    p_ref = O.laplace_cdf(x)
-    assert np.max(np.abs(p_np[idx] - p_ref)) <= 1e-5
-    d = 0.5 * np.exp(-np.abs(x))
-    grad_ref = (d / alpha) * (g_np[idx].astype(np.float64) - gold["G"] / gold["D"])
-    rel = np.linalg.norm(grad_np[idx] - grad_ref) / np.linalg.norm(grad_ref)
-    assert rel <= 1e-4, rel
-
-    # properties at full size
-    m_b = O.mass(s_np, b_gpu, alpha)
-    assert abs(m_b - k) <= 1e-3, m_b - k
-    m_p = float(np.sum(p_np.astype(np.float64)))
-    assert abs(m_p - k) <= 1e-3 + gold["mass_p32_rounding_floor"], m_p - k
-    assert abs(float(np.sum(grad_np.astype(np.float64)))) <= 1e-4 * float(np.sum(np.abs(grad_np)))
+    floor = gold["mass_p32_rounding_floor"]
+    assert abs(st["mass"] - k) <= 1e-3 + floor, st
+    m_p = float(torch.sum(p.double()).item())
+    assert abs(m_p - k) <= 1e-3 + floor, (m_p, k)
+    assert abs(O.mass(s_np, b_gpu, alpha) - k) <= 1e-3

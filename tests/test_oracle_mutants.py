@@ -31,6 +31,10 @@ MUTANTS = {
     "p_direction": ("p_out[i] = laplace_cdf((s[i] - b) / alpha);", "p_out[i] = laplace_cdf((b - s[i]) / alpha);"),
     "vjp_drop_ratio": ("grad_out[i] = (d / alpha) * (g[i] - ratio);", "grad_out[i] = (d / alpha) * g[i];"),
     "vjp_scale": ("grad_out[i] = (d / alpha) * (g[i] - ratio);", "grad_out[i] = d * (g[i] - ratio);"),
+    "mass_direction": ("m += laplace_cdf((s[i] - b) / alpha);", "m += laplace_cdf((b - s[i]) / alpha);"),
+    "mass_overwrite": ("m += laplace_cdf((s[i] - b) / alpha);", "m = laplace_cdf((s[i] - b) / alpha);"),
+    "mass_skip_first": ("for (int64_t i = 0; i < n; ++i)\n        m +=", "for (int64_t i = 1; i < n; ++i)\n        m +="),
+    "mass_scale": ("m += laplace_cdf((s[i] - b) / alpha);", "m += laplace_cdf((s[i] - b) * alpha);"),
     "locate_strict": ("if (BREAK_MASS(mid) >= k)\n                lo = mid;", "if (BREAK_MASS(mid) < k)\n                lo = mid;"),
 }
 
@@ -41,7 +45,7 @@ sys.path.insert(0, %(root)r)
 from oracle.oracle import Oracle
 import oracle_pins as P
 orc = Oracle(sys.argv[1])
-order = [P.pin_two_point_midpoint, P.pin_all_equal, P.pin_symmetric_sets, P.pin_logsumexp_extremes,
+order = [P.pin_mass, P.pin_two_point_midpoint, P.pin_all_equal, P.pin_symmetric_sets, P.pin_logsumexp_extremes,
          P.pin_zero_temperature, P.pin_large_temperature, P.pin_mass_and_order, P.pin_invariances,
          P.pin_vjp, P.pin_bisection]
 for pin in order:
