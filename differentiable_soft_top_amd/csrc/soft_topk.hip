@@ -16,6 +16,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "soft_topk.h"
 #include "stk_common.hpp"
@@ -791,9 +792,51 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
 
 using namespace stk;
 
+// ---- scratch of the allocation-free backward ------------------------------
+// The score-reading backward needs one buffer beyond its inputs and outputs:
+// the (D, G) partials of its reduction, one fp64 pair per work-group.  Its
+// grid is capped at kNoAllocPartials work-groups for every n, so a fixed
+// device array holds them.  Each GPU the library runs on holds its own copy
+// (16 KiB) until the process ends; its address is looked up once per device.
+constexpr int kNoAllocPartials = 1024;
+static_assert(kGridVjpLarge <= kNoAllocPartials && kGridVjpSmall <= kNoAllocPartials,
+              "the score-reading reduction grid must fit the fixed scratch");
+static __device__ __align__(256) double scratch[2 * kNoAllocPartials];
+
 namespace {
 
 bool n_ok(int64_t n) { return n >= 1 && n <= 0x7fffffffLL; }
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    double* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device (the host-side name is a
+// stand-in, not a device address: only this pointer reaches kernels).
+int scratch_on_current_device(double** out)
+{
+    int dev = -1;
+    STK_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices)
+        return hip_fail(hipErrorInvalidDevice);
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot]() {
+        void* p = nullptr;
+        slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (slot.err == hipSuccess && p == nullptr)
+            slot.err = hipErrorInvalidSymbol;
+        slot.ptr = static_cast<double*>(p);
+    });
+    if (slot.err != hipSuccess)
+        return hip_fail(slot.err);
+    *out = slot.ptr;
+    return SOFT_TOPK_OK;
+}
+
 
 bool rows_ok(int64_t rows, int64_t n_row)
 {
@@ -1215,6 +1258,52 @@ int soft_topk_backward_ex(const float* grad_p, const float* scores, int64_t n, d
         }
     }
     STK_HIP(launch_vjp(a, static_cast<hipStream_t>(stream)));
+    return SOFT_TOPK_OK;
+}
+
+int soft_topk_backward_noalloc(const float* grad_p, const float* scores, int64_t n, double alpha, const double* b,
+                               float* grad_s, void* stream)
+{
+    if (!grad_p || !scores || !b || !grad_s || !n_ok(n))
+        return SOFT_TOPK_EINVAL;
+    if (!(alpha > 0.0) || !isfinite(alpha))
+        return SOFT_TOPK_EINVAL;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n <= kRowMax) {
+        // one work-group, no scratch (as soft_topk_backward)
+        RowsArgs ra = rows_args(scores, 1, n, alpha);
+        ra.g = grad_p;
+        ra.b_in = b;
+        ra.grad = grad_s;
+        STK_HIP(launch_row_alone(ra, false, st));
+        return SOFT_TOPK_OK;
+    }
+    const int32_t reduce_blocks = vjp_reduce_blocks(n);
+    if (reduce_blocks > kNoAllocPartials)
+        return SOFT_TOPK_EWORKSPACE;
+    double* partials = nullptr;
+    const int rc = scratch_on_current_device(&partials);
+    if (rc)
+        return rc;
+    // the score-reading route of soft_topk_backward, with its partials in the
+    // fixed scratch: every work-group of the reduction writes its pair before
+    // the gradient kernel reads them, so nothing needs clearing
+    VjpArgs a;
+    a.g = grad_p;
+    a.s = scores;
+    a.n = n;
+    a.alpha = alpha;
+    a.log2e_over_alpha = kLog2e / alpha;
+    a.b = b;
+    a.grad = grad_s;
+    a.partials = partials;
+    a.blocks = vjp_apply_blocks(n);
+    a.reduce_blocks = reduce_blocks;
+    a.fst = nullptr;
+    a.seg = seg_bufs(nullptr, 0, 0, 0);
+    a.seg_tiles = 0;
+    a.gl = nullptr;
+    STK_HIP(launch_vjp(a, st));
     return SOFT_TOPK_OK;
 }
 

@@ -36,7 +36,8 @@
  *    SOFT_TOPK_EINVAL nothing is launched and the outputs are untouched.
  *  - Limits: 1 <= n <= 2^31 - 1.
  *  - Calls on different streams need distinct workspaces; the library keeps
- *    no other state apart from one small pinned host buffer per host thread.
+ *    no other state apart from one small pinned host buffer per host thread
+ *    and the 16 KiB per-GPU array of soft_topk_backward_noalloc.
  */
 #ifndef SOFT_TOPK_H
 #define SOFT_TOPK_H
@@ -217,6 +218,28 @@ int soft_topk_backward_ex(const float* grad_p, const float* scores, int64_t n,
                           double alpha, const double* b, float* grad_s,
                           const void* fwd_workspace, size_t fwd_workspace_bytes,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, result and errors
+ * as soft_topk_backward, whose kernels it runs: up to 8192 scores one
+ * work-group; above, the score-reading reduction and gradient kernels, with
+ * the reduction's (D, G) partials (at most 1024 work-groups, 16 KiB) in a
+ * fixed device array of the library instead of a workspace.  The grid is
+ * capped at that size for every n, so every valid n (1 <= n <= 2^31 - 1)
+ * fits; a grid above it would return SOFT_TOPK_EWORKSPACE.  The array is
+ * per GPU, set up on the first call on each device (its address looked up
+ * with the device current) and held until the process ends; calls on one
+ * GPU share it and keep the last call's contents, so calls that overlap on
+ * one GPU (other streams, other host threads) race and must be ordered by
+ * the caller.  The call must be made with the device of `stream` current.
+ * Fully asynchronous on `stream`; makes no hipMalloc, hipFree or other
+ * allocating call.
+ */
+int soft_topk_backward_noalloc(const float* grad_p, const float* scores, int64_t n,
+                               double alpha, const double* b, float* grad_s,
+                               void* stream);
 
 /*
  * Batched rows.  The aiqbench.com abstract and the gist.science summary of
