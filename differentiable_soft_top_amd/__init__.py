@@ -55,10 +55,11 @@ def forward(s, k: float, alpha: float, params: Params | None = None, out_p=None,
     p = out_p if out_p is not None else torch.empty_like(s)
     b = torch.empty(1, dtype=torch.float64, device=s.device)
     stats = Stats()
+    # a stats record makes the call wait for the certification pass: only on request
     rc = lib.soft_topk_forward_ex(ctypes.c_void_p(s.data_ptr()), n, float(k), float(alpha),
                                   ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(b.data_ptr()),
                                   ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream_handle(s),
-                                  pp, ctypes.byref(stats))
+                                  pp, ctypes.byref(stats) if want_stats else None)
     _lib.check(rc, "soft_topk_forward")
     out = (p, b)
     if want_stats:
@@ -165,7 +166,11 @@ def _function():
         @staticmethod
         def forward(ctx, s, k, alpha, params):
             p, b, ws = forward(s, k, alpha, params, want_workspace=True)
-            ctx.save_for_backward(s, b, ws)
+            # keep only what the backward reads (status block and segment
+            # record), not the sort and band buffers of the whole workspace
+            rec = ws[:_lib.load().soft_topk_record_bytes(s.numel())].clone()
+            del ws
+            ctx.save_for_backward(s, b, rec)
             ctx.alpha = float(alpha)
             ctx.mark_non_differentiable(b)
             return p, b

@@ -77,6 +77,8 @@ def load():
     lib.soft_topk_default_params.restype = None
     lib.soft_topk_workspace_bytes.argtypes = [i64, ctypes.POINTER(Params)]
     lib.soft_topk_workspace_bytes.restype = sz
+    lib.soft_topk_record_bytes.argtypes = [i64]
+    lib.soft_topk_record_bytes.restype = sz
     lib.soft_topk_backward_workspace_bytes.argtypes = [i64]
     lib.soft_topk_backward_workspace_bytes.restype = sz
     lib.soft_topk_forward.argtypes = [fp, i64, dbl, dbl, fp, dp, vp, sz, vp]

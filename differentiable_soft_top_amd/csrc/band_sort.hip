@@ -1,7 +1,7 @@
 // band_sort.hip -- bucketing of the middle band (the band sort's first level).
 //
-// aiqbench.com abstract of Fast LapSum: bracketing "restricts sorting to a
-// narrow band of scores around the threshold"; gist.science summary,
+// aiqbench.com abstract of Fast LapSum: with the bracket in place, only the
+// scores in a thin band near the threshold are sorted; gist.science summary,
 // section 2.2 step 3: the exact solver runs on that band alone.
 //
 // gfx950 design: a value-bucket sort whose second level runs in the solve.  The band lies in [bmin, bmax] (known

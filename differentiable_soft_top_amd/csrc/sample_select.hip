@@ -13,6 +13,7 @@
 #include "stk_common.hpp"
 #include "stk_layout.hpp"
 #include "stk_prof.hpp"
+#include "stk_scan.hpp"
 
 namespace stk {
 
@@ -323,31 +324,54 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs se)
 // many scores at one quantised level) makes the band overflow however the
 // bracket is drawn: no bracket around b can leave the tied scores out when
 // b lies among them.  The host then splits the bracket at that value, which
-// puts the whole cluster into one tail.  This kernel finds the candidate:
-// eight values taken from the buffer, each counted over an evenly spread
-// sample of up to 65,536 buffer entries.  Only a heuristic for the next
-// bracket: the certificate of that round decides.
+// puts the whole cluster into one tail.  These kernels find the candidate:
+// eight values taken from evenly spread places in the band buffer, each
+// counted over kModeChunks contiguous runs of up to kModeRun entries spread
+// evenly over the buffer (65,536 entries in all, read coalesced by
+// kModeChunks work-groups), then folded by one small work-group.  Only a
+// heuristic for the next bracket: the certificate of that round decides.
 // ---------------------------------------------------------------------------
 constexpr int kModeThreads = 256;
 constexpr int kModeCands = 8;
-constexpr int kModeSample = 65536;
+constexpr int kModeChunks = 64;
+constexpr int kModeRun = 1024;  // entries per chunk (4 per thread)
 
-__global__ __launch_bounds__(kModeThreads) void band_mode_kernel(const float* band, int64_t cap, Status* st)
+__device__ __forceinline__ int64_t mode_band_len(const Status* st, int64_t cap)
+{
+    return (int64_t)st->nB < cap ? (int64_t)st->nB : cap;
+}
+
+// [start, end) of chunk j of a band of m entries
+__device__ __forceinline__ void mode_chunk(int64_t m, int j, int64_t* start, int64_t* end)
+{
+    const int64_t s = (int64_t)j * m / kModeChunks;
+    const int64_t e = (int64_t)(j + 1) * m / kModeChunks;
+    *start = s;
+    *end = e - s < kModeRun ? e : s + kModeRun;
+}
+
+__device__ __forceinline__ float mode_cand(const float* band, int64_t m, int c)
+{
+    return band[(2 * c + 1) * m / (2 * kModeCands)];
+}
+
+__global__ __launch_bounds__(kModeThreads) void band_mode_count_kernel(const float* band, int64_t cap, const Status* st,
+                                                                      uint32_t* counts)
 {
     __shared__ uint32_t cnt[kModeThreads / kWave][kModeCands];
     const int tid = threadIdx.x;
-    const int64_t m = (int64_t)st->nB < cap ? (int64_t)st->nB : cap;
+    const int64_t m = mode_band_len(st, cap);
+    int64_t start, end;
+    mode_chunk(m, blockIdx.x, &start, &end);
     float cand[kModeCands];
-#pragma unroll
-    for (int c = 0; c < kModeCands; ++c)
-        cand[c] = m > 0 ? band[(2 * c + 1) * m / (2 * kModeCands)] : 0.0f;
-    const int64_t S = m < kModeSample ? m : kModeSample;
     uint32_t my[kModeCands];
 #pragma unroll
-    for (int c = 0; c < kModeCands; ++c)
+    for (int c = 0; c < kModeCands; ++c) {
+        cand[c] = m > 0 ? mode_cand(band, m, c) : 0.0f;
         my[c] = 0u;
-    for (int64_t j = tid; j < S; j += kModeThreads) {
-        const float v = band[j * m / S];
+    }
+    for (int64_t j = start + tid; j < end; j += kModeThreads) {
+        const float v = band[j];
 #pragma unroll
         for (int c = 0; c < kModeCands; ++c)
             my[c] += v == cand[c] ? 1u : 0u;
@@ -359,16 +383,40 @@ __global__ __launch_bounds__(kModeThreads) void band_mode_kernel(const float* ba
             cnt[tid / kWave][c] = w;
     }
     __syncthreads();
+    if (tid < kModeCands) {
+        uint32_t t = 0u;
+        for (int w = 0; w < kModeThreads / kWave; ++w)
+            t += cnt[w][tid];
+        counts[blockIdx.x * kModeCands + tid] = t;
+    }
+}
+
+__global__ __launch_bounds__(kWave) void band_mode_pick_kernel(const float* band, int64_t cap, Status* st,
+                                                              const uint32_t* counts)
+{
+    __shared__ uint32_t tot[kModeCands];
+    const int tid = threadIdx.x;
+    const int64_t m = mode_band_len(st, cap);
+    if (tid < kModeCands) {
+        uint32_t t = 0u;
+        for (int j = 0; j < kModeChunks; ++j)
+            t += counts[j * kModeCands + tid];
+        tot[tid] = t;
+    }
+    __syncthreads();
     if (tid == 0) {
+        int64_t S = 0;
+        for (int j = 0; j < kModeChunks; ++j) {
+            int64_t s, e;
+            mode_chunk(m, j, &s, &e);
+            S += e - s;
+        }
         uint32_t best = 0u;
         float bv = 0.0f;
         for (int c = 0; c < kModeCands; ++c) {
-            uint32_t t = 0u;
-            for (int w = 0; w < kModeThreads / kWave; ++w)
-                t += cnt[w][c];
-            if (t > best) {
-                best = t;
-                bv = cand[c];
+            if (tot[c] > best) {
+                best = tot[c];
+                bv = mode_cand(band, m, c);
             }
         }
         st->tie_value = bv;
@@ -376,15 +424,20 @@ __global__ __launch_bounds__(kModeThreads) void band_mode_kernel(const float* ba
     }
 }
 
-hipError_t launch_band_mode(const float* band, int64_t cap, Status* st, hipStream_t stream)
+hipError_t launch_band_mode(const float* band, int64_t cap, Status* st, uint32_t* counts, hipStream_t stream)
 {
-    band_mode_kernel<<<1, kModeThreads, 0, stream>>>(band, cap, st);
+    band_mode_count_kernel<<<kModeChunks, kModeThreads, 0, stream>>>(band, cap, st, counts);
+    band_mode_pick_kernel<<<1, kWave, 0, stream>>>(band, cap, st, counts);
     return hipGetLastError();
 }
 
-__global__ void set_bracket_kernel(Status* st, float aL, float aR)
+__global__ void set_bracket_kernel(Status* st, float aL, float aR, int keep_left_tail)
 {
     if (threadIdx.x == 0) {
+        if (keep_left_tail) {
+            st->tie_SL = st->SL;
+            st->tie_nL = st->nL;
+        }
         st->aL = aL;
         st->aR = aR;
         st->select_info = 0u;
@@ -400,24 +453,54 @@ __global__ void set_bracket_kernel(Status* st, float aL, float aR)
     }
 }
 
-hipError_t launch_set_bracket(Status* st, float aL, float aR, hipStream_t stream)
+hipError_t launch_set_bracket(Status* st, float aL, float aR, bool keep_left_tail, hipStream_t stream)
 {
-    set_bracket_kernel<<<1, kWave, 0, stream>>>(st, aL, aR);
+    set_bracket_kernel<<<1, kWave, 0, stream>>>(st, aL, aR, keep_left_tail ? 1 : 0);
     return hipGetLastError();
 }
 
-__global__ void set_root_kernel(Status* st, double* out_b, double b)
+// The split at a tied value T put the cluster into the left tail of the
+// round on [T+, a_R) (T+ the next float above T) and into the right tail of
+// the round on [a_L, T).  When the first rejected low (M(T+) < k) and the
+// second high (M(T) > k), b lies strictly between T and T+, inside the gap
+// right of T.  The closed form of the full-sort solver (gist.science summary
+// of Fast LapSum, section 2.2) there, with both sums anchored at T:
+//   A = the left sum over every score <= T: the first round's left tail,
+//       moved from its anchor T+ to T;
+//   C = the count of scores > T: n less the first round's left count;
+//   B = the right sum over the scores > T: the second round's right tail
+//       (anchored at T) less the cluster, whose terms are exactly 1 each and
+//       number nR - C.
+// A root outside [T, T+] (which rounding alone could cause) leaves the
+// round rejected, and the full sort decides.
+__global__ void tie_root_kernel(TieRootArgs a)
 {
+    Status* st = a.st;
     if (threadIdx.x == 0) {
-        st->b = b;
-        *out_b = b;
-        st->solve_state = kSolveOk;
+        const float T = st->tie_value;
+        const float Tp = nextafterf(T, INFINITY);
+        const double A = st->tie_SL * exp2(((double)Tp - (double)T) * a.log2e_over_alpha);
+        const double C = (double)a.n - (double)st->tie_nL;
+        const double B = st->SR - ((double)st->nR - C);
+        bool ok = A > 0.0 && B > 0.0;
+        double b = 0.0;
+        if (ok) {
+            b = gap_root(node(T, A), node(T, B), C, a.k, a.alpha, a.log2e_over_alpha);
+            ok = b >= (double)T && b <= (double)Tp;
+        }
+        if (ok) {
+            st->b = b;
+            *a.out_b = b;
+            st->solve_state = kSolveOk;
+        }
     }
+    __syncthreads();
+    publish_status(st, a.mirror, a.seq);
 }
 
-hipError_t launch_set_root(Status* st, double* out_b, double b, hipStream_t stream)
+hipError_t launch_tie_root(const TieRootArgs& a, hipStream_t stream)
 {
-    set_root_kernel<<<1, kWave, 0, stream>>>(st, out_b, b);
+    tie_root_kernel<<<1, kWave, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -610,30 +610,30 @@ bool mass_ok(const Status& h, double k, double tol)
 
 // b strictly between the tied value T and the next float T+ (the round
 // above T rejected low, M(T+) < k, and the round below rejected high,
-// M(T) > k): the cluster's weight pins b within one fp32 step of T, inside
-// the gap right of T.  The closed form of the full-sort solver (gist.science
-// summary of Fast LapSum, section 2.2) there, with both sums anchored at T:
-// the left sum A over every score <= T (the cluster included) from the round
-// above T, whose left tail held them; the right sum B over the scores > T
-// from the round below T, whose right tail held the cluster too (its count
-// nR - C is taken off); C the count of scores > T.
-int tie_root(const Ctx& x, float T, float Tp, const Status& above, const Status& below, bool wait_mass, double tol,
-             soft_topk_stats* sx, Status* h, bool* done)
+// M(T) > k): the closed form in the gap right of T runs on the device
+// (tie_root_kernel), from the first round's left tail (kept in the status
+// block when the second round's bracket was set) and the second round's
+// right tail, and publishes the status like a segment solve.
+int tie_root(const Ctx& x, bool wait_mass, double tol, soft_topk_stats* sx, Status* h, bool* done)
 {
-    const double A = above.SL * exp2(((double)Tp - (double)T) * x.c);
-    const double C = (double)x.n - (double)above.nL;
-    const double B = below.SR - ((double)below.nR - C);
-    if (!(A > 0.0) || !(B > 0.0))
-        return SOFT_TOPK_OK;
-    const double cc = C - x.k;
-    const double r = sqrt(cc * cc + A * B);
-    const double b = cc > 0.0 ? (double)T + x.alpha * log((cc + r) / B) : (double)T - x.alpha * log((-cc + r) / A);
-    if (!(b >= (double)T && b <= (double)Tp))
-        return SOFT_TOPK_OK;
-    STK_HIP(launch_set_root(x.st, x.b, b, x.stream));
+    TieRootArgs ta;
+    ta.st = x.st;
+    ta.out_b = x.b;
+    ta.n = x.n;
+    ta.k = x.k;
+    ta.alpha = x.alpha;
+    ta.log2e_over_alpha = x.c;
+    ta.mirror = x.mirror0;
+    ta.seq = next_publication();
+    STK_HIP(launch_tie_root(ta, x.stream));
     int rc = enqueue_certify_emit(x, wait_mass);
     if (rc)
         return rc;
+    rc = wait_solve(x, h);
+    if (rc)
+        return rc;
+    if (h->solve_state != kSolveOk)
+        return SOFT_TOPK_OK;
     if (wait_mass) {
         rc = wait_status(1, h);
         if (rc)
@@ -643,7 +643,6 @@ int tie_root(const Ctx& x, float T, float Tp, const Status& above, const Status&
             return SOFT_TOPK_OK;
         }
     }
-    h->b = b;
     sx->path = SOFT_TOPK_PATH_WIDENED;
     *done = true;
     return SOFT_TOPK_OK;
@@ -661,7 +660,9 @@ int tie_root(const Ctx& x, float T, float Tp, const Status& above, const Status&
 int tie_split(const Ctx& x, Status h0, int rounds_left, bool wait_mass, double tol, soft_topk_stats* sx, Status* h,
               bool* done)
 {
-    STK_HIP(launch_band_mode(at<float>(x, x.plan.off_band), x.plan.cap, x.st, x.stream));
+    // the band histogram region is free until the next round's band sort
+    STK_HIP(launch_band_mode(at<float>(x, x.plan.off_band), x.plan.cap, x.st, at<uint32_t>(x, x.plan.off_hist),
+                             x.stream));
     int rc = read_status(x, h);
     if (rc)
         return rc;
@@ -671,10 +672,10 @@ int tie_split(const Ctx& x, Status h0, int rounds_left, bool wait_mass, double t
     const float T = h->tie_value;
     const float Tp = nextafterf(T, INFINITY);
     const float br[2][2] = {{Tp, h0.aR > Tp ? h0.aR : INFINITY}, {h0.aL < T ? h0.aL : -INFINITY, T}};
-    Status above;
     bool above_low = false;
     for (int i = 0; i < 2 && i < rounds_left; ++i) {
-        STK_HIP(launch_set_bracket(x.st, br[i][0], br[i][1], x.stream));
+        // the second round keeps the first round's left tail for tie_root
+        STK_HIP(launch_set_bracket(x.st, br[i][0], br[i][1], i == 1, x.stream));
         rc = enqueue_pass1(x);
         if (rc)
             return rc;
@@ -714,16 +715,14 @@ int tie_split(const Ctx& x, Status h0, int rounds_left, bool wait_mass, double t
         }
         if (h->solve_state == kSolveRejectLow) {
             sx->reject_mask |= SOFT_TOPK_REJECT_LOW;  // b < T+: the side below
-            if (i == 0) {
-                above = *h;
+            if (i == 0)
                 above_low = true;
-            }
             continue;
         }
         if (h->solve_state == kSolveRejectHigh) {
             sx->reject_mask |= SOFT_TOPK_REJECT_HIGH;
             if (i == 1 && above_low)
-                return tie_root(x, T, Tp, above, *h, wait_mass, tol, sx, h, done);
+                return tie_root(x, wait_mass, tol, sx, h, done);
         } else if (h->solve_state == kSolveOverflow) {
             sx->reject_mask |= SOFT_TOPK_REJECT_OVERFLOW;
         } else if (h->solve_state == kSolveBucketOverflow) {
@@ -837,7 +836,6 @@ int scratch_on_current_device(double** out)
     return SOFT_TOPK_OK;
 }
 
-
 bool rows_ok(int64_t rows, int64_t n_row)
 {
     return rows >= 1 && n_row >= 1 && rows <= 0x7fffffffLL && n_ok(n_row) && rows <= INT64_MAX / n_row;
@@ -889,6 +887,15 @@ size_t soft_topk_workspace_bytes(int64_t n, const soft_topk_params* params)
     if (!params_ok(p))
         return 0;
     return plan_for(n, p).total;
+}
+
+size_t soft_topk_record_bytes(int64_t n)
+{
+    if (!n_ok(n))
+        return 0;
+    int64_t n_seg;
+    size_t off_meta, off_val;
+    return seg_layout(n, align_up(sizeof(Status)), &n_seg, &off_meta, &off_val);
 }
 
 size_t soft_topk_backward_workspace_bytes(int64_t n)

@@ -125,6 +125,10 @@ struct alignas(16) Status {
     // its estimated count there (band_mode_kernel, after a band overflow)
     float tie_value;
     uint32_t tie_count;
+    // the left tail of the split's first round (bracket [T+, a_R)), kept for
+    // the closed form between the tied value T and the next float T+
+    double tie_SL;
+    uint64_t tie_nL;
 };
 static_assert(sizeof(Status) <= 256, "status block must fit 256 bytes");
 static_assert(sizeof(Status) % 4 == 0, "status block is copied as 32-bit words");
@@ -240,13 +244,24 @@ hipError_t launch_localize(const SampleArgs& sa, const SelectArgs& se, hipStream
 // After a band or bucket overflow: estimate, from a sample of the band
 // buffer (its first min(nB, cap) entries), the count of the most frequent
 // of eight candidate values taken from it (Status::tie_value, tie_count).
-hipError_t launch_band_mode(const float* band, int64_t cap, Status* st, hipStream_t stream);
+// `counts`: scratch for 64 x 8 u32 per-chunk candidate counts.
+hipError_t launch_band_mode(const float* band, int64_t cap, Status* st, uint32_t* counts, hipStream_t stream);
 // Start a round on an explicit bracket [aL, aR) (instead of the sampler's):
 // the bracket and the per-round fields the select kernel would set.
-hipError_t launch_set_bracket(Status* st, float aL, float aR, hipStream_t stream);
+hipError_t launch_set_bracket(Status* st, float aL, float aR, bool keep_left_tail, hipStream_t stream);
 // Hand a root found on the host to the emission: b into out_b and the
 // status, and the solve state OK.
-hipError_t launch_set_root(Status* st, double* out_b, double b, hipStream_t stream);
+// b strictly between the tied value T and T+ (see tie_root_kernel); the
+// status is published to `mirror` with `seq` either way.
+struct TieRootArgs {
+    Status* st;
+    double* out_b;
+    int64_t n;
+    double k, alpha, log2e_over_alpha;
+    Mirror* mirror;
+    uint32_t seq;
+};
+hipError_t launch_tie_root(const TieRootArgs& a, hipStream_t stream);
 hipError_t launch_debug_sample(const float* s, int64_t n, float alpha, uint64_t seed, int32_t m,
                                float* out_samples, hipStream_t stream);
 

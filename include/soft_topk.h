@@ -137,6 +137,17 @@ void soft_topk_default_params(soft_topk_params* params);
  */
 size_t soft_topk_workspace_bytes(int64_t n, const soft_topk_params* params);
 
+/*
+ * Bytes at the front of a forward workspace (for n scores) that
+ * soft_topk_backward_ex reads: the status block and the saturated-segment
+ * record (about 1.1 bytes per score from 2^22 scores on, else 256 bytes).
+ * A caller that keeps only this prefix of the forward workspace for the
+ * backward (a copy, 256-byte aligned, passed as fwd_workspace with this many
+ * bytes) gets the same result as with the whole workspace.  0 if n is out of
+ * range.
+ */
+size_t soft_topk_record_bytes(int64_t n);
+
 /* Bytes of device workspace soft_topk_backward needs for n scores. */
 size_t soft_topk_backward_workspace_bytes(int64_t n);
 
