@@ -34,8 +34,19 @@ backward on two row workloads, warm and cold, the same way; each carries the
 traffic of its two kernels when profiles/traffic.json holds current counter
 runs for it (the same three commands with --workload r1 or r2 added to each).
 
-"cpu_baseline" times the fp64 CPU oracle (forward + backward) on a bounded
-sample (the first 2^25 scores, k scaled) and scales by n log2 n.
+"hbm" gives the step's HBM traffic from the same counter runs: the bytes of
+every library kernel of a step (calibrated as above), and that over the median
+step time.  "streaming" lists each linear pass with its per-launch time from
+an event-instrumented pre-pass (event pairs around each launch, so those
+times are a little above the uninstrumented ones and their sum exceeds the
+step), its algorithmic rate and its counter-measured rate against the peak.
+
+"verified" times the same steps with the certification pass waited for
+(verify_mass = 1: the forward folds the fp64 sum of p and checks it against
+k before returning).
+
+"cpu_baseline" times the fp64 CPU oracle (forward + backward) once over the
+whole workload, on one host thread.
 """
 from __future__ import annotations
 
@@ -43,7 +54,6 @@ import argparse
 import ctypes
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -77,8 +87,9 @@ for _k in ROWS_ALGO_BYTES:
 class Runner:
     """Preallocated buffers + direct C-ABI calls (as a training loop would)."""
 
-    def __init__(self, torch, lib, s, g, k, alpha):
+    def __init__(self, torch, lib, s, g, k, alpha, params=None):
         self.torch, self.lib = torch, lib
+        self.params = params
         self.k, self.alpha = float(k), float(alpha)
         # Two input batches, used in turn: the second is the first reversed
         # (the same values, so every step does the same work) in memory of
@@ -103,13 +114,15 @@ class Runner:
 
     def step(self, stats=False):
         """Forward + backward; with stats=True the forward also waits for the
-        certification pass and fills self.stats (not used in timed steps)."""
+        certification pass and fills self.stats (not used in timed steps).
+        self.params (None: the library defaults) goes to every forward."""
         L, v = self.lib, ctypes.c_void_p
         self.s, self.g = self.batches[self.turn]
         self.turn ^= 1
         rc = L.soft_topk_forward_ex(v(self.s.data_ptr()), self.n, self.k, self.alpha, v(self.p.data_ptr()),
                                     v(self.b.data_ptr()), v(self.ws.data_ptr()), self.ws_bytes, self.stream,
-                                    None, ctypes.byref(self.stats) if stats else None)
+                                    ctypes.byref(self.params) if self.params is not None else None,
+                                    ctypes.byref(self.stats) if stats else None)
         self._lib.check(rc, "soft_topk_forward")
         rc = L.soft_topk_backward_ex(v(self.g.data_ptr()), v(self.s.data_ptr()), self.n, self.alpha,
                                      v(self.b.data_ptr()), v(self.grad.data_ptr()), v(self.ws.data_ptr()),
@@ -174,6 +187,31 @@ def src_hash(name):
         with open(os.path.join(ROOT, "differentiable_soft_top_amd", "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def all_src_hash():
+    """Hash of every library source (the whole step's kernels and launches)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "differentiable_soft_top_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, fn), "rb") as f:
+                h.update(fn.encode())
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def step_traffic(workload):
+    """Counter-measured HBM bytes of one step, or None when stale or absent."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    ent = tr.get(workload, {}).get("kernels", {}).get("_step")
+    if not ent or ent.get("source_sha256") != all_src_hash():
+        return None
+    return ent.get("bytes_per_step")
 
 
 def traffic_for(kernel, workload):
@@ -268,6 +306,16 @@ def pmc_summary(fetch_csv, write_csv, workload="c4"):
         ent[kname] = {"kernels": sorted(set(fk)), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                       "bytes_per_launch": fb + wb, "algorithmic_bytes_per_launch": algo[kname] * n,
                       "launches": len(fv), "source_sha256": src_hash(kname)}
+    # the whole step: every library kernel, per step (the backward's last
+    # kernel runs once per step)
+    last = symbols["rows_backward" if workload in ROW_WORKLOADS else "vjp_apply"]
+    n_steps = sum(len(vs) for name, vs in write.items() if any(sym in name for sym in last))
+    if n_steps:
+        fb = sum(v for name, vs in fetch.items() if "stk::" in name for v in vs) * 1024.0 * f_scale
+        wb = sum(v for name, vs in write.items() if "stk::" in name for v in vs) * 1024.0 * w_scale
+        ent["_step"] = {"fetch_bytes_per_step": fb / n_steps, "write_bytes_per_step": wb / n_steps,
+                        "bytes_per_step": (fb + wb) / n_steps, "steps": n_steps,
+                        "source_sha256": all_src_hash()}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     result = {}
     if os.path.exists(path):
@@ -280,24 +328,22 @@ def pmc_summary(fetch_csv, write_csv, workload="c4"):
     print(json.dumps(result, indent=1, sort_keys=True))
 
 
-def cpu_baseline(s_np, g_np, k, alpha, sample_n=1 << 25):
+def cpu_baseline(s_np, g_np, k, alpha, name):
+    """The fp64 CPU oracle (forward then backward) once over the whole
+    workload, single-threaded (qsort, scans, closed form, then the VJP)."""
     from oracle import oracle as O
-    n = s_np.size
-    ns = min(n, sample_n)
-    ks = k * ns / n
     t0 = time.perf_counter()
-    _, b = O.forward(s_np[:ns], ks, alpha)
-    O.backward(g_np[:ns], s_np[:ns], alpha, b)
+    _, b = O.forward(s_np, k, alpha)
+    O.backward(g_np, s_np, alpha, b)
     dt = time.perf_counter() - t0
-    scale = (n * math.log2(n)) / (ns * math.log2(ns)) if ns < n else 1.0
     return {
-        "value": dt * 1e3 * scale,
+        "value": dt * 1e3,
         "unit": "ms",
         "cores": 1,
         "kind": "oracle",
-        "sample": "fp64 C oracle (qsort + prefix/suffix scans + closed form, then VJP), one run on the "
-                  "first %d scores of the workload with k scaled to %.6g; %.2f s measured, scaled by "
-                  "n log2 n to n=%d" % (ns, ks, dt, n),
+        "sample": "one run of the fp64 C oracle (qsort + prefix/suffix scans + closed form, then the VJP) "
+                  "over the whole %s workload (n=%d), input conversion included, on one host thread"
+                  % (name, s_np.size),
     }
 
 
@@ -307,7 +353,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4")
-    ap.add_argument("--sizes", default="c2,c3", help="extra workloads timed (comma list, '' for none)")
+    ap.add_argument("--sizes", default="c1,c2,c3,c5", help="extra workloads timed (comma list, '' for none)")
     ap.add_argument("--rows", default="r1,r2", help="batched-row workloads timed (comma list, '' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
@@ -372,6 +418,34 @@ def main():
     mean = float(np.mean(times))
     st = run.stats.as_dict()
 
+    # the same steps with the certification pass waited for (fp64 sum of p
+    # folded and checked against k inside every forward)
+    vprm = _lib.default_params()
+    vprm.verify_mass = 1
+    vrun = Runner(torch, lib, run.batches[0][0], run.batches[0][1], k, alpha, params=vprm)
+    for _ in range(3):
+        vrun.step()
+    vtimes = time_steps(torch, vrun, args.steps)
+    del vrun
+    torch.cuda.empty_cache()
+
+    # per streaming kernel: pre-pass event times, algorithmic and counter rates
+    streaming_out = {}
+    for kname in ALGO_BYTES:
+        if kname not in per_step:
+            continue
+        t_ms = per_step[kname]
+        tb = traffic_for(kname, args.workload)
+        streaming_out[kname] = {
+            "avg_us_event_prepass": t_ms * 1e3,
+            "algorithmic_bytes": ALGO_BYTES[kname] * n,
+            "algorithmic_GBps": ALGO_BYTES[kname] * n / (t_ms / 1e3) / 1e9,
+            "counter_bytes": tb,
+            "counter_GBps": (tb / (t_ms / 1e3) / 1e9) if tb else None,
+            "counter_frac_of_peak": (tb / (t_ms / 1e3) / 1e9 / PEAK_HBM_GBS) if tb else None,
+        }
+    step_bytes = step_traffic(args.workload)
+
     sizes = {}
     for extra in [x for x in args.sizes.split(",") if x]:
         es_np, eg_np, ek, ealpha, ew, erun = setup(extra)
@@ -384,7 +458,7 @@ def main():
         del flush
         med = float(np.median(warm))
         sizes[extra] = {
-            "workload": ew.description, "n": int(es_np.size),
+            "workload": ew.description, "n": int(es_np.size), "k": ek, "alpha": ealpha,
             "median_ms": med, "p10_ms": float(np.percentile(warm, 10)), "p90_ms": float(np.percentile(warm, 90)),
             "median_ms_cold": float(np.median(cold)),
             "algorithmic_GBps": STEP_BYTES * es_np.size / (med / 1e3) / 1e9,
@@ -419,7 +493,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(s_np, g_np, k, alpha)
+        cpu = cpu_baseline(s_np, g_np, k, alpha, args.workload)
 
     out = {
         "metric": METRIC,
@@ -442,7 +516,15 @@ def main():
         "path": st["path"],
         "band": st["n_band"],
         "certified_mass_error": abs(st["mass"] - k),
-        "kernels_ms_per_step": {kname: round(v, 5) for kname, v in sorted(per_step.items())},
+        "verified": {"median_ms": float(np.median(vtimes)), "p10_ms": float(np.percentile(vtimes, 10)),
+                     "p90_ms": float(np.percentile(vtimes, 90)), "verify_mass": 1},
+        "hbm": {"bytes_per_step": step_bytes,
+                "GBps": (step_bytes / (median / 1e3) / 1e9) if step_bytes else None,
+                "frac_of_peak": (step_bytes / (median / 1e3) / 1e9 / PEAK_HBM_GBS) if step_bytes else None,
+                "source": "rocprofv3 FETCH_SIZE + WRITE_SIZE over every library kernel of a step, "
+                          "calibrated on a device copy (profiles/traffic.json)"},
+        "streaming": streaming_out,
+        "kernels_ms_event_prepass": {kname: round(v, 5) for kname, v in sorted(per_step.items())},
         "roofline": {
             "kernel": dominant,
             "bound": "hbm",
