@@ -45,6 +45,10 @@ def _bind(lib):
     lib.oracle_forward.restype = ctypes.c_int
     lib.oracle_backward.argtypes = [dp, dp, i64, dbl, dbl, dp]
     lib.oracle_backward.restype = ctypes.c_int
+    lib.oracle_dftopk_threshold.argtypes = [dp, i64, dbl, dp]
+    lib.oracle_dftopk_threshold.restype = ctypes.c_int
+    lib.oracle_dftopk_forward.argtypes = [dp, i64, dbl, dbl, dp, dp]
+    lib.oracle_dftopk_forward.restype = ctypes.c_int
     return lib
 
 
@@ -104,6 +108,25 @@ class Oracle:
         x = _as_f64(s)
         return self.lib.oracle_mass(_ptr(x), x.size, float(b), float(alpha))
 
+    def dftopk_threshold(self, s, k: float) -> float:
+        """DFTopK comparator: midpoint of the k-th and (k+1)-th largest scores."""
+        x = _as_f64(s)
+        b = ctypes.c_double(0.0)
+        rc = self.lib.oracle_dftopk_threshold(_ptr(x), x.size, float(k), ctypes.byref(b))
+        if rc != OK:
+            raise OracleError(rc)
+        return b.value
+
+    def dftopk_forward(self, s, k: float, alpha: float):
+        """DFTopK comparator: (p, b) with b the midpoint threshold, p_i = F((s_i - b)/alpha)."""
+        x = _as_f64(s)
+        p = np.empty_like(x)
+        b = ctypes.c_double(0.0)
+        rc = self.lib.oracle_dftopk_forward(_ptr(x), x.size, float(k), float(alpha), _ptr(p), ctypes.byref(b))
+        if rc != OK:
+            raise OracleError(rc)
+        return p, b.value
+
 
 _default = None
 
@@ -132,3 +155,10 @@ def backward(g, s, alpha: float, b: float) -> np.ndarray:
 def mass(s, b: float, alpha: float) -> float:
     return default().mass(s, b, alpha)
 
+
+def dftopk_threshold(s, k: float) -> float:
+    return default().dftopk_threshold(s, k)
+
+
+def dftopk_forward(s, k: float, alpha: float):
+    return default().dftopk_forward(s, k, alpha)

@@ -77,9 +77,9 @@ double oracle_mass(const double* s, int64_t n, double b, double alpha)
 }
 
 /*
- * Closed-form root inside the gap [x_lo, x_hi] (section 2.2: "closed-form
- * root calculation within the specific interval where the budget equation
- * balances").  With v = exp((x_lo - b)/alpha), w = exp((b - x_hi)/alpha),
+ * Closed-form root inside the gap [x_lo, x_hi] (section 2.2: once the gap
+ * between two sorted scores where the mass crosses k is known, the root in it
+ * has a closed form).  With v = exp((x_lo - b)/alpha), w = exp((b - x_hi)/alpha),
  * v*w = g = exp(-(x_hi - x_lo)/alpha), the mass in the gap is
  *     M(b) = A v / 2 + C - B w / 2
  * where A = sum_{x_i <= x_lo} exp((x_i - x_lo)/alpha),
@@ -177,6 +177,53 @@ int oracle_threshold(const double* s, int64_t n, double k, double alpha,
     free(x);
     free(A);
     free(B);
+    *b_out = b;
+    return ORACLE_OK;
+}
+
+/*
+ * DFTopK comparator (mlsanity.com page "Differentiable Fast Top-K Selection
+ * for Large-Scale Recommendation", abstract; gist.science summary of Fast
+ * LapSum, section 2.3 "Relation to DFTopK"): the threshold is fixed at the
+ * midpoint of the k-th and (k+1)-th largest scores instead of solving
+ * M(b) = k, so the selected mass sum_i F((s_i - b)/alpha) may differ from k.
+ * k must be a whole number with 1 <= k <= n - 1.  Sort ascending; the k-th
+ * largest is x[n-k] and the (k+1)-th largest x[n-k-1].
+ */
+int oracle_dftopk_threshold(const double* s, int64_t n, double k, double* b_out)
+{
+    if (s == NULL || b_out == NULL || n < 2)
+        return ORACLE_EINVAL;
+    if (!(k >= 1.0) || !(k <= (double)(n - 1)) || k != floor(k))
+        return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i)
+        if (!isfinite(s[i]))
+            return ORACLE_ENONFINITE;
+    double* x = (double*)malloc(sizeof(double) * (size_t)n);
+    if (!x)
+        return ORACLE_ENOMEM;
+    memcpy(x, s, sizeof(double) * (size_t)n);
+    qsort(x, (size_t)n, sizeof(double), cmp_double);
+    const int64_t kk = (int64_t)k;
+    *b_out = 0.5 * (x[n - kk] + x[n - kk - 1]);
+    free(x);
+    return ORACLE_OK;
+}
+
+/* DFTopK forward: its threshold and p_i = F((s_i - b)/alpha). */
+int oracle_dftopk_forward(const double* s, int64_t n, double k, double alpha,
+                          double* p_out, double* b_out)
+{
+    if (p_out == NULL || b_out == NULL)
+        return ORACLE_EINVAL;
+    if (!(alpha > 0.0) || !isfinite(alpha))
+        return ORACLE_EINVAL;
+    double b;
+    int rc = oracle_dftopk_threshold(s, n, k, &b);
+    if (rc != ORACLE_OK)
+        return rc;
+    for (int64_t j = 0; j < n; ++j)
+        p_out[j] = laplace_cdf((s[j] - b) / alpha);
     *b_out = b;
     return ORACLE_OK;
 }

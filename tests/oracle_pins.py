@@ -350,6 +350,62 @@ def pin_mass(orc):
         assert abs(m - k) <= 1e-9 * max(1.0, k), (n, k, alpha, m)
 
 
+def kth_largest_by_counting(s, j):
+    """The j-th largest score, by counting alone (no sort): v is it when fewer
+    than j scores exceed v and at least j are at or above it."""
+    s = [float(v) for v in s]
+    for v in s:
+        above = sum(1 for w in s if w > v)
+        at_or_above = sum(1 for w in s if w >= v)
+        if above < j <= at_or_above:
+            return v
+    raise AssertionError("no j-th largest")
+
+
+def pin_dftopk(orc):
+    """DFTopK comparator (DFTopK page, abstract; Fast LapSum summary, section
+    2.3): b is the midpoint of the k-th and (k+1)-th largest scores, found
+    here by counting on tiny inputs (ties included); LapSum's threshold tends
+    to it as alpha -> 0 and its p to the hard top-k indicator; reflecting
+    the scores with k -> n - k reflects b; shift, scale and permutation act
+    on b as on the scores; and p_i = F((s_i - b)/alpha) sums to the
+    definition's mass at b."""
+    rng = np.random.default_rng(99)
+    for c in range(60):
+        n = int(rng.integers(2, 65))
+        s = rng.normal(size=n)
+        if c % 3 == 0:
+            s = np.round(s * 2) / 2
+        k = int(rng.integers(1, n))
+        b = orc.dftopk_threshold(s, k)
+        want = 0.5 * (kth_largest_by_counting(s, k) + kth_largest_by_counting(s, k + 1))
+        assert b == want, (n, k, b, want)
+        b2 = orc.dftopk_threshold(-s, n - k)
+        assert b2 == -b, (b, b2)
+        cc = float(rng.normal() * 3)
+        assert abs(orc.dftopk_threshold(s + cc, k) - (b + cc)) <= 1e-12 * (1 + abs(b) + abs(cc))
+        assert orc.dftopk_threshold(2.0 * s, k) == 2.0 * b
+        assert orc.dftopk_threshold(s[rng.permutation(n)], k) == b
+        alpha = float(10 ** rng.uniform(-2, 0.5))
+        p, bp = orc.dftopk_forward(s, k, alpha)
+        assert bp == b
+        assert abs(float(np.sum(p)) - mass_def(s, b, alpha)) <= 1e-12 * n
+        assert np.max(np.abs(p - lap_cdf((s - b) / alpha))) <= 1e-15
+    for _ in range(20):
+        n = int(rng.integers(2, 80))
+        s = rng.permutation(np.arange(n, dtype=np.float64) * 0.37 + rng.uniform(0, 0.3, size=n))
+        gap = float(np.min(np.diff(np.sort(s))))
+        k = int(rng.integers(1, n))
+        alpha = 1e-6 * gap
+        b_lap = orc.threshold(s, float(k), alpha)
+        b_dft = orc.dftopk_threshold(s, k)
+        assert abs(b_lap - b_dft) <= alpha * math.log(n) + 1e-14 * (1 + abs(b_dft)), (b_lap, b_dft)
+        p, _ = orc.dftopk_forward(s, k, alpha)
+        hard = np.zeros(n)
+        hard[np.argsort(-s)[:k]] = 1.0
+        assert np.max(np.abs(p - hard)) <= 1e-6
+
+
 ALL_PINS = [
     pin_bisection,
     pin_two_point_midpoint,
@@ -363,4 +419,5 @@ ALL_PINS = [
     pin_vjp,
     pin_vjp_underflow,
     pin_mass,
+    pin_dftopk,
 ]

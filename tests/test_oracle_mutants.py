@@ -35,6 +35,11 @@ MUTANTS = {
     "mass_overwrite": ("m += laplace_cdf((s[i] - b) / alpha);", "m = laplace_cdf((s[i] - b) / alpha);"),
     "mass_skip_first": ("for (int64_t i = 0; i < n; ++i)\n        m +=", "for (int64_t i = 1; i < n; ++i)\n        m +="),
     "mass_scale": ("m += laplace_cdf((s[i] - b) / alpha);", "m += laplace_cdf((s[i] - b) * alpha);"),
+    "dftopk_kth_only": ("*b_out = 0.5 * (x[n - kk] + x[n - kk - 1]);", "*b_out = 0.5 * (x[n - kk] + x[n - kk]);"),
+    "dftopk_smallest": ("*b_out = 0.5 * (x[n - kk] + x[n - kk - 1]);", "*b_out = 0.5 * (x[kk] + x[kk - 1]);"),
+    "dftopk_shifted_rank": ("*b_out = 0.5 * (x[n - kk] + x[n - kk - 1]);",
+                            "*b_out = 0.5 * (x[n - kk - 1] + x[n - kk - 1 > 0 ? n - kk - 2 : 0]);"),
+    "dftopk_p_direction": ("p_out[j] = laplace_cdf((s[j] - b) / alpha);", "p_out[j] = laplace_cdf((b - s[j]) / alpha);"),
     "locate_strict": ("if (BREAK_MASS(mid) >= k)\n                lo = mid;", "if (BREAK_MASS(mid) < k)\n                lo = mid;"),
 }
 
@@ -45,7 +50,7 @@ sys.path.insert(0, %(root)r)
 from oracle.oracle import Oracle
 import oracle_pins as P
 orc = Oracle(sys.argv[1])
-order = [P.pin_mass, P.pin_two_point_midpoint, P.pin_all_equal, P.pin_symmetric_sets, P.pin_logsumexp_extremes,
+order = [P.pin_mass, P.pin_dftopk, P.pin_two_point_midpoint, P.pin_all_equal, P.pin_symmetric_sets, P.pin_logsumexp_extremes,
          P.pin_zero_temperature, P.pin_large_temperature, P.pin_mass_and_order, P.pin_invariances,
          P.pin_vjp, P.pin_bisection]
 for pin in order:
