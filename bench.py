@@ -45,6 +45,10 @@ step), its algorithmic rate and its counter-measured rate against the peak.
 (verify_mass = 1: the forward folds the fp64 sum of p and checks it against
 k before returning).
 
+"dftopk" times the DFTopK comparator (threshold at the midpoint of the k-th
+and (k+1)-th largest scores; forward only) on c1..c4 and reports the mass
+sum p it selects and its drift from k.
+
 "cpu_baseline" times the fp64 CPU oracle (forward + backward) once over the
 whole workload, on one host thread.
 """
@@ -355,6 +359,8 @@ def main():
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--sizes", default="c1,c2,c3,c5", help="extra workloads timed (comma list, '' for none)")
     ap.add_argument("--rows", default="r1,r2", help="batched-row workloads timed (comma list, '' for none)")
+    ap.add_argument("--dftopk", default="c1,c2,c3,c4",
+                    help="workloads timed with the DFTopK comparator, whose mass drift is reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="counter-collection run: a few steps of --workload (c1..c5 or a row workload "
@@ -491,6 +497,38 @@ def main():
         del rrun
         torch.cuda.empty_cache()
 
+    # DFTopK comparator: forward only (it has no backward), with its mass
+    # drift from k at each workload's alpha
+    dft_out = {}
+    for dname in [x for x in args.dftopk.split(",") if x]:
+        ds_np, dk, dalpha, dw = make_workload(dname)
+        ds = torch.from_numpy(ds_np).to(dev)
+        dp = torch.empty_like(ds)
+        db = torch.empty(1, dtype=torch.float64, device=dev)
+        dm = torch.empty(1, dtype=torch.float64, device=dev)
+        dws_bytes = lib.soft_topk_dftopk_workspace_bytes(ds.numel())
+        dws = torch.empty(dws_bytes, dtype=torch.uint8, device=dev)
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        v = ctypes.c_void_p
+
+        class _DftRun:
+            def step(self):
+                _lib.check(lib.soft_topk_dftopk_forward(v(ds.data_ptr()), ds.numel(), float(int(dk)), dalpha,
+                                                        v(dp.data_ptr()), v(db.data_ptr()), v(dm.data_ptr()),
+                                                        v(dws.data_ptr()), dws_bytes, stream),
+                           "soft_topk_dftopk_forward")
+
+        drun = _DftRun()
+        for _ in range(3):
+            drun.step()
+        dt = time_steps(torch, drun, 20)
+        mass = float(dm.item())
+        dft_out[dname] = {"workload": dw.description, "n": int(ds_np.size), "k": int(dk), "alpha": dalpha,
+                          "forward_median_ms": float(np.median(dt)), "b": float(db.item()), "mass": mass,
+                          "drift": mass - int(dk), "drift_rel": (mass - int(dk)) / int(dk)}
+        del ds, dp, dws
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(s_np, g_np, k, alpha, args.workload)
@@ -539,6 +577,7 @@ def main():
         },
         "sizes": sizes,
         "rows": rows_out,
+        "dftopk": dft_out,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -18,8 +18,8 @@ import ctypes
 from . import _lib
 from ._lib import Params, SoftTopKError, Stats  # noqa: F401
 
-__all__ = ["soft_topk", "forward", "backward", "rows_forward", "rows_backward", "threshold_curve", "Params", "Stats",
-           "SoftTopKError", "default_params"]
+__all__ = ["soft_topk", "forward", "backward", "rows_forward", "rows_backward", "threshold_curve", "dftopk_forward",
+           "Params", "Stats", "SoftTopKError", "default_params"]
 
 
 def default_params() -> Params:
@@ -118,6 +118,29 @@ def threshold_curve(s, alpha: float):
                                        _stream_handle(s))
     _lib.check(rc, "soft_topk_threshold_curve")
     return xs, mass
+
+
+def dftopk_forward(s, k: int, alpha: float, out_p=None):
+    """DFTopK comparator (soft_topk_dftopk_forward): b at the midpoint of the k-th and (k+1)-th
+    largest scores, p = F((s - b)/alpha).  Returns (p, b, mass) with mass = sum p (fp64, device);
+    mass - k is the drift from the budget.  Not differentiable (no backward)."""
+    import torch
+    _check_scores(s)
+    lib = _lib.load()
+    n = s.numel()
+    ws_bytes = lib.soft_topk_dftopk_workspace_bytes(n)
+    if ws_bytes == 0:
+        raise SoftTopKError(_lib.EINVAL, "invalid size (n=%d)" % n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=s.device)
+    p = out_p if out_p is not None else torch.empty_like(s)
+    b = torch.empty(1, dtype=torch.float64, device=s.device)
+    m = torch.empty(1, dtype=torch.float64, device=s.device)
+    rc = lib.soft_topk_dftopk_forward(ctypes.c_void_p(s.data_ptr()), n, float(k), float(alpha),
+                                      ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                                      ctypes.c_void_p(m.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws_bytes,
+                                      _stream_handle(s))
+    _lib.check(rc, "soft_topk_dftopk_forward")
+    return p, b, m
 
 
 def rows_forward(s, k: float, alpha: float, out_p=None):

@@ -92,6 +92,10 @@ def load():
     lib.soft_topk_backward_ex.restype = ctypes.c_int
     lib.soft_topk_backward_noalloc.argtypes = [fp, fp, i64, dbl, dp, fp, vp]
     lib.soft_topk_backward_noalloc.restype = ctypes.c_int
+    lib.soft_topk_dftopk_forward.argtypes = [fp, i64, dbl, dbl, fp, dp, dp, vp, sz, vp]
+    lib.soft_topk_dftopk_forward.restype = ctypes.c_int
+    lib.soft_topk_dftopk_workspace_bytes.argtypes = [i64]
+    lib.soft_topk_dftopk_workspace_bytes.restype = sz
     lib.soft_topk_rows_forward.argtypes = [fp, i64, i64, dbl, dbl, fp, dp, vp, sz, vp]
     lib.soft_topk_rows_forward.restype = ctypes.c_int
     lib.soft_topk_rows_backward.argtypes = [fp, fp, i64, i64, dbl, dp, fp, vp, sz, vp]

@@ -1314,6 +1314,84 @@ int soft_topk_backward_noalloc(const float* grad_p, const float* scores, int64_t
     return SOFT_TOPK_OK;
 }
 
+namespace {
+
+struct DftPlan {
+    int32_t groups, g_emit;
+    size_t off_status, off_state, off_totals, off_rows, off_emitpart, total;
+};
+
+DftPlan dft_plan(int64_t n)
+{
+    DftPlan p;
+    const int64_t tiles = (n + kDftTileScores - 1) / kDftTileScores;
+    p.groups = (int32_t)std::max<int64_t>(1, std::min<int64_t>(tiles, kDftMaxGroups));
+    p.g_emit = emit_blocks(n);
+    size_t o = 0;
+    p.off_status = o;
+    o = align_up(o + sizeof(Status));
+    p.off_state = o;
+    o = align_up(o + sizeof(DftState) * 3);
+    p.off_totals = o;
+    o = align_up(o + sizeof(uint32_t) * 3 * kDftRowWords);
+    p.off_rows = o;
+    o = align_up(o + sizeof(uint32_t) * (size_t)p.groups * kDftRowWords);
+    p.off_emitpart = o;
+    o = align_up(o + sizeof(double) * (size_t)p.g_emit);
+    p.total = o;
+    return p;
+}
+
+}  // namespace
+
+size_t soft_topk_dftopk_workspace_bytes(int64_t n)
+{
+    if (n < 2 || !n_ok(n))
+        return 0;
+    return dft_plan(n).total;
+}
+
+int soft_topk_dftopk_forward(const float* scores, int64_t n, double k, double alpha, float* out_p, double* out_b,
+                             double* out_mass, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!scores || !out_p || !out_b || n < 2 || !n_ok(n))
+        return SOFT_TOPK_EINVAL;
+    if (!(alpha > 0.0) || !isfinite(alpha) || !(k >= 1.0) || !(k <= (double)(n - 1)) || k != floor(k))
+        return SOFT_TOPK_EINVAL;
+    const DftPlan plan = dft_plan(n);
+    if (!workspace || workspace_bytes < plan.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return SOFT_TOPK_EWORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    Status* status = reinterpret_cast<Status*>(ws + plan.off_status);
+    DftArgs a;
+    a.s = scores;
+    a.n = n;
+    a.k = (int64_t)k;
+    a.rows = reinterpret_cast<uint32_t*>(ws + plan.off_rows);
+    a.totals = reinterpret_cast<uint32_t*>(ws + plan.off_totals);
+    a.state = reinterpret_cast<DftState*>(ws + plan.off_state);
+    a.groups = plan.groups;
+    a.st = status;
+    a.out_b = out_b;
+    STK_HIP(launch_dftopk_threshold(a, st));
+    EmitArgs e;
+    e.s = scores;
+    e.n = n;
+    e.alpha = alpha;
+    e.log2e_over_alpha = kLog2e / alpha;
+    e.b = out_b;
+    e.p = out_p;
+    e.partials = reinterpret_cast<double*>(ws + plan.off_emitpart);
+    e.blocks = plan.g_emit;
+    e.st = status;
+    e.mirror = nullptr;
+    e.seg = seg_bufs(nullptr, 0, 0, 0);
+    STK_HIP(launch_emit(e, out_mass != nullptr, st));
+    STK_HIP(launch_dftopk_tail(status, out_p, n, out_mass, plan.g_emit, st));
+    return SOFT_TOPK_OK;
+}
+
 size_t soft_topk_rows_workspace_bytes(int64_t rows, int64_t n_row)
 {
     if (!rows_ok(rows, n_row) || n_row <= kRowMax)

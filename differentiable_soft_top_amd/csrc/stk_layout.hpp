@@ -430,4 +430,35 @@ struct SingleArgs {
 };
 hipError_t launch_single_status(const SingleArgs& a, hipStream_t stream);
 
+// DFTopK comparator: radix selection of the k-th and (k+1)-th largest
+// scores (three passes of 11, 11 and 10 key bits), then b at their midpoint.
+constexpr int kDftThreads = 256;
+constexpr int kDftBins = 2048;                 // digits of the 11-bit passes
+constexpr int kDftRowWords = 2 * kDftBins + 64;  // two targets' counts, the NaN count, padding
+constexpr int kDftMaxGroups = 256;
+constexpr int kDftTileScores = kDftThreads * 8 * 4;
+
+// Before pass P: for the (k+1)-th largest (target 0) and the k-th largest
+// (target 1), the key digits chosen so far and the rank left among the keys
+// that carry them.
+struct alignas(16) DftState {
+    uint32_t prefix[2];
+    uint32_t rank[2];
+};
+
+struct DftArgs {
+    const float* s;
+    int64_t n;
+    int64_t k;
+    uint32_t* rows;               // [groups][kDftRowWords] per-work-group counts
+    uint32_t* totals;             // [3][kDftRowWords] per-pass totals
+    DftState* state;              // [3] state before each pass
+    int32_t groups;
+    Status* st;                   // b, the NaN flag and the emission's mass
+    double* out_b;
+};
+hipError_t launch_dftopk_threshold(const DftArgs& a, hipStream_t stream);
+hipError_t launch_dftopk_tail(const Status* st, float* p, int64_t n, double* out_mass, int32_t blocks,
+                              hipStream_t stream);
+
 }  // namespace stk

@@ -293,6 +293,35 @@ int soft_topk_rows_backward(const float* grad_p, const float* scores, int64_t ro
 size_t soft_topk_rows_workspace_bytes(int64_t rows, int64_t n_row);
 
 /*
+ * DFTopK comparator.  The mlsanity.com page "Differentiable Fast Top-K
+ * Selection for Large-Scale Recommendation" (abstract) and the gist.science
+ * summary of Fast LapSum (section 2.3, "Relation to DFTopK") describe DFTopK
+ * as fixing the threshold at the midpoint of the k-th and (k+1)-th largest
+ * scores, LapSum's zero-temperature limit, which lets the selected mass
+ * drift from k at a finite temperature.  This call computes that operator
+ * for comparison: b = (x_(k) + x_(k+1)) / 2 in fp64 (x_(j) the j-th largest
+ * score, out_b one fp64, device) and out_p[i] = F((scores[i] - b)/alpha)
+ * (fp32, device), F the standard Laplace CDF, with the same emission as
+ * soft_topk_forward.  out_mass (one fp64, device; NULL = not wanted)
+ * receives sum_i p_i in fp64, whose distance from k is the drift.  k must be
+ * a whole number with 1 <= k <= n - 1 (2 <= n <= 2^31 - 1); alpha > 0.
+ * workspace: soft_topk_dftopk_workspace_bytes(n) bytes, 256-byte aligned.
+ * Route: an exact radix selection of the two order statistics, three
+ * streaming passes over the scores (11, 11 and 10 key bits), then the
+ * emission; fully asynchronous on `stream` (no host synchronisation).  A NaN
+ * score makes b, every p and the mass NaN (no error code, since nothing is
+ * read back); infinite scores are ordered like any other value.  There is
+ * no backward for this comparator.  Errors: EINVAL / EWORKSPACE before any
+ * launch; EHIP on a launch failure.
+ */
+int soft_topk_dftopk_forward(const float* scores, int64_t n, double k, double alpha,
+                             float* out_p, double* out_b, double* out_mass,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of soft_topk_dftopk_forward (0 for n outside [2, 2^31 - 1]). */
+size_t soft_topk_dftopk_workspace_bytes(int64_t n);
+
+/*
  * Threshold curve.  The gist.science summary of Fast LapSum (section 2.2,
  * "Full-Sort Solver") reads the root off the masses at the sorted scores;
  * this call returns them.  scores: fp32[n] (device); alpha > 0, finite.
