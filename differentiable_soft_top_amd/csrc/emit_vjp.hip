@@ -282,115 +282,102 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_kernel(VjpArgs a, in
 // emission, which knows b, records for each wave's 1024-score share of a
 // large VJP tile the scores whose fp32 density d_i = dens(s_i) is at least
 // kDensCut = 2^-40 (|s_i - b| < 27.7 alpha) and, when there are at most
-// kSegCap, their d values.  The VJP then reads those instead of the scores:
-// its reduction takes d from the record and 0 elsewhere (dropping terms
-// below 2^-40, which moves D and G by at most n 2^-40 and no gradient element
-// by more than 2^-39 of the largest one) and stores the matching g values
-// compacted in its workspace; its gradient kernel reads only the compacted
-// (d, g) pairs and writes +0 for the other scores.  If G is not finite (a
-// non-finite g) the gradient kernel reads the scores throughout.  The
-// record's metadata (16 masks and the count per segment) is fetched for
-// kMetaChunk tiles at once into LDS, so a tile's data loads are issued
-// together and waited for once.
+// kSegCap, their d values and their places in the segment.  The VJP then
+// reads those instead of the scores: its reduction takes d from the record
+// and 0 elsewhere (dropping terms below 2^-40, which moves D and G by at most
+// n 2^-40 and no gradient element by more than 2^-39 of the largest one) and
+// stores the matching g values, compacted, in its workspace; its gradient
+// kernel reads only the compacted (d, g, place) triples and writes +0 for the
+// other scores.  If G is not finite (a non-finite g) the gradient kernel
+// reads the scores throughout.
+//
+// A segment's place p of element i of lane l (the element at float4
+// tile * 1024 + (i / 4) * 256 + wave * 64 + l, component i mod 4) is
+// (i / 4) * 256 + l * 4 + (i mod 4): its offset in the wave's 1024-float LDS
+// tile when each lane stores its four float4 at float4 offset u * 64 + l.  So
+// the VJP moves whole float4 between registers and LDS and touches single
+// floats only for the listed scores -- one LDS access per listed score
+// instead of a ballot, a rank and a select per score.
 // ---------------------------------------------------------------------------
 namespace {
 
 constexpr float kDensCut = 0x1p-40f;                  // densities the record keeps (at least)
 constexpr int kSegV = 4 * kVjpBatchLarge;             // values per lane in a segment
 constexpr int kSegPerTile = kStreamThreads / kWave;   // segments per large VJP tile
-constexpr int kMetaChunk = 8;                         // tiles whose metadata is fetched at once
-static_assert(kSegV == 16 && kSegMeta == kSegV + 1 && (kSegCap & (kSegCap - 1)) == 0 && kSegCap >= 64,
-              "segment metadata: 16 masks and the count; power-of-two value regions");
+constexpr int kCntChunk = 8;                          // tiles whose counts are fetched at once
+static_assert(kSegV == 16 && kSegScores == kSegV * kWave && (kSegCap & (kSegCap - 1)) == 0 && kSegCap >= 64,
+              "segment record: 16 values per lane; power-of-two value regions");
 
 __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 
-// A segment's listed values move between global memory and a wave's LDS
-// block (kSegCap floats) as whole blocks -- coalesced, ceil(cnt / 64) loads
-// or stores per lane -- and lanes pick or place their own values in LDS.
-// (Per-lane gathers of a few scattered values from global memory cost far
-// more than the bytes they move.)  The record and the listed g values are
-// stored non-temporally: lines left dirty in the caches are written back
-// while the next kernel streams, and slow it more than reading them back
-// from HBM costs (measured at 10^8 scores: 10 us over the two VJP kernels).
 constexpr int kSegSteps = kSegCap / kWave;
 
-// blk[0 .. cnt) <- src[0 .. cnt) (all steps' loads issued, then one wait)
-__device__ __forceinline__ void block_in(const float* __restrict__ src, uint32_t cnt, float* blk)
-{
-    const int lane = lane_id();
-    float tmp[kSegSteps];
-#pragma unroll
-    for (int q = 0; q < kSegSteps; ++q) {
-        const uint32_t j = (uint32_t)(q * kWave + lane);
-        tmp[q] = j < cnt ? src[j] : 0.0f;
-    }
-#pragma unroll
-    for (int q = 0; q < kSegSteps; ++q) {
-        const uint32_t j = (uint32_t)(q * kWave + lane);
-        if (j < cnt)
-            blk[j] = tmp[q];
-    }
-    __builtin_amdgcn_wave_barrier();
-}
-
-// Two blocks at once (one wait for both).
-__device__ __forceinline__ void block_in2(const float* __restrict__ s0, const float* __restrict__ s1, uint32_t cnt,
-                                          float* b0, float* b1)
-{
-    const int lane = lane_id();
-    float t0[kSegSteps], t1[kSegSteps];
-#pragma unroll
-    for (int q = 0; q < kSegSteps; ++q) {
-        const uint32_t j = (uint32_t)(q * kWave + lane);
-        t0[q] = j < cnt ? s0[j] : 0.0f;
-        t1[q] = j < cnt ? s1[j] : 0.0f;
-    }
-#pragma unroll
-    for (int q = 0; q < kSegSteps; ++q) {
-        const uint32_t j = (uint32_t)(q * kWave + lane);
-        if (j < cnt) {
-            b0[j] = t0[q];
-            b1[j] = t1[q];
-        }
-    }
-    __builtin_amdgcn_wave_barrier();
-}
-
-// dst[0 .. cnt) <- blk[0 .. cnt)
-__device__ __forceinline__ void block_out(const float* blk, uint32_t cnt, float* __restrict__ dst)
-{
-    const int lane = lane_id();
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int q = 0; q < kSegSteps; ++q) {
-        const uint32_t j = (uint32_t)(q * kWave + lane);
-        if (j < cnt)
-            __builtin_nontemporal_store(blk[j], &dst[j]);
-    }
-}
-
-// Metadata of this wave's segments of tiles tile(c), c < kMetaChunk, into
-// mlds (tiles without a record, or past the vector, read as dense).
+// The counts of this wave's segments of tiles tile(c), c < kCntChunk
+// (tiles without a record, or past the vector, read as dense).
 template <typename TileOf>
-__device__ __forceinline__ void fetch_meta(const VjpArgs& a, TileOf tile_of, int64_t T, uint64_t (&mlds)[kMetaChunk][kSegMeta])
+__device__ __forceinline__ void fetch_counts(const VjpArgs& a, TileOf tile_of, int64_t T, uint32_t (&cnt)[kCntChunk])
 {
-    const int lane = lane_id();
     const int wave = wave_index();
     const int64_t Ts = a.seg_tiles < T ? a.seg_tiles : T;
-    const int j = lane < kSegMeta ? lane : kSegMeta - 1;
-    uint64_t w[kMetaChunk];
 #pragma unroll
-    for (int c = 0; c < kMetaChunk; ++c) {
-        const int64_t t = tile_of(c);
-        const int64_t tc = (t >= 0 && t < Ts) ? t : 0;
-        w[c] = a.seg.meta[(tc * kSegPerTile + wave) * kSegMeta + j];
-    }
-#pragma unroll
-    for (int c = 0; c < kMetaChunk; ++c) {
+    for (int c = 0; c < kCntChunk; ++c) {
         const int64_t t = tile_of(c);
         const bool has = t >= 0 && t < Ts;
-        if (lane < kSegMeta)
-            mlds[c][lane] = has ? w[c] : (lane == kSegV ? (uint64_t)kSegDense : 0ull);
+        cnt[c] = has ? a.seg.cnt[(has ? t : 0) * kSegPerTile + wave] : kSegDense;
+    }
+}
+
+// The wave's four float4 per lane into / out of its LDS tile.
+__device__ __forceinline__ void tile_store(float* tile, const float4 (&v)[kVjpBatchLarge])
+{
+    float4* t4 = reinterpret_cast<float4*>(tile);
+#pragma unroll
+    for (int u = 0; u < kVjpBatchLarge; ++u)
+        t4[u * kWave + lane_id()] = v[u];
+}
+
+__device__ __forceinline__ void tile_load(const float* tile, float4 (&v)[kVjpBatchLarge])
+{
+    const float4* t4 = reinterpret_cast<const float4*>(tile);
+#pragma unroll
+    for (int u = 0; u < kVjpBatchLarge; ++u)
+        v[u] = t4[u * kWave + lane_id()];
+}
+
+// A record entry: the listed score's fp32 density d (low word) and its
+// place in the segment (high word), one 8-byte store and load.
+__device__ __forceinline__ uint64_t seg_entry(float d, uint32_t place)
+{
+    return ((uint64_t)place << 32) | (uint64_t)__float_as_uint(d);
+}
+__device__ __forceinline__ float entry_d(uint64_t e) { return __uint_as_float((uint32_t)e); }
+__device__ __forceinline__ uint32_t entry_place(uint64_t e) { return (uint32_t)(e >> 32) & (kSegScores - 1); }
+
+// Whether every segment of a chunk has a record listing at most one value
+// per lane (the common case away from b).
+__device__ __forceinline__ bool chunk_is_light(const uint32_t (&cnt)[kCntChunk])
+{
+    bool ok = true;
+#pragma unroll
+    for (int c = 0; c < kCntChunk; ++c)
+        ok = ok && cnt[c] <= (uint32_t)kWave;
+    return ok;
+}
+
+// One light segment of the reduction: the g tile into LDS, the listed
+// lane's g picked at its place, its fp64 terms, and g * 0 of every g.
+__device__ __forceinline__ void light_tile(float* tile, const float4 (&vg)[kVjpBatchLarge], float d, uint32_t place,
+                                           uint32_t rec, double& D, double& G, float& zg, float& g_out)
+{
+    tile_store(tile, vg);
+#pragma unroll
+    for (int u = 0; u < kVjpBatchLarge; ++u)
+        zg += ((vg[u].x * 0.0f + vg[u].y * 0.0f) + (vg[u].z * 0.0f + vg[u].w * 0.0f));
+    __builtin_amdgcn_wave_barrier();
+    if ((uint32_t)lane_id() < rec) {
+        const float gj = tile[place];
+        acc_dg(d, gj, D, G);
+        g_out = gj;
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -400,17 +387,17 @@ __device__ __forceinline__ void fetch_meta(const VjpArgs& a, TileOf tile_of, int
 // Emission with the record, one wave per segment.  A first walk over the
 // wave's 16 values per lane evaluates the fp32 density d of each score and
 // lists the scores with d >= kDensCut (value index order, lanes ascending)
-// in LDS.  An unlisted score lies more than 27.7 alpha from b, so its p is d
-// (left of b) or 1 - d (right of b, 1 in fp32) with d < 2^-40: taken from
-// the fp32 d, p is within 1e-18 of the fp64 value, and the lane's unlisted
-// scores enter the mass as a count (right of b) plus an fp32 sum of their
-// signed d (at most 16 terms below 2^-40 per tile).  The listed scores --
-// about 4% of c4's -- are then evaluated 64 at a time: p with the fp64
-// exponential (as the score-only emission), d again for the record's
-// values, which go straight to global memory when the segment keeps them.
-// A last walk picks each lane's listed p out of LDS and writes p; it also
-// gathers the 16 masks, one per lane, for the record's metadata.  The fp64
-// arithmetic is thus spent once per 64 listed scores, not once per score.
+// in LDS, with their places.  An unlisted score lies more than 27.7 alpha
+// from b, so its p is d (left of b) or 1 - d (right of b, 1 in fp32) with
+// d < 2^-40: taken from the fp32 d, p is within 1e-18 of the fp64 value, and
+// the lane's unlisted scores enter the mass as a count (right of b) plus an
+// fp32 sum of their signed d (at most 16 terms below 2^-40 per tile).  The
+// listed scores -- about 4% of c4's -- are then evaluated 64 at a time: p
+// with the fp64 exponential (as the score-only emission), d again for the
+// record's values, which go straight to global memory with their places
+// when the segment keeps them.  A last walk picks each lane's listed p out
+// of LDS and writes p.  The fp64 arithmetic is thus spent once per 64 listed
+// scores, not once per score.
 template <bool kNT>
 __global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
 {
@@ -418,6 +405,7 @@ __global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
     constexpr int kL = kSegScores + kWave;  // the list, then one slot per lane for unlisted scores
     __shared__ double red[kStreamThreads / kWave];
     __shared__ float lst[kStreamThreads / kWave][kL];  // listed scores, then their p
+    __shared__ uint16_t lpl[kStreamThreads / kWave][kSegScores];  // places of the listed scores
     Status* st = a.st;
     if (st->solve_state != kSolveOk)
         return;
@@ -432,6 +420,7 @@ __global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
     const float4* s4 = reinterpret_cast<const float4*>(a.s);
     float4* p4 = reinterpret_cast<float4*>(a.p);
     float* ls = lst[wave];
+    uint16_t* lp = lpl[wave];
     for (int64_t t0 = blockIdx.x; t0 < T; t0 += G) {
         const int64_t t = T - 1 - t0;  // descending: see the note above
         const int64_t seg = t * kSegPerTile + wave;
@@ -454,22 +443,25 @@ __global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
             const uint64_t lm = __builtin_amdgcn_ballot_w64(nz);
             // unlisted lanes write a slot of their own past the list (no
             // branch, so each value's work stays in one block, in order)
-            ls[nz ? cnt + rank_in_mask(lm) : (uint32_t)(kSegScores + lane)] = sv;
+            const uint32_t at = nz ? cnt + rank_in_mask(lm) : (uint32_t)(kSegScores + lane);
+            ls[at] = sv;
+            if (nz)
+                lp[at] = (uint16_t)((i >> 2) * 256 + lane * 4 + (i & 3));
             cnt += (uint32_t)__popcll(lm);
             __builtin_amdgcn_sched_barrier(0);
         }
         acc += (double)n_right + (double)far_d;  // unlisted scores: p = 1 - d or d
         __builtin_amdgcn_wave_barrier();
         const bool keep = cnt <= (uint32_t)kSegCap;
-        float* val = a.seg.val + seg * kSegCap;
+        uint64_t* ent = a.seg.ent + seg * kSegCap;
         for (uint32_t j = (uint32_t)lane; j < cnt; j += kWave) {
             const float sv = ls[j];
             ls[j] = emit_one(sv, b, c, acc);
             if (keep)
-                __builtin_nontemporal_store(dens(sv, b, c), &val[j]);
+                __builtin_nontemporal_store(seg_entry(dens(sv, b, c), lp[j]), &ent[j]);
         }
         __builtin_amdgcn_wave_barrier();
-        uint32_t pre = 0, mlo = 0, mhi = 0;
+        uint32_t pre = 0;
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
             float o[4];
@@ -478,19 +470,14 @@ __global__ __launch_bounds__(kStreamThreads) void emit_seg_kernel(EmitArgs a)
                 const int i = 4 * u + h;
                 const bool nz = (nzb >> i) & 1u;
                 const uint64_t lm = __builtin_amdgcn_ballot_w64(nz);
-                mlo = lane == i ? (uint32_t)lm : mlo;  // lane i keeps mask i
-                mhi = lane == i ? (uint32_t)(lm >> 32) : mhi;
-                const float lp = ls[nz ? pre + rank_in_mask(lm) : (uint32_t)(kSegScores + lane)];
-                o[h] = nz ? lp : fp[i];
+                const float lpv = ls[nz ? pre + rank_in_mask(lm) : (uint32_t)(kSegScores + lane)];
+                o[h] = nz ? lpv : fp[i];
                 pre += (uint32_t)__popcll(lm);
             }
             store4<kNT>(&p4[t * (kB * kStreamThreads) + u * kStreamThreads + tid], make_float4(o[0], o[1], o[2], o[3]));
         }
-        uint64_t* meta = a.seg.meta + seg * kSegMeta;
-        if (lane < kSegV && keep)
-            __builtin_nontemporal_store(((uint64_t)mhi << 32) | (uint64_t)mlo, &meta[lane]);
-        else if (lane == kSegV)
-            __builtin_nontemporal_store(keep ? (uint64_t)cnt : (uint64_t)kSegDense, &meta[kSegV]);
+        if (lane == 0)
+            __builtin_nontemporal_store(keep ? cnt : kSegDense, &a.seg.cnt[seg]);
         __builtin_amdgcn_wave_barrier();
     }
     for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads)
@@ -508,7 +495,7 @@ namespace {
 
 __device__ __forceinline__ bool vjp_seg_usable(const VjpArgs& a)
 {
-    if (a.fst == nullptr || a.seg.meta == nullptr)
+    if (a.fst == nullptr || a.seg.cnt == nullptr)
         return false;
     const Status* f = a.fst;
     return f->seg_valid != 0u && f->b == *a.b && f->seg_n == (uint64_t)a.n && f->seg_alpha == a.alpha &&
@@ -517,14 +504,19 @@ __device__ __forceinline__ bool vjp_seg_usable(const VjpArgs& a)
 
 }  // namespace
 
+// (D, G) with the record.  A listed segment: the wave's g tile goes to LDS
+// as whole float4, each listed (d, place) pair picks its g there -- one
+// fp64 term per listed score -- and the listed g values are stored,
+// compacted, for the gradient kernel.  Every g still enters G as g * 0 (an
+// fp32 sum, folded in at the end), so a non-finite g makes G non-finite as
+// in the score-reading kernel.  A dense segment reads the scores.
 __global__ __launch_bounds__(kStreamThreads) void vjp_reduce_seg_kernel(VjpArgs a)
 {
     constexpr int kB = kVjpBatchLarge;
     __shared__ double red[2][kStreamThreads / kWave];
-    __shared__ uint64_t mlds[kStreamThreads / kWave][kMetaChunk][kSegMeta];
-    __shared__ float dblk[kStreamThreads / kWave][kSegCap];
-    __shared__ float gblk[kStreamThreads / kWave][kSegCap];
+    __shared__ float gt[kStreamThreads / kWave][kSegScores];
     const int tid = threadIdx.x;
+    const int lane = lane_id();
     const int wave = wave_index();
     const double b = *a.b;
     const double c = a.log2e_over_alpha;
@@ -533,85 +525,121 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_reduce_seg_kernel(VjpArgs 
     const int64_t T = whole_tiles<kB>(a.n);
     const float4* s4 = reinterpret_cast<const float4*>(a.s);
     const float4* g4 = reinterpret_cast<const float4*>(a.g);
+    float* tile = gt[wave];
     double D = 0.0, G_ = 0.0;
-    for (int64_t tb = blockIdx.x; tb < T; tb += kMetaChunk * G) {
+    float zg = 0.0f;  // sum of g * 0 over listed segments: NaN iff some g there is not finite
+    for (int64_t tb = blockIdx.x; tb < T; tb += kCntChunk * G) {
+        uint32_t cnts[kCntChunk];
         if (use_seg)
-            fetch_meta(a, [&](int k) { return tb + (int64_t)k * G; }, T, mlds[wave]);
-        for (int k = 0; k < kMetaChunk; ++k) {
+            fetch_counts(a, [&](int k) { return tb + (int64_t)k * G; }, T, cnts);
+        if (use_seg && chunk_is_light(cnts)) {
+            // every segment of the chunk lists at most one value per lane:
+            // all (d, place) entries are read at once, and the listed g
+            // values are stored at the end, so no store sits between a load
+            // and its use
+            float dj[kCntChunk], gk[kCntChunk];
+            uint32_t pj[kCntChunk];
+#pragma unroll
+            for (int k = 0; k < kCntChunk; ++k) {
+                const int64_t t = tb + (int64_t)k * G;
+                const int64_t seg = (t < T ? t : 0) * kSegPerTile + wave;
+                const uint64_t e = a.seg.ent[seg * kSegCap + lane];
+                dj[k] = entry_d(e);
+                pj[k] = entry_place(e);
+                gk[k] = 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < kCntChunk; ++k) {
+                const int64_t t0 = tb + (int64_t)k * G;
+                float4 va[kB];
+                if (t0 < T) {
+                    load_q<kB>(g4, t0, va);
+                    light_tile(tile, va, dj[k], pj[k], cnts[k], D, G_, zg, gk[k]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kCntChunk; ++k) {
+                const int64_t t = tb + (int64_t)k * G;
+                if (t < T && (uint32_t)lane < cnts[k])
+                    __builtin_nontemporal_store(gk[k], &a.gl[(t * kSegPerTile + wave) * kSegCap + lane]);
+            }
+            continue;
+        }
+        for (int k = 0; k < kCntChunk; ++k) {
             const int64_t t = tb + (int64_t)k * G;
             if (t >= T)
                 break;
-            const uint32_t rec = use_seg ? (uint32_t)mlds[wave][k][kSegV] : kSegDense;
+            const uint32_t rec = use_seg ? cnts[k] : kSegDense;
             float4 vg[kB];
-            float d[kSegV];
-            // each branch issues all of its loads (g first) before any use
             if (rec == kSegDense) {
                 float4 vs[kB];
                 load_q<kB>(g4, t, vg);
                 load_q<kB>(s4, t, vs);
 #pragma unroll
                 for (int u = 0; u < kB; ++u) {
-                    d[4 * u + 0] = dens(vs[u].x, b, c);
-                    d[4 * u + 1] = dens(vs[u].y, b, c);
-                    d[4 * u + 2] = dens(vs[u].z, b, c);
-                    d[4 * u + 3] = dens(vs[u].w, b, c);
+                    acc_dg(dens(vs[u].x, b, c), vg[u].x, D, G_);
+                    acc_dg(dens(vs[u].y, b, c), vg[u].y, D, G_);
+                    acc_dg(dens(vs[u].z, b, c), vg[u].z, D, G_);
+                    acc_dg(dens(vs[u].w, b, c), vg[u].w, D, G_);
                 }
             } else {
+                const int64_t seg = t * kSegPerTile + wave;
+                const uint64_t* ent = a.seg.ent + seg * kSegCap;
+                uint64_t ej[kSegSteps];
                 load_q<kB>(g4, t, vg);
-                block_in(a.seg.val + (t * kSegPerTile + wave) * kSegCap, rec, dblk[wave]);
-                // d from the block; this lane's listed g values into the g block
-                const uint64_t* m = mlds[wave][k];
-                uint64_t mk[kSegV];
 #pragma unroll
-                for (int i = 0; i < kSegV; ++i)
-                    mk[i] = m[i];
-                const int lane = lane_id();
-                uint32_t pre = 0;
-#pragma unroll
-                for (int i = 0; i < kSegV; ++i) {
-                    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(mk[i] >> 32));
-                    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)mk[i]);
-                    const uint64_t lm = ((uint64_t)hi << 32) | lo;
-                    const bool li = (lm >> lane) & 1ull;
-                    const uint32_t p = pre + rank_in_mask(lm);
-                    const float4 g = vg[i / 4];
-                    const float gi = (i & 3) == 0 ? g.x : (i & 3) == 1 ? g.y : (i & 3) == 2 ? g.z : g.w;
-                    d[i] = li ? dblk[wave][p] : 0.0f;
-                    if (li)
-                        gblk[wave][p] = gi;
-                    pre += (uint32_t)__popcll(lm);
+                for (int q = 0; q < kSegSteps; ++q) {
+                    const uint32_t j = (uint32_t)(q * kWave + lane);
+                    ej[q] = j < rec ? ent[j] : 0ull;
                 }
-                block_out(gblk[wave], rec, a.gl + (t * kSegPerTile + wave) * kSegCap);
-                __builtin_amdgcn_wave_barrier();
-            }
-            // the score-reading kernel's sums
+                float dj[kSegSteps];
+                uint32_t pj[kSegSteps];
 #pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                acc_dg(d[4 * u + 0], vg[u].x, D, G_);
-                acc_dg(d[4 * u + 1], vg[u].y, D, G_);
-                acc_dg(d[4 * u + 2], vg[u].z, D, G_);
-                acc_dg(d[4 * u + 3], vg[u].w, D, G_);
+                for (int q = 0; q < kSegSteps; ++q) {
+                    dj[q] = entry_d(ej[q]);
+                    pj[q] = entry_place(ej[q]);
+                }
+                tile_store(tile, vg);
+#pragma unroll
+                for (int u = 0; u < kB; ++u)
+                    zg += ((vg[u].x * 0.0f + vg[u].y * 0.0f) + (vg[u].z * 0.0f + vg[u].w * 0.0f));
+                __builtin_amdgcn_wave_barrier();
+                float* gl = a.gl + seg * kSegCap;
+#pragma unroll
+                for (int q = 0; q < kSegSteps; ++q) {
+                    const uint32_t j = (uint32_t)(q * kWave + lane);
+                    if (j < rec) {
+                        const float gj = tile[pj[q]];
+                        acc_dg(dj[q], gj, D, G_);
+                        __builtin_nontemporal_store(gj, &gl[j]);
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
             }
         }
     }
     for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads) {
         acc_dg(dens(a.s[i], b, c), a.g[i], D, G_);
     }
+    G_ += (double)zg;
     block_sum_to(D, red[0], &a.partials[2 * blockIdx.x]);
     __syncthreads();
     block_sum_to(G_, red[1], &a.partials[2 * blockIdx.x + 1]);
 }
 
+// The gradient with the record.  A listed segment: the wave zeroes its LDS
+// tile, each listed (d, g, place) triple writes (d/alpha)(g - G/D) at its
+// place, and the lanes move the tile out as whole float4.  A dense segment
+// reads the scores and g.
 template <bool kNT>
 __global__ __launch_bounds__(kStreamThreads) void vjp_apply_seg_kernel(VjpArgs a, int32_t reduce_blocks)
 {
     constexpr int kB = kVjpBatchLarge;
     __shared__ double red[2][kStreamThreads / kWave];
     __shared__ double tot[2];
-    __shared__ uint64_t mlds[kStreamThreads / kWave][kMetaChunk][kSegMeta];
-    __shared__ float dblk[kStreamThreads / kWave][kSegCap];
-    __shared__ float gblk[kStreamThreads / kWave][kSegCap];
+    __shared__ float ot[kStreamThreads / kWave][kSegScores];
     const int tid = threadIdx.x;
+    const int lane = lane_id();
     const int wave = wave_index();
     double D = 0.0, G_ = 0.0;
     for (int i = tid; i < reduce_blocks; i += kStreamThreads) {
@@ -634,53 +662,103 @@ __global__ __launch_bounds__(kStreamThreads) void vjp_apply_seg_kernel(VjpArgs a
     const float4* s4 = reinterpret_cast<const float4*>(a.s);
     const float4* g4 = reinterpret_cast<const float4*>(a.g);
     float4* o4 = reinterpret_cast<float4*>(a.grad);
-    for (int64_t tb = blockIdx.x; tb < T; tb += kMetaChunk * G) {
+    float* tile = ot[wave];
+    for (int64_t tb = blockIdx.x; tb < T; tb += kCntChunk * G) {
         // descending tiles: see the note above
+        uint32_t cnts[kCntChunk];
         if (use_seg)
-            fetch_meta(a, [&](int k) { return T - 1 - (tb + (int64_t)k * G); }, T, mlds[wave]);
-        for (int k = 0; k < kMetaChunk; ++k) {
+            fetch_counts(a, [&](int k) { return T - 1 - (tb + (int64_t)k * G); }, T, cnts);
+        if (use_seg && chunk_is_light(cnts)) {
+            // every segment of the chunk lists at most one value per lane:
+            // all (d, g, place) triples are read at once, then each tile is
+            // composed in LDS and stored
+            uint64_t ec[kCntChunk];
+            float gc[kCntChunk];
+#pragma unroll
+            for (int k = 0; k < kCntChunk; ++k) {
+                const int64_t t0 = tb + (int64_t)k * G;
+                const int64_t seg = (t0 < T ? T - 1 - t0 : 0) * kSegPerTile + wave;
+                ec[k] = a.seg.ent[seg * kSegCap + lane];
+                gc[k] = a.gl[seg * kSegCap + lane];
+            }
+#pragma unroll
+            for (int k = 0; k < kCntChunk; ++k) {
+                const int64_t t0 = tb + (int64_t)k * G;
+                if (t0 >= T)
+                    break;
+                const int64_t t = T - 1 - t0;
+                float4 o[kB];
+#pragma unroll
+                for (int u = 0; u < kB; ++u)
+                    o[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                tile_store(tile, o);
+                __builtin_amdgcn_wave_barrier();
+                if ((uint32_t)lane < cnts[k])
+                    tile[entry_place(ec[k])] = entry_d(ec[k]) * inv_alpha * minus_ratio(gc[k], ratio);
+                __builtin_amdgcn_wave_barrier();
+                tile_load(tile, o);
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int u = 0; u < kB; ++u)
+                    store4<kNT>(&o4[t * (kB * kStreamThreads) + u * kStreamThreads + tid], o[u]);
+            }
+            continue;
+        }
+        for (int k = 0; k < kCntChunk; ++k) {
             const int64_t t0 = tb + (int64_t)k * G;
             if (t0 >= T)
                 break;
             const int64_t t = T - 1 - t0;
-            const uint32_t rec = use_seg ? (uint32_t)mlds[wave][k][kSegV] : kSegDense;
-            float o[kSegV];
+            const uint32_t rec = use_seg ? cnts[k] : kSegDense;
+            float4 o[kB];
             if (rec == kSegDense) {
                 float4 vs[kB], vg[kB];
                 load_q<kB>(s4, t, vs);
                 load_q<kB>(g4, t, vg);
 #pragma unroll
                 for (int u = 0; u < kB; ++u) {
-                    o[4 * u + 0] = dens(vs[u].x, b, c) * inv_alpha * minus_ratio(vg[u].x, ratio);
-                    o[4 * u + 1] = dens(vs[u].y, b, c) * inv_alpha * minus_ratio(vg[u].y, ratio);
-                    o[4 * u + 2] = dens(vs[u].z, b, c) * inv_alpha * minus_ratio(vg[u].z, ratio);
-                    o[4 * u + 3] = dens(vs[u].w, b, c) * inv_alpha * minus_ratio(vg[u].w, ratio);
+                    o[u].x = dens(vs[u].x, b, c) * inv_alpha * minus_ratio(vg[u].x, ratio);
+                    o[u].y = dens(vs[u].y, b, c) * inv_alpha * minus_ratio(vg[u].y, ratio);
+                    o[u].z = dens(vs[u].z, b, c) * inv_alpha * minus_ratio(vg[u].z, ratio);
+                    o[u].w = dens(vs[u].w, b, c) * inv_alpha * minus_ratio(vg[u].w, ratio);
                 }
             } else {
                 const int64_t seg = t * kSegPerTile + wave;
-                block_in2(a.seg.val + seg * kSegCap, a.gl + seg * kSegCap, rec, dblk[wave], gblk[wave]);
-                const uint64_t* m = mlds[wave][k];
-                uint64_t mk[kSegV];
+                const uint64_t* ent = a.seg.ent + seg * kSegCap;
+                const float* gl = a.gl + seg * kSegCap;
+                uint64_t ej[kSegSteps];
+                float gj[kSegSteps];
 #pragma unroll
-                for (int i = 0; i < kSegV; ++i)
-                    mk[i] = m[i];
-                const int lane = lane_id();
-                uint32_t pre = 0;
-#pragma unroll
-                for (int i = 0; i < kSegV; ++i) {
-                    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(mk[i] >> 32));
-                    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)mk[i]);
-                    const uint64_t lm = ((uint64_t)hi << 32) | lo;
-                    const bool li = (lm >> lane) & 1ull;
-                    const uint32_t p = pre + rank_in_mask(lm);
-                    o[i] = li ? dblk[wave][p] * inv_alpha * minus_ratio(gblk[wave][p], ratio) : 0.0f;
-                    pre += (uint32_t)__popcll(lm);
+                for (int q = 0; q < kSegSteps; ++q) {
+                    const uint32_t j = (uint32_t)(q * kWave + lane);
+                    ej[q] = j < rec ? ent[j] : 0ull;
+                    gj[q] = j < rec ? gl[j] : 0.0f;
                 }
+                float dj[kSegSteps];
+                uint32_t pj[kSegSteps];
+#pragma unroll
+                for (int q = 0; q < kSegSteps; ++q) {
+                    dj[q] = entry_d(ej[q]);
+                    pj[q] = entry_place(ej[q]);
+                }
+#pragma unroll
+                for (int u = 0; u < kB; ++u)
+                    o[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                tile_store(tile, o);
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int q = 0; q < kSegSteps; ++q) {
+                    const uint32_t j = (uint32_t)(q * kWave + lane);
+                    if (j < rec)
+                        tile[pj[q]] = dj[q] * inv_alpha * minus_ratio(gj[q], ratio);
+                }
+                __builtin_amdgcn_wave_barrier();
+                tile_load(tile, o);
+                __builtin_amdgcn_wave_barrier();
             }
 #pragma unroll
             for (int u = 0; u < kB; ++u)
-                store4<kNT>(&o4[t * (kB * kStreamThreads) + u * kStreamThreads + tid],
-                            make_float4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]));
+                store4<kNT>(&o4[t * (kB * kStreamThreads) + u * kStreamThreads + tid], o[u]);
         }
     }
     for (int64_t i = ragged_start<kB>(a.n, T) + tid; i < a.n; i += kStreamThreads)
@@ -693,9 +771,9 @@ hipError_t launch_emit(const EmitArgs& a, bool fold_mass, hipStream_t stream)
     const dim3 grid(a.blocks), block(kStreamThreads);
     if (!vec)
         STK_LAUNCH(kKEmit, stream, (emit_kernel<1, false, false>), grid, block, 0, stream, a);
-    else if (a.seg.meta != nullptr && a.n >= kSegMinN && a.n >= kNontemporalMin)
+    else if (a.seg.cnt != nullptr && a.n >= kSegMinN && a.n >= kNontemporalMin)
         STK_LAUNCH(kKEmit, stream, emit_seg_kernel<true>, grid, block, 0, stream, a);
-    else if (a.seg.meta != nullptr && a.n >= kSegMinN)
+    else if (a.seg.cnt != nullptr && a.n >= kSegMinN)
         STK_LAUNCH(kKEmit, stream, emit_seg_kernel<false>, grid, block, 0, stream, a);
     else if (a.n >= kNontemporalMin)
         STK_LAUNCH(kKEmit, stream, (emit_kernel<kEmitBatchLarge, true, true>), grid, block, 0, stream, a);
@@ -718,7 +796,7 @@ hipError_t launch_vjp(const VjpArgs& a, hipStream_t stream)
     if (!vec) {
         STK_LAUNCH(kKVjpReduce, stream, (vjp_reduce_kernel<1, false>), gr, block, 0, stream, r);
         STK_LAUNCH(kKVjpApply, stream, (vjp_apply_kernel<1, false, false>), ga, block, 0, stream, a, r.blocks);
-    } else if (a.seg.meta != nullptr && a.n >= kSegMinN) {
+    } else if (a.seg.cnt != nullptr && a.n >= kSegMinN) {
         STK_LAUNCH(kKVjpReduce, stream, vjp_reduce_seg_kernel, gr, block, 0, stream, r);
         if (a.n >= kNontemporalMin)
             STK_LAUNCH(kKVjpApply, stream, vjp_apply_seg_kernel<true>, ga, block, 0, stream, a, r.blocks);

@@ -255,26 +255,26 @@ int64_t seg_count(int64_t n)
     return n >= kSegMinN ? tiles * (kStreamThreads / kWave) : 0;
 }
 
-size_t seg_layout(int64_t n, size_t o, int64_t* n_seg, size_t* off_meta, size_t* off_val)
+size_t seg_layout(int64_t n, size_t o, int64_t* n_seg, size_t* off_cnt, size_t* off_ent)
 {
     const int64_t segs = seg_count(n);
     *n_seg = segs;
-    *off_meta = o;
-    o = align_up(o + sizeof(uint64_t) * kSegMeta * (size_t)segs);
-    *off_val = o;
-    o = align_up(o + sizeof(float) * kSegCap * (size_t)segs);
+    *off_cnt = o;
+    o = align_up(o + sizeof(uint32_t) * (size_t)segs);
+    *off_ent = o;
+    o = align_up(o + sizeof(uint64_t) * kSegCap * (size_t)segs);
     return o;
 }
 
 // The segment buffers of a forward workspace at ws (all null when unused).
-SegBufs seg_bufs(char* ws, int64_t n_seg, size_t off_meta, size_t off_val)
+SegBufs seg_bufs(char* ws, int64_t n_seg, size_t off_cnt, size_t off_ent)
 {
     SegBufs b;
-    b.meta = nullptr;
-    b.val = nullptr;
+    b.cnt = nullptr;
+    b.ent = nullptr;
     if (n_seg > 0) {
-        b.meta = reinterpret_cast<uint64_t*>(ws + off_meta);
-        b.val = reinterpret_cast<float*>(ws + off_val);
+        b.cnt = reinterpret_cast<uint32_t*>(ws + off_cnt);
+        b.ent = reinterpret_cast<uint64_t*>(ws + off_ent);
     }
     return b;
 }
@@ -438,7 +438,7 @@ int enqueue_emit(const Ctx& x, bool fold_mass)
     e.blocks = x.plan.g_emit;
     e.st = x.st;
     e.mirror = x.mirror1;
-    e.seg = seg_bufs(x.ws, x.plan.n_seg, x.plan.off_seg_meta, x.plan.off_seg_val);
+    e.seg = seg_bufs(x.ws, x.plan.n_seg, x.plan.off_seg_cnt, x.plan.off_seg_ent);
     STK_HIP(launch_emit(e, fold_mass, x.stream));
     return SOFT_TOPK_OK;
 }
@@ -753,7 +753,7 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     o = align_up(o + sizeof(Status));
     // saturated-score segments first: their place depends on n alone, so the
     // backward can find them in a forward workspace
-    o = seg_layout(n, o, &p.n_seg, &p.off_seg_meta, &p.off_seg_val);
+    o = seg_layout(n, o, &p.n_seg, &p.off_seg_cnt, &p.off_seg_ent);
     p.off_samples = o;  // candidate keys of the localisation, one region per filter group
     o = align_up(o + sizeof(uint32_t) * (size_t)filter_groups(m) * kFilterPer);
     p.off_frec = o;
@@ -894,8 +894,8 @@ size_t soft_topk_record_bytes(int64_t n)
     if (!n_ok(n))
         return 0;
     int64_t n_seg;
-    size_t off_meta, off_val;
-    return seg_layout(n, align_up(sizeof(Status)), &n_seg, &off_meta, &off_val);
+    size_t off_cnt, off_ent;
+    return seg_layout(n, align_up(sizeof(Status)), &n_seg, &off_cnt, &off_ent);
 }
 
 size_t soft_topk_backward_workspace_bytes(int64_t n)
@@ -1254,12 +1254,12 @@ int soft_topk_backward_ex(const float* grad_p, const float* scores, int64_t n, d
                                     align_up(sizeof(double) * 2 * (size_t)vjp_partial_blocks(n)));
     if (fwd_workspace) {
         int64_t n_seg;
-        size_t off_meta, off_val;
-        const size_t end = seg_layout(n, align_up(sizeof(Status)), &n_seg, &off_meta, &off_val);
+        size_t off_cnt, off_ent;
+        const size_t end = seg_layout(n, align_up(sizeof(Status)), &n_seg, &off_cnt, &off_ent);
         if (n_seg > 0 && fwd_workspace_bytes >= end) {
             char* fw = static_cast<char*>(const_cast<void*>(fwd_workspace));
             a.fst = reinterpret_cast<const Status*>(fw);
-            a.seg = seg_bufs(fw, n_seg, off_meta, off_val);
+            a.seg = seg_bufs(fw, n_seg, off_cnt, off_ent);
             a.reduce_blocks = seg_grid(n, kGridVjpSegReduce);
             a.blocks = seg_grid(n, kGridVjpSegApply);
         }

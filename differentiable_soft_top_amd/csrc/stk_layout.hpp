@@ -50,7 +50,6 @@ constexpr int kFilterPer = 1024;         // samples per filter work-group (one p
 // scores on.
 constexpr int kSegScores = 1024;
 constexpr int kSegCap = 256;
-constexpr int kSegMeta = 17;                 // u64 words per segment: 16 listed masks, count
 constexpr uint32_t kSegDense = 0xFFFFFFFFu;
 constexpr int64_t kSegMinN = 1 << 22;  // measured: from 10^7 scores on the record pays
 static_assert(kStreamThreads == 256 && kVjpBatchLarge == 4,
@@ -205,7 +204,7 @@ struct Plan {
     size_t off_status, off_samples, off_frec, off_p1part, off_band, off_band_sorted;
     size_t off_hist, off_bstart, off_agg, off_scan, off_emitpart, off_keys0, off_keys1, off_rhist, off_super;
     int64_t n_seg;               // saturated-score segments (0: not used at this n)
-    size_t off_seg_meta, off_seg_val;
+    size_t off_seg_cnt, off_seg_ent;
     size_t total;
 };
 
@@ -267,9 +266,9 @@ hipError_t launch_debug_sample(const float* s, int64_t n, float alpha, uint64_t 
 
 // Saturated-score segment storage (all null when not used).
 struct SegBufs {
-    uint64_t* meta;               // [n_seg][kSegMeta]: listed masks (words 0..15, only when sparse),
-                                  // listed count or kSegDense (word 16, low half)
-    float* val;                   // [n_seg][kSegCap] listed d values in (value index, lane) order
+    uint32_t* cnt;                // [n_seg] listed count, or kSegDense
+    uint64_t* ent;                // [n_seg][kSegCap] listed entries in (value index, lane) order:
+                                  // fp32 density d (low word), place in the segment (high word)
 };
 
 struct Pass1Args {

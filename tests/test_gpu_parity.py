@@ -565,10 +565,11 @@ def _assert_score_path_equal(gs, gd, g_np, alpha):
 
 
 def test_segments_nonfinite_cotangent_and_foreign_threshold(dev):
-    """A non-finite cotangent at a saturated score still enters G = sum g d
-    as g * 0 = NaN, so the whole gradient is NaN, as in the score-reading
-    path; a threshold other than the forward's makes the backward read the
-    scores."""
+    """A non-finite cotangent at a saturated score still enters G (as
+    g * 0 = NaN), so the whole gradient is NaN, as in the score-reading path
+    (the sign and payload of a NaN carry no meaning and may differ between
+    the routes); a threshold other than the forward's makes the backward read
+    the scores."""
     s_np, k, alpha, w = make_workload("c4", n=SEG_N)
     g_np = draw_grad(s_np.size, w.seed)
     far = np.flatnonzero(s_np < 0.5)[:3]
@@ -580,7 +581,7 @@ def test_segments_nonfinite_cotangent_and_foreign_threshold(dev):
     g_seg = stk.backward(g, s, alpha, b, fwd_workspace=ws).cpu().numpy()
     g_dense = stk.backward(g, s, alpha, b).cpu().numpy()
     assert np.all(np.isnan(g_seg))
-    assert np.array_equal(_bits(g_seg), _bits(g_dense))
+    assert np.all(np.isnan(g_dense))
     g_np = draw_grad(s_np.size, w.seed)
     g = torch.from_numpy(g_np).to(dev)
     g_seg = stk.backward(g, s, alpha, b, fwd_workspace=ws).cpu().numpy()
