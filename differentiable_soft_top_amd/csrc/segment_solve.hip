@@ -46,6 +46,122 @@ constexpr int kSW = kST / kWave;         // its waves
 static_assert(kTile <= kBucketCap, "full-sort tiles must fit the level-2 buffers");
 static_assert(kBuckets % kST == 0, "pass-1 super partials per thread");
 
+// ---------------------------------------------------------------------------
+// Reference-point sums.  When every point of a solve lies within kRefSpan
+// (in units of alpha / log2 e) of a reference r, the anchored sums of the
+// full-sort solver are ratios of plain sums: with E(x) = 2^{(x - r) c}
+// (c = log2 e / alpha),
+//   sum_{i <= j} e^{(x_i - x_j)/alpha} = (sum_{i <= j} E_i) / E_j,
+//   sum_{i >  j} e^{-(x_i - x_j)/alpha} = E_j * sum_{i > j} 1/E_i,
+// and every E and 1/E is a normal fp64 number.  The work-group scans then
+// carry fp64 additions instead of an exponential per combination, and each
+// point costs one exponential, evaluated independently rather than along a
+// dependency chain.  All sums are of positive terms (relative error ~1e-16
+// times the scan depth), as accurate as the anchored form.  A bracket end at
+// infinity, or a wider span, keeps the anchored form.
+// ---------------------------------------------------------------------------
+constexpr double kRefSpan = 1800.0;
+
+// 2^y for |y| <= 1022: the series of exp2_nonpos without its clamp to y <= 0.
+__device__ __forceinline__ double exp2_ref(double y)
+{
+    const double j = __builtin_rint(y);
+    const double t = (y - j) * kLn2;
+    double p = 2.08767569878681e-09;
+    p = fma(p, t, 2.505210838544172e-08);
+    p = fma(p, t, 2.755731922398589e-07);
+    p = fma(p, t, 2.7557319223985893e-06);
+    p = fma(p, t, 2.48015873015873e-05);
+    p = fma(p, t, 0.0001984126984126984);
+    p = fma(p, t, 0.001388888888888889);
+    p = fma(p, t, 0.008333333333333333);
+    p = fma(p, t, 0.041666666666666664);
+    p = fma(p, t, 0.16666666666666666);
+    p = fma(p, t, 0.5);
+    p = fma(p, t, 1.0);
+    p = fma(p, t, 1.0);
+    return ldexp(p, (int)j);
+}
+
+// Exclusive work-group scans of a pair of fp64 sums and a count: the
+// prefix of p over earlier threads, the suffix of s over later threads,
+// the prefix of the count, and the three totals.  Exclusive values come
+// from shifting the inclusive ones (no subtraction), so a small sum next to
+// a large one keeps its relative accuracy.
+struct RefScan {
+    double p_before, s_after, p_all, s_all;
+    uint32_t c_before, c_all;
+};
+
+template <int kSWn>
+__device__ __forceinline__ RefScan ref_scan_publish(double p, double s, uint32_t cnt, WaveTot* wt, RefScan* part)
+{
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    double pi = p, si = s;
+    uint32_t ci = cnt;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const double op = __shfl_up(pi, off, kWave);
+        const double os = __shfl_down(si, off, kWave);
+        const uint32_t oc = __shfl_up(ci, off, kWave);
+        if (lane >= off) {
+            pi += op;
+            ci += oc;
+        }
+        if (lane + off < kWave)
+            si += os;
+    }
+    RefScan r;
+    r.p_before = __shfl_up(pi, 1, kWave);
+    r.c_before = __shfl_up(ci, 1, kWave);
+    r.s_after = __shfl_down(si, 1, kWave);
+    if (lane == 0) {
+        r.p_before = 0.0;
+        r.c_before = 0u;
+    }
+    if (lane == kWave - 1)
+        r.s_after = 0.0;
+    if (lane == kWave - 1) {
+        wt[wave].pv = pi;
+        wt[wave].cnt = ci;
+    }
+    if (lane == 0)
+        wt[wave].sv = si;
+    *part = r;
+    return r;
+}
+
+// after the barrier that follows ref_scan_publish
+template <int kSWn>
+__device__ __forceinline__ RefScan ref_scan_finish(const WaveTot* wt, const RefScan& part)
+{
+    const int wave = threadIdx.x / kWave;
+    RefScan r = part;
+    double pb = 0.0, sa = 0.0, pall = 0.0, sall = 0.0;
+    uint32_t cb = 0u, call = 0u;
+    for (int w = 0; w < kSWn; ++w) {
+        if (w < wave) {
+            pb += wt[w].pv;
+            cb += wt[w].cnt;
+        }
+        pall += wt[w].pv;
+        call += wt[w].cnt;
+    }
+    for (int w = kSWn - 1; w >= 0; --w) {
+        if (w > wave)
+            sa += wt[w].sv;
+        sall += wt[w].sv;
+    }
+    r.p_before += pb;
+    r.c_before += cb;
+    r.s_after += sa;
+    r.p_all = pall;
+    r.s_all = sall;
+    r.c_all = call;
+    return r;
+}
+
 // Load cnt values (R per thread), sort into keys[0 .. cnt).  Bucket sort
 // first (band values are spread evenly over a narrow range); if a bucket
 // overflows its register network, the values are loaded again and sorted by
@@ -146,7 +262,112 @@ struct Level2Job {
     uint32_t Cu;
 };
 
-__device__ void level2(const SolveArgs& a, SolveLds& L, const Level2Job& job)
+// Whether level 2 can use reference-point sums: the end nodes that carry
+// weight and the group's values within kRefSpan; *ref gets the reference.
+__device__ __forceinline__ bool level2_ref_ok(const Level2Job& job, const SolveLds& L, double c, double* ref)
+{
+    if (job.cntu < 1)
+        return false;
+    double lo = key_to_float(L.keys[0]);
+    double hi = key_to_float(L.keys[job.cntu - 1]);
+    if (job.lo_node.v > 0.0)
+        lo = fmin(lo, (double)job.lo_node.x);
+    if (job.Su.v > 0.0)
+        hi = fmax(hi, (double)job.Su.x);
+    if (!(lo > -INFINITY && hi < INFINITY) || !((hi - lo) * c <= kRefSpan))
+        return false;
+    *ref = 0.5 * (lo + hi);
+    return true;
+}
+
+// Level 2 with reference-point sums (the same breakpoint masses, the same
+// last breakpoint with mass >= k and the same closed form as `level2`).
+__device__ __forceinline__ void level2_ref(const SolveArgs& a, SolveLds& L, const Level2Job& job, double ref)
+{
+    const int cntu = job.cntu;
+    const Anch lo_node = job.lo_node, Su = job.Su;
+    const uint32_t Cu = job.Cu;
+    Status* st = a.st;
+    const int tid = threadIdx.x;
+    const double c = a.log2e_over_alpha;
+    const double k = a.k;
+    const int ept = (cntu + kST - 1) / kST;
+    const int e0 = tid * ept < cntu ? tid * ept : cntu;
+    const int e1 = e0 + ept < cntu ? e0 + ept : cntu;
+    // this thread's points: E in the prefix, 1/E in a suffix kept per point
+    double pe = 0.0, sf = 0.0;
+    for (int j = e1 - 1; j >= e0; --j) {
+        const double E = exp2_ref(((double)key_to_float(L.keys[j]) - ref) * c);
+        pe += E;
+        sf += 1.0 / E;
+        L.bv[j] = sf;
+    }
+    RefScan part;
+    ref_scan_publish<kSW>(pe, sf, 0u, L.wt, &part);
+    __syncthreads();
+    const RefScan rs = ref_scan_finish<kSW>(L.wt, part);
+    // the end nodes in reference units
+    const double Pbase = lo_node.v > 0.0 ? lo_node.v * exp2_ref(((double)lo_node.x - ref) * c) : 0.0;
+    const double Sbase = Su.v > 0.0 ? Su.v * exp2_ref(-((double)Su.x - ref) * c) : 0.0;
+
+    if (job.certify) {
+        // M(a_L) >= k >= M(a_R) from the band's totals and the tails
+        const double all = (double)cntu + (double)Cu;
+        const double mL = job.hasL ? 0.5 * lo_node.v + all -
+                                         0.5 * exp2_ref(((double)lo_node.x - ref) * c) * (rs.s_all + Sbase)
+                                   : all;
+        double mR = 0.0;
+        if (job.hasR)
+            mR = (double)Cu - 0.5 * Su.v + 0.5 * exp2_ref(-((double)Su.x - ref) * c) * (rs.p_all + Pbase);
+        if (tid == 0) {
+            st->massL = mL;
+            st->massR = mR;
+        }
+        const bool rejL = job.hasL && !(mL >= k);
+        const bool rejR = !rejL && job.hasR && !(mR <= k);
+        if (rejL || rejR) {
+            if (tid == 0)
+                st->solve_state = rejL ? kSolveRejectLow : kSolveRejectHigh;
+            return;
+        }
+    }
+
+    // breakpoint masses: M(x_j) = A_j / 2 + C_j - T_j / 2 with
+    // A_j = (Pbase + sum_{i<=j} E_i) / E_j and T_j = E_j (sum_{i>j} 1/E_i + Sbase)
+    int jc = -1;
+    double jA = 0.0, jS = 0.0;
+    double P = Pbase + rs.p_before;
+    for (int j = e0; j < e1; ++j) {
+        const double E = exp2_ref(((double)key_to_float(L.keys[j]) - ref) * c);
+        P += E;
+        const double Safter = rs.s_after + (j + 1 < e1 ? L.bv[j + 1] : 0.0) + Sbase;
+        const double m = 0.5 * (P / E) + ((double)(cntu - 1 - j) + (double)Cu) - 0.5 * (E * Safter);
+        if (m >= k) {
+            jc = j;
+            jA = P / E;
+            jS = Safter;
+        }
+    }
+    int jstar, unused;
+    block_max_min(jc, 0, L, &jstar, &unused);  // [1]
+    if (jstar >= 0) {
+        if (jc == jstar) {
+            // the gap after x_j*: its prefix anchored at x_j*, its suffix at
+            // the next point (or the end node)
+            const float xn = jstar + 1 < cntu ? key_to_float(L.keys[jstar + 1]) : Su.x;
+            const Anch hi = jS > 0.0 ? node(xn, jS * exp2_ref(((double)xn - ref) * c)) : empty_suf();
+            finish(a, gap_root(node(key_to_float(L.keys[jstar]), jA), hi, (double)(cntu - 1 - jstar) + (double)Cu, k,
+                               a.alpha, c));
+        }
+    } else if (tid == 0) {
+        // the root lies before the first point
+        const float x0 = key_to_float(L.keys[0]);
+        const Anch B0 = node(x0, (rs.s_all + Sbase) * exp2_ref(((double)x0 - ref) * c));
+        finish(a, gap_root(lo_node, B0, (double)cntu + (double)Cu, k, a.alpha, c));
+    }
+}
+
+__device__ __forceinline__ void level2(const SolveArgs& a, SolveLds& L, const Level2Job& job)
 {
     const float* xg = job.xg;
     const int cntu = job.cntu;
@@ -174,6 +395,11 @@ __device__ void level2(const SolveArgs& a, SolveLds& L, const Level2Job& job)
             L.keys[i] = float_to_key(xg[i]);
     }
     __syncthreads();
+    double ref = 0.0;
+    if (level2_ref_ok(job, L, c, &ref)) {
+        level2_ref(a, L, job, ref);
+        return;
+    }
     const int ept = (cntu + kST - 1) / kST;
     const int e0 = tid * ept < cntu ? tid * ept : cntu;
     const int e1 = e0 + ept < cntu ? e0 + ept : cntu;
@@ -251,6 +477,115 @@ __device__ void level2(const SolveArgs& a, SolveLds& L, const Level2Job& job)
 
 }  // namespace
 
+// Level 1 of the bucket route in reference-point sums (one group per
+// thread; the bracket ends finite and within kRefSpan): the bracket
+// certificate, the mass at every group end, the two groups around the
+// root, then the level-2 job, as in solve_levels.  left / right: the tail
+// nodes; rs: the scans of this thread's group terms.
+__device__ __forceinline__ bool solve_level1_ref(const SolveArgs& a, SolveLds& L, Level2Job& job, const GroupAgg& mine, int g0,
+                                 double ref, double Eh, const RefScan& rs, Anch left, Anch right, uint64_t nR)
+{
+    Status* st = a.st;
+    const int tid = threadIdx.x;
+    const double c = a.log2e_over_alpha;
+    const double k = a.k;
+    const int T = a.groups;
+    const uint32_t NG = rs.c_all;
+    const double EaL = exp2_ref(((double)left.x - ref) * c);
+    const double FaR = exp2_ref(-((double)right.x - ref) * c);
+    const double Pbase = left.v * EaL;
+    const double Sbase = right.v * FaR;
+
+    // ---- bracket certificate (every thread, same values) ---------------------------
+    const double mL = 0.5 * left.v + ((double)NG + (double)nR) - 0.5 * EaL * (rs.s_all + Sbase);
+    const double mR = (double)nR - 0.5 * right.v + 0.5 * FaR * (rs.p_all + Pbase);
+    if (tid == 0) {
+        st->massL = mL;
+        st->massR = mR;
+    }
+    const bool rejL = !(mL >= k);
+    const bool rejR = !rejL && !(mR <= k);
+    if (rejL || rejR) {
+        if (tid == 0)
+            st->solve_state = rejL ? kSolveRejectLow : kSolveRejectHigh;
+        return false;
+    }
+
+    // ---- masses at the group ends; the two groups around the root ----------------------
+    // after this group: its suffix anchored at the group's end (every later
+    // point lies at or above it)
+    const double s_after = rs.s_after + Sbase;
+    const uint32_t after = NG - (rs.c_before + mine.cnt) + (uint32_t)nR;
+    const Anch suf_here = s_after > 0.0 ? node(mine.hi, s_after * Eh) : empty_suf();
+    int tc = -1, uc = T;
+    if (g0 < T && mine.cnt) {
+        const double A = (Pbase + rs.p_before + mine.TA * Eh) / Eh;
+        const double m = 0.5 * A + (double)after - 0.5 * (Eh * s_after);
+        if (m >= k) {
+            tc = g0;
+            L.lo[tid] = node(mine.hi, A);
+        } else {
+            uc = g0;
+            L.hi[tid].g = mine;
+            L.hi[tid].Sx = suf_here.x;
+            L.hi[tid].Sv = suf_here.v;
+            L.hi[tid].Cafter = after;
+        }
+    }
+    int tstar, u;
+    block_max_min(tc, uc, L, &tstar, &u);  // [1]
+    if (u < tstar) {
+        // rounding broke the monotone order of the group-end masses: take
+        // the first non-empty group after t* instead
+        __syncthreads();
+        int mine_u = T;
+        if (g0 < T && g0 > tstar && mine.cnt) {
+            mine_u = g0;
+            L.hi[tid].g = mine;
+            L.hi[tid].Sx = suf_here.x;
+            L.hi[tid].Sv = suf_here.v;
+            L.hi[tid].Cafter = after;
+        }
+        int dummy;
+        block_max_min(-1, mine_u, L, &dummy, &u);
+    }
+    Anch lo_node = left;
+    if (tstar >= 0)
+        lo_node = L.lo[tstar];
+    if (u >= T) {
+        // root between the last group and the right node
+        if (tid == 0)
+            finish(a, gap_root(lo_node, right, (double)nR, k, a.alpha, c));
+        return false;
+    }
+    const RowHi Ur = L.hi[u];
+    const GroupAgg U = Ur.g;
+    const Anch Su = node(Ur.Sx, Ur.Sv);
+    const uint32_t Cu = Ur.Cafter;
+    if (U.lo == U.hi) {
+        // every value of the group is equal: the root lies before it
+        if (tid == 0)
+            finish(a, gap_root(lo_node, bwd(node(U.lo, U.TB), Su, c), (double)U.cnt + (double)Cu, k, a.alpha, c));
+        return false;
+    }
+    const int cntu = (int)U.cnt;
+    if (cntu > kBucketCap) {
+        if (tid == 0)
+            st->solve_state = kSolveBucketOverflow;
+        return false;
+    }
+    job.xg = a.sorted + U.start;
+    job.cntu = cntu;
+    job.unsorted = true;
+    job.certify = false;
+    job.hasL = false;
+    job.hasR = false;
+    job.lo_node = lo_node;
+    job.Su = Su;
+    job.Cu = Cu;
+    return true;
+}
+
 // One work-group.  Phases (barriers in brackets):
 //   1. fold the pass-1 partials; per-thread level-1 values; wave scans  [1]
 //   2. per-group masses, bracket certificate, the two groups around the
@@ -262,7 +597,7 @@ __device__ void level2(const SolveArgs& a, SolveLds& L, const Level2Job& job)
 //   5. the last breakpoint with mass >= k; its owner applies the closed
 //      form                                                             [1]
 // Returns whether level 2 is needed (false: b or a rejection is recorded).
-__device__ bool solve_levels(const SolveArgs& a, SolveLds& L, Level2Job& job)
+__device__ __forceinline__ bool solve_levels(const SolveArgs& a, SolveLds& L, Level2Job& job)
 {
     Status* st = a.st;
     const int tid = threadIdx.x;
@@ -365,9 +700,25 @@ __device__ bool solve_levels(const SolveArgs& a, SolveLds& L, Level2Job& job)
                 suf = bwd(node(G.lo, G.TB), suf, c);
         }
     }
+    // bucket route with a finite bracket no wider than kRefSpan: level 1 in
+    // reference-point sums (reference at the bracket's midpoint)
+    const bool use_ref = a.tails && !a.direct && gpt == 1 && aL > -INFINITY && aR < INFINITY &&
+                         ((double)aR - (double)aL) * c <= kRefSpan;
+    const double ref = use_ref ? 0.5 * ((double)aL + (double)aR) : 0.0;
+    double Eh = 1.0;  // E at this thread's group end
+    RefScan rpart;
     Scan2Part part1;
-    if (!a.direct)
+    if (use_ref) {
+        double pg = 0.0, sg = 0.0;
+        if (g0 < T && mine.cnt) {
+            Eh = exp2_ref(((double)mine.hi - ref) * c);
+            pg = mine.TA * Eh;
+            sg = mine.TB * exp2_ref(-((double)mine.lo - ref) * c);
+        }
+        ref_scan_publish<kSW>(pg, sg, cnt, L.wt, &rpart);
+    } else if (!a.direct) {
         part1 = scan2_publish(pre, suf, cnt, c, L.wt);
+    }
     __syncthreads();  // [1]
 
     // every thread folds the wave values in the same order
@@ -440,6 +791,8 @@ __device__ bool solve_levels(const SolveArgs& a, SolveLds& L, Level2Job& job)
     } else {
         nR = 0;
     }
+    if (use_ref)
+        return solve_level1_ref(a, L, job, mine, g0, ref, Eh, ref_scan_finish<kSW>(L.wt, rpart), left, right, nR);
     const Scan2 sc = scan2_finish<kSW>(L.wt, part1, c);
     const uint32_t NG = sc.cnt_all;
     const uint32_t cnt_before = sc.cnt_before;
