@@ -91,20 +91,25 @@ __device__ void dft_select(const DftState& in, const uint32_t* totals, int P, Df
     }
 }
 
-// One slot's digit counted for the lanes that `match`: lanes sharing a
-// digit are merged first (a few rounds, one LDS atomic per distinct digit),
-// the remaining lanes add one each.
+// One slot's digit counted for the lanes that `match`: while the digit of
+// the first remaining lane is shared by several lanes, those lanes are
+// merged into one LDS atomic (data concentrated on a few digits); once a
+// digit stands nearly alone, the remaining lanes add one each (spread data,
+// whose atomics rarely collide).
 __device__ __forceinline__ void agg_count(uint32_t* h, bool match, uint32_t d)
 {
     uint64_t active = __ballot(match);
     const int lane = lane_id();
-    for (int it = 0; it < 4 && active != 0ull; ++it) {
+    for (int it = 0; it < 8 && active != 0ull; ++it) {
         const int leader = (int)__builtin_ctzll(active);
         const uint32_t dl = (uint32_t)__shfl((int)d, leader, kWave);
         const uint64_t same = __ballot(match && d == dl);
+        const uint32_t cnt = (uint32_t)__popcll(same);
         if (lane == leader)
-            atomicAdd(&h[dl], (uint32_t)__popcll(same));
+            atomicAdd(&h[dl], cnt);
         active &= ~same;
+        if (cnt < 4u)
+            break;
     }
     if ((active >> lane) & 1ull)
         atomicAdd(&h[d], 1u);

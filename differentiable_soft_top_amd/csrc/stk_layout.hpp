@@ -431,10 +431,10 @@ hipError_t launch_single_status(const SingleArgs& a, hipStream_t stream);
 
 // DFTopK comparator: radix selection of the k-th and (k+1)-th largest
 // scores (three passes of 11, 11 and 10 key bits), then b at their midpoint.
-constexpr int kDftThreads = 256;
+constexpr int kDftThreads = 512;
 constexpr int kDftBins = 2048;                 // digits of the 11-bit passes
 constexpr int kDftRowWords = 2 * kDftBins + 64;  // two targets' counts, the NaN count, padding
-constexpr int kDftMaxGroups = 256;
+constexpr int kDftMaxGroups = 512;
 constexpr int kDftTileScores = kDftThreads * 8 * 4;
 
 // Before pass P: for the (k+1)-th largest (target 0) and the k-th largest
