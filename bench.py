@@ -410,16 +410,20 @@ def main():
     breakdown = _lib.profile_end()
     per_step = {kname: ms / 3.0 for kname, (ms, cnt) in breakdown.items()}
     streaming = {kname: v for kname, v in per_step.items() if kname in ALGO_BYTES}
-    dominant = max(streaming, key=streaming.get)
+    # (a vector short enough for the one-kernel route has no streaming kernel)
+    dominant = max(streaming, key=streaming.get) if streaming else None
 
     # timed region: K steps, the dominant kernel bracketed by events live
-    _lib.profile_begin([dominant])
+    _lib.profile_begin([dominant] if dominant else [])
     times = time_steps(torch, run, args.steps)
     prof = _lib.profile_end()
-    dom_ms, dom_launches = prof[dominant]
-    dom_avg_s = dom_ms / dom_launches / 1e3
-    algo = ALGO_BYTES[dominant] * n
-    achieved = algo / dom_avg_s / 1e9
+    if dominant:
+        dom_ms, dom_launches = prof[dominant]
+        dom_avg_s = dom_ms / dom_launches / 1e3
+        algo = ALGO_BYTES[dominant] * n
+        achieved = algo / dom_avg_s / 1e9
+    else:
+        dom_launches, dom_avg_s, algo, achieved = 0, float("nan"), 0, float("nan")
     median = float(np.median(times))
     mean = float(np.mean(times))
     st = run.stats.as_dict()
@@ -563,14 +567,14 @@ def main():
                           "calibrated on a device copy (profiles/traffic.json)"},
         "streaming": streaming_out,
         "kernels_ms_event_prepass": {kname: round(v, 5) for kname, v in sorted(per_step.items())},
-        "roofline": {
+        "roofline": None if dominant is None else {
             "kernel": dominant,
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": traffic_for(dominant, args.workload),
+            "traffic": traffic_for(dominant, args.workload) if dominant else None,
             "algorithmic_bytes_per_launch": algo,
             "avg_launch_ms": dom_avg_s * 1e3,
             "launches": dom_launches,

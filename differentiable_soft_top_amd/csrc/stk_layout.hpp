@@ -121,7 +121,7 @@ struct alignas(16) Status {
     double seg_alpha;
     uint64_t seg_scores;
     // the most frequent of a few candidate values in the band buffer, and
-    // its estimated count there (band_mode_kernel, after a band overflow)
+    // its estimated count there (band_mode_pick_kernel, after a band overflow)
     float tie_value;
     uint32_t tie_count;
     // the left tail of the split's first round (bracket [T+, a_R)), kept for
