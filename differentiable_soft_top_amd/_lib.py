@@ -12,8 +12,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsofttopk.so")
 
 OK, EINVAL, ENONFINITE, EWORKSPACE, EHIP, ESOLVE = 0, 1, 2, 3, 4, 5
-PATH_BRACKET, PATH_WIDENED, PATH_FULLSORT, PATH_SINGLE = 1, 2, 3, 4
-BAND_DIRECT, BAND_BUCKETS = 1, 2
+PATH_BRACKET, PATH_WIDENED, PATH_FULLSORT, PATH_SINGLE, PATH_ALL_SCORES = 1, 2, 3, 4, 5
+BAND_DIRECT, BAND_BUCKETS, BAND_REFINE, BAND_REFINE_STEPS = 1, 2, 3, 4
 REJECT_LOW, REJECT_HIGH, REJECT_OVERFLOW, REJECT_BUCKET, REJECT_MASS = 1, 2, 4, 8, 16
 
 
@@ -46,6 +46,8 @@ class Stats(ctypes.Structure):
         ("mass_at_right", ctypes.c_double),
         ("b", ctypes.c_double),
         ("mass", ctypes.c_double),
+        ("refine_passes", ctypes.c_int32),
+        ("pad", ctypes.c_int32),
     ]
 
     def as_dict(self):

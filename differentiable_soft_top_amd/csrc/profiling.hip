@@ -14,7 +14,7 @@ namespace {
 const char* const kNames[kKernelCount] = {
     "sample", "filter", "select", "pass1", "band_hist", "band_scatter", "bucket_agg", "solve",
     "radix_upsweep", "radix_downsweep", "radix_scan", "tile_agg", "emit", "emit_finalize", "vjp_reduce", "vjp_apply", "reset",
-    "rows_forward", "rows_backward", "curve_scan", "curve",
+    "rows_forward", "rows_backward", "curve_scan", "curve", "iterate",
 };
 
 struct Pair {

@@ -112,7 +112,8 @@ bool params_ok(const soft_topk_params& p)
         return false;
     if (p.verify_mass != 0 && p.verify_mass != 1)
         return false;
-    if (p.band_route != 0 && p.band_route != SOFT_TOPK_BAND_DIRECT && p.band_route != SOFT_TOPK_BAND_BUCKETS)
+    if (p.band_route != 0 && p.band_route != SOFT_TOPK_BAND_DIRECT && p.band_route != SOFT_TOPK_BAND_BUCKETS &&
+        p.band_route != SOFT_TOPK_BAND_REFINE && p.band_route != SOFT_TOPK_BAND_REFINE_STEPS)
         return false;
     return true;
 }
@@ -484,21 +485,90 @@ int enqueue_band_solve(const Ctx& x, bool direct)
     return SOFT_TOPK_OK;
 }
 
-// Whether a round with sample ranks (rl, rr) sorts its band whole: both
-// bracket ends finite and the expected band n (rr - rl) / m small enough.
+// The band's expected size for sample ranks (rl, rr): n (rr - rl) / m, or
+// infinity when a bracket end is open.
+double band_predict(int64_t n, int64_t m, int64_t rl, int64_t rr)
+{
+    if (rl < 1 || rr > m)
+        return INFINITY;
+    return (double)n * (double)(rr - rl) / (double)m;
+}
+
+// Whether a sorted round with sample ranks (rl, rr) sorts its band whole:
+// both bracket ends finite and the expected band small enough.
 bool band_direct(const soft_topk_params& prm, int64_t n, int64_t m, int64_t rl, int64_t rr)
 {
     if (prm.band_route == SOFT_TOPK_BAND_BUCKETS)
         return false;
     if (prm.band_route == SOFT_TOPK_BAND_DIRECT)
         return true;
-    if (rl < 1 || rr > m)
-        return false;
-    return (double)n * (double)(rr - rl) / (double)m <= kDirectPredictMax;
+    return band_predict(n, m, rl, rr) <= kDirectPredictMax;
 }
 
-// One bracketed round: select with ranks (rl, rr), pass-1, band sort, solve.
-int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q, bool direct)
+// Step kernels per chain: the most passes any of the last kHintCalls chains
+// took (within kIterStepsMin..kIterStepsMax).  Each launch costs 4-5 us
+// whatever it does, so a chain longer than needed costs that much per
+// extra step; one that runs out resumes where it stopped.
+constexpr int kHintCalls = 4;
+thread_local int g_chain_passes[kHintCalls] = {3, 3, 3, 3};
+thread_local int g_chain_next = 0;
+
+int chain_steps()
+{
+    int m = kIterStepsMin;
+    for (int v : g_chain_passes)
+        m = std::max(m, v);
+    return std::min(m, kIterStepsMax);
+}
+
+void note_chain_passes(int passes)
+{
+    g_chain_passes[g_chain_next] = passes;
+    g_chain_next = (g_chain_next + 1) % kHintCalls;
+}
+
+// Partition refinement of the band (or of every score when the band
+// overflowed): one work-group, or a chain of `steps` step kernels (resume:
+// from where the last chain stopped, after passes_before passes).
+int enqueue_refine(const Ctx& x, bool one_group, int steps, bool resume, int passes_before)
+{
+    IterArgs ia;
+    ia.band = at<float>(x, x.plan.off_band);
+    ia.cap = x.plan.cap;
+    ia.s = x.s;
+    ia.n = x.n;
+    ia.p1 = at<Pass1Partial>(x, x.plan.off_p1part);
+    ia.p1_blocks = x.plan.g_pass1;
+    ia.is = at<IterState>(x, x.plan.off_iter);
+    ia.part = at<SplitPartial>(x, x.plan.off_iter + align_up(sizeof(IterState)));
+    ia.groups = kIterGroups;
+    ia.passes_before = passes_before;
+    ia.k = x.k;
+    ia.alpha = x.alpha;
+    ia.log2e_over_alpha = x.c;
+    ia.out_b = x.b;
+    ia.st = x.st;
+    ia.mirror = x.mirror0;
+    ia.seq = next_publication();
+    STK_HIP(launch_partition_solve(ia, one_group, steps, resume, x.stream));
+    return SOFT_TOPK_OK;
+}
+
+// How a round solves its band: refinement (on one work-group when the band
+// is expected to fit it, else by the step kernels), or one of the sorted
+// routes when the parameters force it.
+int round_route(const soft_topk_params& prm, int64_t n, int64_t m, int64_t rl, int64_t rr)
+{
+    if (prm.band_route == SOFT_TOPK_BAND_DIRECT || prm.band_route == SOFT_TOPK_BAND_BUCKETS)
+        return band_direct(prm, n, m, rl, rr) ? SOFT_TOPK_BAND_DIRECT : SOFT_TOPK_BAND_BUCKETS;
+    if (prm.band_route == SOFT_TOPK_BAND_REFINE_STEPS)
+        return SOFT_TOPK_BAND_REFINE_STEPS;
+    return band_predict(n, m, rl, rr) <= kIterOnePredictMax ? SOFT_TOPK_BAND_REFINE : SOFT_TOPK_BAND_REFINE_STEPS;
+}
+
+// One bracketed round: select with ranks (rl, rr), pass-1, then the band's
+// solve by `route`.
+int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q, int route)
 {
     SampleArgs sa;
     sa.s = x.s;
@@ -524,7 +594,9 @@ int enqueue_round(const Ctx& x, int64_t rl, int64_t rr, double q, bool direct)
     int rc = enqueue_pass1(x);
     if (rc)
         return rc;
-    return enqueue_band_solve(x, direct);
+    if (route == SOFT_TOPK_BAND_REFINE || route == SOFT_TOPK_BAND_REFINE_STEPS)
+        return enqueue_refine(x, route == SOFT_TOPK_BAND_REFINE, chain_steps(), false, 0);
+    return enqueue_band_solve(x, route == SOFT_TOPK_BAND_DIRECT);
 }
 
 // Radix sort of all scores and summaries of 4096-score tiles of the sorted
@@ -690,6 +762,7 @@ int tie_split(const Ctx& x, Status h0, int rounds_left, bool wait_mass, double t
             return rc;
         sx->rounds += 1;
         sx->band_route = SOFT_TOPK_BAND_BUCKETS;
+        sx->refine_passes = 0;
         sx->a_left = h->aL;
         sx->a_right = h->aR;
         sx->n_left = (int64_t)h->nL;
@@ -729,6 +802,69 @@ int tie_split(const Ctx& x, Status h0, int rounds_left, bool wait_mass, double t
             sx->reject_mask |= SOFT_TOPK_REJECT_BUCKET;
         }
         return SOFT_TOPK_OK;
+    }
+    return SOFT_TOPK_OK;
+}
+
+// After a refining round: a band larger than the one-work-group form, or
+// than its buffer, is refined by the step kernels (every score, when it
+// overflowed); a band refinement that did not end falls back to sorting the
+// band; every score refined without an end counts as a band overflow (the
+// tie split and the full sort follow).  Each follow-up is one more solve
+// and emission on the same pass-1 output.  *route becomes the route that
+// ran last.
+int settle_refine(const Ctx& x, bool direct, bool wait_mass, Status* h, int* route)
+{
+    int rc;
+    if (*route == SOFT_TOPK_BAND_REFINE && (h->solve_state == kSolveIterBig || h->solve_state == kSolveOverflow)) {
+        *route = SOFT_TOPK_BAND_REFINE_STEPS;
+        rc = enqueue_refine(x, false, chain_steps(), false, 0);
+        if (rc)
+            return rc;
+        rc = enqueue_certify_emit(x, wait_mass);
+        if (rc)
+            return rc;
+        rc = wait_solve(x, h);
+        if (rc)
+            return rc;
+    }
+    // a chain that ran out of steps resumes where it stopped
+    while (h->solve_state == kSolveIterMore && (int)h->iter_steps < kIterPassesMax) {
+        rc = enqueue_refine(x, false, kIterStepsMax, true, (int)h->iter_steps);
+        if (rc)
+            return rc;
+        rc = enqueue_certify_emit(x, wait_mass);
+        if (rc)
+            return rc;
+        rc = wait_solve(x, h);
+        if (rc)
+            return rc;
+    }
+    if (*route == SOFT_TOPK_BAND_REFINE_STEPS && h->solve_state != kSolveNonfinite)
+        note_chain_passes((int)h->iter_steps);
+    if (h->solve_state == kSolveIterMore)
+        h->solve_state = kSolveIterLimit;
+    if (h->solve_state != kSolveIterLimit)
+        return SOFT_TOPK_OK;
+    if (h->iter_mode == 1u) {
+        h->solve_state = kSolveOverflow;
+        return SOFT_TOPK_OK;
+    }
+    *route = direct ? SOFT_TOPK_BAND_DIRECT : SOFT_TOPK_BAND_BUCKETS;
+    for (int i = 0; i < 2; ++i) {
+        rc = enqueue_band_solve(x, direct);
+        if (rc)
+            return rc;
+        rc = enqueue_certify_emit(x, wait_mass);
+        if (rc)
+            return rc;
+        rc = wait_solve(x, h);
+        if (rc)
+            return rc;
+        if (h->solve_state != kSolveDirectOverflow)
+            break;
+        direct = false;  // the band outgrew the whole-band sort: bucket it
+        *route = SOFT_TOPK_BAND_BUCKETS;
     }
     return SOFT_TOPK_OK;
 }
@@ -774,6 +910,8 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     o = align_up(o + sizeof(GroupScan) * (size_t)groups);
     p.off_emitpart = o;
     o = align_up(o + sizeof(double) * (size_t)p.g_emit);
+    p.off_iter = o;
+    o = align_up(o + align_up(sizeof(IterState)) + sizeof(SplitPartial) * 2 * (size_t)kIterGroups);
     p.off_keys0 = o;
     o = align_up(o + sizeof(uint32_t) * (size_t)n);
     p.off_keys1 = o;
@@ -1025,8 +1163,9 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
         int64_t rl = lower_rank(plan.m, q, prm.z);
         int64_t rr = upper_rank(plan.m, q, prm.z);
         for (int round = 0; round <= prm.max_widen && !done; ++round) {
-            bool direct = band_direct(prm, n, plan.m, rl, rr);
-            int rc = enqueue_round(x, rl, rr, q, direct);
+            int route = round_route(prm, n, plan.m, rl, rr);
+            const bool refine = route == SOFT_TOPK_BAND_REFINE || route == SOFT_TOPK_BAND_REFINE_STEPS;
+            int rc = enqueue_round(x, rl, rr, q, route);
             if (rc)
                 return rc;
             rc = enqueue_certify_emit(x, wait_mass);
@@ -1035,9 +1174,13 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
             rc = wait_solve(x, &h);
             if (rc)
                 return rc;
-            if (h.solve_state == kSolveDirectOverflow) {
+            if (refine) {
+                rc = settle_refine(x, band_direct(prm, n, plan.m, rl, rr), wait_mass, &h, &route);
+                if (rc)
+                    return rc;
+            } else if (h.solve_state == kSolveDirectOverflow) {
                 // the band outgrew the whole-band sort: bucket the same band
-                direct = false;
+                route = SOFT_TOPK_BAND_BUCKETS;
                 rc = enqueue_band_solve(x, false);
                 if (rc)
                     return rc;
@@ -1048,8 +1191,14 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
                 if (rc)
                     return rc;
             }
+            const bool all_scores = route == SOFT_TOPK_BAND_REFINE_STEPS && h.iter_mode == 1u;
             sx.rounds = round + 1;
-            sx.band_route = direct ? SOFT_TOPK_BAND_DIRECT : SOFT_TOPK_BAND_BUCKETS;
+            sx.band_route = route;
+            sx.refine_passes = route == SOFT_TOPK_BAND_REFINE || route == SOFT_TOPK_BAND_REFINE_STEPS
+                                   ? (int32_t)h.iter_steps
+                                   : 0;
+            if (all_scores)
+                sx.reject_mask |= SOFT_TOPK_REJECT_OVERFLOW;
             sx.a_left = h.aL;
             sx.a_right = h.aR;
             sx.n_left = (int64_t)h.nL;
@@ -1066,7 +1215,9 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
                         return rc;
                 }
                 if (!wait_mass || mass_ok(h, k, tol)) {
-                    sx.path = round == 0 ? SOFT_TOPK_PATH_BRACKET : SOFT_TOPK_PATH_WIDENED;
+                    sx.path = all_scores ? SOFT_TOPK_PATH_ALL_SCORES
+                              : round == 0 ? SOFT_TOPK_PATH_BRACKET
+                                           : SOFT_TOPK_PATH_WIDENED;
                     done = true;
                     break;
                 }

@@ -73,6 +73,22 @@ constexpr int kRadixKeysPerThread = 32;
 constexpr int kRadixTile = kRadixThreads * kRadixKeysPerThread;  // 8192 keys
 constexpr int kRadixBins = 256;
 constexpr int64_t kNontemporalMin = 1 << 25;  // outputs of at least 128 MiB bypass the caches
+// Partition refinement of the band (no sort): one work-group holds up to
+// kIterOneCap band values in LDS and runs at most kIterOneMax passes;
+// larger bands (and all scores after a band overflow) take a chain of step
+// kernels of kIterGroups work-groups.  The band goes to one work-group when
+// its expected size is at most kIterOnePredictMax (about four binomial
+// spreads below the cap, as for the whole-band sort).
+constexpr int kIterOneThreads = 256;      // 4 waves: reductions cost per wave, the passes do not
+constexpr int kIterOnePer = 64;
+constexpr int kIterOneCap = kIterOneThreads * kIterOnePer;
+constexpr int kIterOneMax = 16;
+constexpr double kIterOnePredictMax = 10240.0;
+constexpr int kIterThreads = 256;
+constexpr int kIterGroups = 256;
+constexpr int kIterStepsMin = 2;         // step kernels of a chain: the recent calls' passes, within these
+constexpr int kIterStepsMax = 8;
+constexpr int kIterPassesMax = 16;       // passes over all chains of one round before the band is sorted
 
 // ---- solve status codes (Status::solve_state) ----------------------------
 enum SolveState : uint32_t {
@@ -84,6 +100,9 @@ enum SolveState : uint32_t {
     kSolveNonfinite = 5,
     kSolveBucketOverflow = 6,  // a band bucket exceeded the LDS sort capacity
     kSolveDirectOverflow = 7,  // the band exceeded the whole-band sort (bucket it instead)
+    kSolveIterLimit = 8,       // partition refinement did not end within its passes
+    kSolveIterBig = 9,         // the band exceeded the one-work-group refinement
+    kSolveIterMore = 10,       // the step kernels ran out before the end (resume the chain)
 };
 
 // Device status block at workspace offset 0.  Every field is written by a
@@ -128,6 +147,10 @@ struct alignas(16) Status {
     // the closed form between the tied value T and the next float T+
     double tie_SL;
     uint64_t tie_nL;
+    // partition refinement: what it refined (0: the band with the pass-1
+    // tails, 1: every score) and the passes it took
+    uint32_t iter_mode;
+    uint32_t iter_steps;
 };
 static_assert(sizeof(Status) <= 256, "status block must fit 256 bytes");
 static_assert(sizeof(Status) % 4 == 0, "status block is copied as 32-bit words");
@@ -202,7 +225,7 @@ struct Plan {
     int32_t n_tiles;             // groups of the full-sort solve
     int32_t g_radix;             // radix tiles
     size_t off_status, off_samples, off_frec, off_p1part, off_band, off_band_sorted;
-    size_t off_hist, off_bstart, off_agg, off_scan, off_emitpart, off_keys0, off_keys1, off_rhist, off_super;
+    size_t off_hist, off_bstart, off_agg, off_scan, off_emitpart, off_iter, off_keys0, off_keys1, off_rhist, off_super;
     int64_t n_seg;               // saturated-score segments (0: not used at this n)
     size_t off_seg_cnt, off_seg_ent;
     size_t total;
@@ -321,6 +344,49 @@ struct SolveArgs {
     uint32_t seq;                 // its publication number (0: none)
 };
 hipError_t launch_solve(const SolveArgs& a, hipStream_t stream);
+
+// Partition sums of one work-group at a split point r: the sum of
+// e^{-(s - r)/alpha} over its scores above r (A), of e^{(s - r)/alpha} over
+// the others (B), the count above r (N), and the nearest scores on each side.
+struct alignas(16) SplitPartial {
+    double A, B;
+    uint64_t N;
+    float lo, hi;
+};
+
+// State of the step kernels between launches (workspace): the split points
+// of the last two steps (alternate steps use alternate entries, so no
+// work-group reads what another work-group of the same step writes), where
+// a chain that ran out stopped, and whether the refinement has ended.
+struct alignas(16) IterState {
+    double x[2];                  // split points of alternate steps
+    double resume_x;              // where a chain that ran out stopped
+    uint32_t done;
+    uint32_t pad;
+};
+
+struct IterArgs {
+    const float* band;            // the unsorted band of the round (st->nB values)
+    int64_t cap;                  // its capacity: a larger band refines every score instead
+    const float* s;               // all scores
+    int64_t n;
+    const Pass1Partial* p1;       // pass-1 partials (tails, band range, finiteness)
+    int32_t p1_blocks;
+    IterState* is;                // step kernels' state
+    SplitPartial* part;           // [2][kIterGroups] sums of alternate steps
+    int32_t groups;               // work-groups of a step (<= kIterGroups)
+    int32_t passes_before;        // passes of earlier chains of this round (resumed)
+    double k;
+    double alpha;
+    double log2e_over_alpha;
+    double* out_b;
+    Status* st;
+    Mirror* mirror;               // host-visible status copy written at the end
+    uint32_t seq;                 // its publication number
+};
+// One work-group (one_group), or a chain of `steps` step kernels and the
+// final kernel (resume: start where the last chain stopped).
+hipError_t launch_partition_solve(const IterArgs& a, bool one_group, int steps, bool resume, hipStream_t stream);
 
 struct RadixArgs {
     const float* s;

@@ -32,6 +32,7 @@ enum KernelId : int {
     kKRowsBackward,
     kKCurveScan,
     kKCurve,
+    kKIterate,      // partition refinement (every kernel of it)
     kKernelCount
 };
 

@@ -63,11 +63,21 @@ extern "C" {
 #define SOFT_TOPK_PATH_FULLSORT 3 /* full device radix sort of all scores   */
 #define SOFT_TOPK_PATH_SINGLE 4   /* n <= 8192: one kernel sorts all scores
                                      in registers and solves them exactly   */
+#define SOFT_TOPK_PATH_ALL_SCORES 5 /* the band overflowed its buffer; the
+                                     partition refinement ran over all n
+                                     scores and ended on the exact root     */
 
 /* How a bracketed round solved its band (soft_topk_params.band_route,
  * soft_topk_stats.band_route). */
 #define SOFT_TOPK_BAND_DIRECT 1   /* the whole band sorted in one LDS sort     */
 #define SOFT_TOPK_BAND_BUCKETS 2  /* value buckets; only the root's is sorted  */
+#define SOFT_TOPK_BAND_REFINE 3   /* no sort: partition refinement of the band
+                                     (closed form around a split point,
+                                     repeated until no score crosses), on one
+                                     work-group                              */
+#define SOFT_TOPK_BAND_REFINE_STEPS 4 /* the same refinement by step kernels of
+                                     many work-groups (larger bands, and all
+                                     scores after a band overflow)           */
 
 /* Why a bracketed round was rejected (soft_topk_stats.reject_mask bits). */
 #define SOFT_TOPK_REJECT_LOW 1       /* certificate: b lies below a_L        */
@@ -105,10 +115,16 @@ typedef struct soft_topk_params {
                                emission's fp64 partial sums of p are not folded
                                (the pass runs in full whenever stats are
                                requested, and stats.mass is NaN otherwise)      */
-    int32_t band_route;     /* 0 auto: sort the band whole when its expected size
-                               n (r_R - r_L) / m is at most 5120, else bucket it;
-                               SOFT_TOPK_BAND_DIRECT / _BUCKETS force a route (a
-                               band over 8192 scores is always bucketed)          */
+    int32_t band_route;     /* 0 auto: refine the unsorted band, on one
+                               work-group (SOFT_TOPK_BAND_REFINE) when its
+                               expected size n (r_R - r_L) / m is at most
+                               10240, else by step kernels (_REFINE_STEPS),
+                               which refine every score when the band
+                               overflows; a band refinement that does not end
+                               sorts the band.  _REFINE_STEPS forces the step
+                               kernels; _DIRECT / _BUCKETS force a sorted
+                               route: the whole band in one LDS sort (a band
+                               over 8192 scores is bucketed), or buckets      */
 } soft_topk_params;
 
 /* Host-side record of one forward call (all fields written on success). */
@@ -121,10 +137,14 @@ typedef struct soft_topk_stats {
     float a_left, a_right;  /* bracket of the last bracketed round (-inf / +inf and
                                n_band = n on SOFT_TOPK_PATH_SINGLE)                */
     int64_t n_left, n_band, n_right; /* scores below / inside / at-or-above it        */
-    double mass_at_left;    /* M(a_L) of the last bracketed round                     */
-    double mass_at_right;   /* M(a_R) of the last bracketed round                     */
+    double mass_at_left;    /* M(a_L) of the last bracketed round (NaN when it
+                               refined: its certificate is the refinement's)      */
+    double mass_at_right;   /* M(a_R) of the last bracketed round (NaN likewise)      */
     double b;               /* the threshold (also written to out_b on the device)    */
     double mass;            /* fp64 sum of the emitted p (the certification pass)     */
+    int32_t refine_passes;  /* passes of the last round's partition refinement (sums
+                               at one split point each; 0 when it sorted)          */
+    int32_t pad;
 } soft_topk_stats;
 
 /* Fill *params with the defaults listed above. */

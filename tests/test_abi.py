@@ -160,7 +160,7 @@ def test_params_validation(lib):
     assert lib.soft_topk_workspace_bytes(1000, ctypes.byref(p)) > 0
     for field, bad in [("samples", 10), ("samples", 1 << 20), ("z", 0.0), ("z", float("nan")),
                        ("max_widen", -1), ("force_path", 7), ("band_capacity", -3), ("verify_mass", 2),
-                       ("band_route", 3)]:
+                       ("band_route", 5)]:
         q = _lib.default_params()
         setattr(q, field, bad)
         assert lib.soft_topk_workspace_bytes(1000, ctypes.byref(q)) == 0, field

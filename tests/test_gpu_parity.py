@@ -91,29 +91,42 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("route", ["auto", "buckets"])
+ROUTES = {"auto": None, "steps": _lib.BAND_REFINE_STEPS, "direct": _lib.BAND_DIRECT, "buckets": _lib.BAND_BUCKETS}
+
+
+@pytest.mark.parametrize("route", list(ROUTES))
 @pytest.mark.parametrize("name,n", SMALL, ids=["%s-%s" % (a, b) for a, b in SMALL])
 def test_small_parity(dev, name, n, route):
-    """Both band routes: at these sizes the band is small enough to be sorted
-    whole (the automatic choice); forcing the value buckets runs the route
-    the larger workloads take on the same inputs.  (c1 is short enough for
+    """Every band route on the same inputs: the automatic one refines the
+    band on one work-group at these sizes; "steps" forces the refinement's
+    step kernels (the route of larger bands); "direct" sorts the band whole
+    and "buckets" sorts it by value buckets (the sorted routes, which a
+    refinement that does not end falls back to).  (c1 is short enough for
     the one-kernel route by default, so the bracketed route is forced.)"""
     s_np, k, alpha, w = make_workload(name, n=n)
     g_np = draw_grad(s_np.size, w.seed)
-    if route == "buckets":
-        prm = params(band_route=_lib.BAND_BUCKETS)
-    else:
-        prm = params(force_path=_lib.PATH_BRACKET) if s_np.size <= 8192 else None
+    prm = params(force_path=_lib.PATH_BRACKET)
+    if ROUTES[route] is not None:
+        prm.band_route = ROUTES[route]
     res = run(dev, s_np, k, alpha, g_np, prm)
-    check_full(res, s_np, k, alpha, g_np)
-    assert res["stats"]["path"] == _lib.PATH_BRACKET, res["stats"]
-    want = _lib.BAND_BUCKETS if route == "buckets" else _lib.BAND_DIRECT
-    assert res["stats"]["band_route"] == want, res["stats"]
+    b_ref = check_full(res, s_np, k, alpha, g_np)
+    st = res["stats"]
+    assert st["path"] == _lib.PATH_BRACKET, st
+    want = ROUTES[route] if ROUTES[route] is not None else _lib.BAND_REFINE
+    assert st["band_route"] == want, st
+    if want in (_lib.BAND_REFINE, _lib.BAND_REFINE_STEPS):
+        # the refinement ends on the exact closed form: fp64 rounding apart
+        assert abs(res["b"] - b_ref) <= 1e-9 * alpha, (res["b"], b_ref)
+        assert 1 <= st["refine_passes"] <= 8, st
+    else:
+        assert st["refine_passes"] == 0, st
 
 
 def test_direct_band_overflow_falls_back_to_buckets(dev):
     """A band forced onto the whole-band sort but larger than it (about 11,700
-    scores here) is bucketed instead, in the same round, without a new pass."""
+    scores here) is bucketed instead, in the same round, without a new pass.
+    The automatic route refines the same band with the step kernels (its
+    expected size is past the one-work-group form) and reaches the same b."""
     s_np, k, alpha, w = make_workload("c4", n=3_000_007)
     res = run(dev, s_np, k, alpha, None, params(band_route=_lib.BAND_DIRECT))
     st = res["stats"]
@@ -121,21 +134,61 @@ def test_direct_band_overflow_falls_back_to_buckets(dev):
     assert st["path"] == _lib.PATH_BRACKET and st["band_route"] == _lib.BAND_BUCKETS, st
     check_full(res, s_np, k, alpha)
     auto = run(dev, s_np, k, alpha)
-    assert auto["stats"]["band_route"] == _lib.BAND_BUCKETS, auto["stats"]
-    assert auto["b"] == res["b"]
+    assert auto["stats"]["band_route"] == _lib.BAND_REFINE_STEPS, auto["stats"]
+    assert abs(auto["b"] - res["b"]) <= 1e-9 * alpha, (auto["b"], res["b"])
+
+
+@pytest.mark.parametrize("k", [1.0, 199_999.0])
+def test_refine_chain_resumes(dev, k):
+    """An open bracket (k near 0 or n with 1024 samples leaves one end at
+    infinity): the step kernels start at the finite end, far from b, and
+    need more passes than a chain holds; each chain that runs out resumes
+    where it stopped, and the end is the exact root."""
+    n = 200_000
+    s_np = draw_scores("normal", n, seed=21)
+    alpha = 0.05
+    g_np = draw_grad(n, 21)
+    res = run(dev, s_np, k, alpha, g_np, params(samples=1024, band_route=_lib.BAND_REFINE_STEPS))
+    b_ref = check_full(res, s_np, k, alpha, g_np)
+    st = res["stats"]
+    assert st["band_route"] == _lib.BAND_REFINE_STEPS, st
+    assert not (np.isfinite(st["a_left"]) and np.isfinite(st["a_right"])), st
+    assert st["refine_passes"] > 8, st  # more than the longest chain
+    assert abs(res["b"] - b_ref) <= 1e-9 * alpha
+
+
+@pytest.mark.parametrize("name,n,cap", [("c2", 100_003, 16), ("c4", 300_007, 256), ("c3", 200_001, 256),
+                                        ("c5", 100_000, 1000), ("c2", 8_193, 16)])
+def test_band_overflow_refines_every_score(dev, name, n, cap):
+    """A band larger than its buffer: the refinement runs over every score
+    (no tails, no bracket) from the bracket's middle and ends on the exact
+    root, in the same round."""
+    s_np, k, alpha, w = make_workload(name, n=n)
+    g_np = draw_grad(s_np.size, w.seed)
+    res = run(dev, s_np, k, alpha, g_np, params(band_capacity=cap, force_path=_lib.PATH_BRACKET))
+    b_ref = check_full(res, s_np, k, alpha, g_np)
+    st = res["stats"]
+    assert st["path"] == _lib.PATH_ALL_SCORES and st["rounds"] == 1, st
+    assert st["reject_mask"] & _lib.REJECT_OVERFLOW and st["band_route"] == _lib.BAND_REFINE_STEPS, st
+    assert abs(res["b"] - b_ref) <= 1e-9 * alpha, (res["b"], b_ref)
 
 
 def test_clustered_small(dev):
     """60% of the scores tied exactly at the threshold.  At this size the tied
-    band still fits its buffer and lands in one all-equal bucket, so the
-    certified route handles it; with a small band capacity the same input
-    takes the full sort.  Both must match the oracle."""
+    band still fits its buffer, so the certified route handles it (refined,
+    and sorted, where the cluster lands in one all-equal bucket); with a
+    small band capacity the refinement runs over every score, and the sorted
+    route takes the full sort.  All must match the oracle."""
     s_np, k, alpha, w = make_workload("c5", n=100_000)
     g_np = draw_grad(s_np.size, w.seed)
-    res = run(dev, s_np, k, alpha, g_np)
-    check_full(res, s_np, k, alpha, g_np)
-    assert res["stats"]["path"] == _lib.PATH_BRACKET, res["stats"]
+    for route in (0, _lib.BAND_BUCKETS):
+        res = run(dev, s_np, k, alpha, g_np, params(band_route=route))
+        check_full(res, s_np, k, alpha, g_np)
+        assert res["stats"]["path"] == _lib.PATH_BRACKET, res["stats"]
     res = run(dev, s_np, k, alpha, g_np, params(band_capacity=1000))
+    check_full(res, s_np, k, alpha, g_np)
+    assert res["stats"]["path"] == _lib.PATH_ALL_SCORES, res["stats"]
+    res = run(dev, s_np, k, alpha, g_np, params(band_capacity=1000, band_route=_lib.BAND_BUCKETS))
     check_full(res, s_np, k, alpha, g_np)
     assert res["stats"]["path"] == _lib.PATH_FULLSORT, res["stats"]
     assert res["stats"]["reject_mask"] & _lib.REJECT_OVERFLOW
@@ -160,7 +213,9 @@ def test_tied_cluster_splits_the_bracket(dev, where, alpha):
     M(T+) and M(T), T+ the next float above T, so b lies strictly inside
     (T, T+): both sides reject and the closed form in the gap right of T
     gives b (at alpha 1e-3 and at the clustered workload's 1e-4).  With no
-    widening rounds allowed, the full sort gives the same b."""
+    widening rounds allowed, the full sort gives the same b.  (The split
+    belongs to the sorted band routes, forced here: by default an overflowing
+    band is refined over every score, which must give the same b too.)"""
     n, n_tie = 1_000_000, 600_000
     rng = np.random.default_rng(31)
     s_np = rng.standard_normal(n).astype(np.float32)
@@ -173,7 +228,7 @@ def test_tied_cluster_splits_the_bracket(dev, where, alpha):
     else:
         k = n_above + (0.49 if where == "above" else 0.51) * n_tie
     g_np = rng.standard_normal(n).astype(np.float32)
-    res = run(dev, s_np, k, alpha, g_np)
+    res = run(dev, s_np, k, alpha, g_np, params(band_route=_lib.BAND_BUCKETS))
     check_full(res, s_np, k, alpha, g_np)
     st = res["stats"]
     assert st["path"] == _lib.PATH_WIDENED and st["reject_mask"] & _lib.REJECT_OVERFLOW, st
@@ -184,9 +239,13 @@ def test_tied_cluster_splits_the_bracket(dev, where, alpha):
     else:
         both = _lib.REJECT_LOW | _lib.REJECT_HIGH
         assert st["reject_mask"] & both == both and 0.5 < res["b"] < t_up, st
-    full = run(dev, s_np, k, alpha, None, params(max_widen=0))
+    full = run(dev, s_np, k, alpha, None, params(max_widen=0, band_route=_lib.BAND_BUCKETS))
     assert full["stats"]["path"] == _lib.PATH_FULLSORT, full["stats"]
     assert abs(full["b"] - res["b"]) <= 2e-5 * alpha
+    refined = run(dev, s_np, k, alpha, g_np)
+    check_full(refined, s_np, k, alpha, g_np)
+    assert refined["stats"]["path"] == _lib.PATH_ALL_SCORES, refined["stats"]
+    assert abs(refined["b"] - full["b"]) <= 2e-5 * alpha
 
 
 def test_route_independence(dev):
@@ -198,12 +257,16 @@ def test_route_independence(dev):
     for tag, prm in [("seed1", params(seed=1)), ("seed2", params(seed=0xABCDEF)),
                      ("narrow", params(z=0.05, max_widen=4)),
                      ("overflow", params(band_capacity=16)),
+                     ("overflow_sorted", params(band_capacity=16, band_route=_lib.BAND_BUCKETS)),
+                     ("narrow_sorted", params(z=0.05, max_widen=4, band_route=_lib.BAND_DIRECT)),
                      ("full", params(force_path=_lib.PATH_FULLSORT))]:
         res = run(dev, s_np, k, alpha, None, prm)
         bs[tag] = (res["b"], res["stats"])
         assert abs(res["b"] - b_ref) <= 1e-5 * alpha, (tag, res["b"], b_ref)
-    assert bs["overflow"][1]["path"] == _lib.PATH_FULLSORT
-    assert bs["overflow"][1]["reject_mask"] & _lib.REJECT_OVERFLOW
+    assert bs["overflow"][1]["path"] == _lib.PATH_ALL_SCORES
+    assert bs["overflow_sorted"][1]["path"] == _lib.PATH_FULLSORT
+    for tag in ("overflow", "overflow_sorted"):
+        assert bs[tag][1]["reject_mask"] & _lib.REJECT_OVERFLOW
     assert bs["full"][1]["path"] == _lib.PATH_FULLSORT
 
 
@@ -219,7 +282,9 @@ def test_narrow_bracket_widens(dev):
         st = res["stats"]
         if st["reject_mask"] & (_lib.REJECT_LOW | _lib.REJECT_HIGH):
             hits += 1
-            assert st["path"] in (_lib.PATH_WIDENED, _lib.PATH_FULLSORT)
+            # (a widened bracket can be open-ended and overflow the band,
+            # which then refines every score)
+            assert st["path"] in (_lib.PATH_WIDENED, _lib.PATH_FULLSORT, _lib.PATH_ALL_SCORES)
             assert st["rounds"] >= 2 or st["path"] == _lib.PATH_FULLSORT
     assert hits >= 1
 
@@ -597,13 +662,13 @@ def test_segments_nonfinite_cotangent_and_foreign_threshold(dev):
 
 
 def test_c5_full_sort_fallback(dev):
-    """The clustered workload with no widening rounds allowed skips the tie
-    split: the band overflow sends it to the full device radix sort, which
-    returns the stored oracle b."""
+    """The clustered workload on a sorted band route with no widening rounds
+    allowed skips the tie split: the band overflow sends it to the full
+    device radix sort, which returns the stored oracle b."""
     gold = GOLD["c5"]
     s_np, k, alpha, w = make_workload("c5")
     s = torch.from_numpy(s_np).to(dev)
-    p, b, st = stk.forward(s, k, alpha, params(max_widen=0), want_stats=True)
+    p, b, st = stk.forward(s, k, alpha, params(max_widen=0, band_route=_lib.BAND_BUCKETS), want_stats=True)
     assert st["path"] == _lib.PATH_FULLSORT and st["reject_mask"] & _lib.REJECT_OVERFLOW, st
     assert abs(float(b.item()) - gold["b"]) <= 1e-5 * alpha
     m = float(torch.sum(p.double()).item())
@@ -656,9 +721,9 @@ def test_full_size_route_and_certified_mass(dev, name):
     b_gpu = float(b.item())
     b_ref = gold["b"]
     assert abs(b_gpu - b_ref) <= 1e-5 * alpha, (b_gpu, b_ref, (b_gpu - b_ref) / alpha)
-    # c5: the tied cluster overflows every band; the split at the tied value
-    # brackets it (its own test forces the full sort on the same input)
-    expect = _lib.PATH_WIDENED if name == "c5" else _lib.PATH_BRACKET
+    # c5: the tied cluster overflows every band; the refinement then runs
+    # over every score (its own tests force the tie split and the full sort)
+    expect = _lib.PATH_ALL_SCORES if name == "c5" else _lib.PATH_BRACKET
     assert st["path"] == expect, st
     floor = gold["mass_p32_rounding_floor"]
     assert abs(st["mass"] - k) <= 1e-3 + floor, st
