@@ -929,6 +929,257 @@ __global__ __launch_bounds__(kGroupThreads) void rows_group_backward_kernel(Rows
     }
 }
 
+// ---------------------------------------------------------------------------
+// Rows without a sort: partition refinement (the band's solve in
+// partition_solve.hip) on each row, held by a lane group in registers.
+// At a split point r the group sums A = sum over s > r of e^{-(s-r)/alpha}
+// and B = sum over s <= r of e^{(s-r)/alpha}, counts N above r and finds
+// the nearest scores on either side; the segment's closed form around r,
+// N - (A/2) u + (B/2)/u = k with u = e^{(b-r)/alpha}, gives the next r; the
+// pass whose root lies between those nearest scores has found b exactly.
+// The steps move monotonically to b (each a one-sided bound), so they end.
+// A pass costs one exponential per score and a few lane-group shuffles, not
+// the sort network's ~log^2 n compare-exchanges.
+//   terms -- each pass splits at an fp64 point r; the scores compare with
+//     and are measured from the largest float rf <= r (the same split), a
+//     lane's terms 2^{-|s - rf| log2(e)/alpha} in fp32 (the difference is
+//     exact for s within a factor 2 of rf, else off by half an ulp; exp2 a
+//     few ulps) summed over its R scores in fp32, the group's sums in fp64
+//     and moved from rf to r by one exact-range factor.  Terms within a few
+//     alpha of r carry relative errors of a few 1e-7, so b moves by about
+//     1e-6 alpha at most (1e-5 alpha is the bar; the tests see 1e-7); a sum
+//     that falls below 2^-100 takes the far-gap form below;
+//   start -- each lane group solves a row, then the row one grid stride on
+//     (rows are loaded, solved and emitted one at a time); the first row
+//     starts at its maximum, each later one at the group's previous b
+//     shifted by the change of the row mean (any start converges; a near
+//     one in 2-4 passes);
+//   far gaps -- when the sum a step rests on underflows about r (r lies in
+//     a gap of hundreds of alpha), the step takes the same segment's closed
+//     form with its sums anchored at the gap's ends (gap_root, the sorted
+//     kernels' form), which needs no sum about r.
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int G>
+__device__ __forceinline__ float group_minf(float v)
+{
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1)
+        v = fminf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ float group_maxf(float v)
+{
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t group_sum_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// 2^-|y| for fp64 y: fp32 exp2 of the fraction, exact power of two
+__device__ __forceinline__ double exp2_neg_abs(double y)
+{
+    const double t = fmin(fabs(y), 1100.0);
+    const double j = floor(t);
+    return ldexp((double)__builtin_amdgcn_exp2f(-(float)(t - j)), -(int)j);
+}
+
+constexpr float kRowIterTol = 0x1p-30f;  // convergence slack, in units of alpha
+constexpr float kRowSumMin = 0x1p-100f;  // smallest sum taken as exact (normal, 2^26 above the fp32 minimum)
+
+}  // namespace
+
+// The j-th largest of the group's values v (one per lane, descending
+// bitonic network over the group's lanes), j in 1..G.
+template <int G>
+__device__ __forceinline__ float group_kth_largest(float v, int j)
+{
+    const int gl = lane_id() & (G - 1);
+#pragma unroll
+    for (int size = 2; size <= G; size <<= 1) {
+#pragma unroll
+        for (int stride = size / 2; stride > 0; stride >>= 1) {
+            const float o = __shfl_xor(v, stride, kWave);
+            const bool desc = (gl & size) == 0;  // this block sorts descending
+            const bool low = (gl & stride) == 0;
+            v = (low == desc) ? fmaxf(v, o) : fminf(v, o);
+        }
+    }
+    return __shfl(v, (lane_id() & ~(G - 1)) + j - 1, kWave);
+}
+
+// kVec: rows of a multiple of 4 scores on 16-byte aligned vectors, moved as
+// whole float4 (lane gl holds float4 u * G + gl); the refinement only needs
+// the row as a set.
+template <int G, int R, bool kVec>
+__global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(R > 16 ? 2 : 3))) void
+rows_refine_kernel(RowsArgs a)
+{
+    static_assert(G >= 1 && G <= kWave && (G & (G - 1)) == 0, "group size");
+    static_assert(!kVec || R % 4 == 0, "whole float4s per lane");
+    const int gl = lane_id() & (G - 1);
+    const int n = a.n_row;
+    const double c = a.log2e_over_alpha;
+    const double k = a.k;
+    const double tol = (double)kRowIterTol * a.alpha;
+    const float cf = (float)c;
+    const int64_t stride = (int64_t)gridDim.x * (kGroupThreads / G);
+    const int max_passes = n + 8;  // each pass that does not end crosses a score
+    // rank, among the G lane maxima, that estimates b on a first row: a lane
+    // holds a score above b with probability about 1 - e^{-k/G}
+    const int jmax = (int)fmin((double)G, fmax(1.0, rint((double)G * (1.0 - exp(-k / (double)G)))));
+    double b_prev = NAN, mean_prev = 0.0;
+    for (int64_t row = (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G; row < a.rows; row += stride) {
+        const float* s = a.s + row * (int64_t)n;
+        float v[R];
+        bool in_[R];
+        if (kVec) {
+            const float4* s4 = reinterpret_cast<const float4*>(s);
+#pragma unroll
+            for (int u = 0; u < R / 4; ++u) {
+                const int q4 = u * G + gl;
+                const bool in = 4 * q4 < n;
+                const float4 f = in ? s4[q4] : make_float4(0.f, 0.f, 0.f, 0.f);
+                v[4 * u + 0] = f.x;
+                v[4 * u + 1] = f.y;
+                v[4 * u + 2] = f.z;
+                v[4 * u + 3] = f.w;
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    in_[4 * u + h] = in;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                const int i = q * G + gl;
+                in_[q] = i < n;
+                v[q] = in_[q] ? s[i] : 0.0f;
+            }
+        }
+        bool bad = false;
+        float vmax = -INFINITY, vsum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            bad = bad || (in_[q] && !isfinite(v[q]));
+            vmax = in_[q] ? fmaxf(vmax, v[q]) : vmax;
+            vsum += in_[q] ? v[q] : 0.0f;
+        }
+        bad = group_any<G>(bad);
+        const double mean = group_sum<G>((double)vsum) / (double)n;
+        double r;
+        if (isfinite(b_prev)) {
+            r = b_prev + (mean - mean_prev);
+        } else if (k <= 4.0 * G) {
+            r = (double)group_kth_largest<G>(vmax, jmax);
+        } else {
+            r = mean;
+        }
+        double b = NAN;
+        for (int pass = 0; pass < max_passes && !bad; ++pass) {
+            // the split point r in fp64; the scores compare with and are
+            // measured from rf, the largest float <= r (no float lies in
+            // (rf, r], so the split is the same), and the group's sums are
+            // moved from rf to r by 2^{+-(r - rf) c}.  Each lane's terms and
+            // sums in fp32, the group's in fp64.
+            const float rf = __double2float_rd(r);
+            const double shift = (r - (double)rf) * c;
+            float Af = 0.0f, Bf = 0.0f;
+            uint32_t N = 0;
+            float lo = -INFINITY, hi = INFINITY;
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                if (in_[q]) {
+                    const float dv = v[q] - rf;
+                    const bool up = v[q] > rf;
+                    const float e = __builtin_amdgcn_exp2f(-fabsf(dv) * cf);
+                    Af += up ? e : 0.0f;
+                    Bf += up ? 0.0f : e;
+                    N += up ? 1u : 0u;
+                    hi = up ? fminf(hi, v[q]) : hi;
+                    lo = up ? lo : fmaxf(lo, v[q]);
+                }
+            }
+            const double A = group_sum<G>((double)Af) * exp2(shift);
+            const double B = group_sum<G>((double)Bf) * exp2(-shift);
+            N = group_sum_u32<G>(N);
+            lo = group_maxf<G>(lo);
+            hi = group_minf<G>(hi);
+            // the closed form in fp32: u to a few ulps, ln u to about 1e-7
+            // absolute, so b to about 1e-7 alpha
+            const float df = (float)(k - (double)N);
+            const float Af1 = (float)A, Bf1 = (float)B;
+            const float disc = sqrtf(df * df + Af1 * Bf1);
+            const float u = df > 0.0f ? Bf1 / (df + disc) : (disc - df) / Af1;
+            double bn;
+            if (u > 0.0f && u < INFINITY && (df > 0.0f ? Bf1 : Af1) > kRowSumMin) {
+                bn = r + a.alpha * (double)(__builtin_amdgcn_logf(u) * 0.6931471805599453f);
+            } else {
+                // the sum the root rests on underflowed (or lost its
+                // precision) about r: r lies in a gap of tens of alpha or
+                // more.  The same segment's closed form, with the sums
+                // anchored at the gap's ends, as the sorted kernels take it.
+                double Alo = 0.0, Bhi = 0.0;
+#pragma unroll
+                for (int q = 0; q < R; ++q) {
+                    if (in_[q]) {
+                        const bool up = v[q] > rf;
+                        const double e = exp2_neg_abs(((double)v[q] - (double)(up ? hi : lo)) * c);
+                        Alo += up ? 0.0 : e;
+                        Bhi += up ? e : 0.0;
+                    }
+                }
+                Alo = group_sum<G>(Alo);
+                Bhi = group_sum<G>(Bhi);
+                bn = gap_root(node(lo, Alo), node(hi, Bhi), (double)N, k, a.alpha, c);
+            }
+            if (bn >= (double)lo - tol && bn <= (double)hi + tol) {
+                b = bn;
+                break;
+            }
+            r = bn;
+        }
+        if (bad)
+            b = NAN;
+        if (gl == 0)
+            a.b[row] = b;
+        float* p = a.p + row * (int64_t)n;
+        if (kVec) {
+            float4* p4 = reinterpret_cast<float4*>(p);
+#pragma unroll
+            for (int u = 0; u < R / 4; ++u) {
+                const int q4 = u * G + gl;
+                if (4 * q4 < n)
+                    p4[q4] = bad ? make_float4(NAN, NAN, NAN, NAN)
+                                 : make_float4(row_p(v[4 * u], b, c), row_p(v[4 * u + 1], b, c),
+                                               row_p(v[4 * u + 2], b, c), row_p(v[4 * u + 3], b, c));
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                const int i = q * G + gl;
+                if (i < n)
+                    p[i] = bad ? NAN : row_p(v[q], b, c);
+            }
+        }
+        if (!bad && isfinite(b)) {
+            b_prev = b;
+            mean_prev = mean;
+        }
+    }
+}
+
 namespace {
 
 template <int kT, int R>
@@ -1016,6 +1267,52 @@ hipError_t launch_group_backward(const RowsArgs& a, hipStream_t stream)
     return launch_group_t<64, 16>(a, false, stream);
 }
 
+// The refinement forward: lane groups of G lanes, R scores each; the grid
+// is what stays resident at once (three waves per SIMD at 16 scores per
+// lane, two at 32), so each group walks several rows one grid stride apart
+// and starts each at the last b.
+template <int G, int R>
+hipError_t launch_refine_t(const RowsArgs& a, hipStream_t stream)
+{
+    constexpr int kRows = kGroupThreads / G;
+    const int64_t want = (a.rows + kRows - 1) / kRows;
+    const int64_t cap = (int64_t)kCUs * (R > 16 ? 2 : 3);
+    const dim3 grid((uint32_t)(want < cap ? want : cap));
+    const bool vec = R % 4 == 0 && (a.n_row % 4) == 0 &&
+                     ((reinterpret_cast<uintptr_t>(a.s) | reinterpret_cast<uintptr_t>(a.p)) & 15u) == 0;
+    if (vec)
+        STK_LAUNCH(kKRowsForward, stream, (rows_refine_kernel<G, R, R % 4 == 0>), grid, dim3(kGroupThreads), 0,
+                   stream, a);
+    else
+        STK_LAUNCH(kKRowsForward, stream, (rows_refine_kernel<G, R, false>), grid, dim3(kGroupThreads), 0, stream,
+                   a);
+    return hipGetLastError();
+}
+
+hipError_t launch_refine_forward(const RowsArgs& a, hipStream_t stream)
+{
+    const int n = a.n_row;
+    if (n <= 4)
+        return launch_refine_t<1, 4>(a, stream);
+    if (n <= 8)
+        return launch_refine_t<2, 4>(a, stream);
+    if (n <= 16)
+        return launch_refine_t<4, 4>(a, stream);
+    if (n <= 32)
+        return launch_refine_t<4, 8>(a, stream);
+    if (n <= 64)
+        return launch_refine_t<4, 16>(a, stream);
+    if (n <= 128)
+        return launch_refine_t<8, 16>(a, stream);
+    if (n <= 256)
+        return launch_refine_t<16, 16>(a, stream);
+    if (n <= 512)
+        return launch_refine_t<32, 16>(a, stream);
+    if (n <= 1024)
+        return launch_refine_t<64, 16>(a, stream);
+    return launch_refine_t<64, 32>(a, stream);
+}
+
 }  // namespace
 
 constexpr int kSingleThreads = 256;
@@ -1081,10 +1378,13 @@ hipError_t launch_single_status(const SingleArgs& a, hipStream_t stream)
 
 // Rows up to 1024 scores: lane groups, several rows per wave; longer rows,
 // one work-group of 256 threads (8 or 16 scores each) or 512 threads (16
-// each) per row.
+// each) per row.  The forward of rows up to 2048 scores refines each row
+// without a sort (rows_refine_kernel).
 hipError_t launch_rows(const RowsArgs& a, bool forward, hipStream_t stream)
 {
     const int n = a.n_row;
+    if (forward && n <= kRefineRowMax)
+        return launch_refine_forward(a, stream);
     if (n <= 1024)
         return forward ? launch_group_forward(a, stream) : launch_group_backward(a, stream);
     if (n <= 2048)

@@ -55,6 +55,7 @@ constexpr int64_t kSegMinN = 1 << 22;  // measured: from 10^7 scores on the reco
 static_assert(kStreamThreads == 256 && kVjpBatchLarge == 4,
               "segment geometry: large VJP tiles of 256 x 4 float4");
 constexpr int kRowMax = 8192;            // longest row one work-group solves (batched rows)
+constexpr int kRefineRowMax = 2048;      // longest row the batched forward refines in a lane group
 constexpr int kBuckets = 512;            // value buckets of the band sort
 constexpr int kBucketCap = 8192;         // largest group the solve sorts in LDS
 // The band is sorted whole (no buckets) when its expected size, n times the
