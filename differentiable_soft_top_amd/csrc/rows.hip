@@ -955,9 +955,10 @@ __global__ __launch_bounds__(kGroupThreads) void rows_group_backward_kernel(Rows
 //     shifted by the change of the row mean (any start converges; a near
 //     one in 2-4 passes);
 //   far gaps -- when the sum a step rests on underflows about r (r lies in
-//     a gap of hundreds of alpha), the step takes the same segment's closed
-//     form with its sums anchored at the gap's ends (gap_root, the sorted
-//     kernels' form), which needs no sum about r.
+//     a gap of tens of alpha or more), the next pass re-sums the same split
+//     with each side measured from its nearest score and takes the
+//     segment's closed form anchored at the gap's ends (gap_root, the
+//     sorted kernels' form), which needs no sum about r.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -980,7 +981,7 @@ __device__ __forceinline__ float group_maxf(float v)
 }
 
 template <int G>
-__device__ __forceinline__ uint32_t group_sum_u32(uint32_t v)
+__device__ __forceinline__ float group_sumf(float v)
 {
 #pragma unroll
     for (int off = G / 2; off > 0; off >>= 1)
@@ -988,12 +989,31 @@ __device__ __forceinline__ uint32_t group_sum_u32(uint32_t v)
     return v;
 }
 
-// 2^-|y| for fp64 y: fp32 exp2 of the fraction, exact power of two
-__device__ __forceinline__ double exp2_neg_abs(double y)
+// The positive root u of (A/2) u^2 + d u - B/2 = 0 in its cancellation-free
+// form, in fp32 (a few ulps).
+__device__ __forceinline__ float row_root_u(float d, float A, float B)
 {
-    const double t = fmin(fabs(y), 1100.0);
-    const double j = floor(t);
-    return ldexp((double)__builtin_amdgcn_exp2f(-(float)(t - j)), -(int)j);
+    const float disc = sqrtf(d * d + A * B);
+    return d > 0.0f ? B / (d + disc) : (disc - d) / A;
+}
+
+// p = F((s - b)/alpha) for b = bf + sb alpha / log2(e), bf a float <= b and
+// 0 <= sb small: (s - bf) in fp32 (exact for s within a factor 2 of bf),
+// the exponential in fp32; to about 1e-7.
+__device__ __forceinline__ float row_p_split(float v, float bf, float sb, float cf)
+{
+    const float x = (v - bf) * cf - sb;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x));
+    return v <= bf ? 0.5f * e : 1.0f - 0.5f * e;
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t group_sum_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
 }
 
 constexpr float kRowIterTol = 0x1p-30f;  // convergence slack, in units of alpha
@@ -1023,14 +1043,15 @@ __device__ __forceinline__ float group_kth_largest(float v, int j)
 // kVec: rows of a multiple of 4 scores on 16-byte aligned vectors, moved as
 // whole float4 (lane gl holds float4 u * G + gl); the refinement only needs
 // the row as a set.
-template <int G, int R, bool kVec>
-__global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(R > 16 ? 2 : 3))) void
+// kFull: n_row == G * R, every slot holds a score (no per-score guards).
+template <int G, int R, bool kVec, bool kFull>
+__global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(R > 16 ? 3 : 4))) void
 rows_refine_kernel(RowsArgs a)
 {
     static_assert(G >= 1 && G <= kWave && (G & (G - 1)) == 0, "group size");
     static_assert(!kVec || R % 4 == 0, "whole float4s per lane");
     const int gl = lane_id() & (G - 1);
-    const int n = a.n_row;
+    const int n = kFull ? G * R : a.n_row;
     const double c = a.log2e_over_alpha;
     const double k = a.k;
     const double tol = (double)kRowIterTol * a.alpha;
@@ -1040,34 +1061,40 @@ rows_refine_kernel(RowsArgs a)
     // rank, among the G lane maxima, that estimates b on a first row: a lane
     // holds a score above b with probability about 1 - e^{-k/G}
     const int jmax = (int)fmin((double)G, fmax(1.0, rint((double)G * (1.0 - exp(-k / (double)G)))));
-    double b_prev = NAN, mean_prev = 0.0;
-    for (int64_t row = (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G; row < a.rows; row += stride) {
-        const float* s = a.s + row * (int64_t)n;
-        float v[R];
-        bool in_[R];
+    // which of the lane's R slots hold a score (the same for every row)
+    bool in_[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+        in_[q] = kFull || (kVec ? 4 * ((q / 4) * G + gl) < n : q * G + gl < n);
+    auto load_row = [&](int64_t rw, float (&dst)[R]) {
+        const float* s = a.s + rw * (int64_t)n;
         if (kVec) {
             const float4* s4 = reinterpret_cast<const float4*>(s);
 #pragma unroll
             for (int u = 0; u < R / 4; ++u) {
-                const int q4 = u * G + gl;
-                const bool in = 4 * q4 < n;
-                const float4 f = in ? s4[q4] : make_float4(0.f, 0.f, 0.f, 0.f);
-                v[4 * u + 0] = f.x;
-                v[4 * u + 1] = f.y;
-                v[4 * u + 2] = f.z;
-                v[4 * u + 3] = f.w;
-#pragma unroll
-                for (int h = 0; h < 4; ++h)
-                    in_[4 * u + h] = in;
+                const float4 f = in_[4 * u] ? s4[u * G + gl] : make_float4(0.f, 0.f, 0.f, 0.f);
+                dst[4 * u + 0] = f.x;
+                dst[4 * u + 1] = f.y;
+                dst[4 * u + 2] = f.z;
+                dst[4 * u + 3] = f.w;
             }
         } else {
 #pragma unroll
-            for (int q = 0; q < R; ++q) {
-                const int i = q * G + gl;
-                in_[q] = i < n;
-                v[q] = in_[q] ? s[i] : 0.0f;
-            }
+            for (int q = 0; q < R; ++q)
+                dst[q] = in_[q] ? s[q * G + gl] : 0.0f;
         }
+    };
+    double b_prev = NAN, mean_prev = 0.0;
+    int64_t row = (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G;
+    float v[R];
+    if (row < a.rows)
+        load_row(row, v);
+    for (; row < a.rows; row += stride) {
+        // the next row's loads go out before this row's passes
+        float nx[R];
+        const bool more = row + stride < a.rows;
+        if (more)
+            load_row(row + stride, nx);
         bool bad = false;
         float vmax = -INFINITY, vsum = 0.0f;
 #pragma unroll
@@ -1087,62 +1114,70 @@ rows_refine_kernel(RowsArgs a)
             r = mean;
         }
         double b = NAN;
+        // gap: this pass re-sums the last pass's split with each side
+        // measured from its nearest score (glo, ghi) instead of from rf
+        bool gap = false;
+        float rf = 0.0f, glo = 0.0f, ghi = 0.0f;
         for (int pass = 0; pass < max_passes && !bad; ++pass) {
             // the split point r in fp64; the scores compare with and are
             // measured from rf, the largest float <= r (no float lies in
-            // (rf, r], so the split is the same), and the group's sums are
-            // moved from rf to r by 2^{+-(r - rf) c}.  Each lane's terms and
-            // sums in fp32, the group's in fp64.
-            const float rf = __double2float_rd(r);
-            const double shift = (r - (double)rf) * c;
-            float Af = 0.0f, Bf = 0.0f;
+            // (rf, r], so the split is the same), and the sums are moved
+            // from rf to r by 2^{+-(r - rf) c}.  Each lane's terms and sums
+            // in fp32 (two partial sums each); the group's sums in fp32 to
+            // steer, and in fp64 for the pass that ends.
+            if (!gap)
+                rf = __double2float_rd(r);
+            const float ref_hi = gap ? ghi : rf, ref_lo = gap ? glo : rf;
+            float Af[2] = {0.0f, 0.0f}, Bf[2] = {0.0f, 0.0f};
             uint32_t N = 0;
             float lo = -INFINITY, hi = INFINITY;
 #pragma unroll
             for (int q = 0; q < R; ++q) {
                 if (in_[q]) {
-                    const float dv = v[q] - rf;
                     const bool up = v[q] > rf;
-                    const float e = __builtin_amdgcn_exp2f(-fabsf(dv) * cf);
-                    Af += up ? e : 0.0f;
-                    Bf += up ? 0.0f : e;
+                    const float e = __builtin_amdgcn_exp2f(-fabsf(v[q] - (up ? ref_hi : ref_lo)) * cf);
+                    Af[q & 1] += up ? e : 0.0f;
+                    Bf[q & 1] += up ? 0.0f : e;
                     N += up ? 1u : 0u;
                     hi = up ? fminf(hi, v[q]) : hi;
                     lo = up ? lo : fmaxf(lo, v[q]);
                 }
             }
-            const double A = group_sum<G>((double)Af) * exp2(shift);
-            const double B = group_sum<G>((double)Bf) * exp2(-shift);
+            const float la = Af[0] + Af[1], lb = Bf[0] + Bf[1];
             N = group_sum_u32<G>(N);
             lo = group_maxf<G>(lo);
             hi = group_minf<G>(hi);
-            // the closed form in fp32: u to a few ulps, ln u to about 1e-7
-            // absolute, so b to about 1e-7 alpha
-            const float df = (float)(k - (double)N);
-            const float Af1 = (float)A, Bf1 = (float)B;
-            const float disc = sqrtf(df * df + Af1 * Bf1);
-            const float u = df > 0.0f ? Bf1 / (df + disc) : (disc - df) / Af1;
             double bn;
-            if (u > 0.0f && u < INFINITY && (df > 0.0f ? Bf1 : Af1) > kRowSumMin) {
-                bn = r + a.alpha * (double)(__builtin_amdgcn_logf(u) * 0.6931471805599453f);
+            if (gap) {
+                // the segment's closed form with its sums anchored at the
+                // gap's ends, as the sorted kernels take it
+                bn = gap_root(node(lo, group_sum<G>((double)lb)), node(hi, group_sum<G>((double)la)), (double)N, k,
+                              a.alpha, c);
+                gap = false;
             } else {
-                // the sum the root rests on underflowed (or lost its
-                // precision) about r: r lies in a gap of tens of alpha or
-                // more.  The same segment's closed form, with the sums
-                // anchored at the gap's ends, as the sorted kernels take it.
-                double Alo = 0.0, Bhi = 0.0;
-#pragma unroll
-                for (int q = 0; q < R; ++q) {
-                    if (in_[q]) {
-                        const bool up = v[q] > rf;
-                        const double e = exp2_neg_abs(((double)v[q] - (double)(up ? hi : lo)) * c);
-                        Alo += up ? 0.0 : e;
-                        Bhi += up ? e : 0.0;
-                    }
+                const float sh = (float)((r - (double)rf) * c);  // >= 0, below an ulp of r times c
+                const float ga = group_sumf<G>(la) * __builtin_amdgcn_exp2f(sh);
+                const float gb = group_sumf<G>(lb) * __builtin_amdgcn_exp2f(-sh);
+                const float df = (float)(k - (double)N);
+                float u = row_root_u(df, ga, gb);
+                if (!(u > 0.0f && u < INFINITY && (df > 0.0f ? gb : ga) > kRowSumMin)) {
+                    // the sum the root rests on underflowed (or lost its
+                    // precision) about r: r lies in a gap of tens of alpha
+                    // or more; the next pass re-sums this split from the
+                    // gap's ends
+                    gap = true;
+                    glo = lo;
+                    ghi = hi;
+                    continue;
                 }
-                Alo = group_sum<G>(Alo);
-                Bhi = group_sum<G>(Bhi);
-                bn = gap_root(node(lo, Alo), node(hi, Bhi), (double)N, k, a.alpha, c);
+                bn = r + a.alpha * (double)(__builtin_amdgcn_logf(u) * 0.6931471805599453f);
+                if (bn >= (double)lo - tol && bn <= (double)hi + tol) {
+                    // the end: the same root from fp64 group sums
+                    const float fa = (float)group_sum<G>((double)la) * __builtin_amdgcn_exp2f(sh);
+                    const float fb = (float)group_sum<G>((double)lb) * __builtin_amdgcn_exp2f(-sh);
+                    u = row_root_u(df, fa, fb);
+                    bn = r + a.alpha * (double)(__builtin_amdgcn_logf(u) * 0.6931471805599453f);
+                }
             }
             if (bn >= (double)lo - tol && bn <= (double)hi + tol) {
                 b = bn;
@@ -1155,27 +1190,35 @@ rows_refine_kernel(RowsArgs a)
         if (gl == 0)
             a.b[row] = b;
         float* p = a.p + row * (int64_t)n;
+        const float bf = isfinite(b) ? __double2float_rd(b) : (float)b;
+        const float sb = isfinite(b) ? (float)((b - (double)bf) * c) : 0.0f;
         if (kVec) {
             float4* p4 = reinterpret_cast<float4*>(p);
 #pragma unroll
             for (int u = 0; u < R / 4; ++u) {
                 const int q4 = u * G + gl;
-                if (4 * q4 < n)
+                if (kFull || 4 * q4 < n)
                     p4[q4] = bad ? make_float4(NAN, NAN, NAN, NAN)
-                                 : make_float4(row_p(v[4 * u], b, c), row_p(v[4 * u + 1], b, c),
-                                               row_p(v[4 * u + 2], b, c), row_p(v[4 * u + 3], b, c));
+                                 : make_float4(row_p_split(v[4 * u], bf, sb, cf), row_p_split(v[4 * u + 1], bf, sb, cf),
+                                               row_p_split(v[4 * u + 2], bf, sb, cf),
+                                               row_p_split(v[4 * u + 3], bf, sb, cf));
             }
         } else {
 #pragma unroll
             for (int q = 0; q < R; ++q) {
                 const int i = q * G + gl;
-                if (i < n)
-                    p[i] = bad ? NAN : row_p(v[q], b, c);
+                if (kFull || i < n)
+                    p[i] = bad ? NAN : row_p_split(v[q], bf, sb, cf);
             }
         }
         if (!bad && isfinite(b)) {
             b_prev = b;
             mean_prev = mean;
+        }
+        if (more) {
+#pragma unroll
+            for (int q = 0; q < R; ++q)
+                v[q] = nx[q];
         }
     }
 }
@@ -1268,24 +1311,28 @@ hipError_t launch_group_backward(const RowsArgs& a, hipStream_t stream)
 }
 
 // The refinement forward: lane groups of G lanes, R scores each; the grid
-// is what stays resident at once (three waves per SIMD at 16 scores per
-// lane, two at 32), so each group walks several rows one grid stride apart
-// and starts each at the last b.
+// is what stays resident at once (four waves per SIMD at 16 scores per
+// lane, three at 32), so each group walks several rows one grid stride
+// apart and starts each at the last b.
 template <int G, int R>
 hipError_t launch_refine_t(const RowsArgs& a, hipStream_t stream)
 {
     constexpr int kRows = kGroupThreads / G;
     const int64_t want = (a.rows + kRows - 1) / kRows;
-    const int64_t cap = (int64_t)kCUs * (R > 16 ? 2 : 3);
+    const int64_t cap = (int64_t)kCUs * (R > 16 ? 3 : 4);
     const dim3 grid((uint32_t)(want < cap ? want : cap));
     const bool vec = R % 4 == 0 && (a.n_row % 4) == 0 &&
                      ((reinterpret_cast<uintptr_t>(a.s) | reinterpret_cast<uintptr_t>(a.p)) & 15u) == 0;
-    if (vec)
-        STK_LAUNCH(kKRowsForward, stream, (rows_refine_kernel<G, R, R % 4 == 0>), grid, dim3(kGroupThreads), 0,
+    const bool full = a.n_row == G * R;
+    if (vec && full)
+        STK_LAUNCH(kKRowsForward, stream, (rows_refine_kernel<G, R, R % 4 == 0, true>), grid, dim3(kGroupThreads), 0,
+                   stream, a);
+    else if (vec)
+        STK_LAUNCH(kKRowsForward, stream, (rows_refine_kernel<G, R, R % 4 == 0, false>), grid, dim3(kGroupThreads), 0,
                    stream, a);
     else
-        STK_LAUNCH(kKRowsForward, stream, (rows_refine_kernel<G, R, false>), grid, dim3(kGroupThreads), 0, stream,
-                   a);
+        STK_LAUNCH(kKRowsForward, stream, (rows_refine_kernel<G, R, false, false>), grid, dim3(kGroupThreads), 0,
+                   stream, a);
     return hipGetLastError();
 }
 
