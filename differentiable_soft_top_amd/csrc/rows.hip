@@ -1352,7 +1352,7 @@ hipError_t launch_refine_forward(const RowsArgs& a, hipStream_t stream)
     if (n <= 128)
         return launch_refine_t<8, 16>(a, stream);
     if (n <= 256)
-        return launch_refine_t<16, 16>(a, stream);
+        return launch_refine_t<8, 32>(a, stream);
     if (n <= 512)
         return launch_refine_t<32, 16>(a, stream);
     if (n <= 1024)
