@@ -1223,6 +1223,298 @@ rows_refine_kernel(RowsArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Rows longer than a lane group holds: the same refinement with one
+// work-group per row (kWgT threads; the work-group walks rows one grid
+// stride apart).  Rows up to kWgT * R scores stay in registers; longer
+// ones are streamed from memory on every pass (kStream), so any row length
+// runs batched, with no host loop.  Reductions go through LDS (two
+// barriers a pass).  A first row starts at the mean of the four waves'
+// lane-maxima quantiles (k/4 of the row above b per wave), the mirrored
+// lane-minima quantile when n - k is small, or the normal quantile of the
+// row's mean and spread otherwise; later rows at the previous b shifted by
+// the change of the row mean.
+// ---------------------------------------------------------------------------
+constexpr int kWgT = 256;
+
+namespace {
+
+struct WgRed {
+    float f[4][kWgT / kWave];
+    double d[2][kWgT / kWave];
+    uint32_t u[kWgT / kWave];
+};
+
+// Work-group totals of one pass (every thread receives them): fp32 sums
+// of the two sides, the count above, the nearest scores below and above.
+__device__ __forceinline__ void wg_pass_totals(float& la, float& lb, uint32_t& N, float& lo, float& hi, WgRed& L)
+{
+    constexpr int kW = kWgT / kWave;
+    const int wave = threadIdx.x / kWave;
+    la = group_sumf<kWave>(la);
+    lb = group_sumf<kWave>(lb);
+    N = group_sum_u32<kWave>(N);
+    lo = group_maxf<kWave>(lo);
+    hi = group_minf<kWave>(hi);
+    if (lane_id() == 0) {
+        L.f[0][wave] = la;
+        L.f[1][wave] = lb;
+        L.f[2][wave] = lo;
+        L.f[3][wave] = hi;
+        L.u[wave] = N;
+    }
+    __syncthreads();
+    la = lb = 0.0f;
+    N = 0;
+    lo = -INFINITY;
+    hi = INFINITY;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        la += L.f[0][w];
+        lb += L.f[1][w];
+        lo = fmaxf(lo, L.f[2][w]);
+        hi = fminf(hi, L.f[3][w]);
+        N += L.u[w];
+    }
+    __syncthreads();
+}
+
+// Work-group fp64 totals of two values.
+__device__ __forceinline__ void wg_sum2(double& x, double& y, WgRed& L)
+{
+    constexpr int kW = kWgT / kWave;
+    const int wave = threadIdx.x / kWave;
+    x = group_sum<kWave>(x);
+    y = group_sum<kWave>(y);
+    if (lane_id() == 0) {
+        L.d[0][wave] = x;
+        L.d[1][wave] = y;
+    }
+    __syncthreads();
+    x = y = 0.0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        x += L.d[0][w];
+        y += L.d[1][w];
+    }
+    __syncthreads();
+}
+
+}  // namespace
+
+template <int R, bool kStream>
+__global__ __launch_bounds__(kWgT) void rows_refine_wg_kernel(RowsArgs a)
+{
+    __shared__ WgRed L;
+    const int tid = threadIdx.x;
+    const int n = a.n_row;
+    const double c = a.log2e_over_alpha;
+    const double k = a.k;
+    const double tol = (double)kRowIterTol * a.alpha;
+    const float cf = (float)c;
+    const bool vec = (n % 4) == 0 && ((reinterpret_cast<uintptr_t>(a.s) | reinterpret_cast<uintptr_t>(a.p)) & 15u) == 0;
+    // slot q of this thread: float4 q / 4 at (q / 4) * kWgT + tid, or the
+    // single score q * kWgT + tid
+    auto pos = [&](int q) -> int { return vec ? 4 * ((q / 4) * kWgT + tid) + (q & 3) : q * kWgT + tid; };
+    const int max_passes = n + 8;
+    const double kw = k / (double)(kWgT / kWave);  // scores above b per wave's quarter
+    const int jw = (int)fmin((double)kWave, fmax(1.0, rint((double)kWave * (1.0 - exp(-kw / (double)kWave)))));
+    const double nkw = ((double)n - k) / (double)(kWgT / kWave);
+    const int jwl = (int)fmin((double)kWave, fmax(1.0, rint((double)kWave * (1.0 - exp(-nkw / (double)kWave)))));
+    double b_prev = NAN, mean_prev = 0.0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const float* s = a.s + row * (int64_t)n;
+        float* p = a.p + row * (int64_t)n;
+        float v[kStream ? 1 : R];
+        // one sweep over this thread's scores: f(score) for each
+        auto sweep = [&](auto&& f) {
+            if (!kStream) {
+#pragma unroll
+                for (int q = 0; q < R; ++q)
+                    if (pos(q) < n)
+                        f(v[q]);
+            } else if (vec) {
+                const float4* s4 = reinterpret_cast<const float4*>(s);
+                for (int i = tid; i < n / 4; i += kWgT) {
+                    const float4 x = s4[i];
+                    f(x.x);
+                    f(x.y);
+                    f(x.z);
+                    f(x.w);
+                }
+            } else {
+                for (int i = tid; i < n; i += kWgT)
+                    f(s[i]);
+            }
+        };
+        if (!kStream) {
+            if (vec) {
+                const float4* s4 = reinterpret_cast<const float4*>(s);
+#pragma unroll
+                for (int u = 0; u < R / 4; ++u) {
+                    const int i4 = u * kWgT + tid;
+                    const float4 x = 4 * i4 < n ? s4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    v[4 * u] = x.x;
+                    v[4 * u + 1] = x.y;
+                    v[4 * u + 2] = x.z;
+                    v[4 * u + 3] = x.w;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < R; ++q)
+                    v[q] = pos(q) < n ? s[pos(q)] : 0.0f;
+            }
+        }
+        // the row's statistics: finiteness, mean and spread, each thread's
+        // extremes
+        float tmax = -INFINITY, tmin = INFINITY, tsum = 0.0f, tsq = 0.0f;
+        bool tbad = false;
+        sweep([&](float x) {
+            tbad = tbad || !isfinite(x);
+            tmax = fmaxf(tmax, x);
+            tmin = fminf(tmin, x);
+            tsum += x;
+            tsq += x * x;
+        });
+        float est = 0.0f;
+        if (kw <= 4.0 * kWave)
+            est = group_kth_largest<kWave>(tmax, jw);
+        else if (nkw <= 4.0 * kWave)
+            est = -group_kth_largest<kWave>(-tmin, jwl);
+        {
+            double ds = tsum, dq = tsq;
+            wg_sum2(ds, dq, L);
+            tsum = (float)ds;
+            tsq = (float)dq;
+        }
+        const double mean = (double)tsum / (double)n;
+        {
+            // the waves' estimates (one lane each) averaged; any bad score
+            float e1 = lane_id() == 0 ? est : 0.0f, e2 = tbad ? 1.0f : 0.0f, e3 = 0.0f, e4 = 0.0f;
+            uint32_t zu = 0;
+            wg_pass_totals(e1, e2, zu, e3, e4, L);
+            est = e1 / (float)(kWgT / kWave);
+            tbad = e2 > 0.0f;
+        }
+        const bool bad = tbad;
+        double r;
+        if (isfinite(b_prev)) {
+            r = b_prev + (mean - mean_prev);
+        } else if (kw <= 4.0 * kWave || nkw <= 4.0 * kWave) {
+            r = (double)est;
+        } else {
+            const double var = fmax((double)tsq / (double)n - mean * mean, 0.0);
+            r = mean - sqrt(2.0 * var) * erfcinv(2.0 * (1.0 - k / (double)n));
+        }
+        double b = NAN;
+        bool gap = false;
+        float rf = 0.0f, glo = 0.0f, ghi = 0.0f;
+        for (int pass = 0; pass < max_passes && !bad; ++pass) {
+            if (!gap)
+                rf = __double2float_rd(r);
+            const float ref_hi = gap ? ghi : rf, ref_lo = gap ? glo : rf;
+            float Af = 0.0f, Bf = 0.0f;
+            uint32_t N = 0;
+            float lo = -INFINITY, hi = INFINITY;
+            sweep([&](float x) {
+                const bool up = x > rf;
+                const float e = __builtin_amdgcn_exp2f(-fabsf(x - (up ? ref_hi : ref_lo)) * cf);
+                Af += up ? e : 0.0f;
+                Bf += up ? 0.0f : e;
+                N += up ? 1u : 0u;
+                hi = up ? fminf(hi, x) : hi;
+                lo = up ? lo : fmaxf(lo, x);
+            });
+            const float la = Af, lb = Bf;
+            float ga = la, gb = lb;
+            wg_pass_totals(ga, gb, N, lo, hi, L);
+            double bn;
+            if (gap) {
+                double A = la, B = lb;
+                wg_sum2(A, B, L);
+                bn = gap_root(node(lo, B), node(hi, A), (double)N, k, a.alpha, c);
+                gap = false;
+            } else {
+                const float sh = (float)((r - (double)rf) * c);
+                const float df = (float)(k - (double)N);
+                float u = row_root_u(df, ga * __builtin_amdgcn_exp2f(sh), gb * __builtin_amdgcn_exp2f(-sh));
+                if (!(u > 0.0f && u < INFINITY && (df > 0.0f ? gb : ga) > kRowSumMin)) {
+                    gap = true;
+                    glo = lo;
+                    ghi = hi;
+                    continue;
+                }
+                bn = r + a.alpha * (double)(__builtin_amdgcn_logf(u) * 0.6931471805599453f);
+                if (bn >= (double)lo - tol && bn <= (double)hi + tol) {
+                    double A = la, B = lb;
+                    wg_sum2(A, B, L);
+                    u = row_root_u(df, (float)A * __builtin_amdgcn_exp2f(sh), (float)B * __builtin_amdgcn_exp2f(-sh));
+                    bn = r + a.alpha * (double)(__builtin_amdgcn_logf(u) * 0.6931471805599453f);
+                }
+            }
+            if (bn >= (double)lo - tol && bn <= (double)hi + tol) {
+                b = bn;
+                break;
+            }
+            r = bn;
+        }
+        if (bad)
+            b = NAN;
+        if (tid == 0)
+            a.b[row] = b;
+        const float bf = isfinite(b) ? __double2float_rd(b) : (float)b;
+        const float sb = isfinite(b) ? (float)((b - (double)bf) * c) : 0.0f;
+        if (!kStream) {
+#pragma unroll
+            for (int q = 0; q < R; ++q)
+                if (pos(q) < n)
+                    p[pos(q)] = bad ? NAN : row_p_split(v[q], bf, sb, cf);
+        } else if (vec) {
+            const float4* s4 = reinterpret_cast<const float4*>(s);
+            float4* p4 = reinterpret_cast<float4*>(p);
+            for (int i = tid; i < n / 4; i += kWgT) {
+                const float4 x = s4[i];
+                p4[i] = bad ? make_float4(NAN, NAN, NAN, NAN)
+                            : make_float4(row_p_split(x.x, bf, sb, cf), row_p_split(x.y, bf, sb, cf),
+                                          row_p_split(x.z, bf, sb, cf), row_p_split(x.w, bf, sb, cf));
+            }
+        } else {
+            for (int i = tid; i < n; i += kWgT)
+                p[i] = bad ? NAN : row_p_split(s[i], bf, sb, cf);
+        }
+        if (!bad && isfinite(b)) {
+            b_prev = b;
+            mean_prev = mean;
+        }
+    }
+}
+
+// The backward of rows longer than kRowMax: one work-group per row, the
+// row streamed twice (D and G, then the gradient), the arithmetic of the
+// other row backwards (fp32 d with s - b in fp64, fp64 sums with exact
+// products, the ratio as a float pair).
+__global__ __launch_bounds__(kWgT) void rows_backward_wg_kernel(RowsArgs a)
+{
+    __shared__ WgRed L;
+    const int tid = threadIdx.x;
+    const int n = a.n_row;
+    const double c = a.log2e_over_alpha;
+    const float inv_alpha = (float)(1.0 / a.alpha);
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const float* s = a.s + row * (int64_t)n;
+        const float* g = a.g + row * (int64_t)n;
+        float* out = a.grad + row * (int64_t)n;
+        const double b = a.b_in[row];
+        double D = 0.0, Gs = 0.0;
+        for (int i = tid; i < n; i += kWgT)
+            acc_dg(row_d(s[i], b, c), g[i], D, Gs);
+        wg_sum2(D, Gs, L);
+        const Ratio2 ratio = split_ratio(D > 0.0 ? Gs / D : 0.0);
+        for (int i = tid; i < n; i += kWgT)
+            out[i] = row_d(s[i], b, c) * inv_alpha * minus_ratio(g[i], ratio);
+    }
+}
+
 namespace {
 
 template <int kT, int R>
@@ -1423,22 +1715,38 @@ hipError_t launch_single_status(const SingleArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Rows up to 1024 scores: lane groups, several rows per wave; longer rows,
-// one work-group of 256 threads (8 or 16 scores each) or 512 threads (16
-// each) per row.  The forward of rows up to 2048 scores refines each row
-// without a sort (rows_refine_kernel).
+// The forward: rows up to 2048 scores refined in lane groups, longer rows
+// by one work-group each (in registers up to 8192 scores, streamed beyond).
+// The backward: lane groups up to 1024 scores, one work-group of 256
+// threads (8 or 16 scores each) or 512 threads (16 each) per row up to
+// kRowMax, and streamed work-groups beyond.
 hipError_t launch_rows(const RowsArgs& a, bool forward, hipStream_t stream)
 {
     const int n = a.n_row;
     if (forward && n <= kRefineRowMax)
         return launch_refine_forward(a, stream);
+    if (forward) {
+        // one work-group per row (resident work-groups walk the rows)
+        const int64_t cap = (int64_t)kCUs * 4;
+        const dim3 grid((uint32_t)(a.rows < cap ? a.rows : cap));
+        if (n <= kWgT * 32)
+            STK_LAUNCH(kKRowsForward, stream, (rows_refine_wg_kernel<32, false>), grid, dim3(kWgT), 0, stream, a);
+        else
+            STK_LAUNCH(kKRowsForward, stream, (rows_refine_wg_kernel<1, true>), grid, dim3(kWgT), 0, stream, a);
+        return hipGetLastError();
+    }
     if (n <= 1024)
-        return forward ? launch_group_forward(a, stream) : launch_group_backward(a, stream);
+        return launch_group_backward(a, stream);
     if (n <= 2048)
-        return launch_rows_t<256, 8>(a, forward, stream);
+        return launch_rows_t<256, 8>(a, false, stream);
     if (n <= 4096)
-        return launch_rows_t<256, 16>(a, forward, stream);
-    return launch_rows_t<512, 16>(a, forward, stream);
+        return launch_rows_t<256, 16>(a, false, stream);
+    if (n <= kRowMax)
+        return launch_rows_t<512, 16>(a, false, stream);
+    const int64_t cap = (int64_t)kCUs * 4;
+    STK_LAUNCH(kKRowsBackward, stream, rows_backward_wg_kernel, dim3((uint32_t)(a.rows < cap ? a.rows : cap)),
+               dim3(kWgT), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace stk

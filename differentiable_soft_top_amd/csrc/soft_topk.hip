@@ -1545,11 +1545,9 @@ int soft_topk_dftopk_forward(const float* scores, int64_t n, double k, double al
 
 size_t soft_topk_rows_workspace_bytes(int64_t rows, int64_t n_row)
 {
-    if (!rows_ok(rows, n_row) || n_row <= kRowMax)
-        return 0;
-    const size_t f = soft_topk_workspace_bytes(n_row, nullptr);
-    const size_t bw = soft_topk_backward_workspace_bytes(n_row);
-    return f > bw ? f : bw;
+    (void)rows;
+    (void)n_row;
+    return 0;  // every row length runs in the batched kernels, in registers or streamed
 }
 
 int soft_topk_rows_forward(const float* scores, int64_t rows, int64_t n_row, double k, double alpha, float* out_p,
@@ -1559,30 +1557,13 @@ int soft_topk_rows_forward(const float* scores, int64_t rows, int64_t n_row, dou
         return SOFT_TOPK_EINVAL;
     if (!(alpha > 0.0) || !isfinite(alpha) || !(k > 0.0) || !(k < (double)n_row) || !isfinite(k))
         return SOFT_TOPK_EINVAL;
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    if (n_row <= kRowMax) {
-        RowsArgs a = rows_args(scores, rows, n_row, alpha);
-        a.p = out_p;
-        a.b = out_b;
-        a.k = k;
-        STK_HIP(launch_rows(a, true, st));
-        return SOFT_TOPK_OK;
-    }
-    // longer rows: the single-vector path, one row after another
-    if (!workspace || workspace_bytes < soft_topk_workspace_bytes(n_row, nullptr))
-        return SOFT_TOPK_EWORKSPACE;
-    for (int64_t r = 0; r < rows; ++r) {
-        float* p = out_p + r * n_row;
-        const int rc = soft_topk_forward(scores + r * n_row, n_row, k, alpha, p, out_b + r, workspace, workspace_bytes,
-                                         stream);
-        if (rc == SOFT_TOPK_ENONFINITE) {
-            // all-ones bytes are a NaN in fp32 and in fp64
-            STK_HIP(hipMemsetAsync(p, 0xFF, sizeof(float) * (size_t)n_row, st));
-            STK_HIP(hipMemsetAsync(out_b + r, 0xFF, sizeof(double), st));
-        } else if (rc) {
-            return rc;
-        }
-    }
+    (void)workspace;
+    (void)workspace_bytes;
+    RowsArgs a = rows_args(scores, rows, n_row, alpha);
+    a.p = out_p;
+    a.b = out_b;
+    a.k = k;
+    STK_HIP(launch_rows(a, true, static_cast<hipStream_t>(stream)));
     return SOFT_TOPK_OK;
 }
 
@@ -1593,22 +1574,13 @@ int soft_topk_rows_backward(const float* grad_p, const float* scores, int64_t ro
         return SOFT_TOPK_EINVAL;
     if (!(alpha > 0.0) || !isfinite(alpha))
         return SOFT_TOPK_EINVAL;
-    if (n_row <= kRowMax) {
-        RowsArgs a = rows_args(scores, rows, n_row, alpha);
-        a.g = grad_p;
-        a.grad = grad_s;
-        a.b_in = b;
-        STK_HIP(launch_rows(a, false, static_cast<hipStream_t>(stream)));
-        return SOFT_TOPK_OK;
-    }
-    if (!workspace || workspace_bytes < soft_topk_backward_workspace_bytes(n_row))
-        return SOFT_TOPK_EWORKSPACE;
-    for (int64_t r = 0; r < rows; ++r) {
-        const int rc = soft_topk_backward(grad_p + r * n_row, scores + r * n_row, n_row, alpha, b + r,
-                                          grad_s + r * n_row, workspace, workspace_bytes, stream);
-        if (rc)
-            return rc;
-    }
+    (void)workspace;
+    (void)workspace_bytes;
+    RowsArgs a = rows_args(scores, rows, n_row, alpha);
+    a.g = grad_p;
+    a.grad = grad_s;
+    a.b_in = b;
+    STK_HIP(launch_rows(a, false, static_cast<hipStream_t>(stream)));
     return SOFT_TOPK_OK;
 }
 

@@ -280,16 +280,18 @@ int soft_topk_backward_noalloc(const float* grad_p, const float* scores, int64_t
  * scores + r * n_row.  Every row gets its own threshold b_r (out_b: fp64[rows],
  * device) with sum_i F((s_ri - b_r)/alpha) = k, and out_p[r * n_row + i] =
  * F((s_ri - b_r)/alpha); k and alpha are shared by all rows (0 < k < n_row,
- * alpha > 0).  Rows of at most 8192 scores are solved on the device alone
- * (several rows per wave up to 1024 scores, one work-group per row above),
- * fully asynchronously on `stream`, and need no workspace; longer rows run
- * the single-vector forward row after row (each waits for its status) in
- * `workspace`.  Accuracy on the device-only rows: the sums use fp32
- * exponentials (relative error a few 1e-7) inside fp64 sums and an fp64
- * closed form, so b is within about 1e-7 * alpha and p within about 1e-7
- * of the exact values.  A row holding a NaN or an infinite score gets
- * b = NaN and p = NaN; the call still returns OK.  Errors: EINVAL,
- * EWORKSPACE before any launch; EHIP on a launch failure.
+ * alpha > 0).  Every row length is solved on the device alone, fully
+ * asynchronously on `stream`, with no workspace (workspace may be NULL):
+ * each row is refined without a sort (the segment's closed form about a
+ * split point, repeated until no score separates the point from its
+ * root), several rows per wave up to 2048 scores, one work-group per row
+ * above (the row in registers up to 8192 scores, streamed beyond).
+ * Accuracy: fp32 exponentials (relative error a few 1e-7) summed in fp32
+ * per thread and in fp64 across the row, and a closed form to a few fp32
+ * ulps, so b is within about 1e-6 * alpha (the tests see 1e-7) and p
+ * within about 1e-7 of the exact values.  A row holding a NaN or an
+ * infinite score gets b = NaN and p = NaN; the call still returns OK.
+ * Errors: EINVAL before any launch; EHIP on a launch failure.
  */
 int soft_topk_rows_forward(const float* scores, int64_t rows, int64_t n_row,
                            double k, double alpha, float* out_p, double* out_b,
@@ -298,9 +300,9 @@ int soft_topk_rows_forward(const float* scores, int64_t rows, int64_t n_row,
 /*
  * Backward of the batched rows: grad_s[r * n_row + i] =
  * (d_ri/alpha)(g_ri - G_r/D_r) with each row's own D_r and G_r, as in
- * soft_topk_backward (b: the forward's out_b).  Rows of at most 8192 scores
- * need no workspace and are fully asynchronous; longer rows run the
- * single-vector backward row after row in `workspace`.  Errors as
+ * soft_topk_backward (b: the forward's out_b).  No workspace (may be NULL);
+ * fully asynchronous: several rows per wave up to 1024 scores, one
+ * work-group per row above (streamed beyond 8192).  Errors as
  * soft_topk_rows_forward.
  */
 int soft_topk_rows_backward(const float* grad_p, const float* scores, int64_t rows,
@@ -308,8 +310,8 @@ int soft_topk_rows_backward(const float* grad_p, const float* scores, int64_t ro
                             float* grad_s, void* workspace, size_t workspace_bytes,
                             void* stream);
 
-/* Workspace bytes for the batched calls: 0 for rows of at most 8192 scores
- * (none needed) and for invalid sizes (the calls then return EINVAL). */
+/* Workspace bytes for the batched calls: always 0 (none needed; kept so
+ * callers that size a workspace need not special-case the batched calls). */
 size_t soft_topk_rows_workspace_bytes(int64_t rows, int64_t n_row);
 
 /*

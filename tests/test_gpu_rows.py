@@ -4,10 +4,11 @@ the fp64 CPU oracle applied row by row.
 Each row is its own soft top-k problem, so every row is held to the bars of
 the single-vector path: |b - b_ref| <= 1e-5 * alpha, max|p - p_ref| <= 1e-5,
 |sum p - k| <= 1e-3 (oracle mass at the GPU's b), backward rel-L2 <= 1e-4.
-The row lengths cover every shape: lane groups of 1 to 64 lanes per row up
-to 1024 scores (several rows per wave, ragged row counts), one work-group
-per row up to 8192, each with ragged ends and the shape boundaries, and the
-longer rows that run the single-vector path row after row.
+The row lengths cover every shape: the forward's lane groups of 1 to 64
+lanes per row up to 2048 scores (several rows per wave, ragged row counts),
+its work-group per row beyond (in registers up to 8192 scores, streamed
+from memory after), the backward's lane groups and work-groups, each with
+ragged ends and the shape boundaries.
 """
 import numpy as np
 import pytest
@@ -124,16 +125,25 @@ def test_rows_nonfinite_row_gives_nan_and_leaves_others(dev):
         check_rows(s_np[ok], 10.0, 0.1, g_np[ok], p[ok], b[ok], grad[ok])
 
 
-@pytest.mark.parametrize("rows,n_row", [(3, 8193), (2, 20000)])
-def test_long_rows_take_the_single_vector_path(dev, rows, n_row):
+@pytest.mark.parametrize("rows,n_row,k,alpha", [(3, 8193, 200.0, 0.05), (2, 20000, 200.0, 0.05),
+                                                (5, 65537, 3.0, 0.01), (4, 100_000, 50_000.5, 0.1),
+                                                (3, 30_001, 29_990.0, 0.2), (600, 4099, 40.0, 0.05)])
+def test_long_rows_run_batched(dev, rows, n_row, k, alpha):
+    """Rows past the lane groups: one work-group per row, the row in
+    registers up to 8192 scores and streamed from memory beyond (no
+    workspace, no host loop).  k near 0, near n and in the middle (the
+    three first-row starts), a NaN row, and more rows than resident
+    work-groups (later rows start at the previous b)."""
     rng = np.random.default_rng(n_row)
     s_np = rng.standard_normal((rows, n_row)).astype(np.float32)
+    if n_row % 3 == 0:
+        s_np[:, ::7] = np.round(s_np[:, ::7] * 8.0) / 8.0  # some ties
     s_np[-1, 5] = np.nan
     g_np = rng.standard_normal((rows, n_row)).astype(np.float32)
-    k, alpha = 200.0, 0.05
     p, b, grad = run_rows(dev, s_np, k, alpha, g_np)
     assert np.isnan(b[-1]) and np.all(np.isnan(p[-1]))
-    check_rows(s_np[:-1], k, alpha, g_np[:-1], p[:-1], b[:-1], grad[:-1])
+    check = list(range(rows - 1)) if rows <= 8 else list(range(0, rows - 1, 37))
+    check_rows(s_np[check], k, alpha, g_np[check], p[check], b[check], grad[check])
 
 
 def test_rows_equal_single_vector_calls(dev):
