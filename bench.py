@@ -79,11 +79,14 @@ KERNEL_SOURCE = {"pass1": "pass1.hip", "emit": "emit_vjp.hip", "vjp_reduce": "em
 KERNEL_SYMBOLS = {"pass1": ("stk::pass1_kernel",), "emit": ("stk::emit_kernel", "stk::emit_seg_kernel"),
                   "vjp_reduce": ("stk::vjp_reduce_kernel", "stk::vjp_reduce_seg_kernel"),
                   "vjp_apply": ("stk::vjp_apply_kernel", "stk::vjp_apply_seg_kernel")}
-# batched rows: the lane-group kernels (rows up to 1024 scores) and the
-# work-group-per-row kernels (longer rows); algorithmic bytes per score
+# batched rows: the forward's refinement in lane groups (rows up to 2048
+# scores) or by one work-group per row; the backward's lane groups (up to
+# 1024), work-groups (up to 8192) and streamed work-groups; algorithmic
+# bytes per score
 ROWS_ALGO_BYTES = {"rows_forward": 8, "rows_backward": 12}
-ROWS_SYMBOLS = {"rows_forward": ("stk::rows_group_forward_kernel", "stk::rows_forward_kernel"),
-                "rows_backward": ("stk::rows_group_backward_kernel", "stk::rows_backward_kernel")}
+ROWS_SYMBOLS = {"rows_forward": ("stk::rows_refine_kernel", "stk::rows_refine_wg_kernel"),
+                "rows_backward": ("stk::rows_group_backward_kernel", "stk::rows_backward_kernel",
+                                  "stk::rows_backward_wg_kernel")}
 for _k in ROWS_ALGO_BYTES:
     KERNEL_SOURCE[_k] = "rows.hip"
 
