@@ -17,13 +17,13 @@
 //     the previous pass's totals, which digit prefix each target continues
 //     (its own copy of a small scan; work-group 0 records it), then streams
 //     its share of the scores and counts, for each target, the next digit of
-//     the keys that carry the target's prefix, in an LDS histogram.  A wave
-//     merges equal digits before touching LDS (up to four distinct digits
-//     per wave and element slot with one atomic each; the rest one atomic
-//     per lane), so data concentrated on a few digits -- a narrow range, ties
-//     -- costs no atomic contention.  Each work-group writes its histograms
-//     as one row.
-//   fold (dft_fold_kernel) -- the rows are summed column by column.
+//     the keys that carry the target's prefix, in an LDS histogram (one
+//     histogram while the two targets' prefixes agree).  A wave merges the
+//     lanes that share its first lane's digit into one add, so a tied
+//     cluster costs no atomic contention.  Each work-group writes its
+//     histograms as one row.
+//   fold (dft_fold_kernel) -- the rows are summed column by column, in
+//     chunks of rows spread over many work-groups.
 //   finalize (dft_finalize_kernel) -- the last digit completes both keys;
 //     b = (x_(k) + x_(k+1)) / 2 in fp64.
 // A NaN score makes b NaN (and every p NaN); infinities are ordered like
@@ -91,28 +91,23 @@ __device__ void dft_select(const DftState& in, const uint32_t* totals, int P, Df
     }
 }
 
-// One slot's digit counted for the lanes that `match`: while the digit of
-// the first remaining lane is shared by several lanes, those lanes are
-// merged into one LDS atomic (data concentrated on a few digits); once a
-// digit stands nearly alone, the remaining lanes add one each (spread data,
-// whose atomics rarely collide).
+// One slot's digit counted for the lanes that `match`, in one LDS atomic
+// instruction: the lanes that share the first matching lane's digit are
+// merged into that lane's add (a tied cluster or a narrow range costs one
+// add, not a 64-way conflict), every other matching lane adds one.  Merging
+// further digits measured slower on spread data (more instructions per
+// slot, while the spread adds rarely collide).
 __device__ __forceinline__ void agg_count(uint32_t* h, bool match, uint32_t d)
 {
-    uint64_t active = __ballot(match);
-    const int lane = lane_id();
-    for (int it = 0; it < 8 && active != 0ull; ++it) {
-        const int leader = (int)__builtin_ctzll(active);
-        const uint32_t dl = (uint32_t)__shfl((int)d, leader, kWave);
-        const uint64_t same = __ballot(match && d == dl);
-        const uint32_t cnt = (uint32_t)__popcll(same);
-        if (lane == leader)
-            atomicAdd(&h[dl], cnt);
-        active &= ~same;
-        if (cnt < 4u)
-            break;
-    }
-    if ((active >> lane) & 1ull)
-        atomicAdd(&h[d], 1u);
+    const uint64_t active = __ballot(match);
+    if (active == 0ull)
+        return;
+    const int leader = (int)__builtin_ctzll(active);
+    const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
+    const uint64_t same = __ballot(match && d == dl);
+    const bool lead = lane_id() == leader;
+    if (match && (lead || d != dl))
+        atomicAdd(&h[d], lead ? (uint32_t)__popcll(same) : 1u);
 }
 
 template <int P>
@@ -130,7 +125,8 @@ __device__ __forceinline__ void dft_count(float v, const DftState& S, uint32_t (
     } else {
         constexpr int kAbove = P == 1 ? 21 : 10;
         agg_count(h[0], (key >> kAbove) == S.prefix[0], d);
-        agg_count(h[1], (key >> kAbove) == S.prefix[1], d);
+        if (S.prefix[1] != S.prefix[0])  // both targets share one histogram when their prefixes agree
+            agg_count(h[1], (key >> kAbove) == S.prefix[1], d);
     }
 }
 
@@ -158,8 +154,13 @@ __global__ __launch_bounds__(kDT) void dft_hist_kernel(DftArgs a)
         dft_select(a.state[P - 1], a.totals + (size_t)(P - 1) * kDftRowWords, P - 1, &S, lds_sum);
     }
     __syncthreads();
-    if (blockIdx.x == 0 && tid == 0)
-        a.state[P] = S;  // the state before this pass, for the next pass and the finalize
+    if (blockIdx.x == 0) {
+        if (tid == 0)
+            a.state[P] = S;  // the state before this pass, for the next pass and the finalize
+        // this pass's totals, folded by the next kernel
+        for (int i = tid; i < kDftRowWords; i += kDT)
+            a.totals[(size_t)P * kDftRowWords + i] = 0u;
+    }
     const DftState Sr = S;
 
     const int64_t G = gridDim.x;
@@ -203,29 +204,57 @@ __global__ __launch_bounds__(kDT) void dft_hist_kernel(DftArgs a)
             const int above = P == 1 ? 21 : 10;
             const uint32_t d = (key >> dft_shift(P)) & (P == 2 ? 1023u : 2047u);
             agg_count(h[0], in && (key >> above) == Sr.prefix[0], d);
-            agg_count(h[1], in && (key >> above) == Sr.prefix[1], d);
+            if (Sr.prefix[1] != Sr.prefix[0])
+                agg_count(h[1], in && (key >> above) == Sr.prefix[1], d);
         }
     }
     __syncthreads();
     uint32_t* row = a.rows + (size_t)blockIdx.x * kDftRowWords;
     for (int i = tid; i < kDftBins; i += kDT) {
         row[i] = h[0][i];
-        row[kDftBins + i] = P == 0 ? h[0][i] : h[1][i];  // pass 0: both targets share the histogram
+        // pass 0, and a later pass whose two prefixes agree: one histogram
+        row[kDftBins + i] = P == 0 || Sr.prefix[1] == Sr.prefix[0] ? h[0][i] : h[1][i];
     }
     if (tid == 0)
         row[2 * kDftBins] = nan_cnt;
 }
 
-// totals[P][col] = sum over the work-group rows of rows[g][col]
+// totals[P][col] = sum over the work-group rows of rows[g][col].  A
+// work-group takes 64 columns (one per lane) of kFoldRows rows; its waves
+// take every kDW-th row, with all their loads in flight at once, and meet
+// in LDS; one atomic per non-zero column folds the chunk into the totals,
+// which pass P's work-group 0 cleared.
+constexpr int kFoldRows = 8 * kDW;
+static_assert(kDftRowWords % kWave == 0, "fold columns come in whole waves");
+
 __global__ __launch_bounds__(kDT) void dft_fold_kernel(DftArgs a, int P)
 {
-    const int col = blockIdx.x * kDT + threadIdx.x;
-    if (col > 2 * kDftBins)
-        return;
+    __shared__ uint32_t part[kDW][kWave];
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int col = blockIdx.x * kWave + lane;
+    const int g0 = blockIdx.y * kFoldRows;
+    const bool live = col <= 2 * kDftBins;  // the padding columns are never written
+    uint32_t v[kFoldRows / kDW];
+#pragma unroll
+    for (int j = 0; j < kFoldRows / kDW; ++j) {
+        const int g = g0 + j * kDW + wave;
+        v[j] = live && g < a.groups ? a.rows[(size_t)g * kDftRowWords + col] : 0u;
+    }
     uint32_t t = 0u;
-    for (int g = 0; g < a.groups; ++g)
-        t += a.rows[(size_t)g * kDftRowWords + col];
-    a.totals[(size_t)P * kDftRowWords + col] = t;
+#pragma unroll
+    for (int j = 0; j < kFoldRows / kDW; ++j)
+        t += v[j];
+    part[wave][lane] = t;
+    __syncthreads();
+    if (wave == 0) {
+        t = 0u;
+#pragma unroll
+        for (int w = 0; w < kDW; ++w)
+            t += part[w][lane];
+        if (t != 0u)
+            atomicAdd(&a.totals[(size_t)P * kDftRowWords + col], t);
+    }
 }
 
 __global__ __launch_bounds__(kDT) void dft_finalize_kernel(DftArgs a)
@@ -269,7 +298,7 @@ __global__ __launch_bounds__(kStreamThreads) void dft_tail_kernel(const Status* 
 
 hipError_t launch_dftopk_threshold(const DftArgs& a, hipStream_t stream)
 {
-    const dim3 block(kDT), gh(a.groups), gf((2 * kDftBins + 1 + kDT - 1) / kDT);
+    const dim3 block(kDT), gh(a.groups), gf(kDftRowWords / kWave, (a.groups + kFoldRows - 1) / kFoldRows);
     dft_hist_kernel<0><<<gh, block, 0, stream>>>(a);
     dft_fold_kernel<<<gf, block, 0, stream>>>(a, 0);
     dft_hist_kernel<1><<<gh, block, 0, stream>>>(a);
