@@ -24,7 +24,9 @@
 // wave then walks that list 64 at a time: near tail scores get the fp64
 // exponential with every lane busy, band scores are appended with one LDS
 // reservation per wave into a work-group stage, flushed with one global
-// reservation per work-group.  A NaN compares false both ways, so it lands in
+// reservation per work-group (past the stage, in chunks of the global band;
+// once a chunk ends past the buffer, the band has overflowed and the group
+// only counts its band scores).  A NaN compares false both ways, so it lands in
 // the window list and is flagged there; +-inf is caught by max |s|.  Counts
 // are exact; sums are fp64; per-group partials are folded in fixed order by
 // the consumer.
@@ -60,6 +62,8 @@ struct Ctx1 {
     unsigned long long* nB;
     float* stage;                               // LDS [kP1Stage]
     uint32_t* stage_count;                      // LDS reservation counter
+    volatile uint32_t* full;                    // LDS: the group saw the band buffer full
+    uint32_t* over;                             // LDS: band scores only counted since then
     float* win;                                 // this wave's LDS window list [kWin]
 };
 
@@ -103,6 +107,18 @@ __device__ __forceinline__ void drain_window(uint32_t cnt, const Ctx1& x, Acc1& 
         if (mb == 0)
             continue;
         const uint32_t total = (uint32_t)__popcll(mb);
+        if (*x.full != 0u) {
+            // the band has overflowed its buffer: only count (a reservation
+            // per 512 band scores from here on would serialise on the
+            // global counter)
+            if (lane == 0)
+                atomicAdd(x.over, total);
+            if (band && x.open) {
+                acc.bmin = fminf(acc.bmin, s);
+                acc.bmax = fmaxf(acc.bmax, s);
+            }
+            continue;
+        }
         uint32_t sbase = 0;
         if (lane == 0)
             sbase = atomicAdd(x.stage_count, total);
@@ -127,6 +143,10 @@ __device__ __forceinline__ void drain_window(uint32_t cnt, const Ctx1& x, Acc1& 
                 g1 = nb;
                 acc.chunk_next = nb + (n_over - take);
                 acc.chunk_left = (uint32_t)kP1Chunk - (n_over - take);
+                // a chunk that ends past the buffer: the count now exceeds
+                // the capacity, so the band overflows whatever follows
+                if (lane == 0 && nb + (unsigned long long)kP1Chunk > (unsigned long long)x.cap)
+                    *x.full = 1u;
             }
         }
         if (band) {
@@ -217,6 +237,7 @@ __global__ __launch_bounds__(kPass1Threads) void pass1_kernel(Pass1Args a)
     __shared__ float stage_buf[kP1Stage];
     __shared__ float win_buf[kWaves1][kWin];
     __shared__ uint32_t stage_count;
+    __shared__ uint32_t band_full, band_over;
     __shared__ unsigned long long stage_base;
     __shared__ unsigned long long tail_at[kWaves1];
     __shared__ uint32_t tail_n[kWaves1];
@@ -229,8 +250,11 @@ __global__ __launch_bounds__(kPass1Threads) void pass1_kernel(Pass1Args a)
     const int wave = tid / kWave;
     Status* st = a.st;
 
-    if (tid == 0)
+    if (tid == 0) {
         stage_count = 0;
+        band_full = a.count_only != 0 ? 1u : 0u;  // counting only from the start
+        band_over = 0;
+    }
     __syncthreads();
 
     Ctx1 x;
@@ -253,6 +277,8 @@ __global__ __launch_bounds__(kPass1Threads) void pass1_kernel(Pass1Args a)
     x.nB = reinterpret_cast<unsigned long long*>(&st->nB);
     x.stage = stage_buf;
     x.stage_count = &stage_count;
+    x.full = &band_full;
+    x.over = &band_over;
     x.win = win_buf[wave];
 
     Acc1 acc{0.0, 0.0, 0u, 0u, 0u, 0u, INFINITY, -INFINITY, 0.f, 0u, 0ull, 0u};
@@ -324,8 +350,11 @@ __global__ __launch_bounds__(kPass1Threads) void pass1_kernel(Pass1Args a)
     for (int w = 0; w < kWaves1; ++w)
         tails += tail_n[w];
     const uint32_t staged = stage_count < (uint32_t)kP1Stage ? stage_count : (uint32_t)kP1Stage;
-    if (tid == 0)
+    if (tid == 0) {
         stage_base = staged > tails ? atomicAdd(x.nB, (unsigned long long)(staged - tails)) : 0ull;
+        if (band_over != 0u)  // the counted-only band scores keep the band count exact
+            atomicAdd(x.nB, (unsigned long long)band_over);
+    }
     __syncthreads();
     for (uint32_t i = tid; i < staged; i += kPass1Threads) {
         uint64_t g;

@@ -302,6 +302,7 @@ struct Ctx {
     uint64_t seed;
     Mirror* mirror0;   // device address of host mirror slot 0 (solve)
     Mirror* mirror1;   // device address of host mirror slot 1 (mass fold)
+    bool count_only = false;  // this round's pass-1 keeps no band (expected to overflow)
 };
 
 // Two status mirrors per host thread in pinned, fine-grained host memory:
@@ -421,6 +422,7 @@ int enqueue_pass1(const Ctx& x)
     a.cap = x.plan.cap;
     a.partials = at<Pass1Partial>(x, x.plan.off_p1part);
     a.blocks = x.plan.g_pass1;
+    a.count_only = x.count_only ? 1 : 0;
     a.st = x.st;
     STK_HIP(launch_pass1(a, x.stream));
     return SOFT_TOPK_OK;
@@ -527,6 +529,32 @@ void note_chain_passes(int passes)
     g_chain_next = (g_chain_next + 1) % kHintCalls;
 }
 
+// The last (n, k, alpha, band capacity) on this thread whose first
+// bracket's band overflowed its buffer.  A call with the same shape expects the same (a
+// tied cluster at the threshold stays there from batch to batch): its
+// pass-1 only counts the band, since filling a buffer that overflows costs
+// one serialised reservation per 512 band scores, and every score is
+// refined.  The count is exact, so a band that turns out to fit clears the
+// hint for the next call; the result is exact either way.
+struct OverflowHint {
+    int64_t n = 0, cap = 0;
+    double k = 0.0, alpha = 0.0;
+};
+thread_local OverflowHint g_overflow;
+
+bool overflow_expected(int64_t n, int64_t cap, double k, double alpha)
+{
+    return g_overflow.n == n && g_overflow.cap == cap && g_overflow.k == k && g_overflow.alpha == alpha;
+}
+
+void note_overflow(int64_t n, int64_t cap, double k, double alpha, bool overflowed)
+{
+    if (overflowed)
+        g_overflow = OverflowHint{n, cap, k, alpha};
+    else if (overflow_expected(n, cap, k, alpha))
+        g_overflow = OverflowHint{};
+}
+
 // Partition refinement of the band (or of every score when the band
 // overflowed): one work-group, or a chain of `steps` step kernels (resume:
 // from where the last chain stopped, after passes_before passes).
@@ -534,7 +562,7 @@ int enqueue_refine(const Ctx& x, bool one_group, int steps, bool resume, int pas
 {
     IterArgs ia;
     ia.band = at<float>(x, x.plan.off_band);
-    ia.cap = x.plan.cap;
+    ia.cap = x.count_only ? 0 : x.plan.cap;  // no band kept: every score is refined (unless none is in it)
     ia.s = x.s;
     ia.n = x.n;
     ia.p1 = at<Pass1Partial>(x, x.plan.off_p1part);
@@ -1165,6 +1193,11 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
         for (int round = 0; round <= prm.max_widen && !done; ++round) {
             int route = round_route(prm, n, plan.m, rl, rr);
             const bool refine = route == SOFT_TOPK_BAND_REFINE || route == SOFT_TOPK_BAND_REFINE_STEPS;
+            // a first bracket whose band overflowed on the last call of this
+            // shape: count the band only and refine every score
+            x.count_only = refine && round == 0 && overflow_expected(n, plan.cap, k, alpha);
+            if (x.count_only)
+                route = SOFT_TOPK_BAND_REFINE_STEPS;
             int rc = enqueue_round(x, rl, rr, q, route);
             if (rc)
                 return rc;
@@ -1178,6 +1211,9 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
                 rc = settle_refine(x, band_direct(prm, n, plan.m, rl, rr), wait_mass, &h, &route);
                 if (rc)
                     return rc;
+                if (round == 0 && !h.nonfinite)
+                    note_overflow(n, plan.cap, k, alpha, h.nB > (uint64_t)plan.cap);
+                x.count_only = false;  // later rounds keep their bands
             } else if (h.solve_state == kSolveDirectOverflow) {
                 // the band outgrew the whole-band sort: bucket the same band
                 route = SOFT_TOPK_BAND_BUCKETS;

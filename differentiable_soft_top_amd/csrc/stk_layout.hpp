@@ -303,6 +303,7 @@ struct Pass1Args {
     int64_t cap;
     Pass1Partial* partials;
     int32_t blocks;
+    int32_t count_only;           // keep no band: only count it (a band expected to overflow)
     Status* st;
 };
 hipError_t launch_pass1(const Pass1Args& a, hipStream_t stream);

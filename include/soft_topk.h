@@ -63,9 +63,13 @@ extern "C" {
 #define SOFT_TOPK_PATH_FULLSORT 3 /* full device radix sort of all scores   */
 #define SOFT_TOPK_PATH_SINGLE 4   /* n <= 8192: one kernel sorts all scores
                                      in registers and solves them exactly   */
-#define SOFT_TOPK_PATH_ALL_SCORES 5 /* the band overflowed its buffer; the
-                                     partition refinement ran over all n
-                                     scores and ended on the exact root     */
+#define SOFT_TOPK_PATH_ALL_SCORES 5 /* the band overflowed its buffer (or,
+                                     as on the last call on this thread with
+                                     the same n, k, alpha and band capacity,
+                                     it was expected to and was only
+                                     counted); the partition
+                                     refinement ran over all n scores and
+                                     ended on the exact root                */
 
 /* How a bracketed round solved its band (soft_topk_params.band_route,
  * soft_topk_stats.band_route). */
@@ -82,7 +86,8 @@ extern "C" {
 /* Why a bracketed round was rejected (soft_topk_stats.reject_mask bits). */
 #define SOFT_TOPK_REJECT_LOW 1       /* certificate: b lies below a_L        */
 #define SOFT_TOPK_REJECT_HIGH 2      /* certificate: b lies at/above a_R     */
-#define SOFT_TOPK_REJECT_OVERFLOW 4  /* band larger than its capacity        */
+#define SOFT_TOPK_REJECT_OVERFLOW 4  /* band larger than its capacity (or
+                                        expected to be: only counted)       */
 #define SOFT_TOPK_REJECT_BUCKET 8    /* a band bucket too large to sort      */
 #define SOFT_TOPK_REJECT_MASS 16     /* post-solve mass check out of bounds  */
 

@@ -194,6 +194,33 @@ def test_clustered_small(dev):
     assert res["stats"]["reject_mask"] & _lib.REJECT_OVERFLOW
 
 
+def test_overflow_expected_from_the_last_call(dev):
+    """After a call whose band overflowed, the next call with the same n, k,
+    alpha and band capacity only counts its band in pass-1 and refines every
+    score: the same b bit for bit, and the same exact band count.  A vector
+    whose band fits, called with that shape, is still solved exactly (every
+    score refined, the band count exact and within the capacity), and the
+    call after it keeps its band again."""
+    cap = 8000
+    s_a, k, alpha, w = make_workload("c5", n=100_000)  # 60% tied: the band holds them
+    g_np = draw_grad(s_a.size, w.seed)
+    first = run(dev, s_a, k, alpha, g_np, params(band_capacity=cap))
+    second = run(dev, s_a, k, alpha, g_np, params(band_capacity=cap))
+    for res in (first, second):
+        check_full(res, s_a, k, alpha, g_np)
+        assert res["stats"]["path"] == _lib.PATH_ALL_SCORES, res["stats"]
+        assert res["stats"]["n_band"] > cap, res["stats"]
+    assert second["b"] == first["b"] and second["stats"]["n_band"] == first["stats"]["n_band"]
+    s_b = np.random.default_rng(5).standard_normal(s_a.size).astype(np.float32)
+    counted = run(dev, s_b, k, alpha, g_np, params(band_capacity=cap))
+    check_full(counted, s_b, k, alpha, g_np)
+    st = counted["stats"]
+    assert st["path"] == _lib.PATH_ALL_SCORES and 0 < st["n_band"] <= cap, st
+    kept = run(dev, s_b, k, alpha, g_np, params(band_capacity=cap))
+    check_full(kept, s_b, k, alpha, g_np)
+    assert kept["stats"]["path"] == _lib.PATH_BRACKET and kept["stats"]["n_band"] == st["n_band"], kept["stats"]
+
+
 @pytest.mark.parametrize("name,n", [("c1", None), ("c2", 100_003), ("c4", 300_007), ("c3", 65_537)])
 def test_forced_full_sort_matches(dev, name, n):
     s_np, k, alpha, w = make_workload(name, n=n)
