@@ -317,6 +317,22 @@ __device__ __forceinline__ Split load_split(const SplitPartial* p)
     return s;
 }
 
+// This thread's share of a step's partials (work-groups tid, tid +
+// kStepT, ...), in a fixed order.
+__device__ __forceinline__ Split load_splits(const SplitPartial* part, int groups)
+{
+    Split s = split_empty();
+    for (int g = threadIdx.x; g < groups; g += kStepT) {
+        const Split q = load_split(&part[g]);
+        s.A += q.A;
+        s.B += q.B;
+        s.N += q.N;
+        s.lo = fmaxf(s.lo, q.lo);
+        s.hi = fminf(s.hi, q.hi);
+    }
+    return s;
+}
+
 }  // namespace
 
 // Step `step` of a chain of `steps`.  Step 0 sums every work-group's share
@@ -342,8 +358,8 @@ __global__ __launch_bounds__(kStepT) void iter_step_kernel(IterArgs a, int step,
     const uint64_t nB = st->nB;
     const float aL = st->aL, aR = st->aR;
     Split s = split_empty();
-    if (step > 0 && tid < a.groups)
-        s = load_split(&a.part[prev * kIterGroups + tid]);
+    if (step > 0)
+        s = load_splits(&a.part[prev * kIterGroupsAll], a.groups);
     if (done)
         return;
     const bool band = nB <= (uint64_t)a.cap;
@@ -404,7 +420,24 @@ __global__ __launch_bounds__(kStepT) void iter_step_kernel(IterArgs a, int step,
         const bool vec = (reinterpret_cast<uintptr_t>(a.s) & 15u) == 0;
         const int64_t n4 = vec ? a.n / 4 : 0;
         const float4* s4 = reinterpret_cast<const float4*>(a.s);
-        for (int64_t i = i0; i < n4; i += stride) {
+        // four loads in flight per lane (one work-group per CU leaves little
+        // else to hide their latency), then their sixteen terms
+        constexpr int kQ = 4;
+        int64_t i = i0;
+        for (; i + (kQ - 1) * stride < n4; i += kQ * stride) {
+            float4 q[kQ];
+#pragma unroll
+            for (int u = 0; u < kQ; ++u)
+                q[u] = s4[i + u * stride];
+#pragma unroll
+            for (int u = 0; u < kQ; ++u) {
+                split_add(s, q[u].x, r, c);
+                split_add(s, q[u].y, r, c);
+                split_add(s, q[u].z, r, c);
+                split_add(s, q[u].w, r, c);
+            }
+        }
+        for (; i < n4; i += stride) {
             const float4 q = s4[i];
             split_add(s, q.x, r, c);
             split_add(s, q.y, r, c);
@@ -422,7 +455,7 @@ __global__ __launch_bounds__(kStepT) void iter_step_kernel(IterArgs a, int step,
         q.N = s.N;
         q.lo = s.lo;
         q.hi = s.hi;
-        a.part[cur * kIterGroups + blockIdx.x] = q;
+        a.part[cur * kIterGroupsAll + blockIdx.x] = q;
     }
 }
 
@@ -441,9 +474,7 @@ __global__ __launch_bounds__(kStepT) void iter_final_kernel(IterArgs a, int step
         const int last = (steps - 1) & 1;
         const uint64_t nB = st->nB;
         const bool band = nB <= (uint64_t)a.cap;
-        Split s = split_empty();
-        if (tid < a.groups)
-            s = load_split(&a.part[last * kIterGroups + tid]);
+        Split s = load_splits(&a.part[last * kIterGroupsAll], a.groups);
         const Tails tl{st->SL, st->SR, st->nL, st->nR};
         s = block_split<kStepT>(s, L);
         StepOut o = refine_step(is->x[last], s, tl, band, st->aL, st->aR, a.k, a.alpha, a.log2e_over_alpha);

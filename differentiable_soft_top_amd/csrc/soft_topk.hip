@@ -569,7 +569,7 @@ int enqueue_refine(const Ctx& x, bool one_group, int steps, bool resume, int pas
     ia.p1_blocks = x.plan.g_pass1;
     ia.is = at<IterState>(x, x.plan.off_iter);
     ia.part = at<SplitPartial>(x, x.plan.off_iter + align_up(sizeof(IterState)));
-    ia.groups = kIterGroups;
+    ia.groups = x.count_only ? kIterGroupsAll : kIterGroups;  // every score refined: a wider grid
     ia.passes_before = passes_before;
     ia.k = x.k;
     ia.alpha = x.alpha;
@@ -939,7 +939,7 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     p.off_emitpart = o;
     o = align_up(o + sizeof(double) * (size_t)p.g_emit);
     p.off_iter = o;
-    o = align_up(o + align_up(sizeof(IterState)) + sizeof(SplitPartial) * 2 * (size_t)kIterGroups);
+    o = align_up(o + align_up(sizeof(IterState)) + sizeof(SplitPartial) * 2 * (size_t)kIterGroupsAll);
     p.off_keys0 = o;
     o = align_up(o + sizeof(uint32_t) * (size_t)n);
     p.off_keys1 = o;

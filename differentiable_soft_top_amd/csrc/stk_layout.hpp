@@ -87,6 +87,7 @@ constexpr int kIterOneMax = 16;
 constexpr double kIterOnePredictMax = 10240.0;
 constexpr int kIterThreads = 256;
 constexpr int kIterGroups = 256;
+constexpr int kIterGroupsAll = 1024;     // step grid known to refine every score (4 waves per SIMD for its fp64 terms)
 constexpr int kIterStepsMin = 2;         // step kernels of a chain: the recent calls' passes, within these
 constexpr int kIterStepsMax = 8;
 constexpr int kIterPassesMax = 16;       // passes over all chains of one round before the band is sorted
@@ -375,8 +376,8 @@ struct IterArgs {
     const Pass1Partial* p1;       // pass-1 partials (tails, band range, finiteness)
     int32_t p1_blocks;
     IterState* is;                // step kernels' state
-    SplitPartial* part;           // [2][kIterGroups] sums of alternate steps
-    int32_t groups;               // work-groups of a step (<= kIterGroups)
+    SplitPartial* part;           // [2][kIterGroupsAll] sums of alternate steps
+    int32_t groups;               // work-groups of a step (kIterGroups, or kIterGroupsAll)
     int32_t passes_before;        // passes of earlier chains of this round (resumed)
     double k;
     double alpha;

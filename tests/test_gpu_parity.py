@@ -197,7 +197,8 @@ def test_clustered_small(dev):
 def test_overflow_expected_from_the_last_call(dev):
     """After a call whose band overflowed, the next call with the same n, k,
     alpha and band capacity only counts its band in pass-1 and refines every
-    score: the same b bit for bit, and the same exact band count.  A vector
+    score, on a wider grid (so its sums round in another order): the same b
+    to 1e-9 alpha, and the same exact band count.  A vector
     whose band fits, called with that shape, is still solved exactly (every
     score refined, the band count exact and within the capacity), and the
     call after it keeps its band again."""
@@ -210,7 +211,7 @@ def test_overflow_expected_from_the_last_call(dev):
         check_full(res, s_a, k, alpha, g_np)
         assert res["stats"]["path"] == _lib.PATH_ALL_SCORES, res["stats"]
         assert res["stats"]["n_band"] > cap, res["stats"]
-    assert second["b"] == first["b"] and second["stats"]["n_band"] == first["stats"]["n_band"]
+    assert abs(second["b"] - first["b"]) <= 1e-9 * alpha and second["stats"]["n_band"] == first["stats"]["n_band"]
     s_b = np.random.default_rng(5).standard_normal(s_a.size).astype(np.float32)
     counted = run(dev, s_b, k, alpha, g_np, params(band_capacity=cap))
     check_full(counted, s_b, k, alpha, g_np)
