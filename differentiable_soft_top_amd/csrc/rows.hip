@@ -28,6 +28,8 @@
 //     by a block max and its owner applies the closed-form root (fp64).
 //     p = F((s - b)/alpha) is then emitted from the registers still holding
 //     the row in load order: s - b in fp64, the exponential in fp32.
+#include <type_traits>
+
 #include "stk_common.hpp"
 #include "stk_layout.hpp"
 #include "stk_prof.hpp"
@@ -1131,18 +1133,31 @@ rows_refine_kernel(RowsArgs a)
             float Af[2] = {0.0f, 0.0f}, Bf[2] = {0.0f, 0.0f};
             uint32_t N = 0;
             float lo = -INFINITY, hi = INFINITY;
+            // one pass's terms; kGap: each side measured from its nearest
+            // score (a re-sum), else both from rf (the common case, one
+            // select less per score)
+            auto terms = [&](auto kGap) {
 #pragma unroll
-            for (int q = 0; q < R; ++q) {
-                if (in_[q]) {
-                    const bool up = v[q] > rf;
-                    const float e = __builtin_amdgcn_exp2f(-fabsf(v[q] - (up ? ref_hi : ref_lo)) * cf);
-                    Af[q & 1] += up ? e : 0.0f;
-                    Bf[q & 1] += up ? 0.0f : e;
-                    N += up ? 1u : 0u;
-                    hi = up ? fminf(hi, v[q]) : hi;
-                    lo = up ? lo : fmaxf(lo, v[q]);
+                for (int q = 0; q < R; ++q) {
+                    if (in_[q]) {
+                        const bool up = v[q] > rf;
+                        const float ref = decltype(kGap)::value ? (up ? ref_hi : ref_lo) : rf;
+                        const float e = __builtin_amdgcn_exp2f(-fabsf(v[q] - ref) * cf);
+                        Af[q & 1] += up ? e : 0.0f;
+                        Bf[q & 1] += up ? 0.0f : e;
+                        N += up ? 1u : 0u;
+                        // nearest scores by compare and select: fminf /
+                        // fmaxf would first quieten both operands (two more
+                        // instructions each); the scores are finite here
+                        hi = up && v[q] < hi ? v[q] : hi;
+                        lo = !up && v[q] > lo ? v[q] : lo;
+                    }
                 }
-            }
+            };
+            if (gap)
+                terms(std::true_type{});
+            else
+                terms(std::false_type{});
             const float la = Af[0] + Af[1], lb = Bf[0] + Bf[1];
             N = group_sum_u32<G>(N);
             lo = group_maxf<G>(lo);
@@ -1416,15 +1431,22 @@ __global__ __launch_bounds__(kWgT) void rows_refine_wg_kernel(RowsArgs a)
             float Af = 0.0f, Bf = 0.0f;
             uint32_t N = 0;
             float lo = -INFINITY, hi = INFINITY;
-            sweep([&](float x) {
+            // kGap: each side measured from its nearest score (a re-sum),
+            // else both from rf
+            auto term = [&](float x, auto kGap) {
                 const bool up = x > rf;
-                const float e = __builtin_amdgcn_exp2f(-fabsf(x - (up ? ref_hi : ref_lo)) * cf);
+                const float ref = decltype(kGap)::value ? (up ? ref_hi : ref_lo) : rf;
+                const float e = __builtin_amdgcn_exp2f(-fabsf(x - ref) * cf);
                 Af += up ? e : 0.0f;
                 Bf += up ? 0.0f : e;
                 N += up ? 1u : 0u;
-                hi = up ? fminf(hi, x) : hi;
-                lo = up ? lo : fmaxf(lo, x);
-            });
+                hi = up && x < hi ? x : hi;  // compare and select (finite scores)
+                lo = !up && x > lo ? x : lo;
+            };
+            if (gap)
+                sweep([&](float x) { term(x, std::true_type{}); });
+            else
+                sweep([&](float x) { term(x, std::false_type{}); });
             const float la = Af, lb = Bf;
             float ga = la, gb = lb;
             wg_pass_totals(ga, gb, N, lo, hi, L);
