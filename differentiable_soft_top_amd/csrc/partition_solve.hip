@@ -92,8 +92,10 @@ __device__ __forceinline__ void split_add(Split& a, float v, double r, double c)
     a.A += up ? e : 0.0;
     a.B += up ? 0.0 : e;
     a.N += up ? 1ull : 0ull;
-    a.hi = up ? fminf(a.hi, v) : a.hi;
-    a.lo = up ? a.lo : fmaxf(a.lo, v);
+    // compare and select: fminf / fmaxf would quieten both operands first
+    // (a NaN score fails both compares; pass-1 has flagged it already)
+    a.hi = up && v < a.hi ? v : a.hi;
+    a.lo = !up && v > a.lo ? v : a.lo;
 }
 
 template <int kThreads>
