@@ -7,16 +7,25 @@
 // row) gets b_r with sum_i F((s_ri - b_r)/alpha) = k, p_ri = F((s_ri -
 // b_r)/alpha), and the VJP of each row as in the single-vector path.
 //
-// gfx950 design: rows up to 1024 scores are held by lane groups, several
-// rows per wave (below); longer rows by one work-group each; the row is
-// held in registers either way.
-//   forward -- the row is loaded coalesced (R scores per thread), copied as
-//     order-preserving keys and sorted by a bitonic network in its
-//     direction-free form (the sorted keys end in blocked order: thread t
-//     holds positions t*R .. t*R+R-1).  The full-sort solver of section 2.2 then needs, at every
-//     breakpoint x_j, the left sum A_j = sum_{i<=j} e^{(x_i-x_j)/alpha} and
-//     the right sum sum_{i>j} e^{(x_j-x_i)/alpha}.  When the row spans at
-//     most kRowSpan in log2 units ((x_max - x_min) log2(e)/alpha), every
+// gfx950 design.  Three families of kernels, every one holding a row (or
+// its share of one) in registers:
+//   batched forward -- partition refinement, no sort (rows_refine_kernel:
+//     lane groups of G lanes, several rows per wave, up to 2048 scores;
+//     rows_refine_wg_kernel: one work-group per row beyond, in registers up
+//     to 8192 scores and streamed after).  The row's split sums at a point
+//     r give the closed-form root of the model that puts every score on its
+//     side of r; the step repeats from that root until no score lies
+//     between the point and its root, which is then the exact root.
+//   sorted solve -- the one-kernel route of a single vector of at most
+//     8192 scores (rows_group_forward_kernel up to 1024 scores,
+//     rows_forward_kernel beyond): the row is loaded coalesced (R scores
+//     per thread), copied as order-preserving keys and sorted by a bitonic
+//     network in its direction-free form (the sorted keys end in blocked
+//     order: thread t holds positions t*R .. t*R+R-1).  The full-sort solver
+//     of section 2.2 then needs, at every breakpoint x_j, the left sum
+//     A_j = sum_{i<=j} e^{(x_i-x_j)/alpha} and the right sum
+//     sum_{i>j} e^{(x_j-x_i)/alpha}.  When the row spans at most kRowSpan
+//     in log2 units ((x_max - x_min) log2(e)/alpha), every
 //     E_i = e^{(x_i-x_r)/alpha} about the row's midpoint x_r and its
 //     reciprocal are normal fp64 numbers, so both sums are plain prefix and
 //     suffix sums of E and 1/E scaled by 1/E_j and E_j: one exponential per
@@ -26,8 +35,12 @@
 //     anchored sums of the single-vector segment solve (an exponential per
 //     combination, any range).  The last breakpoint with mass >= k is found
 //     by a block max and its owner applies the closed-form root (fp64).
-//     p = F((s - b)/alpha) is then emitted from the registers still holding
-//     the row in load order: s - b in fp64, the exponential in fp32.
+//   backward -- each row's D and G, then its gradient (lane groups up to
+//     1024 scores, one work-group per row up to 8192, a streamed work-group
+//     beyond).
+// p = F((s - b)/alpha) is emitted from the registers still holding the row
+// in load order: s - b measured in fp64 (or from the fp32 split of b), the
+// exponential in fp32.
 #include <type_traits>
 
 #include "stk_common.hpp"
