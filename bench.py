@@ -3,9 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
 
 A step is one whole pass of the hot path over one synthetic score vector
-already resident in HBM: sample, bracket, streaming pass, band sort, segment
-solve with certificate, p emission with the fp64 mass check (forward), then
-the two VJP kernels (backward).  Steps alternate between two input batches
+already resident in HBM: sample, bracket, streaming pass, the band's
+partition refinement (whose steps certify the bracket), p emission with its
+fp64 mass partials (forward), then the two VJP kernels (backward).  Steps alternate between two input batches
 (the second is the first reversed, in its own memory) so that no step starts
 on data the previous one left in the caches.  Prints one JSON line.
 

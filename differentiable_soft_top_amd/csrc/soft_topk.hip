@@ -2,15 +2,19 @@
 //
 // Route of one forward call (aiqbench.com abstract of Fast LapSum;
 // gist.science summary, section 2.2, "Probabilistic Bracketing" steps 1-4):
-//   sample -> select bracket -> pass-1 (tails + band) -> band sort ->
-//   segment solve with the bracket certificate -> emit p with the fp64 mass
-//   check -> one status read-back.
-// A rejected certificate widens the bracket on the failing side (the other
-// end becomes the rejected end, which is then a proven bound) and reruns
-// pass-1; an overfull band, an unsortable bucket, a failed mass check or
-// exhausted widenings take the full device radix sort, whose solve needs no
-// bracket.  The host only chooses among these routes; every step of the
-// arithmetic runs in the kernels.
+//   sample -> select bracket -> pass-1 (tails + band) -> the band's
+//   partition refinement (one work-group, or a chain of step kernels),
+//   whose steps certify the bracket -> emit p with its fp64 mass partials
+//   (folded and checked on request) -> one status read-back.
+// Vectors of at most 8192 scores take one kernel instead (a sort and the
+// full-sort solve in one work-group).  A rejected bracket widens on the
+// failing side (the other end becomes the rejected end, which is then a
+// proven bound) and reruns pass-1; an overfull band is refined over every
+// score; a refinement that does not end sorts the band (the sorted routes,
+// also forced by the parameters); an overfull sorted band splits off a tied
+// cluster; a failed mass check or exhausted widenings take the full device
+// radix sort, whose solve needs no bracket.  The host only chooses among
+// these routes; every step of the arithmetic runs in the kernels.
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
