@@ -185,11 +185,12 @@ size_t soft_topk_backward_workspace_bytes(int64_t n);
  * Route: up to 8192 scores (by default) one kernel sorts the whole vector in
  * registers and solves it with the full-sort solver of the gist.science
  * summary of Fast LapSum (section 2.2), exactly, with no bracket to certify;
- * larger n take the bracketed route (sample, streaming pass, band sort,
- * certified segment solve) with the full sort as its fallback.
+ * larger n take the bracketed route (sample, streaming pass, the band's
+ * partition refinement, whose steps certify the bracket; the sorted band
+ * routes and the full sort as fallbacks).
  * Synchronisation: enqueues on `stream` and waits (a 256-byte status
- * read-back) until the segment solve has certified the bracket (or the
- * one-kernel solve has ended), so that the route is settled on return.  b is final in device memory at that point; the
+ * read-back) until the solve has certified the bracket (or the one-kernel
+ * solve has ended), so that the route is settled on return.  b is final in device memory at that point; the
  * emission of p is already enqueued behind it and completes in stream order,
  * so any later work on `stream` sees the final p.  With
  * params->verify_mass = 1 or a stats record, the fp64 mass sum of p is also
