@@ -1202,6 +1202,7 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
             x.count_only = refine && round == 0 && overflow_expected(n, plan.cap, k, alpha);
             if (x.count_only)
                 route = SOFT_TOPK_BAND_REFINE_STEPS;
+            const bool counted_only = x.count_only;  // this round's band buffer holds nothing
             int rc = enqueue_round(x, rl, rr, q, route);
             if (rc)
                 return rc;
@@ -1287,9 +1288,11 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
                 sx.reject_mask |= SOFT_TOPK_REJECT_OVERFLOW;
             else if (h.solve_state == kSolveBucketOverflow)
                 sx.reject_mask |= SOFT_TOPK_REJECT_BUCKET;
-            if ((h.solve_state == kSolveOverflow || h.solve_state == kSolveBucketOverflow) && round < prm.max_widen) {
+            if ((h.solve_state == kSolveOverflow || h.solve_state == kSolveBucketOverflow) && round < prm.max_widen &&
+                !counted_only) {
                 // widening cannot shrink the band; a tied cluster in it can be
-                // split off into a tail
+                // split off into a tail (found in the band buffer, which a
+                // counted-only round left unwritten: the full sort decides)
                 rc = tie_split(x, h, prm.max_widen - round, wait_mass, tol, &sx, &h, &done);
                 if (rc)
                     return rc;
