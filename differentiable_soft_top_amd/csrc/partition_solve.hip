@@ -167,7 +167,11 @@ __device__ __forceinline__ StepOut refine_step(double r, const Split& s, const T
         N += (double)t.nR;
     }
     const double d = k - N;
-    const double disc = sqrt(d * d + A * B);
+    // with d = 0 the discriminant is sqrt(A) sqrt(B): the product A B leaves
+    // the normal fp64 range when both sums are small (the split hundreds of
+    // alpha from the scores on both sides, b between them); any other d is
+    // at least an ulp of k, whose square dwarfs such a product
+    const double disc = d != 0.0 ? sqrt(d * d + A * B) : sqrt(A) * sqrt(B);
     const double u = d > 0.0 ? B / (d + disc) : (disc - d) / A;
     StepOut o;
     o.b = r + alpha * log(u);

@@ -1005,10 +1005,14 @@ __device__ __forceinline__ float group_sumf(float v)
 }
 
 // The positive root u of (A/2) u^2 + d u - B/2 = 0 in its cancellation-free
-// form, in fp32 (a few ulps).
+// form, in fp32 (a few ulps).  With d = 0 (k a whole number equal to the
+// count above the split) the discriminant is sqrt(A) sqrt(B): the product
+// A B would leave the normal fp32 range when both sums are small (two scores
+// tens of alpha from the split, b between them).  Any other d is at least
+// an ulp of k, whose square dwarfs such a product.
 __device__ __forceinline__ float row_root_u(float d, float A, float B)
 {
-    const float disc = sqrtf(d * d + A * B);
+    const float disc = d != 0.0f ? sqrtf(d * d + A * B) : sqrtf(A) * sqrtf(B);
     return d > 0.0f ? B / (d + disc) : (disc - d) / A;
 }
 
@@ -1033,6 +1037,26 @@ __device__ __forceinline__ uint32_t group_sum_u32(uint32_t v)
 
 constexpr float kRowIterTol = 0x1p-30f;  // convergence slack, in units of alpha
 constexpr float kRowSumMin = 0x1p-100f;  // smallest sum taken as exact (normal, 2^26 above the fp32 minimum)
+// Passes of model steps before a long row's split point bisects instead
+// (the work-group form, rows over 2048 scores).  A model step crosses the
+// scores between its split and the root only as far as their terms let it:
+// with alpha far below the spacing of the scores it crosses about one per
+// pass, so a start many scores away from b would take as many passes, each
+// a sweep of the row.  Every step also bounds b from one side (the step moves
+// toward b), so the row keeps a bracket of fp32 keys; bisecting it (from
+// the finite floats, cut by the last step) isolates the gap that holds b in
+// at most 33 more passes (each perhaps followed by a re-sum), where the
+// closed form ends.
+// A row of at most kRowMaxPasses - 8 scores ends within n + 8 model steps
+// and does not bisect.
+constexpr int kRowModelPasses = 8;
+constexpr int kRowMaxPasses = kRowModelPasses + 2 * 34;
+
+// The fp32 split point halfway, in key order, between two keys.
+__device__ __forceinline__ double key_midpoint(uint32_t kl, uint32_t kh)
+{
+    return (double)key_to_float(kl + (kh - kl) / 2u);
+}
 
 }  // namespace
 
@@ -1072,7 +1096,9 @@ rows_refine_kernel(RowsArgs a)
     const double tol = (double)kRowIterTol * a.alpha;
     const float cf = (float)c;
     const int64_t stride = (int64_t)gridDim.x * (kGroupThreads / G);
-    const int max_passes = n + 8;  // each pass that does not end crosses a score
+    // each pass that does not end crosses a score (n <= 2048 here: a bounded
+    // worst case; the work-group form bisects instead for longer rows)
+    const int max_passes = n + 8;
     // rank, among the G lane maxima, that estimates b on a first row: a lane
     // holds a score above b with probability about 1 - e^{-k/G}
     const int jmax = (int)fmin((double)G, fmax(1.0, rint((double)G * (1.0 - exp(-k / (double)G)))));
@@ -1344,7 +1370,10 @@ __global__ __launch_bounds__(kWgT) void rows_refine_wg_kernel(RowsArgs a)
     // slot q of this thread: float4 q / 4 at (q / 4) * kWgT + tid, or the
     // single score q * kWgT + tid
     auto pos = [&](int q) -> int { return vec ? 4 * ((q / 4) * kWgT + tid) + (q & 3) : q * kWgT + tid; };
-    const int max_passes = n + 8;
+    // each model step that does not end crosses a score; past that bound,
+    // bisection bounds the rest
+    const bool may_bisect = n + 8 > kRowMaxPasses;
+    const int max_passes = may_bisect ? kRowMaxPasses : n + 8;
     const double kw = k / (double)(kWgT / kWave);  // scores above b per wave's quarter
     const int jw = (int)fmin((double)kWave, fmax(1.0, rint((double)kWave * (1.0 - exp(-kw / (double)kWave)))));
     const double nkw = ((double)n - k) / (double)(kWgT / kWave);
@@ -1437,6 +1466,8 @@ __global__ __launch_bounds__(kWgT) void rows_refine_wg_kernel(RowsArgs a)
         double b = NAN;
         bool gap = false;
         float rf = 0.0f, glo = 0.0f, ghi = 0.0f;
+        uint32_t kl = 0u, kh = 0xFFFFFFFFu;  // once bisecting: b lies in (key kl, key kh]
+        bool bisect = false;
         for (int pass = 0; pass < max_passes && !bad; ++pass) {
             if (!gap)
                 rf = __double2float_rd(r);
@@ -1491,7 +1522,24 @@ __global__ __launch_bounds__(kWgT) void rows_refine_wg_kernel(RowsArgs a)
                 b = bn;
                 break;
             }
-            r = bn;
+            if (!may_bisect || pass + 1 < kRowModelPasses) {
+                r = bn;
+                continue;
+            }
+            if (!bisect) {
+                // from here on the split bisects a bracket of b: the finite
+                // floats, cut by the last model step (the steps all move one
+                // way, toward b)
+                kl = float_to_key(-0x1.fffffep127f);
+                kh = float_to_key(0x1.fffffep127f);
+                bisect = true;
+            }
+            // the step went toward b: b lies above r, or at most r
+            if (bn > r)
+                kl = max(kl, float_to_key(rf));
+            else
+                kh = min(kh, float_to_key(__double2float_ru(r)));
+            r = kh > kl + 1u ? key_midpoint(kl, kh) : (double)key_to_float(kl);
         }
         if (bad)
             b = NAN;

@@ -276,6 +276,20 @@ def test_tied_cluster_splits_the_bracket(dev, where, alpha):
     assert abs(refined["b"] - full["b"]) <= 2e-5 * alpha
 
 
+@pytest.mark.parametrize("k", [5000.0, 5000.25, 4000.0])
+def test_root_in_a_wide_gap(dev, k):
+    """Scores 0.74 apart with alpha = 1e-3: b lies in a gap of 740 alpha, so at
+    a split near its middle both sums are about e^-370 and their product
+    leaves the normal fp64 range; the steps form the discriminant without
+    it.  k = 5000 puts b exactly in the middle of a gap (d = 0 there)."""
+    n = 10_000
+    s_np = (np.random.default_rng(17).permutation(n) * 0.74).astype(np.float32)
+    g_np = np.random.default_rng(18).standard_normal(n).astype(np.float32)
+    for route in (0, _lib.BAND_REFINE_STEPS):
+        res = run(dev, s_np, k, 1e-3, g_np, params(band_route=route))
+        check_full(res, s_np, k, 1e-3, g_np)
+
+
 def test_route_independence(dev):
     """Different Philox seeds, a too-narrow bracket (forcing rejections and
     widening), an overfull band and the forced full sort all give the same b."""

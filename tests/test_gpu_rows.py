@@ -146,6 +146,22 @@ def test_long_rows_run_batched(dev, rows, n_row, k, alpha):
     check_rows(s_np[check], k, alpha, g_np[check], p[check], b[check], grad[check])
 
 
+@pytest.mark.parametrize("n_row", [1000, 2000, 6000, 20_000])
+def test_rows_of_evenly_spaced_scores_at_small_alpha(dev, n_row):
+    """Rows of the integers 0..n-1 (shuffled) with alpha a hundredth of their
+    spacing: a model step then crosses about one score per pass, and the
+    starts (the row mean or a normal quantile) lie hundreds of scores from b
+    for k away from the middle.  The rows bisect their bracket after a few
+    passes, so they end after a bounded number, on the oracle's b."""
+    rng = np.random.default_rng(n_row)
+    rows = 4
+    s_np = np.stack([rng.permutation(n_row) for _ in range(rows)]).astype(np.float32)
+    g_np = rng.standard_normal(s_np.shape).astype(np.float32)
+    for k in (0.1 * n_row + 0.25, 0.5 * n_row, 0.85 * n_row - 0.5):
+        p, b, grad = run_rows(dev, s_np, k, 0.01, g_np)
+        check_rows(s_np, k, 0.01, g_np, p, b, grad)
+
+
 def test_rows_equal_single_vector_calls(dev):
     """A batch of rows gives each row what the single-vector operator gives
     it (to the parity bar: the two solve with different sorts and scans)."""
