@@ -290,6 +290,20 @@ def test_root_in_a_wide_gap(dev, k):
         check_full(res, s_np, k, 1e-3, g_np)
 
 
+@pytest.mark.parametrize("k", [2000.25, 10_000.0, 17_000.5])
+def test_evenly_spaced_scores_at_small_alpha(dev, k):
+    """A vector of the integers 0..19999 (shuffled) with alpha a hundredth of
+    their spacing: the band's model steps cross about one score per pass, so
+    a refinement that starts far from b may not end within its passes and
+    the band is sorted instead.  Every route gives the oracle's b."""
+    n, alpha = 20_000, 0.01
+    s_np = np.random.default_rng(23).permutation(n).astype(np.float32)
+    g_np = np.random.default_rng(24).standard_normal(n).astype(np.float32)
+    for route in (0, _lib.BAND_REFINE_STEPS, _lib.BAND_BUCKETS):
+        res = run(dev, s_np, k, alpha, g_np, params(band_route=route))
+        check_full(res, s_np, k, alpha, g_np)
+
+
 def test_route_independence(dev):
     """Different Philox seeds, a too-narrow bracket (forcing rejections and
     widening), an overfull band and the forced full sort all give the same b."""
