@@ -118,23 +118,46 @@ class Runner:
         from differentiable_soft_top_amd import _lib
         self._lib = _lib
         self.stats = _lib.Stats()
+        self._calls = self._calls_stats = None
+
+    def _args(self, stats):
+        """The two calls' arguments for each batch, marshalled once (the
+        buffers never move), as a C or C++ caller would hold them: the step
+        then times the library rather than Python's argument handling."""
+        v = ctypes.c_void_p
+        prm = ctypes.byref(self.params) if self.params is not None else None
+        st = ctypes.byref(self.stats) if stats else None
+        out = []
+        for s, g in self.batches:
+            fwd = (v(s.data_ptr()), self.n, ctypes.c_double(self.k), ctypes.c_double(self.alpha), v(self.p.data_ptr()),
+                   v(self.b.data_ptr()), v(self.ws.data_ptr()), self.ws_bytes, self.stream, prm, st)
+            bwd = (v(g.data_ptr()), v(s.data_ptr()), self.n, ctypes.c_double(self.alpha), v(self.b.data_ptr()),
+                   v(self.grad.data_ptr()), v(self.ws.data_ptr()), self.ws_bytes, v(self.bws.data_ptr()),
+                   self.bws_bytes, self.stream)
+            out.append((fwd, bwd))
+        return out
 
     def step(self, stats=False):
         """Forward + backward; with stats=True the forward also waits for the
         certification pass and fills self.stats (not used in timed steps).
         self.params (None: the library defaults) goes to every forward."""
-        L, v = self.lib, ctypes.c_void_p
+        calls = self._calls_stats if stats else self._calls
+        if calls is None:
+            calls = self._args(stats)
+            if stats:
+                self._calls_stats = calls
+            else:
+                self._calls = calls
+        fwd, bwd = calls[self.turn]
         self.s, self.g = self.batches[self.turn]
         self.turn ^= 1
-        rc = L.soft_topk_forward_ex(v(self.s.data_ptr()), self.n, self.k, self.alpha, v(self.p.data_ptr()),
-                                    v(self.b.data_ptr()), v(self.ws.data_ptr()), self.ws_bytes, self.stream,
-                                    ctypes.byref(self.params) if self.params is not None else None,
-                                    ctypes.byref(self.stats) if stats else None)
-        self._lib.check(rc, "soft_topk_forward")
-        rc = L.soft_topk_backward_ex(v(self.g.data_ptr()), v(self.s.data_ptr()), self.n, self.alpha,
-                                     v(self.b.data_ptr()), v(self.grad.data_ptr()), v(self.ws.data_ptr()),
-                                     self.ws_bytes, v(self.bws.data_ptr()), self.bws_bytes, self.stream)
-        self._lib.check(rc, "soft_topk_backward")
+        L = self.lib
+        rc = L.soft_topk_forward_ex(*fwd)
+        if rc:
+            self._lib.check(rc, "soft_topk_forward")
+        rc = L.soft_topk_backward_ex(*bwd)
+        if rc:
+            self._lib.check(rc, "soft_topk_backward")
 
 
 class RowsRunner:
@@ -157,19 +180,27 @@ class RowsRunner:
         self.stream = ctypes.c_void_p(torch.cuda.current_stream(s2d.device).cuda_stream)
         from differentiable_soft_top_amd import _lib
         self._lib = _lib
+        self._calls = None
 
     def step(self):
-        L, v = self.lib, ctypes.c_void_p
-        s, g = self.batches[self.turn]
+        if self._calls is None:
+            # marshalled once per batch (the buffers never move)
+            v, d = ctypes.c_void_p, ctypes.c_double
+            self._calls = [((v(s.data_ptr()), self.rows, self.n_row, d(self.k), d(self.alpha), v(self.p.data_ptr()),
+                             v(self.b.data_ptr()), v(self.ws.data_ptr()), self.ws_bytes, self.stream),
+                            (v(g.data_ptr()), v(s.data_ptr()), self.rows, self.n_row, d(self.alpha),
+                             v(self.b.data_ptr()), v(self.grad.data_ptr()), v(self.ws.data_ptr()), self.ws_bytes,
+                             self.stream))
+                           for s, g in self.batches]
+        fwd, bwd = self._calls[self.turn]
         self.turn ^= 1
-        rc = L.soft_topk_rows_forward(v(s.data_ptr()), self.rows, self.n_row, self.k, self.alpha,
-                                      v(self.p.data_ptr()), v(self.b.data_ptr()), v(self.ws.data_ptr()),
-                                      self.ws_bytes, self.stream)
-        self._lib.check(rc, "soft_topk_rows_forward")
-        rc = L.soft_topk_rows_backward(v(g.data_ptr()), v(s.data_ptr()), self.rows, self.n_row, self.alpha,
-                                       v(self.b.data_ptr()), v(self.grad.data_ptr()), v(self.ws.data_ptr()),
-                                       self.ws_bytes, self.stream)
-        self._lib.check(rc, "soft_topk_rows_backward")
+        L = self.lib
+        rc = L.soft_topk_rows_forward(*fwd)
+        if rc:
+            self._lib.check(rc, "soft_topk_rows_forward")
+        rc = L.soft_topk_rows_backward(*bwd)
+        if rc:
+            self._lib.check(rc, "soft_topk_rows_backward")
 
 
 def time_steps(torch, runner, steps, flush=None):
