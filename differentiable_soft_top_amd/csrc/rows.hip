@@ -372,6 +372,37 @@ __device__ __forceinline__ void solve_anchored(const float (&x)[R], int e0, int 
     }
 }
 
+// The single-vector route: the work-group's fp64 mass of p, then the
+// status block (zeroed, then b, the mass, and the solve's outcome: a
+// non-finite score shows as b = NaN) and its publication to the host.
+template <int kT>
+__device__ __forceinline__ void single_publish(const RowsArgs& a, double m, double b)
+{
+    constexpr int kW = kT / kWave;
+    constexpr int kWords = (int)(sizeof(Status) / 4);
+    __shared__ double red[kW];
+    const int tid = threadIdx.x;
+    m = wave_sum(m);
+    if (lane_id() == 0)
+        red[tid / kWave] = m;
+    if (tid < kWords)
+        reinterpret_cast<uint32_t*>(a.st)[tid] = 0u;
+    __syncthreads();
+    if (tid == 0) {
+        double tot = 0.0;
+        for (int w = 0; w < kW; ++w)
+            tot += red[w];
+        const bool bad = b != b;
+        a.st->b = b;
+        a.st->mass = tot;
+        a.st->emit_done = 1u;
+        a.st->nonfinite = bad ? 1u : 0u;
+        a.st->solve_state = bad ? kSolveNonfinite : kSolveOk;
+    }
+    __syncthreads();
+    publish_status(a.st, a.mirror, a.seq);
+}
+
 template <int kT, int R>
 __global__ __launch_bounds__(kT) void rows_forward_kernel(RowsArgs a)
 {
@@ -412,6 +443,8 @@ __global__ __launch_bounds__(kT) void rows_forward_kernel(RowsArgs a)
         }
         if (tid == 0)
             a.b[row] = NAN;
+        if (a.st != nullptr)
+            single_publish<kT>(a, 0.0, NAN);  // every thread is here: reports the non-finite score
         return;
     }
     block_sort_flip<kT, R>(key, buf0, buf1);
@@ -444,12 +477,18 @@ __global__ __launch_bounds__(kT) void rows_forward_kernel(RowsArgs a)
     if (tid == 0)
         a.b[row] = b;
     float* p = a.p + row * (int64_t)n;
+    double mass = 0.0;  // this thread's share of the fp64 mass of p
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int i = r * kT + tid;
-        if (i < n)
-            p[i] = row_p(vo[r], b, c);
+        if (i < n) {
+            const float pv = row_p(vo[r], b, c);
+            p[i] = pv;
+            mass += (double)pv;
+        }
     }
+    if (a.st != nullptr)
+        single_publish<kT>(a, mass, b);
 }
 
 // kVec: as in the lane-group backward, whole float4s per thread (thread t

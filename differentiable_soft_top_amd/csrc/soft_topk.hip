@@ -1157,21 +1157,30 @@ int soft_topk_forward_ex(const float* scores, int64_t n, double k, double alpha,
 
     if (n <= kRowMax && prm.force_path == 0 && prm.band_route == 0) {
         // one kernel sorts the whole vector in registers and solves it
-        // exactly (the full-sort solver, with no bracket to certify); a
-        // second folds the fp64 mass and publishes the status
+        // exactly (the full-sort solver, with no bracket to certify), then
+        // folds the fp64 mass and publishes the status (up to 64 scores a
+        // second kernel does that)
         RowsArgs ra = rows_args(scores, 1, n, alpha);
         ra.p = out_p;
         ra.b = out_b;
         ra.k = k;
+        const uint32_t seq = next_publication();
+        if (n > 64) {
+            ra.st = x.st;
+            ra.mirror = x.mirror0;
+            ra.seq = seq;
+        }
         STK_HIP(launch_row_alone(ra, true, x.stream));
-        SingleArgs sa;
-        sa.p = out_p;
-        sa.b = out_b;
-        sa.n = n;
-        sa.st = x.st;
-        sa.mirror = x.mirror0;
-        sa.seq = next_publication();
-        STK_HIP(launch_single_status(sa, x.stream));
+        if (n <= 64) {
+            SingleArgs sa;
+            sa.p = out_p;
+            sa.b = out_b;
+            sa.n = n;
+            sa.st = x.st;
+            sa.mirror = x.mirror0;
+            sa.seq = seq;
+            STK_HIP(launch_single_status(sa, x.stream));
+        }
         int rc = wait_solve(x, &h);
         if (rc)
             return rc;

@@ -464,6 +464,12 @@ struct RowsArgs {
     int64_t rows;
     int32_t n_row;
     double k, alpha, log2e_over_alpha;
+    // the single-vector route (one row of more than 64 scores): the forward
+    // kernel also folds the fp64 mass of its p into this status block and
+    // publishes it (nullptr: no status)
+    Status* st;
+    Mirror* mirror;
+    uint32_t seq;
 };
 hipError_t launch_rows(const RowsArgs& a, bool forward, hipStream_t stream);
 // One row (rows == 1, n_row <= kRowMax) with the shortest chain per thread:
