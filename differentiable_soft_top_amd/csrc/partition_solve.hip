@@ -43,7 +43,9 @@
 //     reduction (four waves: the reductions' shuffles and LDS folds cost per
 //     wave, and measured 4 us a pass with sixteen);
 //   several work-groups -- larger bands, or every score when the band
-//     overflowed its buffer: a chain of step kernels, each folding the
+//     overflowed its buffer (kIterGroups work-groups; kIterGroupsAll when
+//     the host knows before launch that every score is refined, since its
+//     fp64 terms want more waves): a chain of step kernels, each folding the
 //     previous step's per-group sums (every work-group the same way, so all
 //     agree on the next split point bit for bit), testing convergence and
 //     summing its share at the new point; the first also folds the pass-1
