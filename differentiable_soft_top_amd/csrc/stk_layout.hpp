@@ -54,7 +54,7 @@ constexpr uint32_t kSegDense = 0xFFFFFFFFu;
 constexpr int64_t kSegMinN = 1 << 22;  // measured: from 10^7 scores on the record pays
 static_assert(kStreamThreads == 256 && kVjpBatchLarge == 4,
               "segment geometry: large VJP tiles of 256 x 4 float4");
-constexpr int kRowMax = 8192;            // longest row one work-group solves (batched rows)
+constexpr int kRowMax = 8192;            // longest row held in one work-group's registers (single vectors, sorted; rows' backward)
 constexpr int kRefineRowMax = 2048;      // longest row the batched forward refines in a lane group
 constexpr int kBuckets = 512;            // value buckets of the band sort
 constexpr int kBucketCap = 8192;         // largest group the solve sorts in LDS
@@ -452,8 +452,8 @@ hipError_t launch_vjp(const VjpArgs& a, hipStream_t stream);
 
 hipError_t launch_reset_status(Status* st, hipStream_t stream, bool open_bracket);
 
-// Batched rows (rows x n_row, row-major, n_row <= kRowMax): one work-group
-// per row.
+// Batched rows (rows x n_row, row-major, any n_row): lane groups, or one
+// work-group per row (see launch_rows).
 struct RowsArgs {
     const float* s;
     const float* g;               // backward: cotangent
