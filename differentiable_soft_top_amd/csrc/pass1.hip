@@ -434,6 +434,7 @@ __global__ __launch_bounds__(kStreamThreads) void range_kernel(const float* __re
     const int64_t i0 = (n * blockIdx.x) / blocks;
     const int64_t i1 = (n * (blockIdx.x + 1)) / blocks;
     float mn = INFINITY, mx = -INFINITY, nf = 0.f;
+#pragma unroll 8
     for (int64_t i = i0 + tid; i < i1; i += kStreamThreads) {
         const float v = s[i];
         mn = fminf(mn, v);

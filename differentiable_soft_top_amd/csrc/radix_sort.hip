@@ -7,15 +7,25 @@
 //
 // Per digit, reduce-then-scan:
 //   upsweep   -- each work-group histograms the digit of its 8192-key tile
-//                into the [digit][tile] histogram;
-//   rowsum, rowscan -- one work-group per digit value: the row's total,
-//                then the row turned into exclusive global offsets (digit
-//                base from the totals of the smaller digits);
-//   downsweep -- each work-group ranks its tile's keys stably (wave-level
-//                match by eight ballots, wave counts combined in LDS in
-//                (round, wave, lane) order, i.e. index order) into LDS in
-//                destination order, then writes each digit's run to
-//                offset[digit][tile] onwards.
+//                into its row of the [tile][digit] counts (every key loaded
+//                before any is counted; one LDS add per key into one of
+//                16 sub-histograms; one coalesced 1 KiB store);
+//   chunk sums, chunk scan -- the counts become exclusive global offsets
+//                (digit base from the totals of the smaller digits, then
+//                the tiles in order): one work-group per chunk of tiles
+//                sums its rows per digit; then every chunk's work-group
+//                takes its prefix and the digit bases from those sums and
+//                rewrites its rows as offsets (all reads and writes are
+//                whole rows);
+//   downsweep -- wave w of a work-group ranks keys w*2048 ... w*2048 + 2047
+//                of its tile, 64 at a time in index order: a key's rank
+//                is its wave's running count of its digit plus the lanes
+//                below it with the same digit (eight ballots); the running
+//                counts live in the wave's own LDS row, so the 32 rounds
+//                need no barrier.  One barrier later the rows become each
+//                digit's prefix over the waves, the keys go to LDS in
+//                destination order, and each digit's run is written to
+//                its offset for this tile onwards.
 // Stability of every pass makes the LSD sort correct for any ties (the
 // clustered workload is 60% one value).
 #include "stk_common.hpp"
@@ -30,10 +40,12 @@ struct PassArgs {
     const float* s;        // pass 0 input
     const uint32_t* in;    // later passes
     uint32_t* out;
-    uint32_t* hist;        // [kRadixBins][gp]
+    uint32_t* hist;        // [g][kRadixBins] counts, then offsets
+    uint32_t* csum;        // [chunks][kRadixBins] chunk sums
     int64_t n;
     int32_t g;             // tiles
-    int32_t gp;            // row stride of hist (g rounded up to 4)
+    int32_t chunk;         // tiles per chunk
+    int32_t chunks;
     uint32_t key_min;
     int32_t shift;
     Status* st;
@@ -60,98 +72,118 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid)
     return peers;
 }
 
+constexpr int kRadixWaves = kRadixThreads / kWave;
+constexpr int kWaveKeys = kRadixTile / kRadixWaves;  // 2048 consecutive keys per wave
+static_assert(kWaveKeys == kRadixKeysPerThread * kWave, "one key per lane per round");
+
+// Key j (0..kRadixKeysPerThread-1) of this lane: wave-contiguous, so every
+// round of a wave reads 64 consecutive keys.
+__device__ __forceinline__ int64_t key_index(int64_t base, int wave, int lane, int j)
+{
+    return base + (int64_t)wave * kWaveKeys + (int64_t)j * kWave + lane;
+}
+
 }  // namespace
+
+// Sub-histograms per work-group: four per wave (one per 16 lanes), rows
+// padded to kHistStride words so one digit falls in a different LDS bank in
+// each row.  A digit that many lanes share (the top digit of narrow-range
+// scores, a tied cluster) then serialises over at most 16 lanes, and the
+// round's most common digit (the first lane's) is counted by one add.
+constexpr int kSubHists = kRadixWaves * 4;
+constexpr int kHistStride = kRadixBins + 1;
 
 template <bool kFromFloat>
 __global__ __launch_bounds__(kRadixThreads) void radix_upsweep(PassArgs a)
 {
-    __shared__ uint32_t hist[kRadixBins];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    for (int i = tid; i < kRadixBins; i += kRadixThreads)
-        hist[i] = 0;
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kRadixTile;
-    for (int r = 0; r < kRadixKeysPerThread; ++r) {
-        const int64_t i = base + (int64_t)r * kRadixThreads + tid;
-        const bool valid = i < a.n;
-        const uint32_t key = valid ? load_key<kFromFloat>(a, i) : 0u;
-        const uint32_t d = (key >> a.shift) & 0xFFu;
-        const uint64_t peers = match_digit(d, valid);
-        if (valid && lane == __ffsll((long long)peers) - 1)
-            atomicAdd(&hist[d], (uint32_t)__popcll(peers));
-    }
-    __syncthreads();
-    for (int dgt = tid; dgt < kRadixBins; dgt += kRadixThreads)
-        a.hist[(size_t)dgt * a.gp + blockIdx.x] = hist[dgt];
-}
-
-// One work-group per digit: its count over all tiles, into the totals row
-// that follows the [digit][tile] histogram.
-__global__ __launch_bounds__(kRadixThreads) void radix_rowsum(PassArgs a)
-{
-    __shared__ uint32_t red[kRadixThreads / kWave];
-    const int tid = threadIdx.x;
-    const uint32_t* row = a.hist + (size_t)blockIdx.x * a.gp;
-    uint32_t s = 0;
-    for (int t = tid; t < a.g; t += kRadixThreads)
-        s += row[t];
-    s = wave_sum_u32(s);
-    if ((tid & (kWave - 1)) == 0)
-        red[tid / kWave] = s;
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t tot = 0;
-        for (int w = 0; w < kRadixThreads / kWave; ++w)
-            tot += red[w];
-        a.hist[(size_t)kRadixBins * a.gp + blockIdx.x] = tot;
-    }
-}
-
-// One work-group per digit: the row's counts become exclusive global offsets
-// (all smaller digits first, then this digit's tiles in order).  Thread t
-// owns a contiguous run of tiles; one work-group scan joins the runs.
-__global__ __launch_bounds__(kRadixThreads) void radix_rowscan(PassArgs a)
-{
-    constexpr int kW = kRadixThreads / kWave;
-    __shared__ uint32_t wsum[kW];
-    __shared__ uint32_t base_sh;
+    __shared__ uint32_t hist[kSubHists * kHistStride];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int d = blockIdx.x;
-    const uint32_t* tot = a.hist + (size_t)kRadixBins * a.gp;
-    if (wave == 0) {
-        uint32_t s = 0;
-        for (int j = lane; j < d; j += kWave)
-            s += tot[j];
-        s = wave_sum_u32(s);
-        if (lane == 0)
-            base_sh = s;
-    }
-    uint32_t* row = a.hist + (size_t)d * a.gp;
-    const int per = (a.g + kRadixThreads - 1) / kRadixThreads;
-    const int t0 = tid * per < a.g ? tid * per : a.g;
-    const int t1 = t0 + per < a.g ? t0 + per : a.g;
-    uint32_t mine = 0;
-    for (int t = t0; t < t1; ++t)
-        mine += row[t];
-    uint32_t incl = mine;
+    for (int i = tid; i < kSubHists * kHistStride; i += kRadixThreads)
+        hist[i] = 0;
+    const int64_t base = (int64_t)blockIdx.x * kRadixTile;
+    uint32_t key[kRadixKeysPerThread];
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off, kWave);
-        if (lane >= off)
-            incl += o;
+    for (int j = 0; j < kRadixKeysPerThread; ++j) {
+        const int64_t i = key_index(base, wave, lane, j);
+        key[j] = i < a.n ? load_key<kFromFloat>(a, i) : 0u;
+    }
+    __syncthreads();  // sub-histograms cleared
+    uint32_t* h = hist + (wave * 4 + lane / 16) * kHistStride;
+#pragma unroll
+    for (int j = 0; j < kRadixKeysPerThread; ++j) {
+        const bool valid = key_index(base, wave, lane, j) < a.n;
+        const uint32_t d = (key[j] >> a.shift) & 0xFFu;
+        // valid lanes come first in every round, so lane 0 is valid
+        // whenever any lane is
+        const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+        const uint64_t same = __ballot(valid && d == d0);
+        if (lane == 0 && same != 0)
+            atomicAdd(&hist[wave * 4 * kHistStride + d0], (uint32_t)__popcll(same));
+        if (valid && d != d0)
+            atomicAdd(&h[d], 1u);
+    }
+    __syncthreads();
+    uint32_t c = 0;
+#pragma unroll
+    for (int q = 0; q < kSubHists; ++q)
+        c += hist[q * kHistStride + tid];
+    a.hist[(size_t)blockIdx.x * kRadixBins + tid] = c;
+}
+
+// One work-group per chunk of tiles: per digit (one per thread), the sum
+// of the chunk's rows.
+__global__ __launch_bounds__(kRadixBins) void radix_chunk_sum(PassArgs a)
+{
+    const int d = threadIdx.x;
+    const int t0 = blockIdx.x * a.chunk;
+    const int t1 = t0 + a.chunk < a.g ? t0 + a.chunk : a.g;
+    uint32_t s = 0;
+#pragma unroll 8
+    for (int t = t0; t < t1; ++t)
+        s += a.hist[(size_t)t * kRadixBins + d];
+    a.csum[(size_t)blockIdx.x * kRadixBins + d] = s;
+}
+
+// One work-group per chunk of tiles: per digit, the totals over all chunks
+// (an exclusive scan of them over the digits gives the digit bases) and
+// over the chunks before this one; then the chunk's rows become exclusive
+// global offsets, tile by tile.
+__global__ __launch_bounds__(kRadixBins) void radix_chunk_scan(PassArgs a)
+{
+    constexpr int kW = kRadixBins / kWave;
+    __shared__ uint32_t wsum[kW];
+    const int d = threadIdx.x;
+    const int lane = d & (kWave - 1);
+    const int wave = d / kWave;
+    const int c = blockIdx.x;
+    uint32_t tot = 0, pre = 0;
+#pragma unroll 8
+    for (int cc = 0; cc < a.chunks; ++cc) {
+        const uint32_t v = a.csum[(size_t)cc * kRadixBins + d];
+        tot += v;
+        pre += cc < c ? v : 0u;
+    }
+    uint32_t incl = tot;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, kWave);
+        if (lane >= o)
+            incl += v;
     }
     if (lane == kWave - 1)
         wsum[wave] = incl;
     __syncthreads();
-    uint32_t run = base_sh + incl - mine;
+    uint32_t run = incl - tot + pre;  // digit base plus the earlier chunks
     for (int w = 0; w < wave; ++w)
         run += wsum[w];
+    const int t0 = c * a.chunk;
+    const int t1 = t0 + a.chunk < a.g ? t0 + a.chunk : a.g;
+#pragma unroll 8
     for (int t = t0; t < t1; ++t) {
-        const uint32_t v = row[t];
-        row[t] = run;
+        const uint32_t v = a.hist[(size_t)t * kRadixBins + d];
+        a.hist[(size_t)t * kRadixBins + d] = run;
         run += v;
     }
 }
@@ -160,39 +192,43 @@ __global__ __launch_bounds__(kRadixThreads) void radix_rowscan(PassArgs a)
 // digit's run in index order), then written out run by run, so the global
 // stores go to consecutive addresses instead of 256 scattered buckets.  A
 // digit's count in this tile is the step from its offset to the next
-// tile's (or, for the last tile, to the next digit's first offset).
+// tile's (or, for the last tile, to the next digit's base).
 template <bool kFromFloat>
 __global__ __launch_bounds__(kRadixThreads) void radix_downsweep(PassArgs a)
 {
-    constexpr int kWaves = kRadixThreads / kWave;
     __shared__ uint32_t goff[kRadixBins];
     __shared__ uint32_t lstart[kRadixBins];
-    __shared__ uint32_t running[kRadixBins];
-    __shared__ uint32_t wcnt[kWaves][kRadixBins];
-    __shared__ uint32_t wpre[kWaves][kRadixBins];
+    __shared__ uint32_t wrun[kRadixWaves][kRadixBins];  // a wave's running counts, then its prefix
     __shared__ uint32_t stage[kRadixTile];
-    __shared__ uint32_t wsum[kWaves];
+    __shared__ uint32_t wsum[kRadixWaves];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int t = blockIdx.x;
     static_assert(kRadixThreads == kRadixBins, "one thread per digit");
+    const int64_t base = (int64_t)t * kRadixTile;
+    uint32_t key[kRadixKeysPerThread];
+#pragma unroll
+    for (int j = 0; j < kRadixKeysPerThread; ++j) {
+        const int64_t i = key_index(base, wave, lane, j);
+        key[j] = i < a.n ? load_key<kFromFloat>(a, i) : 0u;
+    }
     {
         // this thread's digit: global offset and count in this tile
         const int d = tid;
-        const uint32_t off = a.hist[(size_t)d * a.gp + t];
+        const uint32_t off = a.hist[(size_t)t * kRadixBins + d];
         uint32_t next;
         if (t + 1 < a.g)
-            next = a.hist[(size_t)d * a.gp + t + 1];
+            next = a.hist[(size_t)(t + 1) * kRadixBins + d];
         else if (d + 1 < kRadixBins)
-            next = a.hist[(size_t)(d + 1) * a.gp];
+            next = a.hist[d + 1];  // tile 0's offset of the next digit: its base
         else
             next = (uint32_t)a.n;
         const uint32_t cnt = next - off;
         goff[d] = off;
-        running[d] = 0;
-        for (int w = 0; w < kWaves; ++w)
-            wcnt[w][d] = 0;
+#pragma unroll
+        for (int w = 0; w < kRadixWaves; ++w)
+            wrun[w][d] = 0;
         // exclusive scan of the counts over digits: the runs' starts in LDS
         uint32_t incl = cnt;
 #pragma unroll
@@ -209,39 +245,53 @@ __global__ __launch_bounds__(kRadixThreads) void radix_downsweep(PassArgs a)
             ex += wsum[w];
         lstart[d] = ex;
     }
-    __syncthreads();
-    const int64_t base = (int64_t)t * kRadixTile;
-    for (int r = 0; r < kRadixKeysPerThread; ++r) {
-        const int64_t i = base + (int64_t)r * kRadixThreads + tid;
-        const bool valid = i < a.n;
-        const uint32_t key = valid ? load_key<kFromFloat>(a, i) : 0u;
-        const uint32_t d = (key >> a.shift) & 0xFFu;
-        const uint64_t peers = match_digit(d, valid);
-        const uint32_t rank = rank_in_mask(peers);
-        if (valid && rank == 0)
-            wcnt[wave][d] = (uint32_t)__popcll(peers);
-        __syncthreads();
-        for (int dd = tid; dd < kRadixBins; dd += kRadixThreads) {
-            uint32_t run = running[dd];
+    // ranks within this wave's 2048 keys, in index order: the wave's LDS
+    // row is read by every lane, then advanced by the lowest lane of each
+    // digit; one wave's LDS accesses take effect in program order, so no
+    // barrier is needed between rounds
+    // two ranks (each below 2048) per register
+    uint32_t rk[kRadixKeysPerThread / 2];
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                wpre[w][dd] = run;
-                run += wcnt[w][dd];
-                wcnt[w][dd] = 0;
-            }
-            running[dd] = run;
+    for (int j = 0; j < kRadixKeysPerThread; ++j) {
+        const bool valid = key_index(base, wave, lane, j) < a.n;
+        const uint32_t d = (key[j] >> a.shift) & 0xFFu;
+        const uint64_t peers = match_digit(d, valid);
+        const uint32_t below = rank_in_mask(peers);
+        const uint32_t before = wrun[wave][d];
+        if (j & 1)
+            rk[j / 2] |= (before + below) << 16;
+        else
+            rk[j / 2] = before + below;
+        if (valid && below == 0)
+            wrun[wave][d] = before + (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+    {
+        // each digit's counts over the waves become the waves' starts
+        const int d = tid;
+        uint32_t run = 0;
+#pragma unroll
+        for (int w = 0; w < kRadixWaves; ++w) {
+            const uint32_t c = wrun[w][d];
+            wrun[w][d] = run;
+            run += c;
         }
-        __syncthreads();
-        if (valid)
-            stage[lstart[d] + wpre[wave][d] + rank] = key;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRadixKeysPerThread; ++j) {
+        if (key_index(base, wave, lane, j) < a.n) {
+            const uint32_t d = (key[j] >> a.shift) & 0xFFu;
+            stage[lstart[d] + wrun[wave][d] + ((rk[j / 2] >> (16 * (j & 1))) & 0xFFFFu)] = key[j];
+        }
     }
     __syncthreads();
     const int64_t left = a.n - base;
     const int cnt = left < (int64_t)kRadixTile ? (int)left : kRadixTile;
     for (int j = tid; j < cnt; j += kRadixThreads) {
-        const uint32_t key = stage[j];
-        const uint32_t d = (key >> a.shift) & 0xFFu;
-        a.out[goff[d] + (uint32_t)j - lstart[d]] = key;
+        const uint32_t k = stage[j];
+        const uint32_t d = (k >> a.shift) & 0xFFu;
+        a.out[goff[d] + (uint32_t)j - lstart[d]] = k;
     }
 }
 
@@ -251,8 +301,10 @@ hipError_t launch_radix_sort(const RadixArgs& ra, hipStream_t stream)
     a.s = ra.s;
     a.n = ra.n;
     a.g = ra.g_radix;
-    a.gp = (ra.g_radix + 3) & ~3;
+    a.chunk = radix_chunk_tiles(ra.g_radix);
+    a.chunks = (ra.g_radix + a.chunk - 1) / a.chunk;  // <= kRadixMaxChunks
     a.hist = ra.hist;
+    a.csum = ra.hist + (size_t)ra.g_radix * kRadixBins;
     a.key_min = ra.key_min;
     a.st = ra.st;
     uint32_t* bufs[2] = {ra.keys0, ra.keys1};
@@ -265,8 +317,8 @@ hipError_t launch_radix_sort(const RadixArgs& ra, hipStream_t stream)
         } else {
             STK_LAUNCH(kKRadixUp, stream, radix_upsweep<false>, dim3(a.g), dim3(kRadixThreads), 0, stream, a);
         }
-        STK_LAUNCH(kKRadixScan, stream, radix_rowsum, dim3(kRadixBins), dim3(kRadixThreads), 0, stream, a);
-        STK_LAUNCH(kKRadixScan, stream, radix_rowscan, dim3(kRadixBins), dim3(kRadixThreads), 0, stream, a);
+        STK_LAUNCH(kKRadixScan, stream, radix_chunk_sum, dim3(a.chunks), dim3(kRadixBins), 0, stream, a);
+        STK_LAUNCH(kKRadixScan, stream, radix_chunk_scan, dim3(a.chunks), dim3(kRadixBins), 0, stream, a);
         if (p == 0) {
             STK_LAUNCH(kKRadixDown, stream, radix_downsweep<true>, dim3(a.g), dim3(kRadixThreads), 0, stream, a);
         } else {

@@ -949,8 +949,8 @@ Plan make_plan(int64_t n, int32_t m, int64_t cap)
     p.off_keys1 = o;
     o = align_up(o + sizeof(uint32_t) * (size_t)n);
     p.off_rhist = o;
-    // [digit][tile] histogram, then one total per digit
-    o = align_up(o + sizeof(uint32_t) * kRadixBins * ((size_t)((p.g_radix + 3) & ~3) + 1));
+    // [tile][digit] counts (turned into offsets in place), then the chunk sums
+    o = align_up(o + sizeof(uint32_t) * kRadixBins * ((size_t)p.g_radix + kRadixMaxChunks));
     p.off_super = o;
     o = align_up(o + sizeof(Pass1Partial) * (size_t)kBuckets);
     p.total = o;

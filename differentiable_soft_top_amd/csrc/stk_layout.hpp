@@ -73,6 +73,16 @@ constexpr int kRadixThreads = 256;
 constexpr int kRadixKeysPerThread = 32;
 constexpr int kRadixTile = kRadixThreads * kRadixKeysPerThread;  // 8192 keys
 constexpr int kRadixBins = 256;
+// The per-tile digit counts ([tile][digit], one 1 KiB row per tile) are
+// scanned in chunks of tiles: at most kRadixMaxChunks chunks, each of at
+// least kRadixMinChunk tiles.
+constexpr int kRadixMinChunk = 16;
+constexpr int kRadixMaxChunks = 128;
+__host__ __device__ constexpr int32_t radix_chunk_tiles(int32_t g)
+{
+    return (g + kRadixMaxChunks - 1) / kRadixMaxChunks > kRadixMinChunk ? (g + kRadixMaxChunks - 1) / kRadixMaxChunks
+                                                                        : kRadixMinChunk;
+}
 constexpr int64_t kNontemporalMin = 1 << 25;  // outputs of at least 128 MiB bypass the caches
 // Partition refinement of the band (no sort): one work-group holds up to
 // kIterOneCap band values in LDS and runs at most kIterOneMax passes;
@@ -396,7 +406,7 @@ struct RadixArgs {
     int64_t n;
     uint32_t* keys0;
     uint32_t* keys1;
-    uint32_t* hist;               // [kRadixBins][g_radix]
+    uint32_t* hist;               // [g_radix][kRadixBins] counts, then offsets; then [chunks][kRadixBins] chunk sums
     int32_t g_radix;
     uint32_t key_min;             // subtracted from every key
     int32_t passes;               // 8-bit digits to sort

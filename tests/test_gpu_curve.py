@@ -73,6 +73,23 @@ def test_curve_large_sampled_and_brackets_the_forward(dev):
         assert lo - 1e-6 * alpha <= b <= hi + 1e-6 * alpha, (k, j, lo, b, hi)
 
 
+def test_curve_many_tiles_sorted_exactly(dev):
+    """Over 2048 sort tiles of 8192 scores, so the sort's offsets are scanned
+    in chunks of more than the smallest chunk: the sorted output equals
+    numpy's sort and sampled masses match the oracle."""
+    n, alpha = (1 << 25) + 12_345, 1e-3
+    rng = np.random.default_rng(11)
+    s_np = rng.random(n, dtype=np.float32)
+    xs, m = curve(dev, s_np, alpha)
+    same_values(xs, s_np)
+    # tied values (U(0,1) in fp32 repeats values here) get masses equal up to
+    # rounding, and an fp64 ulp of masses near n is 4e-9: the bound scales
+    # with n as the mass bound does
+    assert np.all(np.diff(m) <= 1e-9 + 1e-11 * n)
+    for j in np.concatenate([[0, n - 1], rng.integers(0, n, 30)]):
+        assert abs(m[j] - O.mass(s_np, float(xs[j]), alpha)) <= 1e-7 + 1e-11 * n, j
+
+
 def test_curve_rejects_nonfinite_and_bad_arguments(dev):
     s_np = np.random.default_rng(1).standard_normal(5000).astype(np.float32)
     s_np[17] = np.nan
