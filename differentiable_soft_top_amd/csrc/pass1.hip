@@ -434,12 +434,22 @@ __global__ __launch_bounds__(kStreamThreads) void range_kernel(const float* __re
     const int64_t i0 = (n * blockIdx.x) / blocks;
     const int64_t i1 = (n * (blockIdx.x + 1)) / blocks;
     float mn = INFINITY, mx = -INFINITY, nf = 0.f;
-#pragma unroll 8
-    for (int64_t i = i0 + tid; i < i1; i += kStreamThreads) {
-        const float v = s[i];
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
-        nf = fmaf(v, 0.f, nf);
+    // eight loads in flight per lane; past i1 a load repeats the range's
+    // first score (no branch around a load; a repeat changes no extreme)
+    constexpr int kU = 8;
+    for (int64_t i = i0 + tid; i < i1; i += kU * kStreamThreads) {
+        float v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t j = i + (int64_t)u * kStreamThreads;
+            v[u] = s[j < i1 ? j : i0];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            mn = fminf(mn, v[u]);
+            mx = fmaxf(mx, v[u]);
+            nf = fmaf(v[u], 0.f, nf);
+        }
     }
     uint32_t bad = (nf != 0.f || nf != nf) ? 1u : 0u;
 #pragma unroll

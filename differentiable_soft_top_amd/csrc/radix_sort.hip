@@ -51,13 +51,6 @@ struct PassArgs {
     Status* st;
 };
 
-template <bool kFromFloat>
-__device__ __forceinline__ uint32_t load_key(const PassArgs& a, int64_t i)
-{
-    if (kFromFloat)
-        return float_to_key(a.s[i]) - a.key_min;
-    return a.in[i];
-}
 
 // Lanes of this wave whose digit equals mine (among lanes with valid=true).
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid)
@@ -83,6 +76,34 @@ __device__ __forceinline__ int64_t key_index(int64_t base, int wave, int lane, i
     return base + (int64_t)wave * kWaveKeys + (int64_t)j * kWave + lane;
 }
 
+// The tile's keys of this lane: every load is issued before any key is
+// formed, and no branch sits around a load, so none waits for the one
+// before it (in the last, partial tile a load of the last key stands in
+// past n).
+template <bool kFromFloat>
+__device__ __forceinline__ void load_keys(const PassArgs& a, int64_t base, int wave, int lane,
+                                          uint32_t (&key)[kRadixKeysPerThread])
+{
+    if (base + kRadixTile <= a.n) {
+        const int64_t i0 = key_index(base, wave, lane, 0);
+#pragma unroll
+        for (int j = 0; j < kRadixKeysPerThread; ++j)
+            key[j] = kFromFloat ? __float_as_uint(a.s[i0 + j * kWave]) : a.in[i0 + j * kWave];
+    } else {
+#pragma unroll
+        for (int j = 0; j < kRadixKeysPerThread; ++j) {
+            const int64_t i = key_index(base, wave, lane, j);
+            const int64_t ic = i < a.n ? i : a.n - 1;
+            key[j] = kFromFloat ? __float_as_uint(a.s[ic]) : a.in[ic];
+        }
+    }
+    if (kFromFloat) {
+#pragma unroll
+        for (int j = 0; j < kRadixKeysPerThread; ++j)
+            key[j] = float_to_key(__uint_as_float(key[j])) - a.key_min;
+    }
+}
+
 }  // namespace
 
 // Sub-histograms per work-group: four per wave (one per 16 lanes), rows
@@ -104,11 +125,7 @@ __global__ __launch_bounds__(kRadixThreads) void radix_upsweep(PassArgs a)
         hist[i] = 0;
     const int64_t base = (int64_t)blockIdx.x * kRadixTile;
     uint32_t key[kRadixKeysPerThread];
-#pragma unroll
-    for (int j = 0; j < kRadixKeysPerThread; ++j) {
-        const int64_t i = key_index(base, wave, lane, j);
-        key[j] = i < a.n ? load_key<kFromFloat>(a, i) : 0u;
-    }
+    load_keys<kFromFloat>(a, base, wave, lane, key);
     __syncthreads();  // sub-histograms cleared
     uint32_t* h = hist + (wave * 4 + lane / 16) * kHistStride;
 #pragma unroll
@@ -208,11 +225,7 @@ __global__ __launch_bounds__(kRadixThreads) void radix_downsweep(PassArgs a)
     static_assert(kRadixThreads == kRadixBins, "one thread per digit");
     const int64_t base = (int64_t)t * kRadixTile;
     uint32_t key[kRadixKeysPerThread];
-#pragma unroll
-    for (int j = 0; j < kRadixKeysPerThread; ++j) {
-        const int64_t i = key_index(base, wave, lane, j);
-        key[j] = i < a.n ? load_key<kFromFloat>(a, i) : 0u;
-    }
+    load_keys<kFromFloat>(a, base, wave, lane, key);
     {
         // this thread's digit: global offset and count in this tile
         const int d = tid;
