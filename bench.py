@@ -395,6 +395,10 @@ def main():
     ap.add_argument("--rows", default="r1,r2", help="batched-row workloads timed (comma list, '' for none)")
     ap.add_argument("--dftopk", default="c1,c2,c3,c4",
                     help="workloads timed with the DFTopK comparator, whose mass drift is reported")
+    ap.add_argument("--curve", default="c3,c4",
+                    help="workloads whose threshold curve (full sort of the scores, then the mass at each) is timed")
+    ap.add_argument("--fullsort", default="c2,c3",
+                    help="workloads timed forward+backward on the forced full-sort route (the fallback)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="counter-collection run: a few steps of --workload (c1..c5 or a row workload "
@@ -567,6 +571,57 @@ def main():
         del ds, dp, dws
         torch.cuda.empty_cache()
 
+    # the full-sort route forced (the fallback of the bracketed solver),
+    # forward + backward through the same runner
+    full_out = {}
+    for fname in [x for x in args.fullsort.split(",") if x]:
+        fs_np, fk, falpha, fw = make_workload(fname)
+        fprm = _lib.default_params()
+        fprm.force_path = _lib.PATH_FULLSORT
+        frun = Runner(torch, lib, torch.from_numpy(fs_np).to(dev), torch.from_numpy(draw_grad(fs_np.size, fw.seed)).to(dev),
+                      fk, falpha, params=fprm)
+        frun.step(stats=True)
+        for _ in range(3):
+            frun.step()
+        ft = time_steps(torch, frun, 20)
+        full_out[fname] = {"workload": fw.description, "n": int(fs_np.size), "k": fk, "alpha": falpha,
+                           "median_ms": float(np.median(ft)), "p10_ms": float(np.percentile(ft, 10)),
+                           "p90_ms": float(np.percentile(ft, 90)), "path": frun.stats.path}
+        del frun
+        torch.cuda.empty_cache()
+
+    # the threshold curve: sorted scores and the mass each selects as a
+    # threshold (soft_topk_threshold_curve)
+    curve_out = {}
+    for cname in [x for x in args.curve.split(",") if x]:
+        if cname == args.workload:
+            cs, calpha, cw = run.batches[0][0], alpha, w
+        else:
+            cs_np, _, calpha, cw = make_workload(cname)
+            cs = torch.from_numpy(cs_np).to(dev)
+        cn = cs.numel()
+        c_sorted = torch.empty_like(cs)
+        c_mass = torch.empty(cn, dtype=torch.float64, device=dev)
+        cws_bytes = lib.soft_topk_workspace_bytes(cn, None)
+        cws = torch.empty(cws_bytes, dtype=torch.uint8, device=dev)
+        cstream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        cargs = (ctypes.c_void_p(cs.data_ptr()), cn, ctypes.c_double(calpha), ctypes.c_void_p(c_sorted.data_ptr()),
+                 ctypes.c_void_p(c_mass.data_ptr()), ctypes.c_void_p(cws.data_ptr()), cws_bytes, cstream)
+
+        class _CurveRun:
+            def step(self):
+                _lib.check(lib.soft_topk_threshold_curve(*cargs), "soft_topk_threshold_curve")
+
+        crun = _CurveRun()
+        for _ in range(3):
+            crun.step()
+        ct = time_steps(torch, crun, 10)
+        curve_out[cname] = {"workload": cw.description, "n": int(cn), "alpha": calpha,
+                            "median_ms": float(np.median(ct)), "p10_ms": float(np.percentile(ct, 10)),
+                            "p90_ms": float(np.percentile(ct, 90))}
+        del c_sorted, c_mass, cws
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(s_np, g_np, k, alpha, args.workload)
@@ -616,6 +671,8 @@ def main():
         "sizes": sizes,
         "rows": rows_out,
         "dftopk": dft_out,
+        "fullsort": full_out,
+        "curve": curve_out,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
