@@ -399,6 +399,9 @@ def main():
                     help="workloads whose threshold curve (full sort of the scores, then the mass at each) is timed")
     ap.add_argument("--fullsort", default="c2,c3",
                     help="workloads timed forward+backward on the forced full-sort route (the fallback)")
+    ap.add_argument("--coverage", default="c1,c2,c3,c4",
+                    help="workloads run with 100 sampler seeds each on the bracketed route: how many "
+                         "certify on their first round (no widening, no fallback)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="counter-collection run: a few steps of --workload (c1..c5 or a row workload "
@@ -622,6 +625,34 @@ def main():
         del c_sorted, c_mass, cws
         torch.cuda.empty_cache()
 
+    # path coverage: 100 Philox seeds per workload on the bracketed route
+    # (forced for c1, which would otherwise take the one-kernel route)
+    import differentiable_soft_top_amd as stk
+    cov_out = {}
+    for vname in [x for x in args.coverage.split(",") if x]:
+        if vname == args.workload:
+            vs, vk, valpha = run.batches[0][0], k, alpha
+        else:
+            vs_np, vk, valpha, _ = make_workload(vname)
+            vs = torch.from_numpy(vs_np).to(dev)
+        seeds = [int(x) for x in np.random.default_rng(2024).integers(1, 2 ** 63, 100)]
+        first = widened = other = 0
+        for seed in seeds:
+            vprm_s = _lib.default_params()
+            vprm_s.seed = seed
+            vprm_s.force_path = _lib.PATH_BRACKET
+            _, _, vst = stk.forward(vs, vk, valpha, vprm_s, want_stats=True)
+            if vst["path"] == _lib.PATH_BRACKET and vst["rounds"] == 1:
+                first += 1
+            elif vst["path"] == _lib.PATH_WIDENED:
+                widened += 1
+            else:
+                other += 1
+        cov_out[vname] = {"seeds": len(seeds), "certified_first_round": first, "widened": widened,
+                          "other_route": other}
+        del vs
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(s_np, g_np, k, alpha, args.workload)
@@ -673,6 +704,7 @@ def main():
         "dftopk": dft_out,
         "fullsort": full_out,
         "curve": curve_out,
+        "coverage": cov_out,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
