@@ -90,6 +90,33 @@ def test_curve_many_tiles_sorted_exactly(dev):
         assert abs(m[j] - O.mass(s_np, float(xs[j]), alpha)) <= 1e-7 + 1e-11 * n, j
 
 
+@pytest.mark.parametrize("case", ["all_equal", "wide_magnitudes"])
+def test_curve_sort_edge_distributions(dev, case):
+    """The radix sort on key sets that stress its digit counting: every
+    score equal (one pass, one digit everywhere: every tied point's mass is
+    n/2 exactly up to rounding), and signed scores spread over the whole
+    float exponent range with zeros and repeats (four passes, digits shared
+    by many lanes at the top)."""
+    n = 100_003
+    rng = np.random.default_rng(7)
+    if case == "all_equal":
+        s_np = np.full(n, 0.625, dtype=np.float32)
+        alpha = 0.1
+    else:
+        mag = 10.0 ** rng.uniform(-30, 30, n)
+        s_np = (np.where(rng.random(n) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
+        s_np[rng.integers(0, n, 5000)] = 0.0
+        s_np[rng.integers(0, n, 5000)] = np.float32(3.5)
+        alpha = 1.0
+    xs, m = curve(dev, s_np, alpha)
+    same_values(xs, s_np)
+    assert np.all(np.diff(m) <= 1e-9 + 1e-11 * n)
+    if case == "all_equal":
+        assert np.max(np.abs(m - n / 2.0)) <= 1e-7 + 1e-11 * n
+    for j in np.concatenate([[0, n - 1], rng.integers(0, n, 30)]):
+        assert abs(m[j] - O.mass(s_np, float(xs[j]), alpha)) <= 1e-7 + 1e-11 * n, j
+
+
 def test_curve_rejects_nonfinite_and_bad_arguments(dev):
     s_np = np.random.default_rng(1).standard_normal(5000).astype(np.float32)
     s_np[17] = np.nan
