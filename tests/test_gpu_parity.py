@@ -731,6 +731,25 @@ def test_c5_full_sort_fallback(dev):
     assert abs(m - k) <= 1e-3 + gold["mass_p32_rounding_floor"], (m, k)
 
 
+def test_forced_full_sort_at_full_size(dev):
+    """c4 (1e8 scores) on the forced full-sort route: the radix sort over
+    12,208 tiles (offsets scanned in chunks of 96) and the solve over 24,415
+    summaries return the stored oracle b and the certified mass, and every
+    p agrees with the default route's (whose every element
+    test_gpu_fullsize compares with the oracle)."""
+    gold = GOLD["c4"]
+    s_np, k, alpha, w = make_workload("c4")
+    s = torch.from_numpy(s_np).to(dev)
+    p, b, st = stk.forward(s, k, alpha, params(force_path=_lib.PATH_FULLSORT), want_stats=True)
+    assert st["path"] == _lib.PATH_FULLSORT, st
+    b = float(b.item())
+    assert abs(b - gold["b"]) <= 1e-5 * alpha, (b, gold["b"])
+    assert abs(st["mass"] - k) <= 1e-3 + gold["mass_p32_rounding_floor"], st["mass"]
+    p_default, b_default = stk.forward(s, k, alpha)
+    assert abs(float(b_default.item()) - b) <= 1e-5 * alpha
+    assert float(torch.max(torch.abs(p.double() - p_default.double())).item()) <= 1e-5
+
+
 # --------------------------------------------------------------------------
 # path coverage: the bracket certifies on its first round for every seed
 # --------------------------------------------------------------------------
